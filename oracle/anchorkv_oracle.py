@@ -1,0 +1,487 @@
+"""CPU oracle of the anchor-residual KV-cache hot path (AnchorKV).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It shares no code with the HIP path
+and imports nothing from it.
+
+Plain NumPy in float64, one unit (one layer of one sequence, all of its KV
+heads) at a time, dense and unblocked, in the order the method states its steps.
+Inputs are the exact bf16 / f32 values, upcast to float64.
+
+Sources (web pages on the method; cited by page title and section):
+  [Pith] "Pith review of AnchorKV: Anchor-Residual KV Cache Compression"
+         (pith.science), sections "What carries the argument", "What would
+         settle it", "Referee Report", "Assumptions & free parameters".
+  [Velox] "AnchorKV-adapted - Anchor-Residual Compression, No Eviction"
+         (VeloxQuant-MLX docs), sections "The problem this solves", "The one
+         setting worth tuning: anchorkv_theta", "Adaptation notes", "Evidence".
+Where the pages are silent the reading taken is stated at the step (readings
+R1..R20, listed together in the design notes of the repository).
+
+Implementation contract (not on the pages, fixed for this implementation): the
+residual codec is 2-bit group-affine with one fp16 scale and one fp16 zero per
+32 contiguous coordinates; anchors cost D*e bytes, pointers 4 bytes (2-byte
+index + 2-byte fp16 coefficient), residuals D/4 + D/8 bytes; decode logits are
+gamma * <q, k_anchor> + <q, r~> with no RoPE.
+
+Parity status: every function here is pinned by tests under tests/ (library
+routines, closed forms, brute force, finite differences, invariants), except
+the readings that no printed example fixes (R2-R8, R14-R18), which are pinned
+only by being written once here and checked by brute force against this text.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+POOL = 7            # kappa, positional pooling width [Pith, "Assumptions & free parameters"]
+RHO = 0.7           # scored share of non-window anchors [Pith, same]
+ANCHOR_DIV = 128    # k = S/128 non-window anchors [Pith, same]
+GROUP = 32          # codec group size (implementation contract)
+HEADER_PER_SIDE = 128
+CHUNK = 1024        # tokens per residual-offset chunk
+MAX_ANCHORS = 32767  # anchor index is 15 bits (bit 15 flags a residual)
+FP16_MAX = 65504.0
+
+
+# --------------------------------------------------------------------------
+# Rounding helpers
+# --------------------------------------------------------------------------
+def fp16_rne(x):
+    """Round float64 to the nearest fp16 value (ties to even), saturating to
+    +-65504 instead of overflowing to infinity (reading R12).  Returned as
+    float64.  numpy's double->half conversion is correctly rounded; the tests
+    pin it against a brute-force search over all 65536 half values."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        y = x.astype(np.float16).astype(np.float64)
+    return np.where(np.isinf(y) & np.isfinite(x), np.sign(x) * FP16_MAX, y)
+
+
+def fp32_round(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Byte plan [Pith, "What carries the argument" (per-layer byte accounting, theta
+# the only knob) and "Assumptions & free parameters" (theta, k = S/128, rho,
+# W, b_a = b_gamma = 2 bytes)]; [Velox, "The one setting worth tuning"].
+# --------------------------------------------------------------------------
+@dataclass
+class Plan:
+    H: int
+    N: int
+    D: int
+    e: int
+    theta: float
+    W: int
+    A: int
+    k_s: int
+    k_u: int
+    R_K: int
+    R_V: int
+    budget_unit: int        # floor(theta * H * N * D * e) bytes per side per unit
+    fixed_per_side: int     # header share + anchors + pointers + positions + chunk offsets
+    n_chunks: int
+
+
+def plan(H, N, D, e, theta, W):
+    """Anchor and residual counts of one unit.
+
+    theta is taken at float32 precision (the value the C ABI receives) and all
+    byte arithmetic is done in float64 then floored.
+    Per head and side the budget is B = theta * N * D * e bytes.  Anchors cost
+    D*e bytes plus 2 bytes of position each (the int32 position is shared by the
+    two sides), every token costs a 4-byte pointer, every 1024-token chunk a
+    4-byte residual offset, and the unit header 128 bytes per side, spread over
+    the H heads:
+        A_max = floor((B - 4N - 4*ceil(N/1024) - 128/H) / (D*e + 2)).
+    Reading R2: k = floor(N/128) non-window anchors, capped so the anchors fit
+    the budget and so that there are enough non-window tokens:
+        k_nw = max(0, min(floor(N/128), A_max - W, N - W)).
+    Reading R3: the window is not part of k: A = W + k_nw.
+    Reading R4: k_s = floor(0.7 * k_nw) scored, k_u = k_nw - k_s uniform.
+    Residual slots per side per unit (pooled over heads; reading R16):
+        R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed) / (D/4 + D/8))).
+    """
+    if not (N >= 1 and 1 <= W <= N and D % GROUP == 0 and H >= 1):
+        raise ValueError("bad shape")
+    th = float(np.float32(theta))
+    C = -(-N // CHUNK)
+    B = th * float(N * D * e)
+    A_max = math.floor((B - 4.0 * N - 4.0 * C - HEADER_PER_SIDE / H) / (D * e + 2))
+    if A_max < W:
+        raise ValueError("budget too small for the window anchors and pointers")
+    k_nw = max(0, min(N // ANCHOR_DIV, A_max - W, N - W))
+    k_s = math.floor(RHO * k_nw)
+    k_u = k_nw - k_s
+    A = W + k_nw
+    if A > MAX_ANCHORS:
+        raise ValueError("too many anchors for a 15-bit index")
+    budget_unit = math.floor(th * float(H * N * D * e))
+    fixed = HEADER_PER_SIDE + H * (A * D * e + 4 * N + 2 * A + 4 * C)
+    rec = D // 4 + D // 8
+    R = max(0, min(H * (N - A), (budget_unit - fixed) // rec))
+    return Plan(H, N, D, e, th, W, A, k_s, k_u, R, R, budget_unit, fixed, C)
+
+
+def side_bytes(p: Plan, R: int) -> int:
+    """Bytes one side of one unit occupies: fixed part + R residual records."""
+    return p.fixed_per_side + R * (p.D // 4 + p.D // 8)
+
+
+# --------------------------------------------------------------------------
+# Step 1: observation-window attention [Pith, "What carries the argument"
+# (SnapKV observation-window score) and "Assumptions & free parameters"
+# (last W tokens' attention pooled over GQA query heads)].
+# --------------------------------------------------------------------------
+def obs_attention(Qh, Kh, Vh, n_obs):
+    """Causal softmax attention of one KV head's observation queries.
+
+    Qh: [GQ, D] rows ordered (q-head g, obs index j) -> row g*n_obs + j.
+    Query j sits at position N - n_obs + j and sees keys t <= N - n_obs + j
+    (reading R8).  Returns P [GQ, N] (probabilities), O = P @ V [GQ, D].
+    """
+    GQ, D = Qh.shape
+    N = Kh.shape[0]
+    S = (Qh @ Kh.T) / math.sqrt(D)
+    j = np.arange(GQ) % n_obs
+    visible = np.arange(N)[None, :] <= (N - n_obs + j)[:, None]
+    S = np.where(visible, S, -np.inf)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    P = E / E.sum(axis=1, keepdims=True)
+    return P, P @ Vh
+
+
+# --------------------------------------------------------------------------
+# Step 2: anchor score and positional pooling [Pith, "What carries the
+# argument"; "Assumptions & free parameters" (pooling width kappa = 7, pooled
+# over GQA query heads)].
+# --------------------------------------------------------------------------
+def anchor_score(P, W):
+    """score_t = sum over the head's observation queries of P[:, t] (reading R7),
+    for every t; pooled_t = sum of score_u over |u - t| <= 3 and u < N - W
+    (reading R6: windowed sum = zero-padded mean over 7), for t < N - W."""
+    N = P.shape[1]
+    score = P.sum(axis=0)
+    L = N - W
+    half = POOL // 2
+    pooled = np.zeros(L)
+    for t in range(L):
+        lo, hi = max(0, t - half), min(L, t + half + 1)
+        pooled[t] = score[lo:hi].sum()
+    return score, pooled
+
+
+def select_anchors(pooled, N, W, k_s, k_u):
+    """Anchor positions, ascending (reading R9: the anchor index is the rank).
+
+    * window: the last W positions [Pith, "Assumptions & free parameters"];
+    * scored: the k_s largest pooled scores, ties to the lower position;
+    * uniform (reading R5): with c the remaining non-window positions in
+      ascending order (M of them), take c[floor((2i+1) * M / (2 k_u))], i < k_u.
+    """
+    L = N - W
+    order = np.lexsort((np.arange(L), -pooled))   # by (-pooled, position)
+    scored = np.sort(order[:k_s])
+    taken = np.zeros(L, dtype=bool)
+    taken[scored] = True
+    rest = np.nonzero(~taken)[0]
+    M = rest.size
+    uni = np.array([rest[((2 * i + 1) * M) // (2 * k_u)] for i in range(k_u)], dtype=np.int64)
+    pos = np.concatenate([scored, uni, np.arange(L, N)])
+    return np.sort(pos).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Steps 5-6: nearest-anchor assignment and projection [Pith, "What carries the
+# argument": gamma_i = <x_i, x_a>/||x_a||^2, x^_i = gamma_i x_a + r~_i; nearest
+# anchor by cosine similarity]; [Velox, "Evidence" (anchors reconstruct with
+# coefficient 1 and zero residual; projection + residual is exact)].
+# --------------------------------------------------------------------------
+def cosine_table(X, anchors_x):
+    """c[t, a] = <x_t, x_a> / (||x_t|| ||x_a||), 0 where a norm is 0."""
+    dots = X @ anchors_x.T
+    nx = np.linalg.norm(X, axis=1)
+    na = np.linalg.norm(anchors_x, axis=1)
+    den = nx[:, None] * na[None, :]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        c = np.where(den > 0, dots / np.where(den > 0, den, 1.0), 0.0)
+    return c, dots
+
+
+def assign(X, anchor_pos, idx_override=None):
+    """Per token: anchor index a(t), float64 gamma, fp16 gamma, residual r.
+
+    Non-anchor tokens take the highest signed cosine (reading R11), lowest
+    anchor index on ties.  Anchor tokens are forced onto themselves with
+    gamma = 1 and r = 0 (reading R10).  gamma = 0 when ||x_a|| = 0.
+    r = x - gamma * x_a uses the unrounded gamma (reading R13); the stored
+    coefficient is fp16(gamma), ties to even (reading R12).
+    idx_override: an externally chosen assignment to continue from (used by
+    the parity tests after they have checked it is within the tie margin).
+    Returns dict(idx, gamma, gamma16, r, margin) where margin is the relative
+    gap (c1 - c2)/|c1| between the best and second-best cosine.
+    """
+    N, D = X.shape
+    A = anchor_pos.size
+    ax = X[anchor_pos]
+    c, dots = cosine_table(X, ax)
+    idx = np.argmax(c, axis=1)            # first maximum = lowest index
+    if A > 1:
+        part = np.sort(c, axis=1)
+        c1, c2 = part[:, -1], part[:, -2]
+        with np.errstate(invalid="ignore", divide="ignore"):
+            margin = np.where(np.abs(c1) > 0, (c1 - c2) / np.abs(np.where(c1 == 0, 1, c1)), 0.0)
+    else:
+        margin = np.full(N, np.inf)
+    is_anchor = np.full(N, -1, dtype=np.int64)
+    is_anchor[anchor_pos] = np.arange(A)
+    if idx_override is not None:
+        idx = np.asarray(idx_override, dtype=np.int64).copy()
+    idx = np.where(is_anchor >= 0, is_anchor, idx)
+    margin = np.where(is_anchor >= 0, np.inf, margin)
+    xa = ax[idx]
+    na2 = (xa * xa).sum(axis=1)
+    d = (X * xa).sum(axis=1)
+    gamma = np.where(na2 > 0, d / np.where(na2 > 0, na2, 1.0), 0.0)
+    gamma = np.where(is_anchor >= 0, 1.0, gamma)
+    r = X - gamma[:, None] * xa
+    r[is_anchor >= 0] = 0.0
+    return dict(idx=idx, gamma=gamma, gamma16=fp16_rne(gamma), r=r, margin=margin,
+                is_anchor=is_anchor >= 0)
+
+
+# --------------------------------------------------------------------------
+# Step 7: first-order attention-output error utility [Pith, "What carries the
+# argument" (key-induced and value-induced channels), "Assumptions & free
+# parameters" (first-order softmax expansion, d alpha_t/d s_u =
+# alpha_t (delta_tu - alpha_u); incoherence model making it additive)].
+# Key channel p * |<q, dk>| / sqrt(D) * ||v - o||, value channel p * ||dv||,
+# summed over the observation queries; dk, dv = the residuals a token would
+# lose without a residual slot (reading R15).
+# --------------------------------------------------------------------------
+def utilities(P, O, Qh, V, rK, rV, eligible):
+    GQ, D = Qh.shape
+    qr = (Qh @ rK.T) / math.sqrt(D)                              # [GQ, N]
+    vo = np.empty_like(P)                                        # ||v_t - o_j||
+    for j in range(GQ):
+        vo[j] = np.linalg.norm(V - O[j][None, :], axis=1)
+    uK = (P * np.abs(qr) * vo).sum(axis=0)
+    uV = P.sum(axis=0) * np.linalg.norm(rV, axis=1)
+    uK = np.where(eligible, uK, -np.inf)
+    uV = np.where(eligible, uV, -np.inf)
+    return uK, uV
+
+
+# --------------------------------------------------------------------------
+# Steps 8-9: residual allocation under the byte budget [Pith, "What carries the
+# argument" (residuals where reconstruction error most changes the output);
+# Figure 11 (budget share per KV head); Velox, "Evidence" (budget pooled across
+# heads)].  Greedy by utility, which is optimal for equal-cost additive items.
+# --------------------------------------------------------------------------
+def allocate(u, R):
+    """u: [H, N] with -inf for ineligible items.  Returns a bool mask [H, N] of
+    the R items with the largest u, ties to the lower head, then the lower
+    position (reading R16)."""
+    H, N = u.shape
+    flat = u.reshape(-1)
+    hh = np.repeat(np.arange(H), N)
+    tt = np.tile(np.arange(N), H)
+    order = np.lexsort((tt, hh, -flat))
+    order = order[np.isfinite(flat[order])][:R]
+    mask = np.zeros(H * N, dtype=bool)
+    mask[order] = True
+    return mask.reshape(H, N)
+
+
+def cut_value(u, R):
+    """The R-th largest eligible utility (the selection threshold), or None."""
+    flat = u.reshape(-1)
+    flat = flat[np.isfinite(flat)]
+    if R == 0 or flat.size == 0:
+        return None
+    return np.sort(flat)[::-1][min(R, flat.size) - 1]
+
+
+# --------------------------------------------------------------------------
+# Step 10: 2-bit group-affine residual codec (implementation contract: one fp16
+# scale and one fp16 zero per 32-element group; reading R14 for the details).
+# --------------------------------------------------------------------------
+def quantize(r):
+    """r: [..., D].  Per group of 32 contiguous coordinates:
+    zero = fp16(min), scale = fp16((max - min)/3),
+    code = clamp(round_half_even((r - zero)/scale), 0, 3), code = 0 if scale = 0.
+    Returns (codes uint8 [..., D], scale [..., D/32], zero [..., D/32]) with
+    scale and zero as float64 values of the fp16 numbers."""
+    sh = r.shape
+    D = sh[-1]
+    g = r.reshape(sh[:-1] + (D // GROUP, GROUP))
+    lo = g.min(axis=-1)
+    hi = g.max(axis=-1)
+    zero = fp16_rne(lo)
+    scale = fp16_rne((hi - lo) / 3.0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = np.rint((g - zero[..., None]) / np.where(scale > 0, scale, 1.0)[..., None])
+    q = np.clip(q, 0, 3)
+    q = np.where((scale > 0)[..., None], q, 0)
+    return q.reshape(sh).astype(np.uint8), scale, zero
+
+
+def dequantize(codes, scale, zero):
+    sh = codes.shape
+    D = sh[-1]
+    g = codes.reshape(sh[:-1] + (D // GROUP, GROUP)).astype(np.float64)
+    return (zero[..., None] + scale[..., None] * g).reshape(sh)
+
+
+def code_margin(r, scale, zero):
+    """Distance of (r - zero)/scale from the nearest rounding boundary (x.5);
+    +inf where scale = 0.  Used to skip boundary cases in parity checks."""
+    sh = r.shape
+    D = sh[-1]
+    g = r.reshape(sh[:-1] + (D // GROUP, GROUP))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        y = (g - zero[..., None]) / np.where(scale > 0, scale, 1.0)[..., None]
+    f = np.abs((y - np.floor(y)) - 0.5)
+    f = np.where((scale > 0)[..., None], f, np.inf)
+    return f.reshape(sh)
+
+
+# --------------------------------------------------------------------------
+# The whole compression pass of one unit [Pith, "What carries the argument";
+# Velox, "Adaptation notes" (one-shot compression at the end of prefill)].
+# --------------------------------------------------------------------------
+@dataclass
+class Compressed:
+    plan: Plan
+    G: int
+    anchor_pos: np.ndarray        # [H, A] int
+    idx: np.ndarray               # [2, H, N] anchor index per side (0 = K, 1 = V)
+    gamma: np.ndarray             # [2, H, N] float64 (unrounded)
+    gamma16: np.ndarray           # [2, H, N] float64 value of the fp16 coefficient
+    resid: np.ndarray             # [2, H, N, D] float64 residual (unquantised)
+    flag: np.ndarray              # [2, H, N] bool: residual stored
+    codes: np.ndarray             # [2, H, N, D] uint8 (valid where flag)
+    scale: np.ndarray             # [2, H, N, D/32]
+    zero: np.ndarray              # [2, H, N, D/32]
+    anchors: np.ndarray           # [2, H, A, D] exact anchor vectors
+    score: np.ndarray             # [H, N]
+    pooled: np.ndarray            # [H, N - W]
+    P: list = field(repr=False, default=None)   # per head [GQ, N]
+    O: np.ndarray = None          # [H, GQ, D]
+    u: np.ndarray = None          # [2, H, N] utilities (-inf ineligible)
+    margin: np.ndarray = None     # [2, H, N] top-2 cosine margin
+
+
+def compress_unit(K, V, Q, G, n_obs, theta, W, e,
+                  anchor_override=None, idx_override=None, flag_override=None):
+    """K, V: [H, N, D] float64; Q: [H*G, n_obs, D] float64.
+
+    The *_override arguments let a parity test continue from decisions the GPU
+    took where the oracle's own decision was within the stated tie margin:
+    anchor_override [H, A] positions, idx_override [2, H, N], flag_override
+    [2, H, N] bool.  The test checks the overrides before passing them.
+    """
+    H, N, D = K.shape
+    p = plan(H, N, D, e, theta, W)
+    A = p.A
+    GQ = G * n_obs
+    anchor_pos = np.zeros((H, A), dtype=np.int64)
+    idx = np.zeros((2, H, N), dtype=np.int64)
+    gamma = np.zeros((2, H, N))
+    gamma16 = np.zeros((2, H, N))
+    resid = np.zeros((2, H, N, D))
+    margin = np.zeros((2, H, N))
+    eligible = np.zeros((H, N), dtype=bool)
+    score = np.zeros((H, N))
+    pooled = np.zeros((H, N - W))
+    u = np.zeros((2, H, N))
+    Ps, Os = [], np.zeros((H, GQ, D))
+    for h in range(H):
+        Qh = Q[h * G:(h + 1) * G].reshape(GQ, D)
+        P, O = obs_attention(Qh, K[h], V[h], n_obs)
+        Ps.append(P)
+        Os[h] = O
+        score[h], pooled[h] = anchor_score(P, W)
+        pos = select_anchors(pooled[h], N, W, p.k_s, p.k_u)
+        if anchor_override is not None:
+            pos = np.sort(np.asarray(anchor_override[h], dtype=np.int64))
+        anchor_pos[h] = pos
+        for s, X in enumerate((K[h], V[h])):
+            io = None if idx_override is None else idx_override[s, h]
+            a = assign(X, pos, io)
+            idx[s, h], gamma[s, h], gamma16[s, h] = a["idx"], a["gamma"], a["gamma16"]
+            resid[s, h], margin[s, h] = a["r"], a["margin"]
+            eligible[h] = ~a["is_anchor"]
+        u[0, h], u[1, h] = utilities(P, O, Qh, V[h], resid[0, h], resid[1, h], eligible[h])
+    flag = np.zeros((2, H, N), dtype=bool)
+    for s, R in enumerate((p.R_K, p.R_V)):
+        flag[s] = allocate(u[s], R)
+    if flag_override is not None:
+        flag = np.asarray(flag_override, dtype=bool).copy()
+    codes, sc, ze = quantize(resid)
+    codes = np.where(flag[..., None], codes, 0).astype(np.uint8)
+    anchors = np.stack([K[np.arange(H)[:, None], anchor_pos], V[np.arange(H)[:, None], anchor_pos]])
+    return Compressed(p, G, anchor_pos, idx, gamma, gamma16, resid, flag, codes, sc, ze,
+                      anchors, score, pooled, Ps, Os, u, margin)
+
+
+def reconstruct(c: Compressed):
+    """K^, V^ [H, N, D]: fp16(gamma) * x_a + [flag] * dequantised residual
+    [Pith, "What carries the argument"]."""
+    out = []
+    H = c.anchor_pos.shape[0]
+    for s in range(2):
+        xa = c.anchors[s][np.arange(H)[:, None], c.idx[s]]
+        rt = dequantize(c.codes[s], c.scale[s], c.zero[s])
+        out.append(c.gamma16[s][..., None] * xa + np.where(c.flag[s][..., None], rt, 0.0))
+    return out[0], out[1]
+
+
+def attention(q, K, V):
+    """softmax(q K^T / sqrt(D)) V for q [M, D], K, V [N, D]; no mask."""
+    D = q.shape[-1]
+    s = (q @ K.T) / math.sqrt(D)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    return (p @ V) / p.sum(axis=-1, keepdims=True)
+
+
+def decode_unit(c: Compressed, q):
+    """Decode attention over the compressed cache of one unit.
+    q: [H*G, D] float64; q-head h*G + g reads KV head h.  Returns o [H*G, D]."""
+    Kh, Vh = reconstruct(c)
+    H = Kh.shape[0]
+    G = c.G
+    o = np.zeros_like(q)
+    for h in range(H):
+        o[h * G:(h + 1) * G] = attention(q[h * G:(h + 1) * G], Kh[h], Vh[h])
+    return o
+
+
+# --------------------------------------------------------------------------
+# Theorem 1 output-error bound [Pith, "What carries the argument" and
+# "Referee Report" (E_K = 2 V_max tanh(mu), mu = ||q|| Delta_K / sqrt(D),
+# Delta_K = max_t ||K_t - K^_t||)] (reading R20 for the exact form).
+# --------------------------------------------------------------------------
+def theorem1_terms(q, K, V, Kh, Vh):
+    """Returns (||y - y^||, value term, key term, mirror value term, mirror key term)
+    for one query: value term = sum_t a^_t ||V_t - V^_t|| (a^ from K^), key term =
+    2 max_t ||V_t|| tanh(mu); the mirror form uses a (from K) and max ||V^_t||."""
+    D = q.size
+    y = attention(q[None], K, V)[0]
+    yh = attention(q[None], Kh, Vh)[0]
+    s = (Kh @ q) / math.sqrt(D)
+    ah = np.exp(s - s.max()); ah /= ah.sum()
+    s0 = (K @ q) / math.sqrt(D)
+    a0 = np.exp(s0 - s0.max()); a0 /= a0.sum()
+    dv = np.linalg.norm(V - Vh, axis=1)
+    dK = np.linalg.norm(K - Kh, axis=1).max()
+    mu = np.linalg.norm(q) * dK / math.sqrt(D)
+    return (np.linalg.norm(y - yh), float(ah @ dv), 2 * np.linalg.norm(V, axis=1).max() * math.tanh(mu),
+            float(a0 @ dv), 2 * np.linalg.norm(Vh, axis=1).max() * math.tanh(mu))

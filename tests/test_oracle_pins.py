@@ -1,0 +1,405 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks an oracle function against something other than itself: a
+library routine, a closed form, a hand-worked golden fixture, brute force on
+tiny inputs, finite differences, or an invariant stated on the pages.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import anchorkv_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def clustered(r, H, N, D, ndir=8, noise=0.3):
+    dirs = r.standard_normal((H, ndir, D))
+    dirs /= np.linalg.norm(dirs, axis=-1, keepdims=True)
+    cl = r.integers(0, ndir, (H, N))
+    X = dirs[np.arange(H)[:, None], cl] + noise / math.sqrt(D) * r.standard_normal((H, N, D))
+    return X * np.exp(0.5 * r.standard_normal((H, N)))[..., None]
+
+
+def bf16_exact(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- rounding
+def _fp16_bruteforce(x):
+    allv = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float64)
+    bits = np.arange(65536, dtype=np.uint16)
+    ok = np.isfinite(allv)
+    allv, bits = allv[ok], bits[ok]
+    out = []
+    for v in x:
+        d = np.abs(allv - v)
+        best = d.min()
+        cand = np.nonzero(d == best)[0]
+        if cand.size > 1:   # tie: even mantissa (lowest bit 0)
+            cand = [c for c in cand if bits[c] & 1 == 0] or list(cand)
+        out.append(allv[cand[0]])
+    return np.array(out)
+
+
+def test_fp16_rne_matches_bruteforce():
+    r = rng(1)
+    x = np.concatenate([r.standard_normal(300) * 10.0 ** r.integers(-7, 5, 300),
+                        np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2049.0, 2051.0, -0.5 - 2 ** -12, 6.1e-5, 1e-8])])
+    x = x[np.abs(x) < 65504]
+    np.testing.assert_array_equal(O.fp16_rne(x), _fp16_bruteforce(x))
+    assert O.fp16_rne(np.array([1e6, -1e6])).tolist() == [65504.0, -65504.0]
+
+
+# ---------------------------------------------------------------- byte plan
+def test_plan_matches_hand_worked_counts():
+    cases = json.load(open(os.path.join(GOLD, "plan_workloads.json")))["cases"]
+    for c in cases:
+        p = O.plan(c["H"], c["N"], c["D"], c["e"], c["theta"], c["W"])
+        assert (p.A, p.k_s, p.k_u, p.R_K, p.R_V) == (c["A"], c["k_s"], c["k_u"], c["R"], c["R"]), c["name"]
+
+
+@pytest.mark.parametrize("H,N,D,e,theta,W", [
+    (8, 8192, 128, 2, 0.1, 32), (1, 512, 128, 4, 0.1, 32), (3, 5000, 64, 2, 0.07, 16),
+    (2, 300, 32, 2, 0.9, 8), (4, 2048, 128, 2, 2.0, 32), (8, 65536, 128, 2, 0.02, 64)])
+def test_plan_byte_invariant_and_tightness(H, N, D, e, theta, W):
+    """Per side, the bytes used stay within theta*H*N*D*e and no further
+    residual would fit unless every eligible token already has one."""
+    p = O.plan(H, N, D, e, theta, W)
+    rec = D // 4 + D // 8
+    used = O.side_bytes(p, p.R_K)
+    assert used <= float(np.float32(theta)) * H * N * D * e
+    assert p.R_K == H * (N - p.A) or used + rec > p.budget_unit
+    assert p.A - W == p.k_s + p.k_u and p.A <= N
+
+
+def test_plan_budget_errors():
+    with pytest.raises(ValueError):
+        O.plan(8, 1024, 128, 2, 0.01, 32)     # window + pointers exceed the budget
+    with pytest.raises(ValueError):
+        O.plan(1, 100, 100, 2, 0.1, 8)        # D not a multiple of 32
+
+
+def test_plan_residual_floor_at_short_context():
+    """Velox, "The one setting worth tuning": at short contexts and small theta
+    the anchors and their pointers use (nearly) the whole budget, leaving very
+    few or zero residual slots.  When the anchor count is capped by the budget,
+    what is left per head is less than one more anchor, so R < H*(D*e+2)/rec."""
+    for N, theta in [(256, 0.15), (512, 0.08), (300, 0.2)]:
+        p = O.plan(8, N, 128, 2, theta, 32)
+        if p.A - 32 < N // 128:
+            assert p.R_K < 8 * (128 * 2 + 2) / 48
+    assert O.plan(8, 256, 128, 2, 0.15, 32).R_K <= 2
+    assert O.plan(1, 256, 128, 2, 0.144, 32).R_K == 0
+
+
+# ---------------------------------------------------------------- obs attention
+def test_obs_attention_matches_sdpa_with_offset_causal_mask():
+    r = rng(2)
+    G, n_obs, N, D = 3, 5, 40, 32
+    Q = r.standard_normal((G * n_obs, D))
+    K = r.standard_normal((N, D))
+    V = r.standard_normal((N, D))
+    P, Oo = O.obs_attention(Q, K, V, n_obs)
+    j = np.arange(G * n_obs) % n_obs
+    mask = torch.from_numpy(np.arange(N)[None, :] <= (N - n_obs + j)[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None], attn_mask=mask[None])
+    np.testing.assert_allclose(Oo, ref[0].numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(P.sum(1), 1.0, rtol=1e-13)
+    assert np.all(P[~mask.numpy()] == 0)
+
+
+# ---------------------------------------------------------------- score & anchors
+def test_pooling_is_zero_padded_window_sum():
+    r = rng(3)
+    P = r.random((6, 50))
+    score, pooled = O.anchor_score(P, 10)
+    np.testing.assert_allclose(score, P.sum(0), rtol=1e-15)
+    ref = np.convolve(score[:40], np.ones(7), mode="same")
+    np.testing.assert_allclose(pooled, ref, rtol=1e-13)
+
+
+def _bruteforce_anchors(pooled, N, W, k_s, k_u):
+    L = N - W
+    scored = [t for t in range(L)
+              if sum(1 for u in range(L) if pooled[u] > pooled[t] or (pooled[u] == pooled[t] and u < t)) < k_s]
+    rest = [t for t in range(L) if t not in scored]
+    M = len(rest)
+    # pick i = the candidate at the midpoint of the i-th of k_u equal strata
+    uni = [rest[math.floor(Fraction(2 * i + 1, 2) * Fraction(M, k_u))] for i in range(k_u)]
+    return sorted(scored + uni + list(range(L, N)))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_anchors_bruteforce(seed):
+    r = rng(10 + seed)
+    N, W = int(r.integers(20, 60)), int(r.integers(1, 8))
+    pooled = r.integers(0, 6, N - W).astype(float)   # many ties
+    k_s, k_u = int(r.integers(0, 6)), int(r.integers(1, 6))
+    pos = O.select_anchors(pooled, N, W, k_s, k_u)
+    assert pos.tolist() == _bruteforce_anchors(pooled, N, W, k_s, k_u)
+    assert len(set(pos.tolist())) == W + k_s + k_u
+    assert set(range(N - W, N)) <= set(pos.tolist())
+
+
+# ---------------------------------------------------------------- assignment & projection
+def test_projection_hand_worked_example():
+    g = json.load(open(os.path.join(GOLD, "projection_example.json")))
+    D = 32
+    pad = lambda v: np.array(list(v) + [0] * (D - len(v)), dtype=float)
+    X = np.stack([pad(a) for a in g["anchors"]] + [pad(t["x"]) for t in g["tokens"]])
+    res = O.assign(X, np.arange(3))
+    for i, t in enumerate(g["tokens"]):
+        k = 3 + i
+        assert res["idx"][k] == t["idx"]
+        assert res["gamma"][k] == pytest.approx(t["gamma"], abs=1e-15)
+        np.testing.assert_allclose(res["r"][k], pad(t["r"]), atol=1e-15)
+        c, _ = O.cosine_table(X[k:k + 1], X[:3])
+        assert c[0, t["idx"]] == pytest.approx(t["cos"], abs=1e-15)
+    # anchors reconstruct exactly with coefficient 1 and zero residual (Velox, "Evidence")
+    assert res["idx"][:3].tolist() == [0, 1, 2] and np.all(res["gamma"][:3] == 1) and np.all(res["r"][:3] == 0)
+
+
+def test_assign_bruteforce_and_projection_identities():
+    r = rng(4)
+    N, D, A = 120, 32, 9
+    X = bf16_exact(clustered(r, 1, N, D, ndir=4)[0])
+    X[7] = 0.0                                       # zero token: cosine 0 everywhere -> index 0
+    pos = np.sort(r.choice(N, A, replace=False))
+    res = O.assign(X, pos)
+    for t in range(N):
+        if t in pos:
+            continue
+        cs = []
+        for a in range(A):
+            xa = X[pos[a]]
+            num = math.fsum(float(u) * float(v) for u, v in zip(X[t], xa))
+            den = math.sqrt(math.fsum(float(u) ** 2 for u in X[t])) * math.sqrt(math.fsum(float(v) ** 2 for v in xa))
+            cs.append(num / den if den > 0 else 0.0)
+        best = max(range(A), key=lambda a: (cs[a], -a))
+        if res["margin"][t] > 1e-12:
+            assert res["idx"][t] == best, t
+        xa = X[pos[res["idx"][t]]]
+        rr = res["r"][t]
+        # orthogonal decomposition (Velox "Evidence"; Pith "What carries the argument")
+        np.testing.assert_allclose(res["gamma"][t] * xa + rr, X[t], atol=1e-12)
+        assert abs(rr @ xa) <= 1e-12 * (np.linalg.norm(X[t]) * np.linalg.norm(xa) + 1e-300)
+        # relative residual norm sqrt(1 - c^2) (Pith "Referee Report", minor 5)
+        c = cs[res["idx"][t]]
+        assert np.linalg.norm(rr) == pytest.approx(np.linalg.norm(X[t]) * math.sqrt(max(0.0, 1 - c * c)), abs=1e-10)
+    assert res["idx"][7] == 0 and res["gamma"][7] == 0
+
+
+# ---------------------------------------------------------------- utility (finite differences)
+def _attn(q, K, V):
+    s = K @ q / math.sqrt(q.size)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    return p @ V
+
+
+def test_utility_equals_first_order_output_change():
+    """Key channel: moving k_t by eps*r changes logit t by eps<q,r>/sqrt(D), and by
+    d alpha_t/d s_u = alpha_t(delta_tu - alpha_u) the output moves by
+    eps * alpha_t <q,r>/sqrt(D) (v_t - o) to first order.  Value channel:
+    y changes by exactly alpha_t * dv.  Summed norms over the observation
+    queries must equal the oracle's utilities (Pith, "Assumptions & free
+    parameters")."""
+    r = rng(5)
+    N, D, GQ = 24, 32, 4
+    K = r.standard_normal((N, D))
+    V = r.standard_normal((N, D))
+    Q = r.standard_normal((GQ, D))
+    rK = r.standard_normal((N, D)) * 0.3
+    rV = r.standard_normal((N, D)) * 0.3
+    P, Oo = O.obs_attention(Q, K, V, n_obs=1)   # every row sits at N-1: all keys visible
+    uK, uV = O.utilities(P, Oo, Q, V, rK, rV, np.ones(N, bool))
+    eps = 1e-6
+    for t in range(N):
+        fdK = fdV = 0.0
+        for j in range(GQ):
+            Kp, Km = K.copy(), K.copy()
+            Kp[t] += eps * rK[t]
+            Km[t] -= eps * rK[t]
+            fdK += np.linalg.norm((_attn(Q[j], Kp, V) - _attn(Q[j], Km, V)) / (2 * eps))
+            Vp = V.copy()
+            Vp[t] += rV[t]
+            fdV += np.linalg.norm(_attn(Q[j], K, Vp) - _attn(Q[j], K, V))
+        assert uK[t] == pytest.approx(fdK, rel=1e-6)
+        assert uV[t] == pytest.approx(fdV, rel=1e-10)
+
+
+# ---------------------------------------------------------------- allocation
+def test_allocation_is_optimal_subset_bruteforce():
+    r = rng(6)
+    H, N, R = 2, 6, 4
+    u = r.random((H, N))
+    u[0, 2] = -np.inf                        # an anchor: ineligible
+    mask = O.allocate(u, R)
+    items = [(h, t) for h in range(H) for t in range(N) if np.isfinite(u[h, t])]
+    best = max(itertools.combinations(items, R), key=lambda s: sum(u[h, t] for h, t in s))
+    assert sorted(zip(*np.nonzero(mask))) == sorted(best)
+
+
+def test_allocation_ties_lower_head_then_position():
+    u = np.ones((3, 4))
+    mask = O.allocate(u, 5)
+    assert [tuple(x) for x in np.argwhere(mask)] == [(0, 0), (0, 1), (0, 2), (0, 3), (1, 0)]
+
+
+def test_allocation_pools_across_heads():
+    """Velox, "Evidence": the budget favours the head with higher utility
+    instead of splitting evenly."""
+    r = rng(7)
+    u = r.random((2, 100))
+    u[1] *= 10
+    mask = O.allocate(u, 60)
+    assert mask[1].sum() > mask[0].sum()
+    assert mask.sum() == 60
+
+
+# ---------------------------------------------------------------- codec
+def test_codec_nearest_level_bruteforce():
+    r = rng(8)
+    x = r.standard_normal((50, 64)) * np.exp(r.standard_normal((50, 1)))
+    codes, sc, ze = O.quantize(x)
+    margin = O.code_margin(x, sc, ze)
+    for i in range(50):
+        for d in range(64):
+            g = d // 32
+            levels = [ze[i, g] + sc[i, g] * c for c in range(4)]
+            dist = [abs(x[i, d] - L) for L in levels]
+            best = min(range(4), key=lambda c: (dist[c], c % 2, c))
+            if margin[i, d] > 1e-9:
+                assert codes[i, d] == best
+    rt = O.dequantize(codes, sc, ze)
+    # inside the covered range the error is at most half a step
+    inside = (x >= np.repeat(ze, 32, 1)) & (x <= np.repeat(ze + 3 * sc, 32, 1))
+    assert np.all(np.abs(x - rt)[inside] <= np.repeat(sc, 32, 1)[inside] / 2 * (1 + 1e-12))
+    # and the grid spans the group up to the fp16 rounding of zero and scale
+    assert np.all(np.abs(x - rt) <= np.repeat(sc, 32, 1) / 2 + 2 ** -10 * np.repeat(np.abs(ze) + 3 * sc, 32, 1))
+
+
+def test_codec_reduces_error_in_aggregate():
+    """Velox, "Evidence": the quantised residual is closer than storing nothing.
+    For this codec it holds in aggregate, not per vector (30 zeros and +-1 give
+    error^2 3.33 against ||r||^2 = 2)."""
+    r = rng(9)
+    x = r.standard_normal((500, 128))
+    codes, sc, ze = O.quantize(x)
+    assert (np.linalg.norm(x - O.dequantize(codes, sc, ze)) ** 2) < 0.2 * (np.linalg.norm(x) ** 2)
+    v = np.zeros((1, 32))
+    v[0, 0], v[0, 1] = 1.0, -1.0
+    c, s, z = O.quantize(v)
+    assert np.sum((v - O.dequantize(c, s, z)) ** 2) > np.sum(v ** 2)
+
+
+def test_codec_zero_scale_group():
+    x = np.full((1, 32), 0.25)
+    c, s, z = O.quantize(x)
+    assert s[0, 0] == 0 and np.all(c == 0) and np.all(O.dequantize(c, s, z) == 0.25)
+
+
+# ---------------------------------------------------------------- whole pass, decode, Theorem 1
+def small_unit(seed, H=2, G=2, N=600, D=64, n_obs=8, W=8):
+    r = rng(seed)
+    K = bf16_exact(clustered(r, H, N, D))
+    V = bf16_exact(r.standard_normal((H, N, D)))
+    Q = bf16_exact(r.standard_normal((H * G, n_obs, D)))
+    return K, V, Q
+
+
+def test_compress_invariants_and_determinism():
+    K, V, Q = small_unit(11)
+    c = O.compress_unit(K, V, Q, 2, 8, 0.1, 8, 2)
+    c2 = O.compress_unit(K, V, Q, 2, 8, 0.1, 8, 2)
+    p = c.plan
+    for a, b in [(c.anchor_pos, c2.anchor_pos), (c.idx, c2.idx), (c.flag, c2.flag), (c.codes, c2.codes)]:
+        np.testing.assert_array_equal(a, b)
+    H, N = 2, 600
+    # no token dropped: every position keeps a pointer into [0, A) (Velox, "Evidence")
+    assert c.idx.shape == (2, H, N) and c.idx.min() >= 0 and c.idx.max() < p.A
+    # window always kept exactly (Pith, "Assumptions & free parameters")
+    for h in range(H):
+        assert set(range(N - 8, N)) <= set(c.anchor_pos[h].tolist())
+    assert c.flag[0].sum() == p.R_K and c.flag[1].sum() == p.R_V
+    assert not np.any(c.flag[:, np.arange(H)[:, None], c.anchor_pos])
+    # residuals are given to the highest utilities
+    for s in range(2):
+        cut = O.cut_value(c.u[s], p.R_K)
+        assert np.all(c.u[s][c.flag[s]] >= cut) and np.all(c.u[s][~c.flag[s]] <= cut)
+    # residual orthogonal to its anchor before quantisation
+    for s, X in enumerate((K, V)):
+        for h in range(H):
+            xa = c.anchors[s, h][c.idx[s, h]]
+            dots = (c.resid[s, h] * xa).sum(1)
+            assert np.all(np.abs(dots) <= 1e-11 * (np.linalg.norm(X[h], axis=1) * np.linalg.norm(xa, axis=1) + 1e-300))
+    assert O.side_bytes(p, p.R_K) <= 0.1 * H * N * 64 * 2
+
+
+def test_decode_matches_sdpa_over_reconstruction():
+    K, V, Q = small_unit(12)
+    c = O.compress_unit(K, V, Q, 2, 8, 0.1, 8, 2)
+    q = bf16_exact(rng(13).standard_normal((4, 64)))
+    o = O.decode_unit(c, q)
+    Kh, Vh = O.reconstruct(c)
+    for h in range(2):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[h * 2:(h + 1) * 2])[None], torch.from_numpy(Kh[h])[None], torch.from_numpy(Vh[h])[None])
+        np.testing.assert_allclose(o[h * 2:(h + 1) * 2], ref[0].numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_all_anchor_cache_is_exact_attention():
+    """With W = N every token is an anchor stored exactly, so decode equals
+    plain attention over K, V."""
+    r = rng(14)
+    H, G, N, D = 2, 2, 64, 32
+    K = bf16_exact(r.standard_normal((H, N, D)))
+    V = bf16_exact(r.standard_normal((H, N, D)))
+    Q = bf16_exact(r.standard_normal((H * G, 4, D)))
+    c = O.compress_unit(K, V, Q, G, 4, 1.5, N, 2)
+    assert c.plan.A == N and c.flag.sum() == 0
+    q = bf16_exact(r.standard_normal((H * G, D)))
+    o = O.decode_unit(c, q)
+    for h in range(H):
+        np.testing.assert_allclose(o[h * G:(h + 1) * G], O.attention(q[h * G:(h + 1) * G], K[h], V[h]), rtol=1e-12)
+
+
+def test_theorem1_bound_holds():
+    """Pith, "What carries the argument": ||y - y^|| <= attention-weighted
+    value error + 2 V_max tanh(||q|| Delta_K / sqrt(D)); both the a^- and
+    the a-weighted forms, on compressed caches and on random reconstructions."""
+    K, V, Q = small_unit(15)
+    c = O.compress_unit(K, V, Q, 2, 8, 0.1, 8, 2)
+    Kh, Vh = O.reconstruct(c)
+    r = rng(16)
+    cases = [(K[h], V[h], Kh[h], Vh[h]) for h in range(2)]
+    for _ in range(40):
+        N, D = 30, 32
+        Kx, Vx = r.standard_normal((N, D)), r.standard_normal((N, D))
+        cases.append((Kx, Vx, Kx + r.standard_normal((N, D)) * r.random(), Vx + r.standard_normal((N, D)) * r.random()))
+    for Kx, Vx, Khx, Vhx in cases:
+        for _ in range(5):
+            q = r.standard_normal(Kx.shape[1]) * 3
+            err, val, key, val2, key2 = O.theorem1_terms(q, Kx, Vx, Khx, Vhx)
+            tol = 1e-12 * (1 + np.linalg.norm(Vx))
+            assert err <= val + key + tol
+            assert err <= val2 + key2 + tol
+
+
+def test_worked_example_density_cross_check():
+    """Pith, "Referee Report": 91,056 residuals in the worked example and 17.3 %
+    residual density at 20x; consistent with one 8-head layer at S = 32768 with
+    two sides (the example's own byte costs are not printed)."""
+    assert 91056 / (8 * 32768 * 2) == pytest.approx(0.173, abs=1e-3)
