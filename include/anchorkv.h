@@ -1,0 +1,197 @@
+/*
+ * anchorkv.h - C ABI of the anchor-residual KV-cache hot path (AnchorKV) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (web pages: "Pith review of AnchorKV: Anchor-Residual KV Cache
+ * Compression", section "What carries the argument"; "AnchorKV-adapted -
+ * Anchor-Residual Compression, No Eviction", sections "The problem this
+ * solves" and "Adaptation notes") keeps a few anchor vectors per KV head
+ * exactly and stores every other token as (anchor index a, coefficient gamma,
+ * optional 2-bit residual), x^ = gamma * x_a + r~.  It runs once at the end of
+ * prefill (compress) and decode attention then reads the compressed cache
+ * directly (decode_attn).
+ *
+ * Conventions (all entry points):
+ *  - Return 0 on success or a negative ANCHORKV_E_* code; anchorkv_last_error()
+ *    then gives a message (thread-local, valid until the next call on the
+ *    same thread).  Errors are found synchronously (argument checks, launch
+ *    errors); a device fault surfaces at the caller's next synchronisation.
+ *  - Device buffers are allocated and owned by the caller.  The library never
+ *    allocates or frees device memory and never synchronises: everything is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *  - A "unit" is one layer of one sequence: H KV heads of N tokens.  Units are
+ *    independent; the residual budget is pooled over the H heads of a unit.
+ *  - Supported: head_dim == 128, dtype bf16 or f32, 1 <= window <= n_tokens,
+ *    1 <= n_obs <= n_tokens, anchors per head <= 32767.
+ *  - Inputs must be finite, with |x| small enough that residual scales and
+ *    zeros fit fp16 (|x| < 1e4 is ample).
+ */
+#ifndef ANCHORKV_H
+#define ANCHORKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ANCHORKV_OK = 0,
+  ANCHORKV_E_ARG = -1,          /* null pointer or invalid argument */
+  ANCHORKV_E_DTYPE = -2,        /* unsupported dtype */
+  ANCHORKV_E_SHAPE = -3,        /* unsupported shape */
+  ANCHORKV_E_BUDGET = -4,       /* theta too small for the window anchors and the pointers */
+  ANCHORKV_E_SMALL_BUFFER = -5, /* cache / workspace / output buffer too small */
+  ANCHORKV_E_HIP = -6,          /* a HIP launch or runtime call failed */
+  ANCHORKV_E_LAYOUT = -7        /* a cache header that does not describe a valid cache */
+};
+
+typedef enum { ANCHORKV_BF16 = 1, ANCHORKV_F32 = 2 } anchorkv_dtype;
+
+/* Shapes.  K and V are [units][kv_heads][n_tokens][head_dim]; the observation
+ * queries are [units][kv_heads*q_per_kv][n_obs][head_dim] (q-head h*q_per_kv+g
+ * belongs to KV head h); decode queries are [units][kv_heads*q_per_kv][head_dim]. */
+typedef struct {
+  int32_t units;
+  int32_t kv_heads;
+  int32_t q_per_kv;
+  int32_t n_tokens;
+  int32_t head_dim;
+  int32_t n_obs;
+  int32_t dtype; /* anchorkv_dtype */
+} anchorkv_dims;
+
+/* Everything the host needs about a compressed cache: counts, byte accounting
+ * and the per-unit layout.  Filled by anchorkv_plan or anchorkv_plan_from_header. */
+typedef struct {
+  /* shape and knobs */
+  int32_t units, H, G, N, D, n_obs, dtype, elem_bytes, window;
+  float theta;
+  /* counts per head / per unit (Pith review, "Assumptions & free parameters":
+   * k = S/128 non-window anchors, rho = 0.7 scored, window W) */
+  int32_t A;          /* anchors per head = window + k_scored + k_uniform */
+  int32_t k_scored;   /* anchors picked by the pooled observation-window score */
+  int32_t k_uniform;  /* anchors picked uniformly over the remaining positions */
+  int32_t R_K, R_V;   /* residual slots per unit for keys / values */
+  int32_t n_chunks;   /* ceil(N / 1024): residual-offset chunks per head */
+  /* byte accounting per side per unit (anchors D*e, pointers 4, residual D/4+D/8) */
+  int64_t budget_bytes_per_side; /* floor(theta * H * N * D * e) */
+  int64_t used_bytes_k, used_bytes_v;
+  double compression_ratio;      /* 2*H*N*D*e / unit_bytes */
+  /* per-unit cache layout: byte offsets from the start of a unit */
+  int64_t off_anchor_k, off_anchor_v; /* [H][A][D] input dtype, stored exactly */
+  int64_t off_res_k, off_res_v;       /* [R][48] residual records, sorted by (head, position) */
+  int64_t off_words;                  /* [H][N][2] uint32: K word, V word per token */
+  int64_t off_chunk_k, off_chunk_v;   /* [H][n_chunks] int32: first record of each 1024-token chunk */
+  int64_t off_positions;              /* [H][A] int32 anchor positions, ascending */
+  int64_t unit_bytes;                 /* bytes of one unit's content */
+  int64_t unit_stride;                /* unit_bytes rounded up to 16 */
+  int64_t cache_bytes;                /* units * unit_stride */
+  /* device scratch the caller provides */
+  int64_t compress_workspace_bytes;
+  int64_t decode_workspace_bytes;
+  int32_t decode_splits;              /* token splits per (unit, head) in decode */
+  int32_t reserved[7];
+} anchorkv_plan_info;
+
+/* Pointer word (uint32, one per token per side): bits 0-14 anchor index,
+ * bit 15 set when the token has a residual record, bits 16-31 fp16 gamma.
+ * Residual record (48 bytes): 16 little-endian uint16 code words, then 4 x
+ * (fp16 scale, fp16 zero) for the 32-coordinate groups.  Code word j holds the
+ * 2-bit codes of coordinates j + 16c (c = 0..7) in bits 2c..2c+1; group g is
+ * coordinates 32g..32g+31; the value is zero_g + scale_g * code. */
+
+/* Library version string. */
+const char* anchorkv_version(void);
+
+/* Message for the last non-zero return on this thread. */
+const char* anchorkv_last_error(void);
+
+/* Counts, byte accounting and layout for (dims, theta, window).  Host only, no
+ * HIP calls.  Budget (per KV head and side) B = theta*N*D*e bytes with theta
+ * taken at float32 precision; anchors A = window + min(N/128, A_max - window,
+ * N - window) where A_max is the number of exact anchors the budget pays for
+ * after pointers, chunk offsets and header; residual slots per side per unit
+ * R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed)/(D/4+D/8))).
+ * (Pith review, "What carries the argument" and "Assumptions & free
+ * parameters"; AnchorKV-adapted page, "The one setting worth tuning".)
+ * Errors: E_ARG (null), E_DTYPE, E_SHAPE, E_BUDGET. */
+int anchorkv_plan(const anchorkv_dims* dims, float theta, int32_t window, anchorkv_plan_info* out);
+
+/* Rebuild the plan from a host copy of a unit's first 256 bytes (the header
+ * compress writes at the start of every unit).  Errors: E_ARG, E_LAYOUT. */
+int anchorkv_plan_from_header(const void* header_host, int32_t units, anchorkv_plan_info* out);
+
+/* End-of-prefill compression of all units (Pith review, "What carries the
+ * argument"; AnchorKV-adapted page, "Adaptation notes": one pass, no
+ * calibration).  Per unit and KV head: causal observation-window attention of
+ * the n_obs last queries, pooled score (width 7), anchors = window + top
+ * scored + uniform picks; per side, nearest anchor by cosine (lowest index on
+ * ties, anchors map to themselves), gamma = <x, x_a>/||x_a||^2 stored fp16,
+ * residual r = x - gamma x_a; first-order output-error utilities (key channel
+ * p |<q, r_K>|/sqrt(D) ||v - o||, value channel p ||r_V||, summed over the
+ * observation queries); the R_K / R_V largest utilities per unit get a 2-bit
+ * residual record (ties: lower head, then lower position).
+ *  K, V:    device, [units][H][N][D], dtype of the plan.
+ *  Q_obs:   device, [units][H*G][n_obs][D]; query j of a q-head sits at
+ *           position N - n_obs + j (causal).
+ *  cache:   device, >= plan->cache_bytes, written completely.
+ *  workspace: device, >= plan->compress_workspace_bytes; its contents after
+ *           the call hold the intermediate arrays (see anchorkv_workspace_offsets).
+ * The result is bitwise deterministic for given inputs.
+ * Errors: E_ARG, E_SMALL_BUFFER, E_HIP. */
+int anchorkv_compress(const anchorkv_plan_info* plan, const void* K, const void* V, const void* Q_obs,
+                      void* cache, size_t cache_bytes, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Offsets (bytes from the workspace start) of compress intermediates, for
+ * inspection in tests: [0] score f32 [U][H][N]; [1] m,1/l float2 [U][H][GQp];
+ * [2] o f32 [U][H][GQp][D]; [3] utilities f32 [U][2][H][N] (-1 for anchors);
+ * [4] unrounded gamma f32 [U][2][H][N]; [5] residual norm^2 f32 [U][2][H][N];
+ * [6] anchor index int32 [U][2][H][N].  GQp = H*... padded query count
+ * returned in out[7].  Returns 0 or E_ARG. */
+int anchorkv_workspace_offsets(const anchorkv_plan_info* plan, int64_t out[8]);
+
+/* Decode attention over the compressed cache, one query per q-head per unit
+ * (Pith review, "What carries the argument": logits gamma*<q, k_a> + <q, r~>,
+ * values reconstructed the same way; softmax over all N compressed tokens,
+ * no mask).  The dense cache is never materialised.
+ *  cache:  device, as written by anchorkv_compress (or packed on the host).
+ *  q:      device, [units][H*G][D], cache dtype.
+ *  o:      device, [units][H*G][D] float32.
+ *  workspace: device, >= plan->decode_workspace_bytes.
+ * Errors: E_ARG, E_SMALL_BUFFER, E_HIP. */
+int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, const void* q, float* o,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-side view of one unit's compressed representation, as plain arrays.
+ * All pointers are host memory owned by the caller. */
+typedef struct {
+  int32_t* positions;  /* [H][A] anchor positions, ascending */
+  void* anchors_k;     /* [H][A][D] cache dtype */
+  void* anchors_v;     /* [H][A][D] */
+  int32_t* idx;        /* [2][H][N] anchor index (side 0 = K, 1 = V) */
+  uint16_t* gamma16;   /* [2][H][N] fp16 bits of gamma */
+  uint8_t* flag;       /* [2][H][N] 1 if the token has a residual */
+  uint8_t* codes;      /* [2][H][N][D] 2-bit codes (0..3); read/written only where flag */
+  uint16_t* scale16;   /* [2][H][N][D/32] fp16 bits; only where flag */
+  uint16_t* zero16;    /* [2][H][N][D/32] fp16 bits; only where flag */
+} anchorkv_unit_arrays;
+
+/* Write one unit (plan->unit_bytes bytes, header included) into host memory
+ * `unit_out` from plain arrays: the reference packer used by the tests and by
+ * tools that build a cache outside compress.  Residual records are laid out
+ * in (head, position) order; counts must equal plan->R_K / R_V.
+ * Errors: E_ARG, E_LAYOUT (flag counts differ from the plan, index >= A). */
+int anchorkv_unit_pack_host(const anchorkv_plan_info* plan, const anchorkv_unit_arrays* in, void* unit_out);
+
+/* Inverse of anchorkv_unit_pack_host: decode one unit's bytes (host copy) into
+ * plain arrays.  Errors: E_ARG, E_LAYOUT (bad header or inconsistent records). */
+int anchorkv_unit_unpack_host(const anchorkv_plan_info* plan, const void* unit_in, anchorkv_unit_arrays* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ANCHORKV_H */

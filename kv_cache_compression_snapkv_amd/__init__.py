@@ -1,0 +1,12 @@
+"""AnchorKV anchor-residual KV-cache hot path on AMD MI355X (gfx950).
+
+compress: end-of-prefill compression of K/V into anchors + (index, gamma)
+pointers + 2-bit residual records; decode_attn: attention over the compressed
+cache without reconstructing it.  Both run in hand-written HIP kernels behind
+the C ABI in include/anchorkv.h; this package only marshals arguments.
+"""
+from .binding import (BF16, F32, AnchorKVError, PlanInfo, alloc, compress, decode_attn, lib, pack_unit, plan,
+                      plan_from_header, unpack_unit, version, workspace_offsets)
+
+__all__ = ["BF16", "F32", "AnchorKVError", "PlanInfo", "alloc", "compress", "decode_attn", "lib", "pack_unit", "plan",
+           "plan_from_header", "unpack_unit", "version", "workspace_offsets"]

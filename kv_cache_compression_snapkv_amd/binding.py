@@ -1,0 +1,201 @@
+"""ctypes binding of libanchorkv.so (the C ABI in include/anchorkv.h).
+
+Argument marshalling only: device buffers are torch tensors (for allocation
+and streams); every step of the compress and decode paths runs in the HIP
+library.  There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libanchorkv.so")
+
+BF16, F32 = 1, 2
+
+ERRORS = {-1: "E_ARG", -2: "E_DTYPE", -3: "E_SHAPE", -4: "E_BUDGET", -5: "E_SMALL_BUFFER", -6: "E_HIP", -7: "E_LAYOUT"}
+
+
+class AnchorKVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Dims(ct.Structure):
+    _fields_ = [("units", ct.c_int32), ("kv_heads", ct.c_int32), ("q_per_kv", ct.c_int32), ("n_tokens", ct.c_int32),
+                ("head_dim", ct.c_int32), ("n_obs", ct.c_int32), ("dtype", ct.c_int32)]
+
+
+class PlanInfo(ct.Structure):
+    _fields_ = [
+        ("units", ct.c_int32), ("H", ct.c_int32), ("G", ct.c_int32), ("N", ct.c_int32), ("D", ct.c_int32),
+        ("n_obs", ct.c_int32), ("dtype", ct.c_int32), ("elem_bytes", ct.c_int32), ("window", ct.c_int32),
+        ("theta", ct.c_float),
+        ("A", ct.c_int32), ("k_scored", ct.c_int32), ("k_uniform", ct.c_int32), ("R_K", ct.c_int32),
+        ("R_V", ct.c_int32), ("n_chunks", ct.c_int32),
+        ("budget_bytes_per_side", ct.c_int64), ("used_bytes_k", ct.c_int64), ("used_bytes_v", ct.c_int64),
+        ("compression_ratio", ct.c_double),
+        ("off_anchor_k", ct.c_int64), ("off_anchor_v", ct.c_int64), ("off_res_k", ct.c_int64),
+        ("off_res_v", ct.c_int64), ("off_words", ct.c_int64), ("off_chunk_k", ct.c_int64),
+        ("off_chunk_v", ct.c_int64), ("off_positions", ct.c_int64),
+        ("unit_bytes", ct.c_int64), ("unit_stride", ct.c_int64), ("cache_bytes", ct.c_int64),
+        ("compress_workspace_bytes", ct.c_int64), ("decode_workspace_bytes", ct.c_int64),
+        ("decode_splits", ct.c_int32), ("reserved", ct.c_int32 * 7),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+class UnitArrays(ct.Structure):
+    _fields_ = [("positions", ct.c_void_p), ("anchors_k", ct.c_void_p), ("anchors_v", ct.c_void_p),
+                ("idx", ct.c_void_p), ("gamma16", ct.c_void_p), ("flag", ct.c_void_p), ("codes", ct.c_void_p),
+                ("scale16", ct.c_void_p), ("zero16", ct.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(f"{LIB_PATH} is missing: build it with "
+                                    "`python -m kv_cache_compression_snapkv_amd.build`")
+        L = ct.CDLL(LIB_PATH)
+        L.anchorkv_version.restype = ct.c_char_p
+        L.anchorkv_last_error.restype = ct.c_char_p
+        L.anchorkv_plan.argtypes = [ct.POINTER(Dims), ct.c_float, ct.c_int32, ct.POINTER(PlanInfo)]
+        L.anchorkv_plan_from_header.argtypes = [ct.c_void_p, ct.c_int32, ct.POINTER(PlanInfo)]
+        L.anchorkv_compress.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                        ct.c_size_t, ct.c_void_p, ct.c_size_t, ct.c_void_p]
+        L.anchorkv_workspace_offsets.argtypes = [ct.POINTER(PlanInfo), ct.POINTER(ct.c_int64)]
+        L.anchorkv_decode_attn.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                           ct.c_size_t, ct.c_void_p]
+        L.anchorkv_unit_pack_host.argtypes = [ct.POINTER(PlanInfo), ct.POINTER(UnitArrays), ct.c_void_p]
+        L.anchorkv_unit_unpack_host.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.POINTER(UnitArrays)]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ["anchorkv_version", "anchorkv_last_error", "anchorkv_plan", "anchorkv_plan_from_header",
+            "anchorkv_compress", "anchorkv_workspace_offsets", "anchorkv_decode_attn", "anchorkv_unit_pack_host",
+            "anchorkv_unit_unpack_host"]
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise AnchorKVError(rc, lib().anchorkv_last_error().decode())
+
+
+def version() -> str:
+    return lib().anchorkv_version().decode()
+
+
+def plan(units, kv_heads, q_per_kv, n_tokens, head_dim, n_obs, dtype, theta, window) -> PlanInfo:
+    d = Dims(units, kv_heads, q_per_kv, n_tokens, head_dim, n_obs, dtype)
+    p = PlanInfo()
+    _check(lib().anchorkv_plan(ct.byref(d), ct.c_float(theta), window, ct.byref(p)))
+    return p
+
+
+def plan_from_header(header: bytes, units: int) -> PlanInfo:
+    p = PlanInfo()
+    buf = ct.create_string_buffer(bytes(header[:256]), 256)
+    _check(lib().anchorkv_plan_from_header(buf, units, ct.byref(p)))
+    return p
+
+
+def workspace_offsets(p: PlanInfo) -> dict:
+    out = (ct.c_int64 * 8)()
+    _check(lib().anchorkv_workspace_offsets(ct.byref(p), out))
+    keys = ["score", "ml", "o", "util", "gamma", "rn2", "aidx", "GQp"]
+    return dict(zip(keys, list(out)))
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def compress(p: PlanInfo, K, V, Q, cache, workspace, stream=None):
+    """Enqueue the compression of all units (torch CUDA tensors, contiguous)."""
+    for t in (K, V, Q, cache, workspace):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("compress: inputs must be contiguous device tensors")
+    _check(lib().anchorkv_compress(ct.byref(p), _ptr(K), _ptr(V), _ptr(Q), _ptr(cache), _nbytes(cache),
+                                   _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def decode_attn(p: PlanInfo, cache, q, o, workspace, stream=None):
+    """Enqueue decode attention: q [U, H*G, D] cache dtype -> o [U, H*G, D] float32."""
+    for t in (cache, q, o, workspace):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("decode_attn: inputs must be contiguous device tensors")
+    _check(lib().anchorkv_decode_attn(ct.byref(p), _ptr(cache), _ptr(q), _ptr(o), _ptr(workspace),
+                                      _nbytes(workspace), _stream(stream)))
+
+
+def alloc(p: PlanInfo, device):
+    """Cache, compress workspace and decode workspace as uint8 device tensors."""
+    import torch
+    cache = torch.empty(int(p.cache_bytes), dtype=torch.uint8, device=device)
+    ws = torch.empty(int(p.compress_workspace_bytes), dtype=torch.uint8, device=device)
+    dws = torch.empty(int(p.decode_workspace_bytes), dtype=torch.uint8, device=device)
+    return cache, ws, dws
+
+
+# ---------------------------------------------------------------- host packer
+def _unit_arrays(p: PlanInfo):
+    H, N, D, A = p.H, p.N, p.D, p.A
+    adt = np.uint16 if p.dtype == BF16 else np.float32
+    arr = dict(
+        positions=np.zeros((H, A), np.int32),
+        anchors_k=np.zeros((H, A, D), adt), anchors_v=np.zeros((H, A, D), adt),
+        idx=np.zeros((2, H, N), np.int32), gamma16=np.zeros((2, H, N), np.uint16),
+        flag=np.zeros((2, H, N), np.uint8), codes=np.zeros((2, H, N, D), np.uint8),
+        scale16=np.zeros((2, H, N, D // 32), np.uint16), zero16=np.zeros((2, H, N, D // 32), np.uint16))
+    return arr
+
+
+def _struct(arr) -> UnitArrays:
+    s = UnitArrays()
+    for k in arr:
+        a = arr[k]
+        assert a.flags["C_CONTIGUOUS"]
+        setattr(s, k, a.ctypes.data)
+    return s
+
+
+def pack_unit(p: PlanInfo, arrays: dict) -> bytes:
+    """Pack one unit from host numpy arrays (see anchorkv_unit_arrays)."""
+    base = _unit_arrays(p)
+    for k in base:
+        base[k] = np.ascontiguousarray(arrays[k], dtype=base[k].dtype).reshape(base[k].shape)
+    out = ct.create_string_buffer(int(p.unit_bytes))
+    _check(lib().anchorkv_unit_pack_host(ct.byref(p), ct.byref(_struct(base)), out))
+    return out.raw
+
+
+def unpack_unit(p: PlanInfo, unit: bytes) -> dict:
+    """Decode one unit's bytes into host numpy arrays."""
+    arr = _unit_arrays(p)
+    buf = ct.create_string_buffer(bytes(unit[:int(p.unit_bytes)]), int(p.unit_bytes))
+    _check(lib().anchorkv_unit_unpack_host(ct.byref(p), buf, ct.byref(_struct(arr))))
+    return arr

@@ -1,0 +1,725 @@
+// End-of-prefill compression pass (gfx950).
+//
+// Launch sequence per call (all units at once, one stream, no host sync):
+//   headers -> obs STATS -> ml combine -> obs SCORE -> o combine ->
+//   anchor selection (+ anchor copy, norms) -> nearest-anchor assignment per
+//   side (MFMA similarity, fused argmax and projection) -> obs UTIL ->
+//   top-R radix select (3 digit passes) -> counts -> chunk scan -> flags +
+//   record order -> quantise + pack.
+// Sources: Pith review of AnchorKV ("What carries the argument",
+// "Assumptions & free parameters"); AnchorKV-adapted page ("Evidence",
+// "Adaptation notes").
+#include "obs_kernels.hpp"
+
+namespace akv {
+
+#define AKV_CHECK_LAUNCH(name)                                                              \
+  do {                                                                                      \
+    hipError_t e_ = hipGetLastError();                                                      \
+    if (e_ != hipSuccess) return fail(ANCHORKV_E_HIP, "%s: %s", name, hipGetErrorString(e_)); \
+  } while (0)
+
+// Fill kernel (used instead of a memset so the sequence stays capture-safe).
+__global__ void k_zero_u32(unsigned* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// ------------------------------------------------------------------ headers
+__global__ void k_headers(UnitHeader hd, uint8_t* cache, int64_t stride) {
+  const int u = blockIdx.x;
+  const int i = threadIdx.x;  // 64 threads x 4 bytes
+  uint32_t v;
+  if (i == (int)(offsetof(UnitHeader, unit_index) / 4)) v = (uint32_t)u;
+  else v = reinterpret_cast<const uint32_t*>(&hd)[i];
+  reinterpret_cast<uint32_t*>(cache + (int64_t)u * stride)[i] = v;
+}
+
+// ------------------------------------------------------------ stats combines
+// m (log2 domain) and l over key splits -> (m, 1/l); deterministic order.
+__global__ void k_ml_combine(const float2* part, float2* ml, int S1, int GQp, int GQ, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int q = (int)(i % GQp);
+  const int64_t uh = i / GQp;
+  if (q >= GQ) { ml[i] = make_float2(0.0f, 0.0f); return; }
+  float m = -INFINITY;
+  for (int s = 0; s < S1; ++s) m = fmaxf(m, part[(uh * S1 + s) * GQp + q].x);
+  float l = 0.0f;
+  for (int s = 0; s < S1; ++s) {
+    float2 v = part[(uh * S1 + s) * GQp + q];
+    if (v.x > -INFINITY) l += v.y * exp2_fast(v.x - m);
+  }
+  ml[i] = make_float2(m, 1.0f / l);
+}
+
+// o = sum of split partials (fixed order), its bf16 hi/lo split and ||o||^2.
+// One 128-thread block per (unit, head, query).
+__global__ void k_o_combine(const float* part, float* o, uint16_t* ohl, float* oo, int S1, int GQp) {
+  const int64_t row = blockIdx.x;   // (uh, q)
+  const int q = (int)(row % GQp);
+  const int64_t uh = row / GQp;
+  const int d = threadIdx.x;
+  float v = 0.0f;
+  for (int s = 0; s < S1; ++s) v += part[((uh * S1 + s) * GQp + q) * kHeadDim + d];
+  o[row * kHeadDim + d] = v;
+  const uint16_t hi = f2bf(v);
+  const uint16_t lo = f2bf(v - bf2f(hi));
+  ohl[((uh * 2 + 0) * GQp + q) * kHeadDim + d] = hi;
+  ohl[((uh * 2 + 1) * GQp + q) * kHeadDim + d] = lo;
+  __shared__ float red[2];
+  float sq = wave_sum(v * v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
+  __syncthreads();
+  if (threadIdx.x == 0) oo[row] = red[0] + red[1];
+}
+
+// -------------------------------------------------------------- block scans
+// Exclusive scan of one int per thread over a 1024-thread block; returns the
+// exclusive prefix and writes the total to *total.
+__device__ int block_excl_scan(int v, int* sh /*[32]*/, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < nw; ++w) { int t = sh[w]; sh[w] = acc; acc += t; }
+    sh[31] = acc;
+  }
+  __syncthreads();
+  const int r = sh[wave] + x - v;
+  *total = sh[31];
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------- anchor selection
+// One 1024-thread block per (unit, head).  score -> pooled (width 7 window
+// sum over non-window positions) -> top k_s (radix select on the f32 bits,
+// ties to the lower position) -> k_u stratified picks over the remaining
+// positions (pick i = remaining[floor((2i+1) M / (2 k_u))]) -> + window ->
+// positions ascending, anchor_of map, anchor copies, norms.
+template <int DT>
+__global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv, const float* score, float* pooled,
+                                                 uint8_t* cache, int64_t stride, int64_t off_ak, int64_t off_av,
+                                                 int64_t off_pos, int* anchor_of, float2* anorm, int H, int N, int W,
+                                                 int k_s, int k_u, int A) {
+  using T = typename Elem<DT>::T;
+  constexpr int D = kHeadDim;
+  __shared__ unsigned hist[kHistBins];
+  __shared__ int sh[32];
+  __shared__ unsigned s_prefix, s_need;
+  __shared__ int s_pos[4096];  // scored + uniform positions (A <= 4096 is checked on the host)
+  const int h = blockIdx.x % H;
+  const int u = blockIdx.x / H;
+  const int64_t uh = (int64_t)u * H + h;
+  const int L = N - W;
+  const float* sc = score + uh * N;
+  float* pl = pooled + uh * N;
+  const int tid = threadIdx.x, nt = blockDim.x;
+
+  for (int t = tid; t < L; t += nt) {
+    float v = 0.0f;
+    const int lo = max(0, t - 3), hi = min(L - 1, t + 3);
+    for (int x = lo; x <= hi; ++x) v += sc[x];
+    pl[t] = v;
+  }
+  __syncthreads();
+
+  // radix select of the k_s-th largest key (keys = f32 bits of non-negative values)
+  unsigned prefix = 0, need = (unsigned)k_s;
+  if (k_s > 0) {
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int p = 0; p < 3; ++p) {
+      for (int b = tid; b < kHistBins; b += nt) hist[b] = 0;
+      __syncthreads();
+      const unsigned hmask = p == 0 ? 0u : (0xFFFFFFFFu << (shifts[p] + widths[p]));
+      for (int t = tid; t < L; t += nt) {
+        const unsigned key = __float_as_uint(pl[t]);
+        if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shifts[p]) & ((1u << widths[p]) - 1)], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned cum = 0;
+        int b = (1 << widths[p]) - 1;
+        for (; b > 0; --b) {
+          if (cum + hist[b] >= need) break;
+          cum += hist[b];
+        }
+        s_prefix = prefix | ((unsigned)b << shifts[p]);
+        s_need = need - cum;
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      need = s_need;
+      __syncthreads();
+    }
+  }
+  const unsigned T_key = prefix;
+  // ordered compaction of the scored set: contiguous position ranges per thread
+  const int per = (L + nt - 1) / nt;
+  const int a0 = tid * per, a1 = min(L, a0 + per);
+  int ng = 0, nti = 0;
+  if (k_s > 0)
+    for (int t = a0; t < a1; ++t) {
+      const unsigned key = __float_as_uint(pl[t]);
+      ng += key > T_key;
+      nti += key == T_key;
+    }
+  int tot;
+  const int tie_pre = block_excl_scan(nti, sh, &tot);
+  // selected in this range: all greater + ties while tie rank < need
+  int take_ties = k_s > 0 ? max(0, min(nti, (int)need - tie_pre)) : 0;
+  const int sel_pre = block_excl_scan(k_s > 0 ? ng + take_ties : 0, sh, &tot);
+  if (k_s > 0) {
+    int o = sel_pre, tr = tie_pre;
+    for (int t = a0; t < a1; ++t) {
+      const unsigned key = __float_as_uint(pl[t]);
+      bool sel = key > T_key;
+      if (key == T_key) { sel = tr < (int)need; ++tr; }
+      if (sel) s_pos[o++] = t;
+    }
+  }
+  __syncthreads();
+  // uniform picks: the c-th remaining position is c + j, j = first index with scored[j] - j > c
+  const int M = L - k_s;
+  for (int i = tid; i < k_u; i += nt) {
+    const int64_t c = ((2ll * i + 1) * M) / (2ll * k_u);
+    int lo = 0, hi = k_s;  // first j in [0, k_s] with (j == k_s) or scored[j] - j > c
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)s_pos[mid] - mid > c) hi = mid; else lo = mid + 1;
+    }
+    s_pos[k_s + i] = (int)(c + lo);
+  }
+  __syncthreads();
+  // merge scored (sorted) and uniform (sorted) into anchor order, then the window
+  int* pos_out = reinterpret_cast<int*>(cache + (int64_t)u * stride + off_pos) + (int64_t)h * A;
+  for (int i = tid; i < k_s + k_u; i += nt) {
+    const int v = s_pos[i];
+    int rank;
+    if (i < k_s) {  // count uniform picks below v
+      int lo = 0, hi = k_u;
+      while (lo < hi) { int mid = (lo + hi) >> 1; if (s_pos[k_s + mid] < v) lo = mid + 1; else hi = mid; }
+      rank = i + lo;
+    } else {
+      int lo = 0, hi = k_s;
+      while (lo < hi) { int mid = (lo + hi) >> 1; if (s_pos[mid] < v) lo = mid + 1; else hi = mid; }
+      rank = (i - k_s) + lo;
+    }
+    pos_out[rank] = v;
+  }
+  for (int i = tid; i < W; i += nt) pos_out[k_s + k_u + i] = L + i;
+  int* ao = anchor_of + uh * N;
+  for (int t = tid; t < N; t += nt) ao[t] = -1;
+  __syncthreads();  // global writes of pos_out visible to the block
+  __threadfence_block();
+  for (int i = tid; i < A; i += nt) ao[pos_out[i]] = i;
+  // copy anchor rows and their norms (one wave per anchor)
+  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  const T* Kp = reinterpret_cast<const T*>(Kv) + uh * N * D;
+  const T* Vp = reinterpret_cast<const T*>(Vv) + uh * N * D;
+  T* AK = reinterpret_cast<T*>(cache + (int64_t)u * stride + off_ak) + (int64_t)h * A * D;
+  T* AV = reinterpret_cast<T*>(cache + (int64_t)u * stride + off_av) + (int64_t)h * A * D;
+  for (int i = wave; i < A; i += nw) {
+    const int t = pos_out[i];
+    float sk = 0.0f, sv = 0.0f;
+    for (int d = lane; d < D; d += 64) {
+      const T xk = Kp[(int64_t)t * D + d], xv = Vp[(int64_t)t * D + d];
+      AK[(int64_t)i * D + d] = xk;
+      AV[(int64_t)i * D + d] = xv;
+      const float fk = Elem<DT>::f(xk), fv = Elem<DT>::f(xv);
+      sk = fmaf(fk, fk, sk);
+      sv = fmaf(fv, fv, sv);
+    }
+    sk = wave_sum(sk);
+    sv = wave_sum(sv);
+    if (lane == 0) {
+      anorm[((int64_t)u * 2 * H + h) * A + i] = make_float2(sk, sk > 0.0f ? 1.0f / sqrtf(sk) : 0.0f);
+      anorm[((int64_t)u * 2 * H + H + h) * A + i] = make_float2(sv, sv > 0.0f ? 1.0f / sqrtf(sv) : 0.0f);
+    }
+  }
+}
+
+// ------------------------------------------------- nearest-anchor assignment
+// One 256-thread block per (unit, side, head, 256-token tile); each wave owns
+// 64 tokens (4 MFMA row blocks) held in registers.  Anchors are staged through
+// LDS in chunks; the MFMA tile c[t][a] = <x_t, x_a> is scaled by 1/||x_a|| in
+// f32 and a per-lane running argmax keeps the lowest anchor index on ties.
+// Then gamma = <x_t, x_a>/||x_a||^2 and ||x_t - gamma x_a||^2 in f32, anchor
+// tokens forced onto themselves (gamma 1, residual 0); the pointer word
+// (index | fp16 gamma << 16) is written to the cache.
+template <int DT> struct AssignCfg {
+  static constexpr int AC = DT == ANCHORKV_BF16 ? 256 : 128;   // anchors per LDS chunk
+  static constexpr int PAD = DT == ANCHORKV_BF16 ? 8 : 4;
+  static constexpr int LDA = kHeadDim + PAD;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_assign(const void* Kv, const void* Vv, uint8_t* cache, int64_t stride,
+                                               int64_t off_ak, int64_t off_av, int64_t off_words,
+                                               const float2* anorm, const int* anchor_of, int* aidx, float* gam,
+                                               float* rn2, int H, int N, int A, int ntiles) {
+  using T = typename Elem<DT>::T;
+  using M = Mfma<DT>;
+  using frag = typename M::frag;
+  using Cfg = AssignCfg<DT>;
+  constexpr int D = kHeadDim, NSTEP = D / M::KSTEP, AC = Cfg::AC, LDA = Cfg::LDA;
+  __shared__ __attribute__((aligned(16))) T As[AC * LDA];
+  __shared__ float inv_s[AC];
+
+  int bid = blockIdx.x;
+  const int tile = bid % ntiles; bid /= ntiles;
+  const int h = bid % H; bid /= H;
+  const int side = bid % 2;
+  const int u = bid / 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int64_t uh = (int64_t)u * H + h;
+  const T* X = reinterpret_cast<const T*>(side ? Vv : Kv) + uh * N * D;
+  const T* AX = reinterpret_cast<const T*>(cache + (int64_t)u * stride + (side ? off_av : off_ak)) + (int64_t)h * A * D;
+  const float2* an = anorm + ((int64_t)u * 2 * H + side * H + h) * A;
+  const int tbase = tile * 256 + wave * 64;
+
+  frag xf[4][NSTEP];
+  for (int rb = 0; rb < 4; ++rb) {
+    const int t = tbase + rb * 16 + col;
+    for (int st = 0; st < NSTEP; ++st) {
+      const int kk = st * M::KSTEP + kg * M::KW;
+      xf[rb][st] = t < N ? M::load(X + (int64_t)t * D + kk) : M::zero();
+    }
+  }
+  float best[4][4];
+  int bidx[4][4];
+  for (int rb = 0; rb < 4; ++rb)
+    for (int r = 0; r < 4; ++r) { best[rb][r] = -INFINITY; bidx[rb][r] = 0; }
+
+  constexpr int EPC = 16 / sizeof(T), CPR = D / EPC;
+  for (int c0 = 0; c0 < A; c0 += AC) {
+    const int na = min(AC, A - c0);
+    for (int ch = threadIdx.x; ch < AC * CPR; ch += blockDim.x) {
+      const int r = ch / CPR, cc = ch % CPR;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < na) v = *reinterpret_cast<const uint4*>(AX + (int64_t)(c0 + r) * D + cc * EPC);
+      *reinterpret_cast<uint4*>(&As[r * LDA + cc * EPC]) = v;
+    }
+    for (int i = threadIdx.x; i < AC; i += blockDim.x) inv_s[i] = i < na ? an[c0 + i].y : __int_as_float(0x7fc00000);
+    __syncthreads();
+    const int nab = (na + 15) / 16;
+    for (int ab = 0; ab < nab; ++ab) {
+      frag bf[NSTEP];
+      for (int st = 0; st < NSTEP; ++st) bf[st] = M::load(&As[(ab * 16 + col) * LDA + st * M::KSTEP + kg * M::KW]);
+      const float inv = inv_s[ab * 16 + col];  // NaN for padding anchors: never wins
+      const int aglob = c0 + ab * 16 + col;
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4 acc = {0, 0, 0, 0};
+        for (int st = 0; st < NSTEP; ++st) acc = M::mma(xf[rb][st], bf[st], acc);
+        for (int r = 0; r < 4; ++r) {
+          const float v = acc[r] * inv;
+          if (v > best[rb][r]) { best[rb][r] = v; bidx[rb][r] = aglob; }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // argmax across the 16 anchor-column lanes; lowest index on ties
+  for (int rb = 0; rb < 4; ++rb)
+    for (int r = 0; r < 4; ++r) {
+      float b = best[rb][r];
+      int bi = bidx[rb][r];
+      for (int o = 1; o < 16; o <<= 1) {
+        const float b2 = __shfl_xor(b, o, 64);
+        const int i2 = __shfl_xor(bi, o, 64);
+        if (b2 > b || (b2 == b && i2 < bi)) { b = b2; bi = i2; }
+      }
+      bidx[rb][r] = bi;
+    }
+  // projection epilogue: lane (row col, k-slice kg) holds 32 coordinates of token row col
+  for (int rb = 0; rb < 4; ++rb) {
+    const int t = tbase + rb * 16 + col;
+    // argmax of output row `col` lives in lanes (col/4)*16.., register r = col%4
+    int cand[4];
+    for (int r = 0; r < 4; ++r) cand[r] = __shfl(bidx[rb][r], (col >> 2) * 16, 64);
+    int a = cand[col & 3];
+    const int tt = t < N ? t : N - 1;
+    const int self = anchor_of[uh * N + tt];
+    const bool is_anchor = self >= 0;
+    if (is_anchor) a = self;
+    float xs[NSTEP * M::KW], as_[NSTEP * M::KW];
+    float dot = 0.0f;
+    for (int st = 0; st < NSTEP; ++st) {
+      const int kk = st * M::KSTEP + kg * M::KW;
+      for (int e = 0; e < M::KW; ++e) {
+        xs[st * M::KW + e] = Elem<DT>::f(X[(int64_t)tt * D + kk + e]);
+        as_[st * M::KW + e] = Elem<DT>::f(AX[(int64_t)a * D + kk + e]);
+        dot = fmaf(xs[st * M::KW + e], as_[st * M::KW + e], dot);
+      }
+    }
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    const float na2 = an[a].x;
+    float g = na2 > 0.0f ? dot / na2 : 0.0f;
+    if (is_anchor) g = 1.0f;
+    float r2 = 0.0f;
+    for (int i = 0; i < NSTEP * M::KW; ++i) {
+      const float rr = fmaf(-g, as_[i], xs[i]);
+      r2 = fmaf(rr, rr, r2);
+    }
+    r2 += __shfl_xor(r2, 16, 64);
+    r2 += __shfl_xor(r2, 32, 64);
+    if (is_anchor) r2 = 0.0f;
+    if (kg == 0 && t < N) {
+      const int64_t i = ((int64_t)u * 2 * H + side * H + h) * N + t;
+      aidx[i] = a;
+      gam[i] = g;
+      rn2[i] = r2;
+      uint32_t* words = reinterpret_cast<uint32_t*>(cache + (int64_t)u * stride + off_words);
+      words[((int64_t)h * N + t) * 2 + side] = (uint32_t)a | ((uint32_t)f2h_sat(g) << 16);
+    }
+  }
+}
+
+// ------------------------------------------------------------- top-R select
+// Per (unit, side): choose the R largest utilities over (head, token), ties to
+// the lower head then position.  Keys: f32 bits + 1 for eligible (u >= 0),
+// 0 for anchors.  Blocks are 1024-token chunks of one head, so the running
+// selected count at a chunk start is that chunk's residual offset.
+__device__ __forceinline__ unsigned util_key(float v) { return v >= 0.0f ? __float_as_uint(v) + 1u : 0u; }
+
+__global__ __launch_bounds__(256) void k_topr_hist(const float* util, unsigned* hist, const unsigned* state, int H,
+                                                   int N, int C, int R, int pass) {
+  __shared__ unsigned lh[kHistBins];
+  int bid = blockIdx.x;
+  const int c = bid % C; bid /= C;
+  const int h = bid % H; bid /= H;
+  const int side = bid % 2;
+  const int u = bid / 2;
+  if (R == 0) return;
+  const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+  const int width = pass == 2 ? 10 : 11;
+  const unsigned* st = state + ((int64_t)u * 2 + side) * 4;
+  const unsigned prefix = pass == 0 ? 0u : st[0];
+  const unsigned hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + width));
+  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) lh[b] = 0;
+  __syncthreads();
+  const float* up = util + (((int64_t)u * 2 + side) * H + h) * N;
+  const int t1 = min(N, (c + 1) * kChunk);
+  for (int t = c * kChunk + threadIdx.x; t < t1; t += blockDim.x) {
+    const unsigned key = util_key(up[t]);
+    if (key != 0u && (key & hmask) == (prefix & hmask)) atomicAdd(&lh[(key >> shift) & ((1u << width) - 1)], 1u);
+  }
+  __syncthreads();
+  unsigned* gh = hist + ((int64_t)u * 2 + side) * kHistBins;
+  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x)
+    if (lh[b]) atomicAdd(&gh[b], lh[b]);
+}
+
+__global__ void k_topr_scan(unsigned* hist, unsigned* state, int R, int pass) {
+  const int us = blockIdx.x;
+  unsigned* st = state + (int64_t)us * 4;
+  unsigned* gh = hist + (int64_t)us * kHistBins;
+  if (threadIdx.x == 0 && R > 0) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int width = pass == 2 ? 10 : 11;
+    unsigned prefix = pass == 0 ? 0u : st[0];
+    unsigned need = pass == 0 ? (unsigned)R : st[1];
+    unsigned cum = 0;
+    int b = (1 << width) - 1;
+    for (; b > 0; --b) {
+      if (cum + gh[b] >= need) break;
+      cum += gh[b];
+    }
+    st[0] = prefix | ((unsigned)b << shift);
+    st[1] = need - cum;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) gh[b] = 0;  // ready for the next pass
+}
+
+__global__ __launch_bounds__(256) void k_topr_count(const float* util, const unsigned* state, unsigned* blk, int H,
+                                                    int N, int C, int R) {
+  __shared__ unsigned red[2][4];
+  int bid = blockIdx.x;
+  const int c = bid % C; bid /= C;
+  const int h = bid % H; bid /= H;
+  const int side = bid % 2;
+  const int u = bid / 2;
+  const unsigned T_key = state[((int64_t)u * 2 + side) * 4 + 0];
+  unsigned g = 0, ti = 0;
+  if (R > 0) {
+    const float* up = util + (((int64_t)u * 2 + side) * H + h) * N;
+    const int t1 = min(N, (c + 1) * kChunk);
+    for (int t = c * kChunk + threadIdx.x; t < t1; t += blockDim.x) {
+      const unsigned key = util_key(up[t]);
+      g += key > T_key;
+      ti += key == T_key;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) { g += __shfl_xor(g, o, 64); ti += __shfl_xor(ti, o, 64); }
+  if ((threadIdx.x & 63) == 0) { red[0][threadIdx.x >> 6] = g; red[1][threadIdx.x >> 6] = ti; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* b = blk + ((((int64_t)u * 2 + side) * H + h) * C + c) * 4;
+    b[0] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    b[1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
+}
+
+// Exclusive scans over the H*C chunks of a (unit, side); writes the chunk
+// offsets of the cache.  One 1024-thread block per (unit, side).
+__global__ __launch_bounds__(1024) void k_topr_blockscan(unsigned* blk, const unsigned* state, uint8_t* cache,
+                                                         int64_t stride, int64_t off_ck, int64_t off_cv, int nb,
+                                                         int R) {
+  __shared__ int sh[32];
+  const int us = blockIdx.x;
+  const int u = us / 2, side = us % 2;
+  const unsigned need = R > 0 ? state[(int64_t)us * 4 + 1] : 0u;
+  unsigned* b = blk + (int64_t)us * nb * 4;
+  int* chunk = reinterpret_cast<int*>(cache + (int64_t)u * stride + (side ? off_cv : off_ck));
+  int tie_base = 0, sel_base = 0;
+  for (int b0 = 0; b0 < nb; b0 += blockDim.x) {
+    const int i = b0 + threadIdx.x;
+    const int ties = (i < nb && R > 0) ? (int)b[i * 4 + 1] : 0;
+    const int greater = (i < nb && R > 0) ? (int)b[i * 4 + 0] : 0;
+    int tot;
+    const int tp = block_excl_scan(ties, sh, &tot) + tie_base;
+    const int taken = max(0, min(ties, (int)need - tp));
+    int tot2;
+    const int sp = block_excl_scan(greater + taken, sh, &tot2) + sel_base;
+    if (i < nb) {
+      b[i * 4 + 2] = (unsigned)sp;
+      b[i * 4 + 3] = (unsigned)tp;
+      chunk[i] = sp;
+    }
+    tie_base += tot;
+    sel_base += tot2;
+  }
+}
+
+// Flags and record order: within a chunk, item order is position order.
+__global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsigned* state, const unsigned* blk,
+                                                   uint8_t* cache, int64_t stride, int64_t off_words, int* sel_list,
+                                                   int Rmax, int H, int N, int C, int R) {
+  __shared__ int sh[32];
+  int bid = blockIdx.x;
+  const int c = bid % C; bid /= C;
+  const int h = bid % H; bid /= H;
+  const int side = bid % 2;
+  const int u = bid / 2;
+  if (R == 0) return;
+  const int us = u * 2 + side;
+  const unsigned T_key = state[(int64_t)us * 4 + 0];
+  const int need = (int)state[(int64_t)us * 4 + 1];
+  const unsigned* b = blk + (((int64_t)us * H + h) * C + c) * 4;
+  const int sel_base = (int)b[2], tie_base = (int)b[3];
+  const float* up = util + ((int64_t)us * H + h) * N;
+  const int t0 = c * kChunk + threadIdx.x * 4;
+  unsigned key[4];
+  int nti = 0;
+  for (int k = 0; k < 4; ++k) {
+    const int t = t0 + k;
+    key[k] = t < N && t < (c + 1) * kChunk ? util_key(up[t]) : 0u;
+    nti += key[k] == T_key && key[k] != 0u;
+  }
+  int tot;
+  int tr = block_excl_scan(nti, sh, &tot) + tie_base;
+  bool sel[4];
+  int ns = 0;
+  for (int k = 0; k < 4; ++k) {
+    sel[k] = key[k] != 0u && key[k] > T_key;
+    if (key[k] != 0u && key[k] == T_key) { sel[k] = tr < need; ++tr; }
+    ns += sel[k];
+  }
+  int o = block_excl_scan(ns, sh, &tot) + sel_base;
+  uint32_t* words = reinterpret_cast<uint32_t*>(cache + (int64_t)u * stride + off_words);
+  for (int k = 0; k < 4; ++k) {
+    if (!sel[k]) continue;
+    const int t = t0 + k;
+    if (o >= R) break;  // never more than R records (guards the list bounds)
+    words[((int64_t)h * N + t) * 2 + side] |= 0x8000u;
+    sel_list[(int64_t)us * Rmax + o] = h * N + t;
+    ++o;
+  }
+}
+
+// ------------------------------------------------------------ quantise+pack
+// 16 lanes per residual record; lane j owns coordinates 8j..8j+7 (group j/4).
+// r = x - gamma x_a in f32 with the unrounded gamma; per 32-group: zero =
+// fp16(min), scale = fp16((max-min)/3), code = clamp(rne((r-zero)/scale),0,3).
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, uint8_t* cache, int64_t stride,
+                                              int64_t off_ak, int64_t off_av, int64_t off_rk, int64_t off_rv,
+                                              const int* sel_list, int Rmax, const int* aidx, const float* gam, int H,
+                                              int N, int A, int R, int nblk) {
+  using T = typename Elem<DT>::T;
+  constexpr int D = kHeadDim;
+  __shared__ uint8_t codes_s[16][128];
+  int bid = blockIdx.x;
+  const int blk = bid % nblk; bid /= nblk;
+  const int side = bid % 2;
+  const int u = bid / 2;
+  const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int rec = blk * 16 + grp;
+  const bool active = rec < R;
+  const int us = u * 2 + side;
+  int flat = active ? sel_list[(int64_t)us * Rmax + rec] : 0;
+  const int h = flat / N, t = flat % N;
+  const int64_t iw = ((int64_t)us * H + h) * N + t;
+  const int a = active ? aidx[iw] : 0;
+  const float g = active ? gam[iw] : 0.0f;
+  const T* X = reinterpret_cast<const T*>(side ? Vv : Kv) + (((int64_t)u * H + h) * N + t) * D;
+  const T* AX = reinterpret_cast<const T*>(cache + (int64_t)u * stride + (side ? off_av : off_ak)) + ((int64_t)h * A + a) * D;
+  float r[8];
+  float mn = INFINITY, mx = -INFINITY;
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * j + e;
+    r[e] = active ? fmaf(-g, Elem<DT>::f(AX[d]), Elem<DT>::f(X[d])) : 0.0f;
+    mn = fminf(mn, r[e]);
+    mx = fmaxf(mx, r[e]);
+  }
+  mn = fminf(mn, __shfl_xor(mn, 1, 64)); mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+  mn = fminf(mn, __shfl_xor(mn, 2, 64)); mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+  const uint16_t zb = f2h_sat(mn), sb = f2h_sat((mx - mn) / 3.0f);
+  const float z = h2f(zb), sc = h2f(sb);
+  for (int e = 0; e < 8; ++e) {
+    int code = 0;
+    if (sc > 0.0f) code = (int)fminf(3.0f, fmaxf(0.0f, rintf((r[e] - z) / sc)));
+    codes_s[grp][8 * j + e] = (uint8_t)code;
+  }
+  __syncthreads();
+  if (!active) return;
+  uint16_t w = 0;
+  for (int cc = 0; cc < 8; ++cc) w |= (uint16_t)(codes_s[grp][j + 16 * cc] << (2 * cc));
+  uint8_t* recp = cache + (int64_t)u * stride + (side ? off_rv : off_rk) + (int64_t)rec * kRecBytes;
+  reinterpret_cast<uint16_t*>(recp)[j] = w;
+  // group g's (scale, zero) lives in lanes 4g..4g+3; lane 4g writes it
+  if ((j & 3) == 0) reinterpret_cast<uint32_t*>(recp + 32)[j >> 2] = (uint32_t)sb | ((uint32_t)zb << 16);
+}
+
+// ------------------------------------------------------------ launch sequence
+template <int DT, int MODE>
+static int launch_obs(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t st) {
+  const int QB = a.GQp / 16;
+  int qpw = QB <= 8 ? 1 : 2;
+  if (DT == ANCHORKV_F32 && QB > 8) return fail(ANCHORKV_E_SHAPE, "f32 path supports q_per_kv*n_obs <= 128");
+  if (QB > 16) return fail(ANCHORKV_E_SHAPE, "q_per_kv*n_obs must be <= 256");
+  const int nw = (QB + qpw - 1) / qpw;
+  const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1)), block(64 * nw);
+  if (qpw == 1) k_obs<DT, MODE, 1><<<grid, block, 0, st>>>(a);
+  else if constexpr (DT == ANCHORKV_BF16) k_obs<DT, MODE, 2><<<grid, block, 0, st>>>(a);
+  AKV_CHECK_LAUNCH("k_obs");
+  return 0;
+}
+
+template <int DT>
+static int compress_impl(const anchorkv_plan_info& p, const void* K, const void* V, const void* Q, void* cache_v,
+                         void* ws_v, hipStream_t st) {
+  uint8_t* cache = reinterpret_cast<uint8_t*>(cache_v);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(ws_v);
+  const CompressWs w = compress_ws_layout(p);
+  const int U = p.units, H = p.H, N = p.N, A = p.A, C = p.n_chunks;
+  const int GQ = p.G * p.n_obs;
+  if (A > 4096) return fail(ANCHORKV_E_SHAPE, "anchors per head %d > 4096 not supported", A);
+
+  UnitHeader hd;
+  fill_header(p, &hd);
+  k_headers<<<U, 64, 0, st>>>(hd, cache, p.unit_stride);
+  AKV_CHECK_LAUNCH("k_headers");
+
+  ObsArgs a{};
+  a.K = K; a.V = V; a.Q = Q; a.cache = cache; a.stride = p.unit_stride; a.off_anchor_k = p.off_anchor_k;
+  a.ml_part = reinterpret_cast<float2*>(ws + w.ml_part);
+  a.ml = reinterpret_cast<const float2*>(ws + w.ml);
+  a.o_part = reinterpret_cast<float*>(ws + w.o_part);
+  a.ohl = reinterpret_cast<const uint16_t*>(ws + w.ohl);
+  a.ofull = reinterpret_cast<const float*>(ws + w.o);
+  a.oo = reinterpret_cast<const float*>(ws + w.oo);
+  a.score = reinterpret_cast<float*>(ws + w.score);
+  a.gam = reinterpret_cast<const float*>(ws + w.gam);
+  a.aidx = reinterpret_cast<const int*>(ws + w.aidx);
+  a.rn2 = reinterpret_cast<const float*>(ws + w.rn2);
+  a.anchor_of = reinterpret_cast<const int*>(ws + w.anchor_of);
+  a.util = reinterpret_cast<float*>(ws + w.util);
+  a.U = U; a.H = H; a.G = p.G; a.N = N; a.n_obs = p.n_obs; a.GQ = GQ; a.GQp = w.GQp; a.S1 = w.S1;
+  a.kps = (int)round_up((N + w.S1 - 1) / w.S1, 64);
+  a.A = A;
+  a.c = kLog2e / sqrtf((float)kHeadDim);
+  a.inv_sqrt_d = 1.0f / sqrtf((float)kHeadDim);
+
+  int rc;
+  if ((rc = launch_obs<DT, OBS_STATS>(p, a, st))) return rc;
+  {
+    const int64_t n = (int64_t)U * H * w.GQp;
+    k_ml_combine<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.ml_part, reinterpret_cast<float2*>(ws + w.ml), w.S1,
+                                                             w.GQp, GQ, n);
+    AKV_CHECK_LAUNCH("k_ml_combine");
+  }
+  if ((rc = launch_obs<DT, OBS_SCORE>(p, a, st))) return rc;
+  k_o_combine<<<(unsigned)((int64_t)U * H * w.GQp), 128, 0, st>>>(
+      a.o_part, reinterpret_cast<float*>(ws + w.o), reinterpret_cast<uint16_t*>(ws + w.ohl),
+      reinterpret_cast<float*>(ws + w.oo), w.S1, w.GQp);
+  AKV_CHECK_LAUNCH("k_o_combine");
+
+  k_select<DT><<<(unsigned)(U * H), 1024, 0, st>>>(
+      K, V, a.score, reinterpret_cast<float*>(ws + w.pooled), cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v,
+      p.off_positions, reinterpret_cast<int*>(ws + w.anchor_of), reinterpret_cast<float2*>(ws + w.anorm), H, N,
+      p.window, p.k_scored, p.k_uniform, A);
+  AKV_CHECK_LAUNCH("k_select");
+
+  const int ntiles = (N + 255) / 256;
+  k_assign<DT><<<(unsigned)((int64_t)U * 2 * H * ntiles), 256, 0, st>>>(
+      K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_words,
+      reinterpret_cast<const float2*>(ws + w.anorm), a.anchor_of, reinterpret_cast<int*>(ws + w.aidx),
+      reinterpret_cast<float*>(ws + w.gam), reinterpret_cast<float*>(ws + w.rn2), H, N, A, ntiles);
+  AKV_CHECK_LAUNCH("k_assign");
+
+  if ((rc = launch_obs<DT, OBS_UTIL>(p, a, st))) return rc;
+
+  // top-R per (unit, side); R_K == R_V
+  const int R = p.R_K;
+  unsigned* hist = reinterpret_cast<unsigned*>(ws + w.hist);
+  unsigned* state = reinterpret_cast<unsigned*>(ws + w.sel_state);
+  unsigned* blk = reinterpret_cast<unsigned*>(ws + w.blk);
+  const unsigned nchunkblk = (unsigned)((int64_t)U * 2 * H * C);
+  k_zero_u32<<<(unsigned)((U * 2 * kHistBins + 255) / 256), 256, 0, st>>>(hist, (int64_t)U * 2 * kHistBins);
+  AKV_CHECK_LAUNCH("k_zero_u32");
+  for (int pass = 0; pass < 3; ++pass) {
+    k_topr_hist<<<nchunkblk, 256, 0, st>>>(a.util, hist, state, H, N, C, R, pass);
+    AKV_CHECK_LAUNCH("k_topr_hist");
+    k_topr_scan<<<(unsigned)(U * 2), 256, 0, st>>>(hist, state, R, pass);
+    AKV_CHECK_LAUNCH("k_topr_scan");
+  }
+  k_topr_count<<<nchunkblk, 256, 0, st>>>(a.util, state, blk, H, N, C, R);
+  AKV_CHECK_LAUNCH("k_topr_count");
+  k_topr_blockscan<<<(unsigned)(U * 2), 1024, 0, st>>>(blk, state, cache, p.unit_stride, p.off_chunk_k, p.off_chunk_v,
+                                                      H * C, R);
+  AKV_CHECK_LAUNCH("k_topr_blockscan");
+  const int Rmax = std::max(1, std::max(p.R_K, p.R_V));
+  int* sel_list = reinterpret_cast<int*>(ws + w.sel_list);
+  k_topr_flag<<<nchunkblk, 256, 0, st>>>(a.util, state, blk, cache, p.unit_stride, p.off_words, sel_list, Rmax, H, N,
+                                         C, R);
+  AKV_CHECK_LAUNCH("k_topr_flag");
+  if (R > 0) {
+    const int nblk = (R + 15) / 16;
+    k_quant<DT><<<(unsigned)((int64_t)U * 2 * nblk), 256, 0, st>>>(
+        K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_res_k, p.off_res_v, sel_list, Rmax,
+        reinterpret_cast<const int*>(ws + w.aidx), reinterpret_cast<const float*>(ws + w.gam), H, N, A, R, nblk);
+    AKV_CHECK_LAUNCH("k_quant");
+  }
+  return 0;
+}
+
+int run_compress(const anchorkv_plan_info& p, const void* K, const void* V, const void* Q, void* cache, void* ws,
+                 void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (p.dtype == ANCHORKV_BF16) return compress_impl<ANCHORKV_BF16>(p, K, V, Q, cache, ws, st);
+  return compress_impl<ANCHORKV_F32>(p, K, V, Q, cache, ws, st);
+}
+
+}  // namespace akv

@@ -1,0 +1,336 @@
+// Host side of the C ABI: argument checks, the byte plan, the cache layout,
+// workspace layouts and the reference host packer / unpacker.  No HIP calls
+// here except through run_compress / run_decode.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+#include <algorithm>
+
+#include "anchorkv_internal.hpp"
+
+namespace akv {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int obs_splits(const anchorkv_plan_info& p) {
+  int64_t heads = (int64_t)p.units * p.H;
+  int64_t want = (2048 + heads - 1) / heads;
+  int64_t cap = std::max<int64_t>(1, p.N / 1024);
+  return (int)std::max<int64_t>(1, std::min(want, cap));
+}
+
+CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
+  CompressWs w{};
+  const int64_t U = p.units, H = p.H, N = p.N, D = p.D, A = p.A;
+  const int64_t C = p.n_chunks;
+  w.S1 = obs_splits(p);
+  w.GQp = padded_queries(p);
+  const int64_t GQp = w.GQp;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = round_up(off + bytes, 256); return o; };
+  w.score = take(4 * U * H * N);
+  w.ml = take(8 * U * H * GQp);
+  w.o = take(4 * U * H * GQp * D);
+  w.util = take(4 * U * 2 * H * N);
+  w.gam = take(4 * U * 2 * H * N);
+  w.rn2 = take(4 * U * 2 * H * N);
+  w.aidx = take(4 * U * 2 * H * N);
+  w.ml_part = take(8 * U * H * w.S1 * GQp);
+  w.o_part = take(4 * U * H * w.S1 * GQp * D);
+  w.ohl = take(2 * U * H * 2 * GQp * D);
+  w.oo = take(4 * U * H * GQp);
+  w.anchor_of = take(4 * U * H * N);
+  w.anorm = take(8 * U * 2 * H * A);
+  w.pooled = take(4 * U * H * N);
+  w.hist = take(4 * U * 2 * kHistBins);
+  w.sel_state = take(4 * U * 2 * 4);
+  w.blk = take(16 * U * 2 * H * C);
+  w.sel_list = take(4 * U * 2 * std::max<int64_t>(1, std::max(p.R_K, p.R_V)));
+  w.total = off;
+  return w;
+}
+
+DecodeWs decode_ws_layout(const anchorkv_plan_info& p) {
+  DecodeWs w{};
+  const int64_t U = p.units, H = p.H, G = p.G, A = p.A, D = p.D;
+  w.S2 = p.decode_splits;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { int64_t o = off; off = round_up(off + bytes, 256); return o; };
+  w.stab = take(4 * U * H * G * A);
+  w.qsum = take(4 * U * H * G * 4);
+  w.part_ml = take(8 * U * H * w.S2 * G);
+  w.part_w = take(4 * U * H * w.S2 * G * A);
+  w.part_acc = take(4 * U * H * w.S2 * G * D);
+  w.total = off;
+  return w;
+}
+
+static int decode_split_count(const anchorkv_plan_info& p) {
+  int64_t heads = (int64_t)p.units * p.H;
+  int64_t want = (2048 + heads - 1) / heads;
+  int64_t cap = p.n_chunks;  // splits start on 1024-token chunk boundaries
+  return (int)std::max<int64_t>(1, std::min(want, cap));
+}
+
+static void layout(anchorkv_plan_info* p) {
+  const int64_t H = p->H, N = p->N, D = p->D, A = p->A, e = p->elem_bytes, C = p->n_chunks;
+  int64_t off = kHeaderBytes;
+  p->off_anchor_k = off; off += H * A * D * e;
+  p->off_anchor_v = off; off += H * A * D * e;
+  p->off_res_k = off; off += (int64_t)kRecBytes * p->R_K;
+  p->off_res_v = off; off += (int64_t)kRecBytes * p->R_V;
+  p->off_words = off; off += 8 * H * N;
+  p->off_chunk_k = off; off += 4 * H * C;
+  p->off_chunk_v = off; off += 4 * H * C;
+  p->off_positions = off; off += 4 * H * A;
+  p->unit_bytes = off;
+  p->unit_stride = round_up(off, 16);
+  p->cache_bytes = p->unit_stride * p->units;
+  p->decode_splits = decode_split_count(*p);
+  p->compress_workspace_bytes = compress_ws_layout(*p).total;
+  p->decode_workspace_bytes = decode_ws_layout(*p).total;
+}
+
+void fill_header(const anchorkv_plan_info& p, UnitHeader* h) {
+  std::memset(h, 0, sizeof(*h));
+  h->magic = kMagic;
+  h->version = 1;
+  h->H = p.H; h->G = p.G; h->N = p.N; h->D = p.D; h->n_obs = p.n_obs; h->dtype = p.dtype; h->window = p.window;
+  h->theta = p.theta;
+  h->A = p.A; h->k_scored = p.k_scored; h->k_uniform = p.k_uniform; h->R_K = p.R_K; h->R_V = p.R_V;
+  h->n_chunks = p.n_chunks;
+  h->off_anchor_k = p.off_anchor_k; h->off_anchor_v = p.off_anchor_v;
+  h->off_res_k = p.off_res_k; h->off_res_v = p.off_res_v; h->off_words = p.off_words;
+  h->off_chunk_k = p.off_chunk_k; h->off_chunk_v = p.off_chunk_v; h->off_positions = p.off_positions;
+  h->unit_bytes = p.unit_bytes; h->unit_stride = p.unit_stride;
+}
+
+static int plan_impl(const anchorkv_dims* d, float theta, int32_t window, anchorkv_plan_info* out) {
+  if (!d || !out) return fail(ANCHORKV_E_ARG, "anchorkv_plan: null argument");
+  if (d->dtype != ANCHORKV_BF16 && d->dtype != ANCHORKV_F32)
+    return fail(ANCHORKV_E_DTYPE, "anchorkv_plan: dtype %d is not bf16 (1) or f32 (2)", d->dtype);
+  if (d->head_dim != kHeadDim) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: head_dim %d != 128", d->head_dim);
+  if (d->units < 1 || d->kv_heads < 1 || d->q_per_kv < 1 || d->n_tokens < 1)
+    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: units, kv_heads, q_per_kv, n_tokens must be >= 1");
+  if (d->n_obs < 1 || d->n_obs > d->n_tokens)
+    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: n_obs %d outside [1, n_tokens]", d->n_obs);
+  if (window < 1 || window > d->n_tokens)
+    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: window %d outside [1, n_tokens]", window);
+  if ((int64_t)d->kv_heads * d->n_tokens > (1ll << 30) || (int64_t)d->q_per_kv * d->n_obs > 4096)
+    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: kv_heads*n_tokens or q_per_kv*n_obs too large");
+  if (!(theta > 0.0f) || !std::isfinite(theta)) return fail(ANCHORKV_E_ARG, "anchorkv_plan: theta must be > 0");
+
+  anchorkv_plan_info p;
+  std::memset(&p, 0, sizeof(p));
+  p.units = d->units; p.H = d->kv_heads; p.G = d->q_per_kv; p.N = d->n_tokens; p.D = d->head_dim;
+  p.n_obs = d->n_obs; p.dtype = d->dtype; p.elem_bytes = d->dtype == ANCHORKV_BF16 ? 2 : 4;
+  p.window = window; p.theta = theta;
+  const int64_t H = p.H, N = p.N, D = p.D, e = p.elem_bytes, W = window;
+  const int64_t C = (N + kChunk - 1) / kChunk;
+  p.n_chunks = (int32_t)C;
+  const double th = (double)theta;
+  // Per head and side: B = theta*N*D*e bytes; anchors cost D*e + 2 (their half of the int32
+  // position), every token a 4-byte pointer, every chunk a 4-byte offset, the header 128/H.
+  const double B = th * (double)(N * D * e);
+  const double amax_d = std::floor((B - 4.0 * (double)N - 4.0 * (double)C - 128.0 / (double)H) / (double)(D * e + 2));
+  if (amax_d < (double)W)
+    return fail(ANCHORKV_E_BUDGET, "anchorkv_plan: theta %.6g cannot pay for %d window anchors and the pointers", th, window);
+  const int64_t A_max = (int64_t)amax_d;
+  const int64_t k_nw = std::max<int64_t>(0, std::min(std::min(N / 128, A_max - W), N - W));
+  const int64_t k_s = (int64_t)std::floor(0.7 * (double)k_nw);
+  const int64_t A = W + k_nw;
+  if (A > kMaxAnchors) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %lld anchors exceed the 15-bit index", (long long)A);
+  p.A = (int32_t)A; p.k_scored = (int32_t)k_s; p.k_uniform = (int32_t)(k_nw - k_s);
+  const int64_t budget = (int64_t)std::floor(th * (double)(H * N * D * e));
+  const int64_t fixed = 128 + H * (A * D * e + 4 * N + 2 * A + 4 * C);
+  const int64_t rec = D / 4 + D / 8;
+  const int64_t R = std::max<int64_t>(0, std::min(H * (N - A), (budget - fixed) / rec));
+  p.R_K = p.R_V = (int32_t)R;
+  p.budget_bytes_per_side = budget;
+  p.used_bytes_k = fixed + R * rec;
+  p.used_bytes_v = fixed + R * rec;
+  layout(&p);
+  p.compression_ratio = (double)(2 * H * N * D * e) / (double)p.unit_bytes;
+  *out = p;
+  return 0;
+}
+
+}  // namespace akv
+
+using namespace akv;
+
+extern "C" {
+
+const char* anchorkv_version(void) { return "anchorkv-mi355x 0.1 (gfx950)"; }
+
+const char* anchorkv_last_error(void) { return g_err; }
+
+int anchorkv_plan(const anchorkv_dims* dims, float theta, int32_t window, anchorkv_plan_info* out) {
+  return plan_impl(dims, theta, window, out);
+}
+
+int anchorkv_plan_from_header(const void* header_host, int32_t units, anchorkv_plan_info* out) {
+  if (!header_host || !out || units < 1) return fail(ANCHORKV_E_ARG, "anchorkv_plan_from_header: bad argument");
+  UnitHeader h;
+  std::memcpy(&h, header_host, sizeof(h));
+  if (h.magic != kMagic || h.version != 1) return fail(ANCHORKV_E_LAYOUT, "anchorkv_plan_from_header: bad magic/version");
+  anchorkv_dims d{units, h.H, h.G, h.N, h.D, h.n_obs, h.dtype};
+  int rc = plan_impl(&d, h.theta, h.window, out);
+  if (rc) return rc;
+  if (out->A != h.A || out->R_K != h.R_K || out->R_V != h.R_V || out->unit_bytes != h.unit_bytes ||
+      out->off_words != h.off_words)
+    return fail(ANCHORKV_E_LAYOUT, "anchorkv_plan_from_header: header does not match its own plan");
+  return 0;
+}
+
+int anchorkv_workspace_offsets(const anchorkv_plan_info* plan, int64_t out[8]) {
+  if (!plan || !out) return fail(ANCHORKV_E_ARG, "anchorkv_workspace_offsets: null argument");
+  CompressWs w = compress_ws_layout(*plan);
+  out[0] = w.score; out[1] = w.ml; out[2] = w.o; out[3] = w.util;
+  out[4] = w.gam; out[5] = w.rn2; out[6] = w.aidx; out[7] = w.GQp;
+  return 0;
+}
+
+int anchorkv_compress(const anchorkv_plan_info* plan, const void* K, const void* V, const void* Q_obs,
+                      void* cache, size_t cache_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !K || !V || !Q_obs || !cache || !workspace) return fail(ANCHORKV_E_ARG, "anchorkv_compress: null argument");
+  if ((int64_t)cache_bytes < plan->cache_bytes)
+    return fail(ANCHORKV_E_SMALL_BUFFER, "anchorkv_compress: cache %zu < %lld bytes", cache_bytes, (long long)plan->cache_bytes);
+  if ((int64_t)workspace_bytes < plan->compress_workspace_bytes)
+    return fail(ANCHORKV_E_SMALL_BUFFER, "anchorkv_compress: workspace %zu < %lld bytes", workspace_bytes,
+                (long long)plan->compress_workspace_bytes);
+  if (((uintptr_t)K | (uintptr_t)V | (uintptr_t)Q_obs | (uintptr_t)cache | (uintptr_t)workspace) & 15)
+    return fail(ANCHORKV_E_ARG, "anchorkv_compress: buffers must be 16-byte aligned");
+  return run_compress(*plan, K, V, Q_obs, cache, workspace, stream);
+}
+
+int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, const void* q, float* o, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!plan || !cache || !q || !o || !workspace) return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn: null argument");
+  if ((int64_t)workspace_bytes < plan->decode_workspace_bytes)
+    return fail(ANCHORKV_E_SMALL_BUFFER, "anchorkv_decode_attn: workspace %zu < %lld bytes", workspace_bytes,
+                (long long)plan->decode_workspace_bytes);
+  if (((uintptr_t)cache | (uintptr_t)q | (uintptr_t)o | (uintptr_t)workspace) & 15)
+    return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn: buffers must be 16-byte aligned");
+  return run_decode(*plan, cache, q, o, workspace, stream);
+}
+
+// ---------------------------------------------------------------- host packer
+// Code word j of a record holds coordinates j + 16c (c = 0..7) in bits 2c..2c+1.
+int anchorkv_unit_pack_host(const anchorkv_plan_info* p, const anchorkv_unit_arrays* in, void* unit_out) {
+  if (!p || !in || !unit_out || !in->positions || !in->anchors_k || !in->anchors_v || !in->idx || !in->gamma16 ||
+      !in->flag || !in->codes || !in->scale16 || !in->zero16)
+    return fail(ANCHORKV_E_ARG, "anchorkv_unit_pack_host: null argument");
+  const int64_t H = p->H, N = p->N, D = p->D, A = p->A, e = p->elem_bytes, C = p->n_chunks;
+  uint8_t* base = (uint8_t*)unit_out;
+  std::memset(base, 0, (size_t)p->unit_bytes);
+  UnitHeader hd;
+  fill_header(*p, &hd);
+  std::memcpy(base, &hd, sizeof(hd));
+  std::memcpy(base + p->off_anchor_k, in->anchors_k, (size_t)(H * A * D * e));
+  std::memcpy(base + p->off_anchor_v, in->anchors_v, (size_t)(H * A * D * e));
+  std::memcpy(base + p->off_positions, in->positions, (size_t)(4 * H * A));
+  uint32_t* words = (uint32_t*)(base + p->off_words);
+  for (int s = 0; s < 2; ++s) {
+    const int64_t R = s ? p->R_V : p->R_K;
+    uint8_t* rec = base + (s ? p->off_res_v : p->off_res_k);
+    int32_t* chunk = (int32_t*)(base + (s ? p->off_chunk_v : p->off_chunk_k));
+    int64_t r = 0;
+    for (int64_t h = 0; h < H; ++h) {
+      for (int64_t t = 0; t < N; ++t) {
+        const int64_t i = (s * H + h) * N + t;
+        if (t % kChunk == 0) chunk[h * C + t / kChunk] = (int32_t)r;
+        const int32_t a = in->idx[i];
+        if (a < 0 || a >= A) return fail(ANCHORKV_E_LAYOUT, "pack: anchor index %d out of range", a);
+        uint32_t w = (uint32_t)a | ((uint32_t)in->gamma16[i] << 16);
+        if (in->flag[i]) {
+          if (r >= R) return fail(ANCHORKV_E_LAYOUT, "pack: more flagged tokens than R=%lld", (long long)R);
+          w |= 0x8000u;
+          uint16_t cw[16] = {0};
+          const uint8_t* cd = in->codes + i * D;
+          for (int d = 0; d < D; ++d) cw[d % 16] |= (uint16_t)((cd[d] & 3u) << (2 * (d / 16)));
+          uint8_t* out = rec + r * kRecBytes;
+          std::memcpy(out, cw, 32);
+          for (int g = 0; g < D / kGroup; ++g) {
+            uint16_t sz[2] = {in->scale16[i * (D / kGroup) + g], in->zero16[i * (D / kGroup) + g]};
+            std::memcpy(out + 32 + 4 * g, sz, 4);
+          }
+          ++r;
+        }
+        words[(h * N + t) * 2 + s] = w;
+      }
+    }
+    if (r != R) return fail(ANCHORKV_E_LAYOUT, "pack: %lld flagged tokens on side %d, plan has %lld", (long long)r, s,
+                            (long long)R);
+  }
+  return 0;
+}
+
+int anchorkv_unit_unpack_host(const anchorkv_plan_info* p, const void* unit_in, anchorkv_unit_arrays* out) {
+  if (!p || !unit_in || !out) return fail(ANCHORKV_E_ARG, "anchorkv_unit_unpack_host: null argument");
+  const int64_t H = p->H, N = p->N, D = p->D, A = p->A, e = p->elem_bytes, C = p->n_chunks;
+  const uint8_t* base = (const uint8_t*)unit_in;
+  UnitHeader hd;
+  std::memcpy(&hd, base, sizeof(hd));
+  if (hd.magic != kMagic || hd.A != p->A || hd.N != p->N || hd.H != p->H || hd.R_K != p->R_K || hd.R_V != p->R_V)
+    return fail(ANCHORKV_E_LAYOUT, "unpack: header does not match the plan");
+  if (out->anchors_k) std::memcpy(out->anchors_k, base + p->off_anchor_k, (size_t)(H * A * D * e));
+  if (out->anchors_v) std::memcpy(out->anchors_v, base + p->off_anchor_v, (size_t)(H * A * D * e));
+  if (out->positions) std::memcpy(out->positions, base + p->off_positions, (size_t)(4 * H * A));
+  const uint32_t* words = (const uint32_t*)(base + p->off_words);
+  for (int s = 0; s < 2; ++s) {
+    const int64_t R = s ? p->R_V : p->R_K;
+    const uint8_t* rec = base + (s ? p->off_res_v : p->off_res_k);
+    const int32_t* chunk = (const int32_t*)(base + (s ? p->off_chunk_v : p->off_chunk_k));
+    int64_t r = 0;
+    for (int64_t h = 0; h < H; ++h) {
+      for (int64_t t = 0; t < N; ++t) {
+        const int64_t i = (s * H + h) * N + t;
+        if (t % kChunk == 0 && chunk[h * C + t / kChunk] != r)
+          return fail(ANCHORKV_E_LAYOUT, "unpack: chunk offset mismatch at side %d head %lld chunk %lld", s,
+                      (long long)h, (long long)(t / kChunk));
+        const uint32_t w = words[(h * N + t) * 2 + s];
+        if (out->idx) out->idx[i] = (int32_t)(w & 0x7FFFu);
+        if (out->gamma16) out->gamma16[i] = (uint16_t)(w >> 16);
+        const bool f = (w & 0x8000u) != 0;
+        if (out->flag) out->flag[i] = f ? 1 : 0;
+        if (f) {
+          if (r >= R) return fail(ANCHORKV_E_LAYOUT, "unpack: more flags than records on side %d", s);
+          const uint8_t* in = rec + r * kRecBytes;
+          uint16_t cw[16];
+          std::memcpy(cw, in, 32);
+          if (out->codes)
+            for (int d = 0; d < D; ++d) out->codes[i * D + d] = (uint8_t)((cw[d % 16] >> (2 * (d / 16))) & 3u);
+          for (int g = 0; g < D / kGroup; ++g) {
+            uint16_t sz[2];
+            std::memcpy(sz, in + 32 + 4 * g, 4);
+            if (out->scale16) out->scale16[i * (D / kGroup) + g] = sz[0];
+            if (out->zero16) out->zero16[i * (D / kGroup) + g] = sz[1];
+          }
+          ++r;
+        }
+      }
+    }
+    if (r != R) return fail(ANCHORKV_E_LAYOUT, "unpack: %lld flags on side %d, plan has %lld", (long long)r, s, (long long)R);
+  }
+  return 0;
+}
+
+}  // extern "C"

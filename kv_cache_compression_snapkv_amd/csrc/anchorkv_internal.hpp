@@ -1,0 +1,87 @@
+// Internal declarations shared by the host code and the HIP translation units.
+#pragma once
+
+#include <cstdint>
+#include <cstddef>
+#include <string>
+
+#include "anchorkv.h"
+
+namespace akv {
+
+constexpr int kHeaderBytes = 256;
+constexpr int kChunk = 1024;          // tokens per residual-offset chunk
+constexpr int kRecBytes = 48;         // residual record: 32 B codes + 4 x (fp16 scale, fp16 zero)
+constexpr int kGroup = 32;            // codec group (coordinates)
+constexpr int kHeadDim = 128;         // the only supported head dim
+constexpr uint32_t kMagic = 0x31564B41u;  // "AKV1"
+constexpr int kMaxAnchors = 32767;
+constexpr int kHistBins = 2048;       // radix-select digit bins (11 bits)
+
+void set_error(const char* fmt, ...);
+int fail(int code, const char* fmt, ...);
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Splits of the key range per (unit, head) in the observation-window kernels.
+int obs_splits(const anchorkv_plan_info& p);
+inline int padded_queries(const anchorkv_plan_info& p) { return (int)round_up((int64_t)p.G * p.n_obs, 16); }
+
+// Compress workspace layout (byte offsets from the workspace start).
+struct CompressWs {
+  int S1;          // key splits of the observation kernels
+  int GQp;         // observation queries per KV head, padded to 16
+  int64_t score;   // f32 [U][H][N]
+  int64_t ml;      // float2 [U][H][GQp]   (m * log2(e)/sqrt(D), 1/l)
+  int64_t o;       // f32 [U][H][GQp][D]
+  int64_t util;    // f32 [U][2][H][N]
+  int64_t gam;     // f32 [U][2][H][N]
+  int64_t rn2;     // f32 [U][2][H][N]
+  int64_t aidx;    // int32 [U][2][H][N]
+  int64_t ml_part; // float2 [U][H][S1][GQp]
+  int64_t o_part;  // f32 [U][H][S1][GQp][D]
+  int64_t ohl;     // bf16 [U][H][2][GQp][D] (hi, lo split of o)
+  int64_t oo;      // f32 [U][H][GQp] ||o||^2
+  int64_t anchor_of; // int32 [U][H][N] anchor index of a position, -1 if none
+  int64_t anorm;   // float2 [U][2][H][A] (||x_a||^2, 1/||x_a||)
+  int64_t pooled;  // f32 [U][H][N]
+  int64_t hist;    // u32 [U][2][kHistBins]
+  int64_t sel_state; // u32 [U][2][4]: prefix, need, threshold, done
+  int64_t blk;     // u32 [U][2][H*C][4]: greater, ties, sel_prefix, tie_prefix
+  int64_t sel_list; // int32 [U][2][Rmax] flat (head*N + t) in record order
+  int64_t total;
+};
+CompressWs compress_ws_layout(const anchorkv_plan_info& p);
+
+// Decode workspace layout.
+struct DecodeWs {
+  int S2;          // token splits per (unit, head); boundaries on 1024-token chunks
+  int64_t stab;    // f32 [U][H][G][A]   <q_g, k_a> * log2(e)/sqrt(D)
+  int64_t qsum;    // f32 [U][H][G][4]   per-group sums of q (times log2(e)/sqrt(D))
+  int64_t part_ml; // float2 [U][H][S2][G]
+  int64_t part_w;  // f32 [U][H][S2][G][A]
+  int64_t part_acc; // f32 [U][H][S2][G][D]
+  int64_t total;
+};
+DecodeWs decode_ws_layout(const anchorkv_plan_info& p);
+
+// Device header written at the start of every unit (256 bytes).
+struct UnitHeader {
+  uint32_t magic, version;
+  int32_t H, G, N, D, n_obs, dtype, window;
+  float theta;
+  int32_t A, k_scored, k_uniform, R_K, R_V, n_chunks;
+  int64_t off_anchor_k, off_anchor_v, off_res_k, off_res_v, off_words, off_chunk_k, off_chunk_v, off_positions;
+  int64_t unit_bytes, unit_stride;
+  int32_t unit_index, pad0;
+  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8];
+};
+static_assert(sizeof(UnitHeader) == 256, "header must be 256 bytes");
+void fill_header(const anchorkv_plan_info& p, UnitHeader* h);
+
+// Launch sequences (defined in the HIP translation units).
+int run_compress(const anchorkv_plan_info& p, const void* K, const void* V, const void* Q, void* cache,
+                 void* ws, void* stream);
+int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* ws, void* stream);
+
+}  // namespace akv

@@ -1,0 +1,107 @@
+// Device helpers shared by the gfx950 kernels: element traits, MFMA fragment
+// traits, rounding, wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <cmath>
+
+#include "anchorkv_internal.hpp"
+
+namespace akv {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// float -> fp16 bits, round to nearest even, saturating at +-65504.
+__device__ __forceinline__ uint16_t f2h_sat(float f) {
+  f = fminf(fmaxf(f, -65504.0f), 65504.0f);
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// Element traits: DT 1 = bf16 (stored as uint16), 2 = f32.
+template <int DT> struct Elem;
+template <> struct Elem<ANCHORKV_BF16> {
+  using T = uint16_t;
+  __device__ __forceinline__ static float f(T x) { return bf2f(x); }
+};
+template <> struct Elem<ANCHORKV_F32> {
+  using T = float;
+  __device__ __forceinline__ static float f(T x) { return x; }
+};
+
+// MFMA traits.  16x16 output tile, lane l holds rows 4*(l/16)+r (r = 0..3) of
+// column l%16.  A operand: lane holds row l%16, K-slice (l/16)*KW .. +KW-1 of
+// each KSTEP-wide step; B operand: column l%16, same K-slice.
+template <int DT> struct Mfma;
+template <> struct Mfma<ANCHORKV_BF16> {
+  using frag = bf16x8;
+  static constexpr int KW = 8;
+  static constexpr int KSTEP = 32;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const uint16_t* p) {  // 16-byte aligned
+    return *reinterpret_cast<const frag*>(p);
+  }
+  __device__ __forceinline__ static frag zero() {
+    frag z;
+    for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+    return z;
+  }
+};
+template <> struct Mfma<ANCHORKV_F32> {
+  using frag = float;
+  static constexpr int KW = 1;
+  static constexpr int KSTEP = 4;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const float* p) { return *p; }
+  __device__ __forceinline__ static frag zero() { return 0.0f; }
+};
+
+__device__ __forceinline__ bf16x8 bits_to_frag(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Split 8 floats into bf16 hi + lo so that hi + lo carries ~16 significant bits.
+__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
+  uint16_t h[8], l[8];
+  for (int i = 0; i < 8; ++i) {
+    h[i] = f2bf(v[i]);
+    l[i] = f2bf(v[i] - bf2f(h[i]));
+  }
+  uint4 hh, ll;
+  hh.x = h[0] | ((uint32_t)h[1] << 16); hh.y = h[2] | ((uint32_t)h[3] << 16);
+  hh.z = h[4] | ((uint32_t)h[5] << 16); hh.w = h[6] | ((uint32_t)h[7] << 16);
+  ll.x = l[0] | ((uint32_t)l[1] << 16); ll.y = l[2] | ((uint32_t)l[3] << 16);
+  ll.z = l[4] | ((uint32_t)l[5] << 16); ll.w = l[6] | ((uint32_t)l[7] << 16);
+  hi = bits_to_frag(hh);
+  lo = bits_to_frag(ll);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace akv
