@@ -1,0 +1,231 @@
+"""Benchmark of the AnchorKV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = the whole hot path over one batch of synthetic input: the
+end-of-prefill compression of every unit (all layers of all sequences) of the
+workload, then one decode-attention step over the compressed cache of every
+unit.  Inputs are generated on the GPU before the timed region.  Prints one
+JSON line.  `value` is sequence tokens compressed (and decoded over) per
+second of step time; per-stage times come from HIP events the library records
+between its kernels on the bench stream (anchorkv_profile_*).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed tokens/s (prefill compress) + decode-attn HBM GB/s, % of roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_compression_snapkv_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stage_work(p, stage):
+    """Algorithmic work of one launch of a stage over all units:
+    (flops, bytes).  Re-reads, recomputation and precision splits are not
+    counted."""
+    U, H, G, N, D, A, e = p.units, p.H, p.G, p.N, p.D, p.A, p.elem_bytes
+    GQ = G * p.n_obs
+    xb = U * H * N * D * e                      # one side's inputs
+    qb = U * H * GQ * D * e
+    if stage == "assign":                        # N x A x D similarity per side and head
+        return 2 * U * H * 2.0 * N * A * D, 2 * xb + 2 * U * H * A * D * e + U * 2 * H * N * 4
+    if stage == "obs_stats":                     # Q K^T
+        return U * H * 2.0 * N * GQ * D, xb + qb
+    if stage == "obs_score":                     # Q K^T for p, P V
+        return U * H * 2 * 2.0 * N * GQ * D, 2 * xb + qb + U * H * N * 4
+    if stage == "obs_util":                      # Q K^T for p, Q R_K, V O
+        return U * H * 3 * 2.0 * N * GQ * D, 2 * xb + qb + U * 2 * H * N * 4
+    if stage == "dec_stream":                    # pointer words + residual records
+        return U * H * N * G * 6.0, U * (8 * H * N + 48 * (p.R_K + p.R_V))
+    if stage == "dec_stab":
+        return U * H * G * A * 2.0 * D, U * H * A * D * e
+    if stage == "dec_combine":
+        return U * H * G * A * 2.0 * D, U * H * A * D * e + U * H * G * D * 4
+    return 0.0, 0.0
+
+
+def decode_bytes(p):
+    """Algorithmic bytes of one decode step over all units: the compressed
+    cache (anchors, pointer words, residual records, offsets, positions) plus
+    q and o."""
+    return p.cache_bytes + p.units * p.H * p.G * p.D * (p.elem_bytes + 4)
+
+
+def roofline(p, stage, ms):
+    flops, byts = stage_work(p, stage)
+    peak_f = PEAK_BF16_TFLOPS if p.dtype == 1 else PEAK_F32_MFMA_TFLOPS
+    t_f = flops / (peak_f * 1e12)
+    t_b = byts / (PEAK_HBM_GBS * 1e9)
+    s = ms * 1e-3
+    if stage.startswith("dec_stream") or t_b >= t_f:
+        return {"kernel": stage, "bound": "hbm", "achieved": byts / s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": (byts / s / 1e9) / PEAK_HBM_GBS, "algorithmic_bytes": byts}
+    return {"kernel": stage, "bound": "mfma", "achieved": flops / s / 1e12, "peak": peak_f, "unit": "TFLOP/s",
+            "frac": (flops / s / 1e12) / peak_f, "algorithmic_flops": flops}
+
+
+def cpu_baseline(w, units_sample=3):
+    """The oracle as it stands, on the host cores: compress + one decode step
+    for a bounded sample of units, extrapolated to the workload's tokens/s."""
+    import numpy as np
+    import kvsynth
+    from oracle import anchorkv_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    n = min(units_sample, w.units)
+    t_tot = 0.0
+    for u in range(n):
+        s, l = kvsynth.unit_index(w, u)
+        K, V, Q = kvsynth.unit_inputs(w, s, l, device="cpu")
+        K64, V64, Q64 = (kvsynth.to_f64(x) for x in (K, V, Q))
+        q = kvsynth.to_f64(kvsynth.decode_queries(w, 0, units=1)[0])
+        t0 = time.perf_counter()
+        c = O.compress_unit(K64, V64, Q64, w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes)
+        O.decode_unit(c, q)
+        t_tot += time.perf_counter() - t0
+    per_unit = t_tot / n
+    step_s = per_unit * w.units
+    return {"value": w.seqs * w.n_tokens / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.units} units (compress + 1 decode step each, float64 NumPy), "
+                      f"{per_unit:.2f} s/unit, extrapolated to all units"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3b_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1, help="decode steps per step (default 1)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import kvsynth
+    import kv_cache_compression_snapkv_amd as akv
+
+    w = kvsynth.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print(f"[bench] workload {w.name}: units={w.units} H={w.kv_heads} G={w.q_per_kv} N={w.n_tokens}", file=sys.stderr,
+          flush=True)
+    dt = akv.BF16 if w.dtype == "bf16" else akv.F32
+    p = akv.plan(w.units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs, dt, w.theta, w.window)
+    K = torch.empty(w.units, w.kv_heads, w.n_tokens, w.head_dim, dtype=w.torch_dtype, device=dev)
+    V = torch.empty_like(K)
+    Q = torch.empty(w.units, w.kv_heads * w.q_per_kv, w.n_obs, w.head_dim, dtype=w.torch_dtype, device=dev)
+    for u in range(w.units):
+        s, l = kvsynth.unit_index(w, u)
+        k, v, q = kvsynth.unit_inputs(w, s, l, device=dev)
+        K[u].copy_(k); V[u].copy_(v); Q[u].copy_(q)
+        del k, v, q
+    cache, ws, dws = akv.alloc(p, dev)
+    qs = [kvsynth.decode_queries(w, i, device=dev).contiguous() for i in range(8)]
+    o = torch.empty(w.units, w.kv_heads * w.q_per_kv, w.head_dim, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(i):
+        akv.compress(p, K, V, Q, cache, ws, stream)
+        for j in range(args.decode_steps):
+            akv.decode_attn(p, cache, qs[(i + j) % len(qs)], o, dws, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    akv.profile_enable(True)
+    akv.profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = akv.profile_read()
+    akv.profile_enable(False)
+    total_s = t1 - t0
+    ms_per_step = total_s * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    agg, cnt = {}, {}
+    for name, ms in stages:
+        agg[name] = agg.get(name, 0.0) + ms
+        cnt[name] = cnt.get(name, 0) + 1
+    stage_ms = {k: agg[k] / cnt[k] for k in agg}           # average per launch
+    comp_stages = ["obs_stats", "ml_combine", "obs_score", "o_combine", "select", "assign", "obs_util", "topr", "quant"]
+    dec_stages = ["dec_stab", "dec_stream", "dec_combine"]
+    compress_ms = sum(stage_ms.get(k, 0.0) for k in comp_stages)
+    decode_ms = sum(stage_ms.get(k, 0.0) for k in dec_stages)
+    dom = max(comp_stages + dec_stages, key=lambda k: stage_ms.get(k, 0.0) * (1 if k in comp_stages else args.decode_steps))
+    rl = roofline(p, dom, stage_ms[dom])
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tf):
+        t = json.load(open(tf))
+        if t.get("source_hash") == kernel_source_hash() and dom in t.get("kernels", {}):
+            traffic = t["kernels"][dom]
+    rl["traffic"] = traffic
+    dec_b = decode_bytes(p)
+    seq_tokens = w.seqs * w.n_tokens
+    # compress roofline: algorithmic flops and bytes of the whole pass, each at its peak
+    comp_flops = sum(stage_work(p, k)[0] for k in ("assign", "obs_stats", "obs_score", "obs_util")) \
+        - 2 * stage_work(p, "obs_stats")[0]                 # Q K^T counted once
+    comp_bytes = 2 * p.units * p.H * p.N * p.D * p.elem_bytes + p.cache_bytes
+    t_roof = max(comp_flops / (PEAK_BF16_TFLOPS * 1e12), comp_bytes / (PEAK_HBM_GBS * 1e9))
+    out = {
+        "metric": METRIC,
+        "value": seq_tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded clustered keys, N(0,1) values, N(0,I) queries; no dataset)",
+        "config": {"workload": w.name, "units": w.units, "seqs": w.seqs, "layers": w.layers, "kv_heads": w.kv_heads,
+                   "q_per_kv": w.q_per_kv, "n_tokens": w.n_tokens, "head_dim": w.head_dim, "n_obs": w.n_obs,
+                   "theta": w.theta, "window": w.window, "decode_steps_per_step": args.decode_steps,
+                   "parallelism": "none (1 GPU)"},
+        "compress": {"ms": compress_ms, "tokens_per_s": seq_tokens / (compress_ms * 1e-3),
+                     "roofline_ms": t_roof * 1e3, "roofline_frac": t_roof * 1e3 / compress_ms,
+                     "anchors": p.A, "residuals_per_side_per_unit": p.R_K,
+                     "compression_ratio": p.compression_ratio},
+        "decode": {"us": decode_ms * 1e3, "bytes": dec_b, "GB_s": dec_b / (decode_ms * 1e-3) / 1e9,
+                   "hbm_frac": dec_b / (decode_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                   "note": "cache fits the 256 MB Infinity Cache" if dec_b < 256e6 else "HBM-resident"},
+        "stages_ms": stage_ms,
+        "roofline": rl,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

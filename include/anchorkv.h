@@ -190,6 +190,16 @@ int anchorkv_unit_pack_host(const anchorkv_plan_info* plan, const anchorkv_unit_
  * plain arrays.  Errors: E_ARG, E_LAYOUT (bad header or inconsistent records). */
 int anchorkv_unit_unpack_host(const anchorkv_plan_info* plan, const void* unit_in, anchorkv_unit_arrays* out);
 
+/* Stage profiling for benchmarks (not part of the method).  When enabled,
+ * every compress / decode call records a HIP event on its stream before its
+ * first kernel and after each stage; anchorkv_profile_read waits for the last
+ * recorded event and returns, per stage in call order, its name and elapsed
+ * milliseconds, then clears the record.  Up to 1024 events are kept; stages
+ * beyond that are not recorded.  Global state: enable, run and read from one
+ * thread.  Errors: E_ARG, E_HIP. */
+int anchorkv_profile_enable(int enable);
+int anchorkv_profile_read(const char** names, float* ms, int max_stages, int* n_stages);
+
 #ifdef __cplusplus
 }
 #endif

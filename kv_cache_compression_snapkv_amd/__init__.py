@@ -6,7 +6,7 @@ cache without reconstructing it.  Both run in hand-written HIP kernels behind
 the C ABI in include/anchorkv.h; this package only marshals arguments.
 """
 from .binding import (BF16, F32, AnchorKVError, PlanInfo, alloc, compress, decode_attn, lib, pack_unit, plan,
-                      plan_from_header, unpack_unit, version, workspace_offsets)
+                      plan_from_header, profile_enable, profile_read, unpack_unit, version, workspace_offsets)
 
 __all__ = ["BF16", "F32", "AnchorKVError", "PlanInfo", "alloc", "compress", "decode_attn", "lib", "pack_unit", "plan",
-           "plan_from_header", "unpack_unit", "version", "workspace_offsets"]
+           "plan_from_header", "profile_enable", "profile_read", "unpack_unit", "version", "workspace_offsets"]

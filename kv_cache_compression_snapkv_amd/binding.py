@@ -80,13 +80,16 @@ def lib():
                                            ct.c_size_t, ct.c_void_p]
         L.anchorkv_unit_pack_host.argtypes = [ct.POINTER(PlanInfo), ct.POINTER(UnitArrays), ct.c_void_p]
         L.anchorkv_unit_unpack_host.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.POINTER(UnitArrays)]
+        L.anchorkv_profile_enable.argtypes = [ct.c_int]
+        L.anchorkv_profile_read.argtypes = [ct.POINTER(ct.c_char_p), ct.POINTER(ct.c_float), ct.c_int,
+                                            ct.POINTER(ct.c_int)]
         _lib = L
     return _lib
 
 
 EXPORTED = ["anchorkv_version", "anchorkv_last_error", "anchorkv_plan", "anchorkv_plan_from_header",
             "anchorkv_compress", "anchorkv_workspace_offsets", "anchorkv_decode_attn", "anchorkv_unit_pack_host",
-            "anchorkv_unit_unpack_host"]
+            "anchorkv_unit_unpack_host", "anchorkv_profile_enable", "anchorkv_profile_read"]
 
 
 def _check(rc: int):
@@ -159,6 +162,20 @@ def alloc(p: PlanInfo, device):
     ws = torch.empty(int(p.compress_workspace_bytes), dtype=torch.uint8, device=device)
     dws = torch.empty(int(p.decode_workspace_bytes), dtype=torch.uint8, device=device)
     return cache, ws, dws
+
+
+def profile_enable(on: bool = True):
+    """Record HIP events between the stages of every compress / decode call."""
+    _check(lib().anchorkv_profile_enable(1 if on else 0))
+
+
+def profile_read(max_stages: int = 1024):
+    """[(stage, ms), ...] for the calls since the last read (waits for them)."""
+    names = (ct.c_char_p * max_stages)()
+    ms = (ct.c_float * max_stages)()
+    n = ct.c_int(0)
+    _check(lib().anchorkv_profile_read(names, ms, max_stages, ct.byref(n)))
+    return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
 
 # ---------------------------------------------------------------- host packer

@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libanchorkv.so")
 ARCH = os.environ.get("ANCHORKV_ARCH", "gfx950")
 
-HIP_SOURCES = ["anchorkv_compress.hip", "anchorkv_decode.hip"]
+HIP_SOURCES = ["anchorkv_compress.hip", "anchorkv_decode.hip", "anchorkv_profile.hip"]
 CPP_SOURCES = ["anchorkv_host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

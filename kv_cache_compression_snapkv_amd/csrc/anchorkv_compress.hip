@@ -627,6 +627,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   const int GQ = p.G * p.n_obs;
   if (A > 4096) return fail(ANCHORKV_E_SHAPE, "anchors per head %d > 4096 not supported", A);
 
+  prof_call_begin(st);
   UnitHeader hd;
   fill_header(p, &hd);
   k_headers<<<U, 64, 0, st>>>(hd, cache, p.unit_stride);
@@ -654,23 +655,28 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
 
   int rc;
   if ((rc = launch_obs<DT, OBS_STATS>(p, a, st))) return rc;
+  prof_mark(st, "obs_stats");
   {
     const int64_t n = (int64_t)U * H * w.GQp;
     k_ml_combine<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.ml_part, reinterpret_cast<float2*>(ws + w.ml), w.S1,
                                                              w.GQp, GQ, n);
     AKV_CHECK_LAUNCH("k_ml_combine");
   }
+  prof_mark(st, "ml_combine");
   if ((rc = launch_obs<DT, OBS_SCORE>(p, a, st))) return rc;
+  prof_mark(st, "obs_score");
   k_o_combine<<<(unsigned)((int64_t)U * H * w.GQp), 128, 0, st>>>(
       a.o_part, reinterpret_cast<float*>(ws + w.o), reinterpret_cast<uint16_t*>(ws + w.ohl),
       reinterpret_cast<float*>(ws + w.oo), w.S1, w.GQp);
   AKV_CHECK_LAUNCH("k_o_combine");
+  prof_mark(st, "o_combine");
 
   k_select<DT><<<(unsigned)(U * H), 1024, 0, st>>>(
       K, V, a.score, reinterpret_cast<float*>(ws + w.pooled), cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v,
       p.off_positions, reinterpret_cast<int*>(ws + w.anchor_of), reinterpret_cast<float2*>(ws + w.anorm), H, N,
       p.window, p.k_scored, p.k_uniform, A);
   AKV_CHECK_LAUNCH("k_select");
+  prof_mark(st, "select");
 
   const int ntiles = (N + 255) / 256;
   k_assign<DT><<<(unsigned)((int64_t)U * 2 * H * ntiles), 256, 0, st>>>(
@@ -678,8 +684,10 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
       reinterpret_cast<const float2*>(ws + w.anorm), a.anchor_of, reinterpret_cast<int*>(ws + w.aidx),
       reinterpret_cast<float*>(ws + w.gam), reinterpret_cast<float*>(ws + w.rn2), H, N, A, ntiles);
   AKV_CHECK_LAUNCH("k_assign");
+  prof_mark(st, "assign");
 
   if ((rc = launch_obs<DT, OBS_UTIL>(p, a, st))) return rc;
+  prof_mark(st, "obs_util");
 
   // top-R per (unit, side); R_K == R_V
   const int R = p.R_K;
@@ -705,6 +713,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   k_topr_flag<<<nchunkblk, 256, 0, st>>>(a.util, state, blk, cache, p.unit_stride, p.off_words, sel_list, Rmax, H, N,
                                          C, R);
   AKV_CHECK_LAUNCH("k_topr_flag");
+  prof_mark(st, "topr");
   if (R > 0) {
     const int nblk = (R + 15) / 16;
     k_quant<DT><<<(unsigned)((int64_t)U * 2 * nblk), 256, 0, st>>>(
@@ -712,6 +721,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
         reinterpret_cast<const int*>(ws + w.aidx), reinterpret_cast<const float*>(ws + w.gam), H, N, A, R, nblk);
     AKV_CHECK_LAUNCH("k_quant");
   }
+  prof_mark(st, "quant");
   return 0;
 }
 

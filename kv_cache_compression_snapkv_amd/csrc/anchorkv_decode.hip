@@ -250,8 +250,10 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   const float c = kLog2e / sqrtf((float)kHeadDim);
   float* stab = reinterpret_cast<float*>(ws + w.stab);
   float* qsum = reinterpret_cast<float*>(ws + w.qsum);
+  prof_call_begin(st);
   k_dec_stab<DT><<<(unsigned)(U * H), 256, 0, st>>>(q, cache, p.unit_stride, p.off_anchor_k, stab, qsum, H, G, A, c);
   AKV_CHECK_LAUNCH("k_dec_stab");
+  prof_mark(st, "dec_stab");
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_stream<DT>), hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds) != hipSuccess)
     return fail(ANCHORKV_E_HIP, "decode: cannot raise the dynamic LDS limit");
@@ -260,10 +262,12 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
       reinterpret_cast<float2*>(ws + w.part_ml), reinterpret_cast<float*>(ws + w.part_w),
       reinterpret_cast<float*>(ws + w.part_acc), H, G, N, A, C, S2, c);
   AKV_CHECK_LAUNCH("k_dec_stream");
+  prof_mark(st, "dec_stream");
   k_dec_combine<DT><<<(unsigned)(U * H), 256, sizeof(float) * G * S2, st>>>(
       cache, p.unit_stride, p.off_anchor_v, reinterpret_cast<const float2*>(ws + w.part_ml),
       reinterpret_cast<const float*>(ws + w.part_w), reinterpret_cast<const float*>(ws + w.part_acc), o, H, G, A, S2);
   AKV_CHECK_LAUNCH("k_dec_combine");
+  prof_mark(st, "dec_combine");
   return 0;
 }
 

@@ -79,6 +79,10 @@ struct UnitHeader {
 static_assert(sizeof(UnitHeader) == 256, "header must be 256 bytes");
 void fill_header(const anchorkv_plan_info& p, UnitHeader* h);
 
+// Stage profiler (HIP events between stages; off unless enabled).
+void prof_call_begin(void* stream);
+void prof_mark(void* stream, const char* stage);
+
 // Launch sequences (defined in the HIP translation units).
 int run_compress(const anchorkv_plan_info& p, const void* K, const void* V, const void* Q, void* cache,
                  void* ws, void* stream);
