@@ -98,6 +98,33 @@ __device__ int block_excl_scan(int v, int* sh /*[32]*/, int* total) {
   return r;
 }
 
+// Radix-select step over a histogram in LDS: finds the bucket b (scanning from
+// the top) where the running count first reaches `need`; returns b and the
+// count strictly above it.  Block-parallel: each thread owns a run of
+// consecutive buckets (highest first), one exclusive scan finds the run.
+__device__ void find_bucket(const unsigned* hist, int nbins, unsigned need, int* sh, int* out_b, unsigned* out_above) {
+  const int nt = blockDim.x;
+  const int per = (nbins + nt - 1) / nt;
+  const int hi = nbins - 1 - threadIdx.x * per;  // this thread's buckets: hi, hi-1, ..., hi-per+1
+  unsigned local = 0;
+  for (int k = 0; k < per; ++k) {
+    const int b = hi - k;
+    if (b >= 0) local += hist[b];
+  }
+  int tot;
+  const unsigned above0 = (unsigned)block_excl_scan((int)local, sh, &tot);
+  if (above0 < need && above0 + local >= need) {
+    unsigned cum = above0;
+    for (int k = 0; k < per; ++k) {
+      const int b = hi - k;
+      if (b < 0) break;
+      if (cum + hist[b] >= need) { *out_b = b; *out_above = cum; break; }
+      cum += hist[b];
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------- anchor selection
 // One 1024-thread block per (unit, head).  score -> pooled (width 7 window
 // sum over non-window positions) -> top k_s (radix select on the f32 bits,
@@ -113,7 +140,8 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
   constexpr int D = kHeadDim;
   __shared__ unsigned hist[kHistBins];
   __shared__ int sh[32];
-  __shared__ unsigned s_prefix, s_need;
+  __shared__ int s_b;
+  __shared__ unsigned s_above;
   __shared__ int s_pos[4096];  // scored + uniform positions (A <= 4096 is checked on the host)
   const int h = blockIdx.x % H;
   const int u = blockIdx.x / H;
@@ -145,19 +173,11 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
         if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shifts[p]) & ((1u << widths[p]) - 1)], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        unsigned cum = 0;
-        int b = (1 << widths[p]) - 1;
-        for (; b > 0; --b) {
-          if (cum + hist[b] >= need) break;
-          cum += hist[b];
-        }
-        s_prefix = prefix | ((unsigned)b << shifts[p]);
-        s_need = need - cum;
-      }
+      if (tid == 0) { s_b = 0; s_above = 0; }
       __syncthreads();
-      prefix = s_prefix;
-      need = s_need;
+      find_bucket(hist, 1 << widths[p], need, sh, &s_b, &s_above);
+      prefix = prefix | ((unsigned)s_b << shifts[p]);
+      need = need - s_above;
       __syncthreads();
     }
   }
@@ -355,11 +375,19 @@ __global__ __launch_bounds__(256) void k_assign(const void* Kv, const void* Vv, 
     float dot = 0.0f;
     for (int st = 0; st < NSTEP; ++st) {
       const int kk = st * M::KSTEP + kg * M::KW;
-      for (int e = 0; e < M::KW; ++e) {
-        xs[st * M::KW + e] = Elem<DT>::f(X[(int64_t)tt * D + kk + e]);
-        as_[st * M::KW + e] = Elem<DT>::f(AX[(int64_t)a * D + kk + e]);
-        dot = fmaf(xs[st * M::KW + e], as_[st * M::KW + e], dot);
+      if constexpr (DT == ANCHORKV_BF16) {
+        const uint4 av = *reinterpret_cast<const uint4*>(AX + (int64_t)a * D + kk);
+        uint16_t ab[8];
+        __builtin_memcpy(ab, &av, 16);
+        for (int e = 0; e < 8; ++e) {
+          xs[st * 8 + e] = (float)xf[rb][st][e];
+          as_[st * 8 + e] = bf2f(ab[e]);
+        }
+      } else {
+        xs[st] = xf[rb][st];
+        as_[st] = Elem<DT>::f(AX[(int64_t)a * D + kk]);
       }
+      for (int e = 0; e < M::KW; ++e) dot = fmaf(xs[st * M::KW + e], as_[st * M::KW + e], dot);
     }
     dot += __shfl_xor(dot, 16, 64);
     dot += __shfl_xor(dot, 32, 64);
@@ -420,26 +448,27 @@ __global__ __launch_bounds__(256) void k_topr_hist(const float* util, unsigned* 
     if (lh[b]) atomicAdd(&gh[b], lh[b]);
 }
 
-__global__ void k_topr_scan(unsigned* hist, unsigned* state, int R, int pass) {
+__global__ __launch_bounds__(256) void k_topr_scan(unsigned* hist, unsigned* state, int R, int pass) {
+  __shared__ unsigned lh[kHistBins];
+  __shared__ int sh[32];
+  __shared__ int s_b;
+  __shared__ unsigned s_above;
   const int us = blockIdx.x;
   unsigned* st = state + (int64_t)us * 4;
   unsigned* gh = hist + (int64_t)us * kHistBins;
-  if (threadIdx.x == 0 && R > 0) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int width = pass == 2 ? 10 : 11;
-    unsigned prefix = pass == 0 ? 0u : st[0];
-    unsigned need = pass == 0 ? (unsigned)R : st[1];
-    unsigned cum = 0;
-    int b = (1 << width) - 1;
-    for (; b > 0; --b) {
-      if (cum + gh[b] >= need) break;
-      cum += gh[b];
-    }
-    st[0] = prefix | ((unsigned)b << shift);
-    st[1] = need - cum;
-  }
+  const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+  const int width = pass == 2 ? 10 : 11;
+  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) { lh[b] = gh[b]; gh[b] = 0; }  // clear for the next pass
+  if (threadIdx.x == 0) { s_b = 0; s_above = 0; }
   __syncthreads();
-  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) gh[b] = 0;  // ready for the next pass
+  if (R == 0) return;
+  const unsigned prefix = pass == 0 ? 0u : st[0];
+  const unsigned need = pass == 0 ? (unsigned)R : st[1];
+  find_bucket(lh, 1 << width, need, sh, &s_b, &s_above);
+  if (threadIdx.x == 0) {
+    st[0] = prefix | ((unsigned)s_b << shift);
+    st[1] = need - s_above;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_topr_count(const float* util, const unsigned* state, unsigned* blk, int H,
@@ -549,9 +578,13 @@ __global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsi
 }
 
 // ------------------------------------------------------------ quantise+pack
-// 16 lanes per residual record; lane j owns coordinates 8j..8j+7 (group j/4).
-// r = x - gamma x_a in f32 with the unrounded gamma; per 32-group: zero =
-// fp16(min), scale = fp16((max-min)/3), code = clamp(rne((r-zero)/scale),0,3).
+// 16 lanes per residual record, 4 records per lane group in flight; lane j
+// owns coordinates 8j..8j+7 (group j/4).  r = x - gamma x_a in f32 with the
+// unrounded gamma; per 32-group: zero = fp16(min), scale = fp16((max-min)/3),
+// code = clamp(rne((r - zero)/scale), 0, 3) (0 when scale = 0).  Record: code
+// word j holds coordinates j + 16c in bits 2c..2c+1, then (scale, zero) x 4.
+constexpr int kQuantPerGroup = 4;
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, uint8_t* cache, int64_t stride,
                                               int64_t off_ak, int64_t off_av, int64_t off_rk, int64_t off_rv,
@@ -559,47 +592,78 @@ __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, u
                                               int N, int A, int R, int nblk) {
   using T = typename Elem<DT>::T;
   constexpr int D = kHeadDim;
-  __shared__ uint8_t codes_s[16][128];
+  constexpr int QG = kQuantPerGroup;
+  __shared__ uint8_t codes_s[16][QG][128];
   int bid = blockIdx.x;
   const int blk = bid % nblk; bid /= nblk;
   const int side = bid % 2;
   const int u = bid / 2;
   const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
-  const int rec = blk * 16 + grp;
-  const bool active = rec < R;
   const int us = u * 2 + side;
-  int flat = active ? sel_list[(int64_t)us * Rmax + rec] : 0;
-  const int h = flat / N, t = flat % N;
-  const int64_t iw = ((int64_t)us * H + h) * N + t;
-  const int a = active ? aidx[iw] : 0;
-  const float g = active ? gam[iw] : 0.0f;
-  const T* X = reinterpret_cast<const T*>(side ? Vv : Kv) + (((int64_t)u * H + h) * N + t) * D;
-  const T* AX = reinterpret_cast<const T*>(cache + (int64_t)u * stride + (side ? off_av : off_ak)) + ((int64_t)h * A + a) * D;
-  float r[8];
-  float mn = INFINITY, mx = -INFINITY;
-  for (int e = 0; e < 8; ++e) {
-    const int d = 8 * j + e;
-    r[e] = active ? fmaf(-g, Elem<DT>::f(AX[d]), Elem<DT>::f(X[d])) : 0.0f;
-    mn = fminf(mn, r[e]);
-    mx = fmaxf(mx, r[e]);
+  const int rec0 = (blk * 16 + grp) * QG;
+  int flat[QG], a[QG];
+  float g[QG];
+#pragma unroll
+  for (int k = 0; k < QG; ++k) flat[k] = rec0 + k < R ? sel_list[(int64_t)us * Rmax + rec0 + k] : 0;
+#pragma unroll
+  for (int k = 0; k < QG; ++k) {
+    const int h = flat[k] / N, t = flat[k] % N;
+    const int64_t iw = ((int64_t)us * H + h) * N + t;
+    const bool act = rec0 + k < R;
+    a[k] = act ? aidx[iw] : 0;
+    g[k] = act ? gam[iw] : 0.0f;
   }
-  mn = fminf(mn, __shfl_xor(mn, 1, 64)); mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-  mn = fminf(mn, __shfl_xor(mn, 2, 64)); mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-  const uint16_t zb = f2h_sat(mn), sb = f2h_sat((mx - mn) / 3.0f);
-  const float z = h2f(zb), sc = h2f(sb);
-  for (int e = 0; e < 8; ++e) {
-    int code = 0;
-    if (sc > 0.0f) code = (int)fminf(3.0f, fmaxf(0.0f, rintf((r[e] - z) / sc)));
-    codes_s[grp][8 * j + e] = (uint8_t)code;
+  float r[QG][8];
+#pragma unroll
+  for (int k = 0; k < QG; ++k) {
+    const int h = flat[k] / N, t = flat[k] % N;
+    const T* X = reinterpret_cast<const T*>(side ? Vv : Kv) + (((int64_t)u * H + h) * N + t) * D + 8 * j;
+    const T* AX = reinterpret_cast<const T*>(cache + (int64_t)u * stride + (side ? off_av : off_ak)) +
+                  ((int64_t)h * A + a[k]) * D + 8 * j;
+    T xv[8], av[8];
+    if constexpr (DT == ANCHORKV_BF16) {
+      const uint4 x4 = *reinterpret_cast<const uint4*>(X), a4 = *reinterpret_cast<const uint4*>(AX);
+      __builtin_memcpy(xv, &x4, 16);
+      __builtin_memcpy(av, &a4, 16);
+    } else {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(X), x1 = *reinterpret_cast<const uint4*>(X + 4);
+      const uint4 a0 = *reinterpret_cast<const uint4*>(AX), a1 = *reinterpret_cast<const uint4*>(AX + 4);
+      __builtin_memcpy(xv, &x0, 16); __builtin_memcpy(xv + 4, &x1, 16);
+      __builtin_memcpy(av, &a0, 16); __builtin_memcpy(av + 4, &a1, 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[k][e] = fmaf(-g[k], Elem<DT>::f(av[e]), Elem<DT>::f(xv[e]));
+  }
+  uint16_t zb[QG], sb[QG];
+#pragma unroll
+  for (int k = 0; k < QG; ++k) {
+    float mn = r[k][0], mx = r[k][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) { mn = fminf(mn, r[k][e]); mx = fmaxf(mx, r[k][e]); }
+    mn = fminf(mn, __shfl_xor(mn, 1, 64)); mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    mn = fminf(mn, __shfl_xor(mn, 2, 64)); mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    zb[k] = f2h_sat(mn);
+    sb[k] = f2h_sat((mx - mn) / 3.0f);
+    const float z = h2f(zb[k]), sc = h2f(sb[k]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int code = 0;
+      if (sc > 0.0f) code = (int)fminf(3.0f, fmaxf(0.0f, rintf((r[k][e] - z) / sc)));
+      codes_s[grp][k][8 * j + e] = (uint8_t)code;
+    }
   }
   __syncthreads();
-  if (!active) return;
-  uint16_t w = 0;
-  for (int cc = 0; cc < 8; ++cc) w |= (uint16_t)(codes_s[grp][j + 16 * cc] << (2 * cc));
-  uint8_t* recp = cache + (int64_t)u * stride + (side ? off_rv : off_rk) + (int64_t)rec * kRecBytes;
-  reinterpret_cast<uint16_t*>(recp)[j] = w;
-  // group g's (scale, zero) lives in lanes 4g..4g+3; lane 4g writes it
-  if ((j & 3) == 0) reinterpret_cast<uint32_t*>(recp + 32)[j >> 2] = (uint32_t)sb | ((uint32_t)zb << 16);
+#pragma unroll
+  for (int k = 0; k < QG; ++k) {
+    if (rec0 + k >= R) break;
+    uint16_t wv = 0;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) wv |= (uint16_t)(codes_s[grp][k][j + 16 * cc] << (2 * cc));
+    uint8_t* recp = cache + (int64_t)u * stride + (side ? off_rv : off_rk) + (int64_t)(rec0 + k) * kRecBytes;
+    reinterpret_cast<uint16_t*>(recp)[j] = wv;
+    // group q's (scale, zero) lives in lanes 4q..4q+3; lane 4q writes it
+    if ((j & 3) == 0) reinterpret_cast<uint32_t*>(recp + 32)[j >> 2] = (uint32_t)sb[k] | ((uint32_t)zb[k] << 16);
+  }
 }
 
 // ------------------------------------------------------------ launch sequence
@@ -715,7 +779,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   AKV_CHECK_LAUNCH("k_topr_flag");
   prof_mark(st, "topr");
   if (R > 0) {
-    const int nblk = (R + 15) / 16;
+    const int nblk = (R + 16 * kQuantPerGroup - 1) / (16 * kQuantPerGroup);
     k_quant<DT><<<(unsigned)((int64_t)U * 2 * nblk), 256, 0, st>>>(
         K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_res_k, p.off_res_v, sel_list, Rmax,
         reinterpret_cast<const int*>(ws + w.aidx), reinterpret_cast<const float*>(ws + w.gam), H, N, A, R, nblk);

@@ -4,13 +4,27 @@
 // argument": x^_t = gamma_t x_a(t) + r~_t):
 //   logit_t = gamma^K_t <q, k_a> / sqrt(D) + [t in R_K] <q, r~^K_t> / sqrt(D)
 //   o = sum_t p_t (gamma^V_t v_a(t) + [t in R_V] r~^V_t) / sum_t p_t
-// computed without reconstructing K or V: the anchor logits <q, k_a> form a
-// per-head table S[g][a]; the value side scatters p_t gamma^V_t into
-// w[g][a(t)] and finishes with o = (w V_anchors + sum p r~^V) / l.  The
-// token stream is split into 1024-token-aligned ranges per (unit, head);
-// each range keeps its own online-softmax state and a combine kernel merges
-// them.  Exponentials are base 2 with log2(e)/sqrt(D) folded into S.
+// computed without reconstructing K or V (the paper's fused-decoder idea,
+// AnchorKV-adapted page "Adaptation notes"; the design here is our own):
+//  * the anchor logits <q, k_a> form a per-head table S[g][a] (LDS);
+//  * the value side scatters p_t gamma^V_t into w[g][a(t)] and finishes with
+//    o = (w V_anchors + sum p r~^V) / l in the combine kernel.  The scatter
+//    accumulates 64-bit fixed point (scale 2^21) with LDS integer atomics,
+//    which are an order of magnitude faster than LDS float atomics on this
+//    part and make the sum independent of order;
+//  * residual records are handled in batches on MFMA.  A code c enters as the
+//    exact bf16 value 128 + c (one AND+OR per pair of codes) and the constant
+//    part is cancelled exactly.  Keys: rows = records, columns = (q-head,
+//    group), so one 16x16 tile serves 4 q-heads x 4 groups.  Values: rows =
+//    (q-head, group), K = records, columns = coordinates; A = p * scale split
+//    into bf16 hi + lo.
+// One workgroup (8 waves) per (unit, head, 1024-token-aligned range); each
+// tile of 1024 tokens is one residual-offset chunk.  The running max is
+// shared by the workgroup and only raised (rescaling w, l and the
+// accumulators) when a tile exceeds it by more than 2^8.
 #include "device_common.hpp"
+
+#include <type_traits>
 
 namespace akv {
 
@@ -20,192 +34,465 @@ namespace akv {
     if (e_ != hipSuccess) return fail(ANCHORKV_E_HIP, "%s: %s", name, hipGetErrorString(e_)); \
   } while (0)
 
-constexpr int kMaxG = 16;
+constexpr int kMaxG = 8;          // q-heads per KV head supported by decode
+constexpr int kTile = 1024;       // tokens per tile (= residual-offset chunk)
+constexpr int kWaves = 8;         // waves per workgroup; 128 tokens per wave per tile
+constexpr uint32_t kCodeBias = 0x43004300u;  // bf16 pair (128, 128)
+constexpr float kFxScale = 2097152.0f;          // 2^21: fixed-point scale of the w scatter
+constexpr double kFxInv = 1.0 / 2097152.0;
 
-// S[g][a] = <q_g, k_a> * log2(e)/sqrt(D); qsum[g][grp] = sum of q over the group, same scale.
+// y (already scaled by 2^21) -> two's-complement 64-bit fixed point, any sign
+// and |y| < 2^62.
+__device__ __forceinline__ unsigned long long fx_general(float y) {
+  const float a = fabsf(y);
+  const float hi_f = floorf(a * 2.3283064365386963e-10f);  // 2^-32
+  const float lo_f = fmaf(hi_f, -4294967296.0f, a);           // exact, in [0, 2^32)
+  const unsigned long long v = ((unsigned long long)(unsigned)hi_f << 32) | (unsigned long long)(unsigned)rintf(lo_f);
+  return y < 0.0f ? 0ull - v : v;
+}
+
+// ---------------------------------------------------------------- S table
+// S[g][a] = <q_g, k_a> * log2(e)/sqrt(D).  One wave per anchor row.
 template <int DT>
 __global__ __launch_bounds__(256) void k_dec_stab(const void* qv, const uint8_t* cache, int64_t stride, int64_t off_ak,
-                                                 float* stab, float* qsum, int H, int G, int A, float c) {
+                                                 float* stab, int H, int G, int A, float c) {
   using T = typename Elem<DT>::T;
   constexpr int D = kHeadDim;
-  __shared__ float qs[kMaxG * D];
   const int h = blockIdx.x % H, u = blockIdx.x / H;
   const int64_t uh = (int64_t)u * H + h;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const T* q = reinterpret_cast<const T*>(qv) + uh * G * D;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = Elem<DT>::f(q[i]);
-  __syncthreads();
+  float q0[kMaxG], q1[kMaxG];
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) {
+    q0[g] = g < G ? Elem<DT>::f(q[g * D + lane]) : 0.0f;
+    q1[g] = g < G ? Elem<DT>::f(q[g * D + 64 + lane]) : 0.0f;
+  }
   const T* AK = reinterpret_cast<const T*>(cache + (int64_t)u * stride + off_ak) + (int64_t)h * A * D;
-  for (int i = threadIdx.x; i < G * A; i += blockDim.x) {
-    const int g = i / A, a = i % A;
-    const T* kr = AK + (int64_t)a * D;
-    float s = 0.0f;
-    for (int d = 0; d < D; ++d) s = fmaf(qs[g * D + d], Elem<DT>::f(kr[d]), s);
-    stab[uh * G * A + i] = s * c;
-  }
-  for (int i = threadIdx.x; i < G * 4; i += blockDim.x) {
-    const int g = i / 4, grp = i % 4;
-    float s = 0.0f;
-    for (int d = 0; d < 32; ++d) s += qs[g * D + grp * 32 + d];
-    qsum[uh * G * 4 + i] = s * c;
-  }
-}
-
-__device__ __forceinline__ void decode_record(const uint8_t* rec, float* r /*[128]*/) {
-  uint16_t w[16];
-  uint32_t sz[4];
-  const uint4* p = reinterpret_cast<const uint4*>(rec);
-  uint4 a = p[0], b = p[1], c = p[2];
-  __builtin_memcpy(w, &a, 16);
-  __builtin_memcpy(w + 8, &b, 16);
-  __builtin_memcpy(sz, &c, 16);
-  for (int j = 0; j < 16; ++j)
-    for (int cc = 0; cc < 8; ++cc) {
-      const int d = j + 16 * cc;
-      const int g = d >> 5;
-      const float sc = h2f((uint16_t)(sz[g] & 0xFFFFu)), z = h2f((uint16_t)(sz[g] >> 16));
-      r[d] = fmaf(sc, (float)((w[j] >> (2 * cc)) & 3u), z);
+  for (int a = wave; a < A; a += nw) {
+    const float k0 = Elem<DT>::f(AK[(int64_t)a * D + lane]), k1 = Elem<DT>::f(AK[(int64_t)a * D + 64 + lane]);
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g) {
+      if (g >= G) break;
+      const float s = wave_sum(fmaf(q0[g], k0, q1[g] * k1));
+      if (lane == 0) stab[(uh * G + g) * A + a] = s * c;
     }
+  }
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void k_dec_stream(const void* qv, const uint8_t* cache, int64_t stride,
-                                                   int64_t off_words, int64_t off_rk, int64_t off_rv, int64_t off_ck,
-                                                   int64_t off_cv, const float* stab, float2* part_ml, float* part_w,
-                                                   float* part_acc, int H, int G, int N, int A, int C, int S2,
-                                                   float c) {
+// ---------------------------------------------------------------- stream
+struct DecArgs {
+  const void* q;
+  const uint8_t* cache;
+  int64_t stride, off_words, off_rk, off_rv, off_ck, off_cv;
+  const float* stab;
+  float2* part_ml;
+  float* part_w;
+  float* part_acc;
+  int H, N, A, C, S2, cps, R_K, R_V;
+  float c;
+};
+
+// Record staging: KP 16-byte chunks per thread per side are prefetched, so a
+// tile stages up to 512*KP*16/48 records per side in LDS; records beyond that
+// are read from the cache directly.
+
+__device__ __forceinline__ bf16x8 u4_to_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return bits_to_frag(make_uint4(a, b, c, d));
+}
+
+template <int DT, int G, int KP, int DEPTH>
+__global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
+  constexpr int kPre = KP;
+  constexpr int kRecCap = 512 * KP * 16 / kRecBytes;
   using T = typename Elem<DT>::T;
+  using M = Mfma<ANCHORKV_BF16>;
   constexpr int D = kHeadDim;
-  extern __shared__ float dsm[];
-  float* S = dsm;                 // [G][A]
-  float* w = S + G * A;           // [G][A]
-  float* acc = w + G * A;         // [G][D]
-  float* qsc = acc + G * D;       // [G][D]
-  __shared__ float m_run[kMaxG], scale[kMaxG], tmax_w[4][kMaxG];
-  __shared__ int cnt_w[2][4];
-  __shared__ int any_rescale;
+  constexpr int NB = (4 * G + 15) / 16;          // 16-wide blocks of (q-head, group) pairs
+  constexpr bool QSPLIT = DT == ANCHORKV_F32;   // f32 queries enter the key MFMA as bf16 hi + lo
+  extern __shared__ float sm[];
+  const int A = a.A;
+  float* S = sm;                                                  // [G][A]
+  unsigned long long* wi = reinterpret_cast<unsigned long long*>(S + ((G * A + 1) & ~1));  // [G][A] fixed point
+  float* buf = reinterpret_cast<float*>(wi + G * A);             // [kTile][G]: key-residual logits, p of value-flagged tokens, [G][D]
+  uint4* kst = reinterpret_cast<uint4*>(buf + kTile * G);  // staged key records of the tile (kRecCap x 48 B)
+  uint4* vst = kst + 512 * kPre;                            // staged value records
+  __shared__ int cnt[kWaves][2];
+  __shared__ int offs[2][130];
+  __shared__ float tmax[kWaves][G];
+  __shared__ float zt_s[G * 4];
 
   int bid = blockIdx.x;
-  const int s = bid % S2; bid /= S2;
-  const int h = bid % H;
-  const int u = bid / H;
-  const int64_t uh = (int64_t)u * H + h;
+  const int sp = bid % a.S2; bid /= a.S2;
+  const int h = bid % a.H;
+  const int u = bid / a.H;
+  const int64_t uh = (int64_t)u * a.H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cps = (C + S2 - 1) / S2;
-  const int c0 = s * cps, c1 = min(C, c0 + cps);
-  const int t_beg = c0 * kChunk, t_end = min(N, c1 * kChunk);
-  const uint8_t* base = cache + (int64_t)u * stride;
-  const T* q = reinterpret_cast<const T*>(qv) + uh * G * D;
+  const int col = lane & 15, kg = lane >> 4;
+  const int c0 = sp * a.cps, c1 = min(a.C, c0 + a.cps);
+  const int t_beg = c0 * kTile, t_end = min(a.N, c1 * kTile);
+  const uint8_t* base = a.cache + (int64_t)u * a.stride;
+  const uint8_t* recK = base + a.off_rk;
+  const uint8_t* recV = base + a.off_rv;
+  const T* q = reinterpret_cast<const T*>(a.q) + uh * G * D;
 
-  for (int i = threadIdx.x; i < G * A; i += blockDim.x) { S[i] = stab[uh * G * A + i]; w[i] = 0.0f; }
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) { acc[i] = 0.0f; qsc[i] = Elem<DT>::f(q[i]) * c; }
-  if (threadIdx.x < kMaxG) m_run[threadIdx.x] = -INFINITY;
+  for (int i = threadIdx.x; i < G * A; i += blockDim.x) { S[i] = a.stab[uh * G * A + i]; wi[i] = 0ull; }
+  if (threadIdx.x < G * 4) zt_s[threadIdx.x] = 0.0f;
+  // record offsets of the range's chunks and of the chunk after the last one
+  const int nch = max(0, c1 - c0);
+  for (int i = threadIdx.x; i <= nch; i += blockDim.x) {
+    const int fl = h * a.C + c0 + i;
+    const bool last = fl >= a.H * a.C;
+    offs[0][i] = last ? a.R_K : reinterpret_cast<const int*>(base + a.off_ck)[fl];
+    offs[1][i] = last ? a.R_V : reinterpret_cast<const int*>(base + a.off_cv)[fl];
+  }
+
+  // Key-side B fragments: column kappa = 16*cb + col = 4*g + grp; in MFMA step
+  // st (= coordinate group st) the lane supplies q[g][j + 16c], j = 4kg + (e&3),
+  // c = 2st + (e>>2), when grp == st, zeros otherwise.
+  bf16x8 qB[NB][4], qBl[QSPLIT ? NB : 1][4];
+  float qsum[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    const int kap = 16 * cb + col;
+    const int g = kap >> 2, grp = kap & 3;
+    float qs = 0.0f;
+    if (g < G)
+      for (int d = 32 * grp; d < 32 * grp + 32; ++d) qs += Elem<DT>::f(q[g * D + d]);
+    qsum[cb] = qs;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint16_t vh[8], vl[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = (4 * kg + (e & 3)) + 16 * (2 * st + (e >> 2));
+        const float x = (g < G && grp == st) ? Elem<DT>::f(q[g * D + d]) : 0.0f;
+        vh[e] = f2bf(x);
+        vl[e] = f2bf(x - bf2f(vh[e]));
+      }
+      qB[cb][st] = u4_to_frag(vh[0] | (uint32_t)vh[1] << 16, vh[2] | (uint32_t)vh[3] << 16, vh[4] | (uint32_t)vh[5] << 16,
+                              vh[6] | (uint32_t)vh[7] << 16);
+      if constexpr (QSPLIT)
+        qBl[cb][st] = u4_to_frag(vl[0] | (uint32_t)vl[1] << 16, vl[2] | (uint32_t)vl[3] << 16,
+                                 vl[4] | (uint32_t)vl[5] << 16, vl[6] | (uint32_t)vl[7] << 16);
+    }
+  }
   __syncthreads();
 
-  const uint32_t* words = reinterpret_cast<const uint32_t*>(base + off_words) + (int64_t)h * N * 2;
-  int recK = 0, recV = 0;
-  if (c0 < C) {
-    recK = reinterpret_cast<const int*>(base + off_ck)[h * C + c0];
-    recV = reinterpret_cast<const int*>(base + off_cv)[h * C + c0];
-  }
-  float lp[kMaxG];
-  for (int g = 0; g < kMaxG; ++g) lp[g] = 0.0f;
+  float m_run[G], lacc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; lacc[g] = 0.0f; }
+  f32x4 vacc[NB][8];   // value side: row block rb (rows 4g + grp), column block cc (coordinates j + 16cc)
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] = f32x4{0, 0, 0, 0};
+  float zt[NB];        // value side: sum of p*zero - 128*(p*scale as fed to the MFMA) for row (rb, col)
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) zt[rb] = 0.0f;
 
-  for (int tb = t_beg; tb < t_end; tb += blockDim.x) {
-    const int t = tb + threadIdx.x;
-    const bool valid = t < t_end;
-    uint2 wd = valid ? reinterpret_cast<const uint2*>(words)[t] : make_uint2(0, 0);
-    const int aK = wd.x & 0x7FFF, aV = wd.y & 0x7FFF;
-    const bool fK = valid && (wd.x & 0x8000u), fV = valid && (wd.y & 0x8000u);
-    const float gK = h2f((uint16_t)(wd.x >> 16)), gV = h2f((uint16_t)(wd.y >> 16));
-    // ranks of flagged tokens within the tile (block-wide, in token order)
-    const unsigned long long bK = __ballot(fK), bV = __ballot(fV);
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (lane == 0) { cnt_w[0][wave] = __popcll(bK); cnt_w[1][wave] = __popcll(bV); }
-    __syncthreads();
-    int preK = 0, preV = 0, totK = 0, totV = 0;
-    for (int wv = 0; wv < 4; ++wv) {
-      if (wv < wave) { preK += cnt_w[0][wv]; preV += cnt_w[1][wv]; }
-      totK += cnt_w[0][wv]; totV += cnt_w[1][wv];
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(base + a.off_words) + (int64_t)h * a.N * 2;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // Prefetch (registers), DEPTH tiles ahead: the thread's two pointer-word
+  // pairs and its share of the tile's key / value record bytes (16-byte
+  // chunks).  The tile loop is unrolled by DEPTH so ring slots stay static.
+  uint2 pwa[DEPTH], pwb[DEPTH];
+  uint4 pk[DEPTH][kPre], pv_[DEPTH][kPre];
+  auto prefetch = [&](int i, uint2& wa_, uint2& wb_, uint4* k_, uint4* v_) {
+    const int tt = t_beg + i * kTile + wave * 128 + 2 * lane;
+    wa_ = tt < t_end ? *reinterpret_cast<const uint2*>(words + (int64_t)tt * 2) : make_uint2(0, 0);
+    wb_ = tt + 1 < t_end ? *reinterpret_cast<const uint2*>(words + (int64_t)tt * 2 + 2) : make_uint2(0, 0);
+    const int nk = 3 * min(kRecCap, offs[0][i + 1] - offs[0][i]);
+    const int nv = 3 * min(kRecCap, offs[1][i + 1] - offs[1][i]);
+    const uint4* gk = reinterpret_cast<const uint4*>(recK + (int64_t)offs[0][i] * kRecBytes);
+    const uint4* gv = reinterpret_cast<const uint4*>(recV + (int64_t)offs[1][i] * kRecBytes);
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int ci = threadIdx.x + 512 * k;
+      k_[k] = ci < nk ? gk[ci] : make_uint4(0, 0, 0, 0);
+      v_[k] = ci < nv ? gv[ci] : make_uint4(0, 0, 0, 0);
     }
-    const int rk = recK + preK + __popcll(bK & below);
-    const int rv = recV + preV + __popcll(bV & below);
+  };
+  __syncthreads();  // offs visible
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nch) prefetch(d, pwa[d], pwb[d], pk[d], pv_[d]);
 
-    float sl[kMaxG];
-    for (int g = 0; g < G; ++g) sl[g] = valid ? gK * S[g * A + aK] : -INFINITY;
-    if (fK) {
-      float r[D];
-      decode_record(base + off_rk + (int64_t)rk * kRecBytes, r);
-      for (int g = 0; g < G; ++g) {
-        float dsum = 0.0f;
-        for (int d = 0; d < D; ++d) dsum = fmaf(qsc[g * D + d], r[d], dsum);
-        sl[g] += dsum;
+  for (int base_it = 0; base_it < nch; base_it += DEPTH) {
+#pragma unroll
+  for (int dslot = 0; dslot < DEPTH; ++dslot) {
+    const int it = base_it + dslot;
+    if (it >= nch) break;
+    const int tile = t_beg + it * kTile;
+    const int rk0 = offs[0][it], rv0 = offs[1][it];
+    // stage this tile's records (the previous tile ended with a barrier)
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) { kst[threadIdx.x + 512 * k] = pk[dslot][k]; vst[threadIdx.x + 512 * k] = pv_[dslot][k]; }
+    const uint2 wa = pwa[dslot], wb = pwb[dslot];
+    if (it + DEPTH < nch) prefetch(it + DEPTH, pwa[dslot], pwb[dslot], pk[dslot], pv_[dslot]);
+    // ---- A: pointer words of the lane's two tokens
+    const int t0 = tile + wave * 128 + 2 * lane;
+    const bool v0 = t0 < t_end, v1 = t0 + 1 < t_end;
+    const int aK0 = wa.x & 0x7FFF, aV0 = wa.y & 0x7FFF, aK1 = wb.x & 0x7FFF, aV1 = wb.y & 0x7FFF;
+    const bool fK0 = v0 && (wa.x & 0x8000u), fV0 = v0 && (wa.y & 0x8000u);
+    const bool fK1 = v1 && (wb.x & 0x8000u), fV1 = v1 && (wb.y & 0x8000u);
+    const float gK0 = h2f((uint16_t)(wa.x >> 16)), gV0 = h2f((uint16_t)(wa.y >> 16));
+    const float gK1 = h2f((uint16_t)(wb.x >> 16)), gV1 = h2f((uint16_t)(wb.y >> 16));
+    const unsigned long long bK0 = __ballot(fK0), bK1 = __ballot(fK1), bV0 = __ballot(fV0), bV1 = __ballot(fV1);
+    const int nK = __popcll(bK0) + __popcll(bK1), nV = __popcll(bV0) + __popcll(bV1);
+    if (lane == 0) { cnt[wave][0] = nK; cnt[wave][1] = nV; }
+    lds_barrier();
+    int baseK = 0, baseV = 0;
+    for (int w2 = 0; w2 < wave; ++w2) { baseK += cnt[w2][0]; baseV += cnt[w2][1]; }
+    const int rK0 = baseK + __popcll(bK0 & below) + __popcll(bK1 & below), rK1 = rK0 + (fK0 ? 1 : 0);
+    const int rV0 = baseV + __popcll(bV0 & below) + __popcll(bV1 & below), rV1 = rV0 + (fV0 ? 1 : 0);
+
+    // ---- B: key-residual logits of this wave's records, 16 per MFMA tile.
+    // Batches whose records are all staged read LDS only; the rest (tiles with
+    // more flagged tokens than the staging holds) read the cache directly in a
+    // separate loop, so that loop's waits on global loads do not stall the
+    // prefetch of the next tile in the common case.
+    auto kbatch = [&](int b0, auto from_lds) {
+      constexpr bool LDS = decltype(from_lds)::value;
+      auto rec = [&](int rr) -> const uint8_t* {
+        return LDS ? reinterpret_cast<const uint8_t*>(kst) + rr * kRecBytes : recK + (int64_t)(rk0 + rr) * kRecBytes;
+      };
+      const int i = b0 + col;
+      uint2 x = make_uint2(0, 0);
+      if (i < nK) x = *reinterpret_cast<const uint2*>(rec(baseK + i) + 8 * kg);
+      bf16x8 af[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int s0 = 4 * st, s1 = 4 * st + 2;
+        af[st] = u4_to_frag(((x.x >> s0) & 0x00030003u) | kCodeBias, ((x.y >> s0) & 0x00030003u) | kCodeBias,
+                            ((x.x >> s1) & 0x00030003u) | kCodeBias, ((x.y >> s1) & 0x00030003u) | kCodeBias);
       }
-    }
-    // tile max per q-head, lazy rescale when it grows by more than 2^8
-    for (int g = 0; g < G; ++g) {
-      const float mx = wave_max(sl[g]);
-      if (lane == 0) tmax_w[wave][g] = mx;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int any = 0;
-      for (int g = 0; g < G; ++g) {
-        const float tm = fmaxf(fmaxf(tmax_w[0][g], tmax_w[1][g]), fmaxf(tmax_w[2][g], tmax_w[3][g]));
-        float f = 1.0f;
-        if (tm > m_run[g] + 8.0f) {
-          f = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
-          m_run[g] = tm;
-          any = 1;
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        f32x4 cacc = {0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          cacc = M::mma(af[st], qB[cb][st], cacc);
+          if constexpr (QSPLIT) cacc = M::mma(af[st], qBl[cb][st], cacc);
         }
-        scale[g] = f;
+        const int kap = 16 * cb + col, g = kap >> 2, grp = kap & 3;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ii = b0 + 4 * kg + r;
+          float val = 0.0f;
+          if (ii < nK) {
+            const uint32_t sz = *reinterpret_cast<const uint32_t*>(rec(baseK + ii) + 32 + 4 * grp);
+            const float sc = h2f((uint16_t)(sz & 0xFFFFu)), z = h2f((uint16_t)(sz >> 16));
+            val = fmaf(sc, cacc[r], (z - 128.0f * sc) * qsum[cb]);
+          }
+          val = quad_sum(val);
+          if (ii < nK && grp == 0 && g < G) buf[(baseK + ii) * G + g] = val * a.c;
+        }
       }
-      any_rescale = any;
+    };
+    {
+      const int nfast = max(0, min(nK, kRecCap - baseK));  // records of this wave that are staged
+      int b0 = 0;
+      for (; b0 + 16 <= nfast; b0 += 16) kbatch(b0, std::true_type{});
+      if (b0 < nK) {
+        if (baseK + nK <= kRecCap) kbatch(b0, std::true_type{});
+        else for (; b0 < nK; b0 += 16) kbatch(b0, std::false_type{});
+      }
     }
-    __syncthreads();
-    if (any_rescale) {
-      for (int i = threadIdx.x; i < G * A; i += blockDim.x) w[i] *= scale[i / A];
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x) acc[i] *= scale[i / D];
-      for (int g = 0; g < G; ++g) lp[g] *= scale[g];
-      __syncthreads();
-    }
-    float p[kMaxG];
+    lds_barrier();
+
+    // ---- C: logits of the lane's two tokens; tile max per q-head
+    float s0[G], s1[G];
+#pragma unroll
     for (int g = 0; g < G; ++g) {
-      p[g] = valid ? exp2_fast(sl[g] - m_run[g]) : 0.0f;
-      lp[g] += p[g];
-      if (valid) atomicAdd(&w[g * A + aV], p[g] * gV);
+      s0[g] = v0 ? gK0 * S[g * A + aK0] + (fK0 ? buf[rK0 * G + g] : 0.0f) : -INFINITY;
+      s1[g] = v1 ? gK1 * S[g * A + aK1] + (fK1 ? buf[rK1 * G + g] : 0.0f) : -INFINITY;
+      const float mx = wave_max(fmaxf(s0[g], s1[g]));
+      if (lane == 0) tmax[wave][g] = mx;
     }
-    if (fV) {
-      float r[D];
-      decode_record(base + off_rv + (int64_t)rv * kRecBytes, r);
-      for (int d = 0; d < D; ++d)
-        for (int g = 0; g < G; ++g) atomicAdd(&acc[g * D + d], p[g] * r[d]);
+    lds_barrier();
+    // ---- D: lazy rescale (every thread takes the same decision)
+    bool any = false;
+    float fct[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float tm = tmax[0][g];
+      for (int w2 = 1; w2 < kWaves; ++w2) tm = fmaxf(tm, tmax[w2][g]);
+      fct[g] = 1.0f;
+      if (tm > m_run[g] + 8.0f) {
+        fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
+        m_run[g] = tm;
+        any = true;
+      }
     }
-    recK += totK;
-    recV += totV;
-    __syncthreads();
+    if (any) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        lacc[g] *= fct[g];
+        if (fct[g] != 1.0f)
+          for (int i = threadIdx.x; i < A; i += blockDim.x)
+            wi[g * A + i] = (unsigned long long)__double2ll_rn((double)(long long)wi[g * A + i] * (double)fct[g]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        const int g = 4 * rb + kg;  // accumulator rows 16rb + 4kg + r -> q-head 4rb + kg
+        float f = 1.0f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vacc[rb][cc][r] *= f;
+        const int gz = (16 * rb + col) >> 2;  // z row (rb, col)
+        float fz = 1.0f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) fz = (gg == gz) ? fct[gg] : fz;
+        zt[rb] *= fz;
+      }
+      lds_barrier();
+    }
+    // ---- E: probabilities, scatter p*gamma into w, keep p of value-flagged tokens
+    // p <= 2^8 (lazy rescale), so gamma in [0, 8) keeps p*gamma*2^21 in [0, 2^32).
+    const float gs0 = gV0 * kFxScale, gs1 = gV1 * kFxScale;
+    const bool fast = __all((!v0 || (gV0 >= 0.0f && gV0 < 8.0f)) && (!v1 || (gV1 >= 0.0f && gV1 < 8.0f)));
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float p0 = v0 ? exp2_fast(s0[g] - m_run[g]) : 0.0f;
+      const float p1 = v1 ? exp2_fast(s1[g] - m_run[g]) : 0.0f;
+      lacc[g] += p0 + p1;
+      unsigned long long x0, x1;
+      if (fast) {
+        x0 = (unsigned long long)(unsigned)rintf(p0 * gs0);
+        x1 = (unsigned long long)(unsigned)rintf(p1 * gs1);
+      } else {
+        x0 = fx_general(p0 * gs0);
+        x1 = fx_general(p1 * gs1);
+      }
+      if (v0) atomicAdd(&wi[g * A + aV0], x0);
+      if (v1) atomicAdd(&wi[g * A + aV1], x1);
+      if (fV0) buf[rV0 * G + g] = p0;
+      if (fV1) buf[rV1 * G + g] = p1;
+    }
+    lds_barrier();
+
+    // ---- F: value residuals of this wave's records, 32 per MFMA K-step
+    // (staged records from LDS; overflow records from the cache in a separate loop)
+    auto vbatch = [&](int b0, auto from_lds) {
+      constexpr bool LDS = decltype(from_lds)::value;
+      auto rec = [&](int tr) -> const uint8_t* {
+        return LDS ? reinterpret_cast<const uint8_t*>(vst) + tr * kRecBytes : recV + (int64_t)(rv0 + tr) * kRecBytes;
+      };
+      uint32_t pr[4];  // code words of coordinate column `col`, record pairs
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int r0 = b0 + 8 * kg + 2 * e2;
+        uint32_t w0 = 0, w1 = 0;
+        if (r0 < nV) w0 = *reinterpret_cast<const uint16_t*>(rec(baseV + r0) + 2 * col);
+        if (r0 + 1 < nV) w1 = *reinterpret_cast<const uint16_t*>(rec(baseV + r0 + 1) + 2 * col);
+        pr[e2] = w0 | (w1 << 16);
+      }
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        // A operand: row (4g + grp) = 16rb + col, records b0 + 8kg + e
+        const int g = (16 * rb + col) >> 2, grp = col & 3;
+        uint32_t hp[4], lp[4];
+        float zsum = zt[rb];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int rr = b0 + 8 * kg + e;
+          float pv = 0.0f, sc = 0.0f, z = 0.0f;
+          if (rr < nV && g < G) {
+            pv = buf[(baseV + rr) * G + g];
+            const uint32_t sz = *reinterpret_cast<const uint32_t*>(rec(baseV + rr) + 32 + 4 * grp);
+            sc = h2f((uint16_t)(sz & 0xFFFFu));
+            z = h2f((uint16_t)(sz >> 16));
+          }
+          const float ps = pv * sc;
+          const uint16_t hb = f2bf(ps);
+          const float hf = bf2f(hb);
+          const uint16_t lb = f2bf(ps - hf);
+          zsum = fmaf(pv, z, zsum);
+          zsum = fmaf(-128.0f, hf + bf2f(lb), zsum);
+          if (e & 1) { hp[e >> 1] |= (uint32_t)hb << 16; lp[e >> 1] |= (uint32_t)lb << 16; }
+          else { hp[e >> 1] = hb; lp[e >> 1] = lb; }
+        }
+        zt[rb] = zsum;
+        const bf16x8 ahi = u4_to_frag(hp[0], hp[1], hp[2], hp[3]);
+        const bf16x8 alo = u4_to_frag(lp[0], lp[1], lp[2], lp[3]);
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const int sh = 2 * cc;
+          const bf16x8 bfr = u4_to_frag(((pr[0] >> sh) & 0x00030003u) | kCodeBias, ((pr[1] >> sh) & 0x00030003u) | kCodeBias,
+                                        ((pr[2] >> sh) & 0x00030003u) | kCodeBias, ((pr[3] >> sh) & 0x00030003u) | kCodeBias);
+          vacc[rb][cc] = M::mma(ahi, bfr, vacc[rb][cc]);
+          vacc[rb][cc] = M::mma(alo, bfr, vacc[rb][cc]);
+        }
+      }
+    };
+    {
+      const int nfast = max(0, min(nV, kRecCap - baseV));
+      int b0 = 0;
+      for (; b0 + 32 <= nfast; b0 += 32) vbatch(b0, std::true_type{});
+      if (b0 < nV) {
+        if (baseV + nV <= kRecCap) vbatch(b0, std::true_type{});
+        else for (; b0 < nV; b0 += 32) vbatch(b0, std::false_type{});
+      }
+    }
+    lds_barrier();  // staged records and buf are reused by the next tile
   }
-  // write this range's state
+  }
+
+  // ---- epilogue: reduce over lanes and waves, write this range's partial state
+#pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float l = wave_sum(lp[g]);
-    if (lane == 0) tmax_w[wave][g] = l;
+    const float l = wave_sum(lacc[g]);
+    if (lane == 0) tmax[wave][g] = l;
+  }
+  float* accs = buf;  // [G][D]
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) accs[i] = 0.0f;
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    float z = zt[rb];
+    z += __shfl_xor(z, 16, 64);
+    z += __shfl_xor(z, 32, 64);
+    const int g = (16 * rb + col) >> 2;
+    if (kg == 0 && g < G) atomicAdd(&zt_s[g * 4 + (col & 3)], z);
+    // lane (col j, kg) of column block cc holds rows 16rb + 4kg + r = (q-head 4rb + kg, group r);
+    // only group r == cc/2 covers coordinate j + 16cc.
+    const int gq = 4 * rb + kg;
+    if (gq < G)
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) atomicAdd(&accs[gq * D + col + 16 * cc], vacc[rb][cc][cc >> 1]);
   }
   __syncthreads();
-  const int64_t ps = uh * S2 + s;
+  const int64_t ps = uh * a.S2 + sp;
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
-    part_ml[ps * G + g] = make_float2(m_run[g], tmax_w[0][g] + tmax_w[1][g] + tmax_w[2][g] + tmax_w[3][g]);
+    float l = 0.0f;
+    for (int w2 = 0; w2 < kWaves; ++w2) l += tmax[w2][g];
+    float m = -INFINITY;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) m = (gg == g) ? m_run[gg] : m;
+    a.part_ml[ps * G + g] = make_float2(m, l);
   }
-  for (int i = threadIdx.x; i < G * A; i += blockDim.x) part_w[ps * G * A + i] = w[i];
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) part_acc[ps * G * D + i] = acc[i];
+  for (int i = threadIdx.x; i < G * A; i += blockDim.x) a.part_w[ps * G * A + i] = (float)((double)(long long)wi[i] * kFxInv);
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+    a.part_acc[ps * G * D + i] = accs[i] + zt_s[(i / D) * 4 + (i % D) / 32];
 }
 
+// ---------------------------------------------------------------- combine
+// Per (unit, head): merge the ranges' (m, l, w, acc) and finish
+// o = (sum_a W[g][a] v_a + ACC[g]) / L with W staged in LDS.
 template <int DT>
 __global__ __launch_bounds__(256) void k_dec_combine(const uint8_t* cache, int64_t stride, int64_t off_av,
                                                     const float2* part_ml, const float* part_w,
                                                     const float* part_acc, float* o, int H, int G, int A, int S2) {
   using T = typename Elem<DT>::T;
   constexpr int D = kHeadDim;
-  extern __shared__ float f_s[];  // [G][S2]
+  extern __shared__ float Wsum[];  // [G][A]
+  __shared__ float f_s[kMaxG][64];
   __shared__ float Linv[kMaxG];
   const int h = blockIdx.x % H, u = blockIdx.x / H;
   const int64_t uh = (int64_t)u * H + h;
@@ -217,24 +504,63 @@ __global__ __launch_bounds__(256) void k_dec_combine(const uint8_t* cache, int64
     for (int s = 0; s < S2; ++s) {
       const float2 v = part_ml[(uh * S2 + s) * G + g];
       const float f = v.x == -INFINITY ? 0.0f : exp2_fast(v.x - M);
-      f_s[g * S2 + s] = f;
+      f_s[g][s] = f;
       L += f * v.y;
     }
     Linv[g] = 1.0f / L;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * A; i += blockDim.x) {
+    const int g = i / A;
+    float acc = 0.0f;
+    for (int s = 0; s < S2; ++s) acc = fmaf(f_s[g][s], part_w[(uh * S2 + s) * G * A + i], acc);
+    Wsum[i] = acc;
   }
   __syncthreads();
   const T* AV = reinterpret_cast<const T*>(cache + (int64_t)u * stride + off_av) + (int64_t)h * A * D;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int g = i / D, d = i % D;
     float acc = 0.0f;
-    for (int s = 0; s < S2; ++s) acc = fmaf(f_s[g * S2 + s], part_acc[((uh * S2 + s) * G + g) * D + d], acc);
-    for (int a = 0; a < A; ++a) {
-      float wa = 0.0f;
-      for (int s = 0; s < S2; ++s) wa = fmaf(f_s[g * S2 + s], part_w[((uh * S2 + s) * G + g) * A + a], wa);
-      acc = fmaf(wa, Elem<DT>::f(AV[(int64_t)a * D + d]), acc);
-    }
+    for (int s = 0; s < S2; ++s) acc = fmaf(f_s[g][s], part_acc[(uh * S2 + s) * G * D + i], acc);
+    for (int aa = 0; aa < A; ++aa) acc = fmaf(Wsum[g * A + aa], Elem<DT>::f(AV[(int64_t)aa * D + d]), acc);
     o[(uh * G + g) * D + d] = acc * Linv[g];
   }
+}
+
+// Raise a kernel's dynamic-LDS limit to `bytes` (once per larger value).
+static int set_dyn_lds(const void* fn, size_t bytes, size_t* done) {
+  if (bytes <= *done) return 0;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ANCHORKV_E_SHAPE, "decode: %zu bytes of LDS not available for this shape", bytes);
+  }
+  *done = bytes;
+  return 0;
+}
+
+static size_t stream_lds(int G, int A, int KP) {
+  return sizeof(float) * (((size_t)G * A + 1) & ~(size_t)1) + 8 * (size_t)G * A + sizeof(float) * (size_t)kTile * G +
+         2 * 512 * (size_t)KP * sizeof(uint4);
+}
+constexpr size_t kLdsLimit = 156 * 1024;
+
+template <int DT, int G, int KP, int DEPTH>
+static int launch_stream_kp(const DecArgs& a, unsigned grid, hipStream_t st) {
+  static size_t done = 0;
+  const size_t lds = stream_lds(G, a.A, KP);
+  if (lds > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
+  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G, KP, DEPTH>), lds, &done)) return rc;
+  k_dec_stream<DT, G, KP, DEPTH><<<grid, 64 * kWaves, lds, st>>>(a);
+  AKV_CHECK_LAUNCH("k_dec_stream");
+  return 0;
+}
+
+// Up to 4 q-heads per KV head: 3 staged chunks per side (512 records) and two
+// tiles of prefetch in flight; more q-heads: 1 staged chunk (170 records).
+template <int DT, int G>
+static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
+  if constexpr (G <= 4) return launch_stream_kp<DT, G, 3, 2>(a, grid, st);
+  else return launch_stream_kp<DT, G, 1, 2>(a, grid, st);
 }
 
 template <int DT>
@@ -243,29 +569,44 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   const uint8_t* cache = reinterpret_cast<const uint8_t*>(cache_v);
   uint8_t* ws = reinterpret_cast<uint8_t*>(ws_v);
   const DecodeWs w = decode_ws_layout(p);
-  const int U = p.units, H = p.H, G = p.G, A = p.A, N = p.N, C = p.n_chunks, S2 = w.S2;
+  const int U = p.units, H = p.H, G = p.G, A = p.A, S2 = w.S2;
   if (G > kMaxG) return fail(ANCHORKV_E_SHAPE, "decode supports q_per_kv <= %d", kMaxG);
-  const size_t lds = sizeof(float) * (2 * (size_t)G * A + 2 * (size_t)G * kHeadDim);
-  if (lds > 150 * 1024) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
+  if (S2 > 64) return fail(ANCHORKV_E_SHAPE, "decode: too many splits");
+  if (stream_lds(G, A, 1) > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
+  if (p.n_chunks > 128 * S2) return fail(ANCHORKV_E_SHAPE, "decode: too many chunks per range");
+  const size_t lds_c = sizeof(float) * (size_t)G * A;
   const float c = kLog2e / sqrtf((float)kHeadDim);
   float* stab = reinterpret_cast<float*>(ws + w.stab);
-  float* qsum = reinterpret_cast<float*>(ws + w.qsum);
+  static size_t cdone = 0;
+  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_combine<DT>), lds_c, &cdone)) return rc;
   prof_call_begin(st);
-  k_dec_stab<DT><<<(unsigned)(U * H), 256, 0, st>>>(q, cache, p.unit_stride, p.off_anchor_k, stab, qsum, H, G, A, c);
+  k_dec_stab<DT><<<(unsigned)(U * H), 256, 0, st>>>(q, cache, p.unit_stride, p.off_anchor_k, stab, H, G, A, c);
   AKV_CHECK_LAUNCH("k_dec_stab");
   prof_mark(st, "dec_stab");
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dec_stream<DT>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
-    return fail(ANCHORKV_E_HIP, "decode: cannot raise the dynamic LDS limit");
-  k_dec_stream<DT><<<(unsigned)((int64_t)U * H * S2), 256, lds, st>>>(
-      q, cache, p.unit_stride, p.off_words, p.off_res_k, p.off_res_v, p.off_chunk_k, p.off_chunk_v, stab,
-      reinterpret_cast<float2*>(ws + w.part_ml), reinterpret_cast<float*>(ws + w.part_w),
-      reinterpret_cast<float*>(ws + w.part_acc), H, G, N, A, C, S2, c);
-  AKV_CHECK_LAUNCH("k_dec_stream");
+  DecArgs a;
+  a.q = q; a.cache = cache; a.stride = p.unit_stride; a.off_words = p.off_words; a.off_rk = p.off_res_k;
+  a.off_rv = p.off_res_v; a.off_ck = p.off_chunk_k; a.off_cv = p.off_chunk_v; a.stab = stab;
+  a.part_ml = reinterpret_cast<float2*>(ws + w.part_ml);
+  a.part_w = reinterpret_cast<float*>(ws + w.part_w);
+  a.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
+  a.H = H; a.N = p.N; a.A = A; a.C = p.n_chunks; a.S2 = S2; a.cps = (p.n_chunks + S2 - 1) / S2; a.c = c;
+  a.R_K = p.R_K; a.R_V = p.R_V;
+  const unsigned grid = (unsigned)((int64_t)U * H * S2);
+  int rc = 0;
+  switch (G) {
+    case 1: rc = launch_stream<DT, 1>(a, grid, st); break;
+    case 2: rc = launch_stream<DT, 2>(a, grid, st); break;
+    case 3: rc = launch_stream<DT, 3>(a, grid, st); break;
+    case 4: rc = launch_stream<DT, 4>(a, grid, st); break;
+    case 5: rc = launch_stream<DT, 5>(a, grid, st); break;
+    case 6: rc = launch_stream<DT, 6>(a, grid, st); break;
+    case 7: rc = launch_stream<DT, 7>(a, grid, st); break;
+    default: rc = launch_stream<DT, 8>(a, grid, st); break;
+  }
+  if (rc) return rc;
   prof_mark(st, "dec_stream");
-  k_dec_combine<DT><<<(unsigned)(U * H), 256, sizeof(float) * G * S2, st>>>(
-      cache, p.unit_stride, p.off_anchor_v, reinterpret_cast<const float2*>(ws + w.part_ml),
-      reinterpret_cast<const float*>(ws + w.part_w), reinterpret_cast<const float*>(ws + w.part_acc), o, H, G, A, S2);
+  k_dec_combine<DT><<<(unsigned)(U * H), 256, lds_c, st>>>(
+      cache, p.unit_stride, p.off_anchor_v, a.part_ml, a.part_w, a.part_acc, o, H, G, A, S2);
   AKV_CHECK_LAUNCH("k_dec_combine");
   prof_mark(st, "dec_combine");
   return 0;

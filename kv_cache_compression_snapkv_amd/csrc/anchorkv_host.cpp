@@ -74,7 +74,6 @@ DecodeWs decode_ws_layout(const anchorkv_plan_info& p) {
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = round_up(off + bytes, 256); return o; };
   w.stab = take(4 * U * H * G * A);
-  w.qsum = take(4 * U * H * G * 4);
   w.part_ml = take(8 * U * H * w.S2 * G);
   w.part_w = take(4 * U * H * w.S2 * G * A);
   w.part_acc = take(4 * U * H * w.S2 * G * D);

@@ -57,7 +57,6 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p);
 struct DecodeWs {
   int S2;          // token splits per (unit, head); boundaries on 1024-token chunks
   int64_t stab;    // f32 [U][H][G][A]   <q_g, k_a> * log2(e)/sqrt(D)
-  int64_t qsum;    // f32 [U][H][G][4]   per-group sums of q (times log2(e)/sqrt(D))
   int64_t part_ml; // float2 [U][H][S2][G]
   int64_t part_w;  // f32 [U][H][S2][G][A]
   int64_t part_acc; // f32 [U][H][S2][G][D]

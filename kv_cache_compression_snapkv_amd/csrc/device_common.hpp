@@ -93,15 +93,52 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
   lo = bits_to_frag(ll);
 }
 
+// Cross-lane moves inside a row of 16 lanes with DPP (plain VALU, no LDS).
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;   // quad_perm(2,3,0,1)
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+// Sum / max over each group of 4 lanes (l & ~3 .. l | 3); every lane gets it.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  return v + dpp<kDppXor2>(v);
+}
+// Sum / max over each row of 16 lanes; every lane gets it.
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<kDppRor8>(v);
+  v += dpp<kDppRor4>(v);
+  return quad_sum(v);
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp<kDppRor8>(v));
+  v = fmaxf(v, dpp<kDppRor4>(v));
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  return fmaxf(v, dpp<kDppXor2>(v));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Whole-wave sum / max (wave-uniform result), fixed combination order.
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = row_sum(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row_max(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier for LDS communication only: waits for this wave's LDS
+// (and scalar) operations, not for outstanding global loads, so loads issued
+// ahead (prefetch) keep flying across it.  Global memory is not ordered by it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 }  // namespace akv

@@ -175,17 +175,25 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
     if constexpr (MODE == OBS_UTIL) {
       if (threadIdx.x < 64) {
         const int t = t0 + threadIdx.x;
-        float g = 0.0f, vv = 0.0f;
-        if (t < k1) {
-          g = a.gam[((int64_t)u * 2 * H + h) * N + t];
-          const T* vr = Vp + (int64_t)t * D;
-          for (int d = 0; d < D; ++d) { float x = Elem<DT>::f(vr[d]); vv = fmaf(x, x, vv); }
-        }
-        gam_s[threadIdx.x] = g;
-        vv_s[threadIdx.x] = vv;
+        gam_s[threadIdx.x] = t < k1 ? a.gam[((int64_t)u * 2 * H + h) * N + t] : 0.0f;
       }
     }
     __syncthreads();
+    if constexpr (MODE == OBS_UTIL) {
+      // ||v||^2 per key from the staged tile: 4 consecutive threads per key
+      for (int kk = threadIdx.x >> 2; kk < 64; kk += blockDim.x >> 2) {
+        const int part = threadIdx.x & 3;
+        float vv = 0.0f;
+        for (int d = part * (D / 4); d < (part + 1) * (D / 4); ++d) {
+          const float x = Elem<DT>::f(Vs[kk * LDK + d]);
+          vv = fmaf(x, x, vv);
+        }
+        vv += __shfl_xor(vv, 1, 64);
+        vv += __shfl_xor(vv, 2, 64);
+        if (part == 0) vv_s[kk] = vv;
+      }
+      __syncthreads();
+    }
 
     float colsum[4][4];
     for (int kb = 0; kb < 4; ++kb)
