@@ -149,8 +149,9 @@ int anchorkv_compress(const anchorkv_plan_info* plan, const void* K, const void*
  * inspection in tests: [0] score f32 [U][H][N]; [1] m,1/l float2 [U][H][GQp];
  * [2] o f32 [U][H][GQp][D]; [3] utilities f32 [U][2][H][N] (-1 for anchors);
  * [4] unrounded gamma f32 [U][2][H][N]; [5] residual norm^2 f32 [U][2][H][N];
- * [6] anchor index int32 [U][2][H][N].  GQp = H*... padded query count
- * returned in out[7].  Returns 0 or E_ARG. */
+ * [6] anchor index int32 [U][2][H][N].  out[7] = GQp, the number of
+ * observation queries per KV head (q_per_kv * n_obs) rounded up to a multiple
+ * of 16; query row g*n_obs + j is q-head g, observation j.  Returns 0 or E_ARG. */
 int anchorkv_workspace_offsets(const anchorkv_plan_info* plan, int64_t out[8]);
 
 /* Decode attention over the compressed cache, one query per q-head per unit

@@ -1,0 +1,256 @@
+"""Full-size parity: every workload at its real shape, compressed and decoded
+in the launch configuration the benchmark times (all units in one compress
+call, one decode step over all units).
+
+The 3B-shaped workload is small enough for whole-unit comparisons against
+the oracle (first and last unit).  For the larger workloads the oracle cannot
+redo a whole unit in seconds, so the test samples: one unit (the last, so the
+unit stride is exercised), two of its heads, and a few thousand tokens per
+head, and checks each stage against the oracle on those samples, conditioned
+on the GPU's earlier decisions where they are within the stated tie margins:
+
+* observation score (all tokens of the sampled heads) and the anchor set;
+* stored anchors equal the input rows;
+* nearest anchor, fp16 gamma and residual (oracle assignment on the sampled
+  tokens against the GPU's anchors);
+* utilities of the sampled tokens;
+* the residual selection of the whole unit equals the oracle's allocation
+  applied to the GPU utilities (exact), which with the sampled utility check
+  covers the top-R step;
+* 2-bit codes, scales and zeros of the sampled flagged tokens;
+* decode outputs of the sampled heads' q-heads against attention over the
+  reconstruction of the GPU cache, and (adversarial workload) the Theorem-1
+  output-error bound per sampled head.
+"""
+import copy
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+from oracle import anchorkv_oracle as O
+from tests.parity import (MARGIN, OUT_RTOL, check_anchor_set, compare_unit, f16_bits_to_f64,
+                          fp16_midpoint_distance, storage_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_TOKENS = 3072
+
+
+def _flush(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def akv():
+    import kv_cache_compression_snapkv_amd as m
+    m.lib()
+    return m
+
+
+def ws_view(ws, off, count, dtype=torch.float32):
+    nbytes = count * torch.empty(0, dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype)
+
+
+def run_workload(akv, w, step=0):
+    """Inputs generated in place on the GPU, then compress (all units, one call)
+    and one decode step (all units), as the benchmark launches them."""
+    dev = "cuda"
+    dt = akv.BF16 if w.dtype == "bf16" else akv.F32
+    p = akv.plan(w.units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs, dt, w.theta, w.window)
+    K = torch.empty(w.units, w.kv_heads, w.n_tokens, w.head_dim, dtype=w.torch_dtype, device=dev)
+    V = torch.empty_like(K)
+    Q = torch.empty(w.units, w.kv_heads * w.q_per_kv, w.n_obs, w.head_dim, dtype=w.torch_dtype, device=dev)
+    for u in range(w.units):
+        s, l = kvsynth.unit_index(w, u)
+        k, v, q = kvsynth.unit_inputs(w, s, l, device=dev)
+        K[u].copy_(k); V[u].copy_(v); Q[u].copy_(q)
+        del k, v, q
+    cache, ws, dws = akv.alloc(p, dev)
+    q = kvsynth.decode_queries(w, step, device=dev).contiguous()
+    o = torch.empty(w.units, w.kv_heads * w.q_per_kv, w.head_dim, dtype=torch.float32, device=dev)
+    akv.compress(p, K, V, Q, cache, ws)
+    akv.decode_attn(p, cache, q, o, dws)
+    torch.cuda.synchronize()
+    return p, K, V, Q, cache, ws, q, o
+
+
+def unit_taps(akv, p, ws, u):
+    offs = akv.workspace_offsets(p)
+    U, H, N = p.units, p.H, p.N
+    score = ws_view(ws, offs["score"], U * H * N).view(U, H, N)[u].cpu().numpy().astype(np.float64)
+    util = ws_view(ws, offs["util"], U * 2 * H * N).view(U, 2, H, N)[u].cpu().numpy().astype(np.float64)
+    return score, util
+
+
+def unit_arrays(akv, p, cache, u):
+    unit = cache[u * p.unit_stride: u * p.unit_stride + p.unit_bytes].cpu().numpy().tobytes()
+    return akv.unpack_unit(p, unit)
+
+
+def test_fullsize_llama3b_8k_whole_units(akv):
+    """3B-shaped workload at full size (28 units x 8 heads x 8192 tokens):
+    whole-unit comparison of the first and the last unit."""
+    w = kvsynth.WORKLOADS["llama3b_8k"]
+    _flush(f"[fullsize] {w.name}: units={w.units} N={w.n_tokens}")
+    p, K, V, Q, cache, ws, q, o = run_workload(akv, w)
+    for u in (0, w.units - 1):
+        score, util = unit_taps(akv, p, ws, u)
+        arr = unit_arrays(akv, p, cache, u)
+        K64, V64, Q64 = (kvsynth.to_f64(t[u]) for t in (K, V, Q))
+        rep = compare_unit(K64, V64, Q64, w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes, arr,
+                           taps=dict(score=score, util=util), q=kvsynth.to_f64(q[u]),
+                           o_gpu=o[u].cpu().numpy().astype(np.float64))
+        _flush(f"[fullsize] {w.name} unit {u}: {rep}")
+
+
+def _sampled_tokens(rng, N, A_pos, n):
+    """Sample of token positions: the first and last 64, anchors-adjacent
+    positions and uniform picks (sorted, unique)."""
+    picks = [np.arange(min(64, N)), np.arange(max(0, N - 64), N), rng.choice(A_pos, size=min(64, A_pos.size)) + 1,
+             rng.integers(0, N, size=n)]
+    t = np.unique(np.clip(np.concatenate(picks), 0, N - 1))
+    return t
+
+
+def check_sampled_unit(akv, w, p, K, V, Q, cache, ws, q, o, u, heads, seed=0):
+    rng = np.random.default_rng(seed)
+    H, N, D, G, W = w.kv_heads, w.n_tokens, w.head_dim, w.q_per_kv, w.window
+    e = w.elem_bytes
+    dtype_code = 1 if e == 2 else 2
+    op = O.plan(H, N, D, e, w.theta, W)
+    assert (op.A, op.R_K, op.R_V) == (p.A, p.R_K, p.R_V)
+    score_g, util_g = unit_taps(akv, p, ws, u)
+    arr = unit_arrays(akv, p, cache, u)
+    gpos = arr["positions"].astype(np.int64)
+    gidx = arr["idx"].astype(np.int64)
+    gflag = arr["flag"].astype(bool)
+    rep = {}
+
+    # residual selection over the whole unit: the oracle's allocation applied
+    # to the GPU's own utilities must give exactly the GPU's residual set
+    for s, R in enumerate((p.R_K, p.R_V)):
+        ug = np.where(util_g[s] >= 0, util_g[s], -np.inf)
+        sel = O.allocate(ug, R)
+        assert np.array_equal(sel, gflag[s]), f"side {s}: residual set differs from top-R of the GPU utilities"
+        assert gflag[s].sum() == R
+
+    o_g = o[u].cpu().numpy().astype(np.float64)
+    q64 = kvsynth.to_f64(q[u])
+    for h in heads:
+        Kh = kvsynth.to_f64(K[u, h])
+        Vh = kvsynth.to_f64(V[u, h])
+        Qh = kvsynth.to_f64(Q[u, h * G:(h + 1) * G]).reshape(G * w.n_obs, D)
+        # observation attention, score, anchor set
+        P, Oh = O.obs_attention(Qh, Kh, Vh, w.n_obs)
+        score, pooled = O.anchor_score(P, W)
+        s_err = np.max(np.abs(score_g[h] - score) / np.maximum(score, score.max() * 1e-6))
+        assert s_err < 1e-4, f"head {h}: score mismatch {s_err}"
+        ok, why = check_anchor_set(pooled, gpos[h], N, W, op.k_s, op.k_u)
+        assert ok, f"head {h}: anchor set {why}"
+        rep[f"h{h}_anchors"] = why
+        rep[f"h{h}_score_err"] = float(s_err)
+        # stored anchors are the input rows
+        for s, X in enumerate((Kh, Vh)):
+            ga = storage_to_f64(arr["anchors_k" if s == 0 else "anchors_v"][h], dtype_code)
+            assert np.array_equal(ga, X[gpos[h]]), f"head {h} side {s}: stored anchors differ"
+        # sampled tokens: the oracle's assignment against the GPU's anchors.
+        # Rows 0..A-1 of the small problem are the anchors themselves, so the
+        # sampled rows see exactly the anchor set the GPU used.
+        ts = _sampled_tokens(rng, N, gpos[h], SAMPLE_TOKENS)
+        A = gpos.shape[1]
+        is_anchor = np.zeros(N, bool)
+        is_anchor[gpos[h]] = True
+        anchor_rank = np.full(N, -1)
+        anchor_rank[gpos[h]] = np.arange(A)
+        res = {}
+        for s, X in enumerate((Kh, Vh)):
+            Xs = np.concatenate([X[gpos[h]], X[ts]])
+            a_free = O.assign(Xs, np.arange(A))
+            g_s = gidx[s, h, ts]
+            o_s = a_free["idx"][A:]
+            # anchors among the samples map to their own rank
+            o_s = np.where(is_anchor[ts], anchor_rank[ts], o_s)
+            mism = (g_s != o_s) & ~is_anchor[ts]
+            bad = mism & (a_free["margin"][A:] >= MARGIN)
+            assert not bad.any(), f"head {h} side {s}: {int(bad.sum())} assignments differ outside the margin"
+            assert np.all(g_s[is_anchor[ts]] == anchor_rank[ts][is_anchor[ts]]), "anchor tokens not self-assigned"
+            rep[f"h{h}_s{s}_assign_excused"] = int(mism.sum())
+            # continue from the GPU's assignment
+            a_c = O.assign(Xs, np.arange(A), idx_override=np.concatenate([np.arange(A), g_s]))
+            gam, r = a_c["gamma"][A:], a_c["r"][A:]
+            r[is_anchor[ts]] = 0.0
+            gam = np.where(is_anchor[ts], 1.0, gam)
+            g16 = f16_bits_to_f64(arr["gamma16"][s, h, ts])
+            want16 = O.fp16_rne(gam)
+            near = fp16_midpoint_distance(gam) < 1e-3
+            assert not ((g16 != want16) & ~near).any(), f"head {h} side {s}: fp16 gammas differ"
+            res[s] = r
+        # utilities of the sampled tokens
+        uK, uV = O.utilities(P[:, ts], Oh, Qh, Vh[ts], res[0], res[1], ~is_anchor[ts])
+        for s, uo in enumerate((uK, uV)):
+            el = np.isfinite(uo)
+            if el.any():
+                rel = np.abs(util_g[s, h, ts][el] - uo[el]) / np.maximum(np.abs(uo[el]), 1e-30)
+                rep[f"h{h}_s{s}_util_err"] = float(rel.max())
+                assert rel.max() < 1e-4, f"head {h} side {s}: utility error {rel.max()}"
+            assert np.all(util_g[s, h, ts][~el] < 0), "anchor tokens must be ineligible"
+        # codes of the sampled flagged tokens
+        for s in range(2):
+            fl = gflag[s, h, ts]
+            if not fl.any():
+                continue
+            r = res[s][fl]
+            codes_o, sc_o, ze_o = O.quantize(r)
+            lo = r.reshape(r.shape[0], -1, 32).min(-1)
+            hi = r.reshape(r.shape[0], -1, 32).max(-1)
+            safe_g = (fp16_midpoint_distance(lo) > 1e-3) & (fp16_midpoint_distance((hi - lo) / 3) > 1e-3)
+            sc_g = f16_bits_to_f64(arr["scale16"][s, h, ts][fl])
+            ze_g = f16_bits_to_f64(arr["zero16"][s, h, ts][fl])
+            assert np.all((sc_g == sc_o) | ~safe_g), f"head {h} side {s}: scales differ"
+            assert np.all((ze_g == ze_o) | ~safe_g), f"head {h} side {s}: zeros differ"
+            safe_e = (O.code_margin(r, sc_o, ze_o) > 1e-3) & np.repeat(safe_g, 32, axis=1)
+            bad = (arr["codes"][s, h, ts][fl] != codes_o) & safe_e
+            assert not bad.any(), f"head {h} side {s}: {int(bad.sum())} codes differ"
+            rep[f"h{h}_s{s}_codes_checked"] = int(safe_e.sum())
+        # decode of this head's q-heads over the reconstruction of the GPU cache
+        c = O.Compressed(plan=op, G=G, anchor_pos=gpos[h:h + 1], idx=gidx[:, h:h + 1], gamma=None,
+                         gamma16=f16_bits_to_f64(arr["gamma16"][:, h:h + 1]), resid=None,
+                         flag=gflag[:, h:h + 1],
+                         codes=np.where(gflag[:, h:h + 1, :, None], arr["codes"][:, h:h + 1], 0).astype(np.uint8),
+                         scale=f16_bits_to_f64(arr["scale16"][:, h:h + 1]),
+                         zero=f16_bits_to_f64(arr["zero16"][:, h:h + 1]),
+                         anchors=np.stack([Kh[gpos[h]][None], Vh[gpos[h]][None]]), score=None, pooled=None)
+        Khat, Vhat = O.reconstruct(c)
+        qh = q64[h * G:(h + 1) * G]
+        ref = O.attention(qh, Khat[0], Vhat[0])
+        err = np.linalg.norm(o_g[h * G:(h + 1) * G] - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        rep[f"h{h}_decode_err"] = float(err.max())
+        assert err.max() <= OUT_RTOL, f"head {h}: decode error {err.max()}"
+        if w.stress:
+            worst = 0.0
+            for g in range(G):
+                t = O.theorem1_terms(qh[g], Kh, Vh, Khat[0], Vhat[0])
+                lhs, bound, bound2 = t[0], t[1] + t[2], t[3] + t[4]
+                tol = 1e-12 * (1.0 + np.linalg.norm(Vh, axis=1).max())
+                assert lhs <= bound + tol and lhs <= bound2 + tol, f"head {h} q {g}: Theorem-1 bound violated"
+                worst = max(worst, lhs / max(bound, 1e-300))
+            rep[f"h{h}_thm1_ratio_max"] = worst
+        del P
+    return rep
+
+
+@pytest.mark.parametrize("wname", ["llama8b_32k", "llama70b_128k", "stress_64k"])
+def test_fullsize_sampled(akv, wname):
+    w = kvsynth.WORKLOADS[wname]
+    _flush(f"[fullsize] {wname}: units={w.units} H={w.kv_heads} G={w.q_per_kv} N={w.n_tokens}")
+    p, K, V, Q, cache, ws, q, o = run_workload(akv, w)
+    _flush(f"[fullsize] {wname}: compressed and decoded; checking unit {w.units - 1}")
+    rep = check_sampled_unit(akv, w, p, K, V, Q, cache, ws, q, o, w.units - 1, heads=(0, w.kv_heads - 1))
+    _flush(f"[fullsize] {wname}: {rep}")
+    del K, V, Q, cache, ws
+    torch.cuda.empty_cache()
