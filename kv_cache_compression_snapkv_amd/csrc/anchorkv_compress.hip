@@ -10,6 +10,7 @@
 // "Assumptions & free parameters"); AnchorKV-adapted page ("Evidence",
 // "Adaptation notes").
 #include "obs_kernels.hpp"
+#include "obs_pipe.hpp"
 
 namespace akv {
 
@@ -285,7 +286,8 @@ template <int DT>
 __global__ __launch_bounds__(256) void k_assign(const void* Kv, const void* Vv, uint8_t* cache, int64_t stride,
                                                int64_t off_ak, int64_t off_av, int64_t off_words,
                                                const float2* anorm, const int* anchor_of, int* aidx, float* gam,
-                                               float* rn2, int H, int N, int A, int ntiles) {
+                                               float* rn2, float* vn2, const float* score, float* util, int H, int N,
+                                               int A, int ntiles) {
   using T = typename Elem<DT>::T;
   using M = Mfma<DT>;
   using frag = typename M::frag;
@@ -402,11 +404,22 @@ __global__ __launch_bounds__(256) void k_assign(const void* Kv, const void* Vv, 
     r2 += __shfl_xor(r2, 16, 64);
     r2 += __shfl_xor(r2, 32, 64);
     if (is_anchor) r2 = 0.0f;
+    float xx = 0.0f;
+    if (side == 1) {
+      for (int i = 0; i < NSTEP * M::KW; ++i) xx = fmaf(xs[i], xs[i], xx);
+      xx += __shfl_xor(xx, 16, 64);
+      xx += __shfl_xor(xx, 32, 64);
+    }
     if (kg == 0 && t < N) {
       const int64_t i = ((int64_t)u * 2 * H + side * H + h) * N + t;
       aidx[i] = a;
       gam[i] = g;
       rn2[i] = r2;
+      if (side == 1) {
+        // value channel of the utility: score_t ||r_V|| (anchors ineligible)
+        vn2[uh * N + t] = xx;
+        util[i] = is_anchor ? -1.0f : score[uh * N + t] * sqrtf(r2);
+      }
       uint32_t* words = reinterpret_cast<uint32_t*>(cache + (int64_t)u * stride + off_words);
       words[((int64_t)h * N + t) * 2 + side] = (uint32_t)a | ((uint32_t)f2h_sat(g) << 16);
     }
@@ -674,9 +687,16 @@ static int launch_obs(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t
   if (DT == ANCHORKV_F32 && QB > 8) return fail(ANCHORKV_E_SHAPE, "f32 path supports q_per_kv*n_obs <= 128");
   if (QB > 16) return fail(ANCHORKV_E_SHAPE, "q_per_kv*n_obs must be <= 256");
   const int nw = (QB + qpw - 1) / qpw;
-  const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1)), block(64 * nw);
-  if (qpw == 1) k_obs<DT, MODE, 1><<<grid, block, 0, st>>>(a);
-  else if constexpr (DT == ANCHORKV_BF16) k_obs<DT, MODE, 2><<<grid, block, 0, st>>>(a);
+  const dim3 block(64 * nw);
+  if constexpr (DT == ANCHORKV_BF16) {
+    const dim3 grid((unsigned)((int64_t)p.units * p.H * (MODE == OBS_UTIL ? a.S1u : a.S1)));
+    constexpr int ST = 2;
+    if (qpw == 1) k_obs_pipe<MODE, 1, ST><<<grid, block, 0, st>>>(a);
+    else k_obs_pipe<MODE, 2, ST><<<grid, block, 0, st>>>(a);
+  } else {
+    const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1));
+    k_obs<DT, MODE, 1><<<grid, block, 0, st>>>(a);
+  }
   AKV_CHECK_LAUNCH("k_obs");
   return 0;
 }
@@ -710,9 +730,12 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   a.aidx = reinterpret_cast<const int*>(ws + w.aidx);
   a.rn2 = reinterpret_cast<const float*>(ws + w.rn2);
   a.anchor_of = reinterpret_cast<const int*>(ws + w.anchor_of);
+  a.vn2 = reinterpret_cast<const float*>(ws + w.vn2);
   a.util = reinterpret_cast<float*>(ws + w.util);
   a.U = U; a.H = H; a.G = p.G; a.N = N; a.n_obs = p.n_obs; a.GQ = GQ; a.GQp = w.GQp; a.S1 = w.S1;
   a.kps = (int)round_up((N + w.S1 - 1) / w.S1, 64);
+  a.S1u = std::max(w.S1, (N + kObsUtilMaxKeys - 1) / kObsUtilMaxKeys);
+  a.kps_u = (int)round_up((N + a.S1u - 1) / a.S1u, 64);
   a.A = A;
   a.c = kLog2e / sqrtf((float)kHeadDim);
   a.inv_sqrt_d = 1.0f / sqrtf((float)kHeadDim);
@@ -746,7 +769,8 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   k_assign<DT><<<(unsigned)((int64_t)U * 2 * H * ntiles), 256, 0, st>>>(
       K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_words,
       reinterpret_cast<const float2*>(ws + w.anorm), a.anchor_of, reinterpret_cast<int*>(ws + w.aidx),
-      reinterpret_cast<float*>(ws + w.gam), reinterpret_cast<float*>(ws + w.rn2), H, N, A, ntiles);
+      reinterpret_cast<float*>(ws + w.gam), reinterpret_cast<float*>(ws + w.rn2), reinterpret_cast<float*>(ws + w.vn2),
+      a.score, a.util, H, N, A, ntiles);
   AKV_CHECK_LAUNCH("k_assign");
   prof_mark(st, "assign");
 

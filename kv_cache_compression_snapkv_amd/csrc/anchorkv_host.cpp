@@ -57,6 +57,7 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
   w.ohl = take(2 * U * H * 2 * GQp * D);
   w.oo = take(4 * U * H * GQp);
   w.anchor_of = take(4 * U * H * N);
+  w.vn2 = take(4 * U * H * N);
   w.anorm = take(8 * U * 2 * H * A);
   w.pooled = take(4 * U * H * N);
   w.hist = take(4 * U * 2 * kHistBins);

@@ -43,6 +43,7 @@ struct CompressWs {
   int64_t ohl;     // bf16 [U][H][2][GQp][D] (hi, lo split of o)
   int64_t oo;      // f32 [U][H][GQp] ||o||^2
   int64_t anchor_of; // int32 [U][H][N] anchor index of a position, -1 if none
+  int64_t vn2;     // f32 [U][H][N] ||v_t||^2
   int64_t anorm;   // float2 [U][2][H][A] (||x_a||^2, 1/||x_a||)
   int64_t pooled;  // f32 [U][H][N]
   int64_t hist;    // u32 [U][2][kHistBins]

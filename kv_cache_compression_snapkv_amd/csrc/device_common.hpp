@@ -77,20 +77,23 @@ template <> struct Mfma<ANCHORKV_F32> {
 
 __device__ __forceinline__ bf16x8 bits_to_frag(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Split 8 floats into bf16 hi + lo so that hi + lo carries ~16 significant bits.
+// Split 8 floats into bf16 hi + lo so that hi + lo carries ~16 significant bits
+// (v_cvt_pk_bf16_f32: round to nearest even, two values per instruction).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
 __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
-  uint16_t h[8], l[8];
-  for (int i = 0; i < 8; ++i) {
-    h[i] = f2bf(v[i]);
-    l[i] = f2bf(v[i] - bf2f(h[i]));
+  uint32_t h[4], l[4];
+  for (int i = 0; i < 4; ++i) {
+    h[i] = cvt_pk_bf16(v[2 * i], v[2 * i + 1]);
+    const float r0 = v[2 * i] - __uint_as_float(h[i] << 16);
+    const float r1 = v[2 * i + 1] - __uint_as_float(h[i] & 0xFFFF0000u);
+    l[i] = cvt_pk_bf16(r0, r1);
   }
-  uint4 hh, ll;
-  hh.x = h[0] | ((uint32_t)h[1] << 16); hh.y = h[2] | ((uint32_t)h[3] << 16);
-  hh.z = h[4] | ((uint32_t)h[5] << 16); hh.w = h[6] | ((uint32_t)h[7] << 16);
-  ll.x = l[0] | ((uint32_t)l[1] << 16); ll.y = l[2] | ((uint32_t)l[3] << 16);
-  ll.z = l[4] | ((uint32_t)l[5] << 16); ll.w = l[6] | ((uint32_t)l[7] << 16);
-  hi = bits_to_frag(hh);
-  lo = bits_to_frag(ll);
+  hi = bits_to_frag(make_uint4(h[0], h[1], h[2], h[3]));
+  lo = bits_to_frag(make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 // Cross-lane moves inside a row of 16 lanes with DPP (plain VALU, no LDS).

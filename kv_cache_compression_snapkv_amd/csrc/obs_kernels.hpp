@@ -15,8 +15,8 @@
 //          p |<q, r_K>|/sqrt(D) ||v - o||), with <q, r_K> = <q, k_t> -
 //          gamma_t <q, k_a(t)> (both exact-operand MFMA) and ||v - o||^2 =
 //          ||v||^2 - 2<v, o> + ||o||^2 (o split hi + lo), recomputed directly
-//          when cancellation could cost precision; plus the value channel
-//          score_t ||r_V||.
+//          when cancellation could cost precision.  (The value channel
+//          score_t ||r_V|| is written by the assignment kernel.)
 // Query j of a q-head sits at position N - n_obs + j and sees keys t <=
 // N - n_obs + j.
 #pragma once
@@ -44,8 +44,10 @@ struct ObsArgs {
   const int* aidx;       // [U][2][H][N]
   const float* rn2;      // [U][2][H][N]
   const int* anchor_of;  // [U][H][N]
+  const float* vn2;      // [U][H][N] ||v_t||^2
   float* util;           // [U][2][H][N]
   int U, H, G, N, n_obs, GQ, GQp, S1, kps, A;
+  int S1u, kps_u;         // key splits of the pipelined UTIL kernel (<= 2048 keys each)
   float c;               // log2(e)/sqrt(D)
   float inv_sqrt_d;
 };
@@ -328,9 +330,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
           } else {
             const bool anc = a.anchor_of[uh * N + t] >= 0;
             const int64_t iK = ((int64_t)u * 2 * H + h) * N + t;
-            const int64_t iV = ((int64_t)u * 2 * H + H + h) * N + t;
             a.util[iK] = anc ? -1.0f : v;
-            a.util[iV] = anc ? -1.0f : a.score[uh * N + t] * sqrtf(a.rn2[iV]);
           }
         }
       }

@@ -1,0 +1,534 @@
+// Pipelined observation-window kernels for bf16 inputs (gfx950).
+//
+// Same three modes as k_obs (STATS / SCORE / UTIL; see obs_kernels.hpp for
+// what each computes and the page sections it follows), organised for
+// latency hiding:
+//  * the block streams its key range in 64-key tiles through STAGES LDS
+//    buffers; tiles are copied global -> LDS by asynchronous
+//    global_load_lds_dwordx4 (16 bytes per lane, no registers) STAGES-1
+//    tiles ahead of the one being computed; one barrier per tile; the wait
+//    for the next tile lets the copies issued during this tile stay in
+//    flight (loads complete in issue order);
+//  * every [64][128] bf16 tile is stored with its 16-byte chunks XOR-swizzled
+//    per row, so that MFMA fragment reads (8 rows, same chunk) and the
+//    transposing reads of the value tile (4 rows x 2 chunks) hit distinct
+//    LDS banks;
+//  * SCORE reads the P V operand with ds_read_b64_tr_b16, which hands each
+//    lane 4 consecutive keys of one value coordinate straight from the
+//    row-major tile;
+//  * UTIL keeps the anchor index of every key of its range (<= 2048 keys) in
+//    LDS, loaded once, so the gathered anchor rows can be copied ahead like
+//    the key and value rows;
+//  * per-key sums over the block's query columns are reduced with DPP inside
+//    a wave, written to a small LDS partial array, and combined across waves
+//    one tile later (after the next barrier), in fixed wave order.
+// The stage buffers are distinct __shared__ objects and the tile loop is
+// unrolled by STAGES, so the compiler can tell that compute-phase LDS reads
+// do not alias the copies in flight and does not wait for them.
+#pragma once
+
+#include "device_common.hpp"
+#include "obs_kernels.hpp"
+
+namespace akv {
+
+#define AKV_LDS __attribute__((address_space(3)))
+
+typedef short akv_v4s __attribute__((ext_vector_type(4)));
+
+constexpr int kObsTK = 64;                   // keys per tile
+constexpr int kObsTileChunks = kObsTK * 16;  // 16-byte chunks per [64][128] bf16 tile
+constexpr int kObsUtilMaxKeys = 2048;        // key range of one UTIL block
+constexpr int kObsMaxWaves = 8;
+
+__device__ __forceinline__ int obs_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Physical chunk of logical chunk c (0..15) of tile row r.
+__device__ __forceinline__ int obs_phys(int r, int c) { return r * 16 + (c ^ obs_swz(r)); }
+
+// Asynchronous global -> LDS copies: lane l writes lds_base + size*l; the LDS
+// base must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (AKV_LDS void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (AKV_LDS void*)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters untouched (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).  A builtin,
+// unlike inline asm, is visible to the compiler's own wait-count tracking.
+#define AKV_VMCNT_IMM(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define AKV_VM_CASE(n) case n: __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(n)); break;
+__device__ __forceinline__ void wait_vm_le(int n) {
+  switch (n) {
+    AKV_VM_CASE(0) AKV_VM_CASE(1) AKV_VM_CASE(2) AKV_VM_CASE(3) AKV_VM_CASE(4) AKV_VM_CASE(5)
+    AKV_VM_CASE(6) AKV_VM_CASE(7) AKV_VM_CASE(8) AKV_VM_CASE(9) AKV_VM_CASE(10) AKV_VM_CASE(11)
+    AKV_VM_CASE(12) AKV_VM_CASE(13) AKV_VM_CASE(14) AKV_VM_CASE(15) AKV_VM_CASE(16) AKV_VM_CASE(17)
+    AKV_VM_CASE(18) AKV_VM_CASE(19) AKV_VM_CASE(20) AKV_VM_CASE(21) AKV_VM_CASE(22) AKV_VM_CASE(23)
+    AKV_VM_CASE(24) AKV_VM_CASE(25) AKV_VM_CASE(26) AKV_VM_CASE(27) AKV_VM_CASE(28) AKV_VM_CASE(29)
+    AKV_VM_CASE(30) AKV_VM_CASE(31) AKV_VM_CASE(32) AKV_VM_CASE(33) AKV_VM_CASE(34) AKV_VM_CASE(35)
+    AKV_VM_CASE(36) AKV_VM_CASE(37) AKV_VM_CASE(38) AKV_VM_CASE(39) AKV_VM_CASE(40) AKV_VM_CASE(41)
+    AKV_VM_CASE(42) AKV_VM_CASE(43) AKV_VM_CASE(44) AKV_VM_CASE(45) AKV_VM_CASE(46) AKV_VM_CASE(47)
+    AKV_VM_CASE(48) AKV_VM_CASE(49) AKV_VM_CASE(50) AKV_VM_CASE(51) AKV_VM_CASE(52) AKV_VM_CASE(53)
+    AKV_VM_CASE(54) AKV_VM_CASE(55) AKV_VM_CASE(56) AKV_VM_CASE(57) AKV_VM_CASE(58) AKV_VM_CASE(59)
+    AKV_VM_CASE(60) AKV_VM_CASE(61) AKV_VM_CASE(62)
+    default: __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0)); break;
+  }
+}
+#undef AKV_VM_CASE
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint4* tile, int row, int c) {
+  return bits_to_frag(tile[obs_phys(row, c)]);
+}
+// 4 consecutive keys (rows) of one value coordinate, via the transposing read.
+__device__ __forceinline__ uint2 lds_tr(const uint4* tile, int row, int d) {
+  const uint16_t* p = reinterpret_cast<const uint16_t*>(tile + obs_phys(row, d >> 3)) + (d & 7);
+  akv_v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AKV_LDS akv_v4s*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Per-lane offsets (elements) of the tile copies: chunk-block jj (64 lanes,
+// rows 4jj .. 4jj+3) of a [64][128] tile.  Row r = 4jj + lane/16; logical
+// chunk c = (lane & 15) ^ swz(r), and swz(r) = 2(lane/16) | (jj & 1), so the
+// offset of lane l is jj*512 + off[jj & 1] with two per-lane constants.
+struct DmaLane {
+  int off0, off1;   // element offsets within a 4-row block for even / odd jj
+  int rsub;         // lane / 16: row within the 4-row block
+  int c0, c1;       // chunk (16-byte units) within the row for even / odd jj
+  __device__ __forceinline__ explicit DmaLane(int lane) {
+    rsub = lane >> 4;
+    c0 = (lane & 15) ^ (rsub << 1);
+    c1 = c0 ^ 1;
+    off0 = rsub * kHeadDim + c0 * 8;
+    off1 = rsub * kHeadDim + c1 * 8;
+  }
+};
+
+// Copy one [64][128] tile of contiguous rows starting at `base` (rows beyond
+// nval repeat row nval-1: valid memory, results masked).  Returns the number
+// of copy instructions this wave issued.
+__device__ __forceinline__ int dma_rows(uint4* dst, const uint16_t* base, int nval, int nw, int wave,
+                                        const DmaLane& dl) {
+  int n = 0;
+  if (nval == kObsTK) {
+    for (int jj = wave; jj < 16; jj += nw, ++n)
+      dma16(base + jj * 512 + ((jj & 1) ? dl.off1 : dl.off0), dst + jj * 64);
+  } else {
+    for (int jj = wave; jj < 16; jj += nw, ++n) {
+      const int r = min(jj * 4 + dl.rsub, nval - 1);
+      dma16(base + r * kHeadDim + ((jj & 1) ? dl.c1 : dl.c0) * 8, dst + jj * 64);
+    }
+  }
+  return n;
+}
+// Copy one [64][128] tile of gathered rows: row r is base + idx[r] * 128.
+__device__ __forceinline__ int dma_gather(uint4* dst, const uint16_t* base, const int* idx, int nval, int nw,
+                                          int wave, const DmaLane& dl) {
+  int n = 0;
+  for (int jj = wave; jj < 16; jj += nw, ++n) {
+    const int r = min(jj * 4 + dl.rsub, nval - 1);
+    dma16(base + (int64_t)idx[r] * kHeadDim + ((jj & 1) ? dl.c1 : dl.c0) * 8, dst + jj * 64);
+  }
+  return n;
+}
+
+// One stage's LDS buffers.
+struct ObsBufs {
+  uint4* K;
+  uint4* V;
+  uint4* G;
+  float* S;  // UTIL per-key scalars: [0] gamma_K, [1] ||v||^2, [2] anchor flag (int bits)
+};
+
+template <int MODE, int QPW, int STAGES>
+__global__ __launch_bounds__(512) void k_obs_pipe(ObsArgs a) {
+  constexpr int D = kHeadDim, NSTEP = 4;
+  constexpr bool HAS_V = MODE != OBS_STATS;
+  constexpr bool HAS_G = MODE == OBS_UTIL;
+  constexpr bool HAS_PART = MODE != OBS_STATS;
+  constexpr int TC = kObsTileChunks;
+  constexpr float kLazy = 8.0f;   // STATS: rescale only when the max grows by more than 2^8
+  using M = Mfma<ANCHORKV_BF16>;
+  using frag = bf16x8;
+  static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
+
+  __shared__ __attribute__((aligned(16))) uint4 K0[TC];
+  __shared__ __attribute__((aligned(16))) uint4 K1[TC];
+  __shared__ __attribute__((aligned(16))) uint4 K2[STAGES > 2 ? TC : 1];
+  __shared__ __attribute__((aligned(16))) uint4 V0[HAS_V ? TC : 1];
+  __shared__ __attribute__((aligned(16))) uint4 V1[HAS_V ? TC : 1];
+  __shared__ __attribute__((aligned(16))) uint4 V2[HAS_V && STAGES > 2 ? TC : 1];
+  __shared__ __attribute__((aligned(16))) uint4 G0[HAS_G ? TC : 1];
+  __shared__ __attribute__((aligned(16))) uint4 G1[HAS_G ? TC : 1];
+  __shared__ __attribute__((aligned(16))) uint4 G2[HAS_G && STAGES > 2 ? TC : 1];
+  __shared__ __attribute__((aligned(16))) float S0[HAS_G ? 3 * kObsTK : 1];
+  __shared__ __attribute__((aligned(16))) float S1[HAS_G ? 3 * kObsTK : 1];
+  __shared__ __attribute__((aligned(16))) float S2[HAS_G && STAGES > 2 ? 3 * kObsTK : 1];
+  __shared__ int Ai[HAS_G ? kObsUtilMaxKeys : 1];   // anchor index of every key of the range
+  __shared__ float part[HAS_PART ? 2 : 1][HAS_PART ? kObsMaxWaves : 1][kObsTK];
+  __shared__ float pflag[HAS_G ? 2 : 1][kObsTK];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int nsplit = HAS_G ? a.S1u : a.S1;
+  const int kps = HAS_G ? a.kps_u : a.kps;
+  int bid = blockIdx.x;
+  const int s = bid % nsplit; bid /= nsplit;
+  const int h = bid % a.H;
+  const int u = bid / a.H;
+  const int N = a.N, H = a.H;
+  const int k0 = s * kps;
+  const int k1 = min(N, k0 + kps);
+  const int64_t uh = (int64_t)u * H + h;
+  if (k0 >= k1) {
+    // empty split: neutral partials
+    if constexpr (MODE == OBS_STATS) {
+      for (int qi = 0; qi < QPW; ++qi) {
+        const int qb = wave + qi * nw;
+        if (kg == 0 && qb * 16 < a.GQp) a.ml_part[(uh * a.S1 + s) * a.GQp + qb * 16 + col] = make_float2(-INFINITY, 0.0f);
+      }
+    }
+    if constexpr (MODE == OBS_SCORE) {
+      for (int qi = 0; qi < QPW; ++qi) {
+        const int qb = wave + qi * nw;
+        if (qb * 16 >= a.GQp) continue;
+        for (int db = 0; db < 8; ++db)
+          for (int r = 0; r < 4; ++r)
+            a.o_part[((uh * a.S1 + s) * a.GQp + qb * 16 + kg * 4 + r) * D + db * 16 + col] = 0.0f;
+      }
+    }
+    return;
+  }
+  const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.K) + uh * N * D;
+  const uint16_t* Vp = reinterpret_cast<const uint16_t*>(a.V) + uh * N * D;
+  const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.Q) + ((int64_t)u * H * a.G + (int64_t)h * a.G) * a.n_obs * D;
+  const uint16_t* Ap = reinterpret_cast<const uint16_t*>(a.cache + (int64_t)u * a.stride + a.off_anchor_k) +
+                       (int64_t)h * a.A * D;
+  const int64_t sideK = ((int64_t)u * 2 * H + h) * N;   // K-side rows of [U][2][H][N] arrays
+  const int ntiles = (k1 - k0 + kObsTK - 1) / kObsTK;
+  const DmaLane dl(lane);
+
+  // ---- UTIL: anchor index of every key of the range, loaded once
+  if constexpr (HAS_G) {
+    for (int b = wave; b * kObsTK < k1 - k0; b += nw) {
+      const int t = min(k0 + b * kObsTK + lane, k1 - 1);
+      dma4(a.aidx + sideK + t, Ai + b * kObsTK);
+    }
+  }
+
+  // ---- per-wave query blocks (B fragments, constant over all keys)
+  frag qf[QPW][NSTEP];
+  frag ofh[HAS_G ? QPW : 1][NSTEP];
+  frag ofl[HAS_G ? QPW : 1][NSTEP];
+  float mq[QPW], il[QPW], ooq[QPW];
+  int kmax[QPW];     // key t is visible to this lane's query iff t < kmax
+  bool qvalid[QPW], qactive[QPW];
+  const int vis_base = N - a.n_obs;  // query j sees keys <= vis_base + j
+  for (int qi = 0; qi < QPW; ++qi) {
+    const int qb = wave + qi * nw;
+    const int q = qb * 16 + col;
+    qactive[qi] = qb * 16 < a.GQp;
+    qvalid[qi] = qactive[qi] && q < a.GQ;
+    kmax[qi] = qvalid[qi] ? min(k1, vis_base + q % a.n_obs + 1) : -1;
+    for (int st = 0; st < NSTEP; ++st) {
+      const int kk = st * 32 + kg * 8;
+      qf[qi][st] = qvalid[qi] ? M::load(Qp + (int64_t)q * D + kk) : M::zero();
+      if constexpr (HAS_G) {
+        const uint16_t* oh = a.ohl + (uh * 2 + 0) * a.GQp * D;
+        const uint16_t* ol = a.ohl + (uh * 2 + 1) * a.GQp * D;
+        ofh[qi][st] = qvalid[qi] ? M::load(oh + (int64_t)q * D + kk) : M::zero();
+        ofl[qi][st] = qvalid[qi] ? M::load(ol + (int64_t)q * D + kk) : M::zero();
+      }
+    }
+    mq[qi] = -INFINITY; il[qi] = 0.0f; ooq[qi] = 0.0f;
+    if constexpr (MODE != OBS_STATS) {
+      if (qvalid[qi]) {
+        const float2 v = a.ml[uh * a.GQp + q];
+        mq[qi] = v.x; il[qi] = v.y;
+      }
+    }
+    if constexpr (HAS_G) {
+      if (qvalid[qi]) ooq[qi] = a.oo[uh * a.GQp + q];
+    }
+  }
+  // STATS running max (log2 domain; finite start so that fully masked tiles
+  // add exp2(-inf) = 0) and sum
+  float m_run[QPW], l_run[QPW];
+  for (int qi = 0; qi < QPW; ++qi) { m_run[qi] = -1e30f; l_run[qi] = 0.0f; }
+  f32x4 oacc[MODE == OBS_SCORE ? QPW : 1][MODE == OBS_SCORE ? 8 : 1];
+  if constexpr (MODE == OBS_SCORE)
+    for (int qi = 0; qi < QPW; ++qi)
+      for (int db = 0; db < 8; ++db) oacc[qi][db] = f32x4{0, 0, 0, 0};
+
+  // ---- copies of tile `it` into buffers b; returns this wave's instruction count
+  auto issue = [&](int it, const ObsBufs& b) -> int {
+    const int t0 = k0 + it * kObsTK;
+    const int nval = min(kObsTK, k1 - t0);
+    int n = 0;
+    if constexpr (HAS_G) {
+      n += dma_gather(b.G, Ap, Ai + it * kObsTK, nval, nw, wave, dl);
+      const int tl = min(t0 + lane, k1 - 1);
+      for (int arr = wave; arr < 3; arr += nw, ++n) {
+        const void* src = arr == 0 ? (const void*)(a.gam + sideK + tl)
+                        : arr == 1 ? (const void*)(a.vn2 + uh * N + tl)
+                                   : (const void*)(a.anchor_of + uh * N + tl);
+        dma4(src, b.S + arr * kObsTK);
+      }
+    }
+    n += dma_rows(b.K, Kp + (int64_t)t0 * D, nval, nw, wave, dl);
+    if constexpr (HAS_V) n += dma_rows(b.V, Vp + (int64_t)t0 * D, nval, nw, wave, dl);
+    return n;
+  };
+  // sum of the per-wave partials of tile `it` (one wave), fixed wave order
+  auto combine = [&](int it) {
+    if constexpr (HAS_PART) {
+      if (wave == it % nw) {
+        const int t = k0 + it * kObsTK + lane;
+        float v = 0.0f;
+        for (int w = 0; w < nw; ++w) v += part[it & 1][w][lane];
+        if (t < k1) {
+          if constexpr (MODE == OBS_SCORE) {
+            a.score[uh * N + t] = v;
+          } else {
+            a.util[sideK + t] = pflag[it & 1][lane] != 0.0f ? -1.0f : v * a.inv_sqrt_d;
+          }
+        }
+      }
+    }
+  };
+
+  // ---- UTIL, exact per-pair path for a tile where ||v - o||^2 cancels:
+  // recomputes the tile and evaluates ||v - o||^2 directly where needed
+  auto util_exact = [&](int t0, const ObsBufs& c, float (&colsum)[4][4]) {
+    for (int kb = 0; kb < 4; ++kb)
+      for (int r = 0; r < 4; ++r) colsum[kb][r] = 0.0f;
+    for (int kb = 0; kb < 4; ++kb) {
+      frag af[NSTEP], gf[NSTEP], vf[NSTEP];
+      const int row = kb * 16 + col;
+      for (int st = 0; st < NSTEP; ++st) {
+        af[st] = lds_frag(c.K, row, st * 4 + kg);
+        gf[st] = lds_frag(c.G, row, st * 4 + kg);
+        vf[st] = lds_frag(c.V, row, st * 4 + kg);
+      }
+      for (int qi = 0; qi < QPW; ++qi) {
+        if (!qactive[qi]) continue;
+        f32x4 acc = {0, 0, 0, 0}, accg = {0, 0, 0, 0}, accv = {0, 0, 0, 0};
+        for (int st = 0; st < NSTEP; ++st) acc = M::mma(af[st], qf[qi][st], acc);
+        for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf[st], qf[qi][st], accg);
+        for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[st], ofh[qi][st], accv);
+        for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[st], ofl[qi][st], accv);
+        for (int r = 0; r < 4; ++r) {
+          const int kl = kb * 16 + kg * 4 + r;
+          if (t0 + kl >= kmax[qi]) continue;
+          const float p = exp2_fast(acc[r] * a.c - mq[qi]) * il[qi];
+          if (!(p > 0.0f)) continue;
+          const float gm = c.S[kl], vv = c.S[kObsTK + kl];
+          const float qr = fabsf(acc[r] - gm * accg[r]);
+          const float sum = vv + ooq[qi];
+          float vo2 = fmaf(-2.0f, accv[r], sum);
+          if (vo2 < 0.5f * sum) {
+            const int q = (wave + qi * nw) * 16 + col;
+            const float* orow = a.ofull + (uh * a.GQp + q) * D;
+            const uint16_t* vrow = reinterpret_cast<const uint16_t*>(c.V);
+            float acc2 = 0.0f;
+            for (int d = 0; d < D; ++d) {
+              const float df = bf2f(vrow[obs_phys(kl, d >> 3) * 8 + (d & 7)]) - orow[d];
+              acc2 = fmaf(df, df, acc2);
+            }
+            vo2 = acc2;
+          }
+          colsum[kb][r] = fmaf(p * qr, __builtin_amdgcn_sqrtf(fmaxf(vo2, 0.0f)), colsum[kb][r]);
+        }
+      }
+    }
+  };
+
+  // ---- compute one tile from buffers c
+  auto compute = [&](int it, const ObsBufs& c) {
+    const int t0 = k0 + it * kObsTK;
+    float colsum[4][4];
+    for (int kb = 0; kb < 4; ++kb)
+      for (int r = 0; r < 4; ++r) colsum[kb][r] = 0.0f;
+    float xs[MODE == OBS_STATS ? QPW : 1][4][4];   // STATS: logits of the tile
+    float pv[MODE == OBS_SCORE ? QPW : 1][2][4];
+    bool cancel = false;
+    for (int kb = 0; kb < 4; ++kb) {
+      frag af[NSTEP], gf[HAS_G ? NSTEP : 1], vf[HAS_G ? NSTEP : 1];
+      const int row = kb * 16 + col;
+      for (int st = 0; st < NSTEP; ++st) {
+        af[st] = lds_frag(c.K, row, st * 4 + kg);
+        if constexpr (HAS_G) {
+          gf[st] = lds_frag(c.G, row, st * 4 + kg);
+          vf[st] = lds_frag(c.V, row, st * 4 + kg);
+        }
+      }
+      float4 gm4, vv4;
+      if constexpr (HAS_G) {
+        gm4 = *reinterpret_cast<const float4*>(c.S + kb * 16 + kg * 4);
+        vv4 = *reinterpret_cast<const float4*>(c.S + kObsTK + kb * 16 + kg * 4);
+      }
+      for (int qi = 0; qi < QPW; ++qi) {
+        if (!qactive[qi]) continue;  // wave-uniform
+        f32x4 acc = {0, 0, 0, 0}, accg = {0, 0, 0, 0}, accv = {0, 0, 0, 0};
+        for (int st = 0; st < NSTEP; ++st) acc = M::mma(af[st], qf[qi][st], acc);
+        if constexpr (HAS_G) {
+          for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf[st], qf[qi][st], accg);
+          for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[st], ofh[qi][st], accv);
+          for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[st], ofl[qi][st], accv);
+        }
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + kb * 16 + kg * 4 + r;
+          const bool valid = t < kmax[qi];
+          if constexpr (MODE == OBS_STATS) {
+            xs[qi][kb][r] = valid ? acc[r] * a.c : -INFINITY;
+          } else {
+            const float e = exp2_fast(fmaf(acc[r], a.c, -mq[qi])) * il[qi];
+            const float p = valid ? e : 0.0f;
+            if constexpr (MODE == OBS_SCORE) {
+              pv[qi][kb & 1][r] = p;
+              colsum[kb][r] += p;
+            } else {
+              const float gm = r == 0 ? gm4.x : r == 1 ? gm4.y : r == 2 ? gm4.z : gm4.w;
+              const float vv = r == 0 ? vv4.x : r == 1 ? vv4.y : r == 2 ? vv4.z : vv4.w;
+              const float qr = fabsf(fmaf(-gm, accg[r], acc[r]));
+              const float sum = vv + ooq[qi];
+              const float vo2 = fmaf(-2.0f, accv[r], sum);
+              cancel |= (vo2 < 0.5f * sum) & (p > 0.0f);
+              colsum[kb][r] = fmaf(p * qr, __builtin_amdgcn_sqrtf(fmaxf(vo2, 0.0f)), colsum[kb][r]);
+            }
+          }
+        }
+      }
+      if constexpr (MODE == OBS_SCORE) {
+        if (kb & 1) {
+          // P V for the 32-key chunk c2 = kb/2: value B fragments by transposing reads
+          const int c2 = kb >> 1;
+          const int g = lane >> 4, m = lane & 15;
+          frag vb[8];
+          for (int db = 0; db < 8; ++db) {
+            const int d = db * 16 + (m & 3) * 4;
+            const uint2 lo = lds_tr(c.V, c2 * 32 + g * 4 + (m >> 2), d);
+            const uint2 hi = lds_tr(c.V, c2 * 32 + 16 + g * 4 + (m >> 2), d);
+            vb[db] = bits_to_frag(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          }
+          for (int qi = 0; qi < QPW; ++qi) {
+            if (!qactive[qi]) continue;
+            float p8[8];
+            for (int e = 0; e < 8; ++e) p8[e] = pv[qi][e >> 2][e & 3];
+            bf16x8 ph, pl;
+            split8(p8, ph, pl);
+            for (int db = 0; db < 8; ++db) {
+              oacc[qi][db] = M::mma(ph, vb[db], oacc[qi][db]);
+              oacc[qi][db] = M::mma(pl, vb[db], oacc[qi][db]);
+            }
+          }
+        }
+      }
+    }
+    if constexpr (MODE == OBS_STATS) {
+      // online softmax statistics, one (lazy) rescale per tile
+      for (int qi = 0; qi < QPW; ++qi) {
+        if (!qactive[qi]) continue;
+        float tmax = xs[qi][0][0];
+        for (int kb = 0; kb < 4; ++kb)
+          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, xs[qi][kb][r]);
+        if (tmax > m_run[qi] + kLazy) {
+          l_run[qi] *= exp2_fast(m_run[qi] - tmax);
+          m_run[qi] = tmax;
+        }
+        float l = l_run[qi];
+        for (int kb = 0; kb < 4; ++kb)
+          for (int r = 0; r < 4; ++r) l += exp2_fast(xs[qi][kb][r] - m_run[qi]);
+        l_run[qi] = l;
+      }
+    }
+    if constexpr (HAS_G) {
+      if (__builtin_amdgcn_ballot_w64(cancel) != 0) util_exact(t0, c, colsum);
+    }
+    if constexpr (HAS_PART) {
+      // per-key sums over this wave's 16 query columns (DPP within rows of 16)
+      float* pw = part[it & 1][wave];
+      for (int kb = 0; kb < 4; ++kb) {
+        const float v0 = row_sum(colsum[kb][0]), v1 = row_sum(colsum[kb][1]);
+        const float v2 = row_sum(colsum[kb][2]), v3 = row_sum(colsum[kb][3]);
+        if (col < 4) pw[kb * 16 + kg * 4 + col] = col == 0 ? v0 : col == 1 ? v1 : col == 2 ? v2 : v3;
+      }
+      if constexpr (HAS_G) {
+        if (wave == 0) pflag[it & 1][lane] = reinterpret_cast<const int*>(c.S)[2 * kObsTK + lane] >= 0 ? 1.0f : 0.0f;
+      }
+    }
+  };
+
+  // ---- one step: tile `it` from buffers c while tile it+STAGES-1 is copied into buffers n
+  auto step = [&](int it, const ObsBufs& c, const ObsBufs& n) {
+    __syncthreads();
+    if (it > 0) combine(it - 1);
+    int issued = 0;
+    if (it + STAGES - 1 < ntiles) issued = issue(it + STAGES - 1, n);
+    compute(it, c);
+    // tile it+1 must have landed; with three stages this step's copies (tile
+    // it+2) may stay in flight
+    wait_vm_le(STAGES > 2 ? issued : 0);
+  };
+
+  const ObsBufs B0{K0, V0, G0, S0}, B1{K1, V1, G1, S1}, B2{K2, V2, G2, S2};
+  // ---- prologue: tiles 0 .. STAGES-2
+  if constexpr (HAS_G) {
+    __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));
+    __syncthreads();
+  }
+  issue(0, B0);
+  {
+    int later = 0;
+    if (STAGES > 2 && ntiles > 1) later = issue(1, B1);
+    wait_vm_le(later);
+  }
+  if constexpr (STAGES == 2) {
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, B0, B1);
+      if (it + 1 >= ntiles) break;
+      step(it + 1, B1, B0);
+    }
+  } else {
+    for (int it = 0; it < ntiles; it += 3) {
+      step(it, B0, B2);
+      if (it + 1 >= ntiles) break;
+      step(it + 1, B1, B0);
+      if (it + 2 >= ntiles) break;
+      step(it + 2, B2, B1);
+    }
+  }
+  __syncthreads();
+  combine(ntiles - 1);
+
+  if constexpr (MODE == OBS_STATS) {
+    for (int qi = 0; qi < QPW; ++qi) {
+      float m = l_run[qi] > 0.0f ? m_run[qi] : -INFINITY, l = l_run[qi];
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float m2 = __shfl_xor(m, o, 64), l2 = __shfl_xor(l, o, 64);
+        const float mx = fmaxf(m, m2);
+        if (mx > -INFINITY) {
+          l = l * exp2_fast(m - mx) + l2 * exp2_fast(m2 - mx);
+          m = mx;
+        }
+      }
+      const int qb = wave + qi * nw;
+      if (kg == 0 && qb * 16 < a.GQp) a.ml_part[(uh * a.S1 + s) * a.GQp + qb * 16 + col] = make_float2(m, l);
+    }
+  }
+  if constexpr (MODE == OBS_SCORE) {
+    for (int qi = 0; qi < QPW; ++qi) {
+      const int qb = wave + qi * nw;
+      if (qb * 16 >= a.GQp) continue;
+      for (int db = 0; db < 8; ++db)
+        for (int r = 0; r < 4; ++r) {
+          const int q = qb * 16 + kg * 4 + r;
+          a.o_part[((uh * a.S1 + s) * a.GQp + q) * D + db * 16 + col] = oacc[qi][db][r];
+        }
+    }
+  }
+}
+
+}  // namespace akv
