@@ -9,16 +9,13 @@
 // Sources: Pith review of AnchorKV ("What carries the argument",
 // "Assumptions & free parameters"); AnchorKV-adapted page ("Evidence",
 // "Adaptation notes").
+#include "launch_common.hpp"
 #include "obs_kernels.hpp"
 #include "obs_pipe.hpp"
+#include "assign_kernels.hpp"
 
 namespace akv {
 
-#define AKV_CHECK_LAUNCH(name)                                                              \
-  do {                                                                                      \
-    hipError_t e_ = hipGetLastError();                                                      \
-    if (e_ != hipSuccess) return fail(ANCHORKV_E_HIP, "%s: %s", name, hipGetErrorString(e_)); \
-  } while (0)
 
 // Fill kernel (used instead of a memset so the sequence stays capture-safe).
 __global__ void k_zero_u32(unsigned* p, int64_t n) {
@@ -701,6 +698,63 @@ static int launch_obs(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t
   return 0;
 }
 
+// Nearest-anchor assignment, bf16: one LDS-resident launch when the anchors
+// of a head fit, else parts folded with atomicMax and a projection pass.
+static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, const ObsArgs& oa, const void* K,
+                              const void* V, uint8_t* cache, uint8_t* ws, hipStream_t st) {
+  const int U = p.units, H = p.H, N = p.N, A = p.A;
+  AssignArgs g{};
+  g.K = reinterpret_cast<const uint16_t*>(K);
+  g.V = reinterpret_cast<const uint16_t*>(V);
+  g.cache = cache; g.stride = p.unit_stride;
+  g.off_anchor_k = p.off_anchor_k; g.off_anchor_v = p.off_anchor_v; g.off_words = p.off_words;
+  g.anorm = reinterpret_cast<const float2*>(ws + w.anorm);
+  g.anchor_of = oa.anchor_of;
+  g.aidx = reinterpret_cast<int*>(ws + w.aidx);
+  g.gam = reinterpret_cast<float*>(ws + w.gam);
+  g.rn2 = reinterpret_cast<float*>(ws + w.rn2);
+  g.vn2 = reinterpret_cast<float*>(ws + w.vn2);
+  g.score = oa.score;
+  g.util = oa.util;
+  g.best64 = reinterpret_cast<unsigned long long*>(ws + w.best64);
+  g.H = H; g.N = N; g.A = A;
+  const int ntiles_hs = (N + kAssignTile - 1) / kAssignTile;
+  const int64_t hs = (int64_t)U * 2 * H;
+  // about 4 blocks per compute unit in total, at least one tile each
+  int tpb = (int)std::max<int64_t>(1, (hs * ntiles_hs) / 1024);
+  tpb = std::min(tpb, ntiles_hs);
+  g.tiles_per_block = tpb;
+  g.nblk = (ntiles_hs + tpb - 1) / tpb;
+  const unsigned grid = (unsigned)(hs * g.nblk);
+  auto lds_for = [](int nA) {
+    const size_t rows = (size_t)((nA + 15) / 16) * 16;
+    return rows * kHeadDim * 2 + rows * 4 + 8 * 16 * 17 * 4;
+  };
+  if (A <= kAssignResMax) {
+    static size_t done = 0;
+    const size_t lds = lds_for(A);
+    if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<false>), lds, &done)) return rc;
+    g.a0 = 0; g.a1 = A;
+    k_assign_res<false><<<grid, 512, lds, st>>>(g);
+    AKV_CHECK_LAUNCH("k_assign_res");
+    return 0;
+  }
+  static size_t done_p = 0;
+  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<true>), lds_for(kAssignResMax), &done_p)) return rc;
+  const int64_t total = hs * N;
+  k_zero_u32<<<(unsigned)((2 * total + 255) / 256), 256, 0, st>>>(
+      reinterpret_cast<unsigned*>(g.best64), 2 * total);
+  AKV_CHECK_LAUNCH("k_zero_u32");
+  for (int a0 = 0; a0 < A; a0 += kAssignResMax) {
+    g.a0 = a0; g.a1 = std::min(A, a0 + kAssignResMax);
+    k_assign_res<true><<<grid, 512, lds_for(g.a1 - g.a0), st>>>(g);
+    AKV_CHECK_LAUNCH("k_assign_res");
+  }
+  k_assign_proj<<<(unsigned)((total + 63) / 64), 256, 0, st>>>(g, total);
+  AKV_CHECK_LAUNCH("k_assign_proj");
+  return 0;
+}
+
 template <int DT>
 static int compress_impl(const anchorkv_plan_info& p, const void* K, const void* V, const void* Q, void* cache_v,
                          void* ws_v, hipStream_t st) {
@@ -765,13 +819,17 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   AKV_CHECK_LAUNCH("k_select");
   prof_mark(st, "select");
 
-  const int ntiles = (N + 255) / 256;
-  k_assign<DT><<<(unsigned)((int64_t)U * 2 * H * ntiles), 256, 0, st>>>(
-      K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_words,
-      reinterpret_cast<const float2*>(ws + w.anorm), a.anchor_of, reinterpret_cast<int*>(ws + w.aidx),
-      reinterpret_cast<float*>(ws + w.gam), reinterpret_cast<float*>(ws + w.rn2), reinterpret_cast<float*>(ws + w.vn2),
-      a.score, a.util, H, N, A, ntiles);
-  AKV_CHECK_LAUNCH("k_assign");
+  if constexpr (DT == ANCHORKV_BF16) {
+    if ((rc = launch_assign_bf16(p, w, a, K, V, cache, ws, st))) return rc;
+  } else {
+    const int ntiles = (N + 255) / 256;
+    k_assign<DT><<<(unsigned)((int64_t)U * 2 * H * ntiles), 256, 0, st>>>(
+        K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_words,
+        reinterpret_cast<const float2*>(ws + w.anorm), a.anchor_of, reinterpret_cast<int*>(ws + w.aidx),
+        reinterpret_cast<float*>(ws + w.gam), reinterpret_cast<float*>(ws + w.rn2), reinterpret_cast<float*>(ws + w.vn2),
+        a.score, a.util, H, N, A, ntiles);
+    AKV_CHECK_LAUNCH("k_assign");
+  }
   prof_mark(st, "assign");
 
   if ((rc = launch_obs<DT, OBS_UTIL>(p, a, st))) return rc;

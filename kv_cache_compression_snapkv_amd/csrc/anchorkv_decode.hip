@@ -23,16 +23,12 @@
 // shared by the workgroup and only raised (rescaling w, l and the
 // accumulators) when a tile exceeds it by more than 2^8.
 #include "device_common.hpp"
+#include "launch_common.hpp"
 
 #include <type_traits>
 
 namespace akv {
 
-#define AKV_CHECK_LAUNCH(name)                                                              \
-  do {                                                                                      \
-    hipError_t e_ = hipGetLastError();                                                      \
-    if (e_ != hipSuccess) return fail(ANCHORKV_E_HIP, "%s: %s", name, hipGetErrorString(e_)); \
-  } while (0)
 
 constexpr int kMaxG = 8;          // q-heads per KV head supported by decode
 constexpr int kTile = 1024;       // tokens per tile (= residual-offset chunk)
@@ -528,15 +524,6 @@ __global__ __launch_bounds__(256) void k_dec_combine(const uint8_t* cache, int64
 }
 
 // Raise a kernel's dynamic-LDS limit to `bytes` (once per larger value).
-static int set_dyn_lds(const void* fn, size_t bytes, size_t* done) {
-  if (bytes <= *done) return 0;
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(ANCHORKV_E_SHAPE, "decode: %zu bytes of LDS not available for this shape", bytes);
-  }
-  *done = bytes;
-  return 0;
-}
 
 static size_t stream_lds(int G, int A, int KP) {
   return sizeof(float) * (((size_t)G * A + 1) & ~(size_t)1) + 8 * (size_t)G * A + sizeof(float) * (size_t)kTile * G +

@@ -17,6 +17,7 @@ constexpr int kHeadDim = 128;         // the only supported head dim
 constexpr uint32_t kMagic = 0x31564B41u;  // "AKV1"
 constexpr int kMaxAnchors = 32767;
 constexpr int kHistBins = 2048;       // radix-select digit bins (11 bits)
+constexpr int kAssignResMax = 512;    // anchors per LDS-resident part of the bf16 assignment
 
 void set_error(const char* fmt, ...);
 int fail(int code, const char* fmt, ...);
@@ -44,6 +45,7 @@ struct CompressWs {
   int64_t oo;      // f32 [U][H][GQp] ||o||^2
   int64_t anchor_of; // int32 [U][H][N] anchor index of a position, -1 if none
   int64_t vn2;     // f32 [U][H][N] ||v_t||^2
+  int64_t best64;  // u64 [U][2][H][N] packed part winners (bf16, A > kAssignResMax only)
   int64_t anorm;   // float2 [U][2][H][A] (||x_a||^2, 1/||x_a||)
   int64_t pooled;  // f32 [U][H][N]
   int64_t hist;    // u32 [U][2][kHistBins]
