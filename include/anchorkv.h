@@ -148,7 +148,8 @@ int anchorkv_compress(const anchorkv_plan_info* plan, const void* K, const void*
 /* Offsets (bytes from the workspace start) of compress intermediates, for
  * inspection in tests: [0] score f32 [U][H][N]; [1] m,1/l float2 [U][H][GQp];
  * [2] o f32 [U][H][GQp][D]; [3] utilities f32 [U][2][H][N] (-1 for anchors);
- * [4] unrounded gamma f32 [U][2][H][N]; [5] residual norm^2 f32 [U][2][H][N];
+ * [4] unrounded gamma f32 [U][2][H][N]; [5] residual norm^2 f32 [U][2][H][N]
+ * (value side; the key half is 0 for bf16 caches);
  * [6] anchor index int32 [U][2][H][N].  out[7] = GQp, the number of
  * observation queries per KV head (q_per_kv * n_obs) rounded up to a multiple
  * of 16; query row g*n_obs + j is q-head g, observation j.  Returns 0 or E_ARG. */

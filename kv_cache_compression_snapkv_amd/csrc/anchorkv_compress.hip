@@ -728,14 +728,14 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
   const unsigned grid = (unsigned)(hs * g.nblk);
   auto lds_for = [](int nA) {
     const size_t rows = (size_t)((nA + 15) / 16) * 16;
-    return rows * kHeadDim * 2 + rows * 4 + 8 * 16 * 17 * 4;
+    return rows * kHeadDim * 2 + rows * 8 + kAssignWaves * (16 * 17 + 128) * 4;
   };
   if (A <= kAssignResMax) {
     static size_t done = 0;
     const size_t lds = lds_for(A);
     if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<false>), lds, &done)) return rc;
     g.a0 = 0; g.a1 = A;
-    k_assign_res<false><<<grid, 512, lds, st>>>(g);
+    k_assign_res<false><<<grid, 64 * kAssignWaves, lds, st>>>(g);
     AKV_CHECK_LAUNCH("k_assign_res");
     return 0;
   }
@@ -747,7 +747,7 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
   AKV_CHECK_LAUNCH("k_zero_u32");
   for (int a0 = 0; a0 < A; a0 += kAssignResMax) {
     g.a0 = a0; g.a1 = std::min(A, a0 + kAssignResMax);
-    k_assign_res<true><<<grid, 512, lds_for(g.a1 - g.a0), st>>>(g);
+    k_assign_res<true><<<grid, 64 * kAssignWaves, lds_for(g.a1 - g.a0), st>>>(g);
     AKV_CHECK_LAUNCH("k_assign_res");
   }
   k_assign_proj<<<(unsigned)((total + 63) / 64), 256, 0, st>>>(g, total);

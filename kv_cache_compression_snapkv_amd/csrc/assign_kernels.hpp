@@ -5,9 +5,9 @@
 // coefficient; AnchorKV-adapted page, "Evidence": anchors map to themselves
 // with coefficient 1 and zero residual).
 //
-// Layout of the work: one block of 8 waves owns a run of 512-token tiles of
-// one (unit, side, head); each wave keeps its 64 tokens as MFMA A fragments in
-// registers (the next tile's prefetched alongside) and walks the anchors,
+// Layout of the work: one block of kAssignWaves waves owns a run of token
+// tiles (64 tokens per wave) of one (unit, side, head); each wave keeps its 64
+// tokens as MFMA A fragments in registers and walks the anchors,
 // which sit in LDS for the whole block (<= 512 anchors; larger sets are
 // processed in parts, see below).  c[t][a] = <x_t, x_a> comes from
 // v_mfma_f32_16x16x32_bf16 on exact bf16 operands and is scaled by
@@ -34,10 +34,12 @@
 #include "obs_pipe.hpp"
 
 #include <climits>
+#include <type_traits>
 
 namespace akv {
 
-constexpr int kAssignTile = 512;     // tokens per block tile (8 waves x 64)
+constexpr int kAssignWaves = 16;
+constexpr int kAssignTile = 64 * kAssignWaves;  // tokens per block tile
 
 struct AssignArgs {
   const uint16_t* K;
@@ -59,41 +61,57 @@ struct AssignArgs {
 
 // Projection epilogue of one 16-token row block: lane (col, kg) holds
 // coordinates st*32 + kg*8 .. +7 of token row col in xf[st]; `a` is the
-// token's anchor index (already forced for anchor tokens), `ar` points to the
-// anchor row (LDS tile or global memory).
+// token's anchor index (already forced for anchor tokens), `arow(c)` returns
+// 16-byte chunk c of the anchor row (LDS tile or global memory); na2 is
+// ||x_a||^2 and score the token's observation score (value side).
+// <x, x_a> and ||x||^2 come from v_dot2_f32_bf16 on the bf16 pairs (exact
+// products, f32 sums); on the value side ||r||^2 = ||x||^2 - gamma <x, x_a>,
+// recomputed coordinate by coordinate when that cancels by more than 10x.
 template <typename RowPtr>
 __device__ __forceinline__ void assign_project(const AssignArgs& g, int u, int side, int h, int t, int a, bool is_anchor,
-                                               const bf16x8 (&xf)[4], RowPtr arow, int kg) {
+                                               float na2, float score, const bf16x8 (&xf)[4], RowPtr arow, int kg) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const int64_t uh = (int64_t)u * g.H + h;
+  uint4 ach[4];
+  for (int st = 0; st < 4; ++st) ach[st] = arow(st * 4 + kg);
   float dot = 0.0f, xx = 0.0f;
-  float xs[32], as_[32];
   for (int st = 0; st < 4; ++st) {
-    const uint4 av = arow(st * 4 + kg);
-    uint16_t ab[8];
-    __builtin_memcpy(ab, &av, 16);
-    for (int e = 0; e < 8; ++e) {
-      xs[st * 8 + e] = (float)xf[st][e];
-      as_[st * 8 + e] = bf2f(ab[e]);
-      dot = fmaf(xs[st * 8 + e], as_[st * 8 + e], dot);
-      xx = fmaf(xs[st * 8 + e], xs[st * 8 + e], xx);
+    const uint4 xw = __builtin_bit_cast(uint4, xf[st]);
+    const uint32_t xv[4] = {xw.x, xw.y, xw.z, xw.w};
+    const uint32_t av[4] = {ach[st].x, ach[st].y, ach[st].z, ach[st].w};
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 xp = __builtin_bit_cast(bf16x2, xv[i]);
+      dot = __builtin_amdgcn_fdot2_f32_bf16(xp, __builtin_bit_cast(bf16x2, av[i]), dot, false);
+      if (side == 1) xx = __builtin_amdgcn_fdot2_f32_bf16(xp, xp, xx, false);
     }
   }
   dot += __shfl_xor(dot, 16, 64);
   dot += __shfl_xor(dot, 32, 64);
-  const float na2 = g.anorm[((int64_t)u * 2 * g.H + side * g.H + h) * g.A + a].x;
   float gm = na2 > 0.0f ? dot / na2 : 0.0f;
   if (is_anchor) gm = 1.0f;
   float r2 = 0.0f;
-  for (int i = 0; i < 32; ++i) {
-    const float rr = fmaf(-gm, as_[i], xs[i]);
-    r2 = fmaf(rr, rr, r2);
-  }
-  r2 += __shfl_xor(r2, 16, 64);
-  r2 += __shfl_xor(r2, 32, 64);
-  if (is_anchor) r2 = 0.0f;
   if (side == 1) {
     xx += __shfl_xor(xx, 16, 64);
     xx += __shfl_xor(xx, 32, 64);
+    r2 = fmaxf(fmaf(-gm, dot, xx), 0.0f);
+    const bool cancels = !is_anchor && r2 < 0.1f * xx;
+    if (__builtin_amdgcn_ballot_w64(cancels) != 0) {
+      float d2 = 0.0f;
+      for (int st = 0; st < 4; ++st) {
+        const uint4 xw = __builtin_bit_cast(uint4, xf[st]);
+        const uint32_t xv[4] = {xw.x, xw.y, xw.z, xw.w};
+        const uint32_t av[4] = {ach[st].x, ach[st].y, ach[st].z, ach[st].w};
+        for (int i = 0; i < 4; ++i) {
+          const float r0 = fmaf(-gm, __uint_as_float(av[i] << 16), __uint_as_float(xv[i] << 16));
+          const float r1 = fmaf(-gm, __uint_as_float(av[i] & 0xFFFF0000u), __uint_as_float(xv[i] & 0xFFFF0000u));
+          d2 = fmaf(r0, r0, fmaf(r1, r1, d2));
+        }
+      }
+      d2 += __shfl_xor(d2, 16, 64);
+      d2 += __shfl_xor(d2, 32, 64);
+      if (cancels) r2 = d2;
+    }
+    if (is_anchor) r2 = 0.0f;
   }
   if (kg == 0 && t < g.N) {
     const int64_t i = ((int64_t)u * 2 * g.H + side * g.H + h) * g.N + t;
@@ -105,13 +123,17 @@ __device__ __forceinline__ void assign_project(const AssignArgs& g, int u, int s
     if (side == 1) {
       // value channel of the utility: score_t ||r_V|| (anchors ineligible)
       g.vn2[uh * g.N + t] = xx;
-      g.util[i] = is_anchor ? -1.0f : g.score[uh * g.N + t] * sqrtf(r2);
+      g.util[i] = is_anchor ? -1.0f : score * sqrtf(r2);
     }
   }
 }
 
+// Anchor tile layout: chunk c of row r at r*16 + (c ^ (r & 15)), so the 16
+// rows an MFMA B fragment read touches land on 16 distinct chunk positions.
+__device__ __forceinline__ int res_phys(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+
 template <bool PARTIAL>
-__global__ __launch_bounds__(512) void k_assign_res(AssignArgs g) {
+__global__ __launch_bounds__(64 * kAssignWaves) void k_assign_res(AssignArgs g) {
   using M = Mfma<ANCHORKV_BF16>;
   constexpr int D = kHeadDim;
   extern __shared__ __attribute__((aligned(16))) uint4 dyn_lds[];
@@ -129,8 +151,11 @@ __global__ __launch_bounds__(512) void k_assign_res(AssignArgs g) {
   const int nA = g.a1 - g.a0;
   const int nab = (nA + 15) >> 4;
   uint4* As = dyn_lds;                                        // [nab*16 rows][16 chunks], swizzled
-  float* inv_s = reinterpret_cast<float*>(As + nab * 16 * 16);  // [nab*16]
-  int* red = reinterpret_cast<int*>(inv_s + nab * 16) + wave * (16 * 17);  // per wave [16 tokens][17]
+  float* inv_s = reinterpret_cast<float*>(As + nab * 16 * 16);  // [nab*16] 1/||x_a||
+  float* na2_s = inv_s + nab * 16;                                // [nab*16] ||x_a||^2
+  int* red = reinterpret_cast<int*>(na2_s + nab * 16) + wave * (16 * 17 + 128);  // per wave [16 tokens][17]
+  int* selfs = red + 16 * 17;                                       // per wave [64] anchor_of of its tokens
+  float* scs = reinterpret_cast<float*>(selfs + 64);                // per wave [64] observation scores
   const uint16_t* X = (side ? g.V : g.K) + uh * N * D;
   const uint16_t* AX = reinterpret_cast<const uint16_t*>(g.cache + (int64_t)u * g.stride +
                                                          (side ? g.off_anchor_v : g.off_anchor_k)) +
@@ -139,14 +164,18 @@ __global__ __launch_bounds__(512) void k_assign_res(AssignArgs g) {
 
   // ---- anchors of this part into LDS (rows beyond nA repeat the last one)
   {
-    const DmaLane dl(lane);
-    for (int jj = wave; jj < nab * 4; jj += 8) {
-      const int r = min(jj * 4 + dl.rsub, nA - 1);
-      dma16(AX + (int64_t)(g.a0 + r) * D + ((jj & 1) ? dl.c1 : dl.c0) * 8, As + jj * 64);
+    for (int jj = wave; jj < nab * 4; jj += kAssignWaves) {
+      const int r = jj * 4 + (lane >> 4);               // tile row of this lane's chunk
+      const int c = (lane & 15) ^ (r & 15);             // its logical chunk
+      dma16(AX + (int64_t)(g.a0 + min(r, nA - 1)) * D + c * 8, As + jj * 64);
     }
     // padding rows copy the last anchor (row and 1/||x_a||): they tie with it
     // and lose on the column, so they never win
-    for (int i = threadIdx.x; i < nab * 16; i += blockDim.x) inv_s[i] = an[g.a0 + min(i, nA - 1)].y;
+    for (int i = threadIdx.x; i < nab * 16; i += blockDim.x) {
+      const float2 v = an[g.a0 + min(i, nA - 1)];
+      inv_s[i] = v.y;
+      na2_s[i] = v.x;
+    }
     __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));
     __syncthreads();
   }
@@ -170,39 +199,54 @@ __global__ __launch_bounds__(512) void k_assign_res(AssignArgs g) {
   // the mask lives in a VGPR so that (bits & mask) | tag is one v_and_or_b32
   unsigned keymask;
   __asm__("v_mov_b32 %0, 0xffffffe0" : "=v"(keymask));
-  auto search = [&](const bf16x8 (&xt)[4][4], int (&best)[4][4], bool mono) {
+  auto search = [&](const bf16x8 (&xt)[4][4], int (&best)[4][4], auto mono_tag) {
+    constexpr bool mono = decltype(mono_tag)::value;
     for (int rb = 0; rb < 4; ++rb)
       for (int r = 0; r < 4; ++r) best[rb][r] = INT_MIN;
-    for (int ab = 0; ab < nab; ++ab) {
-      bf16x8 bf[4];
-      for (int st = 0; st < 4; ++st) bf[st] = bits_to_frag(As[obs_phys(ab * 16 + col, st * 4 + kg)]);
+    auto mfmas = [&](int ab, f32x4 (&acc)[4]) {
+      for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0, 0, 0, 0};
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 bf = bits_to_frag(As[res_phys(ab * 16 + col, st * 4 + kg)]);
+        for (int rb = 0; rb < 4; ++rb) acc[rb] = M::mma(xt[rb][st], bf, acc[rb]);
+      }
+    };
+    auto keys = [&](int ab, const f32x4 (&acc)[4]) {
       const float inv = inv_s[ab * 16 + col];
       const unsigned tag = 31u - (unsigned)ab;
-      for (int rb = 0; rb < 4; ++rb) {
-        f32x4 acc = {0, 0, 0, 0};
-        for (int st = 0; st < 4; ++st) acc = M::mma(xt[rb][st], bf[st], acc);
+      for (int rb = 0; rb < 4; ++rb)
         for (int r = 0; r < 4; ++r) {
-          unsigned b = __float_as_uint(acc[r] * inv);
-          if (mono) b ^= (unsigned)((int)b >> 31) & 0x7FFFFFFFu;
+          unsigned b = __float_as_uint(acc[rb][r] * inv);
+          if constexpr (mono) b ^= (unsigned)((int)b >> 31) & 0x7FFFFFFFu;
           const int key = (int)((b & keymask) | tag);
           best[rb][r] = max(best[rb][r], key);
         }
-      }
-    }
+    };
+    f32x4 acc0[4];
+    for (int ab = 0; ab < nab; ++ab) { mfmas(ab, acc0); keys(ab, acc0); }
   };
 
-  bf16x8 xf[4][4], xn[4][4];
+  bf16x8 xf[4][4];
   if (tile0 < tile1) load_tokens(tile0, xf);
   for (int tile = tile0; tile < tile1; ++tile) {
-    if (tile + 1 < tile1) load_tokens(tile + 1, xn);
+    // per-token scalars of the epilogue, copied into this wave's LDS slots
+    // while the search runs (no registers held across it)
+    {
+      const int t = min(tile * kAssignTile + wave * 64 + lane, N - 1);
+      dma4(g.anchor_of + uh * N + t, selfs);
+      if (side) dma4(g.score + uh * N + t, scs);
+    }
     int best[4][4];
-    search(xf, best, false);
+    search(xf, best, std::false_type{});
     bool neg = false;
     for (int rb = 0; rb < 4; ++rb)
       for (int r = 0; r < 4; ++r) neg |= best[rb][r] < 0;
     const bool mono = __builtin_amdgcn_ballot_w64(neg) != 0;
-    if (mono) search(xf, best, true);
-    // ---- per 16-token row block: reduce the 16 anchor columns, then project
+    if (mono) search(xf, best, std::true_type{});
+    __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));   // this wave's copies of selfs / scs
+    // next tile's tokens load while this tile's columns are reduced and projected
+    // ---- reduce the 16 anchor columns of every token (lowest column on
+    // equal keys); lane l < 16 ends up with the winner of token row l
+    int wins[4];
     for (int rb = 0; rb < 4; ++rb) {
       for (int r = 0; r < 4; ++r) red[(kg * 4 + r) * 17 + col] = best[rb][r];
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
@@ -215,29 +259,32 @@ __global__ __launch_bounds__(512) void k_assign_res(AssignArgs g) {
         }
         win = g.a0 + win + 16 * (31 - (wkey & 31));
       }
-      const int tt = tile * kAssignTile + wave * 64 + rb * 16;
+      wins[rb] = win;
       if constexpr (PARTIAL) {
+        const int tt = tile * kAssignTile + wave * 64 + rb * 16;
         if (lane < 16 && tt + lane < N) {
           // signed-monotone key -> unsigned order, then ~index for lowest-index ties
           const unsigned long long key64 = ((unsigned long long)(((unsigned)wkey & keymask) ^ 0x80000000u) << 32) |
                                            (unsigned long long)(0xFFFFFFFFu - (unsigned)win);
           atomicMax(g.best64 + ((int64_t)u * 2 * g.H + side * g.H + h) * N + tt + lane, key64);
         }
-      } else {
-        int a = __shfl(win, col, 64);
-        const int t = tt + col;
-        const int self = g.anchor_of[uh * N + min(t, N - 1)];
-        const bool is_anchor = self >= 0;
-        if (is_anchor) a = self;
-        assign_project(g, u, side, h, t, a, is_anchor, xf[rb],
-                       [&](int c) { return As[obs_phys(a - g.a0, c)]; }, kg);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads of red done before the next row block writes it
       __builtin_amdgcn_wave_barrier();
     }
-    if (tile + 1 < tile1)
-      for (int rb = 0; rb < 4; ++rb)
-        for (int st = 0; st < 4; ++st) xf[rb][st] = xn[rb][st];
+    // ---- projection of every token onto its anchor
+    if constexpr (!PARTIAL) {
+      for (int rb = 0; rb < 4; ++rb) {
+        const int t = tile * kAssignTile + wave * 64 + rb * 16 + col;
+        const int self = selfs[rb * 16 + col];
+        const bool is_anchor = self >= 0;
+        const int w = __shfl(wins[rb], col, 64);   // every lane takes part in the shuffle
+        const int a = is_anchor ? self : w;
+        assign_project(g, u, side, h, t, a, is_anchor, na2_s[a], scs[rb * 16 + col], xf[rb],
+                       [&](int c) { return As[res_phys(a - g.a0, c)]; }, kg);
+      }
+    }
+    if (tile + 1 < tile1) load_tokens(tile + 1, xf);
   }
 }
 
@@ -266,7 +313,9 @@ __global__ __launch_bounds__(256) void k_assign_proj(AssignArgs g, int64_t total
   const bool is_anchor = self >= 0;
   const unsigned long long key = g.best64[tk];
   const int a = is_anchor ? self : (int)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
-  assign_project(g, u, side, h, live ? t : g.N, a, is_anchor, xf,
+  const float na2 = g.anorm[((int64_t)u * 2 * g.H + side * g.H + h) * g.A + a].x;
+  const float sc = side ? g.score[uh * g.N + t] : 0.0f;
+  assign_project(g, u, side, h, live ? t : g.N, a, is_anchor, na2, sc, xf,
                  [&](int c) { return *reinterpret_cast<const uint4*>(AX + (int64_t)a * D + c * 8); }, kg);
 }
 
