@@ -108,6 +108,87 @@ def cpu_baseline(w, units_sample=3):
                       f"{per_unit:.2f} s/unit, extrapolated to all units"}
 
 
+# ---- HBM traffic from rocprofv3 counters (FETCH_SIZE / WRITE_SIZE, KiB per
+# dispatch), scaled by what the same counters read for a copy of known size.
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe():
+    """A plain device-to-device copy of COPY_PROBE_BYTES, three times: the
+    calibration workload of the traffic counters."""
+    import torch
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "repeats": 3}), flush=True)
+
+
+def kernel_stage(name):
+    """Stage of the hot path that a kernel (rocprofv3 kernel name) belongs to."""
+    import re
+    m = re.search(r"k_obs_pipe<(\d)", name) or re.search(r"k_obs<\d, (\d)", name)
+    if m:
+        return {0: "obs_stats", 1: "obs_score", 2: "obs_util", 3: "util_fix"}[int(m.group(1))]
+    for key, stage in (("k_ml_combine", "ml_combine"), ("k_o_combine", "o_combine"), ("k_select", "select"),
+                       ("k_assign", "assign"), ("k_topr", "topr"), ("k_quant", "quant"), ("k_headers", "headers"),
+                       ("k_dec_stab", "dec_stab"), ("k_dec_stream", "dec_stream"), ("k_dec_combine", "dec_combine"),
+                       ("k_zero_u32", "zero")):
+        if key in name:
+            return stage
+    return None
+
+
+def read_counters(d, counter):
+    """[(kernel name, value)] of one counter over all dispatches in a rocprofv3 csv output folder."""
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+    """profiles/traffic_<workload>.json: scaled HBM bytes per launch of every stage."""
+    def copy_kib(d, counter):
+        vals = [v for n, v in read_counters(d, counter) if "copyBuffer" in n or "copy" in n.lower()]
+        if not vals:
+            raise SystemExit(f"no copy kernel in {d}")
+        return max(vals)
+    cf, cw = copy_kib(copy_fetch_dir, "FETCH_SIZE"), copy_kib(copy_write_dir, "WRITE_SIZE")
+    f_scale, w_scale = COPY_PROBE_BYTES / (cf * 1024.0), COPY_PROBE_BYTES / (cw * 1024.0)
+    per = {}
+    for d, counter, key in ((fetch_dir, "FETCH_SIZE", "fetch"), (write_dir, "WRITE_SIZE", "write")):
+        for name, v in read_counters(d, counter):
+            st = kernel_stage(name)
+            if st is None:
+                continue
+            e = per.setdefault(st, {"fetch": 0.0, "write": 0.0, "n_fetch": 0, "n_write": 0})
+            e[key] += v * 1024.0
+            e["n_" + key] += 1
+    calls = max(1, per.get("headers", {}).get("n_fetch", 1))
+    dec_calls = max(1, per.get("dec_stab", {}).get("n_fetch", 1))
+    stages = {}
+    for st, e in per.items():
+        n = dec_calls if st.startswith("dec_") else calls
+        fb, wb = e["fetch"] * f_scale / n, e["write"] * w_scale / n
+        stages[st] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb, "dispatches_per_call": e["n_fetch"] / n}
+    out = {"workload": workload, "source_hash": kernel_source_hash(), "unit": "bytes per call of the stage",
+           "copy_calibration": {"bytes": COPY_PROBE_BYTES, "fetch_counter_bytes": cf * 1024.0,
+                                "write_counter_bytes": cw * 1024.0, "fetch_scale": f_scale, "write_scale": w_scale},
+           "commands": commands, "stages": stages}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps({"written": path, "stages": {k: round(v["bytes"] / 1e6, 2) for k, v in stages.items()}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +197,17 @@ def main():
     ap.add_argument("--workload", default="llama3b_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1, help="decode steps per step (default 1)")
+    ap.add_argument("--copy-probe", action="store_true", help="run only the traffic-counter calibration copy")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from four rocprofv3 --pmc csv folders")
+    ap.add_argument("--traffic-command", action="append", default=[], help="command recorded with --traffic-summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.workload, *args.traffic_summary, args.traffic_command)
+        return
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -174,7 +265,8 @@ def main():
         agg[name] = agg.get(name, 0.0) + ms
         cnt[name] = cnt.get(name, 0) + 1
     stage_ms = {k: agg[k] / cnt[k] for k in agg}           # average per launch
-    comp_stages = ["obs_stats", "ml_combine", "obs_score", "o_combine", "select", "assign", "obs_util", "topr", "quant"]
+    comp_stages = ["obs_stats", "ml_combine", "obs_score", "o_combine", "select", "assign", "obs_util", "util_fix",
+                   "topr", "quant"]
     dec_stages = ["dec_stab", "dec_stream", "dec_combine"]
     compress_ms = sum(stage_ms.get(k, 0.0) for k in comp_stages)
     decode_ms = sum(stage_ms.get(k, 0.0) for k in dec_stages)
@@ -184,8 +276,8 @@ def main():
     tf = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     if os.path.exists(tf):
         t = json.load(open(tf))
-        if t.get("source_hash") == kernel_source_hash() and dom in t.get("kernels", {}):
-            traffic = t["kernels"][dom]
+        if t.get("source_hash") == kernel_source_hash() and dom in t.get("stages", {}):
+            traffic = t["stages"][dom]["bytes"]
     rl["traffic"] = traffic
     dec_b = decode_bytes(p)
     seq_tokens = w.seqs * w.n_tokens

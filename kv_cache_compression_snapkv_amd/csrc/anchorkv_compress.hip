@@ -687,9 +687,17 @@ static int launch_obs(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t
   const dim3 block(64 * nw);
   if constexpr (DT == ANCHORKV_BF16) {
     const dim3 grid((unsigned)((int64_t)p.units * p.H * (MODE == OBS_UTIL ? a.S1u : a.S1)));
-    constexpr int ST = 2;
-    if (qpw == 1) k_obs_pipe<MODE, 1, ST><<<grid, block, 0, st>>>(a);
-    else k_obs_pipe<MODE, 2, ST><<<grid, block, 0, st>>>(a);
+    using C1 = ObsPipeCfg<MODE, 1>;
+    using C2 = ObsPipeCfg<MODE, 2>;
+    if (qpw == 1) k_obs_pipe<MODE, 1, C1::TK, C1::ST, 2><<<grid, block, 0, st>>>(a);
+    else k_obs_pipe<MODE, 2, C2::TK, C2::ST, 2><<<grid, block, 0, st>>>(a);
+    if constexpr (MODE == OBS_UTIL) {
+      // exact recompute of the tiles the fast pass flagged (its own stage)
+      AKV_CHECK_LAUNCH("k_obs_pipe");
+      prof_mark(st, "obs_util");
+      if (qpw == 1) k_obs_pipe<OBS_UTILX, 1, kObsUtilTK, 1, 2><<<grid, block, 0, st>>>(a);
+      else k_obs_pipe<OBS_UTILX, 2, kObsUtilTK, 1, 2><<<grid, block, 0, st>>>(a);
+    }
   } else {
     const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1));
     k_obs<DT, MODE, 1><<<grid, block, 0, st>>>(a);
@@ -786,6 +794,8 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   a.anchor_of = reinterpret_cast<const int*>(ws + w.anchor_of);
   a.vn2 = reinterpret_cast<const float*>(ws + w.vn2);
   a.util = reinterpret_cast<float*>(ws + w.util);
+  a.uflag = ws + w.uflag;
+  a.nflag = (N + kObsUtilTK - 1) / kObsUtilTK;
   a.U = U; a.H = H; a.G = p.G; a.N = N; a.n_obs = p.n_obs; a.GQ = GQ; a.GQp = w.GQp; a.S1 = w.S1;
   a.kps = (int)round_up((N + w.S1 - 1) / w.S1, 64);
   a.S1u = std::max(w.S1, (N + kObsUtilMaxKeys - 1) / kObsUtilMaxKeys);
@@ -833,7 +843,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   prof_mark(st, "assign");
 
   if ((rc = launch_obs<DT, OBS_UTIL>(p, a, st))) return rc;
-  prof_mark(st, "obs_util");
+  prof_mark(st, DT == ANCHORKV_BF16 ? "util_fix" : "obs_util");
 
   // top-R per (unit, side); R_K == R_V
   const int R = p.R_K;

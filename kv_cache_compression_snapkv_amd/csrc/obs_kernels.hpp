@@ -25,7 +25,7 @@
 
 namespace akv {
 
-enum { OBS_STATS = 0, OBS_SCORE = 1, OBS_UTIL = 2 };
+enum { OBS_STATS = 0, OBS_SCORE = 1, OBS_UTIL = 2, OBS_UTILX = 3 };
 
 struct ObsArgs {
   const void* K;
@@ -46,6 +46,8 @@ struct ObsArgs {
   const int* anchor_of;  // [U][H][N]
   const float* vn2;      // [U][H][N] ||v_t||^2
   float* util;           // [U][2][H][N]
+  uint8_t* uflag;        // [U][H][nflag] UTIL tile flags (bf16 path): 1 = recompute in UTILX
+  int nflag;             // tile flags per (unit, head)
   int U, H, G, N, n_obs, GQ, GQp, S1, kps, A;
   int S1u, kps_u;         // key splits of the pipelined UTIL kernel (<= 2048 keys each)
   float c;               // log2(e)/sqrt(D)
