@@ -689,14 +689,19 @@ static int launch_obs(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t
     const dim3 grid((unsigned)((int64_t)p.units * p.H * (MODE == OBS_UTIL ? a.S1u : a.S1)));
     using C1 = ObsPipeCfg<MODE, 1>;
     using C2 = ObsPipeCfg<MODE, 2>;
-    if (qpw == 1) k_obs_pipe<MODE, 1, C1::TK, C1::ST, 2><<<grid, block, 0, st>>>(a);
-    else k_obs_pipe<MODE, 2, C2::TK, C2::ST, 2><<<grid, block, 0, st>>>(a);
     if constexpr (MODE == OBS_UTIL) {
+      // up to 6 query blocks: two key splits (12 waves, 3 per SIMD)
+      if (qpw == 1 && nw <= 6) k_obs_pipe<MODE, 1, C1::TK, C1::ST, 2, 3><<<grid, dim3(2 * 64 * nw), 0, st>>>(a);
+      else if (qpw == 1) k_obs_pipe<MODE, 1, C1::TK, C1::ST, 1, 2><<<grid, block, 0, st>>>(a);
+      else k_obs_pipe<MODE, 2, C2::TK, C2::ST, 1, 2><<<grid, block, 0, st>>>(a);
       // exact recompute of the tiles the fast pass flagged (its own stage)
       AKV_CHECK_LAUNCH("k_obs_pipe");
       prof_mark(st, "obs_util");
-      if (qpw == 1) k_obs_pipe<OBS_UTILX, 1, kObsUtilTK, 1, 2><<<grid, block, 0, st>>>(a);
-      else k_obs_pipe<OBS_UTILX, 2, kObsUtilTK, 1, 2><<<grid, block, 0, st>>>(a);
+      if (qpw == 1) k_obs_pipe<OBS_UTILX, 1, kObsUtilTK, 1, 1, 2><<<grid, block, 0, st>>>(a);
+      else k_obs_pipe<OBS_UTILX, 2, kObsUtilTK, 1, 1, 2><<<grid, block, 0, st>>>(a);
+    } else {
+      if (qpw == 1) k_obs_pipe<MODE, 1, C1::TK, C1::ST, 1, 2><<<grid, block, 0, st>>>(a);
+      else k_obs_pipe<MODE, 2, C2::TK, C2::ST, 1, 2><<<grid, block, 0, st>>>(a);
     }
   } else {
     const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1));

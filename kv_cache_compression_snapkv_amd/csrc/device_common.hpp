@@ -104,6 +104,8 @@ constexpr int kDppXor1 = 0xB1;   // quad_perm(1,0,3,2)
 constexpr int kDppXor2 = 0x4E;   // quad_perm(2,3,0,1)
 constexpr int kDppRor4 = 0x124;  // row_ror:4
 constexpr int kDppRor8 = 0x128;  // row_ror:8
+constexpr int kDppRowMirror = 0x140;   // lane i of a row of 16 <- lane 15 - i
+constexpr int kDppHalfMirror = 0x141;  // lane i of a half-row of 8 <- lane 7 - i
 
 // Sum / max over each group of 4 lanes (l & ~3 .. l | 3); every lane gets it.
 __device__ __forceinline__ float quad_sum(float v) {
@@ -115,6 +117,20 @@ __device__ __forceinline__ float row_sum(float v) {
   v += dpp<kDppRor8>(v);
   v += dpp<kDppRor4>(v);
   return quad_sum(v);
+}
+// Sums over each row of 16 lanes of four per-lane values v[0..3], scattered:
+// every lane of the quad (l >> 2) & 3 = j ends up with the row sum of v[j]
+// (11 VALU operations instead of four full row sums).
+__device__ __forceinline__ float row_sum4_scatter(const float (&v)[4], int col) {
+  const bool hi8 = (col & 8) != 0, hi4 = (col & 4) != 0;
+  // lanes col and 15 - col: keep v[0], v[1] (col < 8) or v[2], v[3]; add the partner's
+  const float s0 = hi8 ? v[0] : v[2], s1 = hi8 ? v[1] : v[3];
+  const float a0 = (hi8 ? v[2] : v[0]) + dpp<kDppRowMirror>(s0);
+  const float a1 = (hi8 ? v[3] : v[1]) + dpp<kDppRowMirror>(s1);
+  // lanes col and 7 - col of the half: keep one value
+  const float sb = hi4 ? a0 : a1;
+  const float b = (hi4 ? a1 : a0) + dpp<kDppHalfMirror>(sb);
+  return quad_sum(b);
 }
 __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp<kDppRor8>(v));

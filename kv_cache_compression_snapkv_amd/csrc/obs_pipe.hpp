@@ -163,10 +163,13 @@ struct ObsBufs {
 };
 
 // ST: tile buffers (ST-1 tiles in flight while one is computed; UTILX uses 1).
-// WPE: waves per SIMD the register allocation must allow (3 lets two blocks
-// of up to 6 waves share a compute unit).
-template <int MODE, int QPW, int TK, int ST, int WPE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void k_obs_pipe(ObsArgs a) {
+// KS: key splits of a tile (UTIL): KS wave sets, each with every query block,
+// take 1/KS of the tile's 16-key blocks, so that a block of 6 query blocks
+// runs 12 waves (3 per SIMD) instead of 6 (2, 2, 1, 1); at most 6 query
+// blocks with two splits.
+// WPE: waves per SIMD the register allocation must allow.
+template <int MODE, int QPW, int TK, int ST, int KS, int WPE>
+__global__ __launch_bounds__(KS == 1 ? 512 : 768) __attribute__((amdgpu_waves_per_eu(WPE))) void k_obs_pipe(ObsArgs a) {
   constexpr int D = kHeadDim, NSTEP = 4, KB = TK / 16;
   constexpr bool UTILX = MODE == OBS_UTILX;
   constexpr bool HAS_V = MODE != OBS_STATS;
@@ -191,11 +194,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   __shared__ int Ai[HAS_G ? kObsUtilMaxKeys : 1];   // anchor index of every key of the range
   __shared__ float part[HAS_PART ? 2 : 1][HAS_PART ? kObsMaxWaves : 1][kObsSlot];
   __shared__ float pflag[HAS_G ? 2 : 1][kObsSlot];
-  __shared__ int tflag[MODE == OBS_UTIL ? 2 : 1][kObsMaxWaves];
+  __shared__ int tflag[MODE == OBS_UTIL ? 2 : 1][kObsMaxWaves * KS];
 
+  static_assert(KS == 1 || (KS == 2 && MODE == OBS_UTIL), "key splits only in the UTIL fast pass");
+  constexpr int KBW = KB / KS;   // 16-key blocks of a tile per wave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x >> 6;
+  const int nw = blockDim.x >> 6;          // waves of the block (copies are spread over all)
+  const int nq = nw / KS;                  // query-block waves per key split
+  const int qw = wave % nq;                // this wave's query group
+  const int kb0 = (wave / nq) * KBW;       // this wave's first 16-key block of a tile
   const int col = lane & 15, kg = lane >> 4;
   const int nsplit = HAS_G ? a.S1u : a.S1;
   const int kps = HAS_G ? a.kps_u : a.kps;
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int vis_base = N - a.n_obs;  // query j sees keys <= vis_base + j
   float oomax = 0.0f;
   for (int qi = 0; qi < QPW; ++qi) {
-    const int qb = wave + qi * nw;
+    const int qb = qw + qi * nq;
     const int q = qb * 16 + col;
     qactive[qi] = qb * 16 < a.GQp;
     const bool qvalid = qactive[qi] && q < a.GQ;
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       if (wave == it % nw) {
         const int t = k0 + it * TK + lane;
         float v = 0.0f;
-        for (int w = 0; w < nw; ++w) v += part[it & 1][w][lane];
+        for (int w = 0; w < nq; ++w) v += part[it & 1][w][lane];
         if (lane < TK && t < k1) {
           if constexpr (MODE == OBS_SCORE) {
             a.score[uh * N + t] = v;
@@ -346,12 +354,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
   };
   // per-key sums over this wave's 16 query columns (DPP within rows of 16)
-  auto write_part = [&](int it, const ObsBufs& c, float (&colsum)[KB][4]) {
-    float* pw = part[it & 1][wave];
-    for (int kb = 0; kb < KB; ++kb) {
-      const float v0 = row_sum(colsum[kb][0]), v1 = row_sum(colsum[kb][1]);
-      const float v2 = row_sum(colsum[kb][2]), v3 = row_sum(colsum[kb][3]);
-      if (col < 4) pw[kb * 16 + kg * 4 + col] = col == 0 ? v0 : col == 1 ? v1 : col == 2 ? v2 : v3;
+  // colsum[i] holds the 16-key block kbase + i
+  auto write_part = [&](int it, const ObsBufs& c, auto& colsum, int kbase) {
+    constexpr int NKB = sizeof(colsum) / sizeof(colsum[0]);
+    float* pw = part[it & 1][qw];
+    for (int i = 0; i < NKB; ++i) {
+      const float v = row_sum4_scatter(colsum[i], col);
+      if ((col & 3) == 0) pw[(kbase + i) * 16 + kg * 4 + (col >> 2)] = v;
     }
     if constexpr (HAS_G) {
       if (wave == 0) pflag[it & 1][lane] = reinterpret_cast<const int*>(c.S)[2 * kObsSlot + lane] >= 0 ? 1.0f : 0.0f;
@@ -362,13 +371,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   auto compute = [&](auto maskc, int it, const ObsBufs& c) {
     constexpr bool MASK = decltype(maskc)::value;
     const int t0 = k0 + it * TK;
-    float colsum[KB][4];
-    for (int kb = 0; kb < KB; ++kb)
+    float colsum[KBW][4];
+    for (int kb = 0; kb < KBW; ++kb)
       for (int r = 0; r < 4; ++r) colsum[kb][r] = 0.0f;
     float xs[MODE == OBS_STATS ? QPW : 1][KB][4];   // STATS: logits of the tile
     float pv[MODE == OBS_SCORE ? QPW : 1][2][4];
     uint64_t cmask = 0;                             // UTIL: lanes whose ||v - o||^2 may cancel
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kbi = 0; kbi < KBW; ++kbi) {
+      const int kb = KS == 1 ? kbi : kb0 + kbi;
       frag af[NSTEP], gf[HAS_G ? NSTEP : 1], vf[HAS_G ? NSTEP : 1];
       const int row = kb * 16 + col;
       for (int st = 0; st < NSTEP; ++st) {
@@ -407,13 +417,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
             if constexpr (MASK) p = t < kmax[qi] ? p : 0.0f;
             if constexpr (MODE == OBS_SCORE) {
               pv[qi][kb & 1][r] = p;
-              colsum[kb][r] += p;
+              colsum[kbi][r] += p;
             } else {
               // accv = <v, o> - ||o||^2 / 2, so ||v - o||^2 = ||v||^2 - 2 accv
               const float qr = fabsf(fmaf(-gm[r], accg[r], acc[r]));
               const float vo2 = fmaf(-2.0f, accv[r], vv[r]);
               cmask |= __builtin_amdgcn_ballot_w64(vo2 < thr[r]);
-              colsum[kb][r] = fmaf(p * qr, __builtin_amdgcn_sqrtf(vo2), colsum[kb][r]);
+              colsum[kbi][r] = fmaf(p * qr, __builtin_amdgcn_sqrtf(vo2), colsum[kbi][r]);
             }
           }
         }
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         l_run[qi] = l;
       }
     }
-    if constexpr (HAS_PART) write_part(it, c, colsum);
+    if constexpr (HAS_PART) write_part(it, c, colsum, KS == 1 ? 0 : kb0);
     if constexpr (MODE == OBS_UTIL) {
       if (lane == 0) tflag[it & 1][wave] = cmask != 0;
     }
@@ -499,7 +509,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
           const float sum = vv + ooq[qi];
           float vo2 = fmaf(-2.0f, accv[r], sum);
           if (vo2 < 0.5f * sum) {
-            const int q = (wave + qi * nw) * 16 + col;
+            const int q = (qw + qi * nq) * 16 + col;
             const float* orow = a.ofull + (uh * a.GQp + q) * D;
             const uint16_t* vrow = reinterpret_cast<const uint16_t*>(c.V);
             float acc2 = 0.0f;
@@ -513,7 +523,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         }
       }
     }
-    write_part(it, c, colsum);
+    write_part(it, c, colsum, 0);
   };
 
   const ObsBufs B[6] = {{K0, V0, G0, S0}, {K1, V1, G1, S1}, {K2, V2, G2, S2},
