@@ -731,36 +731,53 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
   g.util = oa.util;
   g.best64 = reinterpret_cast<unsigned long long*>(ws + w.best64);
   g.H = H; g.N = N; g.A = A;
-  const int ntiles_hs = (N + kAssignTile - 1) / kAssignTile;
   const int64_t hs = (int64_t)U * 2 * H;
-  // about 4 blocks per compute unit in total, at least one tile each
-  int tpb = (int)std::max<int64_t>(1, (hs * ntiles_hs) / 1024);
-  tpb = std::min(tpb, ntiles_hs);
-  g.tiles_per_block = tpb;
-  g.nblk = (ntiles_hs + tpb - 1) / tpb;
+  // 8-wave blocks, two per compute unit, when a part's anchors fit twice in LDS
+  const int part_a = std::min(A, kAssignResMax);
+  const bool w8 = A <= kAssignResMax && 2 * assign_lds_bytes(part_a, 8) <= 160 * 1024;
+  const int waves = w8 ? 8 : 16;
+  const int ntiles_hs = (N + 64 * waves - 1) / (64 * waves);
+  // tiles per block: fewest rounds of resident blocks times (tiles + a prologue
+  // of about half a tile), larger runs on ties
+  {
+    const int64_t slots = 256 * (w8 ? 2 : 1);
+    double best = 1e300;
+    int tpb = 1;
+    for (int c = 1; c <= ntiles_hs; ++c) {
+      const int64_t grid_c = hs * ((ntiles_hs + c - 1) / c);
+      const double cost = (double)((grid_c + slots - 1) / slots) * (c + 0.5);
+      if (cost <= best) { best = cost; tpb = c; }
+    }
+    g.tiles_per_block = tpb;
+    g.nblk = (ntiles_hs + tpb - 1) / tpb;
+  }
   const unsigned grid = (unsigned)(hs * g.nblk);
-  auto lds_for = [](int nA) {
-    const size_t rows = (size_t)((nA + 15) / 16) * 16;
-    return rows * kHeadDim * 2 + rows * 8 + kAssignWaves * (16 * 17 + 128) * 4;
-  };
   if (A <= kAssignResMax) {
-    static size_t done = 0;
-    const size_t lds = lds_for(A);
-    if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<false>), lds, &done)) return rc;
     g.a0 = 0; g.a1 = A;
-    k_assign_res<false><<<grid, 64 * kAssignWaves, lds, st>>>(g);
+    const size_t lds = assign_lds_bytes(A, waves);
+    if (w8) {
+      static size_t done = 0;
+      if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<false, 8>), lds, &done)) return rc;
+      k_assign_res<false, 8><<<grid, 64 * 8, lds, st>>>(g);
+    } else {
+      static size_t done = 0;
+      if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<false, 16>), lds, &done)) return rc;
+      k_assign_res<false, 16><<<grid, 64 * 16, lds, st>>>(g);
+    }
     AKV_CHECK_LAUNCH("k_assign_res");
     return 0;
   }
   static size_t done_p = 0;
-  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<true>), lds_for(kAssignResMax), &done_p)) return rc;
+  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<true, 16>), assign_lds_bytes(kAssignResMax, 16),
+                           &done_p))
+    return rc;
   const int64_t total = hs * N;
   k_zero_u32<<<(unsigned)((2 * total + 255) / 256), 256, 0, st>>>(
       reinterpret_cast<unsigned*>(g.best64), 2 * total);
   AKV_CHECK_LAUNCH("k_zero_u32");
   for (int a0 = 0; a0 < A; a0 += kAssignResMax) {
     g.a0 = a0; g.a1 = std::min(A, a0 + kAssignResMax);
-    k_assign_res<true><<<grid, 64 * kAssignWaves, lds_for(g.a1 - g.a0), st>>>(g);
+    k_assign_res<true, 16><<<grid, 64 * 16, assign_lds_bytes(g.a1 - g.a0, 16), st>>>(g);
     AKV_CHECK_LAUNCH("k_assign_res");
   }
   k_assign_proj<<<(unsigned)((total + 63) / 64), 256, 0, st>>>(g, total);

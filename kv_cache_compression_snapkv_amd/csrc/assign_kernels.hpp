@@ -5,7 +5,7 @@
 // coefficient; AnchorKV-adapted page, "Evidence": anchors map to themselves
 // with coefficient 1 and zero residual).
 //
-// Layout of the work: one block of kAssignWaves waves owns a run of token
+// Layout of the work: one block of 8 or 16 waves owns a run of token
 // tiles (64 tokens per wave) of one (unit, side, head); each wave keeps its 64
 // tokens as MFMA A fragments in registers and walks the anchors,
 // which sit in LDS for the whole block (<= 512 anchors; larger sets are
@@ -21,8 +21,13 @@
 // anchors can only swap order when their cosines are closer than 2^-17
 // (7.6e-6) relative, which the tie rule of the method (top-2 margin below
 // 1e-5 relative) already excuses.  The 16 anchor columns of a token are then
-// reduced through a small per-wave LDS array, lowest column first on equal
-// keys.
+// reduced with a DPP row maximum; the lowest column holding it (a ballot and
+// a bit scan) wins equal keys.
+//
+// Blocks of 8 waves run two per compute unit when the anchors of a part fit
+// twice in LDS (up to ~300 anchors), so that one block's loads (its anchors,
+// its first token tile) overlap the other's compute; larger parts use 16-wave
+// blocks, one per compute unit.
 //
 // Anchor sets larger than kAssignResMax are processed in parts: each part
 // folds its per-token winner into a 64-bit key (monotone cosine bits << 32 |
@@ -38,8 +43,12 @@
 
 namespace akv {
 
-constexpr int kAssignWaves = 16;
-constexpr int kAssignTile = 64 * kAssignWaves;  // tokens per block tile
+constexpr int kAssignSlot = 2 * 64 * 4;   // per-wave LDS bytes: token scalars of a 64-token tile
+// Dynamic LDS of a block with `waves` waves over `nA` anchors.
+inline size_t assign_lds_bytes(int nA, int waves) {
+  const size_t rows = (size_t)((nA + 15) / 16) * 16;
+  return rows * kHeadDim * 2 + rows * 8 + (size_t)waves * kAssignSlot;
+}
 
 struct AssignArgs {
   const uint16_t* K;
@@ -85,14 +94,12 @@ __device__ __forceinline__ void assign_project(const AssignArgs& g, int u, int s
       if (side == 1) xx = __builtin_amdgcn_fdot2_f32_bf16(xp, xp, xx, false);
     }
   }
-  dot += __shfl_xor(dot, 16, 64);
-  dot += __shfl_xor(dot, 32, 64);
+  dot = sum_rows4(dot);
   float gm = na2 > 0.0f ? dot / na2 : 0.0f;
   if (is_anchor) gm = 1.0f;
   float r2 = 0.0f;
   if (side == 1) {
-    xx += __shfl_xor(xx, 16, 64);
-    xx += __shfl_xor(xx, 32, 64);
+    xx = sum_rows4(xx);
     r2 = fmaxf(fmaf(-gm, dot, xx), 0.0f);
     const bool cancels = !is_anchor && r2 < 0.1f * xx;
     if (__builtin_amdgcn_ballot_w64(cancels) != 0) {
@@ -107,8 +114,7 @@ __device__ __forceinline__ void assign_project(const AssignArgs& g, int u, int s
           d2 = fmaf(r0, r0, fmaf(r1, r1, d2));
         }
       }
-      d2 += __shfl_xor(d2, 16, 64);
-      d2 += __shfl_xor(d2, 32, 64);
+      d2 = sum_rows4(d2);
       if (cancels) r2 = d2;
     }
     if (is_anchor) r2 = 0.0f;
@@ -132,8 +138,9 @@ __device__ __forceinline__ void assign_project(const AssignArgs& g, int u, int s
 // rows an MFMA B fragment read touches land on 16 distinct chunk positions.
 __device__ __forceinline__ int res_phys(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 
-template <bool PARTIAL>
-__global__ __launch_bounds__(64 * kAssignWaves) void k_assign_res(AssignArgs g) {
+template <bool PARTIAL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
+  constexpr int kTile = 64 * WAVES;   // tokens per block tile
   using M = Mfma<ANCHORKV_BF16>;
   constexpr int D = kHeadDim;
   extern __shared__ __attribute__((aligned(16))) uint4 dyn_lds[];
@@ -153,18 +160,33 @@ __global__ __launch_bounds__(64 * kAssignWaves) void k_assign_res(AssignArgs g) 
   uint4* As = dyn_lds;                                        // [nab*16 rows][16 chunks], swizzled
   float* inv_s = reinterpret_cast<float*>(As + nab * 16 * 16);  // [nab*16] 1/||x_a||
   float* na2_s = inv_s + nab * 16;                                // [nab*16] ||x_a||^2
-  int* red = reinterpret_cast<int*>(na2_s + nab * 16) + wave * (16 * 17 + 128);  // per wave [16 tokens][17]
-  int* selfs = red + 16 * 17;                                       // per wave [64] anchor_of of its tokens
-  float* scs = reinterpret_cast<float*>(selfs + 64);                // per wave [64] observation scores
+  // per wave: [64] anchor_of of its tokens (then the chosen anchor, bit 31 =
+  // anchor token), [64] observation scores
+  int* selfs = reinterpret_cast<int*>(na2_s + nab * 16) + wave * (kAssignSlot / 4);
+  float* scs = reinterpret_cast<float*>(selfs + 64);
   const uint16_t* X = (side ? g.V : g.K) + uh * N * D;
   const uint16_t* AX = reinterpret_cast<const uint16_t*>(g.cache + (int64_t)u * g.stride +
                                                          (side ? g.off_anchor_v : g.off_anchor_k)) +
                        (int64_t)h * g.A * D;
   const float2* an = g.anorm + ((int64_t)u * 2 * g.H + side * g.H + h) * g.A;
 
-  // ---- anchors of this part into LDS (rows beyond nA repeat the last one)
+  const int ntiles_hs = (N + kTile - 1) / kTile;
+  const int tile0 = blk * g.tiles_per_block;
+  const int tile1 = min(ntiles_hs, tile0 + g.tiles_per_block);
+
+  auto load_tokens = [&](int tile, bf16x8 (&xf)[4][4]) {
+    const int tb = tile * kTile + wave * 64;
+    for (int rb = 0; rb < 4; ++rb) {
+      const int t = min(tb + rb * 16 + col, N - 1);
+      for (int st = 0; st < 4; ++st) xf[rb][st] = M::load(X + (int64_t)t * D + st * 32 + kg * 8);
+    }
+  };
+
+  // ---- anchors of this part into LDS (rows beyond nA repeat the last one),
+  // with the first token tile loading alongside
+  bf16x8 xf[4][4];
   {
-    for (int jj = wave; jj < nab * 4; jj += kAssignWaves) {
+    for (int jj = wave; jj < nab * 4; jj += WAVES) {
       const int r = jj * 4 + (lane >> 4);               // tile row of this lane's chunk
       const int c = (lane & 15) ^ (r & 15);             // its logical chunk
       dma16(AX + (int64_t)(g.a0 + min(r, nA - 1)) * D + c * 8, As + jj * 64);
@@ -176,26 +198,17 @@ __global__ __launch_bounds__(64 * kAssignWaves) void k_assign_res(AssignArgs g) 
       inv_s[i] = v.y;
       na2_s[i] = v.x;
     }
+    if (tile0 < tile1) load_tokens(tile0, xf);
     __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));
     __syncthreads();
   }
 
-  const int ntiles_hs = (N + kAssignTile - 1) / kAssignTile;
-  const int tile0 = blk * g.tiles_per_block;
-  const int tile1 = min(ntiles_hs, tile0 + g.tiles_per_block);
-
-  auto load_tokens = [&](int tile, bf16x8 (&xf)[4][4]) {
-    const int tb = tile * kAssignTile + wave * 64;
-    for (int rb = 0; rb < 4; ++rb) {
-      const int t = min(tb + rb * 16 + col, N - 1);
-      for (int st = 0; st < 4; ++st) xf[rb][st] = M::load(X + (int64_t)t * D + st * 32 + kg * 8);
-    }
-  };
-
   // Running maximum of the keys as signed integers: for non-negative
   // cosines the float bits order like the values, so v_max_i32 needs no NaN
-  // canonicalisation.  A wave holding a token whose best key is negative
-  // (every cosine <= 0, rare) redoes the search with sign-corrected keys.
+  // canonicalisation.  A wave holding a token whose best key over all anchors
+  // is negative (every cosine <= 0, rare) redoes the search with
+  // sign-corrected keys; the test is on the token's row maximum, since a
+  // lane's own column sees only A/16 anchors and is often all negative.
   // the mask lives in a VGPR so that (bits & mask) | tag is one v_and_or_b32
   unsigned keymask;
   __asm__("v_mov_b32 %0, 0xffffffe0" : "=v"(keymask));
@@ -225,65 +238,81 @@ __global__ __launch_bounds__(64 * kAssignWaves) void k_assign_res(AssignArgs g) 
     for (int ab = 0; ab < nab; ++ab) { mfmas(ab, acc0); keys(ab, acc0); }
   };
 
-  bf16x8 xf[4][4];
-  if (tile0 < tile1) load_tokens(tile0, xf);
   for (int tile = tile0; tile < tile1; ++tile) {
     // per-token scalars of the epilogue, copied into this wave's LDS slots
     // while the search runs (no registers held across it)
     {
-      const int t = min(tile * kAssignTile + wave * 64 + lane, N - 1);
+      const int t = min(tile * kTile + wave * 64 + lane, N - 1);
       dma4(g.anchor_of + uh * N + t, selfs);
       if (side) dma4(g.score + uh * N + t, scs);
     }
     int best[4][4];
+    int mk[4][4];   // row (token) maxima of the keys
+    auto row_maxima = [&]() {
+      for (int rb = 0; rb < 4; ++rb)
+        for (int r = 0; r < 4; ++r) mk[rb][r] = row_max_i32(best[rb][r]);
+    };
     search(xf, best, std::false_type{});
+    row_maxima();
     bool neg = false;
     for (int rb = 0; rb < 4; ++rb)
-      for (int r = 0; r < 4; ++r) neg |= best[rb][r] < 0;
-    const bool mono = __builtin_amdgcn_ballot_w64(neg) != 0;
-    if (mono) search(xf, best, std::true_type{});
+      for (int r = 0; r < 4; ++r) neg |= mk[rb][r] < 0;
+    if (__builtin_amdgcn_ballot_w64(neg) != 0) {
+      search(xf, best, std::true_type{});
+      row_maxima();
+    }
     __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));   // this wave's copies of selfs / scs
-    // next tile's tokens load while this tile's columns are reduced and projected
-    // ---- reduce the 16 anchor columns of every token (lowest column on
-    // equal keys); lane l < 16 ends up with the winner of token row l
-    int wins[4];
+    // ---- reduce the 16 anchor columns of every token: row maximum of the
+    // keys, lowest column holding it; lanes col < 4 of row kg publish token
+    // rb*16 + kg*4 + col (chosen anchor, bit 31 = anchor token) in selfs
+#pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      for (int r = 0; r < 4; ++r) red[(kg * 4 + r) * 17 + col] = best[rb][r];
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
-      __builtin_amdgcn_wave_barrier();
-      int win = 0, wkey = INT_MIN;
-      if (lane < 16) {
-        for (int c = 0; c < 16; ++c) {
-          const int k = red[lane * 17 + c];
-          if (k > wkey) { wkey = k; win = c; }   // strict: lowest column on equal keys
-        }
-        win = g.a0 + win + 16 * (31 - (wkey & 31));
+      int wv[4];
+      for (int r = 0; r < 4; ++r) {
+        const int m = mk[rb][r];
+        const unsigned long long eq = __builtin_amdgcn_ballot_w64(best[rb][r] == m);
+        const unsigned bits = (unsigned)(eq >> (kg * 16)) & 0xFFFFu;   // never 0: the row holds its maximum
+        wv[r] = g.a0 + __builtin_ctz(bits) + 16 * (31 - (m & 31));
       }
-      wins[rb] = win;
-      if constexpr (PARTIAL) {
-        const int tt = tile * kAssignTile + wave * 64 + rb * 16;
-        if (lane < 16 && tt + lane < N) {
-          // signed-monotone key -> unsigned order, then ~index for lowest-index ties
-          const unsigned long long key64 = ((unsigned long long)(((unsigned)wkey & keymask) ^ 0x80000000u) << 32) |
-                                           (unsigned long long)(0xFFFFFFFFu - (unsigned)win);
-          atomicMax(g.best64 + ((int64_t)u * 2 * g.H + side * g.H + h) * N + tt + lane, key64);
+      if (col < 4) {
+        const int w = col == 0 ? wv[0] : col == 1 ? wv[1] : col == 2 ? wv[2] : wv[3];
+        const int tl = rb * 16 + kg * 4 + col;   // token of the wave's tile
+        if constexpr (PARTIAL) {
+          const int tt = tile * kTile + wave * 64 + tl;
+          // (one static index per pass: a select over mk would become a
+          // private-memory array lookup)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (col == r && tt < N) {
+              // signed-monotone key -> unsigned order, then ~index for lowest-index ties
+              const unsigned long long key64 =
+                  ((unsigned long long)(((unsigned)mk[rb][r] & keymask) ^ 0x80000000u) << 32) |
+                  (unsigned long long)(0xFFFFFFFFu - (unsigned)wv[r]);
+              atomicMax(g.best64 + ((int64_t)u * 2 * g.H + side * g.H + h) * N + tt, key64);
+            }
+          }
+        } else {
+          const int self = selfs[tl];
+          selfs[tl] = self >= 0 ? (int)(0x80000000u | (unsigned)self) : w;
         }
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads of red done before the next row block writes it
-      __builtin_amdgcn_wave_barrier();
     }
     // ---- projection of every token onto its anchor
     if constexpr (!PARTIAL) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's selfs writes done
+      __builtin_amdgcn_wave_barrier();
       for (int rb = 0; rb < 4; ++rb) {
-        const int t = tile * kAssignTile + wave * 64 + rb * 16 + col;
-        const int self = selfs[rb * 16 + col];
-        const bool is_anchor = self >= 0;
-        const int w = __shfl(wins[rb], col, 64);   // every lane takes part in the shuffle
-        const int a = is_anchor ? self : w;
-        assign_project(g, u, side, h, t, a, is_anchor, na2_s[a], scs[rb * 16 + col], xf[rb],
+        const int t = tile * kTile + wave * 64 + rb * 16 + col;
+        const int sa = selfs[rb * 16 + col];
+        const bool is_anchor = sa < 0;
+        const int a = sa & 0x7FFFFFFF;
+        assign_project(g, u, side, h, t, a, is_anchor, na2_s[a - g.a0], scs[rb * 16 + col], xf[rb],
                        [&](int c) { return As[res_phys(a - g.a0, c)]; }, kg);
       }
     }
+    // this wave's LDS slots are rewritten by the next tile's copies
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
     if (tile + 1 < tile1) load_tokens(tile + 1, xf);
   }
 }

@@ -132,6 +132,25 @@ __device__ __forceinline__ float row_sum4_scatter(const float (&v)[4], int col) 
   const float b = (hi4 ? a1 : a0) + dpp<kDppHalfMirror>(sb);
   return quad_sum(b);
 }
+// Sum over the four rows of 16 lanes (lanes l, l^16, l^32, l^48), every lane
+// gets it; gfx950 lane-swap instructions, no LDS.  The operand pairs are the
+// same for all four lanes, so they all hold the same bits.
+__device__ __forceinline__ float sum_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// Integer maximum over each row of 16 lanes; every lane gets it.
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int row_max_i32(int v) {
+  v = max(v, dpp_i<kDppRor8>(v));
+  v = max(v, dpp_i<kDppRor4>(v));
+  v = max(v, dpp_i<kDppXor1>(v));
+  return max(v, dpp_i<kDppXor2>(v));
+}
 __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp<kDppRor8>(v));
   v = fmaxf(v, dpp<kDppRor4>(v));
