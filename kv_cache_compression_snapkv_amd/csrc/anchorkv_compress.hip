@@ -426,164 +426,215 @@ __global__ __launch_bounds__(256) void k_assign(const void* Kv, const void* Vv, 
 // ------------------------------------------------------------- top-R select
 // Per (unit, side): choose the R largest utilities over (head, token), ties to
 // the lower head then position.  Keys: f32 bits + 1 for eligible (u >= 0),
-// 0 for anchors.  Blocks are 1024-token chunks of one head, so the running
-// selected count at a chunk start is that chunk's residual offset.
+// 0 for anchors.
+//  k_topr_threshold, one 1024-thread block per (unit, side): three radix
+//    passes (11/11/10 bits) find the R-th key T and how many keys equal to T
+//    are taken; then the counts of keys > T and == T of every group of 1024
+//    positions (flat head*N + t order) and their exclusive scans give each
+//    group's record base and tie base;
+//  k_topr_flag, one wave per group: flags the selected tokens in position
+//    order (ballot prefix counts), writes each record's position to the record
+//    list and, at every 1024-token chunk start of a head, the number of
+//    records before it (the chunk's residual offset).
 __device__ __forceinline__ unsigned util_key(float v) { return v >= 0.0f ? __float_as_uint(v) + 1u : 0u; }
 
-__global__ __launch_bounds__(256) void k_topr_hist(const float* util, unsigned* hist, const unsigned* state, int H,
-                                                   int N, int C, int R, int pass) {
-  __shared__ unsigned lh[kHistBins];
-  int bid = blockIdx.x;
-  const int c = bid % C; bid /= C;
-  const int h = bid % H; bid /= H;
-  const int side = bid % 2;
-  const int u = bid / 2;
-  if (R == 0) return;
-  const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-  const int width = pass == 2 ? 10 : 11;
-  const unsigned* st = state + ((int64_t)u * 2 + side) * 4;
-  const unsigned prefix = pass == 0 ? 0u : st[0];
-  const unsigned hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + width));
-  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) lh[b] = 0;
-  __syncthreads();
-  const float* up = util + (((int64_t)u * 2 + side) * H + h) * N;
-  const int t1 = min(N, (c + 1) * kChunk);
-  for (int t = c * kChunk + threadIdx.x; t < t1; t += blockDim.x) {
-    const unsigned key = util_key(up[t]);
-    if (key != 0u && (key & hmask) == (prefix & hmask)) atomicAdd(&lh[(key >> shift) & ((1u << width) - 1)], 1u);
-  }
-  __syncthreads();
-  unsigned* gh = hist + ((int64_t)u * 2 + side) * kHistBins;
-  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x)
-    if (lh[b]) atomicAdd(&gh[b], lh[b]);
-}
+constexpr int kToprThreads = 1024;
+constexpr int kToprBatch = 16;   // loads in flight per thread (streaming form)
+constexpr int kToprKPT = 64;     // keys per thread of the register-resident form
+constexpr int kToprCopies = 8;   // histogram copies
+constexpr int kToprGroup = 1024; // positions per flag group
 
-__global__ __launch_bounds__(256) void k_topr_scan(unsigned* hist, unsigned* state, int R, int pass) {
+// KPT > 0: the block's keys (H*N <= 16 * 64 * KPT) are loaded once into
+// registers, wave w holding positions [w*64*KPT, (w+1)*64*KPT) as
+// w*64*KPT + 64 s + lane; KPT == 0: every pass streams the utilities.  Wave
+// runs are whole groups.
+template <int KPT>
+__global__ __launch_bounds__(kToprThreads) void k_topr_threshold(const float* util, unsigned* groups, int H, int N,
+                                                                 int R) {
+  constexpr int NW = kToprThreads / 64;
+  constexpr bool REG = KPT > 0;
+  constexpr int B = REG ? KPT : kToprBatch;   // keys per batch of a thread
+  static_assert((64 * B) % kToprGroup == 0 || kToprGroup % (64 * B) == 0, "batches and groups nest");
+  // kToprCopies interleaved histogram copies (bin b of copy c at b*copies + c):
+  // keys of one pass share their leading bits, and lanes adding to one LDS
+  // address in the same instruction serialise
+  __shared__ unsigned lhc[kHistBins * kToprCopies];
   __shared__ unsigned lh[kHistBins];
   __shared__ int sh[32];
   __shared__ int s_b;
   __shared__ unsigned s_above;
   const int us = blockIdx.x;
-  unsigned* st = state + (int64_t)us * 4;
-  unsigned* gh = hist + (int64_t)us * kHistBins;
-  const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-  const int width = pass == 2 ? 10 : 11;
-  for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) { lh[b] = gh[b]; gh[b] = 0; }  // clear for the next pass
-  if (threadIdx.x == 0) { s_b = 0; s_above = 0; }
-  __syncthreads();
-  if (R == 0) return;
-  const unsigned prefix = pass == 0 ? 0u : st[0];
-  const unsigned need = pass == 0 ? (unsigned)R : st[1];
-  find_bucket(lh, 1 << width, need, sh, &s_b, &s_above);
-  if (threadIdx.x == 0) {
-    st[0] = prefix | ((unsigned)s_b << shift);
-    st[1] = need - s_above;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t M = (int64_t)H * N;
+  const int64_t ngroups = (M + kToprGroup - 1) / kToprGroup;
+  const float* up = util + (int64_t)us * M;
+  unsigned* gb = groups + (int64_t)us * ngroups * 2;
+  unsigned* tn = groups + (int64_t)gridDim.x * ngroups * 2 + (int64_t)us * 2;   // (T, need)
+  if (R == 0) {
+    if (threadIdx.x == 0) { tn[0] = 0xFFFFFFFFu; tn[1] = 0u; }
+    for (int64_t i = threadIdx.x; i < ngroups; i += kToprThreads) { gb[2 * i] = 0u; gb[2 * i + 1] = 0u; }
+    return;
   }
-}
-
-__global__ __launch_bounds__(256) void k_topr_count(const float* util, const unsigned* state, unsigned* blk, int H,
-                                                    int N, int C, int R) {
-  __shared__ unsigned red[2][4];
-  int bid = blockIdx.x;
-  const int c = bid % C; bid /= C;
-  const int h = bid % H; bid /= H;
-  const int side = bid % 2;
-  const int u = bid / 2;
-  const unsigned T_key = state[((int64_t)u * 2 + side) * 4 + 0];
-  unsigned g = 0, ti = 0;
-  if (R > 0) {
-    const float* up = util + (((int64_t)u * 2 + side) * H + h) * N;
-    const int t1 = min(N, (c + 1) * kChunk);
-    for (int t = c * kChunk + threadIdx.x; t < t1; t += blockDim.x) {
-      const unsigned key = util_key(up[t]);
-      g += key > T_key;
-      ti += key == T_key;
+  // wave-contiguous runs of positions, whole groups
+  const int64_t seg = REG ? (int64_t)64 * KPT : ((M + NW - 1) / NW + kToprGroup - 1) / kToprGroup * kToprGroup;
+  const int64_t w0 = (int64_t)wave * seg, w1 = min(M, w0 + seg);
+  unsigned keyr[REG ? KPT : 1];
+  if constexpr (REG) {
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int64_t i = w0 + 64 * k + lane;
+      keyr[k] = i < w1 ? util_key(up[i]) : 0u;
     }
   }
-  for (int o = 32; o > 0; o >>= 1) { g += __shfl_xor(g, o, 64); ti += __shfl_xor(ti, o, 64); }
-  if ((threadIdx.x & 63) == 0) { red[0][threadIdx.x >> 6] = g; red[1][threadIdx.x >> 6] = ti; }
+  // keys of the batch starting at j0 (streaming: loaded now, B in flight)
+  auto batch = [&](int64_t j0, unsigned (&key)[B]) {
+    if constexpr (REG) {
+#pragma unroll
+      for (int k = 0; k < B; ++k) key[k] = keyr[k];
+    } else {
+      float v[B];
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        const int64_t i = j0 + 64 * k + lane;
+        v[k] = i < w1 ? up[i] : -1.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < B; ++k) key[k] = util_key(v[k]);
+    }
+  };
+  // ---- the R-th largest key T and the number of keys equal to T to take
+  unsigned prefix = 0u, need = (unsigned)R;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int width = pass == 2 ? 10 : 11;
+    const unsigned hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + width));
+    for (int b = threadIdx.x; b < kHistBins * kToprCopies; b += kToprThreads) lhc[b] = 0;
+    if (threadIdx.x == 0) { s_b = 0; s_above = 0; }
+    __syncthreads();
+    const int copy = lane & (kToprCopies - 1);
+    for (int64_t j0 = w0; j0 < w1; j0 += 64 * B) {
+      unsigned key[B];
+      batch(j0, key);
+#pragma unroll
+      for (int k = 0; k < B; ++k)
+        if (key[k] != 0u && (key[k] & hmask) == (prefix & hmask))
+          atomicAdd(&lhc[((key[k] >> shift) & ((1u << width) - 1)) * kToprCopies + copy], 1u);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < kHistBins; b += kToprThreads) {
+      unsigned sum = 0;
+#pragma unroll
+      for (int c = 0; c < kToprCopies; ++c) sum += lhc[b * kToprCopies + c];
+      lh[b] = sum;
+    }
+    __syncthreads();
+    find_bucket(lh, 1 << width, need, sh, &s_b, &s_above);   // ends with a barrier
+    prefix |= (unsigned)s_b << shift;
+    need -= s_above;
+    __syncthreads();
+  }
+  const unsigned T = prefix;
+  if (threadIdx.x == 0) { tn[0] = T; tn[1] = need; }
+  // ---- counts of keys > T and == T per group (kept in LDS), in wave runs
+  unsigned* gcnt = lhc;   // [ngroups][2] while ngroups <= 4 * kHistBins; else the group array itself
+  const bool in_lds = ngroups * 2 <= (int64_t)kHistBins * kToprCopies;
+  unsigned* cnt = in_lds ? gcnt : gb;
+  {
+    unsigned g = 0, ti = 0;
+    for (int64_t j0 = w0; j0 < w1; j0 += 64 * B) {
+      unsigned key[B];
+      batch(j0, key);
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        g += (unsigned)__popcll(__builtin_amdgcn_ballot_w64(key[k] != 0u && key[k] > T));
+        ti += (unsigned)__popcll(__builtin_amdgcn_ballot_w64(key[k] != 0u && key[k] == T));
+        const int64_t pos = j0 + 64 * (k + 1);   // positions covered so far
+        if ((pos - w0) % kToprGroup == 0 || pos >= w1) {
+          if (lane == 0) {
+            const int64_t grp = (pos - 1 - (pos > w1 ? pos - w1 : 0)) / kToprGroup;
+            cnt[2 * grp] = g;
+            cnt[2 * grp + 1] = ti;
+          }
+          g = 0; ti = 0;
+          if (pos >= w1) break;
+        }
+      }
+    }
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned* b = blk + ((((int64_t)u * 2 + side) * H + h) * C + c) * 4;
-    b[0] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    b[1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  // ---- exclusive scans over the groups: ties first (which ties are taken),
+  // then records (greater + taken ties)
+  {
+    unsigned tie_base = 0, rec_base = 0;
+    for (int64_t g0 = 0; g0 < ngroups; g0 += kToprThreads) {
+      const int64_t gi = g0 + threadIdx.x;
+      const unsigned gt = gi < ngroups ? cnt[2 * gi] : 0u;
+      const unsigned ti = gi < ngroups ? cnt[2 * gi + 1] : 0u;
+      int tot;
+      const unsigned tp = (unsigned)block_excl_scan((int)ti, sh, &tot) + tie_base;
+      const unsigned taken = tp >= need ? 0u : min(ti, need - tp);
+      int tot2;
+      const unsigned rp = (unsigned)block_excl_scan((int)(gt + taken), sh, &tot2) + rec_base;
+      if (gi < ngroups) { gb[2 * gi] = rp; gb[2 * gi + 1] = tp; }   // after every read of cnt (scan barriers)
+      tie_base += (unsigned)tot;
+      rec_base += (unsigned)tot2;
+    }
   }
 }
 
-// Exclusive scans over the H*C chunks of a (unit, side); writes the chunk
-// offsets of the cache.  One 1024-thread block per (unit, side).
-__global__ __launch_bounds__(1024) void k_topr_blockscan(unsigned* blk, const unsigned* state, uint8_t* cache,
-                                                         int64_t stride, int64_t off_ck, int64_t off_cv, int nb,
-                                                         int R) {
-  __shared__ int sh[32];
-  const int us = blockIdx.x;
+// One wave per group of 1024 positions of a (unit, side).
+__global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsigned* groups, uint8_t* cache,
+                                                   int64_t stride, int64_t off_words, int64_t off_ck, int64_t off_cv,
+                                                   int* sel_list, int Rmax, int H, int N, int C, int R, int US) {
+  const int lane = threadIdx.x & 63;
+  const int64_t M = (int64_t)H * N;
+  const int64_t ngroups = (M + kToprGroup - 1) / kToprGroup;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // over [US][ngroups]
+  if (gw >= (int64_t)US * ngroups) return;
+  const int us = (int)(gw / ngroups);
+  const int64_t grp = gw - (int64_t)us * ngroups;
   const int u = us / 2, side = us % 2;
-  const unsigned need = R > 0 ? state[(int64_t)us * 4 + 1] : 0u;
-  unsigned* b = blk + (int64_t)us * nb * 4;
   int* chunk = reinterpret_cast<int*>(cache + (int64_t)u * stride + (side ? off_cv : off_ck));
-  int tie_base = 0, sel_base = 0;
-  for (int b0 = 0; b0 < nb; b0 += blockDim.x) {
-    const int i = b0 + threadIdx.x;
-    const int ties = (i < nb && R > 0) ? (int)b[i * 4 + 1] : 0;
-    const int greater = (i < nb && R > 0) ? (int)b[i * 4 + 0] : 0;
-    int tot;
-    const int tp = block_excl_scan(ties, sh, &tot) + tie_base;
-    const int taken = max(0, min(ties, (int)need - tp));
-    int tot2;
-    const int sp = block_excl_scan(greater + taken, sh, &tot2) + sel_base;
-    if (i < nb) {
-      b[i * 4 + 2] = (unsigned)sp;
-      b[i * 4 + 3] = (unsigned)tp;
-      chunk[i] = sp;
-    }
-    tie_base += tot;
-    sel_base += tot2;
-  }
-}
-
-// Flags and record order: within a chunk, item order is position order.
-__global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsigned* state, const unsigned* blk,
-                                                   uint8_t* cache, int64_t stride, int64_t off_words, int* sel_list,
-                                                   int Rmax, int H, int N, int C, int R) {
-  __shared__ int sh[32];
-  int bid = blockIdx.x;
-  const int c = bid % C; bid /= C;
-  const int h = bid % H; bid /= H;
-  const int side = bid % 2;
-  const int u = bid / 2;
-  if (R == 0) return;
-  const int us = u * 2 + side;
-  const unsigned T_key = state[(int64_t)us * 4 + 0];
-  const int need = (int)state[(int64_t)us * 4 + 1];
-  const unsigned* b = blk + (((int64_t)us * H + h) * C + c) * 4;
-  const int sel_base = (int)b[2], tie_base = (int)b[3];
-  const float* up = util + ((int64_t)us * H + h) * N;
-  const int t0 = c * kChunk + threadIdx.x * 4;
-  unsigned key[4];
-  int nti = 0;
-  for (int k = 0; k < 4; ++k) {
-    const int t = t0 + k;
-    key[k] = t < N && t < (c + 1) * kChunk ? util_key(up[t]) : 0u;
-    nti += key[k] == T_key && key[k] != 0u;
-  }
-  int tot;
-  int tr = block_excl_scan(nti, sh, &tot) + tie_base;
-  bool sel[4];
-  int ns = 0;
-  for (int k = 0; k < 4; ++k) {
-    sel[k] = key[k] != 0u && key[k] > T_key;
-    if (key[k] != 0u && key[k] == T_key) { sel[k] = tr < need; ++tr; }
-    ns += sel[k];
-  }
-  int o = block_excl_scan(ns, sh, &tot) + sel_base;
+  const unsigned* tn = groups + (int64_t)US * ngroups * 2 + (int64_t)us * 2;
+  const unsigned T = tn[0], need = tn[1];
+  const unsigned rec_base = groups[((int64_t)us * ngroups + grp) * 2];
+  const unsigned tie_base = groups[((int64_t)us * ngroups + grp) * 2 + 1];
+  const float* up = util + (int64_t)us * M;
   uint32_t* words = reinterpret_cast<uint32_t*>(cache + (int64_t)u * stride + off_words);
-  for (int k = 0; k < 4; ++k) {
-    if (!sel[k]) continue;
-    const int t = t0 + k;
-    if (o >= R) break;  // never more than R records (guards the list bounds)
-    words[((int64_t)h * N + t) * 2 + side] |= 0x8000u;
-    sel_list[(int64_t)us * Rmax + o] = h * N + t;
-    ++o;
+  const int64_t i0 = grp * kToprGroup;
+  constexpr int S = kToprGroup / 64;
+  float v[S];
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const int64_t i = i0 + 64 * k + lane;
+    v[k] = i < M ? up[i] : -1.0f;
+  }
+  unsigned run_tie = 0, run_sel = 0;
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const int64_t i = i0 + 64 * k + lane;
+    const unsigned key = R > 0 ? util_key(v[k]) : 0u;
+    const bool gt = key != 0u && key > T;
+    const bool tie = key != 0u && key == T;
+    const unsigned long long mt = __builtin_amdgcn_ballot_w64(tie);
+    const unsigned tie_rank = tie_base + run_tie + __builtin_amdgcn_mbcnt_hi((unsigned)(mt >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((unsigned)mt, 0u));
+    const bool sel = gt || (tie && tie_rank < need);
+    const unsigned long long ms = __builtin_amdgcn_ballot_w64(sel);
+    const unsigned rec = rec_base + run_sel + __builtin_amdgcn_mbcnt_hi((unsigned)(ms >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((unsigned)ms, 0u));
+    if (i < M) {
+      const unsigned iu = (unsigned)i;   // H*N < 2^31
+      const int h = (int)(iu / (unsigned)N), t = (int)(iu - (unsigned)h * (unsigned)N);
+      if ((t & (kChunk - 1)) == 0) chunk[h * C + t / kChunk] = (int)rec;
+      if (sel && rec < (unsigned)R) {
+        // no-return atomic OR: a read-modify-write would wait for the load
+        atomicOr(&words[((int64_t)h * N + t) * 2 + side], 0x8000u);
+        sel_list[(int64_t)us * Rmax + rec] = h * N + t;
+      }
+    }
+    run_tie += (unsigned)__popcll(mt);
+    run_sel += (unsigned)__popcll(ms);
   }
 }
 
@@ -869,28 +920,21 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
 
   // top-R per (unit, side); R_K == R_V
   const int R = p.R_K;
-  unsigned* hist = reinterpret_cast<unsigned*>(ws + w.hist);
-  unsigned* state = reinterpret_cast<unsigned*>(ws + w.sel_state);
-  unsigned* blk = reinterpret_cast<unsigned*>(ws + w.blk);
-  const unsigned nchunkblk = (unsigned)((int64_t)U * 2 * H * C);
-  k_zero_u32<<<(unsigned)((U * 2 * kHistBins + 255) / 256), 256, 0, st>>>(hist, (int64_t)U * 2 * kHistBins);
-  AKV_CHECK_LAUNCH("k_zero_u32");
-  for (int pass = 0; pass < 3; ++pass) {
-    k_topr_hist<<<nchunkblk, 256, 0, st>>>(a.util, hist, state, H, N, C, R, pass);
-    AKV_CHECK_LAUNCH("k_topr_hist");
-    k_topr_scan<<<(unsigned)(U * 2), 256, 0, st>>>(hist, state, R, pass);
-    AKV_CHECK_LAUNCH("k_topr_scan");
-  }
-  k_topr_count<<<nchunkblk, 256, 0, st>>>(a.util, state, blk, H, N, C, R);
-  AKV_CHECK_LAUNCH("k_topr_count");
-  k_topr_blockscan<<<(unsigned)(U * 2), 1024, 0, st>>>(blk, state, cache, p.unit_stride, p.off_chunk_k, p.off_chunk_v,
-                                                      H * C, R);
-  AKV_CHECK_LAUNCH("k_topr_blockscan");
   const int Rmax = std::max(1, std::max(p.R_K, p.R_V));
   int* sel_list = reinterpret_cast<int*>(ws + w.sel_list);
-  k_topr_flag<<<nchunkblk, 256, 0, st>>>(a.util, state, blk, cache, p.unit_stride, p.off_words, sel_list, Rmax, H, N,
-                                         C, R);
-  AKV_CHECK_LAUNCH("k_topr_flag");
+  unsigned* groups = reinterpret_cast<unsigned*>(ws + w.sel_groups);
+  if ((int64_t)H * N <= (int64_t)kToprThreads * kToprKPT)
+    k_topr_threshold<kToprKPT><<<(unsigned)(U * 2), kToprThreads, 0, st>>>(a.util, groups, H, N, R);
+  else
+    k_topr_threshold<0><<<(unsigned)(U * 2), kToprThreads, 0, st>>>(a.util, groups, H, N, R);
+  AKV_CHECK_LAUNCH("k_topr_threshold");
+  {
+    const int64_t nw = (int64_t)U * 2 * (((int64_t)H * N + kToprGroup - 1) / kToprGroup);
+    k_topr_flag<<<(unsigned)((nw + 3) / 4), 256, 0, st>>>(a.util, groups, cache, p.unit_stride, p.off_words,
+                                                          p.off_chunk_k, p.off_chunk_v, sel_list, Rmax, H, N, C, R,
+                                                          U * 2);
+    AKV_CHECK_LAUNCH("k_topr_flag");
+  }
   prof_mark(st, "topr");
   if (R > 0) {
     const int nblk = (R + 16 * kQuantPerGroup - 1) / (16 * kQuantPerGroup);

@@ -62,10 +62,8 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
   w.best64 = take((p.dtype == ANCHORKV_BF16 && A > kAssignResMax) ? 8 * U * 2 * H * N : 0);
   w.anorm = take(8 * U * 2 * H * A);
   w.pooled = take(4 * U * H * N);
-  w.hist = take(4 * U * 2 * kHistBins);
-  w.sel_state = take(4 * U * 2 * 4);
-  w.blk = take(16 * U * 2 * H * C);
   w.sel_list = take(4 * U * 2 * std::max<int64_t>(1, std::max(p.R_K, p.R_V)));
+  w.sel_groups = take(8 * U * 2 * ((H * N + 1023) / 1024) + 8 * U * 2);
   w.total = off;
   return w;
 }

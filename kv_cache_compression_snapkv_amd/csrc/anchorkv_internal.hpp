@@ -49,10 +49,8 @@ struct CompressWs {
   int64_t best64;  // u64 [U][2][H][N] packed part winners (bf16, A > kAssignResMax only)
   int64_t anorm;   // float2 [U][2][H][A] (||x_a||^2, 1/||x_a||)
   int64_t pooled;  // f32 [U][H][N]
-  int64_t hist;    // u32 [U][2][kHistBins]
-  int64_t sel_state; // u32 [U][2][4]: prefix, need, threshold, done
-  int64_t blk;     // u32 [U][2][H*C][4]: greater, ties, sel_prefix, tie_prefix
   int64_t sel_list; // int32 [U][2][Rmax] flat (head*N + t) in record order
+  int64_t sel_groups; // u32 [U][2][ceil(H*N/1024)][2] record / tie bases per 1024 positions, then [U][2][2] (T, need)
   int64_t total;
 };
 CompressWs compress_ws_layout(const anchorkv_plan_info& p);

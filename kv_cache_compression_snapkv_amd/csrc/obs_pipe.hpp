@@ -56,7 +56,14 @@ template <int QPW> struct ObsPipeCfg<OBS_UTIL, QPW> { static constexpr int TK = 
 constexpr int kObsUtilTK = 64;   // UTIL / UTILX tile; the flag array allows >= 32
 static_assert(ObsPipeCfg<OBS_UTIL, 1>::TK == kObsUtilTK && ObsPipeCfg<OBS_UTIL, 2>::TK == kObsUtilTK, "UTIL tile");
 
-__device__ __forceinline__ int obs_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk swizzle of tile row r, a bijection of r & 15 onto 0..15 (LDS has 64
+// banks of 4 bytes: 16 chunks of 16 bytes per cycle):
+//  * a fragment read takes one logical chunk of 16 consecutive rows -> 16
+//    distinct physical chunks;
+//  * a transposing read takes logical chunks 2k, 2k+1 of 8 rows (r & 8
+//    fixed) per 32-lane half -> f(r) >> 1 is distinct over those rows, so
+//    the 16 (row, chunk) pairs land on 16 distinct chunks.
+__device__ __forceinline__ int obs_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 // Physical chunk of logical chunk c (0..15) of tile row r.
 __device__ __forceinline__ int obs_phys(int r, int c) { return r * 16 + (c ^ obs_swz(r)); }
 
@@ -104,21 +111,16 @@ __device__ __forceinline__ uint2 lds_tr(const uint4* tile, int row, int d) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// Per-lane offsets (elements) of the tile copies: chunk-block jj (64 lanes,
-// rows 4jj .. 4jj+3) of a [TK][128] tile.  Row r = 4jj + lane/16; logical
-// chunk c = (lane & 15) ^ swz(r), and swz(r) = 2(lane/16) | (jj & 1), so the
-// offset of lane l is jj*512 + off[jj & 1] with two per-lane constants.
+// Tile copies: chunk-block jj (64 lanes, rows 4jj .. 4jj+3) of a [TK][128]
+// tile.  Lane l writes physical chunk l & 15 of row r = 4jj + l/16, i.e.
+// logical chunk (l & 15) ^ swz(r), with swz(4jj + rsub) = 8(jj & 1) + 2 rsub +
+// ((jj >> 1) & 1).
 struct DmaLane {
-  int off0, off1;   // element offsets within a 4-row block for even / odd jj
-  int rsub;         // lane / 16: row within the 4-row block
-  int c0, c1;       // chunk (16-byte units) within the row for even / odd jj
-  __device__ __forceinline__ explicit DmaLane(int lane) {
-    rsub = lane >> 4;
-    c0 = (lane & 15) ^ (rsub << 1);
-    c1 = c0 ^ 1;
-    off0 = rsub * kHeadDim + c0 * 8;
-    off1 = rsub * kHeadDim + c1 * 8;
-  }
+  int pc;     // lane & 15: physical chunk written
+  int rsub;   // lane / 16: row within the 4-row block
+  __device__ __forceinline__ explicit DmaLane(int lane) : pc(lane & 15), rsub(lane >> 4) {}
+  // logical chunk this lane copies in chunk-block jj
+  __device__ __forceinline__ int chunk(int jj) const { return pc ^ (8 * (jj & 1) + 2 * rsub + ((jj >> 1) & 1)); }
 };
 
 // Copy one [TK][128] tile of contiguous rows starting at `base` (rows beyond
@@ -126,18 +128,10 @@ struct DmaLane {
 template <int TK>
 __device__ __forceinline__ int dma_rows(uint4* dst, const uint16_t* base, int nval, int nw, int wave,
                                          const DmaLane& dl) {
-  // plain values, selected by value: a member chosen through a reference
-  // would keep the struct in private memory
-  const int o0 = dl.off0, o1 = dl.off1, c0 = dl.c0, c1 = dl.c1, rsub = dl.rsub;
   int n = 0;
-  if (nval == TK) {
-    for (int jj = wave; jj < TK / 4; jj += nw, ++n)
-      dma16(base + jj * 512 + ((jj & 1) ? o1 : o0), dst + jj * 64);
-  } else {
-    for (int jj = wave; jj < TK / 4; jj += nw, ++n) {
-      const int r = min(jj * 4 + rsub, nval - 1);
-      dma16(base + r * kHeadDim + ((jj & 1) ? c1 : c0) * 8, dst + jj * 64);
-    }
+  for (int jj = wave; jj < TK / 4; jj += nw, ++n) {
+    const int r = min(jj * 4 + dl.rsub, nval - 1);
+    dma16(base + r * kHeadDim + dl.chunk(jj) * 8, dst + jj * 64);
   }
   return n;
 }
@@ -145,11 +139,10 @@ __device__ __forceinline__ int dma_rows(uint4* dst, const uint16_t* base, int nv
 template <int TK>
 __device__ __forceinline__ int dma_gather(uint4* dst, const uint16_t* base, const int* idx, int nval, int nw,
                                            int wave, const DmaLane& dl) {
-  const int c0 = dl.c0, c1 = dl.c1, rsub = dl.rsub;
   int n = 0;
   for (int jj = wave; jj < TK / 4; jj += nw, ++n) {
-    const int r = min(jj * 4 + rsub, nval - 1);
-    dma16(base + (int64_t)idx[r] * kHeadDim + ((jj & 1) ? c1 : c0) * 8, dst + jj * 64);
+    const int r = min(jj * 4 + dl.rsub, nval - 1);
+    dma16(base + (int64_t)idx[r] * kHeadDim + dl.chunk(jj) * 8, dst + jj * 64);
   }
   return n;
 }
