@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 #include <vector>
 #include <algorithm>
@@ -82,11 +83,22 @@ DecodeWs decode_ws_layout(const anchorkv_plan_info& p) {
   return w;
 }
 
+// Token splits per (unit, head) of the decode pass.  One block per split
+// walks its 1024-token chunks; about two blocks fit a compute unit.  Fewest
+// rounds of resident blocks times chunks per block; fewer splits on ties
+// (each split adds a prologue, an epilogue and a partial to combine).
 static int decode_split_count(const anchorkv_plan_info& p) {
-  int64_t heads = (int64_t)p.units * p.H;
-  int64_t want = (2048 + heads - 1) / heads;
-  int64_t cap = p.n_chunks;  // splits start on 1024-token chunk boundaries
-  return (int)std::max<int64_t>(1, std::min(want, cap));
+  const int64_t heads = (int64_t)p.units * p.H;
+  const int64_t C = p.n_chunks;   // splits start on 1024-token chunk boundaries
+  const int64_t slots = 2 * 256;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int64_t s = 1; s <= std::min<int64_t>(C, 64); ++s) {
+    const int64_t per = (C + s - 1) / s;
+    const int64_t cost = ((heads * s + slots - 1) / slots) * per;
+    if (cost < best_cost) { best_cost = cost; best = (int)s; }
+  }
+  return best;
 }
 
 static void layout(anchorkv_plan_info* p) {
