@@ -585,7 +585,8 @@ __global__ __launch_bounds__(kToprThreads) void k_topr_threshold(const float* ut
 // One wave per group of 1024 positions of a (unit, side).
 __global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsigned* groups, uint8_t* cache,
                                                    int64_t stride, int64_t off_words, int64_t off_ck, int64_t off_cv,
-                                                   int* sel_list, int Rmax, int H, int N, int C, int R, int US) {
+                                                   int* sel_list, int2* sel_aux, const int* aidx, const float* gam,
+                                                   int Rmax, int H, int N, int C, int R, int US) {
   const int lane = threadIdx.x & 63;
   const int64_t M = (int64_t)H * N;
   const int64_t ngroups = (M + kToprGroup - 1) / kToprGroup;
@@ -600,14 +601,19 @@ __global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsi
   const unsigned rec_base = groups[((int64_t)us * ngroups + grp) * 2];
   const unsigned tie_base = groups[((int64_t)us * ngroups + grp) * 2 + 1];
   const float* up = util + (int64_t)us * M;
+  const int* ap = aidx + (int64_t)us * M;
+  const float* gp = gam + (int64_t)us * M;
   uint32_t* words = reinterpret_cast<uint32_t*>(cache + (int64_t)u * stride + off_words);
   const int64_t i0 = grp * kToprGroup;
   constexpr int S = kToprGroup / 64;
-  float v[S];
+  float v[S], gv[S];
+  int av[S];
 #pragma unroll
   for (int k = 0; k < S; ++k) {
     const int64_t i = i0 + 64 * k + lane;
     v[k] = i < M ? up[i] : -1.0f;
+    av[k] = i < M ? ap[i] : 0;
+    gv[k] = i < M ? gp[i] : 0.0f;
   }
   unsigned run_tie = 0, run_sel = 0;
 #pragma unroll
@@ -631,6 +637,9 @@ __global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsi
         // no-return atomic OR: a read-modify-write would wait for the load
         atomicOr(&words[((int64_t)h * N + t) * 2 + side], 0x8000u);
         sel_list[(int64_t)us * Rmax + rec] = h * N + t;
+        // the record's anchor and coefficient, so that the quantiser's loads
+        // do not wait on the position first
+        sel_aux[(int64_t)us * Rmax + rec] = make_int2(av[k], __float_as_int(gv[k]));
       }
     }
     run_tie += (unsigned)__popcll(mt);
@@ -649,8 +658,8 @@ constexpr int kQuantPerGroup = 4;
 template <int DT>
 __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, uint8_t* cache, int64_t stride,
                                               int64_t off_ak, int64_t off_av, int64_t off_rk, int64_t off_rv,
-                                              const int* sel_list, int Rmax, const int* aidx, const float* gam, int H,
-                                              int N, int A, int R, int nblk) {
+                                              const int* sel_list, const int2* sel_aux, int Rmax, int H, int N, int A,
+                                              int R, int nblk) {
   using T = typename Elem<DT>::T;
   constexpr int D = kHeadDim;
   constexpr int QG = kQuantPerGroup;
@@ -665,19 +674,17 @@ __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, u
   int flat[QG], a[QG];
   float g[QG];
 #pragma unroll
-  for (int k = 0; k < QG; ++k) flat[k] = rec0 + k < R ? sel_list[(int64_t)us * Rmax + rec0 + k] : 0;
-#pragma unroll
   for (int k = 0; k < QG; ++k) {
-    const int h = flat[k] / N, t = flat[k] % N;
-    const int64_t iw = ((int64_t)us * H + h) * N + t;
     const bool act = rec0 + k < R;
-    a[k] = act ? aidx[iw] : 0;
-    g[k] = act ? gam[iw] : 0.0f;
+    flat[k] = act ? sel_list[(int64_t)us * Rmax + rec0 + k] : 0;
+    const int2 x = act ? sel_aux[(int64_t)us * Rmax + rec0 + k] : make_int2(0, 0);
+    a[k] = x.x;
+    g[k] = __int_as_float(x.y);
   }
   float r[QG][8];
 #pragma unroll
   for (int k = 0; k < QG; ++k) {
-    const int h = flat[k] / N, t = flat[k] % N;
+    const int h = (int)((unsigned)flat[k] / (unsigned)N), t = flat[k] - h * N;
     const T* X = reinterpret_cast<const T*>(side ? Vv : Kv) + (((int64_t)u * H + h) * N + t) * D + 8 * j;
     const T* AX = reinterpret_cast<const T*>(cache + (int64_t)u * stride + (side ? off_av : off_ak)) +
                   ((int64_t)h * A + a[k]) * D + 8 * j;
@@ -701,16 +708,19 @@ __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, u
     float mn = r[k][0], mx = r[k][0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) { mn = fminf(mn, r[k][e]); mx = fmaxf(mx, r[k][e]); }
-    mn = fminf(mn, __shfl_xor(mn, 1, 64)); mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-    mn = fminf(mn, __shfl_xor(mn, 2, 64)); mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    // the four lanes of a 32-coordinate group are one quad: DPP, no LDS
+    mn = fminf(mn, dpp<kDppXor1>(mn)); mx = fmaxf(mx, dpp<kDppXor1>(mx));
+    mn = fminf(mn, dpp<kDppXor2>(mn)); mx = fmaxf(mx, dpp<kDppXor2>(mx));
     zb[k] = f2h_sat(mn);
     sb[k] = f2h_sat((mx - mn) / 3.0f);
     const float z = h2f(zb[k]), sc = h2f(sb[k]);
+    // one reciprocal per group: (r - z) * (1/sc) is within an ulp or two of
+    // the quotient, which moves a code only next to a rounding boundary
+    const float rinv = sc > 0.0f ? 1.0f / sc : 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      int code = 0;
-      if (sc > 0.0f) code = (int)fminf(3.0f, fmaxf(0.0f, rintf((r[k][e] - z) / sc)));
-      codes_s[grp][k][8 * j + e] = (uint8_t)code;
+      const float c = fminf(3.0f, fmaxf(0.0f, rintf((r[k][e] - z) * rinv)));
+      codes_s[grp][k][8 * j + e] = (uint8_t)(int)c;
     }
   }
   __syncthreads();
@@ -931,16 +941,19 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   {
     const int64_t nw = (int64_t)U * 2 * (((int64_t)H * N + kToprGroup - 1) / kToprGroup);
     k_topr_flag<<<(unsigned)((nw + 3) / 4), 256, 0, st>>>(a.util, groups, cache, p.unit_stride, p.off_words,
-                                                          p.off_chunk_k, p.off_chunk_v, sel_list, Rmax, H, N, C, R,
-                                                          U * 2);
+                                                          p.off_chunk_k, p.off_chunk_v, sel_list,
+                                                          reinterpret_cast<int2*>(ws + w.sel_aux),
+                                                          reinterpret_cast<const int*>(ws + w.aidx),
+                                                          reinterpret_cast<const float*>(ws + w.gam), Rmax, H, N, C,
+                                                          R, U * 2);
     AKV_CHECK_LAUNCH("k_topr_flag");
   }
   prof_mark(st, "topr");
   if (R > 0) {
     const int nblk = (R + 16 * kQuantPerGroup - 1) / (16 * kQuantPerGroup);
     k_quant<DT><<<(unsigned)((int64_t)U * 2 * nblk), 256, 0, st>>>(
-        K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_res_k, p.off_res_v, sel_list, Rmax,
-        reinterpret_cast<const int*>(ws + w.aidx), reinterpret_cast<const float*>(ws + w.gam), H, N, A, R, nblk);
+        K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_res_k, p.off_res_v, sel_list,
+        reinterpret_cast<const int2*>(ws + w.sel_aux), Rmax, H, N, A, R, nblk);
     AKV_CHECK_LAUNCH("k_quant");
   }
   prof_mark(st, "quant");

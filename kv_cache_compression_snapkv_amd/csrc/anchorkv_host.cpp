@@ -64,6 +64,7 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
   w.anorm = take(8 * U * 2 * H * A);
   w.pooled = take(4 * U * H * N);
   w.sel_list = take(4 * U * 2 * std::max<int64_t>(1, std::max(p.R_K, p.R_V)));
+  w.sel_aux = take(8 * U * 2 * std::max<int64_t>(1, std::max(p.R_K, p.R_V)));
   w.sel_groups = take(8 * U * 2 * ((H * N + 1023) / 1024) + 8 * U * 2);
   w.total = off;
   return w;

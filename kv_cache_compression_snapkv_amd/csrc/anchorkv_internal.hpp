@@ -50,6 +50,7 @@ struct CompressWs {
   int64_t anorm;   // float2 [U][2][H][A] (||x_a||^2, 1/||x_a||)
   int64_t pooled;  // f32 [U][H][N]
   int64_t sel_list; // int32 [U][2][Rmax] flat (head*N + t) in record order
+  int64_t sel_aux;  // (int32 anchor index, f32 unrounded gamma) [U][2][Rmax] in record order
   int64_t sel_groups; // u32 [U][2][ceil(H*N/1024)][2] record / tie bases per 1024 positions, then [U][2][2] (T, need)
   int64_t total;
 };
