@@ -752,7 +752,13 @@ static int launch_obs(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t
     using C2 = ObsPipeCfg<MODE, 2>;
     if constexpr (MODE == OBS_UTIL) {
       // up to 6 query blocks: two key splits (12 waves, 3 per SIMD)
-      if (qpw == 1 && nw <= 6) k_obs_pipe<MODE, 1, C1::TK, C1::ST, 2, 3><<<grid, dim3(2 * 64 * nw), 0, st>>>(a);
+      const size_t qa_bytes = (size_t)((p.A + 15) / 16) * 16 * a.GQp * sizeof(float);
+      if (qpw == 1 && nw <= 6 && qa_bytes <= kObsQaMaxBytes) {
+        auto* fn = &k_obs_pipe<MODE, 1, C1::TK, C1::ST, 2, 3, true>;
+        static size_t done = 0;
+        if (int rc = set_dyn_lds(reinterpret_cast<const void*>(fn), qa_bytes, &done)) return rc;
+        fn<<<grid, dim3(2 * 64 * nw), qa_bytes, st>>>(a);
+      } else if (qpw == 1 && nw <= 6) k_obs_pipe<MODE, 1, C1::TK, C1::ST, 2, 3><<<grid, dim3(2 * 64 * nw), 0, st>>>(a);
       else if (qpw == 1) k_obs_pipe<MODE, 1, C1::TK, C1::ST, 1, 2><<<grid, block, 0, st>>>(a);
       else k_obs_pipe<MODE, 2, C2::TK, C2::ST, 1, 2><<<grid, block, 0, st>>>(a);
       // exact recompute of the tiles the fast pass flagged (its own stage)

@@ -54,6 +54,7 @@ constexpr int kObsSlot = 64;                 // per-key scalar / partial slots p
 template <int MODE, int QPW> struct ObsPipeCfg { static constexpr int TK = 64, ST = 2; };
 template <int QPW> struct ObsPipeCfg<OBS_UTIL, QPW> { static constexpr int TK = 64, ST = 2; };
 constexpr int kObsUtilTK = 64;   // UTIL / UTILX tile; the flag array allows >= 32
+constexpr size_t kObsQaMaxBytes = 64 * 1024;   // largest <q, x_a> table of the UTIL fast pass
 static_assert(ObsPipeCfg<OBS_UTIL, 1>::TK == kObsUtilTK && ObsPipeCfg<OBS_UTIL, 2>::TK == kObsUtilTK, "UTIL tile");
 
 // Chunk swizzle of tile row r, a bijection of r & 15 onto 0..15 (LDS has 64
@@ -161,12 +162,20 @@ struct ObsBufs {
 // runs 12 waves (3 per SIMD) instead of 6 (2, 2, 1, 1); at most 6 query
 // blocks with two splits.
 // WPE: waves per SIMD the register allocation must allow.
-template <int MODE, int QPW, int TK, int ST, int KS, int WPE>
+// QAT (UTIL fast pass): <q, x_a> for every (observation query, anchor) of the
+// head is computed once into an LDS table (dynamic shared memory, A rounded
+// up to 16 rows of GQp floats) with the same MFMA sequence the per-key path
+// uses, and gathered per key by its anchor index: no anchor-row copies, four
+// fewer MFMAs and fragment reads per 16 keys.  For heads whose table fits.
+template <int MODE, int QPW, int TK, int ST, int KS, int WPE, bool QAT = false>
 __global__ __launch_bounds__(KS == 1 ? 512 : 768) __attribute__((amdgpu_waves_per_eu(WPE))) void k_obs_pipe(ObsArgs a) {
   constexpr int D = kHeadDim, NSTEP = 4, KB = TK / 16;
   constexpr bool UTILX = MODE == OBS_UTILX;
   constexpr bool HAS_V = MODE != OBS_STATS;
-  constexpr bool HAS_G = MODE == OBS_UTIL || UTILX;
+  constexpr bool HAS_G = MODE == OBS_UTIL || UTILX;   // anchor-dependent terms
+  constexpr bool G_TILE = HAS_G && !QAT;               // gathered anchor rows in LDS
+  static_assert(!QAT || MODE == OBS_UTIL, "anchor table only in the UTIL fast pass");
+  extern __shared__ float qa_tab[];                    // QAT: [A16][GQp]
   constexpr bool HAS_PART = MODE != OBS_STATS;
   constexpr int TC = TK * 16;     // 16-byte chunks per [TK][128] bf16 tile
   constexpr float kLazy = 8.0f;   // STATS: rescale only when the max grows by more than 2^8
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(KS == 1 ? 512 : 768) __attribute__((amdgpu_waves_pe
 #define AKV_STAGE_BUFS(j)                                                               \
   __shared__ __attribute__((aligned(16))) uint4 K##j[(ST > j) ? TC : 1];                \
   __shared__ __attribute__((aligned(16))) uint4 V##j[(HAS_V && ST > j) ? TC : 1];       \
-  __shared__ __attribute__((aligned(16))) uint4 G##j[(HAS_G && ST > j) ? TC : 1];       \
+  __shared__ __attribute__((aligned(16))) uint4 G##j[(G_TILE && ST > j) ? TC : 1];      \
   __shared__ __attribute__((aligned(16))) float S##j[(HAS_G && ST > j) ? 3 * kObsSlot : 1];
   AKV_STAGE_BUFS(0) AKV_STAGE_BUFS(1) AKV_STAGE_BUFS(2) AKV_STAGE_BUFS(3) AKV_STAGE_BUFS(4) AKV_STAGE_BUFS(5)
 #undef AKV_STAGE_BUFS
@@ -311,7 +320,7 @@ __global__ __launch_bounds__(KS == 1 ? 512 : 768) __attribute__((amdgpu_waves_pe
     const int nval = min(TK, k1 - t0);
     int n = 0;
     if constexpr (HAS_G) {
-      n += dma_gather<TK>(b.G, Ap, Ai + it * TK, nval, nw, wave, dl);
+      if constexpr (G_TILE) n += dma_gather<TK>(b.G, Ap, Ai + it * TK, nval, nw, wave, dl);
       const int tl = min(t0 + lane, k1 - 1);
       for (int arr = wave; arr < 3; arr += nw, ++n) {
         const void* src = arr == 0 ? (const void*)(a.gam + sideK + tl)
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(KS == 1 ? 512 : 768) __attribute__((amdgpu_waves_pe
       for (int st = 0; st < NSTEP; ++st) {
         af[st] = lds_frag(c.K, row, st * 4 + kg);
         if constexpr (HAS_G) {
-          gf[st] = lds_frag(c.G, row, st * 4 + kg);
+          if constexpr (G_TILE) gf[st] = lds_frag(c.G, row, st * 4 + kg);
           vf[st] = lds_frag(c.V, row, st * 4 + kg);
         }
       }
@@ -396,7 +405,12 @@ __global__ __launch_bounds__(KS == 1 ? 512 : 768) __attribute__((amdgpu_waves_pe
         f32x4 accv = {oinit, oinit, oinit, oinit};
         for (int st = 0; st < NSTEP; ++st) acc = M::mma(af[st], qf[qi][st], acc);
         if constexpr (HAS_G) {
-          for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf[st], qf[qi][st], accg);
+          if constexpr (QAT) {
+            const int qcol = (qw + qi * nq) * 16 + col;
+            for (int r = 0; r < 4; ++r) accg[r] = qa_tab[Ai[it * TK + kb * 16 + kg * 4 + r] * a.GQp + qcol];
+          } else {
+            for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf[st], qf[qi][st], accg);
+          }
           for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[st], ofh[qi][st], accv);
           for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[st], ofl[qi][st], accv);
         }
@@ -523,6 +537,22 @@ __global__ __launch_bounds__(KS == 1 ? 512 : 768) __attribute__((amdgpu_waves_pe
                         {K3, V3, G3, S3}, {K4, V4, G4, S4}, {K5, V5, G5, S5}};
   if constexpr (HAS_G) {
     wait_vm_all();     // anchor indices before the gathers that use them
+    __syncthreads();
+  }
+  if constexpr (QAT) {
+    // table rows of 16 anchors per MFMA (A operand: anchor rows from the
+    // cache; B: this wave's query fragments); the key splits share the blocks
+    const int nab = (a.A + 15) / 16;
+    for (int qi = 0; qi < QPW; ++qi) {
+      if (qi > 0 && !qactive[qi]) continue;
+      const int qcol = (qw + qi * nq) * 16 + col;
+      for (int ab = wave / nq; ab < nab; ab += KS) {
+        const int arow = min(ab * 16 + col, a.A - 1);
+        f32x4 acc = {0, 0, 0, 0};
+        for (int st = 0; st < NSTEP; ++st) acc = M::mma(M::load(Ap + (int64_t)arow * D + st * 32 + kg * 8), qf[qi][st], acc);
+        for (int r = 0; r < 4; ++r) qa_tab[(ab * 16 + kg * 4 + r) * a.GQp + qcol] = acc[r];
+      }
+    }
     __syncthreads();
   }
   if constexpr (UTILX) {
