@@ -796,7 +796,6 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
   g.vn2 = reinterpret_cast<float*>(ws + w.vn2);
   g.score = oa.score;
   g.util = oa.util;
-  g.best64 = reinterpret_cast<unsigned long long*>(ws + w.best64);
   g.H = H; g.N = N; g.A = A;
   const int64_t hs = (int64_t)U * 2 * H;
   // 8-wave blocks, two per compute unit, when a part's anchors fit twice in LDS
@@ -819,8 +818,8 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
     g.nblk = (ntiles_hs + tpb - 1) / tpb;
   }
   const unsigned grid = (unsigned)(hs * g.nblk);
+  g.a0 = 0; g.a1 = A;
   if (A <= kAssignResMax) {
-    g.a0 = 0; g.a1 = A;
     const size_t lds = assign_lds_bytes(A, waves);
     if (w8) {
       static size_t done = 0;
@@ -831,24 +830,14 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
       if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<false, 16>), lds, &done)) return rc;
       k_assign_res<false, 16><<<grid, 64 * 16, lds, st>>>(g);
     }
-    AKV_CHECK_LAUNCH("k_assign_res");
-    return 0;
+  } else {
+    // the parts are walked inside the kernel (tokens read once)
+    const size_t lds = assign_lds_bytes(kAssignResMax, 16, true);
+    static size_t done = 0;
+    if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<true, 16>), lds, &done)) return rc;
+    k_assign_res<true, 16><<<grid, 64 * 16, lds, st>>>(g);
   }
-  static size_t done_p = 0;
-  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<true, 16>), assign_lds_bytes(kAssignResMax, 16),
-                           &done_p))
-    return rc;
-  const int64_t total = hs * N;
-  k_zero_u32<<<(unsigned)((2 * total + 255) / 256), 256, 0, st>>>(
-      reinterpret_cast<unsigned*>(g.best64), 2 * total);
-  AKV_CHECK_LAUNCH("k_zero_u32");
-  for (int a0 = 0; a0 < A; a0 += kAssignResMax) {
-    g.a0 = a0; g.a1 = std::min(A, a0 + kAssignResMax);
-    k_assign_res<true, 16><<<grid, 64 * 16, assign_lds_bytes(g.a1 - g.a0, 16), st>>>(g);
-    AKV_CHECK_LAUNCH("k_assign_res");
-  }
-  k_assign_proj<<<(unsigned)((total + 63) / 64), 256, 0, st>>>(g, total);
-  AKV_CHECK_LAUNCH("k_assign_proj");
+  AKV_CHECK_LAUNCH("k_assign_res");
   return 0;
 }
 

@@ -60,7 +60,6 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
   w.anchor_of = take(4 * U * H * N);
   w.vn2 = take(4 * U * H * N);
   w.uflag = take(U * H * ((N + 31) / 32));
-  w.best64 = take((p.dtype == ANCHORKV_BF16 && A > kAssignResMax) ? 8 * U * 2 * H * N : 0);
   w.anorm = take(8 * U * 2 * H * A);
   w.pooled = take(4 * U * H * N);
   w.sel_list = take(4 * U * 2 * std::max<int64_t>(1, std::max(p.R_K, p.R_V)));

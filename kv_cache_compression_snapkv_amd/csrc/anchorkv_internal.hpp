@@ -46,7 +46,6 @@ struct CompressWs {
   int64_t anchor_of; // int32 [U][H][N] anchor index of a position, -1 if none
   int64_t vn2;     // f32 [U][H][N] ||v_t||^2
   int64_t uflag;   // u8 [U][H][ceil(N/32)] utility tile flags (bf16 path)
-  int64_t best64;  // u64 [U][2][H][N] packed part winners (bf16, A > kAssignResMax only)
   int64_t anorm;   // float2 [U][2][H][A] (||x_a||^2, 1/||x_a||)
   int64_t pooled;  // f32 [U][H][N]
   int64_t sel_list; // int32 [U][2][Rmax] flat (head*N + t) in record order

@@ -29,10 +29,10 @@
 // its first token tile) overlap the other's compute; larger parts use 16-wave
 // blocks, one per compute unit.
 //
-// Anchor sets larger than kAssignResMax are processed in parts: each part
-// folds its per-token winner into a 64-bit key (monotone cosine bits << 32 |
-// ~index) with a global atomicMax (order independent, so deterministic), and
-// k_assign_proj then does the projection for every token.
+// Anchor sets larger than kAssignResMax are processed in parts inside the
+// kernel: every token tile walks the parts, keeping each token's best as a
+// 64-bit key (monotone cosine bits << 32 | ~index), so the tokens are read
+// once.
 #pragma once
 
 #include "device_common.hpp"
@@ -45,9 +45,10 @@ namespace akv {
 
 constexpr int kAssignSlot = 2 * 64 * 4;   // per-wave LDS bytes: token scalars of a 64-token tile
 // Dynamic LDS of a block with `waves` waves over `nA` anchors.
-inline size_t assign_lds_bytes(int nA, int waves) {
+// (multi: anchors in parts; a 64-bit running best per token of each wave)
+inline size_t assign_lds_bytes(int nA, int waves, bool multi = false) {
   const size_t rows = (size_t)((nA + 15) / 16) * 16;
-  return rows * kHeadDim * 2 + rows * 8 + (size_t)waves * kAssignSlot;
+  return rows * kHeadDim * 2 + rows * 8 + (size_t)waves * kAssignSlot + (multi ? (size_t)waves * 64 * 8 : 0);
 }
 
 struct AssignArgs {
@@ -63,7 +64,6 @@ struct AssignArgs {
   float* vn2;                // [U][H][N] ||v||^2
   const float* score;        // [U][H][N]
   float* util;               // [U][2][H][N] (value side written here)
-  unsigned long long* best64;  // [U][2][H][N] packed winners of the parts
   int H, N, A, a0, a1;       // anchors [a0, a1) of this launch
   int tiles_per_block, nblk;  // token tiles per block, blocks per (unit, side, head)
 };
@@ -138,7 +138,13 @@ __device__ __forceinline__ void assign_project(const AssignArgs& g, int u, int s
 // rows an MFMA B fragment read touches land on 16 distinct chunk positions.
 __device__ __forceinline__ int res_phys(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 
-template <bool PARTIAL, int WAVES>
+// MULTI: the anchors of the head exceed one LDS part (kAssignResMax); every
+// token tile walks all parts (each copied into LDS in turn, the tokens staying
+// in registers), keeping each token's best as a 64-bit key (monotone cosine
+// bits << 32 | ~anchor index: lowest index on equal keys); the projection
+// then reads the winning anchor row from the cache.  The tokens are read from
+// memory once, whatever the number of parts.
+template <bool MULTI, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
   constexpr int kTile = 64 * WAVES;   // tokens per block tile
   using M = Mfma<ANCHORKV_BF16>;
@@ -153,22 +159,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
   const int h = bid % g.H; bid /= g.H;
   const int side = bid % 2;
   const int u = bid / 2;
-  const int N = g.N;
+  const int N = g.N, A = g.A;
   const int64_t uh = (int64_t)u * g.H + h;
-  const int nA = g.a1 - g.a0;
-  const int nab = (nA + 15) >> 4;
-  uint4* As = dyn_lds;                                        // [nab*16 rows][16 chunks], swizzled
-  float* inv_s = reinterpret_cast<float*>(As + nab * 16 * 16);  // [nab*16] 1/||x_a||
-  float* na2_s = inv_s + nab * 16;                                // [nab*16] ||x_a||^2
+  const int pa = MULTI ? kAssignResMax : A;           // anchors per part
+  const int nparts = (A + pa - 1) / pa;
+  const int nab_max = (pa + 15) >> 4;
+  uint4* As = dyn_lds;                                            // [nab*16 rows][16 chunks], swizzled
+  float* inv_s = reinterpret_cast<float*>(As + nab_max * 16 * 16);  // [nab*16] 1/||x_a||
+  float* na2_s = inv_s + nab_max * 16;                                // [nab*16] ||x_a||^2
   // per wave: [64] anchor_of of its tokens (then the chosen anchor, bit 31 =
   // anchor token), [64] observation scores
-  int* selfs = reinterpret_cast<int*>(na2_s + nab * 16) + wave * (kAssignSlot / 4);
+  int* selfs = reinterpret_cast<int*>(na2_s + nab_max * 16) + wave * (kAssignSlot / 4);
   float* scs = reinterpret_cast<float*>(selfs + 64);
+  // MULTI: [64] running best key of the wave's tokens
+  unsigned long long* runb = reinterpret_cast<unsigned long long*>(
+                                 reinterpret_cast<int*>(na2_s + nab_max * 16) + WAVES * (kAssignSlot / 4)) +
+                             wave * 64;
   const uint16_t* X = (side ? g.V : g.K) + uh * N * D;
   const uint16_t* AX = reinterpret_cast<const uint16_t*>(g.cache + (int64_t)u * g.stride +
                                                          (side ? g.off_anchor_v : g.off_anchor_k)) +
-                       (int64_t)h * g.A * D;
-  const float2* an = g.anorm + ((int64_t)u * 2 * g.H + side * g.H + h) * g.A;
+                       (int64_t)h * A * D;
+  const float2* an = g.anorm + ((int64_t)u * 2 * g.H + side * g.H + h) * A;
 
   const int ntiles_hs = (N + kTile - 1) / kTile;
   const int tile0 = blk * g.tiles_per_block;
@@ -181,38 +192,41 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
       for (int st = 0; st < 4; ++st) xf[rb][st] = M::load(X + (int64_t)t * D + st * 32 + kg * 8);
     }
   };
-
-  // ---- anchors of this part into LDS (rows beyond nA repeat the last one),
-  // with the first token tile loading alongside
-  bf16x8 xf[4][4];
-  {
+  // anchors [a0, a1) into LDS (rows beyond a1 repeat the last one: padding
+  // rows copy the last anchor's row and 1/||x_a||, tie with it and lose on
+  // the column, so they never win)
+  auto load_part = [&](int a0, int a1) {
+    const int nA = a1 - a0, nab = (nA + 15) >> 4;
     for (int jj = wave; jj < nab * 4; jj += WAVES) {
       const int r = jj * 4 + (lane >> 4);               // tile row of this lane's chunk
       const int c = (lane & 15) ^ (r & 15);             // its logical chunk
-      dma16(AX + (int64_t)(g.a0 + min(r, nA - 1)) * D + c * 8, As + jj * 64);
+      dma16(AX + (int64_t)(a0 + min(r, nA - 1)) * D + c * 8, As + jj * 64);
     }
-    // padding rows copy the last anchor (row and 1/||x_a||): they tie with it
-    // and lose on the column, so they never win
     for (int i = threadIdx.x; i < nab * 16; i += blockDim.x) {
-      const float2 v = an[g.a0 + min(i, nA - 1)];
+      const float2 v = an[a0 + min(i, nA - 1)];
       inv_s[i] = v.y;
       na2_s[i] = v.x;
     }
-    if (tile0 < tile1) load_tokens(tile0, xf);
+  };
+
+  bf16x8 xf[4][4];
+  if (!MULTI) load_part(0, A);
+  if (tile0 < tile1) load_tokens(tile0, xf);
+  if (!MULTI) {
     __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));
     __syncthreads();
   }
 
   // Running maximum of the keys as signed integers: for non-negative
   // cosines the float bits order like the values, so v_max_i32 needs no NaN
-  // canonicalisation.  A wave holding a token whose best key over all anchors
-  // is negative (every cosine <= 0, rare) redoes the search with
+  // canonicalisation.  A wave holding a token whose best key over the part's
+  // anchors is negative (every cosine <= 0, rare) redoes the search with
   // sign-corrected keys; the test is on the token's row maximum, since a
   // lane's own column sees only A/16 anchors and is often all negative.
   // the mask lives in a VGPR so that (bits & mask) | tag is one v_and_or_b32
   unsigned keymask;
   __asm__("v_mov_b32 %0, 0xffffffe0" : "=v"(keymask));
-  auto search = [&](const bf16x8 (&xt)[4][4], int (&best)[4][4], auto mono_tag) {
+  auto search = [&](const bf16x8 (&xt)[4][4], int (&best)[4][4], int nab, auto mono_tag) {
     constexpr bool mono = decltype(mono_tag)::value;
     for (int rb = 0; rb < 4; ++rb)
       for (int r = 0; r < 4; ++r) best[rb][r] = INT_MIN;
@@ -246,106 +260,97 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
       dma4(g.anchor_of + uh * N + t, selfs);
       if (side) dma4(g.score + uh * N + t, scs);
     }
-    int best[4][4];
-    int mk[4][4];   // row (token) maxima of the keys
-    auto row_maxima = [&]() {
-      for (int rb = 0; rb < 4; ++rb)
-        for (int r = 0; r < 4; ++r) mk[rb][r] = row_max_i32(best[rb][r]);
-    };
-    search(xf, best, std::false_type{});
-    row_maxima();
-    bool neg = false;
-    for (int rb = 0; rb < 4; ++rb)
-      for (int r = 0; r < 4; ++r) neg |= mk[rb][r] < 0;
-    if (__builtin_amdgcn_ballot_w64(neg) != 0) {
-      search(xf, best, std::true_type{});
-      row_maxima();
-    }
-    __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));   // this wave's copies of selfs / scs
-    // ---- reduce the 16 anchor columns of every token: row maximum of the
-    // keys, lowest column holding it; lanes col < 4 of row kg publish token
-    // rb*16 + kg*4 + col (chosen anchor, bit 31 = anchor token) in selfs
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      int wv[4];
-      for (int r = 0; r < 4; ++r) {
-        const int m = mk[rb][r];
-        const unsigned long long eq = __builtin_amdgcn_ballot_w64(best[rb][r] == m);
-        const unsigned bits = (unsigned)(eq >> (kg * 16)) & 0xFFFFu;   // never 0: the row holds its maximum
-        wv[r] = g.a0 + __builtin_ctz(bits) + 16 * (31 - (m & 31));
+    // MULTI: running best of each token (written by the lane that takes it)
+    if (MULTI) runb[lane] = 0ull;
+    for (int part = 0; part < nparts; ++part) {
+      const int a0 = part * pa, a1 = min(A, a0 + pa);
+      const int nab = (a1 - a0 + 15) >> 4;
+      if (MULTI) {
+        __syncthreads();          // every wave is done with the previous part
+        load_part(a0, a1);
+        __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));
+        __syncthreads();
       }
-      if (col < 4) {
-        const int w = col == 0 ? wv[0] : col == 1 ? wv[1] : col == 2 ? wv[2] : wv[3];
-        const int tl = rb * 16 + kg * 4 + col;   // token of the wave's tile
-        if constexpr (PARTIAL) {
-          const int tt = tile * kTile + wave * 64 + tl;
-          // (one static index per pass: a select over mk would become a
-          // private-memory array lookup)
+      int best[4][4];
+      int mk[4][4];   // row (token) maxima of the keys
+      auto row_maxima = [&]() {
+        for (int rb = 0; rb < 4; ++rb)
+          for (int r = 0; r < 4; ++r) mk[rb][r] = row_max_i32(best[rb][r]);
+      };
+      search(xf, best, nab, std::false_type{});
+      row_maxima();
+      bool neg = false;
+      for (int rb = 0; rb < 4; ++rb)
+        for (int r = 0; r < 4; ++r) neg |= mk[rb][r] < 0;
+      if (__builtin_amdgcn_ballot_w64(neg) != 0) {
+        search(xf, best, nab, std::true_type{});
+        row_maxima();
+      }
+      __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));   // this wave's copies of selfs / scs
+      // ---- reduce the 16 anchor columns of every token: row maximum of the
+      // keys, lowest column holding it; lanes col < 4 of row kg take token
+      // rb*16 + kg*4 + col
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (col == r && tt < N) {
-              // signed-monotone key -> unsigned order, then ~index for lowest-index ties
-              const unsigned long long key64 =
-                  ((unsigned long long)(((unsigned)mk[rb][r] & keymask) ^ 0x80000000u) << 32) |
-                  (unsigned long long)(0xFFFFFFFFu - (unsigned)wv[r]);
-              atomicMax(g.best64 + ((int64_t)u * 2 * g.H + side * g.H + h) * N + tt, key64);
+      for (int rb = 0; rb < 4; ++rb) {
+        int wv[4];
+        for (int r = 0; r < 4; ++r) {
+          const int m = mk[rb][r];
+          const unsigned long long eq = __builtin_amdgcn_ballot_w64(best[rb][r] == m);
+          const unsigned bits = (unsigned)(eq >> (kg * 16)) & 0xFFFFu;   // never 0: the row holds its maximum
+          wv[r] = a0 + __builtin_ctz(bits) + 16 * (31 - (m & 31));
+        }
+        if (col < 4) {
+          if constexpr (MULTI) {
+            // (one static index per pass: a select over mk would become a
+            // private-memory array lookup)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (col == r) {
+                // signed-monotone key -> unsigned order, then ~index for lowest-index ties
+                const unsigned long long key64 =
+                    ((unsigned long long)(((unsigned)mk[rb][r] & keymask) ^ 0x80000000u) << 32) |
+                    (unsigned long long)(0xFFFFFFFFu - (unsigned)wv[r]);
+                const int tl = rb * 16 + kg * 4 + r;
+                runb[tl] = max(runb[tl], key64);
+              }
             }
+          } else {
+            const int w = col == 0 ? wv[0] : col == 1 ? wv[1] : col == 2 ? wv[2] : wv[3];
+            const int tl = rb * 16 + kg * 4 + col;   // token of the wave's tile
+            const int self = selfs[tl];
+            selfs[tl] = self >= 0 ? (int)(0x80000000u | (unsigned)self) : w;
           }
-        } else {
-          const int self = selfs[tl];
-          selfs[tl] = self >= 0 ? (int)(0x80000000u | (unsigned)self) : w;
         }
       }
     }
-    // ---- projection of every token onto its anchor
-    if constexpr (!PARTIAL) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's selfs writes done
+    if constexpr (MULTI) {
+      // each token's entry was written by its own lane: one lane per token now
+      __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
-      for (int rb = 0; rb < 4; ++rb) {
-        const int t = tile * kTile + wave * 64 + rb * 16 + col;
-        const int sa = selfs[rb * 16 + col];
-        const bool is_anchor = sa < 0;
-        const int a = sa & 0x7FFFFFFF;
-        assign_project(g, u, side, h, t, a, is_anchor, na2_s[a - g.a0], scs[rb * 16 + col], xf[rb],
-                       [&](int c) { return As[res_phys(a - g.a0, c)]; }, kg);
-      }
+      const int w = (int)(0xFFFFFFFFu - (unsigned)(runb[lane] & 0xFFFFFFFFull));
+      const int self = selfs[lane];
+      selfs[lane] = self >= 0 ? (int)(0x80000000u | (unsigned)self) : w;
+    }
+    // ---- projection of every token onto its anchor
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's selfs writes done
+    __builtin_amdgcn_wave_barrier();
+    for (int rb = 0; rb < 4; ++rb) {
+      const int t = tile * kTile + wave * 64 + rb * 16 + col;
+      const int sa = selfs[rb * 16 + col];
+      const bool is_anchor = sa < 0;
+      const int a = sa & 0x7FFFFFFF;
+      if constexpr (MULTI)
+        assign_project(g, u, side, h, t, a, is_anchor, an[a].x, scs[rb * 16 + col], xf[rb],
+                       [&](int c) { return *reinterpret_cast<const uint4*>(AX + (int64_t)a * D + c * 8); }, kg);
+      else
+        assign_project(g, u, side, h, t, a, is_anchor, na2_s[a], scs[rb * 16 + col], xf[rb],
+                       [&](int c) { return As[res_phys(a, c)]; }, kg);
     }
     // this wave's LDS slots are rewritten by the next tile's copies
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
     if (tile + 1 < tile1) load_tokens(tile + 1, xf);
   }
-}
-
-// Projection after a partitioned anchor search: one 4-lane group per token
-// (64 tokens per 256-thread block; lanes (col, kg) as in the MFMA layout).
-__global__ __launch_bounds__(256) void k_assign_proj(AssignArgs g, int64_t total) {
-  constexpr int D = kHeadDim;
-  const int lane = threadIdx.x & 63;
-  const int kg = lane >> 4;
-  const int64_t tok = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + (lane & 15);  // over [U][2][H][N]
-  const bool live = tok < total;
-  const int64_t tk = live ? tok : total - 1;
-  const int t = (int)(tk % g.N);
-  int64_t rest = tk / g.N;
-  const int h = (int)(rest % g.H); rest /= g.H;
-  const int side = (int)(rest % 2);
-  const int u = (int)(rest / 2);
-  const int64_t uh = (int64_t)u * g.H + h;
-  const uint16_t* X = (side ? g.V : g.K) + (uh * g.N + t) * D;
-  const uint16_t* AX = reinterpret_cast<const uint16_t*>(g.cache + (int64_t)u * g.stride +
-                                                         (side ? g.off_anchor_v : g.off_anchor_k)) +
-                       (int64_t)h * g.A * D;
-  bf16x8 xf[4];
-  for (int st = 0; st < 4; ++st) xf[st] = Mfma<ANCHORKV_BF16>::load(X + st * 32 + kg * 8);
-  const int self = g.anchor_of[uh * g.N + t];
-  const bool is_anchor = self >= 0;
-  const unsigned long long key = g.best64[tk];
-  const int a = is_anchor ? self : (int)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
-  const float na2 = g.anorm[((int64_t)u * 2 * g.H + side * g.H + h) * g.A + a].x;
-  const float sc = side ? g.score[uh * g.N + t] : 0.0f;
-  assign_project(g, u, side, h, live ? t : g.N, a, is_anchor, na2, sc, xf,
-                 [&](int c) { return *reinterpret_cast<const uint4*>(AX + (int64_t)a * D + c * 8); }, kg);
 }
 
 }  // namespace akv
