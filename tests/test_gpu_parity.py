@@ -35,6 +35,12 @@ SMALL = {
     # every token an anchor: decode is exact attention
     "bf16_all_anchors": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=2, n_tokens=256, n_obs=8,
                                                window=256, theta=1.5, n_dirs=8),
+    # more anchors than one LDS part (512): the assignment walks two parts
+    "bf16_multi_part": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=2, n_tokens=2048, n_obs=16,
+                                              window=600, theta=0.5, n_dirs=8),
+    # kv_heads * n_tokens > 65536: top-R streams the utilities instead of holding them in registers
+    "bf16_long_topr": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=3, q_per_kv=2, n_tokens=22000, n_obs=16,
+                                             window=32, theta=0.1, n_dirs=16),
     # budget leaves no residual slots
     "bf16_no_residuals": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=1, q_per_kv=2, n_tokens=256, n_obs=8,
                                                 window=32, theta=0.144, n_dirs=8),
