@@ -25,6 +25,7 @@
 #include "device_common.hpp"
 #include "launch_common.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace akv {
@@ -36,6 +37,8 @@ constexpr int kWaves = 8;         // waves per workgroup; 128 tokens per wave pe
 constexpr uint32_t kCodeBias = 0x43004300u;  // bf16 pair (128, 128)
 constexpr float kFxScale = 2097152.0f;          // 2^21: fixed-point scale of the w scatter
 constexpr double kFxInv = 1.0 / 2097152.0;
+// floats of the per-tile buffer: [kTile][G], at least the 8 KB of staged words
+template <int G> constexpr int kBufFloats = kTile * G > 2048 ? kTile * G : 2048;
 
 // y (already scaled by 2^21) -> two's-complement 64-bit fixed point, any sign
 // and |y| < 2^62.
@@ -97,6 +100,78 @@ __device__ __forceinline__ bf16x8 u4_to_frag(uint32_t a, uint32_t b, uint32_t c,
   return bits_to_frag(make_uint4(a, b, c, d));
 }
 
+// (a & m) | b as one v_and_or_b32 with m uniform (an SGPR) and b in a VGPR:
+// the three-operand encoding takes no literal here, so with both constants
+// written as literals the compiler would split it into two instructions.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(b));
+  return d;
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+// two floats -> packed bf16 pair (round to nearest even), lo in bits 0..15
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
+  const f32x2v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+
+// Code planes.  In a record, code word j holds coordinates j + 16c (c = 0..7)
+// at bits p = 2c, p + 1.  A 32-bit word of two code words, shifted right by
+// sh in {0, 6, 12}, has the field of plane c at bits 2m, 2m + 1 (m = 0, 1, 2)
+// of both halves; masking it there and OR-ing the exponent of 128 gives the
+// exact bf16 pair 128 + code * 4^m.  The 4^m is folded into the other MFMA
+// operand (keys) or removed at the end (values); the 128 is cancelled by the
+// accumulator's initial value (keys) or by a bias MFMA (values).
+struct Plane {
+  int sh, m;
+};
+__device__ constexpr Plane plane_of(int c) {
+  return c < 3 ? Plane{0, c} : c < 6 ? Plane{6, c - 3} : Plane{12, c - 6};
+}
+constexpr float kPlaneInv[3] = {1.0f, 0.25f, 0.0625f};
+
+// ordered-int image of a float (monotone), for LDS integer max
+__device__ __forceinline__ int fkey(float f) {
+  const int b = __float_as_int(f);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float fkey_inv(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
+constexpr int kKeyNegInf = (int)0x807FFFFF;  // fkey(-inf)
+
+template <int N> struct FVec;
+template <> struct FVec<1> { using T = float; };
+template <> struct FVec<2> { using T = float2; };
+template <> struct FVec<4> { using T = float4; };
+// GP consecutive floats from / to LDS (16-byte aligned for GP >= 4)
+template <int GP> __device__ __forceinline__ void ldsv(const float* p, float (&o)[GP]) {
+  if constexpr (GP <= 4) {
+    const typename FVec<GP>::T v = *reinterpret_cast<const typename FVec<GP>::T*>(p);
+    __builtin_memcpy(o, &v, sizeof(v));
+  } else {
+#pragma unroll
+    for (int k = 0; k < GP / 4; ++k) {
+      const float4 v = reinterpret_cast<const float4*>(p)[k];
+      o[4 * k] = v.x; o[4 * k + 1] = v.y; o[4 * k + 2] = v.z; o[4 * k + 3] = v.w;
+    }
+  }
+}
+template <int GP> __device__ __forceinline__ void stsv(float* p, const float (&o)[GP]) {
+  if constexpr (GP <= 4) {
+    typename FVec<GP>::T v;
+    __builtin_memcpy(&v, o, sizeof(v));
+    *reinterpret_cast<typename FVec<GP>::T*>(p) = v;
+  } else {
+#pragma unroll
+    for (int k = 0; k < GP / 4; ++k)
+      reinterpret_cast<float4*>(p)[k] = make_float4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+  }
+}
+
+template <int G> constexpr int kGPad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+constexpr int kRecPad = 32;  // zeroed records after the value staging (batch tails read them)
+
 template <int DT, int G, int KP, int DEPTH>
 __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   constexpr int kPre = KP;
@@ -104,18 +179,26 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   using T = typename Elem<DT>::T;
   using M = Mfma<ANCHORKV_BF16>;
   constexpr int D = kHeadDim;
+  constexpr int GP = kGPad<G>;                   // q-heads per anchor row in LDS (padded)
   constexpr int NB = (4 * G + 15) / 16;          // 16-wide blocks of (q-head, group) pairs
   constexpr bool QSPLIT = DT == ANCHORKV_F32;   // f32 queries enter the key MFMA as bf16 hi + lo
-  extern __shared__ float sm[];
+  extern __shared__ __align__(16) float sm[];
   const int A = a.A;
-  float* S = sm;                                                  // [G][A]
-  unsigned long long* wi = reinterpret_cast<unsigned long long*>(S + ((G * A + 1) & ~1));  // [G][A] fixed point
-  float* buf = reinterpret_cast<float*>(wi + G * A);             // [kTile][G]: key-residual logits, p of value-flagged tokens, [G][D]
-  uint4* kst = reinterpret_cast<uint4*>(buf + kTile * G);  // staged key records of the tile (kRecCap x 48 B)
-  uint4* vst = kst + 512 * kPre;                            // staged value records
+  unsigned long long* wi = reinterpret_cast<unsigned long long*>(sm);  // [A][GP] fixed point
+  float* S = reinterpret_cast<float*>(wi + A * GP);                      // [A][GP]
+  // [kTile][GP]: key-residual logits, then p of value-flagged tokens; [G][D]
+  // at the end.  At the start of a tile it first holds the staged pointer
+  // words ([512] x 16 B).
+  float* buf = sm + ((3 * GP * A + 3) & ~3);
+  uint4* wst = reinterpret_cast<uint4*>(buf);
+  uint4* kst = reinterpret_cast<uint4*>(buf + kBufFloats<GP>);  // staged key records of the tile
+  uint4* vst = kst + 512 * kPre;                                 // staged value records, then kRecPad zero records
+  const uint8_t* kstb = reinterpret_cast<const uint8_t*>(kst);
+  const uint8_t* vstb = reinterpret_cast<const uint8_t*>(vst);
   __shared__ int cnt[kWaves][2];
   __shared__ int offs[2][130];
-  __shared__ float tmax[kWaves][G];
+  __shared__ __align__(16) int tmaxb[2][GP];
+  __shared__ __align__(16) float zrow[GP];
   __shared__ float zt_s[G * 4];
 
   int bid = blockIdx.x;
@@ -132,8 +215,18 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   const uint8_t* recV = base + a.off_rv;
   const T* q = reinterpret_cast<const T*>(a.q) + uh * G * D;
 
-  for (int i = threadIdx.x; i < G * A; i += blockDim.x) { S[i] = a.stab[uh * G * A + i]; wi[i] = 0ull; }
+  for (int i = threadIdx.x; i < GP * A; i += blockDim.x) {
+    const int aa = i / GP, g = i % GP;
+    S[i] = g < G ? a.stab[(uh * G + g) * A + aa] : 0.0f;
+    wi[i] = 0ull;
+  }
+  for (int i = threadIdx.x; i < kRecPad * kRecBytes / 16; i += blockDim.x) vst[512 * kPre + i] = make_uint4(0, 0, 0, 0);
   if (threadIdx.x < G * 4) zt_s[threadIdx.x] = 0.0f;
+  if (threadIdx.x < GP) {
+    zrow[threadIdx.x] = 0.0f;
+    tmaxb[0][threadIdx.x] = kKeyNegInf;
+    tmaxb[1][threadIdx.x] = kKeyNegInf;
+  }
   // record offsets of the range's chunks and of the chunk after the last one
   const int nch = max(0, c1 - c0);
   for (int i = threadIdx.x; i <= nch; i += blockDim.x) {
@@ -143,28 +236,47 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
     offs[1][i] = last ? a.R_V : reinterpret_cast<const int*>(base + a.off_cv)[fl];
   }
 
+  // code-plane constants: masks (SGPRs) and the exponent bias (one VGPR)
+  const uint32_t MK[3] = {0x00030003u, 0x000C000Cu, 0x00300030u};
+  uint32_t vbias = kCodeBias;
+  asm volatile("" : "+v"(vbias));
+
   // Key-side B fragments: column kappa = 16*cb + col = 4*g + grp; in MFMA step
-  // st (= coordinate group st) the lane supplies q[g][j + 16c], j = 4kg + (e&3),
-  // c = 2st + (e>>2), when grp == st, zeros otherwise.
+  // st (= coordinate group st) the lane supplies q[g][d] / 4^m for
+  // d = j + 16c, j = 4kg + (e&3), c = 2st + (e>>2), when grp == st, zeros
+  // otherwise.  cinit = -128 * (sum of what the column is fed), so the
+  // accumulator ends at sum_d q[g][d] * code_d.
   bf16x8 qB[NB][4], qBl[QSPLIT ? NB : 1][4];
-  float qsum[NB];
+  float qsum[NB], cinit[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const int kap = 16 * cb + col;
     const int g = kap >> 2, grp = kap & 3;
-    float qs = 0.0f;
+    float qs = 0.0f, fed = 0.0f;
     if (g < G)
-      for (int d = 32 * grp; d < 32 * grp + 32; ++d) qs += Elem<DT>::f(q[g * D + d]);
+      for (int d = 32 * grp; d < 32 * grp + 32; ++d) {
+        const float x = Elem<DT>::f(q[g * D + d]);
+        const float sc = kPlaneInv[plane_of(d >> 4).m];
+        const float xh = bf2f(f2bf(x));
+        qs += x;
+        fed += xh * sc;
+        if constexpr (QSPLIT) fed += bf2f(f2bf(x - xh)) * sc;
+      }
     qsum[cb] = qs;
+    cinit[cb] = -128.0f * fed;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint16_t vh[8], vl[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = (4 * kg + (e & 3)) + 16 * (2 * st + (e >> 2));
+        const int c = 2 * st + (e >> 2);
+        const int d = (4 * kg + (e & 3)) + 16 * c;
         const float x = (g < G && grp == st) ? Elem<DT>::f(q[g * D + d]) : 0.0f;
+        const float sc = kPlaneInv[plane_of(c).m];
         vh[e] = f2bf(x);
         vl[e] = f2bf(x - bf2f(vh[e]));
+        vh[e] = f2bf(bf2f(vh[e]) * sc);  // exact: power-of-two scaling
+        vl[e] = f2bf(bf2f(vl[e]) * sc);
       }
       qB[cb][st] = u4_to_frag(vh[0] | (uint32_t)vh[1] << 16, vh[2] | (uint32_t)vh[3] << 16, vh[4] | (uint32_t)vh[5] << 16,
                               vh[6] | (uint32_t)vh[7] << 16);
@@ -173,17 +285,22 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
                                  vl[4] | (uint32_t)vl[5] << 16, vl[6] | (uint32_t)vl[7] << 16);
     }
   }
+  // value side: B = -128 everywhere cancels the code bias of the A rows
+  const bf16x8 bm128 = u4_to_frag(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u);
   __syncthreads();
 
   float m_run[G], lacc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; lacc[g] = 0.0f; }
-  f32x4 vacc[NB][8];   // value side: row block rb (rows 4g + grp), column block cc (coordinates j + 16cc)
+  f32x4 vacc[NB][8];   // value side: row block rb (rows 4g + grp), column block cc (coordinates j + 16cc), x 4^m
+  f32x4 zacc[NB];      // value side: -128 * sum of the A rows (the code bias)
 #pragma unroll
-  for (int rb = 0; rb < NB; ++rb)
+  for (int rb = 0; rb < NB; ++rb) {
+    zacc[rb] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] = f32x4{0, 0, 0, 0};
-  float zt[NB];        // value side: sum of p*zero - 128*(p*scale as fed to the MFMA) for row (rb, col)
+  }
+  float zt[NB];        // value side: sum of p * zero for row (rb, col)
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) zt[rb] = 0.0f;
 
@@ -191,82 +308,104 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   // Prefetch (registers), DEPTH tiles ahead: the thread's two pointer-word
-  // pairs and its share of the tile's key / value record bytes (16-byte
-  // chunks).  The tile loop is unrolled by DEPTH so ring slots stay static.
-  uint2 pwa[DEPTH], pwb[DEPTH];
+  // pairs (one 16-byte load) and its share of the tile's key / value record
+  // bytes (16-byte chunks).  The tile loop is unrolled by DEPTH so ring slots
+  // stay static; each slot is emptied into LDS before it is reloaded.
+  uint4 pw[DEPTH];
   uint4 pk[DEPTH][kPre], pv_[DEPTH][kPre];
-  auto prefetch = [&](int i, uint2& wa_, uint2& wb_, uint4* k_, uint4* v_) {
-    const int tt = t_beg + i * kTile + wave * 128 + 2 * lane;
-    wa_ = tt < t_end ? *reinterpret_cast<const uint2*>(words + (int64_t)tt * 2) : make_uint2(0, 0);
-    wb_ = tt + 1 < t_end ? *reinterpret_cast<const uint2*>(words + (int64_t)tt * 2 + 2) : make_uint2(0, 0);
-    const int nk = 3 * min(kRecCap, offs[0][i + 1] - offs[0][i]);
-    const int nv = 3 * min(kRecCap, offs[1][i + 1] - offs[1][i]);
-    const uint4* gk = reinterpret_cast<const uint4*>(recK + (int64_t)offs[0][i] * kRecBytes);
-    const uint4* gv = reinterpret_cast<const uint4*>(recV + (int64_t)offs[1][i] * kRecBytes);
+  // All loads go through range-checked buffer resources: a lane past the
+  // range (or a tile past the last) reads zeros and no memory.  For an odd
+  // last token the range is rounded up to 16 bytes: the 8 bytes after this
+  // head's words (the next head's or the chunk table) lie inside the unit and
+  // the token-validity flags below ignore them.
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(words + (int64_t)t_beg * 2, (uint32_t)(((t_end - t_beg) * 8 + 15) & ~15));
+  auto prefetch = [&](int i, uint4& w_, uint4* k_, uint4* v_) {
+    w_ = buf_load16(wrs, (uint32_t)(i * kTile + wave * 128 + 2 * lane) * 8u);
+    const int ic = max(0, min(i, nch - 1));
+    const int ok0 = __builtin_amdgcn_readfirstlane(offs[0][ic]), ok1 = __builtin_amdgcn_readfirstlane(offs[0][ic + 1]);
+    const int ov0 = __builtin_amdgcn_readfirstlane(offs[1][ic]), ov1 = __builtin_amdgcn_readfirstlane(offs[1][ic + 1]);
+    const int nk = i < nch ? 3 * min(kRecCap, ok1 - ok0) : 0;
+    const int nv = i < nch ? 3 * min(kRecCap, ov1 - ov0) : 0;
+    const __amdgpu_buffer_rsrc_t krs = buf_rsrc(recK + (int64_t)ok0 * kRecBytes, (uint32_t)nk * 16u);
+    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(recV + (int64_t)ov0 * kRecBytes, (uint32_t)nv * 16u);
 #pragma unroll
     for (int k = 0; k < kPre; ++k) {
-      const int ci = threadIdx.x + 512 * k;
-      k_[k] = ci < nk ? gk[ci] : make_uint4(0, 0, 0, 0);
-      v_[k] = ci < nv ? gv[ci] : make_uint4(0, 0, 0, 0);
+      const uint32_t ci = threadIdx.x + 512 * k;
+      k_[k] = buf_load16(krs, ci * 16u);
+      v_[k] = buf_load16(vrs, ci * 16u);
     }
   };
-  __syncthreads();  // offs visible
+  // issue order = slot order (the loop's waits count the loads issued after a
+  // slot's, so the scheduler must not interleave the slots here)
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nch) prefetch(d, pwa[d], pwb[d], pk[d], pv_[d]);
+  for (int d = 0; d < DEPTH; ++d) {
+    prefetch(d, pw[d], pk[d], pv_[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   for (int base_it = 0; base_it < nch; base_it += DEPTH) {
 #pragma unroll
   for (int dslot = 0; dslot < DEPTH; ++dslot) {
+    // no early exit: a tile past the range (odd tile count) reads nothing and
+    // contributes nothing, and a branch out of the middle of the unrolled body
+    // would let the compiler's wait counting assume a path that skipped the
+    // other slot's loads
     const int it = base_it + dslot;
-    if (it >= nch) break;
+    const int par = it & 1;
     const int tile = t_beg + it * kTile;
-    const int rk0 = offs[0][it], rv0 = offs[1][it];
+    const int rk0 = offs[0][min(it, nch)], rv0 = offs[1][min(it, nch)];
     // stage this tile's records (the previous tile ended with a barrier)
 #pragma unroll
     for (int k = 0; k < kPre; ++k) { kst[threadIdx.x + 512 * k] = pk[dslot][k]; vst[threadIdx.x + 512 * k] = pv_[dslot][k]; }
-    const uint2 wa = pwa[dslot], wb = pwb[dslot];
-    if (it + DEPTH < nch) prefetch(it + DEPTH, pwa[dslot], pwb[dslot], pk[dslot], pv_[dslot]);
+    wst[threadIdx.x] = pw[dslot];
+    // compiler-only fence: the words are read back from LDS below instead of
+    // being forwarded from pw, whose registers are free now for the next
+    // prefetch
+    asm volatile("" ::: "memory");
+    prefetch(it + DEPTH, pw[dslot], pk[dslot], pv_[dslot]);
+    const uint4 w4 = wst[threadIdx.x];  // own write, no barrier needed
     // ---- A: pointer words of the lane's two tokens
     const int t0 = tile + wave * 128 + 2 * lane;
     const bool v0 = t0 < t_end, v1 = t0 + 1 < t_end;
-    const int aK0 = wa.x & 0x7FFF, aV0 = wa.y & 0x7FFF, aK1 = wb.x & 0x7FFF, aV1 = wb.y & 0x7FFF;
-    const bool fK0 = v0 && (wa.x & 0x8000u), fV0 = v0 && (wa.y & 0x8000u);
-    const bool fK1 = v1 && (wb.x & 0x8000u), fV1 = v1 && (wb.y & 0x8000u);
-    const float gK0 = h2f((uint16_t)(wa.x >> 16)), gV0 = h2f((uint16_t)(wa.y >> 16));
-    const float gK1 = h2f((uint16_t)(wb.x >> 16)), gV1 = h2f((uint16_t)(wb.y >> 16));
+    const int aK0 = w4.x & 0x7FFF, aV0 = w4.y & 0x7FFF, aK1 = w4.z & 0x7FFF, aV1 = w4.w & 0x7FFF;
+    // a token past the range has all-zero words (flags clear) except the odd
+    // one after the last token, masked by v1
+    const bool fK0 = w4.x & 0x8000u, fV0 = w4.y & 0x8000u;
+    const bool fK1 = v1 && (w4.z & 0x8000u), fV1 = v1 && (w4.w & 0x8000u);
+    const float gK0 = h2f((uint16_t)(w4.x >> 16)), gV0 = h2f((uint16_t)(w4.y >> 16));
+    const float gK1 = h2f((uint16_t)(w4.z >> 16)), gV1 = h2f((uint16_t)(w4.w >> 16));
     const unsigned long long bK0 = __ballot(fK0), bK1 = __ballot(fK1), bV0 = __ballot(fV0), bV1 = __ballot(fV1);
     const int nK = __popcll(bK0) + __popcll(bK1), nV = __popcll(bV0) + __popcll(bV1);
     if (lane == 0) { cnt[wave][0] = nK; cnt[wave][1] = nV; }
+    if (threadIdx.x < GP) tmaxb[par ^ 1][threadIdx.x] = kKeyNegInf;  // next tile's max (last read a tile ago)
     lds_barrier();
     int baseK = 0, baseV = 0;
     for (int w2 = 0; w2 < wave; ++w2) { baseK += cnt[w2][0]; baseV += cnt[w2][1]; }
     const int rK0 = baseK + __popcll(bK0 & below) + __popcll(bK1 & below), rK1 = rK0 + (fK0 ? 1 : 0);
     const int rV0 = baseV + __popcll(bV0 & below) + __popcll(bV1 & below), rV1 = rV0 + (fV0 ? 1 : 0);
 
-    // ---- B: key-residual logits of this wave's records, 16 per MFMA tile.
-    // Batches whose records are all staged read LDS only; the rest (tiles with
-    // more flagged tokens than the staging holds) read the cache directly in a
-    // separate loop, so that loop's waits on global loads do not stall the
-    // prefetch of the next tile in the common case.
+    // ---- B: key-residual logits of this wave's records, 16 per MFMA tile,
+    // into buf rows [baseK, baseK + nK) (only this wave reads them).  Batches
+    // whose records are all staged read LDS only; the rest (tiles with more
+    // flagged tokens than the staging holds) read the cache directly.
     auto kbatch = [&](int b0, auto from_lds) {
       constexpr bool LDS = decltype(from_lds)::value;
-      auto rec = [&](int rr) -> const uint8_t* {
-        return LDS ? reinterpret_cast<const uint8_t*>(kst) + rr * kRecBytes : recK + (int64_t)(rk0 + rr) * kRecBytes;
-      };
       const int i = b0 + col;
       uint2 x = make_uint2(0, 0);
-      if (i < nK) x = *reinterpret_cast<const uint2*>(rec(baseK + i) + 8 * kg);
+      if constexpr (LDS) x = *reinterpret_cast<const uint2*>(kstb + (baseK + i) * kRecBytes + 8 * kg);
+      else if (i < nK) x = *reinterpret_cast<const uint2*>(recK + (int64_t)(rk0 + baseK + i) * kRecBytes + 8 * kg);
+      const uint32_t xs[3][2] = {{x.x, x.y}, {x.x >> 6, x.y >> 6}, {x.x >> 12, x.y >> 12}};
       bf16x8 af[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int s0 = 4 * st, s1 = 4 * st + 2;
-        af[st] = u4_to_frag(((x.x >> s0) & 0x00030003u) | kCodeBias, ((x.y >> s0) & 0x00030003u) | kCodeBias,
-                            ((x.x >> s1) & 0x00030003u) | kCodeBias, ((x.y >> s1) & 0x00030003u) | kCodeBias);
+        const Plane p0 = plane_of(2 * st), p1 = plane_of(2 * st + 1);
+        const int i0 = p0.sh / 6, i1 = p1.sh / 6;
+        af[st] = u4_to_frag(and_or(xs[i0][0], MK[p0.m], vbias), and_or(xs[i0][1], MK[p0.m], vbias),
+                            and_or(xs[i1][0], MK[p1.m], vbias), and_or(xs[i1][1], MK[p1.m], vbias));
       }
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
-        f32x4 cacc = {0, 0, 0, 0};
+        f32x4 cacc = {cinit[cb], cinit[cb], cinit[cb], cinit[cb]};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           cacc = M::mma(af[st], qB[cb][st], cacc);
@@ -276,14 +415,12 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ii = b0 + 4 * kg + r;
-          float val = 0.0f;
-          if (ii < nK) {
-            const uint32_t sz = *reinterpret_cast<const uint32_t*>(rec(baseK + ii) + 32 + 4 * grp);
-            const float sc = h2f((uint16_t)(sz & 0xFFFFu)), z = h2f((uint16_t)(sz >> 16));
-            val = fmaf(sc, cacc[r], (z - 128.0f * sc) * qsum[cb]);
-          }
-          val = quad_sum(val);
-          if (ii < nK && grp == 0 && g < G) buf[(baseK + ii) * G + g] = val * a.c;
+          uint32_t sz = 0;
+          if constexpr (LDS) sz = *reinterpret_cast<const uint32_t*>(kstb + (baseK + ii) * kRecBytes + 32 + 4 * grp);
+          else if (ii < nK) sz = *reinterpret_cast<const uint32_t*>(recK + (int64_t)(rk0 + baseK + ii) * kRecBytes + 32 + 4 * grp);
+          const float sc = h2f((uint16_t)(sz & 0xFFFFu)), z = h2f((uint16_t)(sz >> 16));
+          const float val = quad_sum(fmaf(sc, cacc[r], z * qsum[cb]));
+          if (ii < nK && grp == 0 && g < G) buf[(baseK + ii) * GP + g] = val * a.c;
         }
       }
     };
@@ -296,39 +433,49 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
         else for (; b0 < nK; b0 += 16) kbatch(b0, std::false_type{});
       }
     }
-    lds_barrier();
+    __builtin_amdgcn_wave_barrier();  // this wave's buf rows written before they are read (LDS is in order per wave)
 
     // ---- C: logits of the lane's two tokens; tile max per q-head
     float s0[G], s1[G];
+    {
+      float S0[GP], S1[GP], R0[GP], R1[GP];
+      ldsv<GP>(S + aK0 * GP, S0);
+      ldsv<GP>(S + aK1 * GP, S1);
+      ldsv<GP>(fK0 ? buf + rK0 * GP : zrow, R0);
+      ldsv<GP>(fK1 ? buf + rK1 * GP : zrow, R1);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      s0[g] = v0 ? gK0 * S[g * A + aK0] + (fK0 ? buf[rK0 * G + g] : 0.0f) : -INFINITY;
-      s1[g] = v1 ? gK1 * S[g * A + aK1] + (fK1 ? buf[rK1 * G + g] : 0.0f) : -INFINITY;
-      const float mx = wave_max(fmaxf(s0[g], s1[g]));
-      if (lane == 0) tmax[wave][g] = mx;
+      for (int g = 0; g < G; ++g) {
+        s0[g] = v0 ? fmaf(gK0, S0[g], R0[g]) : -INFINITY;
+        s1[g] = v1 ? fmaf(gK1, S1[g], R1[g]) : -INFINITY;
+        const float mx = row_max(fmaxf(s0[g], s1[g]));
+        if (col == 0) atomicMax(&tmaxb[par][g], fkey(mx));
+      }
     }
     lds_barrier();
     // ---- D: lazy rescale (every thread takes the same decision)
     bool any = false;
     float fct[G];
+    {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float tm = tmax[0][g];
-      for (int w2 = 1; w2 < kWaves; ++w2) tm = fmaxf(tm, tmax[w2][g]);
-      fct[g] = 1.0f;
-      if (tm > m_run[g] + 8.0f) {
-        fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
-        m_run[g] = tm;
-        any = true;
+      for (int g = 0; g < G; ++g) {
+        const float tm = fkey_inv(tmaxb[par][g]);
+        fct[g] = 1.0f;
+        if (tm > m_run[g] + 8.0f) {
+          fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
+          m_run[g] = tm;
+          any = true;
+        }
       }
     }
     if (any) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        lacc[g] *= fct[g];
-        if (fct[g] != 1.0f)
-          for (int i = threadIdx.x; i < A; i += blockDim.x)
-            wi[g * A + i] = (unsigned long long)__double2ll_rn((double)(long long)wi[g * A + i] * (double)fct[g]);
+      for (int g = 0; g < G; ++g) lacc[g] *= fct[g];
+      for (int i = threadIdx.x; i < A * GP; i += blockDim.x) {
+        const int g = i % GP;
+        float f = 1.0f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
+        if (f != 1.0f) wi[i] = (unsigned long long)__double2ll_rn((double)(long long)wi[i] * (double)f);
       }
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
@@ -337,9 +484,11 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc)
+        for (int r = 0; r < 4; ++r) {
+          zacc[rb][r] *= f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) vacc[rb][cc][r] *= f;
+          for (int cc = 0; cc < 8; ++cc) vacc[rb][cc][r] *= f;
+        }
         const int gz = (16 * rb + col) >> 2;  // z row (rb, col)
         float fz = 1.0f;
 #pragma unroll
@@ -348,81 +497,105 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
       }
       lds_barrier();
     }
-    // ---- E: probabilities, scatter p*gamma into w, keep p of value-flagged tokens
+    // ---- E: probabilities, scatter p*gamma into w, keep p of value-flagged
+    // tokens in buf rows [baseV, baseV + nV) (only this wave reads them; every
+    // wave is past C, so the key logits there are dead).  A token past the
+    // range has p = 0 and adds 0 to w[0].
     // p <= 2^8 (lazy rescale), so gamma in [0, 8) keeps p*gamma*2^21 in [0, 2^32).
-    const float gs0 = gV0 * kFxScale, gs1 = gV1 * kFxScale;
-    const bool fast = __all((!v0 || (gV0 >= 0.0f && gV0 < 8.0f)) && (!v1 || (gV1 >= 0.0f && gV1 < 8.0f)));
+    {
+      const float gs0 = gV0 * kFxScale, gs1 = gV1 * kFxScale;
+      const bool fast = __all((!v0 || (gV0 >= 0.0f && gV0 < 8.0f)) && (!v1 || (gV1 >= 0.0f && gV1 < 8.0f)));
+      float pk0[GP], pk1[GP];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float p0 = v0 ? exp2_fast(s0[g] - m_run[g]) : 0.0f;
-      const float p1 = v1 ? exp2_fast(s1[g] - m_run[g]) : 0.0f;
-      lacc[g] += p0 + p1;
-      unsigned long long x0, x1;
-      if (fast) {
-        x0 = (unsigned long long)(unsigned)rintf(p0 * gs0);
-        x1 = (unsigned long long)(unsigned)rintf(p1 * gs1);
-      } else {
-        x0 = fx_general(p0 * gs0);
-        x1 = fx_general(p1 * gs1);
+      for (int g = 0; g < GP; ++g) { pk0[g] = 0.0f; pk1[g] = 0.0f; }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p0 = exp2_fast(s0[g] - m_run[g]);
+        const float p1 = exp2_fast(s1[g] - m_run[g]);
+        lacc[g] += p0 + p1;
+        unsigned long long x0, x1;
+        if (fast) {
+          x0 = (unsigned long long)(unsigned)fmaf(p0, gs0, 0.5f);
+          x1 = (unsigned long long)(unsigned)fmaf(p1, gs1, 0.5f);
+        } else {
+          x0 = fx_general(p0 * gs0);
+          x1 = fx_general(p1 * gs1);
+        }
+        atomicAdd(&wi[aV0 * GP + g], x0);
+        atomicAdd(&wi[aV1 * GP + g], x1);
+        pk0[g] = p0;
+        pk1[g] = p1;
       }
-      if (v0) atomicAdd(&wi[g * A + aV0], x0);
-      if (v1) atomicAdd(&wi[g * A + aV1], x1);
-      if (fV0) buf[rV0 * G + g] = p0;
-      if (fV1) buf[rV1 * G + g] = p1;
+      if (fV0) stsv<GP>(buf + rV0 * GP, pk0);
+      if (fV1) stsv<GP>(buf + rV1 * GP, pk1);
     }
-    lds_barrier();
+    __builtin_amdgcn_wave_barrier();
 
     // ---- F: value residuals of this wave's records, 32 per MFMA K-step
     // (staged records from LDS; overflow records from the cache in a separate loop)
     auto vbatch = [&](int b0, auto from_lds) {
       constexpr bool LDS = decltype(from_lds)::value;
-      auto rec = [&](int tr) -> const uint8_t* {
-        return LDS ? reinterpret_cast<const uint8_t*>(vst) + tr * kRecBytes : recV + (int64_t)(rv0 + tr) * kRecBytes;
-      };
       uint32_t pr[4];  // code words of coordinate column `col`, record pairs
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int r0 = b0 + 8 * kg + 2 * e2;
         uint32_t w0 = 0, w1 = 0;
-        if (r0 < nV) w0 = *reinterpret_cast<const uint16_t*>(rec(baseV + r0) + 2 * col);
-        if (r0 + 1 < nV) w1 = *reinterpret_cast<const uint16_t*>(rec(baseV + r0 + 1) + 2 * col);
+        if constexpr (LDS) {
+          w0 = *reinterpret_cast<const uint16_t*>(vstb + (baseV + r0) * kRecBytes + 2 * col);
+          w1 = *reinterpret_cast<const uint16_t*>(vstb + (baseV + r0 + 1) * kRecBytes + 2 * col);
+        } else {
+          if (r0 < nV) w0 = *reinterpret_cast<const uint16_t*>(recV + (int64_t)(rv0 + baseV + r0) * kRecBytes + 2 * col);
+          if (r0 + 1 < nV) w1 = *reinterpret_cast<const uint16_t*>(recV + (int64_t)(rv0 + baseV + r0 + 1) * kRecBytes + 2 * col);
+        }
         pr[e2] = w0 | (w1 << 16);
       }
+      // A operands: row (4g + grp) = 16rb + col, records b0 + 8kg + e; rows of
+      // padded q-heads and records past nV get p = 0
+      bf16x8 ahi[NB], alo[NB];
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
-        // A operand: row (4g + grp) = 16rb + col, records b0 + 8kg + e
         const int g = (16 * rb + col) >> 2, grp = col & 3;
-        uint32_t hp[4], lp[4];
+        const int lim = g < G ? nV - b0 - 8 * kg : 0;
+        float ps[8];
         float zsum = zt[rb];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int rr = b0 + 8 * kg + e;
-          float pv = 0.0f, sc = 0.0f, z = 0.0f;
-          if (rr < nV && g < G) {
-            pv = buf[(baseV + rr) * G + g];
-            const uint32_t sz = *reinterpret_cast<const uint32_t*>(rec(baseV + rr) + 32 + 4 * grp);
-            sc = h2f((uint16_t)(sz & 0xFFFFu));
-            z = h2f((uint16_t)(sz >> 16));
-          }
-          const float ps = pv * sc;
-          const uint16_t hb = f2bf(ps);
-          const float hf = bf2f(hb);
-          const uint16_t lb = f2bf(ps - hf);
-          zsum = fmaf(pv, z, zsum);
-          zsum = fmaf(-128.0f, hf + bf2f(lb), zsum);
-          if (e & 1) { hp[e >> 1] |= (uint32_t)hb << 16; lp[e >> 1] |= (uint32_t)lb << 16; }
-          else { hp[e >> 1] = hb; lp[e >> 1] = lb; }
+          float pv = buf[(baseV + rr) * GP + (g < G ? g : 0)];
+          pv = e < lim ? pv : 0.0f;
+          uint32_t sz = 0;
+          if constexpr (LDS) sz = *reinterpret_cast<const uint32_t*>(vstb + (baseV + rr) * kRecBytes + 32 + 4 * grp);
+          else if (e < lim) sz = *reinterpret_cast<const uint32_t*>(recV + (int64_t)(rv0 + baseV + rr) * kRecBytes + 32 + 4 * grp);
+          ps[e] = pv * h2f((uint16_t)(sz & 0xFFFFu));
+          zsum = fmaf(pv, h2f((uint16_t)(sz >> 16)), zsum);
         }
         zt[rb] = zsum;
-        const bf16x8 ahi = u4_to_frag(hp[0], hp[1], hp[2], hp[3]);
-        const bf16x8 alo = u4_to_frag(lp[0], lp[1], lp[2], lp[3]);
+        uint32_t hp[4], lp[4];
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const int sh = 2 * cc;
-          const bf16x8 bfr = u4_to_frag(((pr[0] >> sh) & 0x00030003u) | kCodeBias, ((pr[1] >> sh) & 0x00030003u) | kCodeBias,
-                                        ((pr[2] >> sh) & 0x00030003u) | kCodeBias, ((pr[3] >> sh) & 0x00030003u) | kCodeBias);
-          vacc[rb][cc] = M::mma(ahi, bfr, vacc[rb][cc]);
-          vacc[rb][cc] = M::mma(alo, bfr, vacc[rb][cc]);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t hb = bf16_pack(ps[2 * k], ps[2 * k + 1]);
+          const float d0 = ps[2 * k] - __uint_as_float(hb << 16);
+          const float d1 = ps[2 * k + 1] - __uint_as_float(hb & 0xFFFF0000u);
+          hp[k] = hb;
+          lp[k] = bf16_pack(d0, d1);
+        }
+        ahi[rb] = u4_to_frag(hp[0], hp[1], hp[2], hp[3]);
+        alo[rb] = u4_to_frag(lp[0], lp[1], lp[2], lp[3]);
+        zacc[rb] = M::mma(ahi[rb], bm128, zacc[rb]);
+        zacc[rb] = M::mma(alo[rb], bm128, zacc[rb]);
+      }
+      const uint32_t ps6[4] = {pr[0] >> 6, pr[1] >> 6, pr[2] >> 6, pr[3] >> 6};
+      const uint32_t ps12[4] = {pr[0] >> 12, pr[1] >> 12, pr[2] >> 12, pr[3] >> 12};
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const Plane pl = plane_of(cc);
+        const uint32_t* src = pl.sh == 0 ? pr : pl.sh == 6 ? ps6 : ps12;
+        const bf16x8 bfr = u4_to_frag(and_or(src[0], MK[pl.m], vbias), and_or(src[1], MK[pl.m], vbias),
+                                      and_or(src[2], MK[pl.m], vbias), and_or(src[3], MK[pl.m], vbias));
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+          vacc[rb][cc] = M::mma(ahi[rb], bfr, vacc[rb][cc]);
+          vacc[rb][cc] = M::mma(alo[rb], bfr, vacc[rb][cc]);
         }
       }
     };
@@ -440,10 +613,11 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   }
 
   // ---- epilogue: reduce over lanes and waves, write this range's partial state
+  __shared__ float lsum[kWaves][G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const float l = wave_sum(lacc[g]);
-    if (lane == 0) tmax[wave][g] = l;
+    if (lane == 0) lsum[wave][g] = l;
   }
   float* accs = buf;  // [G][D]
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) accs[i] = 0.0f;
@@ -460,20 +634,26 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
     const int gq = 4 * rb + kg;
     if (gq < G)
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) atomicAdd(&accs[gq * D + col + 16 * cc], vacc[rb][cc][cc >> 1]);
+      for (int cc = 0; cc < 8; ++cc) {
+        const int r = cc >> 1;
+        atomicAdd(&accs[gq * D + col + 16 * cc], (vacc[rb][cc][r] + zacc[rb][r]) * kPlaneInv[plane_of(cc).m]);
+      }
   }
   __syncthreads();
   const int64_t ps = uh * a.S2 + sp;
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
     float l = 0.0f;
-    for (int w2 = 0; w2 < kWaves; ++w2) l += tmax[w2][g];
+    for (int w2 = 0; w2 < kWaves; ++w2) l += lsum[w2][g];
     float m = -INFINITY;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) m = (gg == g) ? m_run[gg] : m;
     a.part_ml[ps * G + g] = make_float2(m, l);
   }
-  for (int i = threadIdx.x; i < G * A; i += blockDim.x) a.part_w[ps * G * A + i] = (float)((double)(long long)wi[i] * kFxInv);
+  for (int i = threadIdx.x; i < G * A; i += blockDim.x) {
+    const int g = i / A, aa = i % A;
+    a.part_w[ps * G * A + i] = (float)((double)(long long)wi[aa * GP + g] * kFxInv);
+  }
   for (int i = threadIdx.x; i < G * D; i += blockDim.x)
     a.part_acc[ps * G * D + i] = accs[i] + zt_s[(i / D) * 4 + (i % D) / 32];
 }
@@ -526,8 +706,9 @@ __global__ __launch_bounds__(256) void k_dec_combine(const uint8_t* cache, int64
 // Raise a kernel's dynamic-LDS limit to `bytes` (once per larger value).
 
 static size_t stream_lds(int G, int A, int KP) {
-  return sizeof(float) * (((size_t)G * A + 1) & ~(size_t)1) + 8 * (size_t)G * A + sizeof(float) * (size_t)kTile * G +
-         2 * 512 * (size_t)KP * sizeof(uint4);
+  const size_t GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  return sizeof(float) * ((3 * GP * A + 3) & ~(size_t)3) + sizeof(float) * (size_t)std::max<size_t>(kTile * GP, 2048) +
+         2 * 512 * (size_t)KP * sizeof(uint4) + (size_t)kRecPad * kRecBytes;
 }
 constexpr size_t kLdsLimit = 156 * 1024;
 

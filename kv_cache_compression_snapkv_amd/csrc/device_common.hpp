@@ -179,4 +179,15 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Raw buffer resource over [p, p + bytes) (p uniform): a load at an offset
+// outside the range returns zero without a memory access, so a masked load
+// needs no branch (and the waitcnt pass sees a fixed number of loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 }  // namespace akv
