@@ -100,14 +100,12 @@ __device__ __forceinline__ bf16x8 u4_to_frag(uint32_t a, uint32_t b, uint32_t c,
   return bits_to_frag(make_uint4(a, b, c, d));
 }
 
-// (a & m) | b as one v_and_or_b32 with m uniform (an SGPR) and b in a VGPR:
-// the three-operand encoding takes no literal here, so with both constants
-// written as literals the compiler would split it into two instructions.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(b));
-  return d;
-}
+// (a & m) | b: with m an opaque SGPR value and b an opaque VGPR value (see
+// the kernel prologue) the compiler selects one v_and_or_b32; with both as
+// literals it would split it (the three-operand encoding takes no literal
+// here).  Plain C on purpose: an instruction hidden in inline asm is invisible
+// to the compiler's hazard checks, which must order it against MFMA writes.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) { return (a & m) | b; }
 
 typedef __attribute__((ext_vector_type(2))) float f32x2v;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
@@ -172,8 +170,8 @@ template <int GP> __device__ __forceinline__ void stsv(float* p, const float (&o
 template <int G> constexpr int kGPad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
 constexpr int kRecPad = 32;  // zeroed records after the value staging (batch tails read them)
 
-template <int DT, int G, int KP, int DEPTH>
-__global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
+template <int DT, int G, int KP, int DEPTH, int WPE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void k_dec_stream(DecArgs a) {
   constexpr int kPre = KP;
   constexpr int kRecCap = 512 * KP * 16 / kRecBytes;
   using T = typename Elem<DT>::T;
@@ -195,7 +193,7 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   uint4* vst = kst + 512 * kPre;                                 // staged value records, then kRecPad zero records
   const uint8_t* kstb = reinterpret_cast<const uint8_t*>(kst);
   const uint8_t* vstb = reinterpret_cast<const uint8_t*>(vst);
-  __shared__ int cnt[kWaves][2];
+  __shared__ int cnt[kWaves];  // per wave: key-flagged | value-flagged << 16
   __shared__ int offs[2][130];
   __shared__ __align__(16) int tmaxb[2][GP];
   __shared__ __align__(16) float zrow[GP];
@@ -237,7 +235,8 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   }
 
   // code-plane constants: masks (SGPRs) and the exponent bias (one VGPR)
-  const uint32_t MK[3] = {0x00030003u, 0x000C000Cu, 0x00300030u};
+  uint32_t MK[3] = {0x00030003u, 0x000C000Cu, 0x00300030u};
+  asm volatile("" : "+s"(MK[0]), "+s"(MK[1]), "+s"(MK[2]));
   uint32_t vbias = kCodeBias;
   asm volatile("" : "+v"(vbias));
 
@@ -246,7 +245,10 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   // d = j + 16c, j = 4kg + (e&3), c = 2st + (e>>2), when grp == st, zeros
   // otherwise.  cinit = -128 * (sum of what the column is fed), so the
   // accumulator ends at sum_d q[g][d] * code_d.
-  bf16x8 qB[NB][4], qBl[QSPLIT ? NB : 1][4];
+  // the fragments are the same in every wave: kept in LDS (after the value
+  // staging and its zero records), written by wave 0
+  constexpr int QH = QSPLIT ? 2 : 1;
+  uint4 (*qbs)[64] = reinterpret_cast<uint4 (*)[64]>(vst + 512 * kPre + kRecPad * kRecBytes / 16);
   float qsum[NB], cinit[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
@@ -278,11 +280,13 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
         vh[e] = f2bf(bf2f(vh[e]) * sc);  // exact: power-of-two scaling
         vl[e] = f2bf(bf2f(vl[e]) * sc);
       }
-      qB[cb][st] = u4_to_frag(vh[0] | (uint32_t)vh[1] << 16, vh[2] | (uint32_t)vh[3] << 16, vh[4] | (uint32_t)vh[5] << 16,
-                              vh[6] | (uint32_t)vh[7] << 16);
-      if constexpr (QSPLIT)
-        qBl[cb][st] = u4_to_frag(vl[0] | (uint32_t)vl[1] << 16, vl[2] | (uint32_t)vl[3] << 16,
-                                 vl[4] | (uint32_t)vl[5] << 16, vl[6] | (uint32_t)vl[7] << 16);
+      if (wave == 0) {
+        qbs[(cb * 4 + st) * QH][lane] = make_uint4(vh[0] | (uint32_t)vh[1] << 16, vh[2] | (uint32_t)vh[3] << 16,
+                                                   vh[4] | (uint32_t)vh[5] << 16, vh[6] | (uint32_t)vh[7] << 16);
+        if constexpr (QSPLIT)
+          qbs[(cb * 4 + st) * QH + 1][lane] = make_uint4(vl[0] | (uint32_t)vl[1] << 16, vl[2] | (uint32_t)vl[3] << 16,
+                                                         vl[4] | (uint32_t)vl[5] << 16, vl[6] | (uint32_t)vl[7] << 16);
+      }
     }
   }
   // value side: B = -128 everywhere cancels the code bias of the A rows
@@ -292,13 +296,17 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
   float m_run[G], lacc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; lacc[g] = 0.0f; }
-  f32x4 vacc[NB][8];   // value side: row block rb (rows 4g + grp), column block cc (coordinates j + 16cc), x 4^m
+  // value side, row block rb (rows 4g + grp), column block cc (coordinates
+  // j + 16cc): of each MFMA tile only the rows of group cc/2 are wanted, so a
+  // batch's tile starts from zero and its row r = cc/2 is added to vacc
+  // (scaled by 4^m of the plane)
+  float vacc[NB][8];
   f32x4 zacc[NB];      // value side: -128 * sum of the A rows (the code bias)
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
     zacc[rb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] = f32x4{0, 0, 0, 0};
+    for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] = 0.0f;
   }
   float zt[NB];        // value side: sum of p * zero for row (rb, col)
 #pragma unroll
@@ -376,11 +384,12 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
     const float gK1 = h2f((uint16_t)(w4.z >> 16)), gV1 = h2f((uint16_t)(w4.w >> 16));
     const unsigned long long bK0 = __ballot(fK0), bK1 = __ballot(fK1), bV0 = __ballot(fV0), bV1 = __ballot(fV1);
     const int nK = __popcll(bK0) + __popcll(bK1), nV = __popcll(bV0) + __popcll(bV1);
-    if (lane == 0) { cnt[wave][0] = nK; cnt[wave][1] = nV; }
+    if (lane == 0) cnt[wave] = nK | (nV << 16);
     if (threadIdx.x < GP) tmaxb[par ^ 1][threadIdx.x] = kKeyNegInf;  // next tile's max (last read a tile ago)
     lds_barrier();
-    int baseK = 0, baseV = 0;
-    for (int w2 = 0; w2 < wave; ++w2) { baseK += cnt[w2][0]; baseV += cnt[w2][1]; }
+    // counts of the earlier waves: lanes 0..wave-1 hold them, summed over the row
+    const int pre = __builtin_amdgcn_readfirstlane(row_sum_i32(lane < wave ? cnt[lane & (kWaves - 1)] : 0));
+    const int baseK = pre & 0xFFFF, baseV = pre >> 16;
     const int rK0 = baseK + __popcll(bK0 & below) + __popcll(bK1 & below), rK1 = rK0 + (fK0 ? 1 : 0);
     const int rV0 = baseV + __popcll(bV0 & below) + __popcll(bV1 & below), rV1 = rV0 + (fV0 ? 1 : 0);
 
@@ -408,8 +417,8 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
         f32x4 cacc = {cinit[cb], cinit[cb], cinit[cb], cinit[cb]};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          cacc = M::mma(af[st], qB[cb][st], cacc);
-          if constexpr (QSPLIT) cacc = M::mma(af[st], qBl[cb][st], cacc);
+          cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH][lane]), cacc);
+          if constexpr (QSPLIT) cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH + 1][lane]), cacc);
         }
         const int kap = 16 * cb + col, g = kap >> 2, grp = kap & 3;
 #pragma unroll
@@ -443,12 +452,22 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
       ldsv<GP>(S + aK1 * GP, S1);
       ldsv<GP>(fK0 ? buf + rK0 * GP : zrow, R0);
       ldsv<GP>(fK1 ? buf + rK1 * GP : zrow, R1);
+      bool hot = false;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         s0[g] = v0 ? fmaf(gK0, S0[g], R0[g]) : -INFINITY;
         s1[g] = v1 ? fmaf(gK1, S1[g], R1[g]) : -INFINITY;
-        const float mx = row_max(fmaxf(s0[g], s1[g]));
-        if (col == 0) atomicMax(&tmaxb[par][g], fkey(mx));
+        hot |= fmaxf(s0[g], s1[g]) > m_run[g] + 8.0f;
+      }
+      // Only a logit above m_run + 8 changes anything (the rescale below);
+      // a wave holding one publishes its exact maximum, the others nothing
+      // (their maxima are smaller than any such logit).
+      if (__any(hot)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int mk = wave_max_i32(fkey(fmaxf(s0[g], s1[g])));
+          if (lane == 0) atomicMax(&tmaxb[par][g], mk);
+        }
       }
     }
     lds_barrier();
@@ -484,11 +503,9 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          zacc[rb][r] *= f;
+        for (int r = 0; r < 4; ++r) zacc[rb][r] *= f;
 #pragma unroll
-          for (int cc = 0; cc < 8; ++cc) vacc[rb][cc][r] *= f;
-        }
+        for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] *= f;
         const int gz = (16 * rb + col) >> 2;  // z row (rb, col)
         float fz = 1.0f;
 #pragma unroll
@@ -510,21 +527,24 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
       for (int g = 0; g < GP; ++g) { pk0[g] = 0.0f; pk1[g] = 0.0f; }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float p0 = exp2_fast(s0[g] - m_run[g]);
-        const float p1 = exp2_fast(s1[g] - m_run[g]);
-        lacc[g] += p0 + p1;
-        unsigned long long x0, x1;
-        if (fast) {
-          x0 = (unsigned long long)(unsigned)fmaf(p0, gs0, 0.5f);
-          x1 = (unsigned long long)(unsigned)fmaf(p1, gs1, 0.5f);
-        } else {
-          x0 = fx_general(p0 * gs0);
-          x1 = fx_general(p1 * gs1);
+        pk0[g] = exp2_fast(s0[g] - m_run[g]);
+        pk1[g] = exp2_fast(s1[g] - m_run[g]);
+        lacc[g] += pk0[g] + pk1[g];
+      }
+      unsigned long long* w0 = wi + aV0 * GP;
+      unsigned long long* w1 = wi + aV1 * GP;
+      if (fast) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          atomicAdd(w0 + g, (unsigned long long)(unsigned)fmaf(pk0[g], gs0, 0.5f));
+          atomicAdd(w1 + g, (unsigned long long)(unsigned)fmaf(pk1[g], gs1, 0.5f));
         }
-        atomicAdd(&wi[aV0 * GP + g], x0);
-        atomicAdd(&wi[aV1 * GP + g], x1);
-        pk0[g] = p0;
-        pk1[g] = p1;
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          atomicAdd(w0 + g, fx_general(pk0[g] * gs0));
+          atomicAdd(w1 + g, fx_general(pk1[g] * gs1));
+        }
       }
       if (fV0) stsv<GP>(buf + rV0 * GP, pk0);
       if (fV1) stsv<GP>(buf + rV1 * GP, pk1);
@@ -594,8 +614,9 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
                                       and_or(src[2], MK[pl.m], vbias), and_or(src[3], MK[pl.m], vbias));
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
-          vacc[rb][cc] = M::mma(ahi[rb], bfr, vacc[rb][cc]);
-          vacc[rb][cc] = M::mma(alo[rb], bfr, vacc[rb][cc]);
+          f32x4 t = M::mma(ahi[rb], bfr, f32x4{0, 0, 0, 0});
+          t = M::mma(alo[rb], bfr, t);
+          vacc[rb][cc] += t[cc >> 1];
         }
       }
     };
@@ -636,7 +657,7 @@ __global__ __launch_bounds__(512) void k_dec_stream(DecArgs a) {
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
         const int r = cc >> 1;
-        atomicAdd(&accs[gq * D + col + 16 * cc], (vacc[rb][cc][r] + zacc[rb][r]) * kPlaneInv[plane_of(cc).m]);
+        atomicAdd(&accs[gq * D + col + 16 * cc], (vacc[rb][cc] + zacc[rb][r]) * kPlaneInv[plane_of(cc).m]);
       }
   }
   __syncthreads();
@@ -705,20 +726,21 @@ __global__ __launch_bounds__(256) void k_dec_combine(const uint8_t* cache, int64
 
 // Raise a kernel's dynamic-LDS limit to `bytes` (once per larger value).
 
-static size_t stream_lds(int G, int A, int KP) {
+static size_t stream_lds(int G, int A, int KP, bool qsplit) {
   const size_t GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  const size_t NB = (4 * (size_t)G + 15) / 16;
   return sizeof(float) * ((3 * GP * A + 3) & ~(size_t)3) + sizeof(float) * (size_t)std::max<size_t>(kTile * GP, 2048) +
-         2 * 512 * (size_t)KP * sizeof(uint4) + (size_t)kRecPad * kRecBytes;
+         2 * 512 * (size_t)KP * sizeof(uint4) + (size_t)kRecPad * kRecBytes + NB * 4 * (qsplit ? 2 : 1) * 64 * sizeof(uint4);
 }
-constexpr size_t kLdsLimit = 156 * 1024;
+constexpr size_t kLdsLimit = 158 * 1024;  // dynamic part; the static part is under 2 KB of the 160 KB
 
-template <int DT, int G, int KP, int DEPTH>
+template <int DT, int G, int KP, int DEPTH, int WPE>
 static int launch_stream_kp(const DecArgs& a, unsigned grid, hipStream_t st) {
   static size_t done = 0;
-  const size_t lds = stream_lds(G, a.A, KP);
+  const size_t lds = stream_lds(G, a.A, KP, DT == ANCHORKV_F32);
   if (lds > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
-  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G, KP, DEPTH>), lds, &done)) return rc;
-  k_dec_stream<DT, G, KP, DEPTH><<<grid, 64 * kWaves, lds, st>>>(a);
+  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G, KP, DEPTH, WPE>), lds, &done)) return rc;
+  k_dec_stream<DT, G, KP, DEPTH, WPE><<<grid, 64 * kWaves, lds, st>>>(a);
   AKV_CHECK_LAUNCH("k_dec_stream");
   return 0;
 }
@@ -727,8 +749,8 @@ static int launch_stream_kp(const DecArgs& a, unsigned grid, hipStream_t st) {
 // tiles of prefetch in flight; more q-heads: 1 staged chunk (170 records).
 template <int DT, int G>
 static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
-  if constexpr (G <= 4) return launch_stream_kp<DT, G, 3, 2>(a, grid, st);
-  else return launch_stream_kp<DT, G, 1, 2>(a, grid, st);
+  if constexpr (G <= 4) return launch_stream_kp<DT, G, 2, 1, 4>(a, grid, st);
+  else return launch_stream_kp<DT, G, 1, 2, 2>(a, grid, st);
 }
 
 template <int DT>
@@ -740,7 +762,7 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   const int U = p.units, H = p.H, G = p.G, A = p.A, S2 = w.S2;
   if (G > kMaxG) return fail(ANCHORKV_E_SHAPE, "decode supports q_per_kv <= %d", kMaxG);
   if (S2 > 64) return fail(ANCHORKV_E_SHAPE, "decode: too many splits");
-  if (stream_lds(G, A, 1) > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
+  if (stream_lds(G, A, 1, DT == ANCHORKV_F32) > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
   if (p.n_chunks > 128 * S2) return fail(ANCHORKV_E_SHAPE, "decode: too many chunks per range");
   const size_t lds_c = sizeof(float) * (size_t)G * A;
   const float c = kLog2e / sqrtf((float)kHeadDim);

@@ -224,8 +224,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
   // sign-corrected keys; the test is on the token's row maximum, since a
   // lane's own column sees only A/16 anchors and is often all negative.
   // the mask lives in a VGPR so that (bits & mask) | tag is one v_and_or_b32
-  unsigned keymask;
-  __asm__("v_mov_b32 %0, 0xffffffe0" : "=v"(keymask));
+  // (an empty asm makes the value opaque; the move itself is the compiler's,
+  // so its hazard checks see every instruction)
+  unsigned keymask = 0xffffffe0u;
+  __asm__ volatile("" : "+v"(keymask));
   auto search = [&](const bf16x8 (&xt)[4][4], int (&best)[4][4], int nab, auto mono_tag) {
     constexpr bool mono = decltype(mono_tag)::value;
     for (int rb = 0; rb < 4; ++rb)

@@ -151,6 +151,18 @@ __device__ __forceinline__ int row_max_i32(int v) {
   v = max(v, dpp_i<kDppXor1>(v));
   return max(v, dpp_i<kDppXor2>(v));
 }
+__device__ __forceinline__ int row_sum_i32(int v) {
+  v += dpp_i<kDppRor8>(v);
+  v += dpp_i<kDppRor4>(v);
+  v += dpp_i<kDppXor1>(v);
+  return v + dpp_i<kDppXor2>(v);
+}
+// Whole-wave integer maximum (wave-uniform result).
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = row_max_i32(v);
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
 __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp<kDppRor8>(v));
   v = fmaxf(v, dpp<kDppRor4>(v));
