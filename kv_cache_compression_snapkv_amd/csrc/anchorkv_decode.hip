@@ -184,12 +184,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int A = a.A;
   unsigned long long* wi = reinterpret_cast<unsigned long long*>(sm);  // [A][GP] fixed point
   float* S = reinterpret_cast<float*>(wi + A * GP);                      // [A][GP]
-  // [kTile][GP]: key-residual logits, then p of value-flagged tokens; [G][D]
-  // at the end.  At the start of a tile it first holds the staged pointer
-  // words ([512] x 16 B).
+  // [kTile][BR]: per wave 128 private rows (its tokens' records by rank):
+  // key-residual logits, then p of value-flagged tokens (zeros in columns
+  // >= G and in the rows up to the next 32); [G][D] at the end.  At the start
+  // of a tile it first holds the staged pointer words ([512] x 16 B).
+  constexpr int BR = 4 * NB;
   float* buf = sm + ((3 * GP * A + 3) & ~3);
   uint4* wst = reinterpret_cast<uint4*>(buf);
-  uint4* kst = reinterpret_cast<uint4*>(buf + kBufFloats<GP>);  // staged key records of the tile
+  uint4* kst = reinterpret_cast<uint4*>(buf + kBufFloats<BR>);  // staged key records of the tile
   uint4* vst = kst + 512 * kPre;                                 // staged value records, then kRecPad zero records
   const uint8_t* kstb = reinterpret_cast<const uint8_t*>(kst);
   const uint8_t* vstb = reinterpret_cast<const uint8_t*>(vst);
@@ -206,6 +208,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int64_t uh = (int64_t)u * a.H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
+  float* wbuf = buf + wave * 128 * BR;  // this wave's rows
   const int c0 = sp * a.cps, c1 = min(a.C, c0 + a.cps);
   const int t_beg = c0 * kTile, t_end = min(a.N, c1 * kTile);
   const uint8_t* base = a.cache + (int64_t)u * a.stride;
@@ -390,11 +393,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     // counts of the earlier waves: lanes 0..wave-1 hold them, summed over the row
     const int pre = __builtin_amdgcn_readfirstlane(row_sum_i32(lane < wave ? cnt[lane & (kWaves - 1)] : 0));
     const int baseK = pre & 0xFFFF, baseV = pre >> 16;
-    const int rK0 = baseK + __popcll(bK0 & below) + __popcll(bK1 & below), rK1 = rK0 + (fK0 ? 1 : 0);
-    const int rV0 = baseV + __popcll(bV0 & below) + __popcll(bV1 & below), rV1 = rV0 + (fV0 ? 1 : 0);
+    // ranks of the lane's tokens among this wave's flagged ones
+    const int rK0 = __popcll(bK0 & below) + __popcll(bK1 & below), rK1 = rK0 + (fK0 ? 1 : 0);
+    const int rV0 = __popcll(bV0 & below) + __popcll(bV1 & below), rV1 = rV0 + (fV0 ? 1 : 0);
 
     // ---- B: key-residual logits of this wave's records, 16 per MFMA tile,
-    // into buf rows [baseK, baseK + nK) (only this wave reads them).  Batches
+    // into this wave's buf rows [0, nK).  Batches
     // whose records are all staged read LDS only; the rest (tiles with more
     // flagged tokens than the staging holds) read the cache directly.
     auto kbatch = [&](int b0, auto from_lds) {
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
           else if (ii < nK) sz = *reinterpret_cast<const uint32_t*>(recK + (int64_t)(rk0 + baseK + ii) * kRecBytes + 32 + 4 * grp);
           const float sc = h2f((uint16_t)(sz & 0xFFFFu)), z = h2f((uint16_t)(sz >> 16));
           const float val = quad_sum(fmaf(sc, cacc[r], z * qsum[cb]));
-          if (ii < nK && grp == 0 && g < G) buf[(baseK + ii) * GP + g] = val * a.c;
+          if (ii < nK && grp == 0 && g < G) wbuf[ii * BR + g] = val * a.c;
         }
       }
     };
@@ -450,8 +454,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       float S0[GP], S1[GP], R0[GP], R1[GP];
       ldsv<GP>(S + aK0 * GP, S0);
       ldsv<GP>(S + aK1 * GP, S1);
-      ldsv<GP>(fK0 ? buf + rK0 * GP : zrow, R0);
-      ldsv<GP>(fK1 ? buf + rK1 * GP : zrow, R1);
+      ldsv<GP>(fK0 ? wbuf + rK0 * BR : zrow, R0);
+      ldsv<GP>(fK1 ? wbuf + rK1 * BR : zrow, R1);
       bool hot = false;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -515,16 +519,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       lds_barrier();
     }
     // ---- E: probabilities, scatter p*gamma into w, keep p of value-flagged
-    // tokens in buf rows [baseV, baseV + nV) (only this wave reads them; every
-    // wave is past C, so the key logits there are dead).  A token past the
-    // range has p = 0 and adds 0 to w[0].
+    // tokens in this wave's buf rows [0, nV) and zeros in the rows after them
+    // up to the next multiple of 32 (the value batches read whole batches).
+    // A token past the range has p = 0 and adds 0 to w[0].
     // p <= 2^8 (lazy rescale), so gamma in [0, 8) keeps p*gamma*2^21 in [0, 2^32).
     {
       const float gs0 = gV0 * kFxScale, gs1 = gV1 * kFxScale;
       const bool fast = __all((!v0 || (gV0 >= 0.0f && gV0 < 8.0f)) && (!v1 || (gV1 >= 0.0f && gV1 < 8.0f)));
-      float pk0[GP], pk1[GP];
+      float pk0[BR], pk1[BR];
 #pragma unroll
-      for (int g = 0; g < GP; ++g) { pk0[g] = 0.0f; pk1[g] = 0.0f; }
+      for (int g = 0; g < BR; ++g) { pk0[g] = 0.0f; pk1[g] = 0.0f; }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         pk0[g] = exp2_fast(s0[g] - m_run[g]);
@@ -546,8 +550,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
           atomicAdd(w1 + g, fx_general(pk1[g] * gs1));
         }
       }
-      if (fV0) stsv<GP>(buf + rV0 * GP, pk0);
-      if (fV1) stsv<GP>(buf + rV1 * GP, pk1);
+      if (fV0) stsv<BR>(wbuf + rV0 * BR, pk0);
+      if (fV1) stsv<BR>(wbuf + rV1 * BR, pk1);
+      const int zr = nV + lane;
+      if (zr < ((nV + 31) & ~31)) {
+        float z0[BR];
+#pragma unroll
+        for (int g = 0; g < BR; ++g) z0[g] = 0.0f;
+        stsv<BR>(wbuf + zr * BR, z0);
+      }
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -569,24 +580,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         }
         pr[e2] = w0 | (w1 << 16);
       }
-      // A operands: row (4g + grp) = 16rb + col, records b0 + 8kg + e; rows of
-      // padded q-heads and records past nV get p = 0
+      // A operands: row (4g + grp) = 16rb + col, records b0 + 8kg + e; the
+      // buf rows give p = 0 to padded q-heads and to records past nV (the
+      // staged records there are finite: other waves' or zeros)
       bf16x8 ahi[NB], alo[NB];
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
         const int g = (16 * rb + col) >> 2, grp = col & 3;
-        const int lim = g < G ? nV - b0 - 8 * kg : 0;
         float ps[8];
         float zsum = zt[rb];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int rr = b0 + 8 * kg + e;
-          float pv = buf[(baseV + rr) * GP + (g < G ? g : 0)];
-          pv = e < lim ? pv : 0.0f;
+          const float pv = wbuf[rr * BR + g];
           uint32_t sz = 0;
           if constexpr (LDS) sz = *reinterpret_cast<const uint32_t*>(vstb + (baseV + rr) * kRecBytes + 32 + 4 * grp);
-          else if (e < lim) sz = *reinterpret_cast<const uint32_t*>(recV + (int64_t)(rv0 + baseV + rr) * kRecBytes + 32 + 4 * grp);
-          ps[e] = pv * h2f((uint16_t)(sz & 0xFFFFu));
+          else if (rr < nV) sz = *reinterpret_cast<const uint32_t*>(recV + (int64_t)(rv0 + baseV + rr) * kRecBytes + 32 + 4 * grp);
+          ps[e] = fmaf(pv, h2f((uint16_t)(sz & 0xFFFFu)), 0.0f);
           zsum = fmaf(pv, h2f((uint16_t)(sz >> 16)), zsum);
         }
         zt[rb] = zsum;
@@ -729,7 +739,7 @@ __global__ __launch_bounds__(256) void k_dec_combine(const uint8_t* cache, int64
 static size_t stream_lds(int G, int A, int KP, bool qsplit) {
   const size_t GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   const size_t NB = (4 * (size_t)G + 15) / 16;
-  return sizeof(float) * ((3 * GP * A + 3) & ~(size_t)3) + sizeof(float) * (size_t)std::max<size_t>(kTile * GP, 2048) +
+  return sizeof(float) * ((3 * GP * A + 3) & ~(size_t)3) + sizeof(float) * (size_t)std::max<size_t>(kTile * 4 * NB, 2048) +
          2 * 512 * (size_t)KP * sizeof(uint4) + (size_t)kRecPad * kRecBytes + NB * 4 * (qsplit ? 2 : 1) * 64 * sizeof(uint4);
 }
 constexpr size_t kLdsLimit = 158 * 1024;  // dynamic part; the static part is under 2 KB of the 160 KB
