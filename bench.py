@@ -54,12 +54,9 @@ def stage_work(p, stage):
         return U * H * 2 * 2.0 * N * GQ * D, 2 * xb + qb + U * H * N * 4
     if stage == "obs_util":                      # Q K^T for p, Q R_K, V O
         return U * H * 3 * 2.0 * N * GQ * D, 2 * xb + qb + U * 2 * H * N * 4
-    if stage == "dec_stream":                    # pointer words + residual records
-        return U * H * N * G * 6.0, U * (8 * H * N + 48 * (p.R_K + p.R_V))
-    if stage == "dec_stab":
-        return U * H * G * A * 2.0 * D, U * H * A * D * e
-    if stage == "dec_combine":
-        return U * H * G * A * 2.0 * D, U * H * A * D * e + U * H * G * D * 4
+    if stage == "dec_stream":                    # anchors, pointer words, residual records, q, o
+        return (U * H * N * G * 6.0 + 2 * U * H * G * A * 2.0 * D,
+                U * (8 * H * N + 48 * (p.R_K + p.R_V) + 2 * H * A * D * e) + U * H * G * D * (e + 4))
     return 0.0, 0.0
 
 
@@ -135,7 +132,7 @@ def kernel_stage(name):
         return {0: "obs_stats", 1: "obs_score", 2: "obs_util", 3: "util_fix"}[int(m.group(1))]
     for key, stage in (("k_ml_combine", "ml_combine"), ("k_o_combine", "o_combine"), ("k_select", "select"),
                        ("k_assign", "assign"), ("k_topr", "topr"), ("k_quant", "quant"), ("k_headers", "headers"),
-                       ("k_dec_stab", "dec_stab"), ("k_dec_stream", "dec_stream"), ("k_dec_combine", "dec_combine"),
+                       ("k_dec_stream", "dec_stream"), ("k_dec_merge", "dec_stream"),
                        ("k_zero_u32", "zero")):
         if key in name:
             return stage
@@ -173,7 +170,7 @@ def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
             e[key] += v * 1024.0
             e["n_" + key] += 1
     calls = max(1, per.get("headers", {}).get("n_fetch", 1))
-    dec_calls = max(1, per.get("dec_stab", {}).get("n_fetch", 1))
+    dec_calls = max(1, per.get("dec_stream", {}).get("n_fetch", 1))
     stages = {}
     for st, e in per.items():
         n = dec_calls if st.startswith("dec_") else calls
@@ -267,7 +264,7 @@ def main():
     stage_ms = {k: agg[k] / cnt[k] for k in agg}           # average per launch
     comp_stages = ["obs_stats", "ml_combine", "obs_score", "o_combine", "select", "assign", "obs_util", "util_fix",
                    "topr", "quant"]
-    dec_stages = ["dec_stab", "dec_stream", "dec_combine"]
+    dec_stages = ["dec_stream"]
     compress_ms = sum(stage_ms.get(k, 0.0) for k in comp_stages)
     decode_ms = sum(stage_ms.get(k, 0.0) for k in dec_stages)
     dom = max(comp_stages + dec_stages, key=lambda k: stage_ms.get(k, 0.0) * (1 if k in comp_stages else args.decode_steps))

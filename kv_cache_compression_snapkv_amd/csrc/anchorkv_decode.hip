@@ -5,23 +5,27 @@
 //   logit_t = gamma^K_t <q, k_a> / sqrt(D) + [t in R_K] <q, r~^K_t> / sqrt(D)
 //   o = sum_t p_t (gamma^V_t v_a(t) + [t in R_V] r~^V_t) / sum_t p_t
 // computed without reconstructing K or V (the paper's fused-decoder idea,
-// AnchorKV-adapted page "Adaptation notes"; the design here is our own):
-//  * the anchor logits <q, k_a> form a per-head table S[g][a] (LDS);
-//  * the value side scatters p_t gamma^V_t into w[g][a(t)] and finishes with
-//    o = (w V_anchors + sum p r~^V) / l in the combine kernel.  The scatter
-//    accumulates 64-bit fixed point (scale 2^21) with LDS integer atomics,
-//    which are an order of magnitude faster than LDS float atomics on this
-//    part and make the sum independent of order;
-//  * residual records are handled in batches on MFMA.  A code c enters as the
-//    exact bf16 value 128 + c (one AND+OR per pair of codes) and the constant
-//    part is cancelled exactly.  Keys: rows = records, columns = (q-head,
-//    group), so one 16x16 tile serves 4 q-heads x 4 groups.  Values: rows =
-//    (q-head, group), K = records, columns = coordinates; A = p * scale split
-//    into bf16 hi + lo.
-// One workgroup (8 waves) per (unit, head, 1024-token-aligned range); each
-// tile of 1024 tokens is one residual-offset chunk.  The running max is
-// shared by the workgroup and only raised (rescaling w, l and the
-// accumulators) when a tile exceeds it by more than 2^8.
+// AnchorKV-adapted page "Adaptation notes"; the design here is our own), in
+// one kernel:
+//  * prologue: the anchor logits S[a][g] = <q_g, k_a> log2(e)/sqrt(D) on MFMA
+//    into LDS;
+//  * tiles of 1024 tokens: S lookups, residual-key logits, softmax weights;
+//    the value side scatters p_t gamma^V_t into w[a(t)][g] (LDS, 64-bit fixed
+//    point with scale 2^21: LDS integer atomics are an order of magnitude
+//    faster than LDS float atomics on this part and make the sum independent
+//    of order) and sums p r~^V on MFMA;
+//  * epilogue: w V_anchors on MFMA plus the residual part; with several
+//    token ranges per head, the last range's workgroup merges the partial
+//    (max, sum, output) triples.
+// Residual records are handled in batches on MFMA.  A code c enters as an
+// exact bf16 value 128 + c * 4^m (one AND-OR per pair of codes) and the
+// constant part is cancelled exactly.  Keys: rows = records, columns =
+// (q-head, group), so one 16x16 tile serves 4 q-heads x 4 groups.  Values:
+// rows = (q-head, group), K = records, columns = coordinates; A = p * scale
+// split into bf16 hi + lo.
+// One workgroup (8 waves) per (unit, head, 1024-token-aligned range).  The
+// running max is shared by the workgroup and only raised (rescaling w, l and
+// the accumulators) when a tile exceeds it by more than 2^8.
 #include "device_common.hpp"
 #include "launch_common.hpp"
 
@@ -50,44 +54,14 @@ __device__ __forceinline__ unsigned long long fx_general(float y) {
   return y < 0.0f ? 0ull - v : v;
 }
 
-// ---------------------------------------------------------------- S table
-// S[g][a] = <q_g, k_a> * log2(e)/sqrt(D).  One wave per anchor row.
-template <int DT>
-__global__ __launch_bounds__(256) void k_dec_stab(const void* qv, const uint8_t* cache, int64_t stride, int64_t off_ak,
-                                                 float* stab, int H, int G, int A, float c) {
-  using T = typename Elem<DT>::T;
-  constexpr int D = kHeadDim;
-  const int h = blockIdx.x % H, u = blockIdx.x / H;
-  const int64_t uh = (int64_t)u * H + h;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const T* q = reinterpret_cast<const T*>(qv) + uh * G * D;
-  float q0[kMaxG], q1[kMaxG];
-#pragma unroll
-  for (int g = 0; g < kMaxG; ++g) {
-    q0[g] = g < G ? Elem<DT>::f(q[g * D + lane]) : 0.0f;
-    q1[g] = g < G ? Elem<DT>::f(q[g * D + 64 + lane]) : 0.0f;
-  }
-  const T* AK = reinterpret_cast<const T*>(cache + (int64_t)u * stride + off_ak) + (int64_t)h * A * D;
-  for (int a = wave; a < A; a += nw) {
-    const float k0 = Elem<DT>::f(AK[(int64_t)a * D + lane]), k1 = Elem<DT>::f(AK[(int64_t)a * D + 64 + lane]);
-#pragma unroll
-    for (int g = 0; g < kMaxG; ++g) {
-      if (g >= G) break;
-      const float s = wave_sum(fmaf(q0[g], k0, q1[g] * k1));
-      if (lane == 0) stab[(uh * G + g) * A + a] = s * c;
-    }
-  }
-}
-
 // ---------------------------------------------------------------- stream
 struct DecArgs {
   const void* q;
   const uint8_t* cache;
-  int64_t stride, off_words, off_rk, off_rv, off_ck, off_cv;
-  const float* stab;
-  float2* part_ml;
-  float* part_w;
-  float* part_acc;
+  int64_t stride, off_words, off_rk, off_rv, off_ck, off_cv, off_ak, off_av;
+  float2* part_ml;   // [U][H][S2][G] (max, sum) of each range (S2 > 1)
+  float* part_acc;   // [U][H][S2][G][D] unnormalised output of each range (S2 > 1)
+  float* o;          // [U][H][G][D]
   int H, N, A, C, S2, cps, R_K, R_V;
   float c;
 };
@@ -167,6 +141,23 @@ template <int GP> __device__ __forceinline__ void stsv(float* p, const float (&o
   }
 }
 
+// MFMA operand from KW consecutive floats in LDS (bf16: 8, exact for bf16
+// data; f32: 1); zeros when !valid
+template <int DT> __device__ __forceinline__ typename Mfma<DT>::frag frag_of(const float* p, bool valid) {
+  if constexpr (DT == ANCHORKV_BF16) {
+    if (!valid) return Mfma<DT>::zero();
+    const float4 x = reinterpret_cast<const float4*>(p)[0], y = reinterpret_cast<const float4*>(p)[1];
+    return u4_to_frag(bf16_pack(x.x, x.y), bf16_pack(x.z, x.w), bf16_pack(y.x, y.y), bf16_pack(y.z, y.w));
+  } else {
+    return valid ? *p : 0.0f;
+  }
+}
+
+// set bits of a wave mask below this lane
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
 template <int G> constexpr int kGPad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
 constexpr int kRecPad = 32;  // zeroed records after the value staging (batch tails read them)
 
@@ -206,7 +197,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int h = bid % a.H;
   const int u = bid / a.H;
   const int64_t uh = (int64_t)u * a.H + h;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave: uniform
   const int col = lane & 15, kg = lane >> 4;
   float* wbuf = buf + wave * 128 * BR;  // this wave's rows
   const int c0 = sp * a.cps, c1 = min(a.C, c0 + a.cps);
@@ -216,11 +207,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const uint8_t* recV = base + a.off_rv;
   const T* q = reinterpret_cast<const T*>(a.q) + uh * G * D;
 
-  for (int i = threadIdx.x; i < GP * A; i += blockDim.x) {
-    const int aa = i / GP, g = i % GP;
-    S[i] = g < G ? a.stab[(uh * G + g) * A + aa] : 0.0f;
-    wi[i] = 0ull;
-  }
+  // q of this head as floats in LDS ([G][D]; buf is free until the first tile)
+  float* qf = buf;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qf[i] = Elem<DT>::f(q[i]);
+  for (int i = threadIdx.x; i < GP * A; i += blockDim.x) wi[i] = 0ull;
   for (int i = threadIdx.x; i < kRecPad * kRecBytes / 16; i += blockDim.x) vst[512 * kPre + i] = make_uint4(0, 0, 0, 0);
   if (threadIdx.x < G * 4) zt_s[threadIdx.x] = 0.0f;
   if (threadIdx.x < GP) {
@@ -236,6 +226,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     offs[0][i] = last ? a.R_K : reinterpret_cast<const int*>(base + a.off_ck)[fl];
     offs[1][i] = last ? a.R_V : reinterpret_cast<const int*>(base + a.off_cv)[fl];
   }
+  __syncthreads();  // qf, offs
 
   // code-plane constants: masks (SGPRs) and the exponent bias (one VGPR)
   uint32_t MK[3] = {0x00030003u, 0x000C000Cu, 0x00300030u};
@@ -252,7 +243,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // staging and its zero records), written by wave 0
   constexpr int QH = QSPLIT ? 2 : 1;
   uint4 (*qbs)[64] = reinterpret_cast<uint4 (*)[64]>(vst + 512 * kPre + kRecPad * kRecBytes / 16);
-  float qsum[NB], cinit[NB];
+  // per lane (column): sum of q over the column's group and cinit, also in
+  // LDS (after the fragments) so that they take no registers in the tile loop
+  float2* qcs = reinterpret_cast<float2*>(qbs + NB * 4 * QH);  // [NB][64]
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const int kap = 16 * cb + col;
@@ -260,15 +253,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     float qs = 0.0f, fed = 0.0f;
     if (g < G)
       for (int d = 32 * grp; d < 32 * grp + 32; ++d) {
-        const float x = Elem<DT>::f(q[g * D + d]);
+        const float x = qf[g * D + d];
         const float sc = kPlaneInv[plane_of(d >> 4).m];
         const float xh = bf2f(f2bf(x));
         qs += x;
         fed += xh * sc;
         if constexpr (QSPLIT) fed += bf2f(f2bf(x - xh)) * sc;
       }
-    qsum[cb] = qs;
-    cinit[cb] = -128.0f * fed;
+    if (wave == 0) qcs[cb * 64 + lane] = make_float2(qs, -128.0f * fed);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint16_t vh[8], vl[8];
@@ -276,7 +268,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       for (int e = 0; e < 8; ++e) {
         const int c = 2 * st + (e >> 2);
         const int d = (4 * kg + (e & 3)) + 16 * c;
-        const float x = (g < G && grp == st) ? Elem<DT>::f(q[g * D + d]) : 0.0f;
+        const float x = (g < G && grp == st) ? qf[g * D + d] : 0.0f;
         const float sc = kPlaneInv[plane_of(c).m];
         vh[e] = f2bf(x);
         vl[e] = f2bf(x - bf2f(vh[e]));
@@ -294,29 +286,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   }
   // value side: B = -128 everywhere cancels the code bias of the A rows
   const bf16x8 bm128 = u4_to_frag(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u);
-  __syncthreads();
 
   float m_run[G], lacc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; lacc[g] = 0.0f; }
   // value side, row block rb (rows 4g + grp), column block cc (coordinates
   // j + 16cc): of each MFMA tile only the rows of group cc/2 are wanted, so a
-  // batch's tile starts from zero and its row r = cc/2 is added to vacc
-  // (scaled by 4^m of the plane)
+  // batch's tile starts from the batch's code-bias term -128 * (row sums of
+  // A) and its row r = cc/2 is added to vacc (scaled by 4^m of the plane)
   float vacc[NB][8];
-  f32x4 zacc[NB];      // value side: -128 * sum of the A rows (the code bias)
 #pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    zacc[rb] = f32x4{0, 0, 0, 0};
+  for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] = 0.0f;
-  }
   float zt[NB];        // value side: sum of p * zero for row (rb, col)
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) zt[rb] = 0.0f;
 
   const uint32_t* words = reinterpret_cast<const uint32_t*>(base + a.off_words) + (int64_t)h * a.N * 2;
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   // Prefetch (registers), DEPTH tiles ahead: the thread's two pointer-word
   // pairs (one 16-byte load) and its share of the tile's key / value record
@@ -353,6 +340,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     prefetch(d, pw[d], pk[d], pv_[d]);
     __builtin_amdgcn_sched_barrier(0);
   }
+
+  // ---- anchor logits S[a][g] = <q_g, k_a> * c on MFMA, 16 anchors per tile
+  // (rows = anchors, K = coordinates, columns = q-heads), while the first
+  // tiles' loads are in flight
+  {
+    using MS = Mfma<DT>;
+    const T* AK = reinterpret_cast<const T*>(base + a.off_ak) + (int64_t)h * A * D;
+#pragma unroll 2
+    for (int t = wave; t < (A + 15) / 16; t += kWaves) {
+      const int ar = 16 * t + col;
+      f32x4 sacc = {0, 0, 0, 0};
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += MS::KSTEP) {
+        const int kk = k0 + kg * MS::KW;
+        const typename MS::frag af = ar < A ? MS::load(AK + (int64_t)ar * D + kk) : MS::zero();
+        sacc = MS::mma(af, frag_of<DT>(qf + col * D + kk, col < G), sacc);
+      }
+      if (col < G)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int aa = 16 * t + 4 * kg + r;
+          if (aa < A) S[aa * GP + col] = sacc[r] * a.c;
+        }
+    }
+  }
+  __syncthreads();  // S, qbs; qf is dead (buf becomes the tiles' buffer)
 
   for (int base_it = 0; base_it < nch; base_it += DEPTH) {
 #pragma unroll
@@ -394,8 +407,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const int pre = __builtin_amdgcn_readfirstlane(row_sum_i32(lane < wave ? cnt[lane & (kWaves - 1)] : 0));
     const int baseK = pre & 0xFFFF, baseV = pre >> 16;
     // ranks of the lane's tokens among this wave's flagged ones
-    const int rK0 = __popcll(bK0 & below) + __popcll(bK1 & below), rK1 = rK0 + (fK0 ? 1 : 0);
-    const int rV0 = __popcll(bV0 & below) + __popcll(bV1 & below), rV1 = rV0 + (fV0 ? 1 : 0);
+    const int rK0 = lanes_below(bK0) + lanes_below(bK1), rK1 = rK0 + (fK0 ? 1 : 0);
+    const int rV0 = lanes_below(bV0) + lanes_below(bV1), rV1 = rV0 + (fV0 ? 1 : 0);
 
     // ---- B: key-residual logits of this wave's records, 16 per MFMA tile,
     // into this wave's buf rows [0, nK).  Batches
@@ -418,7 +431,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
-        f32x4 cacc = {cinit[cb], cinit[cb], cinit[cb], cinit[cb]};
+        const float2 qc = qcs[cb * 64 + lane];  // (sum of q, initial accumulator)
+        f32x4 cacc = {qc.y, qc.y, qc.y, qc.y};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH][lane]), cacc);
@@ -432,7 +446,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
           if constexpr (LDS) sz = *reinterpret_cast<const uint32_t*>(kstb + (baseK + ii) * kRecBytes + 32 + 4 * grp);
           else if (ii < nK) sz = *reinterpret_cast<const uint32_t*>(recK + (int64_t)(rk0 + baseK + ii) * kRecBytes + 32 + 4 * grp);
           const float sc = h2f((uint16_t)(sz & 0xFFFFu)), z = h2f((uint16_t)(sz >> 16));
-          const float val = quad_sum(fmaf(sc, cacc[r], z * qsum[cb]));
+          const float val = quad_sum(fmaf(sc, cacc[r], z * qc.x));
           if (ii < nK && grp == 0 && g < G) wbuf[ii * BR + g] = val * a.c;
         }
       }
@@ -485,7 +499,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         fct[g] = 1.0f;
         if (tm > m_run[g] + 8.0f) {
           fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
-          m_run[g] = tm;
+          m_run[g] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tm)));  // uniform
           any = true;
         }
       }
@@ -506,8 +520,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         float f = 1.0f;
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) zacc[rb][r] *= f;
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] *= f;
         const int gz = (16 * rb + col) >> 2;  // z row (rb, col)
@@ -584,6 +596,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       // buf rows give p = 0 to padded q-heads and to records past nV (the
       // staged records there are finite: other waves' or zeros)
       bf16x8 ahi[NB], alo[NB];
+      f32x4 zb[NB];  // -128 * row sums of A: cancels the code bias
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
         const int g = (16 * rb + col) >> 2, grp = col & 3;
@@ -611,8 +624,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         }
         ahi[rb] = u4_to_frag(hp[0], hp[1], hp[2], hp[3]);
         alo[rb] = u4_to_frag(lp[0], lp[1], lp[2], lp[3]);
-        zacc[rb] = M::mma(ahi[rb], bm128, zacc[rb]);
-        zacc[rb] = M::mma(alo[rb], bm128, zacc[rb]);
+        zb[rb] = M::mma(ahi[rb], bm128, f32x4{0, 0, 0, 0});
+        zb[rb] = M::mma(alo[rb], bm128, zb[rb]);
       }
       const uint32_t ps6[4] = {pr[0] >> 6, pr[1] >> 6, pr[2] >> 6, pr[3] >> 6};
       const uint32_t ps12[4] = {pr[0] >> 12, pr[1] >> 12, pr[2] >> 12, pr[3] >> 12};
@@ -624,7 +637,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
                                       and_or(src[2], MK[pl.m], vbias), and_or(src[3], MK[pl.m], vbias));
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
-          f32x4 t = M::mma(ahi[rb], bfr, f32x4{0, 0, 0, 0});
+          f32x4 t = M::mma(ahi[rb], bfr, zb[rb]);
           t = M::mma(alo[rb], bfr, t);
           vacc[rb][cc] += t[cc >> 1];
         }
@@ -666,12 +679,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     if (gq < G)
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        const int r = cc >> 1;
-        atomicAdd(&accs[gq * D + col + 16 * cc], (vacc[rb][cc] + zacc[rb][r]) * kPlaneInv[plane_of(cc).m]);
+        atomicAdd(&accs[gq * D + col + 16 * cc], vacc[rb][cc] * kPlaneInv[plane_of(cc).m]);
       }
   }
-  __syncthreads();
-  const int64_t ps = uh * a.S2 + sp;
+  // ---- w V on MFMA: wave w takes coordinates 16w .. 16w+15 (rows = q-heads,
+  // K = anchors, columns = coordinates); w in bf16 hi + lo for bf16 data
+  static_assert(kWaves * 16 == D, "one 16-coordinate block per wave");
+  const int d = 16 * wave + col;
+  f32x4 ov = {0, 0, 0, 0};
+  {
+    using MV = Mfma<DT>;
+    const T* AV = reinterpret_cast<const T*>(base + a.off_av) + (int64_t)h * A * D;
+#pragma unroll 4
+    for (int a0 = 0; a0 < A; a0 += MV::KSTEP) {
+      const int ab = a0 + kg * MV::KW;
+      if constexpr (DT == ANCHORKV_BF16) {
+        float wv[8];
+        uint32_t vb[4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          wv[e] = (col < G && ab + e < A) ? (float)((double)(long long)wi[(ab + e) * GP + col] * kFxInv) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t v0 = ab + 2 * k < A ? (uint32_t)AV[(int64_t)(ab + 2 * k) * D + d] : 0u;
+          const uint32_t v1 = ab + 2 * k + 1 < A ? (uint32_t)AV[(int64_t)(ab + 2 * k + 1) * D + d] : 0u;
+          vb[k] = v0 | (v1 << 16);
+        }
+        uint32_t hp[4], lp[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          hp[k] = bf16_pack(wv[2 * k], wv[2 * k + 1]);
+          lp[k] = bf16_pack(wv[2 * k] - __uint_as_float(hp[k] << 16), wv[2 * k + 1] - __uint_as_float(hp[k] & 0xFFFF0000u));
+        }
+        const bf16x8 bv = u4_to_frag(vb[0], vb[1], vb[2], vb[3]);
+        ov = MV::mma(u4_to_frag(hp[0], hp[1], hp[2], hp[3]), bv, ov);
+        ov = MV::mma(u4_to_frag(lp[0], lp[1], lp[2], lp[3]), bv, ov);
+      } else {
+        const float wv = (col < G && ab < A) ? (float)((double)(long long)wi[ab * GP + col] * kFxInv) : 0.0f;
+        const float vv = ab < A ? Elem<DT>::f(AV[(int64_t)ab * D + d]) : 0.0f;
+        ov = MV::mma(wv, vv, ov);
+      }
+    }
+  }
+  // (max, sum) of this range per q-head
+  __shared__ float ml_s[2][kMaxG];
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
     float l = 0.0f;
@@ -679,58 +730,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     float m = -INFINITY;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) m = (gg == g) ? m_run[gg] : m;
-    a.part_ml[ps * G + g] = make_float2(m, l);
+    ml_s[0][g] = m;
+    ml_s[1][g] = l;
   }
-  for (int i = threadIdx.x; i < G * A; i += blockDim.x) {
-    const int g = i / A, aa = i % A;
-    a.part_w[ps * G * A + i] = (float)((double)(long long)wi[aa * GP + g] * kFxInv);
+  __syncthreads();
+  // lane (col, kg) holds rows g = 4kg + r of coordinate d
+  float val[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int g = 4 * kg + r;
+    val[r] = g < G ? ov[r] + accs[g * D + d] + zt_s[g * 4 + d / 32] : 0.0f;
   }
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-    a.part_acc[ps * G * D + i] = accs[i] + zt_s[(i / D) * 4 + (i % D) / 32];
+  if (a.S2 == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * kg + r;
+      if (g < G) a.o[(uh * G + g) * D + d] = val[r] / ml_s[1][g];
+    }
+    return;
+  }
+  // several ranges per head: publish this one (merged by k_dec_merge)
+  const int64_t ps = uh * a.S2 + sp;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int g = 4 * kg + r;
+    if (g < G) a.part_acc[(ps * G + g) * D + d] = val[r];
+  }
+  if (threadIdx.x < G) a.part_ml[ps * G + threadIdx.x] = make_float2(ml_s[0][threadIdx.x], ml_s[1][threadIdx.x]);
 }
 
-// ---------------------------------------------------------------- combine
-// Per (unit, head): merge the ranges' (m, l, w, acc) and finish
-// o = (sum_a W[g][a] v_a + ACC[g]) / L with W staged in LDS.
-template <int DT>
-__global__ __launch_bounds__(256) void k_dec_combine(const uint8_t* cache, int64_t stride, int64_t off_av,
-                                                    const float2* part_ml, const float* part_w,
-                                                    const float* part_acc, float* o, int H, int G, int A, int S2) {
-  using T = typename Elem<DT>::T;
-  constexpr int D = kHeadDim;
-  extern __shared__ float Wsum[];  // [G][A]
-  __shared__ float f_s[kMaxG][64];
-  __shared__ float Linv[kMaxG];
-  const int h = blockIdx.x % H, u = blockIdx.x / H;
-  const int64_t uh = (int64_t)u * H + h;
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
+// Per (unit, head) with several token ranges: o = sum_s f_s acc_s / sum_s f_s l_s
+// with f_s = 2^(m_s - max m).  One thread per (q-head, coordinate).
+__global__ __launch_bounds__(256) void k_dec_merge(const float2* part_ml, const float* part_acc, float* o, int G,
+                                                  int S2) {
+  const int64_t uh = blockIdx.x;
+  for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) {
+    const int g = i / kHeadDim, d = i % kHeadDim;
     float M = -INFINITY;
     for (int s = 0; s < S2; ++s) M = fmaxf(M, part_ml[(uh * S2 + s) * G + g].x);
-    float L = 0.0f;
+    float L = 0.0f, acc = 0.0f;
     for (int s = 0; s < S2; ++s) {
       const float2 v = part_ml[(uh * S2 + s) * G + g];
       const float f = v.x == -INFINITY ? 0.0f : exp2_fast(v.x - M);
-      f_s[g][s] = f;
       L += f * v.y;
+      acc = fmaf(f, part_acc[((uh * S2 + s) * G + g) * kHeadDim + d], acc);
     }
-    Linv[g] = 1.0f / L;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * A; i += blockDim.x) {
-    const int g = i / A;
-    float acc = 0.0f;
-    for (int s = 0; s < S2; ++s) acc = fmaf(f_s[g][s], part_w[(uh * S2 + s) * G * A + i], acc);
-    Wsum[i] = acc;
-  }
-  __syncthreads();
-  const T* AV = reinterpret_cast<const T*>(cache + (int64_t)u * stride + off_av) + (int64_t)h * A * D;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int g = i / D, d = i % D;
-    float acc = 0.0f;
-    for (int s = 0; s < S2; ++s) acc = fmaf(f_s[g][s], part_acc[(uh * S2 + s) * G * D + i], acc);
-    for (int aa = 0; aa < A; ++aa) acc = fmaf(Wsum[g * A + aa], Elem<DT>::f(AV[(int64_t)aa * D + d]), acc);
-    o[(uh * G + g) * D + d] = acc * Linv[g];
+    o[(uh * G + g) * kHeadDim + d] = acc / L;
   }
 }
 
@@ -740,7 +785,8 @@ static size_t stream_lds(int G, int A, int KP, bool qsplit) {
   const size_t GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   const size_t NB = (4 * (size_t)G + 15) / 16;
   return sizeof(float) * ((3 * GP * A + 3) & ~(size_t)3) + sizeof(float) * (size_t)std::max<size_t>(kTile * 4 * NB, 2048) +
-         2 * 512 * (size_t)KP * sizeof(uint4) + (size_t)kRecPad * kRecBytes + NB * 4 * (qsplit ? 2 : 1) * 64 * sizeof(uint4);
+         2 * 512 * (size_t)KP * sizeof(uint4) + (size_t)kRecPad * kRecBytes + NB * 4 * (qsplit ? 2 : 1) * 64 * sizeof(uint4) +
+         NB * 64 * sizeof(float2);
 }
 constexpr size_t kLdsLimit = 158 * 1024;  // dynamic part; the static part is under 2 KB of the 160 KB
 
@@ -774,22 +820,16 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   if (S2 > 64) return fail(ANCHORKV_E_SHAPE, "decode: too many splits");
   if (stream_lds(G, A, 1, DT == ANCHORKV_F32) > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
   if (p.n_chunks > 128 * S2) return fail(ANCHORKV_E_SHAPE, "decode: too many chunks per range");
-  const size_t lds_c = sizeof(float) * (size_t)G * A;
-  const float c = kLog2e / sqrtf((float)kHeadDim);
-  float* stab = reinterpret_cast<float*>(ws + w.stab);
-  static size_t cdone = 0;
-  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_combine<DT>), lds_c, &cdone)) return rc;
   prof_call_begin(st);
-  k_dec_stab<DT><<<(unsigned)(U * H), 256, 0, st>>>(q, cache, p.unit_stride, p.off_anchor_k, stab, H, G, A, c);
-  AKV_CHECK_LAUNCH("k_dec_stab");
-  prof_mark(st, "dec_stab");
   DecArgs a;
   a.q = q; a.cache = cache; a.stride = p.unit_stride; a.off_words = p.off_words; a.off_rk = p.off_res_k;
-  a.off_rv = p.off_res_v; a.off_ck = p.off_chunk_k; a.off_cv = p.off_chunk_v; a.stab = stab;
+  a.off_rv = p.off_res_v; a.off_ck = p.off_chunk_k; a.off_cv = p.off_chunk_v;
+  a.off_ak = p.off_anchor_k; a.off_av = p.off_anchor_v;
   a.part_ml = reinterpret_cast<float2*>(ws + w.part_ml);
-  a.part_w = reinterpret_cast<float*>(ws + w.part_w);
   a.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
-  a.H = H; a.N = p.N; a.A = A; a.C = p.n_chunks; a.S2 = S2; a.cps = (p.n_chunks + S2 - 1) / S2; a.c = c;
+  a.o = o;
+  a.H = H; a.N = p.N; a.A = A; a.C = p.n_chunks; a.S2 = S2; a.cps = (p.n_chunks + S2 - 1) / S2;
+  a.c = kLog2e / sqrtf((float)kHeadDim);
   a.R_K = p.R_K; a.R_V = p.R_V;
   const unsigned grid = (unsigned)((int64_t)U * H * S2);
   int rc = 0;
@@ -804,12 +844,18 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
     default: rc = launch_stream<DT, 8>(a, grid, st); break;
   }
   if (rc) return rc;
+  if (S2 > 1) {
+    k_dec_merge<<<(unsigned)((int64_t)U * H), 256, 0, st>>>(a.part_ml, a.part_acc, o, G, S2);
+    AKV_CHECK_LAUNCH("k_dec_merge");
+  }
   prof_mark(st, "dec_stream");
-  k_dec_combine<DT><<<(unsigned)(U * H), 256, lds_c, st>>>(
-      cache, p.unit_stride, p.off_anchor_v, a.part_ml, a.part_w, a.part_acc, o, H, G, A, S2);
-  AKV_CHECK_LAUNCH("k_dec_combine");
-  prof_mark(st, "dec_combine");
   return 0;
+}
+
+int decode_blocks_per_cu(int G, int A, bool f32) {
+  // G <= 4 runs at four waves per SIMD (two 8-wave workgroups) when two
+  // copies of its LDS fit the 160 KB (static part under 2 KB each)
+  return (G <= 4 && 2 * (stream_lds(G, A, 2, f32) + 2048) <= 160 * 1024) ? 2 : 1;
 }
 
 int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* ws, void* stream) {

@@ -71,31 +71,32 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
 
 DecodeWs decode_ws_layout(const anchorkv_plan_info& p) {
   DecodeWs w{};
-  const int64_t U = p.units, H = p.H, G = p.G, A = p.A, D = p.D;
+  const int64_t U = p.units, H = p.H, G = p.G, D = p.D;
   w.S2 = p.decode_splits;
   int64_t off = 0;
   auto take = [&](int64_t bytes) { int64_t o = off; off = round_up(off + bytes, 256); return o; };
-  w.stab = take(4 * U * H * G * A);
   w.part_ml = take(8 * U * H * w.S2 * G);
-  w.part_w = take(4 * U * H * w.S2 * G * A);
   w.part_acc = take(4 * U * H * w.S2 * G * D);
   w.total = off;
   return w;
 }
 
 // Token splits per (unit, head) of the decode pass.  One block per split
-// walks its 1024-token chunks; about two blocks fit a compute unit.  Fewest
-// rounds of resident blocks times chunks per block; fewer splits on ties
-// (each split adds a prologue, an epilogue and a partial to combine).
+// walks its 1024-token chunks after reading the head's anchors twice (keys for
+// the logit table, values for the output), and one or two blocks fit a
+// compute unit.  Fewest rounds of resident blocks times bytes per block;
+// fewer splits on ties (each split adds anchor reads and a partial to merge).
 static int decode_split_count(const anchorkv_plan_info& p) {
   const int64_t heads = (int64_t)p.units * p.H;
   const int64_t C = p.n_chunks;   // splits start on 1024-token chunk boundaries
-  const int64_t slots = 2 * 256;
+  const int64_t slots = 256 * (int64_t)decode_blocks_per_cu(p.G, p.A, p.dtype == ANCHORKV_F32);
+  const int64_t chunk_bytes = 8 * 1024 + kRecBytes * (p.R_K + p.R_V) / std::max<int64_t>(1, p.H * C);
+  const int64_t anchor_bytes = 2 * (int64_t)p.A * p.D * p.elem_bytes;
   int best = 1;
   int64_t best_cost = INT64_MAX;
   for (int64_t s = 1; s <= std::min<int64_t>(C, 64); ++s) {
     const int64_t per = (C + s - 1) / s;
-    const int64_t cost = ((heads * s + slots - 1) / slots) * per;
+    const int64_t cost = ((heads * s + slots - 1) / slots) * (per * chunk_bytes + anchor_bytes);
     if (cost < best_cost) { best_cost = cost; best = (int)s; }
   }
   return best;

@@ -58,10 +58,8 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p);
 // Decode workspace layout.
 struct DecodeWs {
   int S2;          // token splits per (unit, head); boundaries on 1024-token chunks
-  int64_t stab;    // f32 [U][H][G][A]   <q_g, k_a> * log2(e)/sqrt(D)
-  int64_t part_ml; // float2 [U][H][S2][G]
-  int64_t part_w;  // f32 [U][H][S2][G][A]
-  int64_t part_acc; // f32 [U][H][S2][G][D]
+  int64_t part_ml; // float2 [U][H][S2][G]  (max, sum) of each range
+  int64_t part_acc; // f32 [U][H][S2][G][D] unnormalised output of each range
   int64_t total;
 };
 DecodeWs decode_ws_layout(const anchorkv_plan_info& p);
@@ -88,5 +86,7 @@ void prof_mark(void* stream, const char* stage);
 int run_compress(const anchorkv_plan_info& p, const void* K, const void* V, const void* Q, void* cache,
                  void* ws, void* stream);
 int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* ws, void* stream);
+// Workgroups of the decode kernel that fit one compute unit (LDS and registers).
+int decode_blocks_per_cu(int G, int A, bool f32);
 
 }  // namespace akv
