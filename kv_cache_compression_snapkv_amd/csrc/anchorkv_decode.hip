@@ -173,7 +173,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   constexpr bool QSPLIT = DT == ANCHORKV_F32;   // f32 queries enter the key MFMA as bf16 hi + lo
   extern __shared__ __align__(16) float sm[];
   const int A = a.A;
-  unsigned long long* wi = reinterpret_cast<unsigned long long*>(sm);  // [A][GP] fixed point
+  // w[g][a] in fixed point, q-head-major: the scatter's random anchors then
+  // spread over all banks (an anchor-major row of GP entries would put every
+  // anchor's entry g on the same few banks)
+  unsigned long long* wi = reinterpret_cast<unsigned long long*>(sm);  // [GP][A]
   float* S = reinterpret_cast<float*>(wi + A * GP);                      // [A][GP]
   // [kTile][BR]: per wave 128 private rows (its tokens' records by rank):
   // key-residual logits, then p of value-flagged tokens (zeros in columns
@@ -507,13 +510,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     if (any) {
 #pragma unroll
       for (int g = 0; g < G; ++g) lacc[g] *= fct[g];
-      for (int i = threadIdx.x; i < A * GP; i += blockDim.x) {
-        const int g = i % GP;
-        float f = 1.0f;
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
-        if (f != 1.0f) wi[i] = (unsigned long long)__double2ll_rn((double)(long long)wi[i] * (double)f);
-      }
+      for (int g = 0; g < G; ++g)
+        if (fct[g] != 1.0f)
+          for (int i = threadIdx.x; i < A; i += blockDim.x)
+            wi[g * A + i] = (unsigned long long)__double2ll_rn((double)(long long)wi[g * A + i] * (double)fct[g]);
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
         const int g = 4 * rb + kg;  // accumulator rows 16rb + 4kg + r -> q-head 4rb + kg
@@ -547,19 +548,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         pk1[g] = exp2_fast(s1[g] - m_run[g]);
         lacc[g] += pk0[g] + pk1[g];
       }
-      unsigned long long* w0 = wi + aV0 * GP;
-      unsigned long long* w1 = wi + aV1 * GP;
       if (fast) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          atomicAdd(w0 + g, (unsigned long long)(unsigned)fmaf(pk0[g], gs0, 0.5f));
-          atomicAdd(w1 + g, (unsigned long long)(unsigned)fmaf(pk1[g], gs1, 0.5f));
+          atomicAdd(wi + g * A + aV0, (unsigned long long)(unsigned)fmaf(pk0[g], gs0, 0.5f));
+          atomicAdd(wi + g * A + aV1, (unsigned long long)(unsigned)fmaf(pk1[g], gs1, 0.5f));
         }
       } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          atomicAdd(w0 + g, fx_general(pk0[g] * gs0));
-          atomicAdd(w1 + g, fx_general(pk1[g] * gs1));
+          atomicAdd(wi + g * A + aV0, fx_general(pk0[g] * gs0));
+          atomicAdd(wi + g * A + aV1, fx_general(pk1[g] * gs1));
         }
       }
       if (fV0) stsv<BR>(wbuf + rV0 * BR, pk0);
@@ -698,7 +697,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         uint32_t vb[4];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          wv[e] = (col < G && ab + e < A) ? (float)((double)(long long)wi[(ab + e) * GP + col] * kFxInv) : 0.0f;
+          wv[e] = (col < G && ab + e < A) ? (float)((double)(long long)wi[col * A + ab + e] * kFxInv) : 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const uint32_t v0 = ab + 2 * k < A ? (uint32_t)AV[(int64_t)(ab + 2 * k) * D + d] : 0u;
@@ -715,7 +714,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         ov = MV::mma(u4_to_frag(hp[0], hp[1], hp[2], hp[3]), bv, ov);
         ov = MV::mma(u4_to_frag(lp[0], lp[1], lp[2], lp[3]), bv, ov);
       } else {
-        const float wv = (col < G && ab < A) ? (float)((double)(long long)wi[ab * GP + col] * kFxInv) : 0.0f;
+        const float wv = (col < G && ab < A) ? (float)((double)(long long)wi[col * A + ab] * kFxInv) : 0.0f;
         const float vv = ab < A ? Elem<DT>::f(AV[(int64_t)ab * D + d]) : 0.0f;
         ov = MV::mma(wv, vv, ov);
       }
