@@ -800,12 +800,29 @@ static int launch_stream_kp(const DecArgs& a, unsigned grid, hipStream_t st) {
   return 0;
 }
 
-// Up to 4 q-heads per KV head: 3 staged chunks per side (512 records) and two
-// tiles of prefetch in flight; more q-heads: 1 staged chunk (170 records).
+// Staged 16-byte chunks per thread and side (KP; 512*KP*16/48 records per
+// tile) from the average number of residual records per 1024-token tile:
+// larger staging costs registers and LDS, records beyond it are read from
+// the cache directly.
+static int decode_kp(int G, int64_t R_K, int64_t R_V, int64_t H, int64_t C) {
+  if (G > 4) return 1;
+  const int64_t per = std::max(R_K, R_V) / std::max<int64_t>(1, H * C);
+  return per <= 150 ? 1 : per <= 300 ? 2 : 3;
+}
+
+// Up to 4 q-heads per KV head: four waves per SIMD (two workgroups per CU);
+// more q-heads: two waves per SIMD (one workgroup per CU, LDS-bound).
 template <int DT, int G>
 static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
-  if constexpr (G <= 4) return launch_stream_kp<DT, G, 2, 1, 4>(a, grid, st);
-  else return launch_stream_kp<DT, G, 1, 2, 2>(a, grid, st);
+  if constexpr (G <= 4) {
+    switch (decode_kp(G, a.R_K, a.R_V, a.H, a.C)) {
+      case 1: return launch_stream_kp<DT, G, 1, 1, 4>(a, grid, st);
+      case 2: return launch_stream_kp<DT, G, 2, 1, 4>(a, grid, st);
+      default: return launch_stream_kp<DT, G, 3, 1, 4>(a, grid, st);
+    }
+  } else {
+    return launch_stream_kp<DT, G, 1, 2, 2>(a, grid, st);
+  }
 }
 
 template <int DT>
@@ -851,10 +868,11 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   return 0;
 }
 
-int decode_blocks_per_cu(int G, int A, bool f32) {
+int decode_blocks_per_cu(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C) {
   // G <= 4 runs at four waves per SIMD (two 8-wave workgroups) when two
   // copies of its LDS fit the 160 KB (static part under 2 KB each)
-  return (G <= 4 && 2 * (stream_lds(G, A, 2, f32) + 2048) <= 160 * 1024) ? 2 : 1;
+  const int kp = decode_kp(G, R_K, R_V, H, C);
+  return (G <= 4 && 2 * (stream_lds(G, A, kp, f32) + 2048) <= 160 * 1024) ? 2 : 1;
 }
 
 int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* ws, void* stream) {

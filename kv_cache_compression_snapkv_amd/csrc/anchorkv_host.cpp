@@ -89,7 +89,7 @@ DecodeWs decode_ws_layout(const anchorkv_plan_info& p) {
 static int decode_split_count(const anchorkv_plan_info& p) {
   const int64_t heads = (int64_t)p.units * p.H;
   const int64_t C = p.n_chunks;   // splits start on 1024-token chunk boundaries
-  const int64_t slots = 256 * (int64_t)decode_blocks_per_cu(p.G, p.A, p.dtype == ANCHORKV_F32);
+  const int64_t slots = 256 * (int64_t)decode_blocks_per_cu(p.G, p.A, p.dtype == ANCHORKV_F32, p.R_K, p.R_V, p.H, C);
   const int64_t chunk_bytes = 8 * 1024 + kRecBytes * (p.R_K + p.R_V) / std::max<int64_t>(1, p.H * C);
   const int64_t anchor_bytes = 2 * (int64_t)p.A * p.D * p.elem_bytes;
   int best = 1;

@@ -87,6 +87,6 @@ int run_compress(const anchorkv_plan_info& p, const void* K, const void* V, cons
                  void* ws, void* stream);
 int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* ws, void* stream);
 // Workgroups of the decode kernel that fit one compute unit (LDS and registers).
-int decode_blocks_per_cu(int G, int A, bool f32);
+int decode_blocks_per_cu(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C);
 
 }  // namespace akv

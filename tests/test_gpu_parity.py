@@ -41,6 +41,9 @@ SMALL = {
     # kv_heads * n_tokens > 65536: top-R streams the utilities instead of holding them in registers
     "bf16_long_topr": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=3, q_per_kv=2, n_tokens=22000, n_obs=16,
                                              window=32, theta=0.1, n_dirs=16),
+    # 151..300 residual records per 1024-token tile: the decode's middle staging size
+    "bf16_mid_staging": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, n_obs=16, theta=0.07,
+                                               n_dirs=16),
     # budget leaves no residual slots
     "bf16_no_residuals": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=1, q_per_kv=2, n_tokens=256, n_obs=8,
                                                 window=32, theta=0.144, n_dirs=8),
