@@ -39,11 +39,8 @@ constexpr int kMaxG = 8;          // q-heads per KV head supported by decode
 constexpr int kTile = 1024;       // tokens per tile (= residual-offset chunk)
 constexpr int kWaves = 8;         // waves per workgroup; 128 tokens per wave per tile
 constexpr uint32_t kCodeBias = 0x43004300u;  // bf16 pair (128, 128)
-// Softmax weights are kept as p' = 2^(s - m_run - 8) <= 1 (m_run is raised
-// whenever a logit passes m_run + 8), so one common factor 2^-8 cancels in
-// o = (w V + acc) / l.
-constexpr float kFxScale = 536870912.0f;        // 2^29: fixed-point scale of the w scatter
-constexpr double kFxInv = 1.0 / 536870912.0;
+constexpr float kFxScale = 2097152.0f;          // 2^21: fixed-point scale of the w scatter
+constexpr double kFxInv = 1.0 / 2097152.0;
 // floats of the per-tile buffer: [kTile][G], at least the 8 KB of staged words
 template <int G> constexpr int kBufFloats = kTile * G > 2048 ? kTile * G : 2048;
 
@@ -106,26 +103,6 @@ __device__ constexpr Plane plane_of(int c) {
   return c < 3 ? Plane{0, c} : c < 6 ? Plane{6, c - 3} : Plane{12, c - 6};
 }
 constexpr float kPlaneInv[3] = {1.0f, 0.25f, 0.0625f};
-
-// The value side uses fp16 planes the same way: exponent of 1024 (ten
-// mantissa bits), planes c = 0..4 at bits 2c of the word itself, c = 5..7
-// after a shift by 10; value 1024 + code * 4^m.
-struct PlaneH {
-  int sh, m;
-};
-__device__ constexpr PlaneH plane_h(int c) { return c < 5 ? PlaneH{0, c} : PlaneH{10, c - 5}; }
-constexpr float kPlaneInvH[5] = {1.0f, 0.25f, 0.0625f, 0.015625f, 0.00390625f};
-constexpr uint32_t kCodeBiasH = 0x64006400u;  // fp16 pair (1024, 1024)
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v;
-__device__ __forceinline__ f32x4 mma_f16(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-// two floats -> packed fp16 pair (round to nearest even), lo in bits 0..15
-__device__ __forceinline__ uint32_t f16_pack(float lo, float hi) {
-  const f32x2v f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2v));
-}
 
 // ordered-int image of a float (monotone), for LDS integer max
 __device__ __forceinline__ int fkey(float f) {
@@ -310,12 +287,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
     }
   }
-  // value side (fp16): B = -1024 everywhere cancels the code bias of the A rows
-  const f16x8 hm1024 = __builtin_bit_cast(f16x8, make_uint4(0xE400E400u, 0xE400E400u, 0xE400E400u, 0xE400E400u));
-  uint32_t MH[5] = {0x00030003u, 0x000C000Cu, 0x00300030u, 0x00C000C0u, 0x03000300u};
-  asm volatile("" : "+s"(MH[0]), "+s"(MH[1]), "+s"(MH[2]), "+s"(MH[3]), "+s"(MH[4]));
-  uint32_t hbias = kCodeBiasH;
-  asm volatile("" : "+v"(hbias));
+  // value side: B = -128 everywhere cancels the code bias of the A rows
+  const bf16x8 bm128 = u4_to_frag(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u);
 
   float m_run[G], lacc[G];
 #pragma unroll
@@ -562,7 +535,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     // tokens in this wave's buf rows [0, nV) and zeros in the rows after them
     // up to the next multiple of 32 (the value batches read whole batches).
     // A token past the range has p = 0 and adds 0 to w[0].
-    // p' <= 1 (lazy rescale), so gamma in [0, 8) keeps p'*gamma*2^29 in [0, 2^32).
+    // p <= 2^8 (lazy rescale), so gamma in [0, 8) keeps p*gamma*2^21 in [0, 2^32).
     {
       const float gs0 = gV0 * kFxScale, gs1 = gV1 * kFxScale;
       const bool fast = __all((!v0 || (gV0 >= 0.0f && gV0 < 8.0f)) && (!v1 || (gV1 >= 0.0f && gV1 < 8.0f)));
@@ -571,8 +544,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       for (int g = 0; g < BR; ++g) { pk0[g] = 0.0f; pk1[g] = 0.0f; }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        pk0[g] = exp2_fast(s0[g] - (m_run[g] + 8.0f));
-        pk1[g] = exp2_fast(s1[g] - (m_run[g] + 8.0f));
+        pk0[g] = exp2_fast(s0[g] - m_run[g]);
+        pk1[g] = exp2_fast(s1[g] - m_run[g]);
         lacc[g] += pk0[g] + pk1[g];
       }
       if (fast) {
@@ -618,12 +591,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         }
         pr[e2] = w0 | (w1 << 16);
       }
-      // A operands: row (4g + grp) = 16rb + col, records b0 + 8kg + e, as
-      // fp16 p' * scale (p' <= 1, scale fp16: no overflow); the buf rows give
-      // p' = 0 to padded q-heads and to records past nV (the staged records
-      // there are finite: other waves' or zeros)
-      f16x8 ah[NB];
-      f32x4 zb[NB];  // -1024 * row sums of A: cancels the code bias
+      // A operands: row (4g + grp) = 16rb + col, records b0 + 8kg + e; the
+      // buf rows give p = 0 to padded q-heads and to records past nV (the
+      // staged records there are finite: other waves' or zeros)
+      bf16x8 ahi[NB], alo[NB];
+      f32x4 zb[NB];  // -128 * row sums of A: cancels the code bias
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
         const int g = (16 * rb + col) >> 2, grp = col & 3;
@@ -640,20 +612,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
           zsum = fmaf(pv, h2f((uint16_t)(sz >> 16)), zsum);
         }
         zt[rb] = zsum;
-        ah[rb] = __builtin_bit_cast(f16x8, make_uint4(f16_pack(ps[0], ps[1]), f16_pack(ps[2], ps[3]),
-                                                      f16_pack(ps[4], ps[5]), f16_pack(ps[6], ps[7])));
-        zb[rb] = mma_f16(ah[rb], hm1024, f32x4{0, 0, 0, 0});
+        uint32_t hp[4], lp[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t hb = bf16_pack(ps[2 * k], ps[2 * k + 1]);
+          const float d0 = ps[2 * k] - __uint_as_float(hb << 16);
+          const float d1 = ps[2 * k + 1] - __uint_as_float(hb & 0xFFFF0000u);
+          hp[k] = hb;
+          lp[k] = bf16_pack(d0, d1);
+        }
+        ahi[rb] = u4_to_frag(hp[0], hp[1], hp[2], hp[3]);
+        alo[rb] = u4_to_frag(lp[0], lp[1], lp[2], lp[3]);
+        zb[rb] = M::mma(ahi[rb], bm128, f32x4{0, 0, 0, 0});
+        zb[rb] = M::mma(alo[rb], bm128, zb[rb]);
       }
-      const uint32_t ps10[4] = {pr[0] >> 10, pr[1] >> 10, pr[2] >> 10, pr[3] >> 10};
+      const uint32_t ps6[4] = {pr[0] >> 6, pr[1] >> 6, pr[2] >> 6, pr[3] >> 6};
+      const uint32_t ps12[4] = {pr[0] >> 12, pr[1] >> 12, pr[2] >> 12, pr[3] >> 12};
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        const PlaneH pl = plane_h(cc);
-        const uint32_t* src = pl.sh == 0 ? pr : ps10;
-        const f16x8 bfr = __builtin_bit_cast(f16x8, make_uint4(and_or(src[0], MH[pl.m], hbias), and_or(src[1], MH[pl.m], hbias),
-                                                               and_or(src[2], MH[pl.m], hbias), and_or(src[3], MH[pl.m], hbias)));
+        const Plane pl = plane_of(cc);
+        const uint32_t* src = pl.sh == 0 ? pr : pl.sh == 6 ? ps6 : ps12;
+        const bf16x8 bfr = u4_to_frag(and_or(src[0], MK[pl.m], vbias), and_or(src[1], MK[pl.m], vbias),
+                                      and_or(src[2], MK[pl.m], vbias), and_or(src[3], MK[pl.m], vbias));
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
-          const f32x4 t = mma_f16(ah[rb], bfr, zb[rb]);
+          f32x4 t = M::mma(ahi[rb], bfr, zb[rb]);
+          t = M::mma(alo[rb], bfr, t);
           vacc[rb][cc] += t[cc >> 1];
         }
       }
@@ -694,7 +678,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     if (gq < G)
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        atomicAdd(&accs[gq * D + col + 16 * cc], vacc[rb][cc] * kPlaneInvH[plane_h(cc).m]);
+        atomicAdd(&accs[gq * D + col + 16 * cc], vacc[rb][cc] * kPlaneInv[plane_of(cc).m]);
       }
   }
   // ---- w V on MFMA: wave w takes coordinates 16w .. 16w+15 (rows = q-heads,
