@@ -492,13 +492,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
     }
     lds_barrier();
-    // ---- D: lazy rescale (every thread takes the same decision)
+    // ---- D: lazy rescale (every thread takes the same decision).  The
+    // probabilities are first computed with the current m_run while the
+    // tile maxima are read, and again in the rare case that m_run moves.
+    float pk0[BR], pk1[BR];
+#pragma unroll
+    for (int g = 0; g < BR; ++g) { pk0[g] = 0.0f; pk1[g] = 0.0f; }
+    int tk[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) tk[g] = tmaxb[par][g];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      pk0[g] = exp2_fast(s0[g] - m_run[g]);
+      pk1[g] = exp2_fast(s1[g] - m_run[g]);
+    }
     bool any = false;
     float fct[G];
     {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float tm = fkey_inv(tmaxb[par][g]);
+        const float tm = fkey_inv(tk[g]);
         fct[g] = 1.0f;
         if (tm > m_run[g] + 8.0f) {
           fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
@@ -529,6 +542,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         for (int gg = 0; gg < G; ++gg) fz = (gg == gz) ? fct[gg] : fz;
         zt[rb] *= fz;
       }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        pk0[g] = exp2_fast(s0[g] - m_run[g]);
+        pk1[g] = exp2_fast(s1[g] - m_run[g]);
+      }
       lds_barrier();
     }
     // ---- E: probabilities, scatter p*gamma into w, keep p of value-flagged
@@ -539,15 +557,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     {
       const float gs0 = gV0 * kFxScale, gs1 = gV1 * kFxScale;
       const bool fast = __all((!v0 || (gV0 >= 0.0f && gV0 < 8.0f)) && (!v1 || (gV1 >= 0.0f && gV1 < 8.0f)));
-      float pk0[BR], pk1[BR];
 #pragma unroll
-      for (int g = 0; g < BR; ++g) { pk0[g] = 0.0f; pk1[g] = 0.0f; }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        pk0[g] = exp2_fast(s0[g] - m_run[g]);
-        pk1[g] = exp2_fast(s1[g] - m_run[g]);
-        lacc[g] += pk0[g] + pk1[g];
-      }
+      for (int g = 0; g < G; ++g) lacc[g] += pk0[g] + pk1[g];
       if (fast) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
