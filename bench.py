@@ -80,16 +80,19 @@ def roofline(p, stage, ms):
             "frac": (flops / s / 1e12) / peak_f, "algorithmic_flops": flops}
 
 
-def cpu_baseline(w, units_sample=3):
+def cpu_baseline(w, budget_s=12.0):
     """The oracle as it stands, on the host cores: compress + one decode step
     for a bounded sample of units, extrapolated to the workload's tokens/s."""
     import numpy as np
     import kvsynth
     from oracle import anchorkv_oracle as O
     cores = len(os.sched_getaffinity(0))
-    n = min(units_sample, w.units)
+    n = 0
     t_tot = 0.0
-    for u in range(n):
+    for u in range(w.units):  # whole units until about budget_s of oracle time
+        if t_tot >= budget_s:
+            break
+        n += 1
         s, l = kvsynth.unit_index(w, u)
         K, V, Q = kvsynth.unit_inputs(w, s, l, device="cpu")
         K64, V64, Q64 = (kvsynth.to_f64(x) for x in (K, V, Q))
