@@ -128,8 +128,10 @@ __device__ void find_bucket(const unsigned* hist, int nbins, unsigned need, int*
 // sum over non-window positions) -> top k_s (radix select on the f32 bits,
 // ties to the lower position) -> k_u stratified picks over the remaining
 // positions (pick i = remaining[floor((2i+1) M / (2 k_u))]) -> + window ->
-// positions ascending, anchor_of map, anchor copies, norms.
-template <int DT>
+// positions ascending, anchor_of map, anchor copies, norms.  With LP the
+// pooled score stays in LDS (dynamic, L floats), else it goes through the
+// workspace.
+template <int DT, bool LP>
 __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv, const float* score, float* pooled,
                                                  uint8_t* cache, int64_t stride, int64_t off_ak, int64_t off_av,
                                                  int64_t off_pos, int* anchor_of, float2* anorm, int H, int N, int W,
@@ -141,21 +143,34 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
   __shared__ int s_b;
   __shared__ unsigned s_above;
   __shared__ int s_pos[4096];  // scored + uniform positions (A <= 4096 is checked on the host)
+  __shared__ float stg[1024 + 6];
+  extern __shared__ float plds[];
   const int h = blockIdx.x % H;
   const int u = blockIdx.x / H;
   const int64_t uh = (int64_t)u * H + h;
   const int L = N - W;
   const float* sc = score + uh * N;
-  float* pl = pooled + uh * N;
+  float* pl = LP ? plds : pooled + uh * N;
   const int tid = threadIdx.x, nt = blockDim.x;
 
-  for (int t = tid; t < L; t += nt) {
-    float v = 0.0f;
-    const int lo = max(0, t - 3), hi = min(L - 1, t + 3);
-    for (int x = lo; x <= hi; ++x) v += sc[x];
-    pl[t] = v;
+  // pooled_t = score_{t-3} + ... + score_{t+3} over [0, L) (zeros outside,
+  // added in position order), from 1024-position chunks of the score
+  // staged with a 3-position halo
+  for (int t0 = 0; t0 < L; t0 += nt) {
+    for (int i = tid; i < nt + 6; i += nt) {
+      const int x = t0 - 3 + i;
+      stg[i] = (x >= 0 && x < L) ? sc[x] : 0.0f;
+    }
+    __syncthreads();
+    const int t = t0 + tid;
+    if (t < L) {
+      float v = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 7; ++k) v += stg[tid + k];
+      pl[t] = v;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // radix select of the k_s-th largest key (keys = f32 bits of non-negative values)
   unsigned prefix = 0, need = (unsigned)k_s;
@@ -900,10 +915,23 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   AKV_CHECK_LAUNCH("k_o_combine");
   prof_mark(st, "o_combine");
 
-  k_select<DT><<<(unsigned)(U * H), 1024, 0, st>>>(
-      K, V, a.score, reinterpret_cast<float*>(ws + w.pooled), cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v,
-      p.off_positions, reinterpret_cast<int*>(ws + w.anchor_of), reinterpret_cast<float2*>(ws + w.anorm), H, N,
-      p.window, p.k_scored, p.k_uniform, A);
+  {
+    // pooled score in LDS while it fits next to the static arrays (~26 KB)
+    const size_t plb = sizeof(float) * (size_t)(N - p.window);
+    auto sel = [&](auto kern, size_t dyn) {
+      kern<<<(unsigned)(U * H), 1024, dyn, st>>>(
+          K, V, a.score, reinterpret_cast<float*>(ws + w.pooled), cache, p.unit_stride, p.off_anchor_k,
+          p.off_anchor_v, p.off_positions, reinterpret_cast<int*>(ws + w.anchor_of),
+          reinterpret_cast<float2*>(ws + w.anorm), H, N, p.window, p.k_scored, p.k_uniform, A);
+    };
+    if (plb <= 128 * 1024) {
+      static size_t sdone = 0;
+      if ((rc = set_dyn_lds(reinterpret_cast<const void*>(&k_select<DT, true>), plb, &sdone))) return rc;
+      sel(k_select<DT, true>, plb);
+    } else {
+      sel(k_select<DT, false>, 0);
+    }
+  }
   AKV_CHECK_LAUNCH("k_select");
   prof_mark(st, "select");
 
