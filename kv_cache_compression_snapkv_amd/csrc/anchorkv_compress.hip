@@ -96,6 +96,30 @@ __device__ int block_excl_scan(int v, int* sh /*[32]*/, int* total) {
   return r;
 }
 
+// Adds 1 to hist[bin] for every active lane.  Lanes of a wave that share a
+// bin add their count with one atomic (the common case in the top digits of
+// nearby values, where one bin would otherwise take 64 serialised LDS
+// atomics); after four such rounds the remaining lanes add one by one.
+__device__ __forceinline__ void hist_add_wave(unsigned* hist, unsigned bin, bool act) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long pend = __ballot(act);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (pend == 0) return;
+    const int lead = __builtin_ctzll(pend);
+    const unsigned lb = (unsigned)__builtin_amdgcn_readlane((int)bin, lead);
+    const unsigned long long same = __ballot(act && bin == lb);
+    if (lane == lead) atomicAdd(&hist[lb], (unsigned)__popcll(same));
+    act = act && bin != lb;
+    pend &= ~same;
+  }
+  if (act) atomicAdd(&hist[bin], 1u);
+}
+
+__device__ __forceinline__ int lanes_before(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
 // Radix-select step over a histogram in LDS: finds the bucket b (scanning from
 // the top) where the running count first reaches `need`; returns b and the
 // count strictly above it.  Block-parallel: each thread owns a run of
@@ -124,6 +148,7 @@ __device__ void find_bucket(const unsigned* hist, int nbins, unsigned need, int*
 }
 
 // ---------------------------------------------------------- anchor selection
+constexpr int kSelectLdsMaxL = 32768;   // pooled score in LDS up to this many positions (128 KB)
 // One 1024-thread block per (unit, head).  score -> pooled (width 7 window
 // sum over non-window positions) -> top k_s (radix select on the f32 bits,
 // ties to the lower position) -> k_u stratified picks over the remaining
@@ -154,22 +179,49 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
   const int tid = threadIdx.x, nt = blockDim.x;
 
   // pooled_t = score_{t-3} + ... + score_{t+3} over [0, L) (zeros outside,
-  // added in position order), from 1024-position chunks of the score
-  // staged with a 3-position halo
-  for (int t0 = 0; t0 < L; t0 += nt) {
-    for (int i = tid; i < nt + 6; i += nt) {
-      const int x = t0 - 3 + i;
-      stg[i] = (x >= 0 && x < L) ? sc[x] : 0.0f;
-    }
+  // added in position order)
+  if constexpr (LP) {
+    // whole score in LDS (all loads in flight at once), pooled values in
+    // registers, then written over it
+    static_assert(kSelectLdsMaxL % 1024 == 0, "per-thread slots");
+    constexpr int PER = kSelectLdsMaxL / 1024;
+    for (int t = tid; t < L; t += nt) pl[t] = sc[t];
     __syncthreads();
-    const int t = t0 + tid;
-    if (t < L) {
-      float v = 0.0f;
+    float pv[PER];
 #pragma unroll
-      for (int k = 0; k < 7; ++k) v += stg[tid + k];
-      pl[t] = v;
+    for (int k = 0; k < PER; ++k) {
+      const int t = tid + k * nt;
+      float v = 0.0f;
+      if (t < L)
+#pragma unroll
+        for (int j = 0; j < 7; ++j) {
+          const int x = t - 3 + j;
+          v += (x >= 0 && x < L) ? pl[x] : 0.0f;
+        }
+      pv[k] = v;
     }
     __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      if (tid + k * nt < L) pl[tid + k * nt] = pv[k];
+    __syncthreads();
+  } else {
+    // 1024-position chunks of the score staged with a 3-position halo
+    for (int t0 = 0; t0 < L; t0 += nt) {
+      for (int i = tid; i < nt + 6; i += nt) {
+        const int x = t0 - 3 + i;
+        stg[i] = (x >= 0 && x < L) ? sc[x] : 0.0f;
+      }
+      __syncthreads();
+      const int t = t0 + tid;
+      if (t < L) {
+        float v = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 7; ++k) v += stg[tid + k];
+        pl[t] = v;
+      }
+      __syncthreads();
+    }
   }
 
   // radix select of the k_s-th largest key (keys = f32 bits of non-negative values)
@@ -181,9 +233,10 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
       for (int b = tid; b < kHistBins; b += nt) hist[b] = 0;
       __syncthreads();
       const unsigned hmask = p == 0 ? 0u : (0xFFFFFFFFu << (shifts[p] + widths[p]));
-      for (int t = tid; t < L; t += nt) {
-        const unsigned key = __float_as_uint(pl[t]);
-        if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shifts[p]) & ((1u << widths[p]) - 1)], 1u);
+      for (int t0 = 0; t0 < L; t0 += nt) {  // wave-uniform trip count
+        const int t = t0 + tid;
+        const unsigned key = t < L ? __float_as_uint(pl[t]) : 0u;
+        hist_add_wave(hist, (key >> shifts[p]) & ((1u << widths[p]) - 1), t < L && (key & hmask) == (prefix & hmask));
       }
       __syncthreads();
       if (tid == 0) { s_b = 0; s_above = 0; }
@@ -195,28 +248,37 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
     }
   }
   const unsigned T_key = prefix;
-  // ordered compaction of the scored set: contiguous position ranges per thread
-  const int per = (L + nt - 1) / nt;
-  const int a0 = tid * per, a1 = min(L, a0 + per);
-  int ng = 0, nti = 0;
+  // ordered compaction of the scored set: each wave walks one contiguous range
+  // of positions 64 at a time, ranks from ballots
+  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  const int seg = (((L + nw - 1) / nw) + 63) & ~63;
+  const int s0 = min(L, wave * seg), s1 = min(L, s0 + seg);
+  int ng = 0, nti = 0;  // wave totals (uniform)
   if (k_s > 0)
-    for (int t = a0; t < a1; ++t) {
-      const unsigned key = __float_as_uint(pl[t]);
-      ng += key > T_key;
-      nti += key == T_key;
+    for (int t0 = s0; t0 < s1; t0 += 64) {
+      const int t = t0 + lane;
+      const unsigned key = t < s1 ? __float_as_uint(pl[t]) : 0u;
+      ng += __popcll(__ballot(t < s1 && key > T_key));
+      nti += __popcll(__ballot(t < s1 && key == T_key));
     }
   int tot;
-  const int tie_pre = block_excl_scan(nti, sh, &tot);
+  const int tie_pre = __builtin_amdgcn_readlane(block_excl_scan(lane == 0 ? nti : 0, sh, &tot), 0);
   // selected in this range: all greater + ties while tie rank < need
-  int take_ties = k_s > 0 ? max(0, min(nti, (int)need - tie_pre)) : 0;
-  const int sel_pre = block_excl_scan(k_s > 0 ? ng + take_ties : 0, sh, &tot);
+  const int take_ties = k_s > 0 ? max(0, min(nti, (int)need - tie_pre)) : 0;
+  const int sel_pre =
+      __builtin_amdgcn_readlane(block_excl_scan(lane == 0 && k_s > 0 ? ng + take_ties : 0, sh, &tot), 0);
   if (k_s > 0) {
     int o = sel_pre, tr = tie_pre;
-    for (int t = a0; t < a1; ++t) {
-      const unsigned key = __float_as_uint(pl[t]);
-      bool sel = key > T_key;
-      if (key == T_key) { sel = tr < (int)need; ++tr; }
-      if (sel) s_pos[o++] = t;
+    for (int t0 = s0; t0 < s1; t0 += 64) {
+      const int t = t0 + lane;
+      const unsigned key = t < s1 ? __float_as_uint(pl[t]) : 0u;
+      const bool tie = t < s1 && key == T_key;
+      const unsigned long long tm = __ballot(tie);
+      const bool sel = (t < s1 && key > T_key) || (tie && tr + lanes_before(tm) < (int)need);
+      const unsigned long long sm = __ballot(sel);
+      if (sel) s_pos[o + lanes_before(sm)] = t;
+      o += __popcll(sm);
+      tr += __popcll(tm);
     }
   }
   __syncthreads();
@@ -232,48 +294,83 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
     s_pos[k_s + i] = (int)(c + lo);
   }
   __syncthreads();
-  // merge scored (sorted) and uniform (sorted) into anchor order, then the window
+  // merge scored (sorted) and uniform (sorted) into anchor order (ranks by
+  // binary search, then written over s_pos once every read is done), then the
+  // window
   int* pos_out = reinterpret_cast<int*>(cache + (int64_t)u * stride + off_pos) + (int64_t)h * A;
-  for (int i = tid; i < k_s + k_u; i += nt) {
-    const int v = s_pos[i];
-    int rank;
-    if (i < k_s) {  // count uniform picks below v
-      int lo = 0, hi = k_u;
-      while (lo < hi) { int mid = (lo + hi) >> 1; if (s_pos[k_s + mid] < v) lo = mid + 1; else hi = mid; }
-      rank = i + lo;
-    } else {
-      int lo = 0, hi = k_s;
-      while (lo < hi) { int mid = (lo + hi) >> 1; if (s_pos[mid] < v) lo = mid + 1; else hi = mid; }
-      rank = (i - k_s) + lo;
+  {
+    int mv[4], mr[4];  // k_s + k_u < 4096 = 4 per thread
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + k * nt;
+      mv[k] = -1;
+      mr[k] = 0;
+      if (i < k_s + k_u) {
+        const int v = s_pos[i];
+        int rank;
+        if (i < k_s) {  // count uniform picks below v
+          int lo = 0, hi = k_u;
+          while (lo < hi) { int mid = (lo + hi) >> 1; if (s_pos[k_s + mid] < v) lo = mid + 1; else hi = mid; }
+          rank = i + lo;
+        } else {
+          int lo = 0, hi = k_s;
+          while (lo < hi) { int mid = (lo + hi) >> 1; if (s_pos[mid] < v) lo = mid + 1; else hi = mid; }
+          rank = (i - k_s) + lo;
+        }
+        mv[k] = v;
+        mr[k] = rank;
+      }
     }
-    pos_out[rank] = v;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (mv[k] >= 0) s_pos[mr[k]] = mv[k];
+    for (int i = tid; i < W; i += nt) s_pos[k_s + k_u + i] = L + i;
   }
-  for (int i = tid; i < W; i += nt) pos_out[k_s + k_u + i] = L + i;
   int* ao = anchor_of + uh * N;
   for (int t = tid; t < N; t += nt) ao[t] = -1;
-  __syncthreads();  // global writes of pos_out visible to the block
+  __syncthreads();  // s_pos in anchor order; ao cleared (block-visible)
   __threadfence_block();
-  for (int i = tid; i < A; i += nt) ao[pos_out[i]] = i;
-  // copy anchor rows and their norms (one wave per anchor)
-  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  for (int i = tid; i < A; i += nt) {
+    pos_out[i] = s_pos[i];
+    ao[s_pos[i]] = i;
+  }
+  // copy anchor rows and their norms: 16-byte chunks, 64/CPR rows per wave
+  // instruction, the row's lanes summed by a DPP row reduction
+  constexpr int CPR = D * (int)sizeof(T) / 16;   // chunks per row: 16 (bf16) or 32 (f32)
+  constexpr int RPW = 64 / CPR;
+  constexpr int EPC = 16 / (int)sizeof(T);       // elements per chunk
+  const int rsub = lane / CPR, ch = lane % CPR;
   const T* Kp = reinterpret_cast<const T*>(Kv) + uh * N * D;
   const T* Vp = reinterpret_cast<const T*>(Vv) + uh * N * D;
   T* AK = reinterpret_cast<T*>(cache + (int64_t)u * stride + off_ak) + (int64_t)h * A * D;
   T* AV = reinterpret_cast<T*>(cache + (int64_t)u * stride + off_av) + (int64_t)h * A * D;
-  for (int i = wave; i < A; i += nw) {
-    const int t = pos_out[i];
+  for (int i0 = wave * RPW; i0 < A; i0 += nw * RPW) {
+    const int i = i0 + rsub;
     float sk = 0.0f, sv = 0.0f;
-    for (int d = lane; d < D; d += 64) {
-      const T xk = Kp[(int64_t)t * D + d], xv = Vp[(int64_t)t * D + d];
-      AK[(int64_t)i * D + d] = xk;
-      AV[(int64_t)i * D + d] = xv;
-      const float fk = Elem<DT>::f(xk), fv = Elem<DT>::f(xv);
-      sk = fmaf(fk, fk, sk);
-      sv = fmaf(fv, fv, sv);
+    if (i < A) {
+      const int t = s_pos[i];
+      const uint4 xk = *reinterpret_cast<const uint4*>(Kp + (int64_t)t * D + ch * EPC);
+      const uint4 xv = *reinterpret_cast<const uint4*>(Vp + (int64_t)t * D + ch * EPC);
+      *reinterpret_cast<uint4*>(AK + (int64_t)i * D + ch * EPC) = xk;
+      *reinterpret_cast<uint4*>(AV + (int64_t)i * D + ch * EPC) = xv;
+      T ek[EPC], ev[EPC];
+      __builtin_memcpy(ek, &xk, 16);
+      __builtin_memcpy(ev, &xv, 16);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float fk = Elem<DT>::f(ek[e]), fv = Elem<DT>::f(ev[e]);
+        sk = fmaf(fk, fk, sk);
+        sv = fmaf(fv, fv, sv);
+      }
     }
-    sk = wave_sum(sk);
-    sv = wave_sum(sv);
-    if (lane == 0) {
+    sk = row_sum(sk);
+    sv = row_sum(sv);
+    if constexpr (CPR == 32) {  // rows of 32 lanes: add the other half-row
+      sk += __shfl_xor(sk, 16, 64);
+      sv += __shfl_xor(sv, 16, 64);
+    }
+    if (i < A && ch == 0) {
       anorm[((int64_t)u * 2 * H + h) * A + i] = make_float2(sk, sk > 0.0f ? 1.0f / sqrtf(sk) : 0.0f);
       anorm[((int64_t)u * 2 * H + H + h) * A + i] = make_float2(sv, sv > 0.0f ? 1.0f / sqrtf(sv) : 0.0f);
     }
@@ -924,7 +1021,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
           p.off_anchor_v, p.off_positions, reinterpret_cast<int*>(ws + w.anchor_of),
           reinterpret_cast<float2*>(ws + w.anorm), H, N, p.window, p.k_scored, p.k_uniform, A);
     };
-    if (plb <= 128 * 1024) {
+    if (N - p.window <= kSelectLdsMaxL) {
       static size_t sdone = 0;
       if ((rc = set_dyn_lds(reinterpret_cast<const void*>(&k_select<DT, true>), plb, &sdone))) return rc;
       sel(k_select<DT, true>, plb);
