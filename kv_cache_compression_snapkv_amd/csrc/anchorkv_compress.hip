@@ -58,8 +58,19 @@ __global__ void k_o_combine(const float* part, float* o, uint16_t* ohl, float* o
   const int q = (int)(row % GQp);
   const int64_t uh = row / GQp;
   const int d = threadIdx.x;
-  float v = 0.0f;
-  for (int s = 0; s < S1; ++s) v += part[((uh * S1 + s) * GQp + q) * kHeadDim + d];
+  // the partials are added in split order; with several splits their loads
+  // are issued 8 at a time
+  const float* pp = part + (uh * S1 * GQp + q) * kHeadDim + d;
+  const int64_t ps = (int64_t)GQp * kHeadDim;
+  float v = pp[0];
+  for (int s0 = 1; s0 < S1; s0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = s0 + k < S1 ? pp[(s0 + k) * ps] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < S1) v += x[k];
+  }
   o[row * kHeadDim + d] = v;
   const uint16_t hi = f2bf(v);
   const uint16_t lo = f2bf(v - bf2f(hi));

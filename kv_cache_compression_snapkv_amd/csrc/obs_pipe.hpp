@@ -407,7 +407,7 @@ __global__ __launch_bounds__(KS == 1 ? 512 : 768) __attribute__((amdgpu_waves_pe
         if constexpr (HAS_G) {
           if constexpr (QAT) {
             const int qcol = (qw + qi * nq) * 16 + col;
-            for (int r = 0; r < 4; ++r) accg[r] = qa_tab[Ai[it * TK + kb * 16 + kg * 4 + r] * a.GQp + qcol];
+            for (int r = 0; r < 4; ++r) accg[r] = qa_tab[__umul24(Ai[it * TK + kb * 16 + kg * 4 + r], a.GQp) + qcol];  // index < 2^15, GQp <= 256
           } else {
             for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf[st], qf[qi][st], accg);
           }
