@@ -404,7 +404,7 @@ template <int DT> struct AssignCfg {
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_assign(const void* Kv, const void* Vv, uint8_t* cache, int64_t stride,
-                                               int64_t off_ak, int64_t off_av, int64_t off_words,
+                                               int64_t off_ak, int64_t off_av,
                                                const float2* anorm, const int* anchor_of, int* aidx, float* gam,
                                                float* rn2, float* vn2, const float* score, float* util, int H, int N,
                                                int A, int ntiles) {
@@ -540,8 +540,6 @@ __global__ __launch_bounds__(256) void k_assign(const void* Kv, const void* Vv, 
         vn2[uh * N + t] = xx;
         util[i] = is_anchor ? -1.0f : score[uh * N + t] * sqrtf(r2);
       }
-      uint32_t* words = reinterpret_cast<uint32_t*>(cache + (int64_t)u * stride + off_words);
-      words[((int64_t)h * N + t) * 2 + side] = (uint32_t)a | ((uint32_t)f2h_sat(g) << 16);
     }
   }
 }
@@ -555,10 +553,11 @@ __global__ __launch_bounds__(256) void k_assign(const void* Kv, const void* Vv, 
 //    are taken; then the counts of keys > T and == T of every group of 1024
 //    positions (flat head*N + t order) and their exclusive scans give each
 //    group's record base and tie base;
-//  k_topr_flag, one wave per group: flags the selected tokens in position
-//    order (ballot prefix counts), writes each record's position to the record
-//    list and, at every 1024-token chunk start of a head, the number of
-//    records before it (the chunk's residual offset).
+//  k_topr_flag, one wave per group: selects tokens in position order (ballot
+//    prefix counts), writes every token's pointer word (anchor index, residual
+//    flag, fp16 gamma: plain stores, no read-modify-write), each record's
+//    position to the record list and, at every 1024-token chunk start of a
+//    head, the number of records before it (the chunk's residual offset).
 __device__ __forceinline__ unsigned util_key(float v) { return v >= 0.0f ? __float_as_uint(v) + 1u : 0u; }
 
 constexpr int kToprThreads = 1024;
@@ -756,9 +755,11 @@ __global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsi
       const unsigned iu = (unsigned)i;   // H*N < 2^31
       const int h = (int)(iu / (unsigned)N), t = (int)(iu - (unsigned)h * (unsigned)N);
       if ((t & (kChunk - 1)) == 0) chunk[h * C + t / kChunk] = (int)rec;
-      if (sel && rec < (unsigned)R) {
-        // no-return atomic OR: a read-modify-write would wait for the load
-        atomicOr(&words[((int64_t)h * N + t) * 2 + side], 0x8000u);
+      const bool taken = sel && rec < (unsigned)R;
+      // the token's pointer word: anchor index, residual flag, fp16 gamma
+      words[((int64_t)h * N + t) * 2 + side] =
+          (uint32_t)av[k] | (taken ? 0x8000u : 0u) | ((uint32_t)f2h_sat(gv[k]) << 16);
+      if (taken) {
         sel_list[(int64_t)us * Rmax + rec] = h * N + t;
         // the record's anchor and coefficient, so that the quantiser's loads
         // do not wait on the position first
@@ -910,7 +911,7 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
   g.K = reinterpret_cast<const uint16_t*>(K);
   g.V = reinterpret_cast<const uint16_t*>(V);
   g.cache = cache; g.stride = p.unit_stride;
-  g.off_anchor_k = p.off_anchor_k; g.off_anchor_v = p.off_anchor_v; g.off_words = p.off_words;
+  g.off_anchor_k = p.off_anchor_k; g.off_anchor_v = p.off_anchor_v;
   g.anorm = reinterpret_cast<const float2*>(ws + w.anorm);
   g.anchor_of = oa.anchor_of;
   g.aidx = reinterpret_cast<int*>(ws + w.aidx);
@@ -1048,7 +1049,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   } else {
     const int ntiles = (N + 255) / 256;
     k_assign<DT><<<(unsigned)((int64_t)U * 2 * H * ntiles), 256, 0, st>>>(
-        K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_words,
+        K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v,
         reinterpret_cast<const float2*>(ws + w.anorm), a.anchor_of, reinterpret_cast<int*>(ws + w.aidx),
         reinterpret_cast<float*>(ws + w.gam), reinterpret_cast<float*>(ws + w.rn2), reinterpret_cast<float*>(ws + w.vn2),
         a.score, a.util, H, N, A, ntiles);

@@ -55,7 +55,7 @@ struct AssignArgs {
   const uint16_t* K;
   const uint16_t* V;
   uint8_t* cache;
-  int64_t stride, off_anchor_k, off_anchor_v, off_words;
+  int64_t stride, off_anchor_k, off_anchor_v;
   const float2* anorm;       // [U][2][H][A] (||x_a||^2, 1/||x_a|| or 0)
   const int* anchor_of;      // [U][H][N]
   int* aidx;                 // [U][2][H][N]
@@ -124,8 +124,6 @@ __device__ __forceinline__ void assign_project(const AssignArgs& g, int u, int s
     g.aidx[i] = a;
     g.gam[i] = gm;
     g.rn2[i] = r2;
-    uint32_t* words = reinterpret_cast<uint32_t*>(g.cache + (int64_t)u * g.stride + g.off_words);
-    words[((int64_t)h * g.N + t) * 2 + side] = (uint32_t)a | ((uint32_t)f2h_sat(gm) << 16);
     if (side == 1) {
       // value channel of the utility: score_t ||r_V|| (anchors ineligible)
       g.vn2[uh * g.N + t] = xx;
