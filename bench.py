@@ -312,6 +312,14 @@ def main():
                    "note": "cache fits the 256 MB Infinity Cache" if dec_b < 256e6 else "HBM-resident"},
         "stages_ms": stage_ms,
         "roofline": rl,
+        # each main stage against its own roofline (the contraction of the
+        # assignment also against the bf16 MFMA peak, whatever bounds it)
+        "stage_roofline": {k: {"bound": r["bound"], "frac": r["frac"]}
+                           for k in ("obs_stats", "obs_score", "assign", "obs_util", "dec_stream") if k in stage_ms
+                           for r in [roofline(p, k, stage_ms[k])]},
+        "assign_mfma_frac": (stage_work(p, "assign")[0] / (stage_ms["assign"] * 1e-3)
+                             / ((PEAK_BF16_TFLOPS if p.dtype == 1 else PEAK_F32_MFMA_TFLOPS) * 1e12)
+                             if "assign" in stage_ms else None),
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
