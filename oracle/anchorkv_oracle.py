@@ -464,6 +464,24 @@ def decode_unit(c: Compressed, q):
     return o
 
 
+def decode_unit_tail(c: Compressed, q, K_tail, V_tail):
+    """Decode attention over the compressed cache of one unit followed by a
+    tail of tokens appended after the one-shot compression and kept exact
+    (AnchorKV-adapted page, "Adaptation notes": tokens produced during decode
+    are appended at full precision and never re-anchored).  One softmax per
+    q-head over the N reconstructed tokens and the tail of its KV head.
+    q: [H*G, D]; K_tail, V_tail: [H, T, D] float64, T >= 0.  Returns o [H*G, D]."""
+    Kh, Vh = reconstruct(c)
+    H = Kh.shape[0]
+    G = c.G
+    o = np.zeros_like(q)
+    for h in range(H):
+        K = np.concatenate([Kh[h], K_tail[h]], axis=0)
+        V = np.concatenate([Vh[h], V_tail[h]], axis=0)
+        o[h * G:(h + 1) * G] = attention(q[h * G:(h + 1) * G], K, V)
+    return o
+
+
 # --------------------------------------------------------------------------
 # Theorem 1 output-error bound [Pith, "What carries the argument" and
 # "Referee Report" (E_K = 2 V_max tanh(mu), mu = ||q|| Delta_K / sqrt(D),

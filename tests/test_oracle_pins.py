@@ -376,6 +376,39 @@ def test_all_anchor_cache_is_exact_attention():
         np.testing.assert_allclose(o[h * G:(h + 1) * G], O.attention(q[h * G:(h + 1) * G], K[h], V[h]), rtol=1e-12)
 
 
+def test_decode_tail_pins():
+    """Decode with an exact tail appended after compression: an empty tail is
+    plain decode; with every token an anchor it is attention over the
+    concatenated sequence (library routine); a tail key aligned with the query
+    and far larger than the rest takes the whole softmax."""
+    r = rng(15)
+    H, G, N, D, T = 2, 3, 96, 32, 7
+    K = bf16_exact(clustered(r, H, N, D))
+    V = bf16_exact(r.standard_normal((H, N, D)))
+    Q = bf16_exact(r.standard_normal((H * G, 8, D)))
+    q = bf16_exact(r.standard_normal((H * G, D)))
+    Kt = bf16_exact(r.standard_normal((H, T, D)))
+    Vt = bf16_exact(r.standard_normal((H, T, D)))
+    c = O.compress_unit(K, V, Q, G, 8, 0.2, 8, 2)
+    np.testing.assert_array_equal(O.decode_unit_tail(c, q, Kt[:, :0], Vt[:, :0]), O.decode_unit(c, q))
+    # all anchors: exact attention over [K; K_tail]
+    ca = O.compress_unit(K, V, Q, G, 8, 1.5, N, 2)
+    assert ca.plan.A == N
+    o = O.decode_unit_tail(ca, q, Kt, Vt)
+    for h in range(H):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[h * G:(h + 1) * G])[None], torch.from_numpy(np.concatenate([K[h], Kt[h]]))[None],
+            torch.from_numpy(np.concatenate([V[h], Vt[h]]))[None])
+        np.testing.assert_allclose(o[h * G:(h + 1) * G], ref[0].numpy(), rtol=1e-11, atol=1e-12)
+    # one dominant tail key per head (aligned with the head's first query)
+    Kd = Kt.copy()
+    for h in range(H):
+        Kd[h, 3] = 400.0 * q[h * G] / np.linalg.norm(q[h * G])
+    o = O.decode_unit_tail(c, q, Kd, Vt)
+    for h in range(H):
+        np.testing.assert_allclose(o[h * G], Vt[h, 3], rtol=1e-9, atol=1e-9)
+
+
 def test_theorem1_bound_holds():
     """Pith, "What carries the argument": ||y - y^|| <= attention-weighted
     value error + 2 V_max tanh(||q|| Delta_K / sqrt(D)); both the a^- and
