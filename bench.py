@@ -80,6 +80,32 @@ def roofline(p, stage, ms):
             "frac": (flops / s / 1e12) / peak_f, "algorithmic_flops": flops}
 
 
+def measure_tail(akv, w, p, cache, q, o, dws, stream, n_tail, reps=5):
+    """Decode over the compressed cache plus an exact tail of n_tail tokens per
+    KV head (outside the timed steps): the stream part and the tail part
+    (tail kernel + merge) separately, HIP events, median of reps.  The tail
+    part reads the tail keys and values once: 2*U*H*n_tail*D*e bytes."""
+    import torch
+    g = torch.Generator(device=o.device).manual_seed(0xA7C4)
+    shape = (w.units, w.kv_heads, n_tail, w.head_dim)
+    Kt = torch.randn(shape, generator=g, device=o.device).to(w.torch_dtype)
+    Vt = torch.randn(shape, generator=g, device=o.device).to(w.torch_dtype)
+    akv.decode_attn_tail(p, cache, q, Kt, Vt, n_tail, o, dws, stream)
+    torch.cuda.synchronize()
+    akv.profile_enable(True)
+    akv.profile_read()
+    for _ in range(reps):
+        akv.decode_attn_tail(p, cache, q, Kt, Vt, n_tail, o, dws, stream)
+    torch.cuda.synchronize()
+    st = akv.profile_read()
+    akv.profile_enable(False)
+    tail_ms = sorted(ms for n, ms in st if n == "dec_tail")[reps // 2]
+    stream_ms = sorted(ms for n, ms in st if n == "dec_stream")[reps // 2]
+    tb = 2 * w.units * w.kv_heads * n_tail * w.head_dim * p.elem_bytes
+    return {"n_tail": n_tail, "stream_us": stream_ms * 1e3, "tail_us": tail_ms * 1e3, "tail_bytes": tb,
+            "tail_GB_s": tb / (tail_ms * 1e-3) / 1e9, "tail_hbm_frac": tb / (tail_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle as it stands, on the host cores: compress + one decode step
     for a bounded sample of units, extrapolated to the workload's tokens/s."""
@@ -197,6 +223,8 @@ def main():
     ap.add_argument("--workload", default="llama3b_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1, help="decode steps per step (default 1)")
+    ap.add_argument("--tail", type=int, default=1024,
+                    help="tokens of the exact tail in the separate decode-with-tail measurement (0: skip)")
     ap.add_argument("--copy-probe", action="store_true", help="run only the traffic-counter calibration copy")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from four rocprofv3 --pmc csv folders")
@@ -256,6 +284,7 @@ def main():
     t1 = time.perf_counter()
     stages = akv.profile_read()
     akv.profile_enable(False)
+    tail_rec = measure_tail(akv, w, p, cache, qs[0], o, dws, stream, args.tail) if args.tail > 0 else None
     total_s = t1 - t0
     ms_per_step = total_s * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
@@ -311,6 +340,7 @@ def main():
                    "hbm_frac": dec_b / (decode_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                    "note": "cache fits the 256 MB Infinity Cache" if dec_b < 256e6 else "HBM-resident"},
         "stages_ms": stage_ms,
+        "decode_tail": tail_rec,
         "roofline": rl,
         # each main stage against its own roofline (the contraction of the
         # assignment also against the bf16 MFMA peak, whatever bounds it)

@@ -167,6 +167,23 @@ int anchorkv_workspace_offsets(const anchorkv_plan_info* plan, int64_t out[8]);
 int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, const void* q, float* o,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode attention over the compressed cache followed by a tail of tokens
+ * appended after the one-shot compression and kept uncompressed
+ * (AnchorKV-adapted page, "Adaptation notes": tokens produced during decode
+ * are appended at full precision and never re-anchored).  Each q-head takes
+ * one softmax over the N compressed tokens and the n_tail tail tokens of its
+ * KV head.
+ *  K_tail, V_tail: device, [units][H][tail_cap][D], cache dtype, 16-byte
+ *           aligned; rows [0, n_tail) of every head are read.  The same n_tail
+ *           applies to every unit.  May be null when n_tail = 0.
+ *  n_tail = 0 runs exactly the launches of anchorkv_decode_attn.
+ *  The other arguments are those of anchorkv_decode_attn (same workspace).
+ * Errors: E_ARG (null or misaligned buffers, n_tail < 0, n_tail > tail_cap),
+ *         E_SMALL_BUFFER, E_HIP. */
+int anchorkv_decode_attn_tail(const anchorkv_plan_info* plan, const void* cache, const void* q, const void* K_tail,
+                              const void* V_tail, int32_t n_tail, int32_t tail_cap, float* o, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Host-side view of one unit's compressed representation, as plain arrays.
  * All pointers are host memory owned by the caller. */
 typedef struct {

@@ -2,11 +2,14 @@
 
 compress: end-of-prefill compression of K/V into anchors + (index, gamma)
 pointers + 2-bit residual records; decode_attn: attention over the compressed
-cache without reconstructing it.  Both run in hand-written HIP kernels behind
+cache without reconstructing it; decode_attn_tail: the same plus an exact tail
+of tokens appended after compression.  Both run in hand-written HIP kernels behind
 the C ABI in include/anchorkv.h; this package only marshals arguments.
 """
-from .binding import (BF16, F32, AnchorKVError, PlanInfo, alloc, compress, decode_attn, lib, pack_unit, plan,
-                      plan_from_header, profile_enable, profile_read, unpack_unit, version, workspace_offsets)
+from .binding import (BF16, F32, AnchorKVError, PlanInfo, alloc, compress, decode_attn, decode_attn_tail, lib,
+                      pack_unit, plan, plan_from_header, profile_enable, profile_read, unpack_unit, version,
+                      workspace_offsets)
 
-__all__ = ["BF16", "F32", "AnchorKVError", "PlanInfo", "alloc", "compress", "decode_attn", "lib", "pack_unit", "plan",
-           "plan_from_header", "profile_enable", "profile_read", "unpack_unit", "version", "workspace_offsets"]
+__all__ = ["BF16", "F32", "AnchorKVError", "PlanInfo", "alloc", "compress", "decode_attn", "decode_attn_tail", "lib",
+           "pack_unit", "plan", "plan_from_header", "profile_enable", "profile_read", "unpack_unit", "version",
+           "workspace_offsets"]

@@ -78,6 +78,9 @@ def lib():
         L.anchorkv_workspace_offsets.argtypes = [ct.POINTER(PlanInfo), ct.POINTER(ct.c_int64)]
         L.anchorkv_decode_attn.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                            ct.c_size_t, ct.c_void_p]
+        L.anchorkv_decode_attn_tail.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                                ct.c_void_p, ct.c_int32, ct.c_int32, ct.c_void_p, ct.c_void_p,
+                                                ct.c_size_t, ct.c_void_p]
         L.anchorkv_unit_pack_host.argtypes = [ct.POINTER(PlanInfo), ct.POINTER(UnitArrays), ct.c_void_p]
         L.anchorkv_unit_unpack_host.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.POINTER(UnitArrays)]
         L.anchorkv_profile_enable.argtypes = [ct.c_int]
@@ -88,7 +91,8 @@ def lib():
 
 
 EXPORTED = ["anchorkv_version", "anchorkv_last_error", "anchorkv_plan", "anchorkv_plan_from_header",
-            "anchorkv_compress", "anchorkv_workspace_offsets", "anchorkv_decode_attn", "anchorkv_unit_pack_host",
+            "anchorkv_compress", "anchorkv_workspace_offsets", "anchorkv_decode_attn", "anchorkv_decode_attn_tail",
+            "anchorkv_unit_pack_host",
             "anchorkv_unit_unpack_host", "anchorkv_profile_enable", "anchorkv_profile_read"]
 
 
@@ -153,6 +157,20 @@ def decode_attn(p: PlanInfo, cache, q, o, workspace, stream=None):
             raise ValueError("decode_attn: inputs must be contiguous device tensors")
     _check(lib().anchorkv_decode_attn(ct.byref(p), _ptr(cache), _ptr(q), _ptr(o), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream)))
+
+
+def decode_attn_tail(p: PlanInfo, cache, q, K_tail, V_tail, n_tail: int, o, workspace, stream=None):
+    """Enqueue decode attention over the compressed cache plus an exact tail:
+    K_tail, V_tail [U, H, tail_cap, D] cache dtype (rows [0, n_tail) used);
+    q [U, H*G, D] cache dtype -> o [U, H*G, D] float32."""
+    for t in (cache, q, o, workspace, K_tail, V_tail):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("decode_attn_tail: inputs must be contiguous device tensors")
+    if K_tail.shape != V_tail.shape or K_tail.dim() != 4:
+        raise ValueError("decode_attn_tail: K_tail and V_tail must share a [U, H, tail_cap, D] shape")
+    _check(lib().anchorkv_decode_attn_tail(ct.byref(p), _ptr(cache), _ptr(q), _ptr(K_tail), _ptr(V_tail),
+                                           int(n_tail), int(K_tail.shape[2]), _ptr(o), _ptr(workspace),
+                                           _nbytes(workspace), _stream(stream)))
 
 
 def alloc(p: PlanInfo, device):

@@ -63,6 +63,7 @@ struct DecArgs {
   float* part_acc;   // [U][H][S2][G][D] unnormalised output of each range (S2 > 1)
   float* o;          // [U][H][G][D]
   int H, N, A, C, S2, cps, R_K, R_V;
+  int force_part;    // publish partials even with one range (a tail follows)
   float c;
 };
 
@@ -751,7 +752,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const int g = 4 * kg + r;
     val[r] = g < G ? ov[r] + accs[g * D + d] + zt_s[g * 4 + d / 32] : 0.0f;
   }
-  if (a.S2 == 1) {
+  if (a.S2 == 1 && !a.force_part) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int g = 4 * kg + r;
@@ -769,15 +770,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   if (threadIdx.x < G) a.part_ml[ps * G + threadIdx.x] = make_float2(ml_s[0][threadIdx.x], ml_s[1][threadIdx.x]);
 }
 
-// Per (unit, head) with several token ranges: o = sum_s f_s acc_s / sum_s f_s l_s
-// with f_s = 2^(m_s - max m).  One thread per (q-head, coordinate).
-__global__ __launch_bounds__(256) void k_dec_merge(const float2* part_ml, const float* part_acc, float* o, int G,
-                                                  int S2) {
+// Per (unit, head) with several token ranges (and an optional tail partial):
+// o = sum_s f_s acc_s / sum_s f_s l_s with f_s = 2^(m_s - max m).  One thread
+// per (q-head, coordinate).
+__global__ __launch_bounds__(256) void k_dec_merge(const float2* part_ml, const float* part_acc, const float2* tail_ml,
+                                                  const float* tail_acc, float* o, int G, int S2, int St) {
   const int64_t uh = blockIdx.x;
   for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) {
     const int g = i / kHeadDim, d = i % kHeadDim;
     float M = -INFINITY;
     for (int s = 0; s < S2; ++s) M = fmaxf(M, part_ml[(uh * S2 + s) * G + g].x);
+    for (int s = 0; s < St; ++s) M = fmaxf(M, tail_ml[(uh * St + s) * G + g].x);
     float L = 0.0f, acc = 0.0f;
     for (int s = 0; s < S2; ++s) {
       const float2 v = part_ml[(uh * S2 + s) * G + g];
@@ -785,8 +788,111 @@ __global__ __launch_bounds__(256) void k_dec_merge(const float2* part_ml, const 
       L += f * v.y;
       acc = fmaf(f, part_acc[((uh * S2 + s) * G + g) * kHeadDim + d], acc);
     }
+    for (int s = 0; s < St; ++s) {
+      const float2 v = tail_ml[(uh * St + s) * G + g];
+      const float f = v.x == -INFINITY ? 0.0f : exp2_fast(v.x - M);
+      L += f * v.y;
+      acc = fmaf(f, tail_acc[((uh * St + s) * G + g) * kHeadDim + d], acc);
+    }
     o[(uh * G + g) * kHeadDim + d] = acc / L;
   }
+}
+
+// Exact tail of one (unit, KV head): tokens appended after the one-shot
+// compression and kept at the cache's element type (AnchorKV-adapted page,
+// "Adaptation notes").  Workgroup s of the head takes tail range s (whole
+// 64-token tiles).  Per tile: the value rows are staged in LDS with 16-byte
+// loads; lane (token j, quarter) of wave w dots a quarter of key row 16w + j
+// with every q-head (quad sums), wave 0 raises the running maxima and turns
+// the logits (c <q, k>, log2 domain) into probabilities, and thread
+// (half, d) adds p v for coordinate d of q-heads half, half + 2, ...  Writes
+// the range's (max, sum, unnormalised output) partial for k_dec_merge.
+template <int DT>
+__global__ __launch_bounds__(256) void k_dec_tail(const void* q, const void* Kt, const void* Vt, int n_tail,
+                                                 int tail_cap, int G, int St, float c, float2* tml, float* tacc) {
+  using T = typename Elem<DT>::T;
+  constexpr int D = kHeadDim, TT = 64, EPC = 16 / (int)sizeof(T), CPR = D / EPC;
+  __shared__ float qs[kMaxG][D];
+  __shared__ __align__(16) T vs[TT][D];
+  __shared__ float ps[kMaxG][TT];
+  __shared__ float fr[kMaxG], mrun[kMaxG], lrun[kMaxG];
+  const int s = blockIdx.x % St;
+  const int64_t uh = blockIdx.x / St;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int span = ((n_tail + St - 1) / St + TT - 1) / TT * TT;
+  const int t_beg = min(n_tail, s * span), t_end = min(n_tail, t_beg + span);
+  const T* qp = reinterpret_cast<const T*>(q) + uh * G * D;
+  for (int i = tid; i < G * D; i += 256) qs[i / D][i % D] = Elem<DT>::f(qp[i]);
+  if (tid < kMaxG) { mrun[tid] = -INFINITY; lrun[tid] = 0.0f; }
+  const T* Kp = reinterpret_cast<const T*>(Kt) + uh * (int64_t)tail_cap * D;
+  const T* Vp = reinterpret_cast<const T*>(Vt) + uh * (int64_t)tail_cap * D;
+  const int d = tid & (D - 1), half = tid >> 7;
+  const int jt = 16 * wave + (lane >> 2), qq = lane & 3;   // logit lanes: token, quarter of the row
+  float acc[kMaxG / 2];
+#pragma unroll
+  for (int k = 0; k < kMaxG / 2; ++k) acc[k] = 0.0f;
+  __syncthreads();
+  for (int t0 = t_beg; t0 < t_end; t0 += TT) {
+    const int nt = min(TT, t_end - t0);
+    for (int i = tid; i < TT * CPR; i += 256) {
+      const int r = i / CPR, ch = i % CPR;
+      *reinterpret_cast<uint4*>(&vs[r][ch * EPC]) =
+          r < nt ? *reinterpret_cast<const uint4*>(Vp + (int64_t)(t0 + r) * D + ch * EPC) : make_uint4(0, 0, 0, 0);
+    }
+    float sg[kMaxG];
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g) sg[g] = 0.0f;
+    if (jt < nt) {
+      const T* kr = Kp + (int64_t)(t0 + jt) * D + 32 * qq;
+#pragma unroll
+      for (int c0 = 0; c0 < 32; c0 += EPC) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(kr + c0);
+        T kv[EPC];
+        __builtin_memcpy(kv, &raw, 16);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const float kf = Elem<DT>::f(kv[e]);
+#pragma unroll
+          for (int g = 0; g < kMaxG; ++g)
+            if (g < G) sg[g] = fmaf(qs[g][32 * qq + c0 + e], kf, sg[g]);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g)
+      if (g < G) {
+        const float v = quad_sum(sg[g]);
+        if (qq == 0) ps[g][jt] = jt < nt ? v * c : -INFINITY;
+      }
+    __syncthreads();
+    if (wave == 0) {
+      for (int g = 0; g < G; ++g) {
+        const float x = ps[g][lane];
+        const float mn = fmaxf(mrun[g], wave_max(x));
+        const float f = mrun[g] == -INFINITY ? 0.0f : exp2_fast(mrun[g] - mn);
+        const float p = lane < nt ? exp2_fast(x - mn) : 0.0f;
+        ps[g][lane] = p;
+        const float sum = wave_sum(p);
+        if (lane == 0) { fr[g] = f; lrun[g] = fmaf(lrun[g], f, sum); mrun[g] = mn; }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxG / 2; ++k) {
+      const int g = half + 2 * k;
+      if (g < G) {
+        float a = acc[k] * fr[g];
+        for (int t = 0; t < nt; ++t) a = fmaf(ps[g][t], Elem<DT>::f(vs[t][d]), a);
+        acc[k] = a;
+      }
+    }
+    __syncthreads();   // vs, ps, fr are rewritten by the next tile
+  }
+  const int64_t slot = uh * St + s;
+  if (tid < G) tml[slot * G + tid] = make_float2(mrun[tid], lrun[tid]);
+#pragma unroll
+  for (int k = 0; k < kMaxG / 2; ++k)
+    if (half + 2 * k < G) tacc[(slot * G + half + 2 * k) * D + d] = acc[k];
 }
 
 // Raise a kernel's dynamic-LDS limit to `bytes` (once per larger value).
@@ -838,7 +944,8 @@ static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
 
 template <int DT>
 static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const void* q, float* o, void* ws_v,
-                       hipStream_t st) {
+                       hipStream_t st, const void* K_tail = nullptr, const void* V_tail = nullptr, int n_tail = 0,
+                       int tail_cap = 0) {
   const uint8_t* cache = reinterpret_cast<const uint8_t*>(cache_v);
   uint8_t* ws = reinterpret_cast<uint8_t*>(ws_v);
   const DecodeWs w = decode_ws_layout(p);
@@ -858,6 +965,7 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   a.H = H; a.N = p.N; a.A = A; a.C = p.n_chunks; a.S2 = S2; a.cps = (p.n_chunks + S2 - 1) / S2;
   a.c = kLog2e / sqrtf((float)kHeadDim);
   a.R_K = p.R_K; a.R_V = p.R_V;
+  a.force_part = n_tail > 0 ? 1 : 0;
   const unsigned grid = (unsigned)((int64_t)U * H * S2);
   int rc = 0;
   switch (G) {
@@ -871,8 +979,20 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
     default: rc = launch_stream<DT, 8>(a, grid, st); break;
   }
   if (rc) return rc;
+  if (n_tail > 0) {
+    prof_mark(st, "dec_stream");
+    float2* tml = reinterpret_cast<float2*>(ws + w.tail_ml);
+    float* tacc = reinterpret_cast<float*>(ws + w.tail_acc);
+    k_dec_tail<DT><<<(unsigned)((int64_t)U * H * w.St), 256, 0, st>>>(q, K_tail, V_tail, n_tail, tail_cap, G, w.St,
+                                                                        a.c, tml, tacc);
+    AKV_CHECK_LAUNCH("k_dec_tail");
+    k_dec_merge<<<(unsigned)((int64_t)U * H), 256, 0, st>>>(a.part_ml, a.part_acc, tml, tacc, o, G, S2, w.St);
+    AKV_CHECK_LAUNCH("k_dec_merge");
+    prof_mark(st, "dec_tail");
+    return 0;
+  }
   if (S2 > 1) {
-    k_dec_merge<<<(unsigned)((int64_t)U * H), 256, 0, st>>>(a.part_ml, a.part_acc, o, G, S2);
+    k_dec_merge<<<(unsigned)((int64_t)U * H), 256, 0, st>>>(a.part_ml, a.part_acc, nullptr, nullptr, o, G, S2, 0);
     AKV_CHECK_LAUNCH("k_dec_merge");
   }
   prof_mark(st, "dec_stream");
@@ -890,6 +1010,14 @@ int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, fl
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (p.dtype == ANCHORKV_BF16) return decode_impl<ANCHORKV_BF16>(p, cache, q, o, ws, st);
   return decode_impl<ANCHORKV_F32>(p, cache, q, o, ws, st);
+}
+
+int run_decode_tail(const anchorkv_plan_info& p, const void* cache, const void* q, const void* K_tail,
+                    const void* V_tail, int n_tail, int tail_cap, float* o, void* ws, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (p.dtype == ANCHORKV_BF16)
+    return decode_impl<ANCHORKV_BF16>(p, cache, q, o, ws, st, K_tail, V_tail, n_tail, tail_cap);
+  return decode_impl<ANCHORKV_F32>(p, cache, q, o, ws, st, K_tail, V_tail, n_tail, tail_cap);
 }
 
 }  // namespace akv

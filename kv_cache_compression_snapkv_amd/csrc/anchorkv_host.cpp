@@ -77,6 +77,11 @@ DecodeWs decode_ws_layout(const anchorkv_plan_info& p) {
   auto take = [&](int64_t bytes) { int64_t o = off; off = round_up(off + bytes, 256); return o; };
   w.part_ml = take(8 * U * H * w.S2 * G);
   w.part_acc = take(4 * U * H * w.S2 * G * D);
+  // tail ranges: enough workgroups to cover the chip (about 2048) when the
+  // tail is long, at most 16 per head
+  w.St = (int)std::min<int64_t>(16, std::max<int64_t>(1, (2048 + U * H - 1) / (U * H)));
+  w.tail_ml = take(8 * U * H * w.St * G);
+  w.tail_acc = take(4 * U * H * w.St * G * D);
   w.total = off;
   return w;
 }
@@ -243,6 +248,21 @@ int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, cons
   if (((uintptr_t)cache | (uintptr_t)q | (uintptr_t)o | (uintptr_t)workspace) & 15)
     return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn: buffers must be 16-byte aligned");
   return run_decode(*plan, cache, q, o, workspace, stream);
+}
+
+int anchorkv_decode_attn_tail(const anchorkv_plan_info* plan, const void* cache, const void* q, const void* K_tail,
+                              const void* V_tail, int32_t n_tail, int32_t tail_cap, float* o, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!plan || !cache || !q || !o || !workspace) return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_tail: null argument");
+  if (n_tail < 0 || tail_cap < n_tail)
+    return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_tail: need 0 <= n_tail (%d) <= tail_cap (%d)", n_tail, tail_cap);
+  if (n_tail > 0 && (!K_tail || !V_tail)) return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_tail: null tail");
+  if ((int64_t)workspace_bytes < plan->decode_workspace_bytes)
+    return fail(ANCHORKV_E_SMALL_BUFFER, "anchorkv_decode_attn_tail: workspace %zu < %lld bytes", workspace_bytes,
+                (long long)plan->decode_workspace_bytes);
+  if (((uintptr_t)cache | (uintptr_t)q | (uintptr_t)o | (uintptr_t)workspace | (uintptr_t)K_tail | (uintptr_t)V_tail) & 15)
+    return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_tail: buffers must be 16-byte aligned");
+  return run_decode_tail(*plan, cache, q, K_tail, V_tail, n_tail, tail_cap, o, workspace, stream);
 }
 
 // ---------------------------------------------------------------- host packer

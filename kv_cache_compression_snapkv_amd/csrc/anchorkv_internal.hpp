@@ -60,6 +60,9 @@ struct DecodeWs {
   int S2;          // token splits per (unit, head); boundaries on 1024-token chunks
   int64_t part_ml; // float2 [U][H][S2][G]  (max, sum) of each range
   int64_t part_acc; // f32 [U][H][S2][G][D] unnormalised output of each range
+  int St;           // ranges per (unit, head) of an appended exact tail
+  int64_t tail_ml;  // float2 [U][H][St][G] (max, sum) of each tail range
+  int64_t tail_acc; // f32 [U][H][St][G][D] unnormalised output of each tail range
   int64_t total;
 };
 DecodeWs decode_ws_layout(const anchorkv_plan_info& p);
@@ -86,6 +89,10 @@ void prof_mark(void* stream, const char* stage);
 int run_compress(const anchorkv_plan_info& p, const void* K, const void* V, const void* Q, void* cache,
                  void* ws, void* stream);
 int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* ws, void* stream);
+// Decode with an exact tail of n_tail tokens per KV head appended after the
+// compressed ones: K_tail / V_tail [U][H][tail_cap][D] in the cache dtype.
+int run_decode_tail(const anchorkv_plan_info& p, const void* cache, const void* q, const void* K_tail,
+                    const void* V_tail, int n_tail, int tail_cap, float* o, void* ws, void* stream);
 // Workgroups of the decode kernel that fit one compute unit (LDS and registers).
 int decode_blocks_per_cu(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C);
 
