@@ -798,20 +798,38 @@ __global__ __launch_bounds__(256) void k_dec_merge(const float2* part_ml, const 
   }
 }
 
+// One tail tile's loads: VPT value chunks of the thread, the lane's key-row quarter.
+template <typename T, int VPT, int KPL, int CPR, int EPC>
+__device__ __forceinline__ void tail_load(uint4 (&vr)[VPT], uint4 (&kr)[KPL], const T* Vp, const T* Kp, int t0,
+                                          int last, int tid, int jt, int qoff) {
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = tid + 256 * k;
+    vr[k] = *reinterpret_cast<const uint4*>(Vp + (int64_t)min(t0 + i / CPR, last) * kHeadDim + (i % CPR) * EPC);
+  }
+  const T* row = Kp + (int64_t)min(t0 + jt, last) * kHeadDim + qoff;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) kr[k] = *reinterpret_cast<const uint4*>(row + k * EPC);
+}
+
 // Exact tail of one (unit, KV head): tokens appended after the one-shot
 // compression and kept at the cache's element type (AnchorKV-adapted page,
 // "Adaptation notes").  Workgroup s of the head takes tail range s (whole
-// 64-token tiles).  Per tile: the value rows are staged in LDS with 16-byte
-// loads; lane (token j, quarter) of wave w dots a quarter of key row 16w + j
-// with every q-head (quad sums), wave 0 raises the running maxima and turns
-// the logits (c <q, k>, log2 domain) into probabilities, and thread
-// (half, d) adds p v for coordinate d of q-heads half, half + 2, ...  Writes
-// the range's (max, sum, unnormalised output) partial for k_dec_merge.
+// 64-token tiles).  Per tile: all key and value loads are issued at once (16
+// bytes per lane; rows past the range clamped to its last row, so no
+// branches; other resident workgroups cover the latency); the value rows go
+// to LDS; lane (token j, quarter) of wave w dots a quarter of key row 16w + j
+// with every q-head (quad sums); wave 0 raises the running maxima and turns
+// the logits (c <q, k>, log2 domain) into probabilities; thread (half, d)
+// adds p v for coordinate d of q-heads half, half + 2, ...  Writes the range's
+// (max, sum, unnormalised output) partial for k_dec_merge.
 template <int DT>
 __global__ __launch_bounds__(256) void k_dec_tail(const void* q, const void* Kt, const void* Vt, int n_tail,
                                                  int tail_cap, int G, int St, float c, float2* tml, float* tacc) {
   using T = typename Elem<DT>::T;
   constexpr int D = kHeadDim, TT = 64, EPC = 16 / (int)sizeof(T), CPR = D / EPC;
+  constexpr int VPT = TT * CPR / 256;   // 16-byte value chunks per thread and tile
+  constexpr int KPL = 32 / EPC;         // 16-byte chunks of a key-row quarter
   __shared__ float qs[kMaxG][D];
   __shared__ __align__(16) T vs[TT][D];
   __shared__ float ps[kMaxG][TT];
@@ -831,31 +849,32 @@ __global__ __launch_bounds__(256) void k_dec_tail(const void* q, const void* Kt,
   float acc[kMaxG / 2];
 #pragma unroll
   for (int k = 0; k < kMaxG / 2; ++k) acc[k] = 0.0f;
+  const int qoff = 32 * qq;
   __syncthreads();
   for (int t0 = t_beg; t0 < t_end; t0 += TT) {
     const int nt = min(TT, t_end - t0);
-    for (int i = tid; i < TT * CPR; i += 256) {
-      const int r = i / CPR, ch = i % CPR;
-      *reinterpret_cast<uint4*>(&vs[r][ch * EPC]) =
-          r < nt ? *reinterpret_cast<const uint4*>(Vp + (int64_t)(t0 + r) * D + ch * EPC) : make_uint4(0, 0, 0, 0);
+    // all of the tile's key and value loads at once (rows clamped: no branches)
+    uint4 vr[VPT], kr4[KPL];
+    tail_load<T, VPT, KPL, CPR, EPC>(vr, kr4, Vp, Kp, t0, t_end - 1, tid, jt, qoff);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int i = tid + 256 * k, r = i / CPR, ch = i % CPR;
+      *reinterpret_cast<uint4*>(&vs[r][ch * EPC]) = vr[k];
     }
     float sg[kMaxG];
 #pragma unroll
     for (int g = 0; g < kMaxG; ++g) sg[g] = 0.0f;
-    if (jt < nt) {
-      const T* kr = Kp + (int64_t)(t0 + jt) * D + 32 * qq;
 #pragma unroll
-      for (int c0 = 0; c0 < 32; c0 += EPC) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(kr + c0);
-        T kv[EPC];
-        __builtin_memcpy(kv, &raw, 16);
+    for (int k = 0; k < KPL; ++k) {
+      const uint4 raw = kr4[k];
+      T kv[EPC];
+      __builtin_memcpy(kv, &raw, 16);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const float kf = Elem<DT>::f(kv[e]);
+      for (int e = 0; e < EPC; ++e) {
+        const float kf = Elem<DT>::f(kv[e]);
 #pragma unroll
-          for (int g = 0; g < kMaxG; ++g)
-            if (g < G) sg[g] = fmaf(qs[g][32 * qq + c0 + e], kf, sg[g]);
-        }
+        for (int g = 0; g < kMaxG; ++g)
+          if (g < G) sg[g] = fmaf(qs[g][32 * qq + k * EPC + e], kf, sg[g]);
       }
     }
 #pragma unroll
@@ -881,8 +900,10 @@ __global__ __launch_bounds__(256) void k_dec_tail(const void* q, const void* Kt,
     for (int k = 0; k < kMaxG / 2; ++k) {
       const int g = half + 2 * k;
       if (g < G) {
+        // all TT rows: past nt, p = 0 and the value rows are clamped copies
         float a = acc[k] * fr[g];
-        for (int t = 0; t < nt; ++t) a = fmaf(ps[g][t], Elem<DT>::f(vs[t][d]), a);
+#pragma unroll 16
+        for (int t = 0; t < TT; ++t) a = fmaf(ps[g][t], Elem<DT>::f(vs[t][d]), a);
         acc[k] = a;
       }
     }
