@@ -819,8 +819,9 @@ __device__ __forceinline__ void tail_load(uint4 (&vr)[VPT], uint4 (&kr)[KPL], co
 // bytes per lane; rows past the range clamped to its last row, so no
 // branches; other resident workgroups cover the latency); the value rows go
 // to LDS; lane (token j, quarter) of wave w dots a quarter of key row 16w + j
-// with every q-head (quad sums); wave 0 raises the running maxima and turns
-// the logits (c <q, k>, log2 domain) into probabilities; thread (half, d)
+// with every q-head (quad sums); wave w raises the running maxima of q-heads
+// w and w + 4 and turns their logits (c <q, k>, log2 domain) into
+// probabilities; thread (half, d)
 // adds p v for coordinate d of q-heads half, half + 2, ...  Writes the range's
 // (max, sum, unnormalised output) partial for k_dec_merge.
 template <int DT>
@@ -884,16 +885,14 @@ __global__ __launch_bounds__(256) void k_dec_tail(const void* q, const void* Kt,
         if (qq == 0) ps[g][jt] = jt < nt ? v * c : -INFINITY;
       }
     __syncthreads();
-    if (wave == 0) {
-      for (int g = 0; g < G; ++g) {
-        const float x = ps[g][lane];
-        const float mn = fmaxf(mrun[g], wave_max(x));
-        const float f = mrun[g] == -INFINITY ? 0.0f : exp2_fast(mrun[g] - mn);
-        const float p = lane < nt ? exp2_fast(x - mn) : 0.0f;
-        ps[g][lane] = p;
-        const float sum = wave_sum(p);
-        if (lane == 0) { fr[g] = f; lrun[g] = fmaf(lrun[g], f, sum); mrun[g] = mn; }
-      }
+    for (int g = wave; g < G; g += 4) {   // wave w: q-heads w, w + 4
+      const float x = ps[g][lane];
+      const float mn = fmaxf(mrun[g], wave_max(x));
+      const float f = mrun[g] == -INFINITY ? 0.0f : exp2_fast(mrun[g] - mn);
+      const float p = lane < nt ? exp2_fast(x - mn) : 0.0f;
+      ps[g][lane] = p;
+      const float sum = wave_sum(p);
+      if (lane == 0) { fr[g] = f; lrun[g] = fmaf(lrun[g], f, sum); mrun[g] = mn; }
     }
     __syncthreads();
 #pragma unroll
