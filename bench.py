@@ -161,7 +161,7 @@ def kernel_stage(name):
         return {0: "obs_stats", 1: "obs_score", 2: "obs_util", 3: "util_fix"}[int(m.group(1))]
     for key, stage in (("k_ml_combine", "ml_combine"), ("k_o_combine", "o_combine"), ("k_select", "select"),
                        ("k_assign", "assign"), ("k_topr", "topr"), ("k_quant", "quant"), ("k_headers", "headers"),
-                       ("k_dec_stream", "dec_stream"), ("k_dec_merge", "dec_stream"),
+                       ("k_dec_stream", "dec_stream"), ("k_dec_merge", "dec_stream"), ("k_dec_tail", "dec_tail"),
                        ("k_zero_u32", "zero")):
         if key in name:
             return stage
@@ -199,10 +199,11 @@ def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
             e[key] += v * 1024.0
             e["n_" + key] += 1
     calls = max(1, per.get("headers", {}).get("n_fetch", 1))
-    dec_calls = max(1, per.get("dec_stream", {}).get("n_fetch", 1))
+    # one decode call = one k_dec_stream dispatch (plus a merge when split)
+    dec_calls = max(1, sum(1 for n, _ in read_counters(fetch_dir, "FETCH_SIZE") if "k_dec_stream" in n))
     stages = {}
     for st, e in per.items():
-        n = dec_calls if st.startswith("dec_") else calls
+        n = dec_calls if st == "dec_stream" else (e["n_fetch"] or 1) if st == "dec_tail" else calls
         fb, wb = e["fetch"] * f_scale / n, e["write"] * w_scale / n
         stages[st] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb, "dispatches_per_call": e["n_fetch"] / n}
     out = {"workload": workload, "source_hash": kernel_source_hash(), "unit": "bytes per call of the stage",
