@@ -106,6 +106,28 @@ def measure_tail(akv, w, p, cache, q, o, dws, stream, n_tail, reps=5):
             "tail_GB_s": tb / (tail_ms * 1e-3) / 1e9, "tail_hbm_frac": tb / (tail_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def measure_one_unit(akv, w, cache, p, q, stream, reps=20):
+    """Decode of one unit (one layer of one sequence) per launch: the latency a
+    per-layer caller sees (outside the timed steps; HIP events, median).  The
+    unit's plan and cache bytes are those of unit 0 of the full cache."""
+    import torch
+    p1 = akv.plan(1, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs, p.dtype, w.theta, w.window)
+    _, _, dws1 = akv.alloc(p1, q.device)
+    q1 = q[:1].contiguous()
+    o1 = torch.empty(1, w.kv_heads * w.q_per_kv, w.head_dim, dtype=torch.float32, device=q.device)
+    c1 = cache[:p1.cache_bytes]
+    akv.decode_attn(p1, c1, q1, o1, dws1, stream)
+    torch.cuda.synchronize()
+    akv.profile_enable(True)
+    akv.profile_read()
+    for _ in range(reps):
+        akv.decode_attn(p1, c1, q1, o1, dws1, stream)
+    torch.cuda.synchronize()
+    st = sorted(ms for n, ms in akv.profile_read() if n == "dec_stream")
+    akv.profile_enable(False)
+    return {"units": 1, "us": st[len(st) // 2] * 1e3, "bytes": decode_bytes(p1)}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle as it stands, on the host cores: compress + one decode step
     for a bounded sample of units, extrapolated to the workload's tokens/s."""
@@ -286,6 +308,7 @@ def main():
     stages = akv.profile_read()
     akv.profile_enable(False)
     tail_rec = measure_tail(akv, w, p, cache, qs[0], o, dws, stream, args.tail) if args.tail > 0 else None
+    unit_rec = measure_one_unit(akv, w, cache, p, qs[0], stream)
     total_s = t1 - t0
     ms_per_step = total_s * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
@@ -342,6 +365,7 @@ def main():
                    "note": "cache fits the 256 MB Infinity Cache" if dec_b < 256e6 else "HBM-resident"},
         "stages_ms": stage_ms,
         "decode_tail": tail_rec,
+        "decode_one_unit": unit_rec,
         "roofline": rl,
         # each main stage against its own roofline (the contraction of the
         # assignment also against the bf16 MFMA peak, whatever bounds it)
