@@ -59,8 +59,8 @@ struct DecArgs {
   const void* q;
   const uint8_t* cache;
   int64_t stride, off_words, off_rk, off_rv, off_ck, off_cv, off_ak, off_av;
-  float2* part_ml;   // [U][H][S2][G] (max, sum) of each range (S2 > 1)
-  float* part_acc;   // [U][H][S2][G][D] unnormalised output of each range (S2 > 1)
+  float2* part_ml;   // [U][H][S2][G] (max, sum) of each range (S2 > 1 or a tail follows)
+  float* part_acc;   // [U][H][S2][G][D] unnormalised output of each range (same cases)
   float* o;          // [U][H][G][D]
   int H, N, A, C, S2, cps, R_K, R_V;
   int force_part;    // publish partials even with one range (a tail follows)
@@ -760,7 +760,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
     return;
   }
-  // several ranges per head: publish this one (merged by k_dec_merge)
+  // several ranges per head, or a tail to follow: publish this one (merged by k_dec_merge)
   const int64_t ps = uh * a.S2 + sp;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {

@@ -40,7 +40,6 @@ int obs_splits(const anchorkv_plan_info& p) {
 CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
   CompressWs w{};
   const int64_t U = p.units, H = p.H, N = p.N, D = p.D, A = p.A;
-  const int64_t C = p.n_chunks;
   w.S1 = obs_splits(p);
   w.GQp = padded_queries(p);
   const int64_t GQp = w.GQp;
