@@ -248,6 +248,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1, help="decode steps per step (default 1)")
     ap.add_argument("--tail", type=int, default=1024,
                     help="tokens of the exact tail in the separate decode-with-tail measurement (0: skip)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements after the timed steps (decode with a tail, one-unit decode)")
     ap.add_argument("--copy-probe", action="store_true", help="run only the traffic-counter calibration copy")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from four rocprofv3 --pmc csv folders")
@@ -307,8 +309,9 @@ def main():
     t1 = time.perf_counter()
     stages = akv.profile_read()
     akv.profile_enable(False)
-    tail_rec = measure_tail(akv, w, p, cache, qs[0], o, dws, stream, args.tail) if args.tail > 0 else None
-    unit_rec = measure_one_unit(akv, w, cache, p, qs[0], stream)
+    extras = not args.no_extras
+    tail_rec = measure_tail(akv, w, p, cache, qs[0], o, dws, stream, args.tail) if extras and args.tail > 0 else None
+    unit_rec = measure_one_unit(akv, w, cache, p, qs[0], stream) if extras else None
     total_s = t1 - t0
     ms_per_step = total_s * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
