@@ -81,6 +81,21 @@ def test_plan_argument_errors(akv):
     assert lib.anchorkv_plan(None, ct.c_float(0.1), 32, None) == -1
     assert lib.anchorkv_compress(None, None, None, None, None, 0, None, 0, None) == -1
     assert lib.anchorkv_decode_attn(None, None, None, None, None, 0, None) == -1
+    # decode with a tail: host-side checks, before any device call (fake,
+    # 16-byte aligned addresses that are never dereferenced)
+    p = akv.plan(1, 2, 2, 1024, 128, 8, akv.BF16, 0.1, 32)
+    fake = 1 << 20
+    ws = int(p.decode_workspace_bytes)
+
+    def tail(n, cap, kt=fake, vt=fake, wsb=ws, q=fake):
+        return lib.anchorkv_decode_attn_tail(ct.byref(p), fake, q, kt, vt, n, cap, fake, fake, wsb, None)
+    assert tail(5, 4) == -1                 # n_tail > tail_cap
+    assert tail(-1, 4) == -1                # negative n_tail
+    assert tail(3, 4, kt=None) == -1        # null tail with n_tail > 0
+    assert tail(3, 4, vt=fake + 8) == -1    # misaligned tail
+    assert tail(3, 4, q=fake + 4) == -1     # misaligned query
+    assert tail(3, 4, wsb=ws - 1) == -5     # workspace too small
+    assert "tail" in lib.anchorkv_last_error().decode()
 
 
 def test_pack_unpack_roundtrip_of_oracle_unit(akv):
