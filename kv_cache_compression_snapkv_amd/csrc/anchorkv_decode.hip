@@ -915,6 +915,113 @@ __global__ __launch_bounds__(256) void k_dec_tail(const void* q, const void* Kt,
     if (half + 2 * k < G) tacc[(slot * G + half + 2 * k) * D + d] = acc[k];
 }
 
+// The bf16 tail on MFMA, same ranges, tiles and partials as k_dec_tail:
+// logits with rows = the wave's 16 tokens (key rows as A fragments straight
+// from memory), columns = q-heads (the query as B fragments, exact bf16);
+// p v with rows = q-heads (p as bf16 hi + lo from LDS), K = 32 tokens,
+// columns = 16 coordinates (value B fragments gathered from the LDS tile);
+// wave w owns coordinate blocks 2w and 2w + 1.
+__global__ __launch_bounds__(256) void k_dec_tail_bf16(const void* q, const void* Kt, const void* Vt, int n_tail,
+                                                      int tail_cap, int G, int St, float c, float2* tml,
+                                                      float* tacc) {
+  using M = Mfma<ANCHORKV_BF16>;
+  constexpr int D = kHeadDim, TT = 64, CPR = D / 8, VPT = TT * CPR / 256;
+  __shared__ __align__(16) uint16_t vs[TT][D];
+  __shared__ __align__(16) float ps[16][TT];   // rows >= G stay zero
+  __shared__ float fr[kMaxG], mrun[kMaxG], lrun[kMaxG];
+  const int s = blockIdx.x % St;
+  const int64_t uh = blockIdx.x / St;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int span = ((n_tail + St - 1) / St + TT - 1) / TT * TT;
+  const int t_beg = min(n_tail, s * span), t_end = min(n_tail, t_beg + span);
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(q) + uh * G * D;
+  const uint16_t* Kp = reinterpret_cast<const uint16_t*>(Kt) + uh * (int64_t)tail_cap * D;
+  const uint16_t* Vp = reinterpret_cast<const uint16_t*>(Vt) + uh * (int64_t)tail_cap * D;
+  bf16x8 qf[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) qf[st] = col < G ? M::load(qp + col * D + st * 32 + kg * 8) : M::zero();
+  for (int i = tid; i < 16 * TT; i += 256) ps[i / TT][i % TT] = 0.0f;
+  if (tid < kMaxG) { mrun[tid] = -INFINITY; lrun[tid] = 0.0f; }
+  f32x4 oacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  __syncthreads();
+  for (int t0 = t_beg; t0 < t_end; t0 += TT) {
+    const int nt = min(TT, t_end - t0), last = t_end - 1;
+    // all of the tile's loads at once (rows clamped to the range: no branches)
+    uint4 vr[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int i = tid + 256 * k;
+      vr[k] = *reinterpret_cast<const uint4*>(Vp + (int64_t)min(t0 + i / CPR, last) * D + (i % CPR) * 8);
+    }
+    const uint16_t* kr = Kp + (int64_t)min(t0 + 16 * wave + col, last) * D + kg * 8;
+    bf16x8 kf[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) kf[st] = M::load(kr + st * 32);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int i = tid + 256 * k;
+      *reinterpret_cast<uint4*>(&vs[i / CPR][(i % CPR) * 8]) = vr[k];
+    }
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc = M::mma(kf[st], qf[st], acc);
+    if (col < G)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * wave + 4 * kg + r;
+        ps[col][j] = j < nt ? acc[r] * c : -INFINITY;
+      }
+    __syncthreads();
+    for (int g = wave; g < G; g += 4) {   // wave w: q-heads w, w + 4
+      const float x = ps[g][lane];
+      const float mn = fmaxf(mrun[g], wave_max(x));
+      const float f = mrun[g] == -INFINITY ? 0.0f : exp2_fast(mrun[g] - mn);
+      const float p = lane < nt ? exp2_fast(x - mn) : 0.0f;
+      ps[g][lane] = p;
+      const float sum = wave_sum(p);
+      if (lane == 0) { fr[g] = f; lrun[g] = fmaf(lrun[g], f, sum); mrun[g] = mn; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * kg + r;
+      const float f = g < G ? fr[g] : 0.0f;
+      oacc[0][r] *= f;
+      oacc[1][r] *= f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < TT / 32; ++ks) {
+      float p8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p8[e] = ps[col][ks * 32 + kg * 8 + e];
+      bf16x8 ph, pl;
+      split8(p8, ph, pl);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int d = (2 * wave + b) * 16 + col;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)vs[ks * 32 + kg * 8 + 2 * e][d] | ((uint32_t)vs[ks * 32 + kg * 8 + 2 * e + 1][d] << 16);
+        const bf16x8 vb = bits_to_frag(make_uint4(w[0], w[1], w[2], w[3]));
+        oacc[b] = M::mma(ph, vb, oacc[b]);
+        oacc[b] = M::mma(pl, vb, oacc[b]);
+      }
+    }
+    __syncthreads();   // vs, ps, fr are rewritten by the next tile
+  }
+  const int64_t slot = uh * St + s;
+  if (tid < G) tml[slot * G + tid] = make_float2(mrun[tid], lrun[tid]);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * kg + r;
+      if (g < G) tacc[(slot * G + g) * D + (2 * wave + b) * 16 + col] = oacc[b][r];
+    }
+}
+
 // Raise a kernel's dynamic-LDS limit to `bytes` (once per larger value).
 
 static size_t stream_lds(int G, int A, int KP, bool qsplit) {
@@ -1003,8 +1110,12 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
     prof_mark(st, "dec_stream");
     float2* tml = reinterpret_cast<float2*>(ws + w.tail_ml);
     float* tacc = reinterpret_cast<float*>(ws + w.tail_acc);
-    k_dec_tail<DT><<<(unsigned)((int64_t)U * H * w.St), 256, 0, st>>>(q, K_tail, V_tail, n_tail, tail_cap, G, w.St,
-                                                                        a.c, tml, tacc);
+    if constexpr (DT == ANCHORKV_BF16)
+      k_dec_tail_bf16<<<(unsigned)((int64_t)U * H * w.St), 256, 0, st>>>(q, K_tail, V_tail, n_tail, tail_cap, G,
+                                                                         w.St, a.c, tml, tacc);
+    else
+      k_dec_tail<DT><<<(unsigned)((int64_t)U * H * w.St), 256, 0, st>>>(q, K_tail, V_tail, n_tail, tail_cap, G, w.St,
+                                                                          a.c, tml, tacc);
     AKV_CHECK_LAUNCH("k_dec_tail");
     k_dec_merge<<<(unsigned)((int64_t)U * H), 256, 0, st>>>(a.part_ml, a.part_acc, tml, tacc, o, G, S2, w.St);
     AKV_CHECK_LAUNCH("k_dec_merge");
