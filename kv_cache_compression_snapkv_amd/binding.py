@@ -141,11 +141,26 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
+def _expect(fn, name, t, shape, dtype):
+    """The C ABI takes bare pointers: check what the kernels will index."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{fn}: {name} must be {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def _elem_dtype(p: PlanInfo):
+    import torch
+    return torch.bfloat16 if p.dtype == BF16 else torch.float32
+
+
 def compress(p: PlanInfo, K, V, Q, cache, workspace, stream=None):
     """Enqueue the compression of all units (torch CUDA tensors, contiguous)."""
     for t in (K, V, Q, cache, workspace):
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError("compress: inputs must be contiguous device tensors")
+    dt = _elem_dtype(p)
+    _expect("compress", "K", K, (p.units, p.H, p.N, p.D), dt)
+    _expect("compress", "V", V, (p.units, p.H, p.N, p.D), dt)
+    _expect("compress", "Q_obs", Q, (p.units, p.H * p.G, p.n_obs, p.D), dt)
     _check(lib().anchorkv_compress(ct.byref(p), _ptr(K), _ptr(V), _ptr(Q), _ptr(cache), _nbytes(cache),
                                    _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
@@ -155,6 +170,9 @@ def decode_attn(p: PlanInfo, cache, q, o, workspace, stream=None):
     for t in (cache, q, o, workspace):
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError("decode_attn: inputs must be contiguous device tensors")
+    import torch
+    _expect("decode_attn", "q", q, (p.units, p.H * p.G, p.D), _elem_dtype(p))
+    _expect("decode_attn", "o", o, (p.units, p.H * p.G, p.D), torch.float32)
     _check(lib().anchorkv_decode_attn(ct.byref(p), _ptr(cache), _ptr(q), _ptr(o), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream)))
 
@@ -166,8 +184,14 @@ def decode_attn_tail(p: PlanInfo, cache, q, K_tail, V_tail, n_tail: int, o, work
     for t in (cache, q, o, workspace, K_tail, V_tail):
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError("decode_attn_tail: inputs must be contiguous device tensors")
-    if K_tail.shape != V_tail.shape or K_tail.dim() != 4:
-        raise ValueError("decode_attn_tail: K_tail and V_tail must share a [U, H, tail_cap, D] shape")
+    import torch
+    if K_tail.dim() != 4:
+        raise ValueError("decode_attn_tail: K_tail must be [U, H, tail_cap, D]")
+    cap = int(K_tail.shape[2])
+    _expect("decode_attn_tail", "q", q, (p.units, p.H * p.G, p.D), _elem_dtype(p))
+    _expect("decode_attn_tail", "o", o, (p.units, p.H * p.G, p.D), torch.float32)
+    _expect("decode_attn_tail", "K_tail", K_tail, (p.units, p.H, cap, p.D), _elem_dtype(p))
+    _expect("decode_attn_tail", "V_tail", V_tail, (p.units, p.H, cap, p.D), _elem_dtype(p))
     _check(lib().anchorkv_decode_attn_tail(ct.byref(p), _ptr(cache), _ptr(q), _ptr(K_tail), _ptr(V_tail),
                                            int(n_tail), int(K_tail.shape[2]), _ptr(o), _ptr(workspace),
                                            _nbytes(workspace), _stream(stream)))
