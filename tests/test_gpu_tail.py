@@ -102,7 +102,7 @@ def test_decode_tail_parity(akv, name):
         assert np.isfinite(o_h).all() and worst <= 1e-3, (n, worst)
 
 
-def test_decode_tail_argument_errors(akv):
+def test_decode_argument_errors(akv):
     w = CASES["bf16_ragged"]
     p = plan_for(akv, w)
     cache, _, dws = akv.alloc(p, "cuda")
@@ -113,3 +113,12 @@ def test_decode_tail_argument_errors(akv):
         akv.decode_attn_tail(p, cache, q, Kt, Kt, 5, o, dws)   # n_tail > tail_cap
     with pytest.raises(akv.AnchorKVError):
         akv.decode_attn_tail(p, cache, q, Kt, Kt, -1, o, dws)
+    # shapes / dtypes that the kernels would index past: refused before any launch
+    with pytest.raises(ValueError):
+        akv.decode_attn_tail(p, cache, q[:, :1].contiguous(), Kt, Kt, 2, o, dws)
+    with pytest.raises(ValueError):
+        akv.decode_attn_tail(p, cache, q, Kt[:, :1].contiguous(), Kt[:, :1].contiguous(), 2, o, dws)
+    with pytest.raises(ValueError):
+        akv.decode_attn(p, cache, q.float(), o, dws)
+    with pytest.raises(ValueError):
+        akv.decode_attn(p, cache, q, o[:, :1].contiguous(), dws)
