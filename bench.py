@@ -151,7 +151,14 @@ def cpu_baseline(w, budget_s=12.0):
         t_tot += time.perf_counter() - t0
     per_unit = t_tot / n
     step_s = per_unit * w.units
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {"value": w.seqs * w.n_tokens / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model, "per_unit_s": per_unit,
             "sample": f"{n} of {w.units} units (compress + 1 decode step each, float64 NumPy), "
                       f"{per_unit:.2f} s/unit, extrapolated to all units"}
 
