@@ -209,8 +209,8 @@ def read_counters(d, counter):
     return out
 
 
-def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
-    """profiles/traffic_<workload>.json: scaled HBM bytes per launch of every stage."""
+def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands, path=None):
+    """profiles/traffic_<workload>.json (or `path`): scaled HBM bytes per launch of every stage."""
     def copy_kib(d, counter):
         vals = [v for n, v in read_counters(d, counter) if "copyBuffer" in n or "copy" in n.lower()]
         if not vals:
@@ -239,7 +239,7 @@ def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
            "copy_calibration": {"bytes": COPY_PROBE_BYTES, "fetch_counter_bytes": cf * 1024.0,
                                 "write_counter_bytes": cw * 1024.0, "fetch_scale": f_scale, "write_scale": w_scale},
            "commands": commands, "stages": stages}
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = path or os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps({"written": path, "stages": {k: round(v["bytes"] / 1e6, 2) for k, v in stages.items()}}))
