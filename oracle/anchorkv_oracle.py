@@ -61,10 +61,6 @@ def fp16_rne(x):
     return np.where(np.isinf(y) & np.isfinite(x), np.sign(x) * FP16_MAX, y)
 
 
-def fp32_round(x):
-    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
-
-
 # --------------------------------------------------------------------------
 # Byte plan [Pith, "What carries the argument" (per-layer byte accounting, theta
 # the only knob) and "Assumptions & free parameters" (theta, k = S/128, rho,

@@ -436,3 +436,118 @@ def test_worked_example_density_cross_check():
     residual density at 20x; consistent with one 8-head layer at S = 32768 with
     two sides (the example's own byte costs are not printed)."""
     assert 91056 / (8 * 32768 * 2) == pytest.approx(0.173, abs=1e-3)
+
+
+# ---------------------------------------------------------------- reconstruction, code margin, cut value
+def _independent_reconstruction(c, K, V):
+    """K^, V^ of a compressed unit built element by element from the stored
+    fields, without the oracle's reconstruct / dequantize: x^_t = h(gamma_t)
+    x_a(t) + [t flagged] (zero_g + scale_g code_d) (Pith, "What carries the
+    argument": x^ = gamma x_a + r~), with h() the fp16 rounding done by numpy's
+    float16 cast and gamma recomputed from the projection formula."""
+    H, N, D = K.shape
+    out = []
+    for s, X in enumerate((K, V)):
+        Xh = np.zeros((H, N, D))
+        for h in range(H):
+            pos = c.anchor_pos[h]
+            for t in range(N):
+                a = int(c.idx[s, h, t])
+                xa = X[h, pos[a]]
+                na2 = float(sum(v * v for v in xa))
+                g = 1.0 if t == pos[a] else (float(sum(X[h, t, d] * xa[d] for d in range(D))) / na2 if na2 > 0 else 0.0)
+                g16 = float(np.float16(g))
+                for d in range(D):
+                    val = g16 * xa[d]
+                    if c.flag[s, h, t]:
+                        grp = d // 32
+                        val += c.zero[s, h, t, grp] + c.scale[s, h, t, grp] * int(c.codes[s, h, t, d])
+                    Xh[h, t, d] = val
+        out.append(Xh)
+    return out
+
+
+def _tiny_flagged_unit(seed):
+    r = rng(seed)
+    H, G, N, D, n_obs, W = 2, 2, 160, 32, 4, 4
+    K = bf16_exact(clustered(r, H, N, D, ndir=4))
+    V = bf16_exact(r.standard_normal((H, N, D)) + 1.0)
+    Q = bf16_exact(r.standard_normal((H * G, n_obs, D)))
+    c = O.compress_unit(K, V, Q, G, n_obs, 0.2, W, 2)
+    assert 0 < c.flag[0].sum() < H * (N - c.plan.A) and 0 < c.flag[1].sum()
+    return c, K, V, G
+
+
+def test_reconstruct_matches_elementwise_definition():
+    """Unflagged tokens reconstruct to exactly fp16(gamma) x_a; flagged tokens
+    to fp16(gamma) x_a + dequantised codes, on both sides (a dropped residual,
+    a residual added to unflagged tokens, the unrounded gamma or swapped sides
+    all fail here)."""
+    c, K, V, _ = _tiny_flagged_unit(21)
+    Kh, Vh = O.reconstruct(c)
+    Ki, Vi = _independent_reconstruction(c, K, V)
+    np.testing.assert_array_equal(Kh, Ki)
+    np.testing.assert_array_equal(Vh, Vi)
+    # the stored fp16 gammas are not all exact: the rounding matters here
+    assert np.any(c.gamma16 != c.gamma)
+
+
+def test_reconstruct_error_bound():
+    """||x - x^|| <= ||r - r~|| + |gamma - fp16(gamma)| ||x_a|| for flagged
+    tokens and ||r|| + |gamma - fp16(gamma)| ||x_a|| for the rest, since
+    x - x^ = (r - [flag] r~) + (gamma - fp16(gamma)) x_a."""
+    c, K, V, _ = _tiny_flagged_unit(22)
+    for s, (X, Xh) in enumerate(zip((K, V), O.reconstruct(c))):
+        for h in range(X.shape[0]):
+            xa = X[h, c.anchor_pos[h]][c.idx[s, h]]
+            err = np.linalg.norm(X[h] - Xh[h], axis=1)
+            rt = c.zero[s, h][:, np.arange(X.shape[2]) // 32] + c.scale[s, h][:, np.arange(X.shape[2]) // 32] * c.codes[s, h]
+            kept = np.where(c.flag[s, h][:, None], rt, 0.0)
+            bound = np.linalg.norm(c.resid[s, h] - kept, axis=1) + np.abs(c.gamma[s, h] - c.gamma16[s, h]) * np.linalg.norm(xa, axis=1)
+            assert np.all(err <= bound * (1 + 1e-12) + 1e-300)
+            # and a flagged residual does better than nothing in aggregate
+            fl = c.flag[s, h]
+            if fl.any():
+                assert np.sum(err[fl] ** 2) < np.sum(np.linalg.norm(c.resid[s, h][fl], axis=1) ** 2)
+
+
+def test_decode_matches_sdpa_over_independent_reconstruction():
+    """decode_unit equals library attention (torch SDPA, fp64) over K^, V^
+    built without the oracle's reconstruct."""
+    c, K, V, G = _tiny_flagged_unit(23)
+    Ki, Vi = _independent_reconstruction(c, K, V)
+    q = bf16_exact(rng(24).standard_normal((K.shape[0] * G, K.shape[2])) * 2.0)
+    o = O.decode_unit(c, q)
+    for h in range(K.shape[0]):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[h * G:(h + 1) * G])[None], torch.from_numpy(Ki[h])[None], torch.from_numpy(Vi[h])[None])
+        np.testing.assert_allclose(o[h * G:(h + 1) * G], ref[0].numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_code_margin_hand_values():
+    """Distance of (r - zero)/scale from the nearest rounding midpoint k + 1/2,
+    worked by hand; +inf where the scale is 0."""
+    r = np.zeros((3, 32))
+    r[0, :4] = [0.5, 1.4999, 2.0, 0.1]       # zero 0, scale 1
+    r[1, :3] = [-0.75, -0.5, 0.25]           # zero -1, scale 0.5: y = 0.5, 1.0, 2.5
+    scale = np.array([[1.0], [0.5], [0.0]])
+    zero = np.array([[0.0], [-1.0], [3.0]])
+    m = O.code_margin(r, scale, zero)
+    np.testing.assert_allclose(m[0, :4], [0.0, 1e-4, 0.5, 0.4], atol=1e-12)
+    np.testing.assert_allclose(m[1, :3], [0.0, 0.5, 0.0], atol=1e-12)
+    assert np.all(np.isinf(m[2]))
+
+
+def test_cut_value_hand_values():
+    """The R-th largest eligible utility, ties counted with multiplicity;
+    ineligible (-inf) items never count; R beyond the eligible items gives the
+    smallest eligible one; R = 0 gives None."""
+    u = np.array([[3.0, 1.0, 2.0], [2.0, -np.inf, 5.0]])
+    assert [O.cut_value(u, R) for R in (1, 2, 3, 4, 5, 9)] == [5.0, 3.0, 2.0, 2.0, 1.0, 1.0]
+    assert O.cut_value(u, 0) is None
+    assert O.cut_value(np.full((2, 2), -np.inf), 3) is None
+    # consistent with the allocation: flagged >= cut >= unflagged, and exactly R flagged
+    for R in range(1, 6):
+        mask = O.allocate(u, R)
+        cut = O.cut_value(u, R)
+        assert mask.sum() == R and np.all(u[mask] >= cut) and np.all(u[~mask & np.isfinite(u)] <= cut)
