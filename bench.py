@@ -128,39 +128,56 @@ def measure_one_unit(akv, w, cache, p, q, stream, reps=20):
     return {"units": 1, "us": st[len(st) // 2] * 1e3, "bytes": decode_bytes(p1)}
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The oracle as it stands, on the host cores: compress + one decode step
-    for a bounded sample of units, extrapolated to the workload's tokens/s."""
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle as it stands, on the host cores, with the BLAS thread pool
+    set to every core this process may run on: compress + one decode step of
+    a bounded sample, extrapolated to the workload's tokens/s.
+
+    Whole units while they take about budget_s each or less; at shapes where
+    one unit takes longer (131072 tokens x 8 heads), one KV head of unit 0
+    compressed as a one-head unit plus its decode step, scaled by the heads of
+    the workload (the oracle's work is per head: the pooled budget only
+    changes the residual count)."""
     import numpy as np
+    import threadpoolctl
     import kvsynth
     from oracle import anchorkv_oracle as O
     cores = len(os.sched_getaffinity(0))
+    threadpoolctl.threadpool_limits(cores)
+    per_head = w.n_tokens * w.kv_heads > 8 * 32768
     n = 0
     t_tot = 0.0
-    for u in range(w.units):  # whole units until about budget_s of oracle time
-        if t_tot >= budget_s:
+    for u in range(w.units):
+        if t_tot >= budget_s or (per_head and n == 1):
             break
         n += 1
         s, l = kvsynth.unit_index(w, u)
         K, V, Q = kvsynth.unit_inputs(w, s, l, device="cpu")
         K64, V64, Q64 = (kvsynth.to_f64(x) for x in (K, V, Q))
         q = kvsynth.to_f64(kvsynth.decode_queries(w, 0, units=1)[0])
+        if per_head:
+            K64, V64, Q64, q = K64[:1], V64[:1], Q64[:w.q_per_kv], q[:w.q_per_kv]
         t0 = time.perf_counter()
         c = O.compress_unit(K64, V64, Q64, w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes)
         O.decode_unit(c, q)
         t_tot += time.perf_counter() - t0
-    per_unit = t_tot / n
-    step_s = per_unit * w.units
+    per_sample = t_tot / n
+    step_s = per_sample * (w.units * w.kv_heads if per_head else w.units)
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
     except OSError:
         pass
+    if per_head:
+        sample = (f"1 KV head of unit 0 (compress as a 1-head unit + 1 decode step, float64 NumPy) in "
+                  f"{per_sample:.1f} s, extrapolated x{w.units * w.kv_heads} heads (labelled extrapolation)")
+    else:
+        sample = (f"{n} of {w.units} units (compress + 1 decode step each, float64 NumPy), "
+                  f"{per_sample:.2f} s/unit, extrapolated to all units")
     return {"value": w.seqs * w.n_tokens / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "cpu_model": cpu_model, "per_unit_s": per_unit,
-            "sample": f"{n} of {w.units} units (compress + 1 decode step each, float64 NumPy), "
-                      f"{per_unit:.2f} s/unit, extrapolated to all units"}
+            "cpu_model": cpu_model, "blas_threads": cores, "seconds_per_sample": per_sample,
+            "extrapolated_step_s": step_s, "sample": sample}
 
 
 # ---- HBM traffic from rocprofv3 counters (FETCH_SIZE / WRITE_SIZE, KiB per
@@ -250,7 +267,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3b_8k")
+    ap.add_argument("--workload", default="llama70b_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1, help="decode steps per step (default 1)")
     ap.add_argument("--tail", type=int, default=1024,
@@ -335,13 +352,16 @@ def main():
     decode_ms = sum(stage_ms.get(k, 0.0) for k in dec_stages)
     dom = max(comp_stages + dec_stages, key=lambda k: stage_ms.get(k, 0.0) * (1 if k in comp_stages else args.decode_steps))
     rl = roofline(p, dom, stage_ms[dom])
-    traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
-    if os.path.exists(tf):
-        t = json.load(open(tf))
-        if t.get("source_hash") == kernel_source_hash() and dom in t.get("stages", {}):
-            traffic = t["stages"][dom]["bytes"]
-    rl["traffic"] = traffic
+    tjson = json.load(open(tf)) if os.path.exists(tf) else None
+
+    def stage_traffic(stage):
+        """HBM bytes per launch of a stage from the committed counter summary,
+        or None when it is missing or the kernels changed since it was taken."""
+        if tjson and tjson.get("source_hash") == kernel_source_hash() and stage in tjson.get("stages", {}):
+            return tjson["stages"][stage]["bytes"]
+        return None
+    rl["traffic"] = stage_traffic(dom)
     dec_b = decode_bytes(p)
     seq_tokens = w.seqs * w.n_tokens
     # compress roofline: algorithmic flops and bytes of the whole pass, each at its peak
@@ -379,6 +399,13 @@ def main():
         "roofline": rl,
         # each main stage against its own roofline (the contraction of the
         # assignment also against the bf16 MFMA peak, whatever bounds it)
+        # the decode kernel against HBM and the whole compression pass against
+        # max(flops at the bf16 MFMA peak, bytes at the HBM peak)
+        "decode_roofline": dict(roofline(p, "dec_stream", stage_ms["dec_stream"]), traffic=stage_traffic("dec_stream")),
+        "compress_roofline": {"bound": "mfma" if comp_flops / (PEAK_BF16_TFLOPS * 1e12) >= comp_bytes / (PEAK_HBM_GBS * 1e9)
+                              else "hbm", "roofline_ms": t_roof * 1e3, "measured_ms": compress_ms,
+                              "frac": t_roof * 1e3 / compress_ms, "algorithmic_flops": comp_flops,
+                              "algorithmic_bytes": comp_bytes},
         "stage_roofline": {k: {"bound": r["bound"], "frac": r["frac"]}
                            for k in ("obs_stats", "obs_score", "assign", "obs_util", "dec_stream") if k in stage_ms
                            for r in [roofline(p, k, stage_ms[k])]},

@@ -22,7 +22,8 @@
  *  - A "unit" is one layer of one sequence: H KV heads of N tokens.  Units are
  *    independent; the residual budget is pooled over the H heads of a unit.
  *  - Supported: head_dim == 128, dtype bf16 or f32, 1 <= window <= n_tokens,
- *    1 <= n_obs <= n_tokens, anchors per head <= 32767.
+ *    1 <= n_obs <= n_tokens, q_per_kv <= 8, anchors per head <= 4096 (see
+ *    anchorkv_plan for the full list; the plan refuses what the kernels cannot run).
  *  - Inputs must be finite, with |x| small enough that residual scales and
  *    zeros fit fp16 (|x| < 1e4 is ample).
  */
@@ -62,12 +63,30 @@ typedef struct {
   int32_t dtype; /* anchorkv_dtype */
 } anchorkv_dims;
 
+/* The method's parameters (Pith review of AnchorKV, "Assumptions & free
+ * parameters": theta the byte budget, W the recency window, k = S/128
+ * non-window anchors, rho = 0.7 of them picked by the observation score,
+ * positional pooling of width kappa = 7; AnchorKV-adapted page, "The one
+ * setting worth tuning": theta is the only knob a user is meant to turn).
+ * Fill with anchorkv_params_default, then change fields as needed. */
+typedef struct {
+  float theta;             /* bytes per side kept: floor(theta*H*N*D*e) per unit (> 0) */
+  int32_t window;          /* last `window` positions are always anchors (1 <= window <= n_tokens) */
+  int32_t anchor_div;      /* non-window anchors k = floor(N / anchor_div), capped by the budget (>= 1; 128) */
+  int32_t pool;            /* width of the positional pooling of the score (odd, 1..15; 7) */
+  double rho;              /* k_scored = floor(rho * k) in double precision, the rest picked uniformly ([0, 1]; 0.7) */
+  int32_t group;           /* residual codec group: one fp16 scale and zero per `group` coordinates (32 only) */
+  int32_t pool_kv_jointly; /* 0: separate residual budgets for K and V (the only value supported) */
+  int32_t reserved[8];     /* zero */
+} anchorkv_params;
+
 /* Everything the host needs about a compressed cache: counts, byte accounting
  * and the per-unit layout.  Filled by anchorkv_plan or anchorkv_plan_from_header. */
 typedef struct {
   /* shape and knobs */
   int32_t units, H, G, N, D, n_obs, dtype, elem_bytes, window;
   float theta;
+  anchorkv_params params;  /* as passed to anchorkv_plan (theta and window repeated above) */
   /* counts per head / per unit (Pith review, "Assumptions & free parameters":
    * k = S/128 non-window anchors, rho = 0.7 scored, window W) */
   int32_t A;          /* anchors per head = window + k_scored + k_uniform */
@@ -108,20 +127,45 @@ const char* anchorkv_version(void);
 /* Message for the last non-zero return on this thread. */
 const char* anchorkv_last_error(void);
 
-/* Counts, byte accounting and layout for (dims, theta, window).  Host only, no
- * HIP calls.  Budget (per KV head and side) B = theta*N*D*e bytes with theta
- * taken at float32 precision; anchors A = window + min(N/128, A_max - window,
+/* Defaults of the method's fixed parameters (anchor_div 128, rho 0.7, pool 7,
+ * group 32, separate K/V budgets) with the given theta and window.  Null is
+ * ignored. */
+void anchorkv_params_default(anchorkv_params* params, float theta, int32_t window);
+
+/* Counts, byte accounting and layout for (dims, params).  Host only, no HIP
+ * calls.  Budget (per KV head and side) B = theta*N*D*e bytes with theta taken
+ * at float32 precision; anchors A = window + min(N/anchor_div, A_max - window,
  * N - window) where A_max is the number of exact anchors the budget pays for
- * after pointers, chunk offsets and header; residual slots per side per unit
+ * after pointers, chunk offsets and header; k_scored = floor(rho*(A - window));
+ * residual slots per side per unit
  * R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed)/(D/4+D/8))).
  * (Pith review, "What carries the argument" and "Assumptions & free
  * parameters"; AnchorKV-adapted page, "The one setting worth tuning".)
- * Errors: E_ARG (null), E_DTYPE, E_SHAPE, E_BUDGET. */
-int anchorkv_plan(const anchorkv_dims* dims, float theta, int32_t window, anchorkv_plan_info* out);
+ * A shape that compress or decode cannot run is refused here: more than 4096
+ * anchors per head, q_per_kv > 8, q_per_kv*n_obs > 256 (128 for f32), or a
+ * decode working set (anchor logits and weights of q_per_kv q-heads) beyond
+ * the 160 KB of LDS.
+ * Errors: E_ARG (null, parameters out of range), E_DTYPE, E_SHAPE, E_BUDGET. */
+int anchorkv_plan(const anchorkv_dims* dims, const anchorkv_params* params, anchorkv_plan_info* out);
 
 /* Rebuild the plan from a host copy of a unit's first 256 bytes (the header
- * compress writes at the start of every unit).  Errors: E_ARG, E_LAYOUT. */
+ * compress writes at the start of every unit; it records dims and params).
+ * Errors: E_ARG, E_LAYOUT. */
 int anchorkv_plan_from_header(const void* header_host, int32_t units, anchorkv_plan_info* out);
+
+/* Section offsets of one unit of a compressed cache (bytes from the unit's
+ * start), read from a host copy of its 256-byte header: for inspection and for
+ * tools that read the cache without the plan. */
+typedef struct {
+  int64_t off_anchor_k, off_anchor_v, off_res_k, off_res_v, off_words, off_chunk_k, off_chunk_v, off_positions;
+  int64_t unit_bytes, unit_stride;
+  int32_t A, R_K, R_V, n_chunks, record_bytes, reserved[3];
+} anchorkv_layout;
+int anchorkv_cache_layout(const void* header_host, anchorkv_layout* out);
+
+/* Decode workspace bytes for `units` units of the cache whose header (host
+ * copy) is given: what anchorkv_decode_attn needs.  Errors: E_ARG, E_LAYOUT. */
+int anchorkv_decode_workspace_bytes(const void* header_host, int32_t units, size_t* out);
 
 /* End-of-prefill compression of all units (Pith review, "What carries the
  * argument"; AnchorKV-adapted page, "Adaptation notes": one pass, no
@@ -159,13 +203,22 @@ int anchorkv_workspace_offsets(const anchorkv_plan_info* plan, int64_t out[8]);
  * (Pith review, "What carries the argument": logits gamma*<q, k_a> + <q, r~>,
  * values reconstructed the same way; softmax over all N compressed tokens,
  * no mask).  The dense cache is never materialised.
- *  cache:  device, as written by anchorkv_compress (or packed on the host).
+ *  plan:   host; the plan the cache was written with (anchorkv_plan, or
+ *          anchorkv_plan_from_header on a host copy of the first unit's
+ *          header).  The launch shape depends on it, and reading it from the
+ *          device cache would cost a device-to-host copy and a wait per call,
+ *          which the library never does.  Instead every workgroup checks its
+ *          unit's header on the device against the plan (magic, H, N, A, R_K,
+ *          R_V, unit size) and, on a mismatch, writes NaN to that unit's
+ *          outputs without reading the rest of the unit.
+ *  cache:  device, >= plan->cache_bytes (cache_bytes is checked), as written
+ *          by anchorkv_compress or packed on the host.
  *  q:      device, [units][H*G][D], cache dtype.
  *  o:      device, [units][H*G][D] float32.
  *  workspace: device, >= plan->decode_workspace_bytes.
  * Errors: E_ARG, E_SMALL_BUFFER, E_HIP. */
-int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, const void* q, float* o,
-                         void* workspace, size_t workspace_bytes, void* stream);
+int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, size_t cache_bytes, const void* q,
+                         float* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode attention over the compressed cache followed by a tail of tokens
  * appended after the one-shot compression and kept uncompressed
@@ -180,9 +233,9 @@ int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, cons
  *  The other arguments are those of anchorkv_decode_attn (same workspace).
  * Errors: E_ARG (null or misaligned buffers, n_tail < 0, n_tail > tail_cap),
  *         E_SMALL_BUFFER, E_HIP. */
-int anchorkv_decode_attn_tail(const anchorkv_plan_info* plan, const void* cache, const void* q, const void* K_tail,
-                              const void* V_tail, int32_t n_tail, int32_t tail_cap, float* o, void* workspace,
-                              size_t workspace_bytes, void* stream);
+int anchorkv_decode_attn_tail(const anchorkv_plan_info* plan, const void* cache, size_t cache_bytes, const void* q,
+                              const void* K_tail, const void* V_tail, int32_t n_tail, int32_t tail_cap, float* o,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-side view of one unit's compressed representation, as plain arrays.
  * All pointers are host memory owned by the caller. */

@@ -31,11 +31,30 @@ class Dims(ct.Structure):
                 ("head_dim", ct.c_int32), ("n_obs", ct.c_int32), ("dtype", ct.c_int32)]
 
 
+class Params(ct.Structure):
+    _fields_ = [("theta", ct.c_float), ("window", ct.c_int32), ("anchor_div", ct.c_int32), ("pool", ct.c_int32),
+                ("rho", ct.c_double), ("group", ct.c_int32), ("pool_kv_jointly", ct.c_int32),
+                ("reserved", ct.c_int32 * 8)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+class Layout(ct.Structure):
+    _fields_ = [(f, ct.c_int64) for f in ("off_anchor_k", "off_anchor_v", "off_res_k", "off_res_v", "off_words",
+                                           "off_chunk_k", "off_chunk_v", "off_positions", "unit_bytes",
+                                           "unit_stride")] + \
+               [(f, ct.c_int32) for f in ("A", "R_K", "R_V", "n_chunks", "record_bytes")] + [("reserved", ct.c_int32 * 3)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
 class PlanInfo(ct.Structure):
     _fields_ = [
         ("units", ct.c_int32), ("H", ct.c_int32), ("G", ct.c_int32), ("N", ct.c_int32), ("D", ct.c_int32),
         ("n_obs", ct.c_int32), ("dtype", ct.c_int32), ("elem_bytes", ct.c_int32), ("window", ct.c_int32),
-        ("theta", ct.c_float),
+        ("theta", ct.c_float), ("params", Params),
         ("A", ct.c_int32), ("k_scored", ct.c_int32), ("k_uniform", ct.c_int32), ("R_K", ct.c_int32),
         ("R_V", ct.c_int32), ("n_chunks", ct.c_int32),
         ("budget_bytes_per_side", ct.c_int64), ("used_bytes_k", ct.c_int64), ("used_bytes_v", ct.c_int64),
@@ -49,7 +68,9 @@ class PlanInfo(ct.Structure):
     ]
 
     def as_dict(self):
-        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("reserved", "params")}
+        d.update({"param_" + k: v for k, v in self.params.as_dict().items()})
+        return d
 
 
 class UnitArrays(ct.Structure):
@@ -71,16 +92,20 @@ def lib():
         L = ct.CDLL(LIB_PATH)
         L.anchorkv_version.restype = ct.c_char_p
         L.anchorkv_last_error.restype = ct.c_char_p
-        L.anchorkv_plan.argtypes = [ct.POINTER(Dims), ct.c_float, ct.c_int32, ct.POINTER(PlanInfo)]
+        L.anchorkv_params_default.argtypes = [ct.POINTER(Params), ct.c_float, ct.c_int32]
+        L.anchorkv_params_default.restype = None
+        L.anchorkv_plan.argtypes = [ct.POINTER(Dims), ct.POINTER(Params), ct.POINTER(PlanInfo)]
         L.anchorkv_plan_from_header.argtypes = [ct.c_void_p, ct.c_int32, ct.POINTER(PlanInfo)]
+        L.anchorkv_cache_layout.argtypes = [ct.c_void_p, ct.POINTER(Layout)]
+        L.anchorkv_decode_workspace_bytes.argtypes = [ct.c_void_p, ct.c_int32, ct.POINTER(ct.c_size_t)]
         L.anchorkv_compress.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                         ct.c_size_t, ct.c_void_p, ct.c_size_t, ct.c_void_p]
         L.anchorkv_workspace_offsets.argtypes = [ct.POINTER(PlanInfo), ct.POINTER(ct.c_int64)]
-        L.anchorkv_decode_attn.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_void_p, ct.c_void_p, ct.c_void_p,
-                                           ct.c_size_t, ct.c_void_p]
-        L.anchorkv_decode_attn_tail.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_void_p, ct.c_void_p,
-                                                ct.c_void_p, ct.c_int32, ct.c_int32, ct.c_void_p, ct.c_void_p,
-                                                ct.c_size_t, ct.c_void_p]
+        L.anchorkv_decode_attn.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_void_p,
+                                           ct.c_void_p, ct.c_size_t, ct.c_void_p]
+        L.anchorkv_decode_attn_tail.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_size_t, ct.c_void_p,
+                                                ct.c_void_p, ct.c_void_p, ct.c_int32, ct.c_int32, ct.c_void_p,
+                                                ct.c_void_p, ct.c_size_t, ct.c_void_p]
         L.anchorkv_unit_pack_host.argtypes = [ct.POINTER(PlanInfo), ct.POINTER(UnitArrays), ct.c_void_p]
         L.anchorkv_unit_unpack_host.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.POINTER(UnitArrays)]
         L.anchorkv_profile_enable.argtypes = [ct.c_int]
@@ -90,7 +115,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ["anchorkv_version", "anchorkv_last_error", "anchorkv_plan", "anchorkv_plan_from_header",
+EXPORTED = ["anchorkv_version", "anchorkv_last_error", "anchorkv_params_default", "anchorkv_plan",
+            "anchorkv_plan_from_header", "anchorkv_cache_layout", "anchorkv_decode_workspace_bytes",
             "anchorkv_compress", "anchorkv_workspace_offsets", "anchorkv_decode_attn", "anchorkv_decode_attn_tail",
             "anchorkv_unit_pack_host",
             "anchorkv_unit_unpack_host", "anchorkv_profile_enable", "anchorkv_profile_read"]
@@ -105,10 +131,25 @@ def version() -> str:
     return lib().anchorkv_version().decode()
 
 
-def plan(units, kv_heads, q_per_kv, n_tokens, head_dim, n_obs, dtype, theta, window) -> PlanInfo:
+def params(theta, window, **kw) -> Params:
+    """The method's parameters: defaults (anchorkv_params_default) with the
+    given theta and window, then any of anchor_div, rho, pool, group,
+    pool_kv_jointly replaced."""
+    q = Params()
+    lib().anchorkv_params_default(ct.byref(q), ct.c_float(theta), int(window))
+    for k, v in kw.items():
+        if k not in ("anchor_div", "rho", "pool", "group", "pool_kv_jointly"):
+            raise TypeError(f"unknown parameter {k}")
+        setattr(q, k, v)
+    return q
+
+
+def plan(units, kv_heads, q_per_kv, n_tokens, head_dim, n_obs, dtype, theta, window, **kw) -> PlanInfo:
+    """anchorkv_plan for the dims and params(theta, window, **kw)."""
     d = Dims(units, kv_heads, q_per_kv, n_tokens, head_dim, n_obs, dtype)
+    q = params(theta, window, **kw)
     p = PlanInfo()
-    _check(lib().anchorkv_plan(ct.byref(d), ct.c_float(theta), window, ct.byref(p)))
+    _check(lib().anchorkv_plan(ct.byref(d), ct.byref(q), ct.byref(p)))
     return p
 
 
@@ -117,6 +158,21 @@ def plan_from_header(header: bytes, units: int) -> PlanInfo:
     buf = ct.create_string_buffer(bytes(header[:256]), 256)
     _check(lib().anchorkv_plan_from_header(buf, units, ct.byref(p)))
     return p
+
+
+def cache_layout(header: bytes) -> dict:
+    """Section offsets of a unit, from a host copy of its header."""
+    lay = Layout()
+    buf = ct.create_string_buffer(bytes(header[:256]), 256)
+    _check(lib().anchorkv_cache_layout(buf, ct.byref(lay)))
+    return lay.as_dict()
+
+
+def decode_workspace_bytes(header: bytes, units: int) -> int:
+    n = ct.c_size_t(0)
+    buf = ct.create_string_buffer(bytes(header[:256]), 256)
+    _check(lib().anchorkv_decode_workspace_bytes(buf, units, ct.byref(n)))
+    return int(n.value)
 
 
 def workspace_offsets(p: PlanInfo) -> dict:
@@ -165,15 +221,23 @@ def compress(p: PlanInfo, K, V, Q, cache, workspace, stream=None):
                                    _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
+def _check_cache(fn, p: PlanInfo, cache):
+    import torch
+    if cache.dtype != torch.uint8 or cache.numel() < p.cache_bytes:
+        raise ValueError(f"{fn}: cache must be a uint8 tensor of >= {p.cache_bytes} bytes, "
+                         f"got {cache.dtype} with {cache.numel()} elements")
+
+
 def decode_attn(p: PlanInfo, cache, q, o, workspace, stream=None):
     """Enqueue decode attention: q [U, H*G, D] cache dtype -> o [U, H*G, D] float32."""
     for t in (cache, q, o, workspace):
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError("decode_attn: inputs must be contiguous device tensors")
     import torch
+    _check_cache("decode_attn", p, cache)
     _expect("decode_attn", "q", q, (p.units, p.H * p.G, p.D), _elem_dtype(p))
     _expect("decode_attn", "o", o, (p.units, p.H * p.G, p.D), torch.float32)
-    _check(lib().anchorkv_decode_attn(ct.byref(p), _ptr(cache), _ptr(q), _ptr(o), _ptr(workspace),
+    _check(lib().anchorkv_decode_attn(ct.byref(p), _ptr(cache), _nbytes(cache), _ptr(q), _ptr(o), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream)))
 
 
@@ -188,11 +252,12 @@ def decode_attn_tail(p: PlanInfo, cache, q, K_tail, V_tail, n_tail: int, o, work
     if K_tail.dim() != 4:
         raise ValueError("decode_attn_tail: K_tail must be [U, H, tail_cap, D]")
     cap = int(K_tail.shape[2])
+    _check_cache("decode_attn_tail", p, cache)
     _expect("decode_attn_tail", "q", q, (p.units, p.H * p.G, p.D), _elem_dtype(p))
     _expect("decode_attn_tail", "o", o, (p.units, p.H * p.G, p.D), torch.float32)
     _expect("decode_attn_tail", "K_tail", K_tail, (p.units, p.H, cap, p.D), _elem_dtype(p))
     _expect("decode_attn_tail", "V_tail", V_tail, (p.units, p.H, cap, p.D), _elem_dtype(p))
-    _check(lib().anchorkv_decode_attn_tail(ct.byref(p), _ptr(cache), _ptr(q), _ptr(K_tail), _ptr(V_tail),
+    _check(lib().anchorkv_decode_attn_tail(ct.byref(p), _ptr(cache), _nbytes(cache), _ptr(q), _ptr(K_tail), _ptr(V_tail),
                                            int(n_tail), int(K_tail.shape[2]), _ptr(o), _ptr(workspace),
                                            _nbytes(workspace), _stream(stream)))
 

@@ -160,8 +160,8 @@ __device__ void find_bucket(const unsigned* hist, int nbins, unsigned need, int*
 
 // ---------------------------------------------------------- anchor selection
 constexpr int kSelectLdsMaxL = 32768;   // pooled score in LDS up to this many positions (128 KB)
-// One 1024-thread block per (unit, head).  score -> pooled (width 7 window
-// sum over non-window positions) -> top k_s (radix select on the f32 bits,
+// One 1024-thread block per (unit, head).  score -> pooled (window sum of
+// odd width `pool`, 7 by default, over non-window positions) -> top k_s (radix select on the f32 bits,
 // ties to the lower position) -> k_u stratified picks over the remaining
 // positions (pick i = remaining[floor((2i+1) M / (2 k_u))]) -> + window ->
 // positions ascending, anchor_of map, anchor copies, norms.  With LP the
@@ -171,7 +171,7 @@ template <int DT, bool LP>
 __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv, const float* score, float* pooled,
                                                  uint8_t* cache, int64_t stride, int64_t off_ak, int64_t off_av,
                                                  int64_t off_pos, int* anchor_of, float2* anorm, int H, int N, int W,
-                                                 int k_s, int k_u, int A) {
+                                                 int k_s, int k_u, int A, int pool) {
   using T = typename Elem<DT>::T;
   constexpr int D = kHeadDim;
   __shared__ unsigned hist[kHistBins];
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
   __shared__ int s_b;
   __shared__ unsigned s_above;
   __shared__ int s_pos[4096];  // scored + uniform positions (A <= 4096 is checked on the host)
-  __shared__ float stg[1024 + 6];
+  __shared__ float stg[1024 + kMaxPool - 1];
   extern __shared__ float plds[];
   const int h = blockIdx.x % H;
   const int u = blockIdx.x / H;
@@ -189,8 +189,9 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
   float* pl = LP ? plds : pooled + uh * N;
   const int tid = threadIdx.x, nt = blockDim.x;
 
-  // pooled_t = score_{t-3} + ... + score_{t+3} over [0, L) (zeros outside,
-  // added in position order)
+  // pooled_t = score_{t-hw} + ... + score_{t+hw} over [0, L), hw = pool/2
+  // (zeros outside, added in position order)
+  const int hw = pool >> 1;
   if constexpr (LP) {
     // whole score in LDS (all loads in flight at once), pooled values in
     // registers, then written over it
@@ -204,9 +205,8 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
       const int t = tid + k * nt;
       float v = 0.0f;
       if (t < L)
-#pragma unroll
-        for (int j = 0; j < 7; ++j) {
-          const int x = t - 3 + j;
+        for (int j = 0; j < pool; ++j) {
+          const int x = t - hw + j;
           v += (x >= 0 && x < L) ? pl[x] : 0.0f;
         }
       pv[k] = v;
@@ -217,18 +217,17 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
       if (tid + k * nt < L) pl[tid + k * nt] = pv[k];
     __syncthreads();
   } else {
-    // 1024-position chunks of the score staged with a 3-position halo
+    // 1024-position chunks of the score staged with an hw-position halo
     for (int t0 = 0; t0 < L; t0 += nt) {
-      for (int i = tid; i < nt + 6; i += nt) {
-        const int x = t0 - 3 + i;
+      for (int i = tid; i < nt + 2 * hw; i += nt) {
+        const int x = t0 - hw + i;
         stg[i] = (x >= 0 && x < L) ? sc[x] : 0.0f;
       }
       __syncthreads();
       const int t = t0 + tid;
       if (t < L) {
         float v = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 7; ++k) v += stg[tid + k];
+        for (int k = 0; k < pool; ++k) v += stg[tid + k];
         pl[t] = v;
       }
       __syncthreads();
@@ -1031,7 +1030,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
       kern<<<(unsigned)(U * H), 1024, dyn, st>>>(
           K, V, a.score, reinterpret_cast<float*>(ws + w.pooled), cache, p.unit_stride, p.off_anchor_k,
           p.off_anchor_v, p.off_positions, reinterpret_cast<int*>(ws + w.anchor_of),
-          reinterpret_cast<float2*>(ws + w.anorm), H, N, p.window, p.k_scored, p.k_uniform, A);
+          reinterpret_cast<float2*>(ws + w.anorm), H, N, p.window, p.k_scored, p.k_uniform, A, p.params.pool);
     };
     if (N - p.window <= kSelectLdsMaxL) {
       static size_t sdone = 0;
@@ -1089,6 +1088,15 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
     AKV_CHECK_LAUNCH("k_quant");
   }
   prof_mark(st, "quant");
+  return 0;
+}
+
+int compress_supports(const anchorkv_plan_info& p) {
+  const int QB = padded_queries(p) / 16;
+  if (p.dtype == ANCHORKV_F32 && QB > 8) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: f32 needs q_per_kv*n_obs <= 128");
+  if (QB > 16) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: q_per_kv*n_obs must be <= 256");
+  if (p.A > 4096) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %d anchors per head; compress supports <= 4096", p.A);
+  if (p.params.pool > kMaxPool) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: pool width > %d", kMaxPool);
   return 0;
 }
 

@@ -11,9 +11,9 @@
 //    into LDS;
 //  * tiles of 1024 tokens: S lookups, residual-key logits, softmax weights;
 //    the value side scatters p_t gamma^V_t into w[a(t)][g] (LDS, 64-bit fixed
-//    point with scale 2^21: LDS integer atomics are an order of magnitude
-//    faster than LDS float atomics on this part and make the sum independent
-//    of order) and sums p r~^V on MFMA;
+//    point with scale 2^38, each term rounded to nearest: LDS integer atomics
+//    are an order of magnitude faster than LDS float atomics on this part and
+//    make the sum independent of order) and sums p r~^V on MFMA;
 //  * epilogue: w V_anchors on MFMA plus the residual part; with several
 //    token ranges per head, the last range's workgroup merges the partial
 //    (max, sum, output) triples.
@@ -25,7 +25,14 @@
 // split into bf16 hi + lo.
 // One workgroup (8 waves) per (unit, head, 1024-token-aligned range).  The
 // running max is shared by the workgroup and only raised (rescaling w, l and
-// the accumulators) when a tile exceeds it by more than 2^8.
+// the accumulators) when a tile exceeds it by more than 2^1, so p <= 2.
+//
+// Fixed-point range: a term is p gamma 2^38 rounded to the nearest integer,
+// so terms down to about 2^-28 of the running maximum keep 10 significant
+// bits and the rounding bias over a whole range (<= 2^17 tokens) stays below
+// 2^-21 of it; a peaked softmax (a few keys 15-20 nats above a long flat
+// background) therefore keeps its background mass.  The sum over a range
+// stays below 2^63 while the mean |gamma| of its tokens is below 2^6.
 #include "device_common.hpp"
 #include "launch_common.hpp"
 
@@ -39,12 +46,16 @@ constexpr int kMaxG = 8;          // q-heads per KV head supported by decode
 constexpr int kTile = 1024;       // tokens per tile (= residual-offset chunk)
 constexpr int kWaves = 8;         // waves per workgroup; 128 tokens per wave per tile
 constexpr uint32_t kCodeBias = 0x43004300u;  // bf16 pair (128, 128)
-constexpr float kFxScale = 2097152.0f;          // 2^21: fixed-point scale of the w scatter
-constexpr double kFxInv = 1.0 / 2097152.0;
+constexpr float kFxScale = 0x1p38f;               // fixed-point scale of the w scatter
+constexpr double kFxScaleD = 0x1p38;
+constexpr double kFxInv = 0x1p-38;
+constexpr double kRoundMagic = 0x1.8p52;           // x + 1.5*2^52 rounds x (|x| < 2^51) to an integer
+constexpr unsigned long long kMagicMask = 0x0007FFFFFFFFFFFFull;  // low 51 bits: that integer, for x >= 0
+constexpr float kLazy = 1.0f;                      // rescale when a logit passes m_run + kLazy (log2 units)
 // floats of the per-tile buffer: [kTile][G], at least the 8 KB of staged words
 template <int G> constexpr int kBufFloats = kTile * G > 2048 ? kTile * G : 2048;
 
-// y (already scaled by 2^21) -> two's-complement 64-bit fixed point, any sign
+// y (already scaled by 2^38) -> two's-complement 64-bit fixed point, any sign
 // and |y| < 2^62.
 __device__ __forceinline__ unsigned long long fx_general(float y) {
   const float a = fabsf(y);
@@ -210,6 +221,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const uint8_t* recK = base + a.off_rk;
   const uint8_t* recV = base + a.off_rv;
   const T* q = reinterpret_cast<const T*>(a.q) + uh * G * D;
+
+  // The unit's header must describe the cache the plan describes; a unit that
+  // does not (another plan's cache, a unit never written) gives NaN outputs
+  // and nothing past its header is read.  Uniform: every thread reads the
+  // same words.
+  {
+    const UnitHeader* hd = reinterpret_cast<const UnitHeader*>(base);
+    if (hd->magic != kMagic || hd->H != a.H || hd->N != a.N || hd->A != A || hd->R_K != a.R_K || hd->R_V != a.R_V ||
+        hd->unit_stride != a.stride || hd->off_words != a.off_words) {
+      const float nan = __builtin_nanf("");
+      if (a.S2 == 1 && !a.force_part) {
+        for (int i = threadIdx.x; i < G * D; i += blockDim.x) a.o[uh * G * D + i] = nan;
+      } else {
+        const int64_t ps = uh * a.S2 + sp;
+        for (int i = threadIdx.x; i < G * D; i += blockDim.x) a.part_acc[ps * G * D + i] = nan;
+        if (threadIdx.x < G) a.part_ml[ps * G + threadIdx.x] = make_float2(nan, nan);
+      }
+      return;
+    }
+  }
 
   // q of this head as floats in LDS ([G][D]; buf is free until the first tile)
   float* qf = buf;
@@ -479,9 +510,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       for (int g = 0; g < G; ++g) {
         s0[g] = v0 ? fmaf(gK0, S0[g], R0[g]) : -INFINITY;
         s1[g] = v1 ? fmaf(gK1, S1[g], R1[g]) : -INFINITY;
-        hot |= fmaxf(s0[g], s1[g]) > m_run[g] + 8.0f;
+        hot |= fmaxf(s0[g], s1[g]) > m_run[g] + kLazy;
       }
-      // Only a logit above m_run + 8 changes anything (the rescale below);
+      // Only a logit above m_run + kLazy changes anything (the rescale below);
       // a wave holding one publishes its exact maximum, the others nothing
       // (their maxima are smaller than any such logit).
       if (__any(hot)) {
@@ -514,7 +545,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       for (int g = 0; g < G; ++g) {
         const float tm = fkey_inv(tk[g]);
         fct[g] = 1.0f;
-        if (tm > m_run[g] + 8.0f) {
+        if (tm > m_run[g] + kLazy) {
           fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
           m_run[g] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tm)));  // uniform
           any = true;
@@ -554,17 +585,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     // tokens in this wave's buf rows [0, nV) and zeros in the rows after them
     // up to the next multiple of 32 (the value batches read whole batches).
     // A token past the range has p = 0 and adds 0 to w[0].
-    // p <= 2^8 (lazy rescale), so gamma in [0, 8) keeps p*gamma*2^21 in [0, 2^32).
+    // p <= 2 (lazy rescale), so gamma in [0, 8) keeps y = p*gamma*2^38 in
+    // [0, 2^42): one f64 fma adds 1.5*2^52, which rounds y to the nearest
+    // integer and leaves it in the low 51 bits (p and gamma are exact in f64,
+    // so this is the only rounding).
     {
       const float gs0 = gV0 * kFxScale, gs1 = gV1 * kFxScale;
       const bool fast = __all((!v0 || (gV0 >= 0.0f && gV0 < 8.0f)) && (!v1 || (gV1 >= 0.0f && gV1 < 8.0f)));
 #pragma unroll
       for (int g = 0; g < G; ++g) lacc[g] += pk0[g] + pk1[g];
       if (fast) {
+        const double gd0 = (double)gV0 * kFxScaleD, gd1 = (double)gV1 * kFxScaleD;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          atomicAdd(wi + g * A + aV0, (unsigned long long)(unsigned)fmaf(pk0[g], gs0, 0.5f));
-          atomicAdd(wi + g * A + aV1, (unsigned long long)(unsigned)fmaf(pk1[g], gs1, 0.5f));
+          atomicAdd(wi + g * A + aV0,
+                    (unsigned long long)__double_as_longlong(fma((double)pk0[g], gd0, kRoundMagic)) & kMagicMask);
+          atomicAdd(wi + g * A + aV1,
+                    (unsigned long long)__double_as_longlong(fma((double)pk1[g], gd1, kRoundMagic)) & kMagicMask);
         }
       } else {
 #pragma unroll
@@ -1048,10 +1085,14 @@ static int launch_stream_kp(const DecArgs& a, unsigned grid, hipStream_t st) {
 // tile) from the average number of residual records per 1024-token tile:
 // larger staging costs registers and LDS, records beyond it are read from
 // the cache directly.
-static int decode_kp(int G, int64_t R_K, int64_t R_V, int64_t H, int64_t C) {
+// Falls back to the largest staging that fits LDS (KP = 1 always fits a plan
+// that anchorkv_plan accepted).
+static int decode_kp(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C) {
   if (G > 4) return 1;
   const int64_t per = std::max(R_K, R_V) / std::max<int64_t>(1, H * C);
-  return per <= 150 ? 1 : per <= 300 ? 2 : 3;
+  int kp = per <= 150 ? 1 : per <= 300 ? 2 : 3;
+  while (kp > 1 && stream_lds(G, A, kp, f32) > kLdsLimit) --kp;
+  return kp;
 }
 
 // Up to 4 q-heads per KV head: four waves per SIMD (two workgroups per CU);
@@ -1059,7 +1100,7 @@ static int decode_kp(int G, int64_t R_K, int64_t R_V, int64_t H, int64_t C) {
 template <int DT, int G>
 static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
   if constexpr (G <= 4) {
-    switch (decode_kp(G, a.R_K, a.R_V, a.H, a.C)) {
+    switch (decode_kp(G, a.A, DT == ANCHORKV_F32, a.R_K, a.R_V, a.H, a.C)) {
       case 1: return launch_stream_kp<DT, G, 1, 1, 4>(a, grid, st);
       case 2: return launch_stream_kp<DT, G, 2, 1, 4>(a, grid, st);
       default: return launch_stream_kp<DT, G, 3, 1, 4>(a, grid, st);
@@ -1133,8 +1174,17 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
 int decode_blocks_per_cu(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C) {
   // G <= 4 runs at four waves per SIMD (two 8-wave workgroups) when two
   // copies of its LDS fit the 160 KB (static part under 2 KB each)
-  const int kp = decode_kp(G, R_K, R_V, H, C);
+  const int kp = decode_kp(G, A, f32, R_K, R_V, H, C);
   return (G <= 4 && 2 * (stream_lds(G, A, kp, f32) + 2048) <= 160 * 1024) ? 2 : 1;
+}
+
+int decode_supports(const anchorkv_plan_info& p) {
+  if (p.G > kMaxG) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: decode supports q_per_kv <= %d", kMaxG);
+  if (stream_lds(p.G, p.A, 1, p.dtype == ANCHORKV_F32) > kLdsLimit)
+    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %d anchors x %d q-heads exceed the decode kernel's LDS", p.A, p.G);
+  if (p.decode_splits > 64 || p.n_chunks > 128 * p.decode_splits)
+    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: n_tokens %d too large for the decode ranges", p.N);
+  return 0;
 }
 
 int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* ws, void* stream) {

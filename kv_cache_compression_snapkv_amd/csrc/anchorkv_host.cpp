@@ -137,10 +137,41 @@ void fill_header(const anchorkv_plan_info& p, UnitHeader* h) {
   h->off_res_k = p.off_res_k; h->off_res_v = p.off_res_v; h->off_words = p.off_words;
   h->off_chunk_k = p.off_chunk_k; h->off_chunk_v = p.off_chunk_v; h->off_positions = p.off_positions;
   h->unit_bytes = p.unit_bytes; h->unit_stride = p.unit_stride;
+  h->anchor_div = p.params.anchor_div; h->pool = p.params.pool; h->group = p.params.group;
+  h->pool_kv_jointly = p.params.pool_kv_jointly; h->rho = p.params.rho;
 }
 
-static int plan_impl(const anchorkv_dims* d, float theta, int32_t window, anchorkv_plan_info* out) {
-  if (!d || !out) return fail(ANCHORKV_E_ARG, "anchorkv_plan: null argument");
+static void params_default(anchorkv_params* q, float theta, int32_t window) {
+  std::memset(q, 0, sizeof(*q));
+  q->theta = theta;
+  q->window = window;
+  q->anchor_div = 128;
+  q->rho = 0.7;
+  q->pool = 7;
+  q->group = kGroup;
+  q->pool_kv_jointly = 0;
+}
+
+static int check_params(const anchorkv_params& q) {
+  if (!(q.theta > 0.0f) || !std::isfinite(q.theta)) return fail(ANCHORKV_E_ARG, "anchorkv_plan: theta must be > 0");
+  if (q.anchor_div < 1) return fail(ANCHORKV_E_ARG, "anchorkv_plan: anchor_div %d must be >= 1", q.anchor_div);
+  if (!(q.rho >= 0.0 && q.rho <= 1.0)) return fail(ANCHORKV_E_ARG, "anchorkv_plan: rho must be in [0, 1]");
+  if (q.pool < 1 || q.pool > kMaxPool || q.pool % 2 == 0)
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: pool %d must be odd and in [1, %d]", q.pool, kMaxPool);
+  if (q.group != kGroup) return fail(ANCHORKV_E_ARG, "anchorkv_plan: codec group %d: only %d is supported", q.group, kGroup);
+  if (q.pool_kv_jointly != 0)
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: pool_kv_jointly %d: only separate K/V budgets (0) are supported",
+                q.pool_kv_jointly);
+  for (int i = 0; i < (int)(sizeof(q.reserved) / sizeof(q.reserved[0])); ++i)
+    if (q.reserved[i] != 0) return fail(ANCHORKV_E_ARG, "anchorkv_plan: reserved parameter fields must be zero");
+  return 0;
+}
+
+static int plan_impl(const anchorkv_dims* d, const anchorkv_params* prm, anchorkv_plan_info* out) {
+  if (!d || !prm || !out) return fail(ANCHORKV_E_ARG, "anchorkv_plan: null argument");
+  if (int rc = check_params(*prm)) return rc;
+  const float theta = prm->theta;
+  const int32_t window = prm->window;
   if (d->dtype != ANCHORKV_BF16 && d->dtype != ANCHORKV_F32)
     return fail(ANCHORKV_E_DTYPE, "anchorkv_plan: dtype %d is not bf16 (1) or f32 (2)", d->dtype);
   if (d->head_dim != kHeadDim) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: head_dim %d != 128", d->head_dim);
@@ -152,10 +183,10 @@ static int plan_impl(const anchorkv_dims* d, float theta, int32_t window, anchor
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: window %d outside [1, n_tokens]", window);
   if ((int64_t)d->kv_heads * d->n_tokens > (1ll << 30) || (int64_t)d->q_per_kv * d->n_obs > 4096)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: kv_heads*n_tokens or q_per_kv*n_obs too large");
-  if (!(theta > 0.0f) || !std::isfinite(theta)) return fail(ANCHORKV_E_ARG, "anchorkv_plan: theta must be > 0");
 
   anchorkv_plan_info p;
   std::memset(&p, 0, sizeof(p));
+  p.params = *prm;
   p.units = d->units; p.H = d->kv_heads; p.G = d->q_per_kv; p.N = d->n_tokens; p.D = d->head_dim;
   p.n_obs = d->n_obs; p.dtype = d->dtype; p.elem_bytes = d->dtype == ANCHORKV_BF16 ? 2 : 4;
   p.window = window; p.theta = theta;
@@ -170,8 +201,8 @@ static int plan_impl(const anchorkv_dims* d, float theta, int32_t window, anchor
   if (amax_d < (double)W)
     return fail(ANCHORKV_E_BUDGET, "anchorkv_plan: theta %.6g cannot pay for %d window anchors and the pointers", th, window);
   const int64_t A_max = (int64_t)amax_d;
-  const int64_t k_nw = std::max<int64_t>(0, std::min(std::min(N / 128, A_max - W), N - W));
-  const int64_t k_s = (int64_t)std::floor(0.7 * (double)k_nw);
+  const int64_t k_nw = std::max<int64_t>(0, std::min(std::min(N / prm->anchor_div, A_max - W), N - W));
+  const int64_t k_s = std::min(k_nw, (int64_t)std::floor(prm->rho * (double)k_nw));
   const int64_t A = W + k_nw;
   if (A > kMaxAnchors) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %lld anchors exceed the 15-bit index", (long long)A);
   p.A = (int32_t)A; p.k_scored = (int32_t)k_s; p.k_uniform = (int32_t)(k_nw - k_s);
@@ -185,7 +216,28 @@ static int plan_impl(const anchorkv_dims* d, float theta, int32_t window, anchor
   p.used_bytes_v = fixed + R * rec;
   layout(&p);
   p.compression_ratio = (double)(2 * H * N * D * e) / (double)p.unit_bytes;
+  if (int rc = compress_supports(p)) return rc;
+  if (int rc = decode_supports(p)) return rc;
   *out = p;
+  return 0;
+}
+
+// Plan of `units` units from a host copy of a unit header.
+static int plan_from_header_impl(const void* header_host, int32_t units, anchorkv_plan_info* out, const char* fn) {
+  if (!header_host || !out || units < 1) return fail(ANCHORKV_E_ARG, "%s: bad argument", fn);
+  UnitHeader h;
+  std::memcpy(&h, header_host, sizeof(h));
+  if (h.magic != kMagic || h.version != 1) return fail(ANCHORKV_E_LAYOUT, "%s: bad magic/version", fn);
+  anchorkv_dims d{units, h.H, h.G, h.N, h.D, h.n_obs, h.dtype};
+  anchorkv_params q;
+  params_default(&q, h.theta, h.window);
+  q.anchor_div = h.anchor_div; q.rho = h.rho; q.pool = h.pool; q.group = h.group;
+  q.pool_kv_jointly = h.pool_kv_jointly;
+  int rc = plan_impl(&d, &q, out);
+  if (rc) return rc == ANCHORKV_E_ARG ? fail(ANCHORKV_E_LAYOUT, "%s: header parameters are invalid", fn) : rc;
+  if (out->A != h.A || out->R_K != h.R_K || out->R_V != h.R_V || out->unit_bytes != h.unit_bytes ||
+      out->off_words != h.off_words || out->k_scored != h.k_scored || out->unit_stride != h.unit_stride)
+    return fail(ANCHORKV_E_LAYOUT, "%s: header does not match its own plan", fn);
   return 0;
 }
 
@@ -199,21 +251,36 @@ const char* anchorkv_version(void) { return "anchorkv-mi355x 0.1 (gfx950)"; }
 
 const char* anchorkv_last_error(void) { return g_err; }
 
-int anchorkv_plan(const anchorkv_dims* dims, float theta, int32_t window, anchorkv_plan_info* out) {
-  return plan_impl(dims, theta, window, out);
+void anchorkv_params_default(anchorkv_params* params, float theta, int32_t window) {
+  if (params) params_default(params, theta, window);
+}
+
+int anchorkv_plan(const anchorkv_dims* dims, const anchorkv_params* params, anchorkv_plan_info* out) {
+  return plan_impl(dims, params, out);
 }
 
 int anchorkv_plan_from_header(const void* header_host, int32_t units, anchorkv_plan_info* out) {
-  if (!header_host || !out || units < 1) return fail(ANCHORKV_E_ARG, "anchorkv_plan_from_header: bad argument");
-  UnitHeader h;
-  std::memcpy(&h, header_host, sizeof(h));
-  if (h.magic != kMagic || h.version != 1) return fail(ANCHORKV_E_LAYOUT, "anchorkv_plan_from_header: bad magic/version");
-  anchorkv_dims d{units, h.H, h.G, h.N, h.D, h.n_obs, h.dtype};
-  int rc = plan_impl(&d, h.theta, h.window, out);
-  if (rc) return rc;
-  if (out->A != h.A || out->R_K != h.R_K || out->R_V != h.R_V || out->unit_bytes != h.unit_bytes ||
-      out->off_words != h.off_words)
-    return fail(ANCHORKV_E_LAYOUT, "anchorkv_plan_from_header: header does not match its own plan");
+  return plan_from_header_impl(header_host, units, out, "anchorkv_plan_from_header");
+}
+
+int anchorkv_cache_layout(const void* header_host, anchorkv_layout* out) {
+  if (!out) return fail(ANCHORKV_E_ARG, "anchorkv_cache_layout: null argument");
+  anchorkv_plan_info p;
+  if (int rc = plan_from_header_impl(header_host, 1, &p, "anchorkv_cache_layout")) return rc;
+  std::memset(out, 0, sizeof(*out));
+  out->off_anchor_k = p.off_anchor_k; out->off_anchor_v = p.off_anchor_v;
+  out->off_res_k = p.off_res_k; out->off_res_v = p.off_res_v; out->off_words = p.off_words;
+  out->off_chunk_k = p.off_chunk_k; out->off_chunk_v = p.off_chunk_v; out->off_positions = p.off_positions;
+  out->unit_bytes = p.unit_bytes; out->unit_stride = p.unit_stride;
+  out->A = p.A; out->R_K = p.R_K; out->R_V = p.R_V; out->n_chunks = p.n_chunks; out->record_bytes = kRecBytes;
+  return 0;
+}
+
+int anchorkv_decode_workspace_bytes(const void* header_host, int32_t units, size_t* out) {
+  if (!out) return fail(ANCHORKV_E_ARG, "anchorkv_decode_workspace_bytes: null argument");
+  anchorkv_plan_info p;
+  if (int rc = plan_from_header_impl(header_host, units, &p, "anchorkv_decode_workspace_bytes")) return rc;
+  *out = (size_t)p.decode_workspace_bytes;
   return 0;
 }
 
@@ -238,9 +305,12 @@ int anchorkv_compress(const anchorkv_plan_info* plan, const void* K, const void*
   return run_compress(*plan, K, V, Q_obs, cache, workspace, stream);
 }
 
-int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, const void* q, float* o, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, size_t cache_bytes, const void* q, float* o,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan || !cache || !q || !o || !workspace) return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn: null argument");
+  if ((int64_t)cache_bytes < plan->cache_bytes)
+    return fail(ANCHORKV_E_SMALL_BUFFER, "anchorkv_decode_attn: cache %zu < %lld bytes", cache_bytes,
+                (long long)plan->cache_bytes);
   if ((int64_t)workspace_bytes < plan->decode_workspace_bytes)
     return fail(ANCHORKV_E_SMALL_BUFFER, "anchorkv_decode_attn: workspace %zu < %lld bytes", workspace_bytes,
                 (long long)plan->decode_workspace_bytes);
@@ -249,10 +319,13 @@ int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, cons
   return run_decode(*plan, cache, q, o, workspace, stream);
 }
 
-int anchorkv_decode_attn_tail(const anchorkv_plan_info* plan, const void* cache, const void* q, const void* K_tail,
-                              const void* V_tail, int32_t n_tail, int32_t tail_cap, float* o, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+int anchorkv_decode_attn_tail(const anchorkv_plan_info* plan, const void* cache, size_t cache_bytes, const void* q,
+                              const void* K_tail, const void* V_tail, int32_t n_tail, int32_t tail_cap, float* o,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan || !cache || !q || !o || !workspace) return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_tail: null argument");
+  if ((int64_t)cache_bytes < plan->cache_bytes)
+    return fail(ANCHORKV_E_SMALL_BUFFER, "anchorkv_decode_attn_tail: cache %zu < %lld bytes", cache_bytes,
+                (long long)plan->cache_bytes);
   if (n_tail < 0 || tail_cap < n_tail)
     return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_tail: need 0 <= n_tail (%d) <= tail_cap (%d)", n_tail, tail_cap);
   if (n_tail > 0 && (!K_tail || !V_tail)) return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_tail: null tail");

@@ -76,7 +76,10 @@ struct UnitHeader {
   int64_t off_anchor_k, off_anchor_v, off_res_k, off_res_v, off_words, off_chunk_k, off_chunk_v, off_positions;
   int64_t unit_bytes, unit_stride;
   int32_t unit_index, pad0;
-  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8];
+  // the method's fixed parameters the unit was compressed with
+  int32_t anchor_div, pool, group, pool_kv_jointly;
+  double rho;
+  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8 - 4 * 4 - 8];
 };
 static_assert(sizeof(UnitHeader) == 256, "header must be 256 bytes");
 void fill_header(const anchorkv_plan_info& p, UnitHeader* h);
@@ -95,5 +98,10 @@ int run_decode_tail(const anchorkv_plan_info& p, const void* cache, const void* 
                     const void* V_tail, int n_tail, int tail_cap, float* o, void* ws, void* stream);
 // Workgroups of the decode kernel that fit one compute unit (LDS and registers).
 int decode_blocks_per_cu(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C);
+// Host-only checks (no HIP calls) that the kernels can run a plan: 0, or a
+// negative code with the message set.  anchorkv_plan refuses what fails them.
+int compress_supports(const anchorkv_plan_info& p);
+int decode_supports(const anchorkv_plan_info& p);
+constexpr int kMaxPool = 15;          // widest positional pooling of the anchor score
 
 }  // namespace akv

@@ -84,8 +84,11 @@ class Plan:
     n_chunks: int
 
 
-def plan(H, N, D, e, theta, W):
+def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO):
     """Anchor and residual counts of one unit.
+
+    anchor_div and rho are the method's k = S/128 and 0.7 [Pith, "Assumptions
+    & free parameters"], exposed as parameters (defaults are the pages' values).
 
     theta is taken at float32 precision (the value the C ABI receives) and all
     byte arithmetic is done in float64 then floored.
@@ -95,11 +98,11 @@ def plan(H, N, D, e, theta, W):
     4-byte residual offset, and the unit header 128 bytes per side, spread over
     the H heads:
         A_max = floor((B - 4N - 4*ceil(N/1024) - 128/H) / (D*e + 2)).
-    Reading R2: k = floor(N/128) non-window anchors, capped so the anchors fit
-    the budget and so that there are enough non-window tokens:
-        k_nw = max(0, min(floor(N/128), A_max - W, N - W)).
+    Reading R2: k = floor(N/anchor_div) non-window anchors, capped so the
+    anchors fit the budget and so that there are enough non-window tokens:
+        k_nw = max(0, min(floor(N/anchor_div), A_max - W, N - W)).
     Reading R3: the window is not part of k: A = W + k_nw.
-    Reading R4: k_s = floor(0.7 * k_nw) scored, k_u = k_nw - k_s uniform.
+    Reading R4: k_s = floor(rho * k_nw) scored (float64), k_u = k_nw - k_s uniform.
     Residual slots per side per unit (pooled over heads; reading R16):
         R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed) / (D/4 + D/8))).
     """
@@ -111,8 +114,8 @@ def plan(H, N, D, e, theta, W):
     A_max = math.floor((B - 4.0 * N - 4.0 * C - HEADER_PER_SIDE / H) / (D * e + 2))
     if A_max < W:
         raise ValueError("budget too small for the window anchors and pointers")
-    k_nw = max(0, min(N // ANCHOR_DIV, A_max - W, N - W))
-    k_s = math.floor(RHO * k_nw)
+    k_nw = max(0, min(N // anchor_div, A_max - W, N - W))
+    k_s = math.floor(rho * k_nw)
     k_u = k_nw - k_s
     A = W + k_nw
     if A > MAX_ANCHORS:
@@ -158,14 +161,15 @@ def obs_attention(Qh, Kh, Vh, n_obs):
 # argument"; "Assumptions & free parameters" (pooling width kappa = 7, pooled
 # over GQA query heads)].
 # --------------------------------------------------------------------------
-def anchor_score(P, W):
+def anchor_score(P, W, pool=POOL):
     """score_t = sum over the head's observation queries of P[:, t] (reading R7),
-    for every t; pooled_t = sum of score_u over |u - t| <= 3 and u < N - W
-    (reading R6: windowed sum = zero-padded mean over 7), for t < N - W."""
+    for every t; pooled_t = sum of score_u over |u - t| <= pool // 2 and
+    u < N - W (reading R6: windowed sum = zero-padded mean over the odd width
+    pool, 7 on the pages), for t < N - W."""
     N = P.shape[1]
     score = P.sum(axis=0)
     L = N - W
-    half = POOL // 2
+    half = pool // 2
     pooled = np.zeros(L)
     for t in range(L):
         lo, hi = max(0, t - half), min(L, t + half + 1)
@@ -375,8 +379,12 @@ class Compressed:
 
 
 def compress_unit(K, V, Q, G, n_obs, theta, W, e,
-                  anchor_override=None, idx_override=None, flag_override=None):
+                  anchor_override=None, idx_override=None, flag_override=None,
+                  anchor_div=ANCHOR_DIV, rho=RHO, pool=POOL):
     """K, V: [H, N, D] float64; Q: [H*G, n_obs, D] float64.
+
+    anchor_div, rho, pool: the method's fixed parameters (see plan and
+    anchor_score), the pages' values by default.
 
     The *_override arguments let a parity test continue from decisions the GPU
     took where the oracle's own decision was within the stated tie margin:
@@ -384,7 +392,7 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
     [2, H, N] bool.  The test checks the overrides before passing them.
     """
     H, N, D = K.shape
-    p = plan(H, N, D, e, theta, W)
+    p = plan(H, N, D, e, theta, W, anchor_div, rho)
     A = p.A
     GQ = G * n_obs
     anchor_pos = np.zeros((H, A), dtype=np.int64)
@@ -403,7 +411,7 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
         P, O = obs_attention(Qh, K[h], V[h], n_obs)
         Ps.append(P)
         Os[h] = O
-        score[h], pooled[h] = anchor_score(P, W)
+        score[h], pooled[h] = anchor_score(P, W, pool)
         pos = select_anchors(pooled[h], N, W, p.k_s, p.k_u)
         if anchor_override is not None:
             pos = np.sort(np.asarray(anchor_override[h], dtype=np.int64))

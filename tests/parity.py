@@ -94,16 +94,19 @@ def check_anchor_set(pooled, gpu_pos, N, W, k_s, k_u):
     return False, "no tie-band explanation"
 
 
-def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=None, report=None):
+def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=None, report=None, params=None):
     """Compare one unit.  K, V, Q: float64 inputs; gpu: unpacked GPU arrays;
     taps: optional dict of GPU workspace arrays for this unit (score [H,N],
-    util [2,H,N]); q [H*G, D] float64 and o_gpu [H*G, D] for decode."""
+    util [2,H,N]); q [H*G, D] float64 and o_gpu [H*G, D] for decode;
+    params: the method's parameters other than theta and window (anchor_div,
+    rho, pool) when they differ from the pages' values."""
     rep = {} if report is None else report
+    prm = dict(params or {})
     H, N, D = K.shape
     dtype_code = 1 if e == 2 else 2
-    p = O.plan(H, N, D, e, theta, W)
+    p = O.plan(H, N, D, e, theta, W, **{k: v for k, v in prm.items() if k in ("anchor_div", "rho")})
     # 1. anchors (per head), from the oracle's own pooled score
-    first = O.compress_unit(K, V, Q, G, n_obs, theta, W, e)
+    first = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, **prm)
     if taps is not None and "score" in taps:
         s_err = np.max(np.abs(taps["score"] - first.score) / np.maximum(first.score, 1e-30 + first.score.max() * 1e-6))
         rep["score_max_rel_err"] = float(s_err)
@@ -122,7 +125,7 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
         exact += why == "exact"
     rep["anchor_heads_exact"] = exact
     # 2. assignments (conditioned on the GPU anchors)
-    second = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, anchor_override=gpos)
+    second = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, anchor_override=gpos, **prm)
     gidx = gpu["idx"].astype(np.int64)
     mism = gidx != second.idx
     if mism.any():
@@ -130,7 +133,7 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
         assert not bad.any(), f"{int(bad.sum())} assignments differ outside the tie margin"
     rep["assign_mismatch_excused"] = int(mism.sum())
     # 3. gamma (fp16), utilities and residual choice (conditioned on GPU assignments)
-    third = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, anchor_override=gpos, idx_override=gidx)
+    third = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, anchor_override=gpos, idx_override=gidx, **prm)
     g16 = f16_bits_to_f64(gpu["gamma16"])
     near = fp16_midpoint_distance(third.gamma) < 1e-3
     diff = (g16 != third.gamma16) & ~near
@@ -154,7 +157,7 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
         assert gflag[s].sum() == R
     # 4. codes, scales, zeros on the GPU's residual set
     fourth = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, anchor_override=gpos, idx_override=gidx,
-                             flag_override=gflag)
+                             flag_override=gflag, **prm)
     for s in range(2):
         fl = gflag[s]
         r = fourth.resid[s][fl]                       # [R, D]

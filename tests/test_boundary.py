@@ -78,17 +78,17 @@ def test_plan_argument_errors(akv):
         akv.plan(1, 8, 4, 1024, 128, 32, akv.BF16, 0.1, 2000)
     assert e.value.code == -3
     lib = akv.lib()
-    assert lib.anchorkv_plan(None, ct.c_float(0.1), 32, None) == -1
+    assert lib.anchorkv_plan(None, None, None) == -1
     assert lib.anchorkv_compress(None, None, None, None, None, 0, None, 0, None) == -1
-    assert lib.anchorkv_decode_attn(None, None, None, None, None, 0, None) == -1
+    assert lib.anchorkv_decode_attn(None, None, 0, None, None, None, 0, None) == -1
     # decode with a tail: host-side checks, before any device call (fake,
     # 16-byte aligned addresses that are never dereferenced)
     p = akv.plan(1, 2, 2, 1024, 128, 8, akv.BF16, 0.1, 32)
     fake = 1 << 20
     ws = int(p.decode_workspace_bytes)
 
-    def tail(n, cap, kt=fake, vt=fake, wsb=ws, q=fake):
-        return lib.anchorkv_decode_attn_tail(ct.byref(p), fake, q, kt, vt, n, cap, fake, fake, wsb, None)
+    def tail(n, cap, kt=fake, vt=fake, wsb=ws, q=fake, cb=int(p.cache_bytes)):
+        return lib.anchorkv_decode_attn_tail(ct.byref(p), fake, cb, q, kt, vt, n, cap, fake, fake, wsb, None)
     assert tail(5, 4) == -1                 # n_tail > tail_cap
     assert tail(-1, 4) == -1                # negative n_tail
     assert tail(3, 4, kt=None) == -1        # null tail with n_tail > 0
@@ -96,6 +96,13 @@ def test_plan_argument_errors(akv):
     assert tail(3, 4, q=fake + 4) == -1     # misaligned query
     assert tail(3, 4, wsb=ws - 1) == -5     # workspace too small
     assert "tail" in lib.anchorkv_last_error().decode()
+    assert tail(3, 4, cb=int(p.cache_bytes) - 16) == -5   # cache too small
+    assert "cache" in lib.anchorkv_last_error().decode()
+    # decode without a tail: the same host-side checks
+    dec = lambda cb, wsb=ws, q=fake: lib.anchorkv_decode_attn(ct.byref(p), fake, cb, q, fake, fake, wsb, None)
+    assert dec(int(p.cache_bytes) - 1) == -5
+    assert dec(int(p.cache_bytes), wsb=ws - 1) == -5
+    assert dec(int(p.cache_bytes), q=fake + 2) == -1
 
 
 def test_pack_unpack_roundtrip_of_oracle_unit(akv):
@@ -147,3 +154,98 @@ def test_record_code_word_layout(akv):
     for j in range(16):
         for c in range(8):
             assert (words[j] >> (2 * c)) & 3 == codes[j + 16 * c]
+
+
+def test_params_defaults_and_range_checks(akv):
+    """anchorkv_params_default gives the pages' values (Pith review, "Assumptions
+    & free parameters": k = S/128, rho = 0.7, pooling width 7) and the plan
+    refuses parameters outside their documented ranges."""
+    q = akv.params(0.05, 32)
+    assert (q.theta, q.window, q.anchor_div, q.rho, q.pool, q.group, q.pool_kv_jointly) == \
+        (pytest.approx(0.05), 32, 128, 0.7, 7, 32, 0)
+    E = akv.AnchorKVError
+    for kw in (dict(pool=6), dict(pool=17), dict(pool=0), dict(group=64), dict(pool_kv_jointly=2),
+               dict(rho=-0.1), dict(rho=1.5), dict(anchor_div=0)):
+        with pytest.raises(E) as e:
+            akv.plan(1, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32, **kw)
+        assert e.value.code == -1, kw
+    d = akv.binding.Dims(1, 8, 4, 8192, 128, 32, akv.BF16)
+    q = akv.params(0.1, 32)
+    q.reserved[3] = 1
+    out = akv.PlanInfo()
+    assert akv.lib().anchorkv_plan(ct.byref(d), ct.byref(q), ct.byref(out)) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(anchor_div=64), dict(rho=0.5), dict(pool=5), dict(pool=1), dict(pool=15),
+                                dict(anchor_div=64, rho=0.5, pool=5), dict(rho=0.0), dict(rho=1.0)])
+def test_plan_with_params_matches_oracle(akv, kw):
+    okw = {k: v for k, v in kw.items() if k in ("anchor_div", "rho")}
+    for H, N, theta, W in [(8, 8192, 0.1, 32), (8, 32768, 0.05, 32), (3, 5000, 0.07, 16), (8, 2000, 0.5, 8)]:
+        p = akv.plan(1, H, 2, N, 128, 8, akv.BF16, theta, W, **kw)
+        o = O.plan(H, N, 128, 2, theta, W, **okw)
+        assert (p.A, p.k_scored, p.k_uniform, p.R_K) == (o.A, o.k_s, o.k_u, o.R_K), (kw, H, N)
+        assert p.params.pool == kw.get("pool", 7)
+        # the header records the parameters: the plan rebuilt from it is the same
+        if N <= 8192:
+            blob = akv.pack_unit(p, _flagged_arrays(akv, p))
+            assert akv.plan_from_header(blob[:256], 1).as_dict() == p.as_dict()
+
+
+def _no_residual_arrays(akv, p):
+    arr = {k: np.zeros(v.shape, v.dtype) for k, v in akv.binding._unit_arrays(p).items()}
+    arr["positions"][:] = np.arange(p.A) + (p.N - p.A)
+    return arr
+
+
+def test_rho_multiple_of_ten_is_exact(akv):
+    """k_scored = floor(rho * k) in double precision: 70 % of 80 non-window
+    anchors is 56 (a float32 rho of 0.7 would give 55)."""
+    p = akv.plan(1, 1, 1, 80 * 128 + 32, 128, 8, akv.BF16, 0.9, 32)
+    assert p.A - 32 == 80 and p.k_scored == 56
+    assert O.plan(1, 80 * 128 + 32, 128, 2, 0.9, 32).k_s == 56
+
+
+def test_plan_refuses_shapes_the_kernels_cannot_run(akv):
+    E = akv.AnchorKVError
+    cases = [
+        dict(G=9, n_obs=8, N=8192, theta=0.1, kw={}),                        # q_per_kv > 8
+        dict(G=8, n_obs=40, N=8192, theta=0.1, kw={}),                       # q_per_kv * n_obs > 256
+        dict(G=4, n_obs=8, N=600000, theta=0.5, kw=dict(anchor_div=100)),    # > 4096 anchors per head
+        dict(G=8, n_obs=8, N=262144, theta=0.1, kw=dict(anchor_div=64)),     # anchor logits + weights beyond LDS
+    ]
+    for c in cases:
+        with pytest.raises(E) as e:
+            akv.plan(1, 1, c["G"], c["N"], 128, c["n_obs"], akv.BF16, c["theta"], 32, **c["kw"])
+        assert e.value.code == -3, c
+    with pytest.raises(E) as e:
+        akv.plan(1, 1, 4, 8192, 128, 33, akv.F32, 0.1, 32)                  # f32: q_per_kv * n_obs > 128
+    assert e.value.code == -3
+
+
+def test_cache_layout_and_workspace_from_header(akv):
+    p = akv.plan(3, 2, 4, 5000, 128, 16, akv.BF16, 0.1, 16, pool=5, rho=0.5)
+    blob = akv.pack_unit(akv.plan(1, 2, 4, 5000, 128, 16, akv.BF16, 0.1, 16, pool=5, rho=0.5),
+                         _flagged_arrays(akv, akv.plan(1, 2, 4, 5000, 128, 16, akv.BF16, 0.1, 16, pool=5, rho=0.5)))
+    lay = akv.cache_layout(blob[:256])
+    for k in ("off_anchor_k", "off_anchor_v", "off_res_k", "off_res_v", "off_words", "off_chunk_k", "off_chunk_v",
+              "off_positions", "unit_bytes", "unit_stride", "A", "R_K", "R_V", "n_chunks"):
+        assert lay[k] == getattr(p, k), k
+    assert lay["record_bytes"] == 48
+    assert akv.decode_workspace_bytes(blob[:256], 3) == p.decode_workspace_bytes
+    p3 = akv.plan_from_header(blob[:256], 3)
+    assert p3.as_dict() == p.as_dict()
+    with pytest.raises(akv.AnchorKVError) as e:
+        akv.cache_layout(b"\0" * 256)
+    assert e.value.code == -7
+
+
+def _flagged_arrays(akv, p):
+    arr = _no_residual_arrays(akv, p)
+    H, N = p.H, p.N
+    for s, R in enumerate((p.R_K, p.R_V)):
+        flat = arr["flag"][s].reshape(-1)
+        elig = np.ones(H * N, bool)
+        for h in range(H):
+            elig[h * N + arr["positions"][h]] = False
+        flat[np.flatnonzero(elig)[:R]] = 1
+    return arr

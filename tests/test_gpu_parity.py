@@ -47,7 +47,13 @@ SMALL = {
     # budget leaves no residual slots
     "bf16_no_residuals": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=1, q_per_kv=2, n_tokens=256, n_obs=8,
                                                 window=32, theta=0.144, n_dirs=8),
+    # the method's fixed parameters away from the pages' values: pooling width
+    # 5, half the non-window anchors scored, k = N/64
+    "bf16_params": W_["llama8b_32k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=4000, n_dirs=32),
+    "f32_params": W_["tiny_f32"].scaled(n_tokens=1200),
 }
+# non-default method parameters of some cases (anchorkv_params)
+PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40)}
 
 
 def _flush(msg):
@@ -64,9 +70,9 @@ def make_inputs(w, device="cuda"):
     return torch.stack(Ks).contiguous(), torch.stack(Vs).contiguous(), torch.stack(Qs).contiguous()
 
 
-def plan_for(akv, w):
+def plan_for(akv, w, params=None):
     return akv.plan(w.units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs,
-                    akv.BF16 if w.dtype == "bf16" else akv.F32, w.theta, w.window)
+                    akv.BF16 if w.dtype == "bf16" else akv.F32, w.theta, w.window, **(params or {}))
 
 
 def ws_view(ws, off, count, dtype=torch.float32):
@@ -85,8 +91,9 @@ def akv():
 def test_compress_decode_parity(akv, name):
     w = SMALL[name]
     _flush(f"[parity] {name}: U={w.units} H={w.kv_heads} G={w.q_per_kv} N={w.n_tokens} dtype={w.dtype}")
+    prm = PARAMS.get(name, {})
     K, V, Q = make_inputs(w)
-    p = plan_for(akv, w)
+    p = plan_for(akv, w, prm)
     cache, ws, dws = akv.alloc(p, "cuda")
     akv.compress(p, K, V, Q, cache, ws)
     q = kvsynth.decode_queries(w, 0, device="cuda").contiguous()
@@ -104,7 +111,7 @@ def test_compress_decode_parity(akv, name):
         unit = cache_h[u * p.unit_stride: u * p.unit_stride + p.unit_bytes].tobytes()
         arr = akv.unpack_unit(p, unit)
         rep = compare_unit(K64[u], V64[u], Q64[u], w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes, arr,
-                           taps=dict(score=score[u], util=util[u]), q=q64[u], o_gpu=o_h[u])
+                           taps=dict(score=score[u], util=util[u]), q=q64[u], o_gpu=o_h[u], params=prm)
         _flush(f"[parity] {name} unit {u}: {rep}")
 
 
@@ -155,3 +162,28 @@ def test_compress_is_deterministic_and_header_roundtrips(akv):
     hdr = c1[:256].cpu().numpy().tobytes()
     p2 = akv.plan_from_header(hdr, w.units)
     assert p2.as_dict() == p.as_dict()
+
+
+def test_decode_of_a_cache_written_under_another_plan_gives_nan(akv):
+    """Every decode workgroup checks its unit's header against the plan it was
+    given: a cache compressed under another plan (here another theta, so other
+    residual counts and section offsets) decodes to NaN, and only the unit
+    headers are read (the buffer is as large as either plan's cache)."""
+    w = SMALL["bf16_ragged"]
+    _flush("[header-check] bf16_ragged, theta 0.1 cache decoded with a theta 0.2 plan")
+    K, V, Q = make_inputs(w)
+    p1 = plan_for(akv, w)
+    p2 = plan_for(akv, w.scaled(theta=0.2))
+    assert p1.R_K != p2.R_K
+    cache = torch.zeros(max(p1.cache_bytes, p2.cache_bytes), dtype=torch.uint8, device="cuda")
+    _, ws, dws1 = akv.alloc(p1, "cuda")
+    akv.compress(p1, K, V, Q, cache[:p1.cache_bytes], ws)
+    _, _, dws2 = akv.alloc(p2, "cuda")
+    q = kvsynth.decode_queries(w, 0, device="cuda").contiguous()
+    o = torch.zeros(w.units, w.kv_heads * w.q_per_kv, w.head_dim, dtype=torch.float32, device="cuda")
+    akv.decode_attn(p2, cache, q, o, dws2)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all()
+    akv.decode_attn(p1, cache, q, o, dws1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()

@@ -121,13 +121,29 @@ def test_obs_attention_matches_sdpa_with_offset_causal_mask():
 
 
 # ---------------------------------------------------------------- score & anchors
-def test_pooling_is_zero_padded_window_sum():
+@pytest.mark.parametrize("pool", [7, 1, 3, 5, 15])
+def test_pooling_is_zero_padded_window_sum(pool):
+    """Library routine: numpy's centred convolution with a box of the pooling
+    width over the non-window scores; width 1 is no pooling."""
     r = rng(3)
     P = r.random((6, 50))
-    score, pooled = O.anchor_score(P, 10)
+    score, pooled = O.anchor_score(P, 10) if pool == 7 else O.anchor_score(P, 10, pool)
     np.testing.assert_allclose(score, P.sum(0), rtol=1e-15)
-    ref = np.convolve(score[:40], np.ones(7), mode="same")
+    ref = np.convolve(score[:40], np.ones(pool), mode="same")
     np.testing.assert_allclose(pooled, ref, rtol=1e-13)
+    if pool == 1:
+        np.testing.assert_array_equal(pooled, score[:40])
+
+
+def test_plan_anchor_parameters_hand_worked():
+    """k = floor(N/anchor_div) non-window anchors, floor(rho k) of them scored,
+    worked by hand at budgets that do not cap k: N = 8192 gives 64 at the
+    pages' 128, 128 at 64; rho 0.7 of 64 is 44, 0.5 of 128 is 64, rho 1 keeps no
+    uniform picks and rho 0 no scored ones."""
+    for kw, (k, ks) in [({}, (64, 44)), (dict(anchor_div=64), (128, 89)), (dict(anchor_div=64, rho=0.5), (128, 64)),
+                        (dict(rho=1.0), (64, 64)), (dict(rho=0.0), (64, 0)), (dict(anchor_div=1000), (8, 5))]:
+        p = O.plan(8, 8192, 128, 2, 0.1, 32, **kw)
+        assert (p.A - 32, p.k_s, p.k_u) == (k, ks, k - ks), kw
 
 
 def _bruteforce_anchors(pooled, N, W, k_s, k_u):
