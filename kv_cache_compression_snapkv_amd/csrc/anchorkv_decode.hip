@@ -44,7 +44,7 @@ namespace akv {
 
 constexpr int kMaxG = 8;          // q-heads per KV head supported by decode
 constexpr int kTile = 1024;       // tokens per tile (= residual-offset chunk)
-constexpr int kWaves = 8;         // waves per workgroup; 128 tokens per wave per tile
+constexpr int kWaves = 16;        // waves per workgroup; 64 tokens per wave per tile, one per lane
 constexpr uint32_t kCodeBias = 0x43004300u;  // bf16 pair (128, 128)
 constexpr float kFxScale = 0x1p38f;               // fixed-point scale of the w scatter
 constexpr double kFxScaleD = 0x1p38;
@@ -52,8 +52,6 @@ constexpr double kFxInv = 0x1p-38;
 constexpr double kRoundMagic = 0x1.8p52;           // x + 1.5*2^52 rounds x (|x| < 2^51) to an integer
 constexpr unsigned long long kMagicMask = 0x0007FFFFFFFFFFFFull;  // low 51 bits: that integer, for x >= 0
 constexpr float kLazy = 1.0f;                      // rescale when a logit passes m_run + kLazy (log2 units)
-// floats of the per-tile buffer: [kTile][G], at least the 8 KB of staged words
-template <int G> constexpr int kBufFloats = kTile * G > 2048 ? kTile * G : 2048;
 
 // y (already scaled by 2^38) -> two's-complement 64-bit fixed point, any sign
 // and |y| < 2^62.
@@ -78,12 +76,14 @@ struct DecArgs {
   float c;
 };
 
-// Record staging: KP 16-byte chunks per thread per side are prefetched, so a
-// tile stages up to 512*KP*16/48 records per side in LDS; records beyond that
-// are read from the cache directly.
-
 __device__ __forceinline__ bf16x8 u4_to_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return bits_to_frag(make_uint4(a, b, c, d));
+}
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+__device__ __forceinline__ bf16x4 u2_to_frag4(uint32_t a, uint32_t b) { return __builtin_bit_cast(bf16x4, make_uint2(a, b)); }
+// 16x16x16 bf16 MFMA (K = 16: lane (col, kg) holds K indices 4kg .. 4kg + 3)
+__device__ __forceinline__ f32x4 mma16k(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // (a & m) | b: with m an opaque SGPR value and b an opaque VGPR value (see
@@ -171,41 +171,84 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
 }
 
 template <int G> constexpr int kGPad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-constexpr int kRecPad = 32;  // zeroed records after the value staging (batch tails read them)
 
-template <int DT, int G, int KP, int DEPTH, int WPE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void k_dec_stream(DecArgs a) {
-  constexpr int kPre = KP;
-  constexpr int kRecCap = 512 * KP * 16 / kRecBytes;
+// LDS of the stream kernel (bytes from the start of the dynamic region).
+// Main phase: w [G][A] u64 | S [A][GP] f32 | rows [kWaves][64][BR] f32 |
+// K-batch query fragments [NB*4*QH][64] uint4 | their column sums [NB][64]
+// float2.  Epilogue (after the last read of w): the per-wave partial outputs
+// [kWaves][G][D], the two halves of w V [2][G][D], the zero-point sums
+// [kWaves][BR*4] and the softmax sums [kWaves][GP] reuse the region.
+struct DecLds {
+  size_t S, rows, qbs, qcs, main;
+  size_t pv, pwv, pz, pl, epi;
+  size_t total;
+};
+__host__ __device__ constexpr size_t lds_align(size_t x) { return (x + 15) & ~(size_t)15; }
+__host__ __device__ inline DecLds dec_lds(int G, int A, bool qsplit) {
+  const size_t GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  const size_t NB = (4 * (size_t)G + 15) / 16, BR = 4 * NB;
+  DecLds L{};
+  L.S = lds_align(8 * (size_t)G * A);
+  L.rows = L.S + lds_align(4 * GP * (size_t)A);
+  L.qbs = L.rows + (size_t)kWaves * 64 * BR * 4;
+  L.qcs = L.qbs + NB * 4 * (qsplit ? 2 : 1) * 64 * 16;
+  L.main = L.qcs + NB * 64 * 8;
+  L.pv = 0;
+  L.pwv = L.pv + (size_t)kWaves * G * kHeadDim * 4;
+  L.pz = L.pwv + 2 * (size_t)G * kHeadDim * 4;
+  L.pl = L.pz + (size_t)kWaves * BR * 4 * 4;
+  L.epi = L.pl + (size_t)kWaves * GP * 4;
+  L.total = L.main > L.epi ? L.main : L.epi;
+  return L;
+}
+
+// One workgroup of kWaves waves (1024 threads) per (unit, head, range of
+// 1024-token chunks).  Wave w owns tokens 64w .. 64w + 63 of every tile, one
+// per lane.  Per tile there is one workgroup barrier, between the logits (all
+// waves publish a new tile maximum only when one passes m_run + kLazy) and the
+// softmax weights; everything else a wave needs is its own:
+//  * the residual records of a wave's flagged tokens are a contiguous run of
+//    the tile's records; the run starts at the tile's chunk offset plus the
+//    flagged counts of the waves before it, which every wave publishes a tile
+//    ahead (its pointer words are loaded two tiles ahead);
+//  * the first 16 key records and 32 value records of the run are loaded into
+//    registers a tile ahead, directly in MFMA operand layout (range-checked
+//    buffer loads: records past the run read as zeros); more are read when
+//    needed;
+//  * key-residual logits and the weights of value-flagged tokens pass through
+//    rows of LDS private to the wave;
+//  * the tile maxima are triple-buffered, so resetting the one for the next
+//    tile cannot race with a wave still reading the previous one.
+// The epilogue sums the waves' partial outputs in a fixed order (no float
+// atomics), so the output does not depend on the order the waves ran in.
+template <int DT, int G>
+__global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
   using T = typename Elem<DT>::T;
   using M = Mfma<ANCHORKV_BF16>;
   constexpr int D = kHeadDim;
   constexpr int GP = kGPad<G>;                   // q-heads per anchor row in LDS (padded)
   constexpr int NB = (4 * G + 15) / 16;          // 16-wide blocks of (q-head, group) pairs
+  constexpr int BR = 4 * NB;                     // floats per wave row (q-heads >= G read as 0)
   constexpr bool QSPLIT = DT == ANCHORKV_F32;   // f32 queries enter the key MFMA as bf16 hi + lo
+  constexpr int QH = QSPLIT ? 2 : 1;
   extern __shared__ __align__(16) float sm[];
   const int A = a.A;
-  // w[g][a] in fixed point, q-head-major: the scatter's random anchors then
-  // spread over all banks (an anchor-major row of GP entries would put every
-  // anchor's entry g on the same few banks)
-  unsigned long long* wi = reinterpret_cast<unsigned long long*>(sm);  // [GP][A]
-  float* S = reinterpret_cast<float*>(wi + A * GP);                      // [A][GP]
-  // [kTile][BR]: per wave 128 private rows (its tokens' records by rank):
-  // key-residual logits, then p of value-flagged tokens (zeros in columns
-  // >= G and in the rows up to the next 32); [G][D] at the end.  At the start
-  // of a tile it first holds the staged pointer words ([512] x 16 B).
-  constexpr int BR = 4 * NB;
-  float* buf = sm + ((3 * GP * A + 3) & ~3);
-  uint4* wst = reinterpret_cast<uint4*>(buf);
-  uint4* kst = reinterpret_cast<uint4*>(buf + kBufFloats<BR>);  // staged key records of the tile
-  uint4* vst = kst + 512 * kPre;                                 // staged value records, then kRecPad zero records
-  const uint8_t* kstb = reinterpret_cast<const uint8_t*>(kst);
-  const uint8_t* vstb = reinterpret_cast<const uint8_t*>(vst);
-  __shared__ int cnt[kWaves];  // per wave: key-flagged | value-flagged << 16
-  __shared__ int offs[2][130];
-  __shared__ __align__(16) int tmaxb[2][GP];
-  __shared__ __align__(16) float zrow[GP];
-  __shared__ float zt_s[G * 4];
+  const DecLds L = dec_lds(G, A, QSPLIT);
+  uint8_t* smb = reinterpret_cast<uint8_t*>(sm);
+  // w[g][a] in fixed point, q-head-major (random anchors spread over the banks)
+  unsigned long long* wi = reinterpret_cast<unsigned long long*>(smb);
+  float* S = reinterpret_cast<float*>(smb + L.S);         // [A][GP]
+  float* rows = reinterpret_cast<float*>(smb + L.rows);   // [kWaves][64][BR]
+  uint4 (*qbs)[64] = reinterpret_cast<uint4 (*)[64]>(smb + L.qbs);
+  float2* qcs = reinterpret_cast<float2*>(smb + L.qcs);  // [NB][64]
+  __shared__ int cnt[2][kWaves];   // per wave and tile parity: key-flagged | value-flagged << 16
+  __shared__ int offs[2][130];     // first record of each chunk of the range (and of the chunk after)
+  __shared__ __align__(16) int tmaxb[3][GP];
+  __shared__ __align__(16) float zrow[BR];
+  // running maximum per q-head (log2 units), one copy per wave: every wave
+  // takes the same decisions from the same tile maxima; kept in LDS rather
+  // than registers (it is read twice per tile)
+  __shared__ __align__(16) float mrun_s[kWaves][GP];
 
   int bid = blockIdx.x;
   const int sp = bid % a.S2; bid /= a.S2;
@@ -214,9 +257,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int64_t uh = (int64_t)u * a.H + h;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave: uniform
   const int col = lane & 15, kg = lane >> 4;
-  float* wbuf = buf + wave * 128 * BR;  // this wave's rows
+  float* wrow = rows + wave * 64 * BR;   // this wave's rows
   const int c0 = sp * a.cps, c1 = min(a.C, c0 + a.cps);
   const int t_beg = c0 * kTile, t_end = min(a.N, c1 * kTile);
+  const int nch = max(0, c1 - c0);
   const uint8_t* base = a.cache + (int64_t)u * a.stride;
   const uint8_t* recK = base + a.off_rk;
   const uint8_t* recV = base + a.off_rv;
@@ -242,19 +286,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
   }
 
-  // q of this head as floats in LDS ([G][D]; buf is free until the first tile)
-  float* qf = buf;
+  // q of this head as floats in LDS ([G][D], in the rows region, free until the first tile)
+  float* qf = rows;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) qf[i] = Elem<DT>::f(q[i]);
-  for (int i = threadIdx.x; i < GP * A; i += blockDim.x) wi[i] = 0ull;
-  for (int i = threadIdx.x; i < kRecPad * kRecBytes / 16; i += blockDim.x) vst[512 * kPre + i] = make_uint4(0, 0, 0, 0);
-  if (threadIdx.x < G * 4) zt_s[threadIdx.x] = 0.0f;
-  if (threadIdx.x < GP) {
-    zrow[threadIdx.x] = 0.0f;
-    tmaxb[0][threadIdx.x] = kKeyNegInf;
-    tmaxb[1][threadIdx.x] = kKeyNegInf;
-  }
-  // record offsets of the range's chunks and of the chunk after the last one
-  const int nch = max(0, c1 - c0);
+  for (int i = threadIdx.x; i < G * A; i += blockDim.x) wi[i] = 0ull;
+  if (threadIdx.x < BR) zrow[threadIdx.x] = 0.0f;
+  if (threadIdx.x < 3 * GP) (&tmaxb[0][0])[threadIdx.x] = kKeyNegInf;
+  if (threadIdx.x < kWaves * GP) (&mrun_s[0][0])[threadIdx.x] = -INFINITY;
   for (int i = threadIdx.x; i <= nch; i += blockDim.x) {
     const int fl = h * a.C + c0 + i;
     const bool last = fl >= a.H * a.C;
@@ -273,44 +311,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // st (= coordinate group st) the lane supplies q[g][d] / 4^m for
   // d = j + 16c, j = 4kg + (e&3), c = 2st + (e>>2), when grp == st, zeros
   // otherwise.  cinit = -128 * (sum of what the column is fed), so the
-  // accumulator ends at sum_d q[g][d] * code_d.
-  // the fragments are the same in every wave: kept in LDS (after the value
-  // staging and its zero records), written by wave 0
-  constexpr int QH = QSPLIT ? 2 : 1;
-  uint4 (*qbs)[64] = reinterpret_cast<uint4 (*)[64]>(vst + 512 * kPre + kRecPad * kRecBytes / 16);
-  // per lane (column): sum of q over the column's group and cinit, also in
-  // LDS (after the fragments) so that they take no registers in the tile loop
-  float2* qcs = reinterpret_cast<float2*>(qbs + NB * 4 * QH);  // [NB][64]
+  // accumulator ends at sum_d q[g][d] * code_d.  The same in every wave: wave 0
+  // writes them to LDS, with each column's query sum and initial value.
+  if (wave == 0) {
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    const int kap = 16 * cb + col;
-    const int g = kap >> 2, grp = kap & 3;
-    float qs = 0.0f, fed = 0.0f;
-    if (g < G)
-      for (int d = 32 * grp; d < 32 * grp + 32; ++d) {
-        const float x = qf[g * D + d];
-        const float sc = kPlaneInv[plane_of(d >> 4).m];
-        const float xh = bf2f(f2bf(x));
-        qs += x;
-        fed += xh * sc;
-        if constexpr (QSPLIT) fed += bf2f(f2bf(x - xh)) * sc;
-      }
-    if (wave == 0) qcs[cb * 64 + lane] = make_float2(qs, -128.0f * fed);
+    for (int cb = 0; cb < NB; ++cb) {
+      const int kap = 16 * cb + col;
+      const int g = kap >> 2, grp = kap & 3;
+      float qs = 0.0f, fed = 0.0f;
+      if (g < G)
+        for (int d = 32 * grp; d < 32 * grp + 32; ++d) {
+          const float x = qf[g * D + d];
+          const float sc = kPlaneInv[plane_of(d >> 4).m];
+          const float xh = bf2f(f2bf(x));
+          qs += x;
+          fed += xh * sc;
+          if constexpr (QSPLIT) fed += bf2f(f2bf(x - xh)) * sc;
+        }
+      qcs[cb * 64 + lane] = make_float2(qs, -128.0f * fed);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint16_t vh[8], vl[8];
+      for (int st = 0; st < 4; ++st) {
+        uint16_t vh[8], vl[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 2 * st + (e >> 2);
-        const int d = (4 * kg + (e & 3)) + 16 * c;
-        const float x = (g < G && grp == st) ? qf[g * D + d] : 0.0f;
-        const float sc = kPlaneInv[plane_of(c).m];
-        vh[e] = f2bf(x);
-        vl[e] = f2bf(x - bf2f(vh[e]));
-        vh[e] = f2bf(bf2f(vh[e]) * sc);  // exact: power-of-two scaling
-        vl[e] = f2bf(bf2f(vl[e]) * sc);
-      }
-      if (wave == 0) {
+        for (int e = 0; e < 8; ++e) {
+          const int c = 2 * st + (e >> 2);
+          const int d = (4 * kg + (e & 3)) + 16 * c;
+          const float x = (g < G && grp == st) ? qf[g * D + d] : 0.0f;
+          const float sc = kPlaneInv[plane_of(c).m];
+          vh[e] = f2bf(x);
+          vl[e] = f2bf(x - bf2f(vh[e]));
+          vh[e] = f2bf(bf2f(vh[e]) * sc);  // exact: power-of-two scaling
+          vl[e] = f2bf(bf2f(vl[e]) * sc);
+        }
         qbs[(cb * 4 + st) * QH][lane] = make_uint4(vh[0] | (uint32_t)vh[1] << 16, vh[2] | (uint32_t)vh[3] << 16,
                                                    vh[4] | (uint32_t)vh[5] << 16, vh[6] | (uint32_t)vh[7] << 16);
         if constexpr (QSPLIT)
@@ -320,69 +352,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
   }
   // value side: B = -128 everywhere cancels the code bias of the A rows
-  const bf16x8 bm128 = u4_to_frag(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u);
+  const bf16x4 bm128_4 = u2_to_frag4(0xC300C300u, 0xC300C300u);
 
-  float m_run[G], lacc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; lacc[g] = 0.0f; }
-  // value side, row block rb (rows 4g + grp), column block cc (coordinates
-  // j + 16cc): of each MFMA tile only the rows of group cc/2 are wanted, so a
-  // batch's tile starts from the batch's code-bias term -128 * (row sums of
-  // A) and its row r = cc/2 is added to vacc (scaled by 4^m of the plane)
-  float vacc[NB][8];
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb)
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] = 0.0f;
-  float zt[NB];        // value side: sum of p * zero for row (rb, col)
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) zt[rb] = 0.0f;
-
+  // pointer words: one 8-byte load per lane and tile, two tiles ahead
+  // (range-checked: a token past the range reads zero words, so no flags)
   const uint32_t* words = reinterpret_cast<const uint32_t*>(base + a.off_words) + (int64_t)h * a.N * 2;
-
-  // Prefetch (registers), DEPTH tiles ahead: the thread's two pointer-word
-  // pairs (one 16-byte load) and its share of the tile's key / value record
-  // bytes (16-byte chunks).  The tile loop is unrolled by DEPTH so ring slots
-  // stay static; each slot is emptied into LDS before it is reloaded.
-  uint4 pw[DEPTH];
-  uint4 pk[DEPTH][kPre], pv_[DEPTH][kPre];
-  // All loads go through range-checked buffer resources: a lane past the
-  // range (or a tile past the last) reads zeros and no memory.  For an odd
-  // last token the range is rounded up to 16 bytes: the 8 bytes after this
-  // head's words (the next head's or the chunk table) lie inside the unit and
-  // the token-validity flags below ignore them.
-  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(words + (int64_t)t_beg * 2, (uint32_t)(((t_end - t_beg) * 8 + 15) & ~15));
-  auto prefetch = [&](int i, uint4& w_, uint4* k_, uint4* v_) {
-    w_ = buf_load16(wrs, (uint32_t)(i * kTile + wave * 128 + 2 * lane) * 8u);
-    const int ic = max(0, min(i, nch - 1));
-    const int ok0 = __builtin_amdgcn_readfirstlane(offs[0][ic]), ok1 = __builtin_amdgcn_readfirstlane(offs[0][ic + 1]);
-    const int ov0 = __builtin_amdgcn_readfirstlane(offs[1][ic]), ov1 = __builtin_amdgcn_readfirstlane(offs[1][ic + 1]);
-    const int nk = i < nch ? 3 * min(kRecCap, ok1 - ok0) : 0;
-    const int nv = i < nch ? 3 * min(kRecCap, ov1 - ov0) : 0;
-    const __amdgpu_buffer_rsrc_t krs = buf_rsrc(recK + (int64_t)ok0 * kRecBytes, (uint32_t)nk * 16u);
-    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(recV + (int64_t)ov0 * kRecBytes, (uint32_t)nv * 16u);
-#pragma unroll
-    for (int k = 0; k < kPre; ++k) {
-      const uint32_t ci = threadIdx.x + 512 * k;
-      k_[k] = buf_load16(krs, ci * 16u);
-      v_[k] = buf_load16(vrs, ci * 16u);
-    }
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(words + (int64_t)t_beg * 2, (uint32_t)(t_end - t_beg) * 8u);
+  auto load_words = [&](int it) -> uint2 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(wrs, (int)((uint32_t)(it * kTile + wave * 64 + lane) * 8u), 0, 0);
+    return make_uint2(v[0], v[1]);
   };
-  // issue order = slot order (the loop's waits count the loads issued after a
-  // slot's, so the scheduler must not interleave the slots here)
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    prefetch(d, pw[d], pk[d], pv_[d]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  uint2 wq[2];
+  wq[0] = load_words(0);
+  wq[1] = load_words(1);
 
   // ---- anchor logits S[a][g] = <q_g, k_a> * c on MFMA, 16 anchors per tile
-  // (rows = anchors, K = coordinates, columns = q-heads), while the first
-  // tiles' loads are in flight
+  // (rows = anchors, K = coordinates, columns = q-heads), while the words load
   {
     using MS = Mfma<DT>;
     const T* AK = reinterpret_cast<const T*>(base + a.off_ak) + (int64_t)h * A * D;
-#pragma unroll 2
     for (int t = wave; t < (A + 15) / 16; t += kWaves) {
       const int ar = 16 * t + col;
       f32x4 sacc = {0, 0, 0, 0};
@@ -400,159 +388,260 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         }
     }
   }
-  __syncthreads();  // S, qbs; qf is dead (buf becomes the tiles' buffer)
+  // flagged counts of tile 0
+  {
+    const unsigned long long bk = __ballot((wq[0].x & 0x8000u) != 0), bv = __ballot((wq[0].y & 0x8000u) != 0);
+    if (lane == 0) cnt[0][wave] = __popcll(bk) | (__popcll(bv) << 16);
+  }
+  __syncthreads();  // S, qbs, qcs, cnt[0]; qf is dead (rows become the waves' rows)
 
-  for (int base_it = 0; base_it < nch; base_it += DEPTH) {
+  // Record prefetch of a tile: this wave's run of key / value records starts at
+  // the tile's chunk offset plus the counts of the waves before it.
+  auto run_of = [&](int it, int par, int& kb, int& nk, int& vb, int& nv) {
+    const int ic = min(it, nch);
+    const int mine = cnt[par][wave];
+    const int pre = __builtin_amdgcn_readfirstlane(row_sum_i32(lane < wave ? cnt[par][lane & (kWaves - 1)] : 0));
+    kb = __builtin_amdgcn_readfirstlane(offs[0][ic]) + (pre & 0xFFFF);
+    vb = __builtin_amdgcn_readfirstlane(offs[1][ic]) + (pre >> 16);
+    nk = it < nch ? (mine & 0xFFFF) : 0;
+    nv = it < nch ? (mine >> 16) : 0;
+  };
+  // key batch 0: lane (col, kg) holds bytes 8kg..8kg+7 of record col and the
+  // (scale, zero) word of group col & 3 of records 4kg + r
+  uint2 kx;
+  uint32_t ksz[4];
+  auto load_keys = [&](int kb, int nk) {
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)kb * kRecBytes, (uint32_t)min(nk, 16) * kRecBytes);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, col * kRecBytes + 8 * kg, 0, 0);
+    kx = make_uint2(x[0], x[1]);
 #pragma unroll
-  for (int dslot = 0; dslot < DEPTH; ++dslot) {
-    // no early exit: a tile past the range (odd tile count) reads nothing and
-    // contributes nothing, and a branch out of the middle of the unrolled body
-    // would let the compiler's wait counting assume a path that skipped the
-    // other slot's loads
-    const int it = base_it + dslot;
-    const int par = it & 1;
-    const int tile = t_beg + it * kTile;
-    const int rk0 = offs[0][min(it, nch)], rv0 = offs[1][min(it, nch)];
-    // stage this tile's records (the previous tile ended with a barrier)
+    for (int rr = 0; rr < 4; ++rr)
+      ksz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
+  };
+  // value batch 0: code word col of records 4kg + e (pairs packed), and the
+  // (scale, zero) word of group col & 3 of the same records
+  uint32_t vpr[2], vsz[4];
+  auto load_values = [&](int vb, int nv) {
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)vb * kRecBytes, (uint32_t)min(nv, 16) * kRecBytes);
 #pragma unroll
-    for (int k = 0; k < kPre; ++k) { kst[threadIdx.x + 512 * k] = pk[dslot][k]; vst[threadIdx.x + 512 * k] = pv_[dslot][k]; }
-    wst[threadIdx.x] = pw[dslot];
-    // compiler-only fence: the words are read back from LDS below instead of
-    // being forwarded from pw, whose registers are free now for the next
-    // prefetch
-    asm volatile("" ::: "memory");
-    prefetch(it + DEPTH, pw[dslot], pk[dslot], pv_[dslot]);
-    const uint4 w4 = wst[threadIdx.x];  // own write, no barrier needed
-    // ---- A: pointer words of the lane's two tokens
-    const int t0 = tile + wave * 128 + 2 * lane;
-    const bool v0 = t0 < t_end, v1 = t0 + 1 < t_end;
-    const int aK0 = w4.x & 0x7FFF, aV0 = w4.y & 0x7FFF, aK1 = w4.z & 0x7FFF, aV1 = w4.w & 0x7FFF;
-    // a token past the range has all-zero words (flags clear) except the odd
-    // one after the last token, masked by v1
-    const bool fK0 = w4.x & 0x8000u, fV0 = w4.y & 0x8000u;
-    const bool fK1 = v1 && (w4.z & 0x8000u), fV1 = v1 && (w4.w & 0x8000u);
-    const float gK0 = h2f((uint16_t)(w4.x >> 16)), gV0 = h2f((uint16_t)(w4.y >> 16));
-    const float gK1 = h2f((uint16_t)(w4.z >> 16)), gV1 = h2f((uint16_t)(w4.w >> 16));
-    const unsigned long long bK0 = __ballot(fK0), bK1 = __ballot(fK1), bV0 = __ballot(fV0), bV1 = __ballot(fV1);
-    const int nK = __popcll(bK0) + __popcll(bK1), nV = __popcll(bV0) + __popcll(bV1);
-    if (lane == 0) cnt[wave] = nK | (nV << 16);
-    if (threadIdx.x < GP) tmaxb[par ^ 1][threadIdx.x] = kKeyNegInf;  // next tile's max (last read a tile ago)
-    lds_barrier();
-    // counts of the earlier waves: lanes 0..wave-1 hold them, summed over the row
-    const int pre = __builtin_amdgcn_readfirstlane(row_sum_i32(lane < wave ? cnt[lane & (kWaves - 1)] : 0));
-    const int baseK = pre & 0xFFFF, baseV = pre >> 16;
-    // ranks of the lane's tokens among this wave's flagged ones
-    const int rK0 = lanes_below(bK0) + lanes_below(bK1), rK1 = rK0 + (fK0 ? 1 : 0);
-    const int rV0 = lanes_below(bV0) + lanes_below(bV1), rV1 = rV0 + (fV0 ? 1 : 0);
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int r0 = 4 * kg + 2 * e2;
+      const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b16(r, r0 * kRecBytes + 2 * col, 0, 0);
+      const uint32_t w1 = __builtin_amdgcn_raw_buffer_load_b16(r, (r0 + 1) * kRecBytes + 2 * col, 0, 0);
+      vpr[e2] = w0 | (w1 << 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      vsz[e] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + e) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
+  };
+  int kb_cur, nk_cur, vb_cur, nv_cur;
+  run_of(0, 0, kb_cur, nk_cur, vb_cur, nv_cur);
+  load_keys(kb_cur, nk_cur);
+  load_values(vb_cur, nv_cur);
 
-    // ---- B: key-residual logits of this wave's records, 16 per MFMA tile,
-    // into this wave's buf rows [0, nK).  Batches
-    // whose records are all staged read LDS only; the rest (tiles with more
-    // flagged tokens than the staging holds) read the cache directly.
-    auto kbatch = [&](int b0, auto from_lds) {
-      constexpr bool LDS = decltype(from_lds)::value;
-      const int i = b0 + col;
-      uint2 x = make_uint2(0, 0);
-      if constexpr (LDS) x = *reinterpret_cast<const uint2*>(kstb + (baseK + i) * kRecBytes + 8 * kg);
-      else if (i < nK) x = *reinterpret_cast<const uint2*>(recK + (int64_t)(rk0 + baseK + i) * kRecBytes + 8 * kg);
-      const uint32_t xs[3][2] = {{x.x, x.y}, {x.x >> 6, x.y >> 6}, {x.x >> 12, x.y >> 12}};
-      bf16x8 af[4];
+  float* mrun = mrun_s[wave];
+  float lacc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) lacc[g] = 0.0f;
+  // value side, row block rb (rows 4g + grp), column block cc (coordinates
+  // j + 16cc): of each MFMA tile only the rows of group cc/2 are wanted, so a
+  // batch's tile starts from the batch's code-bias term -128 * (row sums of
+  // A) and its row r = cc/2 is added to vacc (scaled by 4^m of the plane)
+  float vacc[NB][8];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] = 0.0f;
+  float zt[NB];        // value side: sum of p * zero for row (rb, col)
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) zt[rb] = 0.0f;
+
+  // ---- key-residual logits of records b0 .. b0+15 of the wave's run, from the
+  // fragments (x, sz) into the wave's rows [b0, b0 + 16) (row = rank)
+  auto kbatch = [&](int b0, int nk, uint2 x, const uint32_t (&sz)[4]) {
+    const uint32_t xs[3][2] = {{x.x, x.y}, {x.x >> 6, x.y >> 6}, {x.x >> 12, x.y >> 12}};
+    bf16x8 af[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const Plane p0 = plane_of(2 * st), p1 = plane_of(2 * st + 1);
+      const int i0 = p0.sh / 6, i1 = p1.sh / 6;
+      af[st] = u4_to_frag(and_or(xs[i0][0], MK[p0.m], vbias), and_or(xs[i0][1], MK[p0.m], vbias),
+                          and_or(xs[i1][0], MK[p1.m], vbias), and_or(xs[i1][1], MK[p1.m], vbias));
+    }
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      const float2 qc = qcs[cb * 64 + lane];  // (sum of q, initial accumulator)
+      f32x4 cacc = {qc.y, qc.y, qc.y, qc.y};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const Plane p0 = plane_of(2 * st), p1 = plane_of(2 * st + 1);
-        const int i0 = p0.sh / 6, i1 = p1.sh / 6;
-        af[st] = u4_to_frag(and_or(xs[i0][0], MK[p0.m], vbias), and_or(xs[i0][1], MK[p0.m], vbias),
-                            and_or(xs[i1][0], MK[p1.m], vbias), and_or(xs[i1][1], MK[p1.m], vbias));
+        cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH][lane]), cacc);
+        if constexpr (QSPLIT) cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH + 1][lane]), cacc);
       }
+      const int kap = 16 * cb + col, g = kap >> 2, grp = kap & 3;
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        const float2 qc = qcs[cb * 64 + lane];  // (sum of q, initial accumulator)
-        f32x4 cacc = {qc.y, qc.y, qc.y, qc.y};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH][lane]), cacc);
-          if constexpr (QSPLIT) cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH + 1][lane]), cacc);
-        }
-        const int kap = 16 * cb + col, g = kap >> 2, grp = kap & 3;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ii = b0 + 4 * kg + r;
-          uint32_t sz = 0;
-          if constexpr (LDS) sz = *reinterpret_cast<const uint32_t*>(kstb + (baseK + ii) * kRecBytes + 32 + 4 * grp);
-          else if (ii < nK) sz = *reinterpret_cast<const uint32_t*>(recK + (int64_t)(rk0 + baseK + ii) * kRecBytes + 32 + 4 * grp);
-          const float sc = h2f((uint16_t)(sz & 0xFFFFu)), z = h2f((uint16_t)(sz >> 16));
-          const float val = quad_sum(fmaf(sc, cacc[r], z * qc.x));
-          if (ii < nK && grp == 0 && g < G) wbuf[ii * BR + g] = val * a.c;
-        }
-      }
-    };
-    {
-      const int nfast = max(0, min(nK, kRecCap - baseK));  // records of this wave that are staged
-      int b0 = 0;
-      for (; b0 + 16 <= nfast; b0 += 16) kbatch(b0, std::true_type{});
-      if (b0 < nK) {
-        if (baseK + nK <= kRecCap) kbatch(b0, std::true_type{});
-        else for (; b0 < nK; b0 += 16) kbatch(b0, std::false_type{});
+      for (int r = 0; r < 4; ++r) {
+        const int ii = b0 + 4 * kg + r;
+        const float sc = h2f((uint16_t)(sz[r] & 0xFFFFu)), z = h2f((uint16_t)(sz[r] >> 16));
+        const float val = quad_sum(fmaf(sc, cacc[r], z * qc.x));
+        if (ii < nk && grp == 0 && g < G) wrow[ii * BR + g] = val * a.c;
       }
     }
-    __builtin_amdgcn_wave_barrier();  // this wave's buf rows written before they are read (LDS is in order per wave)
+  };
+  // ---- value residuals of records b0 .. b0+15 of the wave's run (weights in
+  // the wave's rows [b0, b0 + 16), zeros past the run), on the K = 16 MFMA:
+  // lane (col, kg) feeds records 4kg .. 4kg + 3 of the batch
+  auto vbatch = [&](int b0, const uint32_t (&pr)[2], const uint32_t (&sz)[4]) {
+    bf16x4 ahi[NB], alo[NB];
+    f32x4 zb[NB];  // -128 * row sums of A: cancels the code bias
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int g = (16 * rb + col) >> 2;
+      float ps[4];
+      float zsum = zt[rb];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pv = wrow[(b0 + 4 * kg + e) * BR + g];
+        ps[e] = pv * h2f((uint16_t)(sz[e] & 0xFFFFu));
+        zsum = fmaf(pv, h2f((uint16_t)(sz[e] >> 16)), zsum);
+      }
+      zt[rb] = zsum;
+      uint32_t hp[2], lp[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t hb = bf16_pack(ps[2 * k], ps[2 * k + 1]);
+        const float d0 = ps[2 * k] - __uint_as_float(hb << 16);
+        const float d1 = ps[2 * k + 1] - __uint_as_float(hb & 0xFFFF0000u);
+        hp[k] = hb;
+        lp[k] = bf16_pack(d0, d1);
+      }
+      ahi[rb] = u2_to_frag4(hp[0], hp[1]);
+      alo[rb] = u2_to_frag4(lp[0], lp[1]);
+      zb[rb] = mma16k(ahi[rb], bm128_4, f32x4{0, 0, 0, 0});
+      zb[rb] = mma16k(alo[rb], bm128_4, zb[rb]);
+    }
+    const uint32_t ps6[2] = {pr[0] >> 6, pr[1] >> 6};
+    const uint32_t ps12[2] = {pr[0] >> 12, pr[1] >> 12};
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const Plane pl = plane_of(cc);
+      const uint32_t* src = pl.sh == 0 ? pr : pl.sh == 6 ? ps6 : ps12;
+      const bf16x4 bfr = u2_to_frag4(and_or(src[0], MK[pl.m], vbias), and_or(src[1], MK[pl.m], vbias));
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        f32x4 t = mma16k(ahi[rb], bfr, zb[rb]);
+        t = mma16k(alo[rb], bfr, t);
+        vacc[rb][cc] += t[cc >> 1];
+      }
+    }
+  };
 
-    // ---- C: logits of the lane's two tokens; tile max per q-head
-    float s0[G], s1[G];
+  for (int base_it = 0; base_it < nch; base_it += 2) {
+#pragma unroll
+  for (int slot = 0; slot < 2; ++slot) {
+    // no early exit: a tile past the range (odd tile count) has no valid
+    // token, no record and no maximum, and every wave still takes its barrier
+    const int it = base_it + slot;
+    const int t = t_beg + it * kTile + wave * 64 + lane;
+    const bool valid = it < nch && t < t_end;
+    const uint2 wd = wq[slot];
+    const uint2 wn = wq[slot ^ 1];       // words of tile it + 1 (loaded a tile ago)
+    wq[slot] = load_words(it + 2);
+    // flagged counts of tile it + 1 (read after this tile's barrier)
     {
-      float S0[GP], S1[GP], R0[GP], R1[GP];
-      ldsv<GP>(S + aK0 * GP, S0);
-      ldsv<GP>(S + aK1 * GP, S1);
-      ldsv<GP>(fK0 ? wbuf + rK0 * BR : zrow, R0);
-      ldsv<GP>(fK1 ? wbuf + rK1 * BR : zrow, R1);
+      const unsigned long long bk = __ballot((wn.x & 0x8000u) != 0), bv = __ballot((wn.y & 0x8000u) != 0);
+      if (lane == 0) cnt[slot ^ 1][wave] = __popcll(bk) | (__popcll(bv) << 16);
+    }
+    // ---- pointer words of the lane's token
+    const int aK = wd.x & 0x7FFF, aV = wd.y & 0x7FFF;
+    const bool fK = (wd.x & 0x8000u) != 0, fV = (wd.y & 0x8000u) != 0;
+    const float gK = h2f((uint16_t)(wd.x >> 16)), gV = h2f((uint16_t)(wd.y >> 16));
+    const unsigned long long bK = __ballot(fK), bV = __ballot(fV);
+    const int rK = lanes_below(bK), rV = lanes_below(bV);
+    const int nK = nk_cur, nV = nv_cur;
+
+    // ---- key-residual logits of the wave's records, 16 per batch; the first
+    // batch was loaded a tile ahead, more (rare: over 16 of the wave's 64
+    // tokens) are read here
+    {
+      uint2 x = kx;
+      uint32_t sz[4] = {ksz[0], ksz[1], ksz[2], ksz[3]};
+      for (int b0 = 0; b0 < nK; b0 += 16) {
+        if (b0 > 0) {
+          const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)(kb_cur + b0) * kRecBytes,
+                                                    (uint32_t)min(nK - b0, 16) * kRecBytes);
+          const auto xx = __builtin_amdgcn_raw_buffer_load_b64(r, col * kRecBytes + 8 * kg, 0, 0);
+          x = make_uint2(xx[0], xx[1]);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            sz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
+        }
+        kbatch(b0, nK, x, sz);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // the wave's rows written before other lanes read them
+
+    // ---- logits of the lane's token; tile maximum when it passes m_run + kLazy
+    // (recomputed after the barrier rather than kept in registers across it)
+    const float* srow = S + aK * GP;
+    const float* rrow = fK ? wrow + rK * BR : zrow;
+    auto logits = [&](float (&s)[G]) {
+      float Sv[GP], Rv[GP];
+      ldsv<GP>(srow, Sv);
+      ldsv<GP>(rrow, Rv);
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[g] = valid ? fmaf(gK, Sv[g], Rv[g]) : -INFINITY;
+    };
+    {
+      float s[G], mv[GP];
+      logits(s);
+      ldsv<GP>(mrun, mv);
       bool hot = false;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        s0[g] = v0 ? fmaf(gK0, S0[g], R0[g]) : -INFINITY;
-        s1[g] = v1 ? fmaf(gK1, S1[g], R1[g]) : -INFINITY;
-        hot |= fmaxf(s0[g], s1[g]) > m_run[g] + kLazy;
-      }
-      // Only a logit above m_run + kLazy changes anything (the rescale below);
-      // a wave holding one publishes its exact maximum, the others nothing
-      // (their maxima are smaller than any such logit).
+      for (int g = 0; g < G; ++g) hot |= s[g] > mv[g] + kLazy;
       if (__any(hot)) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const int mk = wave_max_i32(fkey(fmaxf(s0[g], s1[g])));
-          if (lane == 0) atomicMax(&tmaxb[par][g], mk);
+          const int mk = wave_max_i32(fkey(s[g]));
+          if (lane == 0) atomicMax(&tmaxb[it % 3][g], mk);
         }
       }
     }
+    if (threadIdx.x < GP) tmaxb[(it + 1) % 3][threadIdx.x] = kKeyNegInf;  // last read two tiles ago
     lds_barrier();
-    // ---- D: lazy rescale (every thread takes the same decision).  The
-    // probabilities are first computed with the current m_run while the
-    // tile maxima are read, and again in the rare case that m_run moves.
-    float pk0[BR], pk1[BR];
-#pragma unroll
-    for (int g = 0; g < BR; ++g) { pk0[g] = 0.0f; pk1[g] = 0.0f; }
-    int tk[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) tk[g] = tmaxb[par][g];
+
+    // ---- runs of tile it + 1 (its counts are published); its key records
+    // go to the key registers now (this tile's are consumed), its value
+    // records after this tile's value batch
+    int vb_next, nv_next;
+    {
+      int kb2, nk2;
+      run_of(it + 1, slot ^ 1, kb2, nk2, vb_next, nv_next);
+      load_keys(kb2, nk2);
+      kb_cur = kb2;
+      nk_cur = nk2;
+    }
+    // ---- lazy rescale (every thread takes the same decision)
+    bool any = false;
+    float fct[G], m_run[GP];
+    ldsv<GP>(mrun, m_run);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      pk0[g] = exp2_fast(s0[g] - m_run[g]);
-      pk1[g] = exp2_fast(s1[g] - m_run[g]);
-    }
-    bool any = false;
-    float fct[G];
-    {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float tm = fkey_inv(tk[g]);
-        fct[g] = 1.0f;
-        if (tm > m_run[g] + kLazy) {
-          fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
-          m_run[g] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tm)));  // uniform
-          any = true;
-        }
+      const float tm = fkey_inv(tmaxb[it % 3][g]);
+      fct[g] = 1.0f;
+      if (tm > m_run[g] + kLazy) {
+        fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
+        m_run[g] = tm;
+        any = true;
       }
     }
     if (any) {
+      __builtin_amdgcn_wave_barrier();
+      if (lane < G) {
+        float mn = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) mn = (g == lane) ? m_run[g] : mn;
+        mrun[lane] = mn;
+      }
 #pragma unroll
       for (int g = 0; g < G; ++g) lacc[g] *= fct[g];
 #pragma unroll
@@ -574,172 +663,86 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
         for (int gg = 0; gg < G; ++gg) fz = (gg == gz) ? fct[gg] : fz;
         zt[rb] *= fz;
       }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        pk0[g] = exp2_fast(s0[g] - m_run[g]);
-        pk1[g] = exp2_fast(s1[g] - m_run[g]);
-      }
       lds_barrier();
     }
-    // ---- E: probabilities, scatter p*gamma into w, keep p of value-flagged
-    // tokens in this wave's buf rows [0, nV) and zeros in the rows after them
-    // up to the next multiple of 32 (the value batches read whole batches).
-    // A token past the range has p = 0 and adds 0 to w[0].
+    // ---- softmax weights, w scatter, weights of value-flagged tokens into the
+    // wave's rows (zeros after them up to the next multiple of 32)
+    float pk[BR];
+    {
+      float s[G];
+      logits(s);
+#pragma unroll
+      for (int g = 0; g < BR; ++g) pk[g] = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        pk[g] = exp2_fast(s[g] - m_run[g]);   // 0 for a token past the range
+        lacc[g] += pk[g];
+      }
+    }
     // p <= 2 (lazy rescale), so gamma in [0, 8) keeps y = p*gamma*2^38 in
     // [0, 2^42): one f64 fma adds 1.5*2^52, which rounds y to the nearest
-    // integer and leaves it in the low 51 bits (p and gamma are exact in f64,
-    // so this is the only rounding).
+    // integer and leaves it in the low 51 bits (p and gamma are exact in f64).
+    if (__all(!valid || (gV >= 0.0f && gV < 8.0f))) {
+      const double gd = (double)gV * kFxScaleD;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        atomicAdd(wi + g * A + aV, (unsigned long long)__double_as_longlong(fma((double)pk[g], gd, kRoundMagic)) & kMagicMask);
+    } else {
+      const float gs = gV * kFxScale;
+#pragma unroll
+      for (int g = 0; g < G; ++g) atomicAdd(wi + g * A + aV, fx_general(pk[g] * gs));
+    }
+    if (fV) stsv<BR>(wrow + rV * BR, pk);
     {
-      const float gs0 = gV0 * kFxScale, gs1 = gV1 * kFxScale;
-      const bool fast = __all((!v0 || (gV0 >= 0.0f && gV0 < 8.0f)) && (!v1 || (gV1 >= 0.0f && gV1 < 8.0f)));
-#pragma unroll
-      for (int g = 0; g < G; ++g) lacc[g] += pk0[g] + pk1[g];
-      if (fast) {
-        const double gd0 = (double)gV0 * kFxScaleD, gd1 = (double)gV1 * kFxScaleD;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          atomicAdd(wi + g * A + aV0,
-                    (unsigned long long)__double_as_longlong(fma((double)pk0[g], gd0, kRoundMagic)) & kMagicMask);
-          atomicAdd(wi + g * A + aV1,
-                    (unsigned long long)__double_as_longlong(fma((double)pk1[g], gd1, kRoundMagic)) & kMagicMask);
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          atomicAdd(wi + g * A + aV0, fx_general(pk0[g] * gs0));
-          atomicAdd(wi + g * A + aV1, fx_general(pk1[g] * gs1));
-        }
-      }
-      if (fV0) stsv<BR>(wbuf + rV0 * BR, pk0);
-      if (fV1) stsv<BR>(wbuf + rV1 * BR, pk1);
       const int zr = nV + lane;
-      if (zr < ((nV + 31) & ~31)) {
-        float z0[BR];
+      float z0[BR];
 #pragma unroll
-        for (int g = 0; g < BR; ++g) z0[g] = 0.0f;
-        stsv<BR>(wbuf + zr * BR, z0);
-      }
+      for (int g = 0; g < BR; ++g) z0[g] = 0.0f;
+      if (zr < ((nV + 15) & ~15)) stsv<BR>(wrow + zr * BR, z0);
     }
     __builtin_amdgcn_wave_barrier();
 
-    // ---- F: value residuals of this wave's records, 32 per MFMA K-step
-    // (staged records from LDS; overflow records from the cache in a separate loop)
-    auto vbatch = [&](int b0, auto from_lds) {
-      constexpr bool LDS = decltype(from_lds)::value;
-      uint32_t pr[4];  // code words of coordinate column `col`, record pairs
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int r0 = b0 + 8 * kg + 2 * e2;
-        uint32_t w0 = 0, w1 = 0;
-        if constexpr (LDS) {
-          w0 = *reinterpret_cast<const uint16_t*>(vstb + (baseV + r0) * kRecBytes + 2 * col);
-          w1 = *reinterpret_cast<const uint16_t*>(vstb + (baseV + r0 + 1) * kRecBytes + 2 * col);
-        } else {
-          if (r0 < nV) w0 = *reinterpret_cast<const uint16_t*>(recV + (int64_t)(rv0 + baseV + r0) * kRecBytes + 2 * col);
-          if (r0 + 1 < nV) w1 = *reinterpret_cast<const uint16_t*>(recV + (int64_t)(rv0 + baseV + r0 + 1) * kRecBytes + 2 * col);
-        }
-        pr[e2] = w0 | (w1 << 16);
-      }
-      // A operands: row (4g + grp) = 16rb + col, records b0 + 8kg + e; the
-      // buf rows give p = 0 to padded q-heads and to records past nV (the
-      // staged records there are finite: other waves' or zeros)
-      bf16x8 ahi[NB], alo[NB];
-      f32x4 zb[NB];  // -128 * row sums of A: cancels the code bias
-#pragma unroll
-      for (int rb = 0; rb < NB; ++rb) {
-        const int g = (16 * rb + col) >> 2, grp = col & 3;
-        float ps[8];
-        float zsum = zt[rb];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rr = b0 + 8 * kg + e;
-          const float pv = wbuf[rr * BR + g];
-          uint32_t sz = 0;
-          if constexpr (LDS) sz = *reinterpret_cast<const uint32_t*>(vstb + (baseV + rr) * kRecBytes + 32 + 4 * grp);
-          else if (rr < nV) sz = *reinterpret_cast<const uint32_t*>(recV + (int64_t)(rv0 + baseV + rr) * kRecBytes + 32 + 4 * grp);
-          ps[e] = fmaf(pv, h2f((uint16_t)(sz & 0xFFFFu)), 0.0f);
-          zsum = fmaf(pv, h2f((uint16_t)(sz >> 16)), zsum);
-        }
-        zt[rb] = zsum;
-        uint32_t hp[4], lp[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t hb = bf16_pack(ps[2 * k], ps[2 * k + 1]);
-          const float d0 = ps[2 * k] - __uint_as_float(hb << 16);
-          const float d1 = ps[2 * k + 1] - __uint_as_float(hb & 0xFFFF0000u);
-          hp[k] = hb;
-          lp[k] = bf16_pack(d0, d1);
-        }
-        ahi[rb] = u4_to_frag(hp[0], hp[1], hp[2], hp[3]);
-        alo[rb] = u4_to_frag(lp[0], lp[1], lp[2], lp[3]);
-        zb[rb] = M::mma(ahi[rb], bm128, f32x4{0, 0, 0, 0});
-        zb[rb] = M::mma(alo[rb], bm128, zb[rb]);
-      }
-      const uint32_t ps6[4] = {pr[0] >> 6, pr[1] >> 6, pr[2] >> 6, pr[3] >> 6};
-      const uint32_t ps12[4] = {pr[0] >> 12, pr[1] >> 12, pr[2] >> 12, pr[3] >> 12};
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        const Plane pl = plane_of(cc);
-        const uint32_t* src = pl.sh == 0 ? pr : pl.sh == 6 ? ps6 : ps12;
-        const bf16x8 bfr = u4_to_frag(and_or(src[0], MK[pl.m], vbias), and_or(src[1], MK[pl.m], vbias),
-                                      and_or(src[2], MK[pl.m], vbias), and_or(src[3], MK[pl.m], vbias));
-#pragma unroll
-        for (int rb = 0; rb < NB; ++rb) {
-          f32x4 t = M::mma(ahi[rb], bfr, zb[rb]);
-          t = M::mma(alo[rb], bfr, t);
-          vacc[rb][cc] += t[cc >> 1];
-        }
-      }
-    };
+    // ---- value residuals of the wave's records, 16 per batch (the first
+    // batch loaded a tile ahead, more read here)
     {
-      const int nfast = max(0, min(nV, kRecCap - baseV));
-      int b0 = 0;
-      for (; b0 + 32 <= nfast; b0 += 32) vbatch(b0, std::true_type{});
-      if (b0 < nV) {
-        if (baseV + nV <= kRecCap) vbatch(b0, std::true_type{});
-        else for (; b0 < nV; b0 += 32) vbatch(b0, std::false_type{});
+      uint32_t pr[2] = {vpr[0], vpr[1]};
+      uint32_t sz[4] = {vsz[0], vsz[1], vsz[2], vsz[3]};
+      for (int b0 = 0; b0 < nV; b0 += 16) {
+        if (b0 > 0) {
+          const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)(vb_cur + b0) * kRecBytes,
+                                                    (uint32_t)min(nV - b0, 16) * kRecBytes);
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int r0 = 4 * kg + 2 * e2;
+            const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b16(r, r0 * kRecBytes + 2 * col, 0, 0);
+            const uint32_t w1 = __builtin_amdgcn_raw_buffer_load_b16(r, (r0 + 1) * kRecBytes + 2 * col, 0, 0);
+            pr[e2] = w0 | (w1 << 16);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sz[e] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + e) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
+        }
+        vbatch(b0, pr, sz);
       }
     }
-    lds_barrier();  // staged records and buf are reused by the next tile
+    load_values(vb_next, nv_next);
+    vb_cur = vb_next;
+    nv_cur = nv_next;
   }
   }
 
-  // ---- epilogue: reduce over lanes and waves, write this range's partial state
-  __shared__ float lsum[kWaves][G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float l = wave_sum(lacc[g]);
-    if (lane == 0) lsum[wave][g] = l;
-  }
-  float* accs = buf;  // [G][D]
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) accs[i] = 0.0f;
-  __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    float z = zt[rb];
-    z += __shfl_xor(z, 16, 64);
-    z += __shfl_xor(z, 32, 64);
-    const int g = (16 * rb + col) >> 2;
-    if (kg == 0 && g < G) atomicAdd(&zt_s[g * 4 + (col & 3)], z);
-    // lane (col j, kg) of column block cc holds rows 16rb + 4kg + r = (q-head 4rb + kg, group r);
-    // only group r == cc/2 covers coordinate j + 16cc.
-    const int gq = 4 * rb + kg;
-    if (gq < G)
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        atomicAdd(&accs[gq * D + col + 16 * cc], vacc[rb][cc] * kPlaneInv[plane_of(cc).m]);
-      }
-  }
-  // ---- w V on MFMA: wave w takes coordinates 16w .. 16w+15 (rows = q-heads,
-  // K = anchors, columns = coordinates); w in bf16 hi + lo for bf16 data
-  static_assert(kWaves * 16 == D, "one 16-coordinate block per wave");
-  const int d = 16 * wave + col;
+  // ---- epilogue.  w V on MFMA: wave w takes coordinates 16 (w & 7) .. + 15
+  // and every other K-step of anchors from (w >> 3); rows = q-heads, K =
+  // anchors, columns = coordinates; w in bf16 hi + lo for bf16 data
+  __syncthreads();  // every scatter into w done
+  static_assert(kWaves == 16 && D == 128, "two waves per 16-coordinate block");
+  const int half = wave >> 3;
+  const int d = 16 * (wave & 7) + col;
   f32x4 ov = {0, 0, 0, 0};
   {
     using MV = Mfma<DT>;
     const T* AV = reinterpret_cast<const T*>(base + a.off_av) + (int64_t)h * A * D;
-#pragma unroll 4
-    for (int a0 = 0; a0 < A; a0 += MV::KSTEP) {
+    for (int a0 = half * MV::KSTEP; a0 < A; a0 += 2 * MV::KSTEP) {
       const int ab = a0 + kg * MV::KW;
       if constexpr (DT == ANCHORKV_BF16) {
         float wv[8];
@@ -769,42 +772,55 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
     }
   }
-  // (max, sum) of this range per q-head
-  __shared__ float ml_s[2][kMaxG];
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float l = 0.0f;
-    for (int w2 = 0; w2 < kWaves; ++w2) l += lsum[w2][g];
-    float m = -INFINITY;
+  float lw[G];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) m = (gg == g) ? m_run[gg] : m;
-    ml_s[0][g] = m;
-    ml_s[1][g] = l;
+  for (int g = 0; g < G; ++g) lw[g] = wave_sum(lacc[g]);
+  __syncthreads();  // w, S and the rows are no longer read: the region holds the partials
+  float* pv = reinterpret_cast<float*>(smb + L.pv);    // [kWaves][G][D]
+  float* pwv = reinterpret_cast<float*>(smb + L.pwv);  // [2][G][D]
+  float* pz = reinterpret_cast<float*>(smb + L.pz);    // [kWaves][4 BR]: (q-head, group) = 4g + grp
+  float* pl = reinterpret_cast<float*>(smb + L.pl);    // [kWaves][GP]
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    // lane (col, kg) of column block cc holds q-head 4rb + kg, coordinate col + 16cc
+    const int gq = 4 * rb + kg;
+    if (gq < G)
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) pv[(wave * G + gq) * D + col + 16 * cc] = vacc[rb][cc] * kPlaneInv[plane_of(cc).m];
+    float z = zt[rb];
+    z += __shfl_xor(z, 16, 64);
+    z += __shfl_xor(z, 32, 64);
+    if (kg == 0) pz[wave * 4 * BR + 16 * rb + col] = z;
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int g = 4 * kg + r;
+    if (g < G) pwv[(half * G + g) * D + d] = ov[r];
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (lane == g) pl[wave * GP + g] = lw[g];
   __syncthreads();
-  // lane (col, kg) holds rows g = 4kg + r of coordinate d
-  float val[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int g = 4 * kg + r;
-    val[r] = g < G ? ov[r] + accs[g * D + d] + zt_s[g * 4 + d / 32] : 0.0f;
-  }
-  if (a.S2 == 1 && !a.force_part) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int g = 4 * kg + r;
-      if (g < G) a.o[(uh * G + g) * D + d] = val[r] / ml_s[1][g];
-    }
-    return;
-  }
-  // several ranges per head, or a tail to follow: publish this one (merged by k_dec_merge)
+  // thread (q-head, coordinate): the waves' partials in a fixed order
   const int64_t ps = uh * a.S2 + sp;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int g = 4 * kg + r;
-    if (g < G) a.part_acc[(ps * G + g) * D + d] = val[r];
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int g = i / D, dd = i % D;
+    float val = pwv[g * D + dd] + pwv[(G + g) * D + dd];
+    float l = 0.0f;
+#pragma unroll 4
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      val += pv[(w2 * G + g) * D + dd] + pz[w2 * 4 * BR + 4 * g + dd / 32];
+      l += pl[w2 * GP + g];
+    }
+    const float m = mrun_s[0][g];
+    if (a.S2 == 1 && !a.force_part) {
+      a.o[(uh * G + g) * D + dd] = val / l;
+    } else {
+      // several ranges per head, or a tail to follow: publish this one (merged by k_dec_merge)
+      a.part_acc[(ps * G + g) * D + dd] = val;
+      if (dd == 0) a.part_ml[ps * G + g] = make_float2(m, l);
+    }
   }
-  if (threadIdx.x < G) a.part_ml[ps * G + threadIdx.x] = make_float2(ml_s[0][threadIdx.x], ml_s[1][threadIdx.x]);
 }
 
 // Per (unit, head) with several token ranges (and an optional tail partial):
@@ -1059,55 +1075,17 @@ __global__ __launch_bounds__(256) void k_dec_tail_bf16(const void* q, const void
     }
 }
 
-// Raise a kernel's dynamic-LDS limit to `bytes` (once per larger value).
-
-static size_t stream_lds(int G, int A, int KP, bool qsplit) {
-  const size_t GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-  const size_t NB = (4 * (size_t)G + 15) / 16;
-  return sizeof(float) * ((3 * GP * A + 3) & ~(size_t)3) + sizeof(float) * (size_t)std::max<size_t>(kTile * 4 * NB, 2048) +
-         2 * 512 * (size_t)KP * sizeof(uint4) + (size_t)kRecPad * kRecBytes + NB * 4 * (qsplit ? 2 : 1) * 64 * sizeof(uint4) +
-         NB * 64 * sizeof(float2);
-}
 constexpr size_t kLdsLimit = 158 * 1024;  // dynamic part; the static part is under 2 KB of the 160 KB
 
-template <int DT, int G, int KP, int DEPTH, int WPE>
-static int launch_stream_kp(const DecArgs& a, unsigned grid, hipStream_t st) {
-  static size_t done = 0;
-  const size_t lds = stream_lds(G, a.A, KP, DT == ANCHORKV_F32);
-  if (lds > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
-  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G, KP, DEPTH, WPE>), lds, &done)) return rc;
-  k_dec_stream<DT, G, KP, DEPTH, WPE><<<grid, 64 * kWaves, lds, st>>>(a);
-  AKV_CHECK_LAUNCH("k_dec_stream");
-  return 0;
-}
-
-// Staged 16-byte chunks per thread and side (KP; 512*KP*16/48 records per
-// tile) from the average number of residual records per 1024-token tile:
-// larger staging costs registers and LDS, records beyond it are read from
-// the cache directly.
-// Falls back to the largest staging that fits LDS (KP = 1 always fits a plan
-// that anchorkv_plan accepted).
-static int decode_kp(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C) {
-  if (G > 4) return 1;
-  const int64_t per = std::max(R_K, R_V) / std::max<int64_t>(1, H * C);
-  int kp = per <= 150 ? 1 : per <= 300 ? 2 : 3;
-  while (kp > 1 && stream_lds(G, A, kp, f32) > kLdsLimit) --kp;
-  return kp;
-}
-
-// Up to 4 q-heads per KV head: four waves per SIMD (two workgroups per CU);
-// more q-heads: two waves per SIMD (one workgroup per CU, LDS-bound).
 template <int DT, int G>
 static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
-  if constexpr (G <= 4) {
-    switch (decode_kp(G, a.A, DT == ANCHORKV_F32, a.R_K, a.R_V, a.H, a.C)) {
-      case 1: return launch_stream_kp<DT, G, 1, 1, 4>(a, grid, st);
-      case 2: return launch_stream_kp<DT, G, 2, 1, 4>(a, grid, st);
-      default: return launch_stream_kp<DT, G, 3, 1, 4>(a, grid, st);
-    }
-  } else {
-    return launch_stream_kp<DT, G, 1, 2, 2>(a, grid, st);
-  }
+  static size_t done = 0;
+  const size_t lds = dec_lds(G, a.A, DT == ANCHORKV_F32).total;
+  if (lds > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
+  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G>), lds, &done)) return rc;
+  k_dec_stream<DT, G><<<grid, 64 * kWaves, lds, st>>>(a);
+  AKV_CHECK_LAUNCH("k_dec_stream");
+  return 0;
 }
 
 template <int DT>
@@ -1118,10 +1096,7 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   uint8_t* ws = reinterpret_cast<uint8_t*>(ws_v);
   const DecodeWs w = decode_ws_layout(p);
   const int U = p.units, H = p.H, G = p.G, A = p.A, S2 = w.S2;
-  if (G > kMaxG) return fail(ANCHORKV_E_SHAPE, "decode supports q_per_kv <= %d", kMaxG);
-  if (S2 > 64) return fail(ANCHORKV_E_SHAPE, "decode: too many splits");
-  if (stream_lds(G, A, 1, DT == ANCHORKV_F32) > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
-  if (p.n_chunks > 128 * S2) return fail(ANCHORKV_E_SHAPE, "decode: too many chunks per range");
+  if (int rc = decode_supports(p)) return rc;
   prof_call_begin(st);
   DecArgs a;
   a.q = q; a.cache = cache; a.stride = p.unit_stride; a.off_words = p.off_words; a.off_rk = p.off_res_k;
@@ -1171,16 +1146,14 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   return 0;
 }
 
-int decode_blocks_per_cu(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C) {
-  // G <= 4 runs at four waves per SIMD (two 8-wave workgroups) when two
-  // copies of its LDS fit the 160 KB (static part under 2 KB each)
-  const int kp = decode_kp(G, A, f32, R_K, R_V, H, C);
-  return (G <= 4 && 2 * (stream_lds(G, A, kp, f32) + 2048) <= 160 * 1024) ? 2 : 1;
+int decode_blocks_per_cu(int, int, bool, int64_t, int64_t, int64_t, int64_t) {
+  // one 1024-thread workgroup per compute unit (four waves per SIMD)
+  return 1;
 }
 
 int decode_supports(const anchorkv_plan_info& p) {
   if (p.G > kMaxG) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: decode supports q_per_kv <= %d", kMaxG);
-  if (stream_lds(p.G, p.A, 1, p.dtype == ANCHORKV_F32) > kLdsLimit)
+  if (dec_lds(p.G, p.A, p.dtype == ANCHORKV_F32).total > kLdsLimit)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %d anchors x %d q-heads exceed the decode kernel's LDS", p.A, p.G);
   if (p.decode_splits > 64 || p.n_chunks > 128 * p.decode_splits)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: n_tokens %d too large for the decode ranges", p.N);
