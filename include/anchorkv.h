@@ -220,6 +220,22 @@ int anchorkv_workspace_offsets(const anchorkv_plan_info* plan, int64_t out[8]);
 int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, size_t cache_bytes, const void* q,
                          float* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode attention exactly as anchorkv_decode_attn, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument.  The workspace
+ * lives in a static device array of 16 MiB that each GPU the library runs on
+ * holds until the process ends; its device address is looked up once per
+ * device.  Plans that need more decode workspace than that (more than about
+ * 16 MiB of per-range partials: units * kv_heads * splits * q_per_kv * 520
+ * bytes) are refused with E_SMALL_BUFFER.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.  The library allocates and
+ * frees nothing here.
+ * Errors: E_ARG, E_SMALL_BUFFER (cache too small, or the plan's workspace
+ * exceeds the static array), E_HIP. */
+int anchorkv_decode_attn_noalloc(const anchorkv_plan_info* plan, const void* cache, size_t cache_bytes, const void* q,
+                                 float* o, void* stream);
+
 /* Decode attention over the compressed cache followed by a tail of tokens
  * appended after the one-shot compression and kept uncompressed
  * (AnchorKV-adapted page, "Adaptation notes": tokens produced during decode

@@ -106,6 +106,8 @@ def lib():
         L.anchorkv_decode_attn_tail.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_size_t, ct.c_void_p,
                                                 ct.c_void_p, ct.c_void_p, ct.c_int32, ct.c_int32, ct.c_void_p,
                                                 ct.c_void_p, ct.c_size_t, ct.c_void_p]
+        L.anchorkv_decode_attn_noalloc.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.c_size_t, ct.c_void_p,
+                                                   ct.c_void_p, ct.c_void_p]
         L.anchorkv_unit_pack_host.argtypes = [ct.POINTER(PlanInfo), ct.POINTER(UnitArrays), ct.c_void_p]
         L.anchorkv_unit_unpack_host.argtypes = [ct.POINTER(PlanInfo), ct.c_void_p, ct.POINTER(UnitArrays)]
         L.anchorkv_profile_enable.argtypes = [ct.c_int]
@@ -118,6 +120,7 @@ def lib():
 EXPORTED = ["anchorkv_version", "anchorkv_last_error", "anchorkv_params_default", "anchorkv_plan",
             "anchorkv_plan_from_header", "anchorkv_cache_layout", "anchorkv_decode_workspace_bytes",
             "anchorkv_compress", "anchorkv_workspace_offsets", "anchorkv_decode_attn", "anchorkv_decode_attn_tail",
+            "anchorkv_decode_attn_noalloc",
             "anchorkv_unit_pack_host",
             "anchorkv_unit_unpack_host", "anchorkv_profile_enable", "anchorkv_profile_read"]
 
@@ -239,6 +242,20 @@ def decode_attn(p: PlanInfo, cache, q, o, workspace, stream=None):
     _expect("decode_attn", "o", o, (p.units, p.H * p.G, p.D), torch.float32)
     _check(lib().anchorkv_decode_attn(ct.byref(p), _ptr(cache), _nbytes(cache), _ptr(q), _ptr(o), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream)))
+
+
+def decode_attn_noalloc(p: PlanInfo, cache, q, o, stream=None):
+    """decode_attn with the library's static device workspace (no workspace
+    tensor; calls that overlap on one GPU race)."""
+    for t in (cache, q, o):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("decode_attn_noalloc: inputs must be contiguous device tensors")
+    import torch
+    _check_cache("decode_attn_noalloc", p, cache)
+    _expect("decode_attn_noalloc", "q", q, (p.units, p.H * p.G, p.D), _elem_dtype(p))
+    _expect("decode_attn_noalloc", "o", o, (p.units, p.H * p.G, p.D), torch.float32)
+    _check(lib().anchorkv_decode_attn_noalloc(ct.byref(p), _ptr(cache), _nbytes(cache), _ptr(q), _ptr(o),
+                                              _stream(stream)))
 
 
 def decode_attn_tail(p: PlanInfo, cache, q, K_tail, V_tail, n_tail: int, o, workspace, stream=None):

@@ -37,6 +37,7 @@
 #include "launch_common.hpp"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace akv {
@@ -44,7 +45,6 @@ namespace akv {
 
 constexpr int kMaxG = 8;          // q-heads per KV head supported by decode
 constexpr int kTile = 1024;       // tokens per tile (= residual-offset chunk)
-constexpr int kWaves = 16;        // waves per workgroup; 64 tokens per wave per tile, one per lane
 constexpr uint32_t kCodeBias = 0x43004300u;  // bf16 pair (128, 128)
 constexpr float kFxScale = 0x1p38f;               // fixed-point scale of the w scatter
 constexpr double kFxScaleD = 0x1p38;
@@ -172,46 +172,50 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
 
 template <int G> constexpr int kGPad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
 
-// LDS of the stream kernel (bytes from the start of the dynamic region).
-// Main phase: w [G][A] u64 | S [A][GP] f32 | rows [kWaves][64][BR] f32 |
-// K-batch query fragments [NB*4*QH][64] uint4 | their column sums [NB][64]
-// float2.  Epilogue (after the last read of w): the per-wave partial outputs
-// [kWaves][G][D], the two halves of w V [2][G][D], the zero-point sums
-// [kWaves][BR*4] and the softmax sums [kWaves][GP] reuse the region.
+// LDS of the stream kernel (bytes from the start of the dynamic region), for
+// NW waves of 64 * (16 / NW) tokens each per 1024-token tile.  Main phase:
+// w [G][A] u64 | S [A][GP] f32 | rows [1024][BR] f32 (each wave its own
+// 1024 / NW rows) | K-batch query fragments [NB*4*QH][64] uint4 | their column
+// sums [NB][64] float2.  Epilogue (after the last read of w): the per-wave
+// partial outputs [NW][G][D], the parts of w V [NW / 8][G][D], the zero-point
+// sums [NW][4 BR] and the softmax sums [NW][GP] reuse the region.
 struct DecLds {
   size_t S, rows, qbs, qcs, main;
   size_t pv, pwv, pz, pl, epi;
   size_t total;
 };
 __host__ __device__ constexpr size_t lds_align(size_t x) { return (x + 15) & ~(size_t)15; }
-__host__ __device__ inline DecLds dec_lds(int G, int A, bool qsplit) {
+__host__ __device__ inline DecLds dec_lds(int G, int A, bool qsplit, int NW) {
   const size_t GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   const size_t NB = (4 * (size_t)G + 15) / 16, BR = 4 * NB;
   DecLds L{};
   L.S = lds_align(8 * (size_t)G * A);
   L.rows = L.S + lds_align(4 * GP * (size_t)A);
-  L.qbs = L.rows + (size_t)kWaves * 64 * BR * 4;
+  L.qbs = L.rows + (size_t)kTile * BR * 4;
   L.qcs = L.qbs + NB * 4 * (qsplit ? 2 : 1) * 64 * 16;
   L.main = L.qcs + NB * 64 * 8;
   L.pv = 0;
-  L.pwv = L.pv + (size_t)kWaves * G * kHeadDim * 4;
-  L.pz = L.pwv + 2 * (size_t)G * kHeadDim * 4;
-  L.pl = L.pz + (size_t)kWaves * BR * 4 * 4;
-  L.epi = L.pl + (size_t)kWaves * GP * 4;
+  L.pwv = L.pv + (size_t)NW * G * kHeadDim * 4;
+  L.pz = L.pwv + (size_t)(NW / 8) * G * kHeadDim * 4;
+  L.pl = L.pz + (size_t)NW * BR * 4 * 4;
+  L.epi = L.pl + (size_t)NW * GP * 4;
   L.total = L.main > L.epi ? L.main : L.epi;
   return L;
 }
 
-// One workgroup of kWaves waves (1024 threads) per (unit, head, range of
-// 1024-token chunks).  Wave w owns tokens 64w .. 64w + 63 of every tile, one
-// per lane.  Per tile there is one workgroup barrier, between the logits (all
-// waves publish a new tile maximum only when one passes m_run + kLazy) and the
-// softmax weights; everything else a wave needs is its own:
+// One workgroup of NW waves per (unit, head, range of 1024-token chunks).
+// Wave w owns tokens w*TT .. w*TT + TT - 1 of every tile (TT = 1024 / NW),
+// TPL = TT / 64 adjacent tokens per lane: NW = 16 (one token per lane, 1024
+// threads, one workgroup per compute unit) or NW = 8 (two tokens per lane,
+// two workgroups per compute unit when their LDS fits).  Per tile there is
+// one workgroup barrier, between the logits (a wave publishes its maxima
+// only when a logit passes m_run + kLazy) and the softmax weights;
+// everything else a wave needs is its own:
 //  * the residual records of a wave's flagged tokens are a contiguous run of
 //    the tile's records; the run starts at the tile's chunk offset plus the
 //    flagged counts of the waves before it, which every wave publishes a tile
 //    ahead (its pointer words are loaded two tiles ahead);
-//  * the first 16 key records and 32 value records of the run are loaded into
+//  * the first 16 key records and 16 value records of the run are loaded into
 //    registers a tile ahead, directly in MFMA operand layout (range-checked
 //    buffer loads: records past the run read as zeros); more are read when
 //    needed;
@@ -221,11 +225,14 @@ __host__ __device__ inline DecLds dec_lds(int G, int A, bool qsplit) {
 //    tile cannot race with a wave still reading the previous one.
 // The epilogue sums the waves' partial outputs in a fixed order (no float
 // atomics), so the output does not depend on the order the waves ran in.
-template <int DT, int G>
-__global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
+template <int DT, int G, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stream(DecArgs a) {
   using T = typename Elem<DT>::T;
   using M = Mfma<ANCHORKV_BF16>;
   constexpr int D = kHeadDim;
+  constexpr int TT = kTile / NW;                 // tokens per wave per tile
+  constexpr int TPL = TT / 64;                   // tokens per lane (adjacent)
+  static_assert(TPL == 1 || TPL == 2, "one or two tokens per lane");
   constexpr int GP = kGPad<G>;                   // q-heads per anchor row in LDS (padded)
   constexpr int NB = (4 * G + 15) / 16;          // 16-wide blocks of (q-head, group) pairs
   constexpr int BR = 4 * NB;                     // floats per wave row (q-heads >= G read as 0)
@@ -233,22 +240,23 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
   constexpr int QH = QSPLIT ? 2 : 1;
   extern __shared__ __align__(16) float sm[];
   const int A = a.A;
-  const DecLds L = dec_lds(G, A, QSPLIT);
+  const DecLds L = dec_lds(G, A, QSPLIT, NW);
   uint8_t* smb = reinterpret_cast<uint8_t*>(sm);
   // w[g][a] in fixed point, q-head-major (random anchors spread over the banks)
   unsigned long long* wi = reinterpret_cast<unsigned long long*>(smb);
   float* S = reinterpret_cast<float*>(smb + L.S);         // [A][GP]
-  float* rows = reinterpret_cast<float*>(smb + L.rows);   // [kWaves][64][BR]
+  float* rows = reinterpret_cast<float*>(smb + L.rows);   // [NW][TT][BR]
   uint4 (*qbs)[64] = reinterpret_cast<uint4 (*)[64]>(smb + L.qbs);
   float2* qcs = reinterpret_cast<float2*>(smb + L.qcs);  // [NB][64]
-  __shared__ int cnt[2][kWaves];   // per wave and tile parity: key-flagged | value-flagged << 16
+  __shared__ int cnt[2][NW];       // per wave and tile parity: key-flagged | value-flagged << 16
   __shared__ int offs[2][130];     // first record of each chunk of the range (and of the chunk after)
   __shared__ __align__(16) int tmaxb[3][GP];
+  __shared__ int hot_any[3];       // some wave published a tile maximum
   __shared__ __align__(16) float zrow[BR];
   // running maximum per q-head (log2 units), one copy per wave: every wave
   // takes the same decisions from the same tile maxima; kept in LDS rather
   // than registers (it is read twice per tile)
-  __shared__ __align__(16) float mrun_s[kWaves][GP];
+  __shared__ __align__(16) float mrun_s[NW][GP];
 
   int bid = blockIdx.x;
   const int sp = bid % a.S2; bid /= a.S2;
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
   const int64_t uh = (int64_t)u * a.H + h;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave: uniform
   const int col = lane & 15, kg = lane >> 4;
-  float* wrow = rows + wave * 64 * BR;   // this wave's rows
+  float* wrow = rows + wave * TT * BR;   // this wave's rows
   const int c0 = sp * a.cps, c1 = min(a.C, c0 + a.cps);
   const int t_beg = c0 * kTile, t_end = min(a.N, c1 * kTile);
   const int nch = max(0, c1 - c0);
@@ -292,7 +300,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
   for (int i = threadIdx.x; i < G * A; i += blockDim.x) wi[i] = 0ull;
   if (threadIdx.x < BR) zrow[threadIdx.x] = 0.0f;
   if (threadIdx.x < 3 * GP) (&tmaxb[0][0])[threadIdx.x] = kKeyNegInf;
-  if (threadIdx.x < kWaves * GP) (&mrun_s[0][0])[threadIdx.x] = -INFINITY;
+  if (threadIdx.x < 3) hot_any[threadIdx.x] = 0;
+  if (threadIdx.x < NW * GP) (&mrun_s[0][0])[threadIdx.x] = -INFINITY;
   for (int i = threadIdx.x; i <= nch; i += blockDim.x) {
     const int fl = h * a.C + c0 + i;
     const bool last = fl >= a.H * a.C;
@@ -310,9 +319,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
   // Key-side B fragments: column kappa = 16*cb + col = 4*g + grp; in MFMA step
   // st (= coordinate group st) the lane supplies q[g][d] / 4^m for
   // d = j + 16c, j = 4kg + (e&3), c = 2st + (e>>2), when grp == st, zeros
-  // otherwise.  cinit = -128 * (sum of what the column is fed), so the
-  // accumulator ends at sum_d q[g][d] * code_d.  The same in every wave: wave 0
-  // writes them to LDS, with each column's query sum and initial value.
+  // otherwise (exact for bf16 queries: the scale by 4^-m is a power of two).
+  // cinit = -128 * (sum of what the column is fed), so the accumulator ends at
+  // sum_d q[g][d] code_d.  The same in every wave: wave 0 writes them to LDS,
+  // with each column's query sum and initial value.
   if (wave == 0) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
@@ -354,15 +364,38 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
   // value side: B = -128 everywhere cancels the code bias of the A rows
   const bf16x4 bm128_4 = u2_to_frag4(0xC300C300u, 0xC300C300u);
 
-  // pointer words: one 8-byte load per lane and tile, two tiles ahead
-  // (range-checked: a token past the range reads zero words, so no flags)
+  // pointer words: TPL adjacent tokens' (K word, V word) pairs per lane and
+  // tile, loaded two tiles ahead (range-checked: a token past the range reads
+  // zero words, so no flags)
+  using Words = typename std::conditional<TPL == 1, uint2, uint4>::type;
   const uint32_t* words = reinterpret_cast<const uint32_t*>(base + a.off_words) + (int64_t)h * a.N * 2;
   const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(words + (int64_t)t_beg * 2, (uint32_t)(t_end - t_beg) * 8u);
-  auto load_words = [&](int it) -> uint2 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(wrs, (int)((uint32_t)(it * kTile + wave * 64 + lane) * 8u), 0, 0);
-    return make_uint2(v[0], v[1]);
+  auto load_words = [&](int it) -> Words {
+    const int off = (int)((uint32_t)(it * kTile + wave * TT + lane * TPL) * 8u);
+    if constexpr (TPL == 1) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(wrs, off, 0, 0);
+      return make_uint2(v[0], v[1]);
+    } else {
+      // an odd last token: the 8 bytes past it read as zero only if the whole
+      // 16-byte access is out of range, so a 16-byte access that straddles
+      // the end is split into two 8-byte loads
+      const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(wrs, off, 0, 0);
+      const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(wrs, off + 8, 0, 0);
+      return make_uint4(v0[0], v0[1], v1[0], v1[1]);
+    }
   };
-  uint2 wq[2];
+  auto flag_counts = [&](const Words& wv) {
+    int nk, nv;
+    if constexpr (TPL == 1) {
+      nk = __popcll(__ballot((wv.x & 0x8000u) != 0));
+      nv = __popcll(__ballot((wv.y & 0x8000u) != 0));
+    } else {
+      nk = __popcll(__ballot((wv.x & 0x8000u) != 0)) + __popcll(__ballot((wv.z & 0x8000u) != 0));
+      nv = __popcll(__ballot((wv.y & 0x8000u) != 0)) + __popcll(__ballot((wv.w & 0x8000u) != 0));
+    }
+    return nk | (nv << 16);
+  };
+  Words wq[2];
   wq[0] = load_words(0);
   wq[1] = load_words(1);
 
@@ -371,7 +404,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
   {
     using MS = Mfma<DT>;
     const T* AK = reinterpret_cast<const T*>(base + a.off_ak) + (int64_t)h * A * D;
-    for (int t = wave; t < (A + 15) / 16; t += kWaves) {
+    for (int t = wave; t < (A + 15) / 16; t += NW) {
       const int ar = 16 * t + col;
       f32x4 sacc = {0, 0, 0, 0};
 #pragma unroll
@@ -388,56 +421,55 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
         }
     }
   }
-  // flagged counts of tile 0
   {
-    const unsigned long long bk = __ballot((wq[0].x & 0x8000u) != 0), bv = __ballot((wq[0].y & 0x8000u) != 0);
-    if (lane == 0) cnt[0][wave] = __popcll(bk) | (__popcll(bv) << 16);
+    const int fc = flag_counts(wq[0]);   // flagged counts of tile 0
+    if (lane == 0) cnt[0][wave] = fc;
   }
   __syncthreads();  // S, qbs, qcs, cnt[0]; qf is dead (rows become the waves' rows)
 
-  // Record prefetch of a tile: this wave's run of key / value records starts at
-  // the tile's chunk offset plus the counts of the waves before it.
+  // Record runs of a tile: this wave's key / value records start at the
+  // tile's chunk offset plus the counts of the waves before it.
   auto run_of = [&](int it, int par, int& kb, int& nk, int& vb, int& nv) {
     const int ic = min(it, nch);
     const int mine = cnt[par][wave];
-    const int pre = __builtin_amdgcn_readfirstlane(row_sum_i32(lane < wave ? cnt[par][lane & (kWaves - 1)] : 0));
+    const int pre = __builtin_amdgcn_readfirstlane(row_sum_i32(lane < wave ? cnt[par][lane & (NW - 1)] : 0));
     kb = __builtin_amdgcn_readfirstlane(offs[0][ic]) + (pre & 0xFFFF);
     vb = __builtin_amdgcn_readfirstlane(offs[1][ic]) + (pre >> 16);
     nk = it < nch ? (mine & 0xFFFF) : 0;
     nv = it < nch ? (mine >> 16) : 0;
   };
-  // key batch 0: lane (col, kg) holds bytes 8kg..8kg+7 of record col and the
+  // key batch: lane (col, kg) holds bytes 8kg..8kg+7 of record col and the
   // (scale, zero) word of group col & 3 of records 4kg + r
   uint2 kx;
   uint32_t ksz[4];
-  auto load_keys = [&](int kb, int nk) {
-    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)kb * kRecBytes, (uint32_t)min(nk, 16) * kRecBytes);
-    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, col * kRecBytes + 8 * kg, 0, 0);
-    kx = make_uint2(x[0], x[1]);
+  auto load_keys = [&](int kb, int nk, uint2& x, uint32_t (&sz)[4]) {
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)kb * kRecBytes, (uint32_t)min(max(nk, 0), 16) * kRecBytes);
+    const auto xx = __builtin_amdgcn_raw_buffer_load_b64(r, col * kRecBytes + 8 * kg, 0, 0);
+    x = make_uint2(xx[0], xx[1]);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      ksz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
+      sz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
   };
-  // value batch 0: code word col of records 4kg + e (pairs packed), and the
+  // value batch: code word col of records 4kg + e (pairs packed), and the
   // (scale, zero) word of group col & 3 of the same records
   uint32_t vpr[2], vsz[4];
-  auto load_values = [&](int vb, int nv) {
-    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)vb * kRecBytes, (uint32_t)min(nv, 16) * kRecBytes);
+  auto load_values = [&](int vb, int nv, uint32_t (&pr)[2], uint32_t (&sz)[4]) {
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)vb * kRecBytes, (uint32_t)min(max(nv, 0), 16) * kRecBytes);
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
       const int r0 = 4 * kg + 2 * e2;
       const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b16(r, r0 * kRecBytes + 2 * col, 0, 0);
       const uint32_t w1 = __builtin_amdgcn_raw_buffer_load_b16(r, (r0 + 1) * kRecBytes + 2 * col, 0, 0);
-      vpr[e2] = w0 | (w1 << 16);
+      pr[e2] = w0 | (w1 << 16);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      vsz[e] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + e) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
+      sz[e] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + e) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
   };
   int kb_cur, nk_cur, vb_cur, nv_cur;
   run_of(0, 0, kb_cur, nk_cur, vb_cur, nv_cur);
-  load_keys(kb_cur, nk_cur);
-  load_values(vb_cur, nv_cur);
+  load_keys(kb_cur, nk_cur, kx, ksz);
+  load_values(vb_cur, nv_cur, vpr, vsz);
 
   float* mrun = mrun_s[wave];
   float lacc[G];
@@ -456,8 +488,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) zt[rb] = 0.0f;
 
-  // ---- key-residual logits of records b0 .. b0+15 of the wave's run, from the
-  // fragments (x, sz) into the wave's rows [b0, b0 + 16) (row = rank)
+  // ---- key-residual logits (log2 units) of records b0 .. b0+15 of the
+  // wave's run, from the fragments (x, sz) into the wave's rows [b0, b0 + 16)
+  // (row = rank)
   auto kbatch = [&](int b0, int nk, uint2 x, const uint32_t (&sz)[4]) {
     const uint32_t xs[3][2] = {{x.x, x.y}, {x.x >> 6, x.y >> 6}, {x.x >> 12, x.y >> 12}};
     bf16x8 af[4];
@@ -478,12 +511,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
         if constexpr (QSPLIT) cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH + 1][lane]), cacc);
       }
       const int kap = 16 * cb + col, g = kap >> 2, grp = kap & 3;
+      const bool wr = grp == 0 && g < G;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ii = b0 + 4 * kg + r;
         const float sc = h2f((uint16_t)(sz[r] & 0xFFFFu)), z = h2f((uint16_t)(sz[r] >> 16));
         const float val = quad_sum(fmaf(sc, cacc[r], z * qc.x));
-        if (ii < nk && grp == 0 && g < G) wrow[ii * BR + g] = val * a.c;
+        if (wr && ii < nk) wrow[ii * BR + g] = val * a.c;
       }
     }
   };
@@ -541,72 +575,88 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
     // no early exit: a tile past the range (odd tile count) has no valid
     // token, no record and no maximum, and every wave still takes its barrier
     const int it = base_it + slot;
-    const int t = t_beg + it * kTile + wave * 64 + lane;
-    const bool valid = it < nch && t < t_end;
-    const uint2 wd = wq[slot];
-    const uint2 wn = wq[slot ^ 1];       // words of tile it + 1 (loaded a tile ago)
+    const int tm3 = it % 3;
+    const int t0 = t_beg + it * kTile + wave * TT + lane * TPL;   // the lane's first token
+    const Words wd = wq[slot];
+    const Words wn = wq[slot ^ 1];       // words of tile it + 1 (loaded a tile ago)
     wq[slot] = load_words(it + 2);
-    // flagged counts of tile it + 1 (read after this tile's barrier)
     {
-      const unsigned long long bk = __ballot((wn.x & 0x8000u) != 0), bv = __ballot((wn.y & 0x8000u) != 0);
-      if (lane == 0) cnt[slot ^ 1][wave] = __popcll(bk) | (__popcll(bv) << 16);
+      const int fc = flag_counts(wn);    // flagged counts of tile it + 1 (read after this tile's barrier)
+      if (lane == 0) cnt[slot ^ 1][wave] = fc;
     }
-    // ---- pointer words of the lane's token
-    const int aK = wd.x & 0x7FFF, aV = wd.y & 0x7FFF;
-    const bool fK = (wd.x & 0x8000u) != 0, fV = (wd.y & 0x8000u) != 0;
-    const float gK = h2f((uint16_t)(wd.x >> 16)), gV = h2f((uint16_t)(wd.y >> 16));
-    const unsigned long long bK = __ballot(fK), bV = __ballot(fV);
-    const int rK = lanes_below(bK), rV = lanes_below(bV);
+    // ---- pointer words of the lane's tokens
+    uint32_t wk[TPL], wv[TPL];
+    if constexpr (TPL == 1) { wk[0] = wd.x; wv[0] = wd.y; }
+    else { wk[0] = wd.x; wv[0] = wd.y; wk[1] = wd.z; wv[1] = wd.w; }
+    bool valid[TPL], fK[TPL], fV[TPL];
+    int rK[TPL], rV[TPL];
+    {
+      unsigned long long bK[TPL], bV[TPL];
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) {
+        valid[k] = it < nch && t0 + k < t_end;
+        fK[k] = (wk[k] & 0x8000u) != 0;
+        fV[k] = (wv[k] & 0x8000u) != 0;
+        bK[k] = __ballot(fK[k]);
+        bV[k] = __ballot(fV[k]);
+      }
+      // rank of token (lane, k) among the wave's flagged tokens, in token order
+      int below_k = 0, below_v = 0;
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) { below_k += lanes_below(bK[k]); below_v += lanes_below(bV[k]); }
+      rK[0] = below_k; rV[0] = below_v;
+      if constexpr (TPL == 2) { rK[1] = below_k + (fK[0] ? 1 : 0); rV[1] = below_v + (fV[0] ? 1 : 0); }
+    }
     const int nK = nk_cur, nV = nv_cur;
 
     // ---- key-residual logits of the wave's records, 16 per batch; the first
-    // batch was loaded a tile ahead, more (rare: over 16 of the wave's 64
-    // tokens) are read here
+    // batch was loaded a tile ahead, more are read here
     {
       uint2 x = kx;
       uint32_t sz[4] = {ksz[0], ksz[1], ksz[2], ksz[3]};
       for (int b0 = 0; b0 < nK; b0 += 16) {
-        if (b0 > 0) {
-          const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)(kb_cur + b0) * kRecBytes,
-                                                    (uint32_t)min(nK - b0, 16) * kRecBytes);
-          const auto xx = __builtin_amdgcn_raw_buffer_load_b64(r, col * kRecBytes + 8 * kg, 0, 0);
-          x = make_uint2(xx[0], xx[1]);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            sz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
-        }
+        if (b0 > 0) load_keys(kb_cur + b0, nK - b0, x, sz);
         kbatch(b0, nK, x, sz);
       }
     }
     __builtin_amdgcn_wave_barrier();  // the wave's rows written before other lanes read them
 
-    // ---- logits of the lane's token; tile maximum when it passes m_run + kLazy
+    // ---- logits of the lane's tokens; tile maximum when one passes m_run + kLazy
     // (recomputed after the barrier rather than kept in registers across it)
-    const float* srow = S + aK * GP;
-    const float* rrow = fK ? wrow + rK * BR : zrow;
-    auto logits = [&](float (&s)[G]) {
+    auto logits = [&](int k, float (&s)[G]) {
       float Sv[GP], Rv[GP];
-      ldsv<GP>(srow, Sv);
-      ldsv<GP>(rrow, Rv);
+      ldsv<GP>(S + (wk[k] & 0x7FFF) * GP, Sv);
+      ldsv<GP>(fK[k] ? wrow + rK[k] * BR : zrow, Rv);
+      const float gK = h2f((uint16_t)(wk[k] >> 16));
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = valid ? fmaf(gK, Sv[g], Rv[g]) : -INFINITY;
+      for (int g = 0; g < G; ++g) s[g] = valid[k] ? fmaf(gK, Sv[g], Rv[g]) : -INFINITY;
     };
     {
-      float s[G], mv[GP];
-      logits(s);
+      float mv[GP];
       ldsv<GP>(mrun, mv);
       bool hot = false;
+      float smax[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) hot |= s[g] > mv[g] + kLazy;
+      for (int k = 0; k < TPL; ++k) {
+        float s[G];
+        logits(k, s);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          smax[g] = k == 0 ? s[g] : fmaxf(smax[g], s[g]);
+          hot |= s[g] > mv[g] + kLazy;
+        }
+      }
       if (__any(hot)) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const int mk = wave_max_i32(fkey(s[g]));
-          if (lane == 0) atomicMax(&tmaxb[it % 3][g], mk);
+          const int mk = wave_max_i32(fkey(smax[g]));
+          if (lane == 0) atomicMax(&tmaxb[tm3][g], mk);
         }
+        if (lane == 0) hot_any[tm3] = 1;
       }
     }
     if (threadIdx.x < GP) tmaxb[(it + 1) % 3][threadIdx.x] = kKeyNegInf;  // last read two tiles ago
+    if (threadIdx.x == 0) hot_any[(it + 1) % 3] = 0;
     lds_barrier();
 
     // ---- runs of tile it + 1 (its counts are published); its key records
@@ -616,88 +666,110 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
     {
       int kb2, nk2;
       run_of(it + 1, slot ^ 1, kb2, nk2, vb_next, nv_next);
-      load_keys(kb2, nk2);
+      load_keys(kb2, nk2, kx, ksz);
       kb_cur = kb2;
       nk_cur = nk2;
     }
-    // ---- lazy rescale (every thread takes the same decision)
-    bool any = false;
-    float fct[G], m_run[GP];
+    // ---- lazy rescale (every thread takes the same decision); skipped
+    // unless some wave published a tile maximum
+    float m_run[GP];
     ldsv<GP>(mrun, m_run);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float tm = fkey_inv(tmaxb[it % 3][g]);
-      fct[g] = 1.0f;
-      if (tm > m_run[g] + kLazy) {
-        fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
-        m_run[g] = tm;
-        any = true;
-      }
-    }
-    if (any) {
-      __builtin_amdgcn_wave_barrier();
-      if (lane < G) {
-        float mn = 0.0f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) mn = (g == lane) ? m_run[g] : mn;
-        mrun[lane] = mn;
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) lacc[g] *= fct[g];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        if (fct[g] != 1.0f)
-          for (int i = threadIdx.x; i < A; i += blockDim.x)
-            wi[g * A + i] = (unsigned long long)__double2ll_rn((double)(long long)wi[g * A + i] * (double)fct[g]);
-#pragma unroll
-      for (int rb = 0; rb < NB; ++rb) {
-        const int g = 4 * rb + kg;  // accumulator rows 16rb + 4kg + r -> q-head 4rb + kg
-        float f = 1.0f;
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] *= f;
-        const int gz = (16 * rb + col) >> 2;  // z row (rb, col)
-        float fz = 1.0f;
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg) fz = (gg == gz) ? fct[gg] : fz;
-        zt[rb] *= fz;
-      }
-      lds_barrier();
-    }
-    // ---- softmax weights, w scatter, weights of value-flagged tokens into the
-    // wave's rows (zeros after them up to the next multiple of 32)
-    float pk[BR];
-    {
-      float s[G];
-      logits(s);
-#pragma unroll
-      for (int g = 0; g < BR; ++g) pk[g] = 0.0f;
+    if (__builtin_amdgcn_readfirstlane(hot_any[tm3])) {
+      bool any = false;
+      float fct[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        pk[g] = exp2_fast(s[g] - m_run[g]);   // 0 for a token past the range
-        lacc[g] += pk[g];
+        const float tm = fkey_inv(tmaxb[tm3][g]);
+        fct[g] = 1.0f;
+        if (tm > m_run[g] + kLazy) {
+          fct[g] = (m_run[g] == -INFINITY) ? 0.0f : exp2_fast(m_run[g] - tm);
+          m_run[g] = tm;
+          any = true;
+        }
+      }
+      if (any) {
+        __builtin_amdgcn_wave_barrier();
+        if (lane < G) {
+          float mn = 0.0f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) mn = (g == lane) ? m_run[g] : mn;
+          mrun[lane] = mn;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) lacc[g] *= fct[g];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (fct[g] != 1.0f)
+            for (int i = threadIdx.x; i < A; i += blockDim.x)
+              wi[g * A + i] = (unsigned long long)__double2ll_rn((double)(long long)wi[g * A + i] * (double)fct[g]);
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+          const int g = 4 * rb + kg;  // accumulator rows 16rb + 4kg + r -> q-head 4rb + kg
+          float f = 1.0f;
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) vacc[rb][cc] *= f;
+          const int gz = (16 * rb + col) >> 2;  // z row (rb, col)
+          float fz = 1.0f;
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) fz = (gg == gz) ? fct[gg] : fz;
+          zt[rb] *= fz;
+        }
+        lds_barrier();
       }
     }
+    // ---- softmax weights, w scatter, weights of value-flagged tokens into the
+    // wave's rows (zeros after them up to the next multiple of 16).
     // p <= 2 (lazy rescale), so gamma in [0, 8) keeps y = p*gamma*2^38 in
     // [0, 2^42): one f64 fma adds 1.5*2^52, which rounds y to the nearest
     // integer and leaves it in the low 51 bits (p and gamma are exact in f64).
-    if (__all(!valid || (gV >= 0.0f && gV < 8.0f))) {
-      const double gd = (double)gV * kFxScaleD;
+    bool fast = true;
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-        atomicAdd(wi + g * A + aV, (unsigned long long)__double_as_longlong(fma((double)pk[g], gd, kRoundMagic)) & kMagicMask);
-    } else {
-      const float gs = gV * kFxScale;
-#pragma unroll
-      for (int g = 0; g < G; ++g) atomicAdd(wi + g * A + aV, fx_general(pk[g] * gs));
+    for (int k = 0; k < TPL; ++k) {
+      const float gV = h2f((uint16_t)(wv[k] >> 16));
+      fast = fast && (!valid[k] || (gV >= 0.0f && gV < 8.0f));
     }
-    if (fV) stsv<BR>(wrow + rV * BR, pk);
+    fast = __all(fast);
+    // every token's logits are read from the rows before any value row is
+    // written over them (the rows of key logits and of value weights are the
+    // same wave-private rows)
+    float pk[TPL][BR];
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      float s[G];
+      logits(k, s);
+#pragma unroll
+      for (int g = 0; g < BR; ++g) pk[k][g] = 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        pk[k][g] = exp2_fast(s[g] - m_run[g]);   // 0 for a token past the range
+        lacc[g] += pk[k][g];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      const int aV = wv[k] & 0x7FFF;
+      const float gV = h2f((uint16_t)(wv[k] >> 16));
+      if (fast) {
+        const double gd = (double)gV * kFxScaleD;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          atomicAdd(wi + g * A + aV,
+                    (unsigned long long)__double_as_longlong(fma((double)pk[k][g], gd, kRoundMagic)) & kMagicMask);
+      } else {
+        const float gs = gV * kFxScale;
+#pragma unroll
+        for (int g = 0; g < G; ++g) atomicAdd(wi + g * A + aV, fx_general(pk[k][g] * gs));
+      }
+      if (fV[k]) stsv<BR>(wrow + rV[k] * BR, pk[k]);
+    }
     {
-      const int zr = nV + lane;
       float z0[BR];
 #pragma unroll
       for (int g = 0; g < BR; ++g) z0[g] = 0.0f;
+      const int zr = nV + lane;
       if (zr < ((nV + 15) & ~15)) stsv<BR>(wrow + zr * BR, z0);
     }
     __builtin_amdgcn_wave_barrier();
@@ -708,48 +780,36 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
       uint32_t pr[2] = {vpr[0], vpr[1]};
       uint32_t sz[4] = {vsz[0], vsz[1], vsz[2], vsz[3]};
       for (int b0 = 0; b0 < nV; b0 += 16) {
-        if (b0 > 0) {
-          const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)(vb_cur + b0) * kRecBytes,
-                                                    (uint32_t)min(nV - b0, 16) * kRecBytes);
-#pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2) {
-            const int r0 = 4 * kg + 2 * e2;
-            const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b16(r, r0 * kRecBytes + 2 * col, 0, 0);
-            const uint32_t w1 = __builtin_amdgcn_raw_buffer_load_b16(r, (r0 + 1) * kRecBytes + 2 * col, 0, 0);
-            pr[e2] = w0 | (w1 << 16);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sz[e] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + e) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
-        }
+        if (b0 > 0) load_values(vb_cur + b0, nV - b0, pr, sz);
         vbatch(b0, pr, sz);
       }
     }
-    load_values(vb_next, nv_next);
+    load_values(vb_next, nv_next, vpr, vsz);
     vb_cur = vb_next;
     nv_cur = nv_next;
   }
   }
 
   // ---- epilogue.  w V on MFMA: wave w takes coordinates 16 (w & 7) .. + 15
-  // and every other K-step of anchors from (w >> 3); rows = q-heads, K =
-  // anchors, columns = coordinates; w in bf16 hi + lo for bf16 data
+  // and, with 16 waves, every other K-step of anchors from (w >> 3); rows =
+  // q-heads, K = anchors, columns = coordinates; w in bf16 hi + lo for bf16 data
   __syncthreads();  // every scatter into w done
-  static_assert(kWaves == 16 && D == 128, "two waves per 16-coordinate block");
-  const int half = wave >> 3;
+  static_assert(D == 128 && (NW == 8 || NW == 16), "eight 16-coordinate blocks");
+  constexpr int NPART = NW / 8;
+  const int part = wave >> 3;
   const int d = 16 * (wave & 7) + col;
   f32x4 ov = {0, 0, 0, 0};
   {
     using MV = Mfma<DT>;
     const T* AV = reinterpret_cast<const T*>(base + a.off_av) + (int64_t)h * A * D;
-    for (int a0 = half * MV::KSTEP; a0 < A; a0 += 2 * MV::KSTEP) {
+    for (int a0 = part * MV::KSTEP; a0 < A; a0 += NPART * MV::KSTEP) {
       const int ab = a0 + kg * MV::KW;
       if constexpr (DT == ANCHORKV_BF16) {
-        float wv[8];
+        float wvv[8];
         uint32_t vb[4];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          wv[e] = (col < G && ab + e < A) ? (float)((double)(long long)wi[col * A + ab + e] * kFxInv) : 0.0f;
+          wvv[e] = (col < G && ab + e < A) ? (float)((double)(long long)wi[col * A + ab + e] * kFxInv) : 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const uint32_t v0 = ab + 2 * k < A ? (uint32_t)AV[(int64_t)(ab + 2 * k) * D + d] : 0u;
@@ -759,16 +819,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
         uint32_t hp[4], lp[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          hp[k] = bf16_pack(wv[2 * k], wv[2 * k + 1]);
-          lp[k] = bf16_pack(wv[2 * k] - __uint_as_float(hp[k] << 16), wv[2 * k + 1] - __uint_as_float(hp[k] & 0xFFFF0000u));
+          hp[k] = bf16_pack(wvv[2 * k], wvv[2 * k + 1]);
+          lp[k] = bf16_pack(wvv[2 * k] - __uint_as_float(hp[k] << 16), wvv[2 * k + 1] - __uint_as_float(hp[k] & 0xFFFF0000u));
         }
         const bf16x8 bv = u4_to_frag(vb[0], vb[1], vb[2], vb[3]);
         ov = MV::mma(u4_to_frag(hp[0], hp[1], hp[2], hp[3]), bv, ov);
         ov = MV::mma(u4_to_frag(lp[0], lp[1], lp[2], lp[3]), bv, ov);
       } else {
-        const float wv = (col < G && ab < A) ? (float)((double)(long long)wi[col * A + ab] * kFxInv) : 0.0f;
+        const float wvv = (col < G && ab < A) ? (float)((double)(long long)wi[col * A + ab] * kFxInv) : 0.0f;
         const float vv = ab < A ? Elem<DT>::f(AV[(int64_t)ab * D + d]) : 0.0f;
-        ov = MV::mma(wv, vv, ov);
+        ov = MV::mma(wvv, vv, ov);
       }
     }
   }
@@ -776,10 +836,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
 #pragma unroll
   for (int g = 0; g < G; ++g) lw[g] = wave_sum(lacc[g]);
   __syncthreads();  // w, S and the rows are no longer read: the region holds the partials
-  float* pv = reinterpret_cast<float*>(smb + L.pv);    // [kWaves][G][D]
-  float* pwv = reinterpret_cast<float*>(smb + L.pwv);  // [2][G][D]
-  float* pz = reinterpret_cast<float*>(smb + L.pz);    // [kWaves][4 BR]: (q-head, group) = 4g + grp
-  float* pl = reinterpret_cast<float*>(smb + L.pl);    // [kWaves][GP]
+  float* pv = reinterpret_cast<float*>(smb + L.pv);    // [NW][G][D]
+  float* pwv = reinterpret_cast<float*>(smb + L.pwv);  // [NPART][G][D]
+  float* pz = reinterpret_cast<float*>(smb + L.pz);    // [NW][4 BR]: (q-head, group) = 4g + grp
+  float* pl = reinterpret_cast<float*>(smb + L.pl);    // [NW][GP]
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) {
     // lane (col, kg) of column block cc holds q-head 4rb + kg, coordinate col + 16cc
@@ -795,7 +855,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int g = 4 * kg + r;
-    if (g < G) pwv[(half * G + g) * D + d] = ov[r];
+    if (g < G) pwv[(part * G + g) * D + d] = ov[r];
   }
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -805,10 +865,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_dec_stream(DecArgs a) {
   const int64_t ps = uh * a.S2 + sp;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int g = i / D, dd = i % D;
-    float val = pwv[g * D + dd] + pwv[(G + g) * D + dd];
+    float val = 0.0f;
+#pragma unroll
+    for (int pp = 0; pp < NPART; ++pp) val += pwv[(pp * G + g) * D + dd];
     float l = 0.0f;
 #pragma unroll 4
-    for (int w2 = 0; w2 < kWaves; ++w2) {
+    for (int w2 = 0; w2 < NW; ++w2) {
       val += pv[(w2 * G + g) * D + dd] + pz[w2 * 4 * BR + 4 * g + dd / 32];
       l += pl[w2 * GP + g];
     }
@@ -1077,15 +1139,27 @@ __global__ __launch_bounds__(256) void k_dec_tail_bf16(const void* q, const void
 
 constexpr size_t kLdsLimit = 158 * 1024;  // dynamic part; the static part is under 2 KB of the 160 KB
 
-template <int DT, int G>
-static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
+// Waves per workgroup: 8 (two tokens per lane) when two workgroups fit a
+// compute unit's LDS, else 16 (one token per lane, one workgroup).
+static int decode_waves(int G, int A, bool f32) {
+  return 2 * (dec_lds(G, A, f32, 8).total + 2048) <= 160 * 1024 ? 8 : 16;
+}
+
+template <int DT, int G, int NW>
+static int launch_stream_nw(const DecArgs& a, unsigned grid, hipStream_t st) {
   static size_t done = 0;
-  const size_t lds = dec_lds(G, a.A, DT == ANCHORKV_F32).total;
+  const size_t lds = dec_lds(G, a.A, DT == ANCHORKV_F32, NW).total;
   if (lds > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
-  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G>), lds, &done)) return rc;
-  k_dec_stream<DT, G><<<grid, 64 * kWaves, lds, st>>>(a);
+  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G, NW>), lds, &done)) return rc;
+  k_dec_stream<DT, G, NW><<<grid, 64 * NW, lds, st>>>(a);
   AKV_CHECK_LAUNCH("k_dec_stream");
   return 0;
+}
+
+template <int DT, int G>
+static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
+  if (decode_waves(G, a.A, DT == ANCHORKV_F32) == 8) return launch_stream_nw<DT, G, 8>(a, grid, st);
+  return launch_stream_nw<DT, G, 16>(a, grid, st);
 }
 
 template <int DT>
@@ -1146,14 +1220,14 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   return 0;
 }
 
-int decode_blocks_per_cu(int, int, bool, int64_t, int64_t, int64_t, int64_t) {
-  // one 1024-thread workgroup per compute unit (four waves per SIMD)
-  return 1;
+int decode_blocks_per_cu(int G, int A, bool f32, int64_t, int64_t, int64_t, int64_t) {
+  // 8-wave workgroups two per compute unit, 16-wave ones alone (four waves per SIMD either way)
+  return decode_waves(G, A, f32) == 8 ? 2 : 1;
 }
 
 int decode_supports(const anchorkv_plan_info& p) {
   if (p.G > kMaxG) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: decode supports q_per_kv <= %d", kMaxG);
-  if (dec_lds(p.G, p.A, p.dtype == ANCHORKV_F32).total > kLdsLimit)
+  if (dec_lds(p.G, p.A, p.dtype == ANCHORKV_F32, decode_waves(p.G, p.A, p.dtype == ANCHORKV_F32)).total > kLdsLimit)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %d anchors x %d q-heads exceed the decode kernel's LDS", p.A, p.G);
   if (p.decode_splits > 64 || p.n_chunks > 128 * p.decode_splits)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: n_tokens %d too large for the decode ranges", p.N);
@@ -1164,6 +1238,45 @@ int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, fl
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (p.dtype == ANCHORKV_BF16) return decode_impl<ANCHORKV_BF16>(p, cache, q, o, ws, st);
   return decode_impl<ANCHORKV_F32>(p, cache, q, o, ws, st);
+}
+
+// ---- allocation-free decode.  Its workspace (the per-range partials when a
+// head is split into several token ranges) lives in a file-scope device array
+// that each GPU holds until the process ends.  Host code must not pass the
+// array's name to a kernel (in host code it is a stand-in, not a device
+// address): the device address is looked up once per device with
+// hipGetSymbolAddress and kept.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(ANCHORKV_E_HIP, "anchorkv_decode_attn_noalloc: no current device (or device index >= %d)", kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(ANCHORKV_E_HIP, "anchorkv_decode_attn_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
+
+int run_decode_noalloc(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* stream) {
+  // the decode without a tail uses the workspace up to the tail partials
+  const int64_t need = decode_ws_layout(p).tail_ml;
+  if (need > (int64_t)kStaticScratchBytes)
+    return fail(ANCHORKV_E_SMALL_BUFFER,
+                "anchorkv_decode_attn_noalloc: this plan needs %lld bytes of workspace, the static workspace holds %zu",
+                (long long)need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (int rc = static_scratch(&ws)) return rc;
+  return run_decode(p, cache, q, o, ws, stream);
 }
 
 int run_decode_tail(const anchorkv_plan_info& p, const void* cache, const void* q, const void* K_tail,

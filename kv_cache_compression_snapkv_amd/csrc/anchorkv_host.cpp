@@ -319,6 +319,17 @@ int anchorkv_decode_attn(const anchorkv_plan_info* plan, const void* cache, size
   return run_decode(*plan, cache, q, o, workspace, stream);
 }
 
+int anchorkv_decode_attn_noalloc(const anchorkv_plan_info* plan, const void* cache, size_t cache_bytes, const void* q,
+                                 float* o, void* stream) {
+  if (!plan || !cache || !q || !o) return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_noalloc: null argument");
+  if ((int64_t)cache_bytes < plan->cache_bytes)
+    return fail(ANCHORKV_E_SMALL_BUFFER, "anchorkv_decode_attn_noalloc: cache %zu < %lld bytes", cache_bytes,
+                (long long)plan->cache_bytes);
+  if (((uintptr_t)cache | (uintptr_t)q | (uintptr_t)o) & 15)
+    return fail(ANCHORKV_E_ARG, "anchorkv_decode_attn_noalloc: buffers must be 16-byte aligned");
+  return run_decode_noalloc(*plan, cache, q, o, stream);
+}
+
 int anchorkv_decode_attn_tail(const anchorkv_plan_info* plan, const void* cache, size_t cache_bytes, const void* q,
                               const void* K_tail, const void* V_tail, int32_t n_tail, int32_t tail_cap, float* o,
                               void* workspace, size_t workspace_bytes, void* stream) {

@@ -96,6 +96,10 @@ int run_decode(const anchorkv_plan_info& p, const void* cache, const void* q, fl
 // compressed ones: K_tail / V_tail [U][H][tail_cap][D] in the cache dtype.
 int run_decode_tail(const anchorkv_plan_info& p, const void* cache, const void* q, const void* K_tail,
                     const void* V_tail, int n_tail, int tail_cap, float* o, void* ws, void* stream);
+// Decode with its workspace in a static device array (no allocation by the
+// caller or the library); at most kStaticScratchBytes of workspace.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+int run_decode_noalloc(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* stream);
 // Workgroups of the decode kernel that fit one compute unit (LDS and registers).
 int decode_blocks_per_cu(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C);
 // Host-only checks (no HIP calls) that the kernels can run a plan: 0, or a

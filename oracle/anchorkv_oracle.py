@@ -82,9 +82,11 @@ class Plan:
     budget_unit: int        # floor(theta * H * N * D * e) bytes per side per unit
     fixed_per_side: int     # header share + anchors + pointers + positions + chunk offsets
     n_chunks: int
+    joint: bool = False     # one residual ranking over both sides (reading R18b)
+    R_total: int = 0        # residual slots of both sides together when joint
 
 
-def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO):
+def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO, pool_kv_jointly=False):
     """Anchor and residual counts of one unit.
 
     anchor_div and rho are the method's k = S/128 and 0.7 [Pith, "Assumptions
@@ -105,6 +107,10 @@ def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO):
     Reading R4: k_s = floor(rho * k_nw) scored (float64), k_u = k_nw - k_s uniform.
     Residual slots per side per unit (pooled over heads; reading R16):
         R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed) / (D/4 + D/8))).
+    With pool_kv_jointly (reading R18b: residuals go to the best token-sides,
+    [Pith] "Referee Report", 17.3 % of token-sides) the two sides share what
+    their budgets leave after the fixed parts:
+        R_total = min(2*H*(N-A), floor(2*(floor(theta*H*N*D*e) - fixed) / (D/4 + D/8))).
     """
     if not (N >= 1 and 1 <= W <= N and D % GROUP == 0 and H >= 1):
         raise ValueError("bad shape")
@@ -124,12 +130,18 @@ def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO):
     fixed = HEADER_PER_SIDE + H * (A * D * e + 4 * N + 2 * A + 4 * C)
     rec = D // 4 + D // 8
     R = max(0, min(H * (N - A), (budget_unit - fixed) // rec))
-    return Plan(H, N, D, e, th, W, A, k_s, k_u, R, R, budget_unit, fixed, C)
+    R_total = max(0, min(2 * H * (N - A), (2 * (budget_unit - fixed)) // rec)) if pool_kv_jointly else 0
+    return Plan(H, N, D, e, th, W, A, k_s, k_u, R, R, budget_unit, fixed, C, bool(pool_kv_jointly), R_total)
 
 
 def side_bytes(p: Plan, R: int) -> int:
     """Bytes one side of one unit occupies: fixed part + R residual records."""
     return p.fixed_per_side + R * (p.D // 4 + p.D // 8)
+
+
+def unit_bytes(p: Plan, R_K: int, R_V: int) -> int:
+    """Bytes of both sides of one unit with R_K and R_V residual records."""
+    return side_bytes(p, R_K) + side_bytes(p, R_V)
 
 
 # --------------------------------------------------------------------------
@@ -380,11 +392,14 @@ class Compressed:
 
 def compress_unit(K, V, Q, G, n_obs, theta, W, e,
                   anchor_override=None, idx_override=None, flag_override=None,
-                  anchor_div=ANCHOR_DIV, rho=RHO, pool=POOL):
+                  anchor_div=ANCHOR_DIV, rho=RHO, pool=POOL, pool_kv_jointly=False):
     """K, V: [H, N, D] float64; Q: [H*G, n_obs, D] float64.
 
     anchor_div, rho, pool: the method's fixed parameters (see plan and
-    anchor_score), the pages' values by default.
+    anchor_score), the pages' values by default.  pool_kv_jointly: one
+    ranking of the key and value utilities of every (side, head, token) under
+    the combined budget, ties to K before V, then lower head, then lower
+    position (reading R18b); otherwise each side ranks its own items.
 
     The *_override arguments let a parity test continue from decisions the GPU
     took where the oracle's own decision was within the stated tie margin:
@@ -392,7 +407,7 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
     [2, H, N] bool.  The test checks the overrides before passing them.
     """
     H, N, D = K.shape
-    p = plan(H, N, D, e, theta, W, anchor_div, rho)
+    p = plan(H, N, D, e, theta, W, anchor_div, rho, pool_kv_jointly)
     A = p.A
     GQ = G * n_obs
     anchor_pos = np.zeros((H, A), dtype=np.int64)
@@ -424,8 +439,12 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
             eligible[h] = ~a["is_anchor"]
         u[0, h], u[1, h] = utilities(P, O, Qh, V[h], resid[0, h], resid[1, h], eligible[h])
     flag = np.zeros((2, H, N), dtype=bool)
-    for s, R in enumerate((p.R_K, p.R_V)):
-        flag[s] = allocate(u[s], R)
+    if p.joint:
+        # the stacked (side, head) rows rank by (-u, side, head, position)
+        flag = allocate(u.reshape(2 * H, N), p.R_total).reshape(2, H, N)
+    else:
+        for s, R in enumerate((p.R_K, p.R_V)):
+            flag[s] = allocate(u[s], R)
     if flag_override is not None:
         flag = np.asarray(flag_override, dtype=bool).copy()
     codes, sc, ze = quantize(resid)

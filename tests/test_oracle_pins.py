@@ -567,3 +567,54 @@ def test_cut_value_hand_values():
         mask = O.allocate(u, R)
         cut = O.cut_value(u, R)
         assert mask.sum() == R and np.all(u[mask] >= cut) and np.all(u[~mask & np.isfinite(u)] <= cut)
+
+
+# ---------------------------------------------------------------- joint ranking of token-sides
+def test_joint_plan_budget_and_tightness():
+    """Both sides together stay within 2 floor(theta H N D e) and no further
+    record would fit; pooling the two remainders never loses a slot."""
+    for H, N, D, e, theta, W in [(8, 8192, 128, 2, 0.1, 32), (8, 32768, 128, 2, 0.05, 32), (3, 5000, 64, 2, 0.07, 16),
+                                 (1, 512, 128, 4, 0.1, 32), (8, 65536, 128, 2, 0.02, 64)]:
+        p = O.plan(H, N, D, e, theta, W, pool_kv_jointly=True)
+        rec = D // 4 + D // 8
+        used = 2 * p.fixed_per_side + rec * p.R_total
+        assert used <= 2 * p.budget_unit
+        assert p.R_total == 2 * H * (N - p.A) or used + rec > 2 * p.budget_unit
+        assert p.R_total >= p.R_K + p.R_V and p.R_total <= p.R_K + p.R_V + 1
+
+
+def test_joint_allocation_bruteforce():
+    """With equal record costs the best R_total token-sides are the top
+    R_total utilities over both sides: brute force over every subset of a
+    tiny unit, and ties go to K before V, then head, then position."""
+    r = rng(31)
+    H, N, R = 2, 4, 5
+    u = r.random((2, H, N))
+    u[0, 1, 2] = -np.inf                     # an anchor
+    u[1, 1, 2] = -np.inf
+    flag = O.allocate(u.reshape(2 * H, N), R).reshape(2, H, N)
+    items = [(s, h, t) for s in range(2) for h in range(H) for t in range(N) if np.isfinite(u[s, h, t])]
+    best = max(itertools.combinations(items, R), key=lambda c: sum(u[i] for i in c))
+    assert sorted(zip(*np.nonzero(flag))) == sorted(best)
+    tied = np.ones((2, H, N))
+    flag = O.allocate(tied.reshape(2 * H, N), 3).reshape(2, H, N)
+    assert [tuple(x) for x in np.argwhere(flag)] == [(0, 0, 0), (0, 0, 1), (0, 0, 2)]
+    flag = O.allocate(tied.reshape(2 * H, N), 2 * H * N - 1).reshape(2, H, N)
+    assert not flag[1, H - 1, N - 1] and flag.sum() == 2 * H * N - 1
+
+
+def test_joint_allocation_follows_the_larger_utilities():
+    """Pooling across sides: with the value utilities scaled up, the value
+    side takes more than its separate share of the records, the total stays
+    the pooled slot count, and the compressed unit decodes like any other."""
+    K, V, Q = small_unit(32)
+    c = O.compress_unit(K, V * 8.0, Q, 2, 8, 0.1, 8, 2, pool_kv_jointly=True)
+    p = c.plan
+    assert p.joint and c.flag.sum() == p.R_total
+    assert c.flag[1].sum() > p.R_V
+    cut = O.cut_value(c.u.reshape(4, -1), p.R_total)
+    assert np.all(c.u[c.flag] >= cut) and np.all(c.u[~c.flag & np.isfinite(c.u)] <= cut)
+    q = bf16_exact(rng(33).standard_normal((4, 64)))
+    Kh, Vh = O.reconstruct(c)
+    o = O.decode_unit(c, q)
+    np.testing.assert_allclose(o[:2], O.attention(q[:2], Kh[0], Vh[0]), rtol=1e-12)

@@ -1,0 +1,70 @@
+"""GPU test of the allocation-free decode entry point (anchorkv_decode_attn_noalloc):
+through the C ABI it gives bit-for-bit the output of anchorkv_decode_attn with a
+caller workspace, on two calls in a row, the second with a smaller input (the
+static workspace keeps the first call's contents), including plans whose heads
+are split into several token ranges (the partials are the workspace)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+from tests.test_gpu_parity import SMALL, make_inputs, plan_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def akv():
+    import kv_cache_compression_snapkv_amd as m
+    m.lib()
+    return m
+
+
+def _run_both(akv, w):
+    K, V, Q = make_inputs(w)
+    p = plan_for(akv, w)
+    cache, ws, dws = akv.alloc(p, "cuda")
+    akv.compress(p, K, V, Q, cache, ws)
+    q = kvsynth.decode_queries(w, 1, device="cuda").contiguous()
+    o_ref = torch.full((w.units, w.kv_heads * w.q_per_kv, w.head_dim), float("nan"), device="cuda")
+    o_na = torch.full_like(o_ref, float("nan"))
+    akv.decode_attn(p, cache, q, o_ref, dws)
+    akv.decode_attn_noalloc(p, cache, q, o_na)
+    torch.cuda.synchronize()
+    return p, o_ref, o_na
+
+
+def test_noalloc_decode_matches_workspace_decode_twice(akv):
+    big = SMALL["bf16_ragged"].scaled(layers=3, n_tokens=5000)       # 3 units, heads split into ranges
+    small = SMALL["bf16_ragged"].scaled(layers=1, n_tokens=2000)     # then a smaller input
+    for w in (big, small):
+        p, o_ref, o_na = _run_both(akv, w)
+        _flush(f"[noalloc] units={w.units} N={w.n_tokens} ranges/head={p.decode_splits}")
+        assert p.decode_splits > 1
+        assert torch.isfinite(o_ref).all()
+        assert torch.equal(o_ref, o_na)
+    # f32 cache, one range per head
+    p, o_ref, o_na = _run_both(akv, SMALL["f32_tiny"])
+    assert torch.equal(o_ref, o_na)
+
+
+def test_noalloc_refuses_plans_beyond_the_static_workspace(akv):
+    # 4096 units x 8 heads x 4 q-heads of partials need far more than 16 MiB
+    p = akv.plan(4096, 8, 4, 4096, 128, 32, akv.BF16, 0.05, 32)
+    need = p.decode_workspace_bytes
+    assert need > (16 << 20)
+    cache = torch.empty(16, dtype=torch.uint8, device="cuda")
+    q = torch.empty(16, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty(16, dtype=torch.float32, device="cuda")
+    # host-side refusal before any launch (the buffers are never touched)
+    import ctypes as ct
+    rc = akv.lib().anchorkv_decode_attn_noalloc(ct.byref(p), cache.data_ptr(), int(p.cache_bytes), q.data_ptr(),
+                                                o.data_ptr(), None)
+    assert rc == -5 and b"static workspace" in akv.lib().anchorkv_last_error()
