@@ -76,7 +76,8 @@ typedef struct {
   int32_t pool;            /* width of the positional pooling of the score (odd, 1..15; 7) */
   double rho;              /* k_scored = floor(rho * k) in double precision, the rest picked uniformly ([0, 1]; 0.7) */
   int32_t group;           /* residual codec group: one fp16 scale and zero per `group` coordinates (32 only) */
-  int32_t pool_kv_jointly; /* 0: separate residual budgets for K and V (the only value supported) */
+  int32_t pool_kv_jointly; /* 0: separate residual budgets for K and V; 1: one ranking of all (side, head,
+                              token) items under both sides' budgets together (0) */
   int32_t reserved[8];     /* zero */
 } anchorkv_params;
 
@@ -92,7 +93,8 @@ typedef struct {
   int32_t A;          /* anchors per head = window + k_scored + k_uniform */
   int32_t k_scored;   /* anchors picked by the pooled observation-window score */
   int32_t k_uniform;  /* anchors picked uniformly over the remaining positions */
-  int32_t R_K, R_V;   /* residual slots per unit for keys / values */
+  int32_t R_K, R_V;   /* residual slots per unit for keys / values (separate budgets; with joint
+                       * ranking the slots of each side's budget alone, for reference) */
   int32_t n_chunks;   /* ceil(N / 1024): residual-offset chunks per head */
   /* byte accounting per side per unit (anchors D*e, pointers 4, residual D/4+D/8) */
   int64_t budget_bytes_per_side; /* floor(theta * H * N * D * e) */
@@ -100,7 +102,10 @@ typedef struct {
   double compression_ratio;      /* 2*H*N*D*e / unit_bytes */
   /* per-unit cache layout: byte offsets from the start of a unit */
   int64_t off_anchor_k, off_anchor_v; /* [H][A][D] input dtype, stored exactly */
-  int64_t off_res_k, off_res_v;       /* [R][48] residual records, sorted by (head, position) */
+  int64_t off_res_k, off_res_v;       /* [R][48] residual records, sorted by (head, position); joint:
+                                       * one section of R_total records, all key records first, then
+                                       * the value records (off_res_v == off_res_k, and the value
+                                       * chunk offsets count from the section start) */
   int64_t off_words;                  /* [H][N][2] uint32: K word, V word per token */
   int64_t off_chunk_k, off_chunk_v;   /* [H][n_chunks] int32: first record of each 1024-token chunk */
   int64_t off_positions;              /* [H][A] int32 anchor positions, ascending */
@@ -111,7 +116,9 @@ typedef struct {
   int64_t compress_workspace_bytes;
   int64_t decode_workspace_bytes;
   int32_t decode_splits;              /* token splits per (unit, head) in decode */
-  int32_t reserved[7];
+  int32_t joint;                      /* params.pool_kv_jointly */
+  int32_t R_total;                    /* joint: residual records per unit, both sides together */
+  int32_t reserved[5];
 } anchorkv_plan_info;
 
 /* Pointer word (uint32, one per token per side): bits 0-14 anchor index,

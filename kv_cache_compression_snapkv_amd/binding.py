@@ -64,7 +64,7 @@ class PlanInfo(ct.Structure):
         ("off_chunk_v", ct.c_int64), ("off_positions", ct.c_int64),
         ("unit_bytes", ct.c_int64), ("unit_stride", ct.c_int64), ("cache_bytes", ct.c_int64),
         ("compress_workspace_bytes", ct.c_int64), ("decode_workspace_bytes", ct.c_int64),
-        ("decode_splits", ct.c_int32), ("reserved", ct.c_int32 * 7),
+        ("decode_splits", ct.c_int32), ("joint", ct.c_int32), ("R_total", ct.c_int32), ("reserved", ct.c_int32 * 5),
     ]
 
     def as_dict(self):

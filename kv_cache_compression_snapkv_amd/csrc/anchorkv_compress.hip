@@ -703,20 +703,24 @@ __global__ __launch_bounds__(kToprThreads) void k_topr_threshold(const float* ut
   }
 }
 
-// One wave per group of 1024 positions of a (unit, side).
+// One wave per group of 1024 positions of a (unit, side), or of a unit's
+// joint list (joint: positions (side * H + head) * N + token, both sides ranked
+// together, the records numbered across both; the record list holds the
+// side-inclusive position).
 __global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsigned* groups, uint8_t* cache,
                                                    int64_t stride, int64_t off_words, int64_t off_ck, int64_t off_cv,
                                                    int* sel_list, int2* sel_aux, const int* aidx, const float* gam,
-                                                   int Rmax, int H, int N, int C, int R, int US) {
+                                                   int Rmax, int H, int N, int C, int R, int US, int joint) {
   const int lane = threadIdx.x & 63;
-  const int64_t M = (int64_t)H * N;
+  const int64_t M = (int64_t)(joint ? 2 * H : H) * N;
   const int64_t ngroups = (M + kToprGroup - 1) / kToprGroup;
   const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // over [US][ngroups]
   if (gw >= (int64_t)US * ngroups) return;
   const int us = (int)(gw / ngroups);
   const int64_t grp = gw - (int64_t)us * ngroups;
-  const int u = us / 2, side = us % 2;
-  int* chunk = reinterpret_cast<int*>(cache + (int64_t)u * stride + (side ? off_cv : off_ck));
+  const int u = joint ? us : us / 2, side_us = joint ? 0 : us % 2;
+  int* chunk_k = reinterpret_cast<int*>(cache + (int64_t)u * stride + off_ck);
+  int* chunk_v = reinterpret_cast<int*>(cache + (int64_t)u * stride + off_cv);
   const unsigned* tn = groups + (int64_t)US * ngroups * 2 + (int64_t)us * 2;
   const unsigned T = tn[0], need = tn[1];
   const unsigned rec_base = groups[((int64_t)us * ngroups + grp) * 2];
@@ -751,15 +755,17 @@ __global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsi
     const unsigned rec = rec_base + run_sel + __builtin_amdgcn_mbcnt_hi((unsigned)(ms >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((unsigned)ms, 0u));
     if (i < M) {
-      const unsigned iu = (unsigned)i;   // H*N < 2^31
-      const int h = (int)(iu / (unsigned)N), t = (int)(iu - (unsigned)h * (unsigned)N);
-      if ((t & (kChunk - 1)) == 0) chunk[h * C + t / kChunk] = (int)rec;
+      const unsigned iu = (unsigned)i;   // 2*H*N < 2^31
+      const int hr = (int)(iu / (unsigned)N), t = (int)(iu - (unsigned)hr * (unsigned)N);
+      const int side = joint ? (hr >= H ? 1 : 0) : side_us;
+      const int h = hr - (joint && side ? H : 0);
+      if ((t & (kChunk - 1)) == 0) (side ? chunk_v : chunk_k)[h * C + t / kChunk] = (int)rec;
       const bool taken = sel && rec < (unsigned)R;
       // the token's pointer word: anchor index, residual flag, fp16 gamma
       words[((int64_t)h * N + t) * 2 + side] =
           (uint32_t)av[k] | (taken ? 0x8000u : 0u) | ((uint32_t)f2h_sat(gv[k]) << 16);
       if (taken) {
-        sel_list[(int64_t)us * Rmax + rec] = h * N + t;
+        sel_list[(int64_t)us * Rmax + rec] = hr * N + t;
         // the record's anchor and coefficient, so that the quantiser's loads
         // do not wait on the position first
         sel_aux[(int64_t)us * Rmax + rec] = make_int2(av[k], __float_as_int(gv[k]));
@@ -778,23 +784,25 @@ __global__ __launch_bounds__(256) void k_topr_flag(const float* util, const unsi
 // word j holds coordinates j + 16c in bits 2c..2c+1, then (scale, zero) x 4.
 constexpr int kQuantPerGroup = 4;
 
+// joint: one list of R records per unit over both sides (blocks per unit, not
+// per (unit, side)); a record's side is in its position (side * H + head) * N + t.
 template <int DT>
 __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, uint8_t* cache, int64_t stride,
                                               int64_t off_ak, int64_t off_av, int64_t off_rk, int64_t off_rv,
                                               const int* sel_list, const int2* sel_aux, int Rmax, int H, int N, int A,
-                                              int R, int nblk) {
+                                              int R, int nblk, int joint) {
   using T = typename Elem<DT>::T;
   constexpr int D = kHeadDim;
   constexpr int QG = kQuantPerGroup;
   __shared__ uint8_t codes_s[16][QG][128];
   int bid = blockIdx.x;
   const int blk = bid % nblk; bid /= nblk;
-  const int side = bid % 2;
-  const int u = bid / 2;
+  const int side_b = joint ? 0 : bid % 2;
+  const int u = joint ? bid : bid / 2;
   const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
-  const int us = u * 2 + side;
+  const int us = joint ? u : u * 2 + side_b;
   const int rec0 = (blk * 16 + grp) * QG;
-  int flat[QG], a[QG];
+  int flat[QG], a[QG], sd[QG];
   float g[QG];
 #pragma unroll
   for (int k = 0; k < QG; ++k) {
@@ -803,10 +811,13 @@ __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, u
     const int2 x = act ? sel_aux[(int64_t)us * Rmax + rec0 + k] : make_int2(0, 0);
     a[k] = x.x;
     g[k] = __int_as_float(x.y);
+    sd[k] = joint ? (flat[k] >= H * N ? 1 : 0) : side_b;
+    flat[k] -= joint && sd[k] ? H * N : 0;
   }
   float r[QG][8];
 #pragma unroll
   for (int k = 0; k < QG; ++k) {
+    const int side = sd[k];
     const int h = (int)((unsigned)flat[k] / (unsigned)N), t = flat[k] - h * N;
     const T* X = reinterpret_cast<const T*>(side ? Vv : Kv) + (((int64_t)u * H + h) * N + t) * D + 8 * j;
     const T* AX = reinterpret_cast<const T*>(cache + (int64_t)u * stride + (side ? off_av : off_ak)) +
@@ -853,7 +864,8 @@ __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, u
     uint16_t wv = 0;
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) wv |= (uint16_t)(codes_s[grp][k][j + 16 * cc] << (2 * cc));
-    uint8_t* recp = cache + (int64_t)u * stride + (side ? off_rv : off_rk) + (int64_t)(rec0 + k) * kRecBytes;
+    // (joint: off_rv == off_rk and the record index counts across both sides)
+    uint8_t* recp = cache + (int64_t)u * stride + (sd[k] ? off_rv : off_rk) + (int64_t)(rec0 + k) * kRecBytes;
     reinterpret_cast<uint16_t*>(recp)[j] = wv;
     // group q's (scale, zero) lives in lanes 4q..4q+3; lane 4q writes it
     if ((j & 3) == 0) reinterpret_cast<uint32_t*>(recp + 32)[j >> 2] = (uint32_t)sb[k] | ((uint32_t)zb[k] << 16);
@@ -1059,32 +1071,35 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   if ((rc = launch_obs<DT, OBS_UTIL>(p, a, st))) return rc;
   prof_mark(st, DT == ANCHORKV_BF16 ? "util_fix" : "obs_util");
 
-  // top-R per (unit, side); R_K == R_V
-  const int R = p.R_K;
-  const int Rmax = std::max(1, std::max(p.R_K, p.R_V));
+  // top-R per (unit, side) with R_K == R_V, or per unit over both sides (joint)
+  const bool joint = p.joint != 0;
+  const int R = joint ? p.R_total : p.R_K;
+  const int Rmax = (int)std::max<int64_t>(1, sel_stride(p));
+  const int HS = joint ? 2 * H : H;           // rows of one ranking
+  const int US = joint ? U : U * 2;           // rankings
   int* sel_list = reinterpret_cast<int*>(ws + w.sel_list);
   unsigned* groups = reinterpret_cast<unsigned*>(ws + w.sel_groups);
-  if ((int64_t)H * N <= (int64_t)kToprThreads * kToprKPT)
-    k_topr_threshold<kToprKPT><<<(unsigned)(U * 2), kToprThreads, 0, st>>>(a.util, groups, H, N, R);
+  if ((int64_t)HS * N <= (int64_t)kToprThreads * kToprKPT)
+    k_topr_threshold<kToprKPT><<<(unsigned)US, kToprThreads, 0, st>>>(a.util, groups, HS, N, R);
   else
-    k_topr_threshold<0><<<(unsigned)(U * 2), kToprThreads, 0, st>>>(a.util, groups, H, N, R);
+    k_topr_threshold<0><<<(unsigned)US, kToprThreads, 0, st>>>(a.util, groups, HS, N, R);
   AKV_CHECK_LAUNCH("k_topr_threshold");
   {
-    const int64_t nw = (int64_t)U * 2 * (((int64_t)H * N + kToprGroup - 1) / kToprGroup);
+    const int64_t nw = (int64_t)US * (((int64_t)HS * N + kToprGroup - 1) / kToprGroup);
     k_topr_flag<<<(unsigned)((nw + 3) / 4), 256, 0, st>>>(a.util, groups, cache, p.unit_stride, p.off_words,
                                                           p.off_chunk_k, p.off_chunk_v, sel_list,
                                                           reinterpret_cast<int2*>(ws + w.sel_aux),
                                                           reinterpret_cast<const int*>(ws + w.aidx),
                                                           reinterpret_cast<const float*>(ws + w.gam), Rmax, H, N, C,
-                                                          R, U * 2);
+                                                          R, US, joint ? 1 : 0);
     AKV_CHECK_LAUNCH("k_topr_flag");
   }
   prof_mark(st, "topr");
   if (R > 0) {
     const int nblk = (R + 16 * kQuantPerGroup - 1) / (16 * kQuantPerGroup);
-    k_quant<DT><<<(unsigned)((int64_t)U * 2 * nblk), 256, 0, st>>>(
+    k_quant<DT><<<(unsigned)((int64_t)US * nblk), 256, 0, st>>>(
         K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_res_k, p.off_res_v, sel_list,
-        reinterpret_cast<const int2*>(ws + w.sel_aux), Rmax, H, N, A, R, nblk);
+        reinterpret_cast<const int2*>(ws + w.sel_aux), Rmax, H, N, A, R, nblk, joint ? 1 : 0);
     AKV_CHECK_LAUNCH("k_quant");
   }
   prof_mark(st, "quant");

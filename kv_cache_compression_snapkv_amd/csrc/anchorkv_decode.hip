@@ -73,6 +73,7 @@ struct DecArgs {
   float* o;          // [U][H][G][D]
   int H, N, A, C, S2, cps, R_K, R_V;
   int force_part;    // publish partials even with one range (a tail follows)
+  int joint, R_total; // one record section for both sides (keys first), R_total records
   float c;
 };
 
@@ -302,11 +303,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (threadIdx.x < 3 * GP) (&tmaxb[0][0])[threadIdx.x] = kKeyNegInf;
   if (threadIdx.x < 3) hot_any[threadIdx.x] = 0;
   if (threadIdx.x < NW * GP) (&mrun_s[0][0])[threadIdx.x] = -INFINITY;
-  for (int i = threadIdx.x; i <= nch; i += blockDim.x) {
-    const int fl = h * a.C + c0 + i;
-    const bool last = fl >= a.H * a.C;
-    offs[0][i] = last ? a.R_K : reinterpret_cast<const int*>(base + a.off_ck)[fl];
-    offs[1][i] = last ? a.R_V : reinterpret_cast<const int*>(base + a.off_cv)[fl];
+  {
+    // end of the key records and of the value records: with a joint ranking
+    // the key records end where the value records start (the value chunk
+    // offsets count from the start of the one record section)
+    const int* chk = reinterpret_cast<const int*>(base + a.off_ck);
+    const int* chv = reinterpret_cast<const int*>(base + a.off_cv);
+    const int kend = a.joint ? chv[0] : a.R_K, vend = a.joint ? a.R_total : a.R_V;
+    for (int i = threadIdx.x; i <= nch; i += blockDim.x) {
+      const int fl = h * a.C + c0 + i;
+      const bool last = fl >= a.H * a.C;
+      offs[0][i] = last ? kend : chk[fl];
+      offs[1][i] = last ? vend : chv[fl];
+    }
   }
   __syncthreads();  // qf, offs
 
@@ -1182,6 +1191,7 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   a.H = H; a.N = p.N; a.A = A; a.C = p.n_chunks; a.S2 = S2; a.cps = (p.n_chunks + S2 - 1) / S2;
   a.c = kLog2e / sqrtf((float)kHeadDim);
   a.R_K = p.R_K; a.R_V = p.R_V;
+  a.joint = p.joint; a.R_total = p.R_total;
   a.force_part = n_tail > 0 ? 1 : 0;
   const unsigned grid = (unsigned)((int64_t)U * H * S2);
   int rc = 0;

@@ -61,8 +61,8 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
   w.uflag = take(U * H * ((N + 31) / 32));
   w.anorm = take(8 * U * 2 * H * A);
   w.pooled = take(4 * U * H * N);
-  w.sel_list = take(4 * U * 2 * std::max<int64_t>(1, std::max(p.R_K, p.R_V)));
-  w.sel_aux = take(8 * U * 2 * std::max<int64_t>(1, std::max(p.R_K, p.R_V)));
+  w.sel_list = take(4 * U * 2 * std::max<int64_t>(1, sel_stride(p)));
+  w.sel_aux = take(8 * U * 2 * std::max<int64_t>(1, sel_stride(p)));
   w.sel_groups = take(8 * U * 2 * ((H * N + 1023) / 1024) + 8 * U * 2);
   w.total = off;
   return w;
@@ -94,7 +94,7 @@ static int decode_split_count(const anchorkv_plan_info& p) {
   const int64_t heads = (int64_t)p.units * p.H;
   const int64_t C = p.n_chunks;   // splits start on 1024-token chunk boundaries
   const int64_t slots = 256 * (int64_t)decode_blocks_per_cu(p.G, p.A, p.dtype == ANCHORKV_F32, p.R_K, p.R_V, p.H, C);
-  const int64_t chunk_bytes = 8 * 1024 + kRecBytes * (p.R_K + p.R_V) / std::max<int64_t>(1, p.H * C);
+  const int64_t chunk_bytes = 8 * 1024 + kRecBytes * (int64_t)records_per_unit(p) / std::max<int64_t>(1, p.H * C);
   const int64_t anchor_bytes = 2 * (int64_t)p.A * p.D * p.elem_bytes;
   int best = 1;
   int64_t best_cost = INT64_MAX;
@@ -111,8 +111,15 @@ static void layout(anchorkv_plan_info* p) {
   int64_t off = kHeaderBytes;
   p->off_anchor_k = off; off += H * A * D * e;
   p->off_anchor_v = off; off += H * A * D * e;
-  p->off_res_k = off; off += (int64_t)kRecBytes * p->R_K;
-  p->off_res_v = off; off += (int64_t)kRecBytes * p->R_V;
+  if (p->joint) {
+    // one section: key records first, then value records (the split is the data's)
+    p->off_res_k = off;
+    p->off_res_v = off;
+    off += (int64_t)kRecBytes * p->R_total;
+  } else {
+    p->off_res_k = off; off += (int64_t)kRecBytes * p->R_K;
+    p->off_res_v = off; off += (int64_t)kRecBytes * p->R_V;
+  }
   p->off_words = off; off += 8 * H * N;
   p->off_chunk_k = off; off += 4 * H * C;
   p->off_chunk_v = off; off += 4 * H * C;
@@ -139,6 +146,7 @@ void fill_header(const anchorkv_plan_info& p, UnitHeader* h) {
   h->unit_bytes = p.unit_bytes; h->unit_stride = p.unit_stride;
   h->anchor_div = p.params.anchor_div; h->pool = p.params.pool; h->group = p.params.group;
   h->pool_kv_jointly = p.params.pool_kv_jointly; h->rho = p.params.rho;
+  h->R_total = p.R_total;
 }
 
 static void params_default(anchorkv_params* q, float theta, int32_t window) {
@@ -159,9 +167,8 @@ static int check_params(const anchorkv_params& q) {
   if (q.pool < 1 || q.pool > kMaxPool || q.pool % 2 == 0)
     return fail(ANCHORKV_E_ARG, "anchorkv_plan: pool %d must be odd and in [1, %d]", q.pool, kMaxPool);
   if (q.group != kGroup) return fail(ANCHORKV_E_ARG, "anchorkv_plan: codec group %d: only %d is supported", q.group, kGroup);
-  if (q.pool_kv_jointly != 0)
-    return fail(ANCHORKV_E_ARG, "anchorkv_plan: pool_kv_jointly %d: only separate K/V budgets (0) are supported",
-                q.pool_kv_jointly);
+  if (q.pool_kv_jointly != 0 && q.pool_kv_jointly != 1)
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: pool_kv_jointly %d must be 0 or 1", q.pool_kv_jointly);
   for (int i = 0; i < (int)(sizeof(q.reserved) / sizeof(q.reserved[0])); ++i)
     if (q.reserved[i] != 0) return fail(ANCHORKV_E_ARG, "anchorkv_plan: reserved parameter fields must be zero");
   return 0;
@@ -214,6 +221,16 @@ static int plan_impl(const anchorkv_dims* d, const anchorkv_params* prm, anchork
   p.budget_bytes_per_side = budget;
   p.used_bytes_k = fixed + R * rec;
   p.used_bytes_v = fixed + R * rec;
+  if (prm->pool_kv_jointly) {
+    // both sides' remainders pooled: R_total = min(2H(N-A), floor(2(budget - fixed)/rec))
+    const int64_t Rt = std::max<int64_t>(0, std::min(2 * H * (N - A), 2 * (budget - fixed) / rec));
+    if (Rt > INT32_MAX) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: too many residual records");
+    p.joint = 1;
+    p.R_total = (int32_t)Rt;
+    // the split between the sides is the data's: each side is charged half of the records here
+    p.used_bytes_k = fixed + (Rt / 2) * rec;
+    p.used_bytes_v = fixed + (Rt - Rt / 2) * rec;
+  }
   layout(&p);
   p.compression_ratio = (double)(2 * H * N * D * e) / (double)p.unit_bytes;
   if (int rc = compress_supports(p)) return rc;
@@ -235,7 +252,8 @@ static int plan_from_header_impl(const void* header_host, int32_t units, anchork
   q.pool_kv_jointly = h.pool_kv_jointly;
   int rc = plan_impl(&d, &q, out);
   if (rc) return rc == ANCHORKV_E_ARG ? fail(ANCHORKV_E_LAYOUT, "%s: header parameters are invalid", fn) : rc;
-  if (out->A != h.A || out->R_K != h.R_K || out->R_V != h.R_V || out->unit_bytes != h.unit_bytes ||
+  if (out->A != h.A || out->R_K != h.R_K || out->R_V != h.R_V || out->R_total != h.R_total ||
+      out->unit_bytes != h.unit_bytes ||
       out->off_words != h.off_words || out->k_scored != h.k_scored || out->unit_stride != h.unit_stride)
     return fail(ANCHORKV_E_LAYOUT, "%s: header does not match its own plan", fn);
   return 0;
@@ -364,11 +382,13 @@ int anchorkv_unit_pack_host(const anchorkv_plan_info* p, const anchorkv_unit_arr
   std::memcpy(base + p->off_anchor_v, in->anchors_v, (size_t)(H * A * D * e));
   std::memcpy(base + p->off_positions, in->positions, (size_t)(4 * H * A));
   uint32_t* words = (uint32_t*)(base + p->off_words);
+  int64_t r = 0;   // record index from the section start (joint: runs on from the key records)
   for (int s = 0; s < 2; ++s) {
-    const int64_t R = s ? p->R_V : p->R_K;
     uint8_t* rec = base + (s ? p->off_res_v : p->off_res_k);
     int32_t* chunk = (int32_t*)(base + (s ? p->off_chunk_v : p->off_chunk_k));
-    int64_t r = 0;
+    if (!p->joint) r = 0;
+    const int64_t r0 = r;
+    const int64_t cap = p->joint ? p->R_total : (s ? p->R_V : p->R_K);
     for (int64_t h = 0; h < H; ++h) {
       for (int64_t t = 0; t < N; ++t) {
         const int64_t i = (s * H + h) * N + t;
@@ -377,7 +397,7 @@ int anchorkv_unit_pack_host(const anchorkv_plan_info* p, const anchorkv_unit_arr
         if (a < 0 || a >= A) return fail(ANCHORKV_E_LAYOUT, "pack: anchor index %d out of range", a);
         uint32_t w = (uint32_t)a | ((uint32_t)in->gamma16[i] << 16);
         if (in->flag[i]) {
-          if (r >= R) return fail(ANCHORKV_E_LAYOUT, "pack: more flagged tokens than R=%lld", (long long)R);
+          if (r >= cap) return fail(ANCHORKV_E_LAYOUT, "pack: more flagged tokens than %lld records", (long long)cap);
           w |= 0x8000u;
           uint16_t cw[16] = {0};
           const uint8_t* cd = in->codes + i * D;
@@ -393,9 +413,12 @@ int anchorkv_unit_pack_host(const anchorkv_plan_info* p, const anchorkv_unit_arr
         words[(h * N + t) * 2 + s] = w;
       }
     }
-    if (r != R) return fail(ANCHORKV_E_LAYOUT, "pack: %lld flagged tokens on side %d, plan has %lld", (long long)r, s,
-                            (long long)R);
+    if (!p->joint && r - r0 != cap)
+      return fail(ANCHORKV_E_LAYOUT, "pack: %lld flagged tokens on side %d, plan has %lld", (long long)(r - r0), s,
+                  (long long)cap);
   }
+  if (p->joint && r != p->R_total)
+    return fail(ANCHORKV_E_LAYOUT, "pack: %lld flagged token-sides, plan has %lld", (long long)r, (long long)p->R_total);
   return 0;
 }
 
@@ -405,17 +428,20 @@ int anchorkv_unit_unpack_host(const anchorkv_plan_info* p, const void* unit_in, 
   const uint8_t* base = (const uint8_t*)unit_in;
   UnitHeader hd;
   std::memcpy(&hd, base, sizeof(hd));
-  if (hd.magic != kMagic || hd.A != p->A || hd.N != p->N || hd.H != p->H || hd.R_K != p->R_K || hd.R_V != p->R_V)
+  if (hd.magic != kMagic || hd.A != p->A || hd.N != p->N || hd.H != p->H || hd.R_K != p->R_K || hd.R_V != p->R_V ||
+      hd.R_total != p->R_total)
     return fail(ANCHORKV_E_LAYOUT, "unpack: header does not match the plan");
   if (out->anchors_k) std::memcpy(out->anchors_k, base + p->off_anchor_k, (size_t)(H * A * D * e));
   if (out->anchors_v) std::memcpy(out->anchors_v, base + p->off_anchor_v, (size_t)(H * A * D * e));
   if (out->positions) std::memcpy(out->positions, base + p->off_positions, (size_t)(4 * H * A));
   const uint32_t* words = (const uint32_t*)(base + p->off_words);
+  int64_t r = 0;   // record index from the section start (joint: runs on from the key records)
   for (int s = 0; s < 2; ++s) {
-    const int64_t R = s ? p->R_V : p->R_K;
     const uint8_t* rec = base + (s ? p->off_res_v : p->off_res_k);
     const int32_t* chunk = (const int32_t*)(base + (s ? p->off_chunk_v : p->off_chunk_k));
-    int64_t r = 0;
+    if (!p->joint) r = 0;
+    const int64_t r0 = r;
+    const int64_t cap = p->joint ? p->R_total : (s ? p->R_V : p->R_K);
     for (int64_t h = 0; h < H; ++h) {
       for (int64_t t = 0; t < N; ++t) {
         const int64_t i = (s * H + h) * N + t;
@@ -428,7 +454,7 @@ int anchorkv_unit_unpack_host(const anchorkv_plan_info* p, const void* unit_in, 
         const bool f = (w & 0x8000u) != 0;
         if (out->flag) out->flag[i] = f ? 1 : 0;
         if (f) {
-          if (r >= R) return fail(ANCHORKV_E_LAYOUT, "unpack: more flags than records on side %d", s);
+          if (r >= cap) return fail(ANCHORKV_E_LAYOUT, "unpack: more flags than records on side %d", s);
           const uint8_t* in = rec + r * kRecBytes;
           uint16_t cw[16];
           std::memcpy(cw, in, 32);
@@ -444,8 +470,13 @@ int anchorkv_unit_unpack_host(const anchorkv_plan_info* p, const void* unit_in, 
         }
       }
     }
-    if (r != R) return fail(ANCHORKV_E_LAYOUT, "unpack: %lld flags on side %d, plan has %lld", (long long)r, s, (long long)R);
+    if (!p->joint && r - r0 != cap)
+      return fail(ANCHORKV_E_LAYOUT, "unpack: %lld flags on side %d, plan has %lld", (long long)(r - r0), s,
+                  (long long)cap);
   }
+  if (p->joint && r != p->R_total)
+    return fail(ANCHORKV_E_LAYOUT, "unpack: %lld flagged token-sides, plan has %lld", (long long)r,
+                (long long)p->R_total);
   return 0;
 }
 

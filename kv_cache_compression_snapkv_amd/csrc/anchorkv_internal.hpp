@@ -4,6 +4,7 @@
 #include <cstdint>
 #include <cstddef>
 #include <string>
+#include <algorithm>
 
 #include "anchorkv.h"
 
@@ -23,6 +24,15 @@ void set_error(const char* fmt, ...);
 int fail(int code, const char* fmt, ...);
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Residual records of one unit (both sides) and the stride of the per-unit
+// record lists of compress: per side, or both sides together when joint.
+inline int64_t records_per_unit(const anchorkv_plan_info& p) {
+  return p.joint ? (int64_t)p.R_total : (int64_t)p.R_K + p.R_V;
+}
+inline int64_t sel_stride(const anchorkv_plan_info& p) {
+  return p.joint ? (int64_t)p.R_total : (int64_t)std::max(p.R_K, p.R_V);
+}
 
 // Splits of the key range per (unit, head) in the observation-window kernels.
 int obs_splits(const anchorkv_plan_info& p);
@@ -79,7 +89,8 @@ struct UnitHeader {
   // the method's fixed parameters the unit was compressed with
   int32_t anchor_div, pool, group, pool_kv_jointly;
   double rho;
-  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8 - 4 * 4 - 8];
+  int32_t R_total, pad1;   // joint ranking: residual records of both sides
+  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8 - 4 * 4 - 8 - 8];
 };
 static_assert(sizeof(UnitHeader) == 256, "header must be 256 bytes");
 void fill_header(const anchorkv_plan_info& p, UnitHeader* h);

@@ -104,7 +104,7 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
     prm = dict(params or {})
     H, N, D = K.shape
     dtype_code = 1 if e == 2 else 2
-    p = O.plan(H, N, D, e, theta, W, **{k: v for k, v in prm.items() if k in ("anchor_div", "rho")})
+    p = O.plan(H, N, D, e, theta, W, **{k: v for k, v in prm.items() if k in ("anchor_div", "rho", "pool_kv_jointly")})
     # 1. anchors (per head), from the oracle's own pooled score
     first = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, **prm)
     if taps is not None and "score" in taps:
@@ -146,15 +146,18 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
         elig = u_o >= 0
         rep["util_max_rel_err"] = float(rel[elig].max()) if elig.any() else 0.0
     gflag = gpu["flag"].astype(bool)
-    for s, R in enumerate((p.R_K, p.R_V)):
-        cut = O.cut_value(third.u[s], R)
-        dif = gflag[s] != third.flag[s]
+    # the rankings: per side, or one over both sides (joint)
+    lists = [(third.u.reshape(2 * H, N), third.flag.reshape(2 * H, N), gflag.reshape(2 * H, N), p.R_total, "joint")] \
+        if p.joint else [(third.u[s], third.flag[s], gflag[s], R, str(s)) for s, R in enumerate((p.R_K, p.R_V))]
+    for u_l, of_l, gf_l, R, name in lists:
+        cut = O.cut_value(u_l, R)
+        dif = gf_l != of_l
         if dif.any():
-            uu = third.u[s][dif]
+            uu = u_l[dif]
             assert cut is not None and np.all(np.abs(uu - cut) <= MARGIN * abs(cut)), \
-                f"side {s}: {int(dif.sum())} residual ids differ outside the utility margin"
-        rep[f"flag_mismatch_excused_{s}"] = int(dif.sum())
-        assert gflag[s].sum() == R
+                f"ranking {name}: {int(dif.sum())} residual ids differ outside the utility margin"
+        rep[f"flag_mismatch_excused_{name}"] = int(dif.sum())
+        assert gf_l.sum() == R
     # 4. codes, scales, zeros on the GPU's residual set
     fourth = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, anchor_override=gpos, idx_override=gidx,
                              flag_override=gflag, **prm)

@@ -249,3 +249,45 @@ def _flagged_arrays(akv, p):
             elig[h * N + arr["positions"][h]] = False
         flat[np.flatnonzero(elig)[:R]] = 1
     return arr
+
+
+@pytest.mark.parametrize("H,N,theta,W,e", [(8, 8192, 0.1, 32, 2), (8, 32768, 0.05, 32, 2), (3, 5000, 0.07, 16, 2),
+                                           (1, 512, 0.1, 32, 4), (8, 65536, 0.02, 64, 2)])
+def test_joint_plan_matches_oracle(akv, H, N, theta, W, e):
+    p = akv.plan(1, H, 2, N, 128, 8, akv.BF16 if e == 2 else akv.F32, theta, W, pool_kv_jointly=1)
+    o = O.plan(H, N, 128, e, theta, W, pool_kv_jointly=True)
+    assert p.joint == 1 and (p.A, p.R_K, p.R_V, p.R_total) == (o.A, o.R_K, o.R_V, o.R_total)
+    # one record section, both sides within twice the per-side budget
+    assert p.off_res_v == p.off_res_k
+    assert p.unit_bytes == p.used_bytes_k + p.used_bytes_v <= 2 * p.budget_bytes_per_side
+    assert p.unit_bytes == 2 * o.fixed_per_side + 48 * o.R_total
+
+
+def test_joint_pack_unpack_roundtrip(akv):
+    """A joint cache: the key records first, then the value records, in one
+    section; chunk offsets of the value side count from the section start."""
+    r = np.random.default_rng(5)
+    H, G, N, D, n_obs, W = 2, 2, 1500, 128, 8, 8
+    K = r.standard_normal((H, N, D)).astype(np.float32).astype(np.float64)
+    V = (4.0 * r.standard_normal((H, N, D))).astype(np.float32).astype(np.float64)
+    Q = r.standard_normal((H * G, n_obs, D)).astype(np.float32).astype(np.float64)
+    c = O.compress_unit(K, V, Q, G, n_obs, 0.1, W, 4, pool_kv_jointly=True)
+    p = akv.plan(1, H, G, N, D, n_obs, akv.F32, 0.1, W, pool_kv_jointly=1)
+    nk = int(c.flag[0].sum())
+    assert c.flag.sum() == p.R_total and nk != p.R_total // 2
+    from tests.parity import oracle_arrays
+    arr = oracle_arrays(c, 2)
+    blob = akv.pack_unit(p, arr)
+    back = akv.unpack_unit(p, blob)
+    for k in ("idx", "gamma16", "flag"):
+        np.testing.assert_array_equal(back[k], arr[k])
+    fl = arr["flag"].astype(bool)
+    np.testing.assert_array_equal(back["codes"][fl], arr["codes"][fl])
+    chv = np.frombuffer(blob[p.off_chunk_v:p.off_chunk_v + 4], np.int32)[0]
+    assert chv == nk
+    assert akv.plan_from_header(blob[:256], 1).as_dict() == p.as_dict()
+    bad = dict(arr)
+    bad["flag"] = arr["flag"].copy()
+    bad["flag"][1, 0, 5] ^= 1
+    with pytest.raises(akv.AnchorKVError):
+        akv.pack_unit(p, bad)

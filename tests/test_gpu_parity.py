@@ -51,9 +51,15 @@ SMALL = {
     # 5, half the non-window anchors scored, k = N/64
     "bf16_params": W_["llama8b_32k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=4000, n_dirs=32),
     "f32_params": W_["tiny_f32"].scaled(n_tokens=1200),
+    # one ranking of key and value token-sides under both budgets together
+    "bf16_joint": W_["llama8b_32k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=3000, n_dirs=32),
+    "bf16_joint_stress": W_["stress_64k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, theta=0.06),
+    "f32_joint": W_["tiny_f32"],
 }
 # non-default method parameters of some cases (anchorkv_params)
-PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40)}
+PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40),
+          "bf16_joint": dict(pool_kv_jointly=1), "bf16_joint_stress": dict(pool_kv_jointly=1),
+          "f32_joint": dict(pool_kv_jointly=1)}
 
 
 def _flush(msg):
@@ -115,20 +121,21 @@ def test_compress_decode_parity(akv, name):
         _flush(f"[parity] {name} unit {u}: {rep}")
 
 
-@pytest.mark.parametrize("name", ["bf16_ragged", "f32_tiny", "bf16_stress_short"])
+@pytest.mark.parametrize("name", ["bf16_ragged", "f32_tiny", "bf16_stress_short", "bf16_joint"])
 def test_decode_on_host_packed_oracle_cache(akv, name):
     """Decode alone: the oracle's compressed representation, packed on the
     host into the cache layout, decoded on the GPU."""
     w = SMALL[name]
+    prm = PARAMS.get(name, {})
     _flush(f"[decode-packed] {name}")
     K, V, Q = make_inputs(w)
-    p = plan_for(akv, w)
+    p = plan_for(akv, w, prm)
     K64, V64, Q64 = (kvsynth.to_f64(t) for t in (K, V, Q))
     dtype_code = 1 if w.dtype == "bf16" else 2
     cache_h = np.zeros(p.cache_bytes, dtype=np.uint8)
     comps = []
     for u in range(w.units):
-        c = O.compress_unit(K64[u], V64[u], Q64[u], w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes)
+        c = O.compress_unit(K64[u], V64[u], Q64[u], w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes, **prm)
         comps.append(c)
         unit = akv.pack_unit(p, oracle_arrays(c, dtype_code))
         cache_h[u * p.unit_stride: u * p.unit_stride + p.unit_bytes] = np.frombuffer(unit, np.uint8)
