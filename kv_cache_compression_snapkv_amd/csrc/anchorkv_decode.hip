@@ -440,19 +440,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // tile's chunk offset plus the counts of the waves before it.
   auto run_of = [&](int it, int par, int& kb, int& nk, int& vb, int& nv) {
     const int ic = min(it, nch);
-    const int mine = cnt[par][wave];
+    // uniform values (every lane reads the same word): the record buffer
+    // descriptors built from them then live in scalar registers
+    const int mine = __builtin_amdgcn_readfirstlane(cnt[par][wave]);
     const int pre = __builtin_amdgcn_readfirstlane(row_sum_i32(lane < wave ? cnt[par][lane & (NW - 1)] : 0));
     kb = __builtin_amdgcn_readfirstlane(offs[0][ic]) + (pre & 0xFFFF);
     vb = __builtin_amdgcn_readfirstlane(offs[1][ic]) + (pre >> 16);
     nk = it < nch ? (mine & 0xFFFF) : 0;
     nv = it < nch ? (mine >> 16) : 0;
   };
+  // bytes of a batch of at most 16 records; the clamp has no scalar
+  // instruction, so the result is read back from the first lane to keep the
+  // buffer descriptor in scalar registers (a descriptor in vector registers
+  // turns every load into a loop over its distinct values)
+  auto run_bytes = [](int n) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(min(max(n, 0), 16) * kRecBytes);
+  };
   // key batch: lane (col, kg) holds bytes 8kg..8kg+7 of record col and the
   // (scale, zero) word of group col & 3 of records 4kg + r
   uint2 kx;
   uint32_t ksz[4];
   auto load_keys = [&](int kb, int nk, uint2& x, uint32_t (&sz)[4]) {
-    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)kb * kRecBytes, (uint32_t)min(max(nk, 0), 16) * kRecBytes);
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)kb * kRecBytes, run_bytes(nk));
     const auto xx = __builtin_amdgcn_raw_buffer_load_b64(r, col * kRecBytes + 8 * kg, 0, 0);
     x = make_uint2(xx[0], xx[1]);
 #pragma unroll
@@ -463,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // (scale, zero) word of group col & 3 of the same records
   uint32_t vpr[2], vsz[4];
   auto load_values = [&](int vb, int nv, uint32_t (&pr)[2], uint32_t (&sz)[4]) {
-    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)vb * kRecBytes, (uint32_t)min(max(nv, 0), 16) * kRecBytes);
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)vb * kRecBytes, run_bytes(nv));
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
       const int r0 = 4 * kg + 2 * e2;
