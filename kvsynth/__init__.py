@@ -99,7 +99,7 @@ def _gen(device, *parts: int) -> torch.Generator:
     return g
 
 
-def _keys(w: Workload, g: torch.Generator, device) -> torch.Tensor:
+def _keys(w: Workload, g: torch.Generator, device, iso_out: Optional[list] = None) -> torch.Tensor:
     H, N, D = w.kv_heads, w.n_tokens, w.head_dim
     dirs = torch.randn(H, w.n_dirs, D, generator=g, device=device)
     dirs = dirs / dirs.norm(dim=-1, keepdim=True)
@@ -119,6 +119,8 @@ def _keys(w: Workload, g: torch.Generator, device) -> torch.Tensor:
         ziso = torch.randn(H, N, D, generator=g, device=device)
         ziso = ziso / ziso.norm(dim=-1, keepdim=True)
         k = torch.where(iso.unsqueeze(-1), ziso, k * scale.unsqueeze(1))
+        if iso_out is not None:
+            iso_out.append(iso)
     return k * s.unsqueeze(-1)
 
 
@@ -140,6 +142,33 @@ def unit_inputs(w: Workload, seq: int, layer: int, device="cpu"):
     Q = torch.randn(w.kv_heads * w.q_per_kv, w.n_obs, w.head_dim, generator=g, device=device)
     dt = w.torch_dtype
     return K.to(dt), V.to(dt), Q.to(dt)
+
+
+def stress_isotropic_check(w: Workload, seq: int = 0, layer: int = 0, device="cpu", stride: int = 128):
+    """Self-check of the adversarial workload's structure: the isotropic 5 %
+    of the keys must be the worst-covered tokens.  For each head, every
+    token's largest cosine to a reference dictionary (every stride-th token,
+    the token itself excluded) is computed; returns, per head, the fraction of
+    the isotropic tokens that fall among the |iso| lowest such cosines, and
+    the largest isotropic / smallest clustered max-cosine."""
+    assert w.stress
+    g = _gen(device, SEED_TAG, w.index, seq, layer)
+    iso_l: list = []
+    K = _keys(w, g, device, iso_out=iso_l).to(w.torch_dtype).to(torch.float64)
+    iso = iso_l[0]
+    out = []
+    for h in range(w.kv_heads):
+        x = K[h] / K[h].norm(dim=-1, keepdim=True)
+        ref = torch.arange(0, w.n_tokens, stride, device=device)
+        c = x @ x[ref].T
+        c[ref, torch.arange(ref.numel(), device=device)] = -2.0    # not the token itself
+        mc = c.max(dim=1).values
+        m = iso[h]
+        n = int(m.sum())
+        low = torch.argsort(mc)[:n]
+        frac = float(m[low].float().mean()) if n else 1.0
+        out.append(dict(iso=n, frac_lowest=frac, iso_max=float(mc[m].max()), clustered_min=float(mc[~m].min())))
+    return out
 
 
 def decode_queries(w: Workload, step: int, units: Optional[int] = None, device="cpu") -> torch.Tensor:

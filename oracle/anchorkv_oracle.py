@@ -19,10 +19,12 @@ Where the pages are silent the reading taken is stated at the step (readings
 R1..R20, listed together in the design notes of the repository).
 
 Implementation contract (not on the pages, fixed for this implementation): the
-residual codec is 2-bit group-affine with one fp16 scale and one fp16 zero per
-32 contiguous coordinates; anchors cost D*e bytes, pointers 4 bytes (2-byte
-index + 2-byte fp16 coefficient), residuals D/4 + D/8 bytes; decode logits are
-gamma * <q, k_anchor> + <q, r~> with no RoPE.
+default residual codec is 2-bit group-affine with one fp16 scale and one fp16
+zero per 32 contiguous coordinates (residual records of D/4 + D/8 bytes); the
+paper's codec (randomized Hadamard rotation + 4-level Lloyd-Max, one fp16
+scale per residual, records of D/4 + 4 bytes) is the alternative; anchors cost
+D*e bytes, pointers 4 bytes (2-byte index + 2-byte fp16 coefficient); decode
+logits are gamma * <q, k_anchor> + <q, r~> with no RoPE.
 
 Parity status: every function here is pinned by tests under tests/ (library
 routines, closed forms, brute force, finite differences, invariants), except
@@ -45,6 +47,9 @@ HEADER_PER_SIDE = 128
 CHUNK = 1024        # tokens per residual-offset chunk
 MAX_ANCHORS = 32767  # anchor index is 15 bits (bit 15 flags a residual)
 FP16_MAX = 65504.0
+CODEC_AFFINE = 0    # 2-bit group-affine residual codec (implementation contract)
+CODEC_HLM = 1       # the paper's codec: randomized Hadamard rotation + 4-level Lloyd-Max
+SIGN_SEED = 0x416E63686F724B56   # seed of the default rotation signs (reading R22)
 
 
 # --------------------------------------------------------------------------
@@ -84,9 +89,18 @@ class Plan:
     n_chunks: int
     joint: bool = False     # one residual ranking over both sides (reading R18b)
     R_total: int = 0        # residual slots of both sides together when joint
+    codec: int = CODEC_AFFINE
 
 
-def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO, pool_kv_jointly=False):
+def rec_bytes(D, codec=CODEC_AFFINE):
+    """Bytes of one residual record: D/4 bytes of 2-bit codes plus, for the
+    group-affine codec, an fp16 scale and zero per 32 coordinates (D/8 bytes),
+    for the Hadamard / Lloyd-Max codec one fp16 scale and 2 bytes of padding
+    (reading R22)."""
+    return D // 4 + (D // 8 if codec == CODEC_AFFINE else 4)
+
+
+def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO, pool_kv_jointly=False, codec=CODEC_AFFINE):
     """Anchor and residual counts of one unit.
 
     anchor_div and rho are the method's k = S/128 and 0.7 [Pith, "Assumptions
@@ -106,11 +120,12 @@ def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO, pool_kv_jointly=F
     Reading R3: the window is not part of k: A = W + k_nw.
     Reading R4: k_s = floor(rho * k_nw) scored (float64), k_u = k_nw - k_s uniform.
     Residual slots per side per unit (pooled over heads; reading R16):
-        R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed) / (D/4 + D/8))).
+        R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed) / rec)),
+    rec = rec_bytes(D, codec) (D/4 + D/8 for the group-affine codec).
     With pool_kv_jointly (reading R18b: residuals go to the best token-sides,
     [Pith] "Referee Report", 17.3 % of token-sides) the two sides share what
     their budgets leave after the fixed parts:
-        R_total = min(2*H*(N-A), floor(2*(floor(theta*H*N*D*e) - fixed) / (D/4 + D/8))).
+        R_total = min(2*H*(N-A), floor(2*(floor(theta*H*N*D*e) - fixed) / rec)).
     """
     if not (N >= 1 and 1 <= W <= N and D % GROUP == 0 and H >= 1):
         raise ValueError("bad shape")
@@ -128,15 +143,17 @@ def plan(H, N, D, e, theta, W, anchor_div=ANCHOR_DIV, rho=RHO, pool_kv_jointly=F
         raise ValueError("too many anchors for a 15-bit index")
     budget_unit = math.floor(th * float(H * N * D * e))
     fixed = HEADER_PER_SIDE + H * (A * D * e + 4 * N + 2 * A + 4 * C)
-    rec = D // 4 + D // 8
+    if codec not in (CODEC_AFFINE, CODEC_HLM) or (codec == CODEC_HLM and D & (D - 1)):
+        raise ValueError("bad codec")
+    rec = rec_bytes(D, codec)
     R = max(0, min(H * (N - A), (budget_unit - fixed) // rec))
     R_total = max(0, min(2 * H * (N - A), (2 * (budget_unit - fixed)) // rec)) if pool_kv_jointly else 0
-    return Plan(H, N, D, e, th, W, A, k_s, k_u, R, R, budget_unit, fixed, C, bool(pool_kv_jointly), R_total)
+    return Plan(H, N, D, e, th, W, A, k_s, k_u, R, R, budget_unit, fixed, C, bool(pool_kv_jointly), R_total, codec)
 
 
 def side_bytes(p: Plan, R: int) -> int:
     """Bytes one side of one unit occupies: fixed part + R residual records."""
-    return p.fixed_per_side + R * (p.D // 4 + p.D // 8)
+    return p.fixed_per_side + R * rec_bytes(p.D, p.codec)
 
 
 def unit_bytes(p: Plan, R_K: int, R_V: int) -> int:
@@ -365,6 +382,119 @@ def code_margin(r, scale, zero):
 
 
 # --------------------------------------------------------------------------
+# Step 10, the paper's codec [Pith, "Referee Report" Summary (2-bit
+# Hadamard-rotated, Lloyd-Max-quantised residuals) and "Assumptions & free
+# parameters" (four-level Lloyd-Max codebook for a unit Gaussian, randomized
+# Hadamard rotation with a shared fixed seed; after the rotation a residual's
+# coordinates are modelled as Gaussian with variance ||r||^2 / D)].
+# Reading R22 for the details: rotation y = (1/sqrt(D)) H_D diag(s) r with the
+# Sylvester Hadamard matrix and a fixed sign vector s; scale sigma =
+# fp16(||r|| / sqrt(D)); code of coordinate i from u_i = y_i / sigma against
+# the Lloyd-Max thresholds -t, 0, t (a value on a threshold takes the upper
+# cell); reconstruction r~ = diag(s) (1/sqrt(D)) H_D (sigma * level[code]).
+# --------------------------------------------------------------------------
+def splitmix64(state):
+    """One step of the SplitMix64 generator (Steele, Lea and Flood, "Fast
+    splittable pseudorandom number generators", 2014): returns (new state,
+    output), all arithmetic modulo 2^64."""
+    M = (1 << 64) - 1
+    state = (state + 0x9E3779B97F4A7C15) & M
+    z = state
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M
+    return state, z ^ (z >> 31)
+
+
+def default_sign_words(seed=SIGN_SEED):
+    """The default rotation signs as four 32-bit words (bit i % 32 of word
+    i // 32 set means s_i = -1): the first two SplitMix64 outputs from the
+    seed, low word first."""
+    st, a = splitmix64(seed)
+    st, b = splitmix64(st)
+    return [a & 0xFFFFFFFF, a >> 32, b & 0xFFFFFFFF, b >> 32]
+
+
+def signs_from_words(words, D):
+    """s [D] in {+1, -1} from the sign words."""
+    bits = np.array([(words[i // 32] >> (i % 32)) & 1 for i in range(D)])
+    return np.where(bits == 1, -1.0, 1.0)
+
+
+def hadamard_matrix(D):
+    """Orthonormal Sylvester-Hadamard matrix (1/sqrt(D)) H_D with
+    H_D[i, j] = (-1)^popcount(i & j); D a power of two."""
+    i = np.arange(D)
+    par = np.array([[bin(a & b).count("1") & 1 for b in i] for a in i])
+    return np.where(par == 1, -1.0, 1.0) / math.sqrt(D)
+
+
+def _phi(x):
+    return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def _Phi(x):
+    return 0.5 * math.erfc(-x / math.sqrt(2.0))
+
+
+def lloyd_max_gaussian4(iters=200):
+    """Four-level Lloyd-Max quantiser of a unit Gaussian (Lloyd 1982, Max
+    1960), by Lloyd's iteration on the symmetric cells (-inf, -t), [-t, 0),
+    [0, t), [t, inf): each level is the conditional mean of its cell and the
+    inner threshold t the midpoint of the two positive levels.  Returns
+    (levels [-l2, -l1, l1, l2], t)."""
+    l1, l2 = 0.5, 1.5
+    for _ in range(iters):
+        t = 0.5 * (l1 + l2)
+        l1 = (_phi(0.0) - _phi(t)) / (_Phi(t) - 0.5)     # E[X | 0 <= X < t]
+        l2 = _phi(t) / (1.0 - _Phi(t))                     # E[X | X >= t]
+    t = 0.5 * (l1 + l2)
+    return np.array([-l2, -l1, l1, l2]), t
+
+
+def rotate(r, words):
+    """y = (1/sqrt(D)) H_D diag(s) r over the last axis."""
+    D = r.shape[-1]
+    return (r * signs_from_words(words, D)) @ hadamard_matrix(D).T
+
+
+def unrotate(y, words):
+    """r = diag(s) (1/sqrt(D)) H_D y (the inverse of rotate: the orthonormal
+    Sylvester matrix is symmetric and its own inverse)."""
+    D = y.shape[-1]
+    return (y @ hadamard_matrix(D).T) * signs_from_words(words, D)
+
+
+def quantize_hlm(r, words):
+    """r: [..., D].  Returns (codes uint8 [..., D], sigma [...]) with sigma the
+    float64 value of fp16(||r|| / sqrt(D)); codes 0 where sigma = 0."""
+    D = r.shape[-1]
+    lv, t = lloyd_max_gaussian4()
+    sigma = fp16_rne(np.linalg.norm(r, axis=-1) / math.sqrt(D))
+    y = rotate(r, words)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        u = y / np.where(sigma > 0, sigma, 1.0)[..., None]
+    codes = (u >= -t).astype(np.uint8) + (u >= 0.0) + (u >= t)
+    codes = np.where((sigma > 0)[..., None], codes, 0)
+    return codes.astype(np.uint8), sigma
+
+
+def dequantize_hlm(codes, sigma, words):
+    lv, _ = lloyd_max_gaussian4()
+    return unrotate(sigma[..., None] * lv[codes.astype(np.int64)], words)
+
+
+def hlm_code_margin(r, sigma, words):
+    """Distance of u = y / sigma from the nearest threshold (-t, 0, t); +inf
+    where sigma = 0.  Used to skip boundary cases in parity checks."""
+    _, t = lloyd_max_gaussian4()
+    y = rotate(r, words)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        u = y / np.where(sigma > 0, sigma, 1.0)[..., None]
+    m = np.minimum(np.minimum(np.abs(u + t), np.abs(u)), np.abs(u - t))
+    return np.where((sigma > 0)[..., None], m, np.inf)
+
+
+# --------------------------------------------------------------------------
 # The whole compression pass of one unit [Pith, "What carries the argument";
 # Velox, "Adaptation notes" (one-shot compression at the end of prefill)].
 # --------------------------------------------------------------------------
@@ -388,11 +518,15 @@ class Compressed:
     O: np.ndarray = None          # [H, GQ, D]
     u: np.ndarray = None          # [2, H, N] utilities (-inf ineligible)
     margin: np.ndarray = None     # [2, H, N] top-2 cosine margin
+    codec: int = CODEC_AFFINE
+    sigma: np.ndarray = None      # [2, H, N] fp16 scale of the Hadamard / Lloyd-Max codec
+    sign_words: tuple = None      # rotation signs of that codec
 
 
 def compress_unit(K, V, Q, G, n_obs, theta, W, e,
                   anchor_override=None, idx_override=None, flag_override=None,
-                  anchor_div=ANCHOR_DIV, rho=RHO, pool=POOL, pool_kv_jointly=False):
+                  anchor_div=ANCHOR_DIV, rho=RHO, pool=POOL, pool_kv_jointly=False,
+                  codec=CODEC_AFFINE, sign_words=None):
     """K, V: [H, N, D] float64; Q: [H*G, n_obs, D] float64.
 
     anchor_div, rho, pool: the method's fixed parameters (see plan and
@@ -400,6 +534,9 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
     ranking of the key and value utilities of every (side, head, token) under
     the combined budget, ties to K before V, then lower head, then lower
     position (reading R18b); otherwise each side ranks its own items.
+    codec: CODEC_AFFINE (group-affine, scale and zero per 32 coordinates) or
+    CODEC_HLM (randomized Hadamard rotation with the signs sign_words, the
+    default ones when None, and the Lloyd-Max codebook; reading R22).
 
     The *_override arguments let a parity test continue from decisions the GPU
     took where the oracle's own decision was within the stated tie margin:
@@ -407,7 +544,7 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
     [2, H, N] bool.  The test checks the overrides before passing them.
     """
     H, N, D = K.shape
-    p = plan(H, N, D, e, theta, W, anchor_div, rho, pool_kv_jointly)
+    p = plan(H, N, D, e, theta, W, anchor_div, rho, pool_kv_jointly, codec)
     A = p.A
     GQ = G * n_obs
     anchor_pos = np.zeros((H, A), dtype=np.int64)
@@ -447,21 +584,33 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
             flag[s] = allocate(u[s], R)
     if flag_override is not None:
         flag = np.asarray(flag_override, dtype=bool).copy()
-    codes, sc, ze = quantize(resid)
+    sigma = None
+    words = None
+    if codec == CODEC_HLM:
+        words = tuple(default_sign_words() if sign_words is None else sign_words)
+        codes, sigma = quantize_hlm(resid, words)
+        sigma = np.where(flag, sigma, 0.0)
+        sc = np.zeros((2, H, N, D // GROUP))
+        ze = np.zeros((2, H, N, D // GROUP))
+    else:
+        codes, sc, ze = quantize(resid)
     codes = np.where(flag[..., None], codes, 0).astype(np.uint8)
     anchors = np.stack([K[np.arange(H)[:, None], anchor_pos], V[np.arange(H)[:, None], anchor_pos]])
     return Compressed(p, G, anchor_pos, idx, gamma, gamma16, resid, flag, codes, sc, ze,
-                      anchors, score, pooled, Ps, Os, u, margin)
+                      anchors, score, pooled, Ps, Os, u, margin, codec, sigma, words)
 
 
 def reconstruct(c: Compressed):
     """K^, V^ [H, N, D]: fp16(gamma) * x_a + [flag] * dequantised residual
-    [Pith, "What carries the argument"]."""
+    [Pith, "What carries the argument"], with the cache's codec."""
     out = []
     H = c.anchor_pos.shape[0]
     for s in range(2):
         xa = c.anchors[s][np.arange(H)[:, None], c.idx[s]]
-        rt = dequantize(c.codes[s], c.scale[s], c.zero[s])
+        if c.codec == CODEC_HLM:
+            rt = dequantize_hlm(c.codes[s], c.sigma[s], c.sign_words)
+        else:
+            rt = dequantize(c.codes[s], c.scale[s], c.zero[s])
         out.append(c.gamma16[s][..., None] * xa + np.where(c.flag[s][..., None], rt, 0.0))
     return out[0], out[1]
 

@@ -618,3 +618,213 @@ def test_joint_allocation_follows_the_larger_utilities():
     Kh, Vh = O.reconstruct(c)
     o = O.decode_unit(c, q)
     np.testing.assert_allclose(o[:2], O.attention(q[:2], Kh[0], Vh[0]), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- the paper's codec (Hadamard + Lloyd-Max)
+def test_splitmix64_published_vector():
+    """SplitMix64 from seed 1234567 gives 6457827717110365317 then
+    3203168211198807973 (the generator's published reference outputs); the
+    default sign words are its first two outputs from the fixed seed."""
+    st, a = O.splitmix64(1234567)
+    st, b = O.splitmix64(st)
+    assert (a, b) == (6457827717110365317, 3203168211198807973)
+    st, x = O.splitmix64(O.SIGN_SEED)
+    st, y = O.splitmix64(st)
+    assert O.default_sign_words() == [x & 0xFFFFFFFF, x >> 32, y & 0xFFFFFFFF, y >> 32]
+    s = O.signs_from_words(O.default_sign_words(), 128)
+    assert set(np.unique(s)) == {-1.0, 1.0} and 40 < (s < 0).sum() < 88
+
+
+@pytest.mark.parametrize("D", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_hadamard_matches_library(D):
+    """The orthonormal Sylvester matrix equals scipy's Hadamard matrix / sqrt(D),
+    is symmetric and orthogonal."""
+    from scipy.linalg import hadamard
+    Hm = O.hadamard_matrix(D)
+    np.testing.assert_array_equal(Hm * math.sqrt(D), hadamard(D).astype(np.float64))
+    np.testing.assert_allclose(Hm @ Hm.T, np.eye(D), atol=1e-14)
+    np.testing.assert_array_equal(Hm, Hm.T)
+
+
+def test_rotation_definition_and_inverse():
+    """rotate = H diag(s) r with the library Hadamard matrix, norm preserving,
+    and unrotate inverts it; an all-zero sign word is the plain transform."""
+    from scipy.linalg import hadamard
+    r = rng(31).standard_normal((5, 128))
+    words = O.default_sign_words()
+    s = np.array([-1.0 if (words[i // 32] >> (i % 32)) & 1 else 1.0 for i in range(128)])
+    ref = np.array([hadamard(128) @ (s * x) for x in r]) / math.sqrt(128)
+    y = O.rotate(r, words)
+    np.testing.assert_allclose(y, ref, atol=1e-13)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(r, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(O.unrotate(y, words), r, atol=1e-13)
+    np.testing.assert_allclose(O.rotate(r, [0, 0, 0, 0]), r @ hadamard(128).T / math.sqrt(128), atol=1e-13)
+
+
+def test_lloyd_max_conditions_by_quadrature():
+    """The four-level codebook satisfies the Lloyd-Max conditions, checked by
+    numerical integration of the Gaussian (not the closed forms the oracle
+    iterates): each level is its cell's conditional mean and the threshold the
+    midpoint; it matches Max's published values (0.4528, 1.510, 0.9816) and
+    its mean squared error is Max's 0.1175."""
+    from scipy import integrate
+    lv, t = O.lloyd_max_gaussian4()
+    pdf = lambda x: math.exp(-x * x / 2) / math.sqrt(2 * math.pi)
+    cells = [(-np.inf, -t), (-t, 0.0), (0.0, t), (t, np.inf)]
+    for k, (a, b) in enumerate(cells):
+        m0 = integrate.quad(pdf, a, b, epsabs=1e-14, epsrel=1e-13)[0]
+        m1 = integrate.quad(lambda x: x * pdf(x), a, b, epsabs=1e-14, epsrel=1e-13)[0]
+        assert abs(m1 / m0 - lv[k]) < 1e-10
+    assert abs(t - 0.5 * (lv[2] + lv[3])) < 1e-15 and lv[1] == -lv[2] and lv[0] == -lv[3]
+    assert abs(lv[2] - 0.4528) < 5e-5 and abs(lv[3] - 1.510) < 5e-4 and abs(t - 0.9816) < 5e-5
+    mse = sum(integrate.quad(lambda x: (x - lv[k]) ** 2 * pdf(x), a, b, epsabs=1e-14)[0]
+              for k, (a, b) in enumerate(cells))
+    assert abs(mse - 0.1175) < 5e-5
+
+
+def test_lloyd_max_is_the_mse_minimum():
+    """Brute force: no symmetric four-level quantiser on a grid of (t, l1, l2)
+    around the codebook has a smaller Gaussian MSE."""
+    from scipy.stats import norm
+    lv, t0 = O.lloyd_max_gaussian4()
+
+    def mse(t, l1, l2):
+        # 2 * [int_0^t (x - l1)^2 phi + int_t^inf (x - l2)^2 phi], closed form via scipy.stats moments
+        def part(a, b, c):
+            m0 = norm.cdf(b) - norm.cdf(a)
+            m1 = norm.pdf(a) - norm.pdf(b)
+            m2 = m0 + (a * norm.pdf(a) if np.isfinite(a) else 0) - (b * norm.pdf(b) if np.isfinite(b) else 0)
+            return m2 - 2 * c * m1 + c * c * m0
+        return 2 * (part(0, t, l1) + part(t, np.inf, l2))
+    best = mse(t0, lv[2], lv[3])
+    for dt, d1, d2 in itertools.product(np.linspace(-0.01, 0.01, 5), repeat=3):
+        assert mse(t0 + dt, lv[2] + d1, lv[3] + d2) >= best - 1e-15
+
+
+def test_hlm_codes_are_nearest_level_bruteforce():
+    """Each code is the level nearest to y / sigma (the Lloyd-Max cells are the
+    nearest-level cells); sigma = fp16(||r|| / sqrt(D)); a zero residual gets
+    scale 0 and codes 0."""
+    r = rng(32).standard_normal((40, 128)) * rng(33).uniform(0.01, 3.0, (40, 1))
+    r[3] = 0.0
+    words = O.default_sign_words()
+    codes, sigma = O.quantize_hlm(r, words)
+    lv, _ = O.lloyd_max_gaussian4()
+    y = O.rotate(r, words)
+    for i in range(r.shape[0]):
+        assert sigma[i] == O.fp16_rne(np.linalg.norm(r[i]) / math.sqrt(128))
+        if sigma[i] == 0:
+            assert not codes[i].any()
+            continue
+        for d in range(128):
+            u = y[i, d] / sigma[i]
+            assert codes[i, d] == int(np.argmin(np.abs(u - lv)))
+    assert sigma[3] == 0
+
+
+def test_hlm_dequantize_elementwise():
+    """r~_i = s_i * sum_j H[i, j] sigma level[c_j] / sqrt(D), by explicit loops
+    over a small D with scipy's Hadamard matrix."""
+    from scipy.linalg import hadamard
+    D = 16
+    words = [0b1010011100011101, 0, 0, 0]
+    codes = rng(34).integers(0, 4, (3, D)).astype(np.uint8)
+    sigma = np.array([0.5, 1.25, 0.0])
+    lv, _ = O.lloyd_max_gaussian4()
+    Hd = hadamard(D)
+    out = O.dequantize_hlm(codes, sigma, words)
+    for n in range(3):
+        for i in range(D):
+            s_i = -1.0 if (words[0] >> i) & 1 else 1.0
+            acc = sum(Hd[i, j] * sigma[n] * lv[codes[n, j]] for j in range(D))
+            assert abs(out[n, i] - s_i * acc / math.sqrt(D)) < 1e-14
+
+
+def test_hlm_distortion_matches_the_gaussian_model():
+    """For Gaussian residuals the relative squared error of the codec is the
+    Lloyd-Max distortion 0.1175 (per coordinate, in units of sigma^2), within
+    sampling error, whatever the signs."""
+    r = rng(35).standard_normal((4000, 128))
+    for words in (O.default_sign_words(), [0, 0, 0, 0]):
+        codes, sigma = O.quantize_hlm(r, words)
+        rt = O.dequantize_hlm(codes, sigma, words)
+        rel = np.sum((r - rt) ** 2) / np.sum(r ** 2)
+        assert abs(rel - 0.1175) < 0.004
+
+
+def test_hlm_code_margin_hand_values():
+    """Distance of y / sigma from the nearest of -t, 0, t, by hand through the
+    inverse rotation: a residual whose rotation is sigma * (0.1, t + 0.02,
+    -t - 0.3, 2.0, ...) with sigma = 1."""
+    _, t = O.lloyd_max_gaussian4()
+    words = [0x5, 0, 0, 0]
+    D = 8
+    u = np.array([0.1, t + 0.02, -t - 0.3, 2.0, -0.45, 0.0, 1.0, -2.0])
+    u = u * math.sqrt(D) / np.linalg.norm(u)          # ||r|| / sqrt(D) = 1 exactly representable scale
+    r = O.unrotate(u[None], words)
+    sigma = np.array([1.0])
+    m = O.hlm_code_margin(r, sigma, words)[0]
+    want = np.minimum(np.minimum(np.abs(u + t), np.abs(u)), np.abs(u - t))
+    np.testing.assert_allclose(m, want, atol=1e-13)
+    assert np.all(np.isinf(O.hlm_code_margin(r, np.array([0.0]), words)))
+
+
+def test_hlm_plan_hand_worked():
+    """Records of the paper's codec cost D/4 + 4 = 36 bytes at D = 128, so with
+    the fixed part of the affine plan R = floor((budget - fixed) / 36)."""
+    pa = O.plan(8, 32768, 128, 2, 0.05, 32)
+    ph = O.plan(8, 32768, 128, 2, 0.05, 32, codec=O.CODEC_HLM)
+    assert O.rec_bytes(128, O.CODEC_HLM) == 36 and O.rec_bytes(128) == 48
+    assert (ph.A, ph.fixed_per_side) == (pa.A, pa.fixed_per_side)
+    assert ph.R_K == (ph.budget_unit - ph.fixed_per_side) // 36
+    assert pa.R_K == (pa.budget_unit - pa.fixed_per_side) // 48
+    assert O.side_bytes(ph, ph.R_K) <= ph.budget_unit < O.side_bytes(ph, ph.R_K + 1)
+    with pytest.raises(ValueError):
+        O.plan(8, 1024, 96, 2, 0.2, 32, codec=O.CODEC_HLM)
+
+
+def _independent_reconstruction_hlm(c, K, V):
+    from scipy.linalg import hadamard
+    H, N, D = K.shape
+    lv, _ = O.lloyd_max_gaussian4()
+    s = np.array([-1.0 if (c.sign_words[i // 32] >> (i % 32)) & 1 else 1.0 for i in range(D)])
+    Hd = hadamard(D) / math.sqrt(D)
+    out = []
+    for side, X in enumerate((K, V)):
+        Xh = np.zeros_like(X)
+        for h in range(H):
+            anc = X[h, c.anchor_pos[h]]
+            for t in range(N):
+                v = c.gamma16[side, h, t] * anc[c.idx[side, h, t]]
+                if c.flag[side, h, t]:
+                    v = v + s * (Hd @ (c.sigma[side, h, t] * lv[c.codes[side, h, t].astype(int)]))
+                Xh[h, t] = v
+        out.append(Xh)
+    return out
+
+
+def test_hlm_compress_reconstruct_and_decode():
+    """With the paper's codec the compressed unit's flagged tokens carry the
+    codes and scale of their unquantised residual, the reconstruction equals
+    an element-wise build, and decode equals SDPA over that build."""
+    r = rng(38)
+    H, N, D, G, n_obs, W = 2, 384, 128, 2, 16, 16
+    K = bf16_exact(clustered(r, H, N, D))
+    V = bf16_exact(r.standard_normal((H, N, D)) + 1.0)
+    Q = bf16_exact(r.standard_normal((H * G, n_obs, D)))
+    c = O.compress_unit(K, V, Q, G, n_obs, 0.2, W, 2, codec=O.CODEC_HLM)
+    assert c.plan.codec == O.CODEC_HLM and 0 < c.flag[0].sum() and 0 < c.flag[1].sum()
+    words = O.default_sign_words()
+    codes, sigma = O.quantize_hlm(c.resid, words)
+    np.testing.assert_array_equal(c.codes, np.where(c.flag[..., None], codes, 0))
+    np.testing.assert_array_equal(c.sigma, np.where(c.flag, sigma, 0.0))
+    Kh, Vh = O.reconstruct(c)
+    Ki, Vi = _independent_reconstruction_hlm(c, K, V)
+    np.testing.assert_allclose(Kh, Ki, atol=1e-12)
+    np.testing.assert_allclose(Vh, Vi, atol=1e-12)
+    q = bf16_exact(rng(39).standard_normal((H * G, D)))
+    o = O.decode_unit(c, q)
+    for h in range(H):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[h * G:(h + 1) * G])[None], torch.from_numpy(Ki[h])[None], torch.from_numpy(Vi[h])[None])
+        np.testing.assert_allclose(o[h * G:(h + 1) * G], ref[0].numpy(), rtol=1e-11, atol=1e-12)
