@@ -194,3 +194,35 @@ def test_decode_of_a_cache_written_under_another_plan_gives_nan(akv):
     akv.decode_attn(p1, cache, q, o, dws1)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all()
+
+
+def test_save_restore_decodes_bitwise_identically(akv, tmp_path):
+    """A compressed cache written to a file and read back into a fresh device
+    buffer decodes, under the plan rebuilt from its own header, to outputs
+    bitwise equal to those of the original buffer (the cache is position
+    independent: offsets inside it are relative to the unit)."""
+    w = SMALL["bf16_multi_part"].scaled(layers=3)
+    _flush("[save-restore] bf16_multi_part, 3 units")
+    K, V, Q = make_inputs(w)
+    p = plan_for(akv, w)
+    cache, ws, dws = akv.alloc(p, "cuda")
+    akv.compress(p, K, V, Q, cache, ws)
+    q = kvsynth.decode_queries(w, 2, device="cuda").contiguous()
+    o1 = torch.empty(w.units, w.kv_heads * w.q_per_kv, w.head_dim, dtype=torch.float32, device="cuda")
+    akv.decode_attn(p, cache, q, o1, dws)
+    torch.cuda.synchronize()
+    f = tmp_path / "cache.bin"
+    f.write_bytes(cache.cpu().numpy().tobytes())
+    del cache
+    raw = np.frombuffer(f.read_bytes(), dtype=np.uint8)
+    p2 = akv.plan_from_header(raw[:256].tobytes(), w.units)
+    assert p2.as_dict() == p.as_dict()
+    # restored at another device address (offset by 4 KiB inside a larger buffer)
+    big = torch.zeros(raw.size + 4096, dtype=torch.uint8, device="cuda")
+    restored = big[4096:]
+    restored.copy_(torch.from_numpy(raw.copy()))
+    _, _, dws2 = akv.alloc(p2, "cuda")
+    o2 = torch.full_like(o1, float("nan"))
+    akv.decode_attn(p2, restored, q, o2, dws2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
