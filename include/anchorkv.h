@@ -75,11 +75,28 @@ typedef struct {
   int32_t anchor_div;      /* non-window anchors k = floor(N / anchor_div), capped by the budget (>= 1; 128) */
   int32_t pool;            /* width of the positional pooling of the score (odd, 1..15; 7) */
   double rho;              /* k_scored = floor(rho * k) in double precision, the rest picked uniformly ([0, 1]; 0.7) */
-  int32_t group;           /* residual codec group: one fp16 scale and zero per `group` coordinates (32 only) */
+  int32_t group;           /* group-affine codec: one fp16 scale and zero per `group` coordinates (32 only) */
   int32_t pool_kv_jointly; /* 0: separate residual budgets for K and V; 1: one ranking of all (side, head,
                               token) items under both sides' budgets together (0) */
-  int32_t reserved[8];     /* zero */
+  int32_t codec;           /* residual codec: ANCHORKV_CODEC_AFFINE (default) or ANCHORKV_CODEC_HADAMARD_LM */
+  uint32_t hadamard_signs[4]; /* ANCHORKV_CODEC_HADAMARD_LM: rotation signs, bit i (bit i%32 of word i/32)
+                                 set means coordinate i is negated before the transform; the default is
+                                 the first two SplitMix64 outputs from seed 0x416E63686F724B56, low word
+                                 first (Steele, Lea and Flood 2014) */
+  int32_t reserved[3];     /* zero */
 } anchorkv_params;
+
+/* Residual codecs.  AFFINE: 2-bit codes with an fp16 scale and zero per 32
+ * coordinates (48-byte records at head_dim 128).  HADAMARD_LM, the paper's
+ * codec (Pith review of AnchorKV, "Referee Report" summary and "Assumptions &
+ * free parameters": randomized Hadamard rotation with a fixed seed, 2-bit
+ * Lloyd-Max codebook for a unit Gaussian): y = (1/sqrt(D)) H_D diag(s) r with
+ * the Sylvester Hadamard matrix, one fp16 scale sigma = ||r||/sqrt(D) per
+ * residual, code of y_i/sigma against the thresholds -t, 0, t (t = 0.9815988,
+ * a value on a threshold takes the upper cell), levels -1.5104176, -0.4527800,
+ * 0.4527800, 1.5104176; r~ = diag(s) (1/sqrt(D)) H_D (sigma * level[code])
+ * (36-byte records). */
+typedef enum { ANCHORKV_CODEC_AFFINE = 0, ANCHORKV_CODEC_HADAMARD_LM = 1 } anchorkv_codec;
 
 /* Everything the host needs about a compressed cache: counts, byte accounting
  * and the per-unit layout.  Filled by anchorkv_plan or anchorkv_plan_from_header. */
@@ -102,7 +119,7 @@ typedef struct {
   double compression_ratio;      /* 2*H*N*D*e / unit_bytes */
   /* per-unit cache layout: byte offsets from the start of a unit */
   int64_t off_anchor_k, off_anchor_v; /* [H][A][D] input dtype, stored exactly */
-  int64_t off_res_k, off_res_v;       /* [R][48] residual records, sorted by (head, position); joint:
+  int64_t off_res_k, off_res_v;       /* [R][48 or 36] residual records, sorted by (head, position); joint:
                                        * one section of R_total records, all key records first, then
                                        * the value records (off_res_v == off_res_k, and the value
                                        * chunk offsets count from the section start) */
@@ -123,10 +140,13 @@ typedef struct {
 
 /* Pointer word (uint32, one per token per side): bits 0-14 anchor index,
  * bit 15 set when the token has a residual record, bits 16-31 fp16 gamma.
- * Residual record (48 bytes): 16 little-endian uint16 code words, then 4 x
- * (fp16 scale, fp16 zero) for the 32-coordinate groups.  Code word j holds the
- * 2-bit codes of coordinates j + 16c (c = 0..7) in bits 2c..2c+1; group g is
- * coordinates 32g..32g+31; the value is zero_g + scale_g * code. */
+ * Residual record, group-affine codec (48 bytes): 16 little-endian uint16 code
+ * words, then 4 x (fp16 scale, fp16 zero) for the 32-coordinate groups.  Code
+ * word j holds the 2-bit codes of coordinates j + 16c (c = 0..7) in bits
+ * 2c..2c+1; group g is coordinates 32g..32g+31; the value is zero_g +
+ * scale_g * code.  Hadamard / Lloyd-Max codec (36 bytes): the same 16 code
+ * words over the rotated coordinates, then the fp16 scale sigma and two zero
+ * bytes. */
 
 /* Library version string. */
 const char* anchorkv_version(void);
@@ -135,8 +155,8 @@ const char* anchorkv_version(void);
 const char* anchorkv_last_error(void);
 
 /* Defaults of the method's fixed parameters (anchor_div 128, rho 0.7, pool 7,
- * group 32, separate K/V budgets) with the given theta and window.  Null is
- * ignored. */
+ * group 32, separate K/V budgets, group-affine codec, the default rotation
+ * signs) with the given theta and window.  Null is ignored. */
 void anchorkv_params_default(anchorkv_params* params, float theta, int32_t window);
 
 /* Counts, byte accounting and layout for (dims, params).  Host only, no HIP
@@ -145,7 +165,8 @@ void anchorkv_params_default(anchorkv_params* params, float theta, int32_t windo
  * N - window) where A_max is the number of exact anchors the budget pays for
  * after pointers, chunk offsets and header; k_scored = floor(rho*(A - window));
  * residual slots per side per unit
- * R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed)/(D/4+D/8))).
+ * R = min(H*(N-A), floor((floor(theta*H*N*D*e) - fixed)/rec)) with rec the
+ * record size of the codec (D/4+D/8, or D/4+4 for the Hadamard / Lloyd-Max codec).
  * (Pith review, "What carries the argument" and "Assumptions & free
  * parameters"; AnchorKV-adapted page, "The one setting worth tuning".)
  * A shape that compress or decode cannot run is refused here: more than 4096
@@ -270,8 +291,9 @@ typedef struct {
   uint16_t* gamma16;   /* [2][H][N] fp16 bits of gamma */
   uint8_t* flag;       /* [2][H][N] 1 if the token has a residual */
   uint8_t* codes;      /* [2][H][N][D] 2-bit codes (0..3); read/written only where flag */
-  uint16_t* scale16;   /* [2][H][N][D/32] fp16 bits; only where flag */
-  uint16_t* zero16;    /* [2][H][N][D/32] fp16 bits; only where flag */
+  uint16_t* scale16;   /* [2][H][N][D/32] fp16 bits; only where flag (Hadamard / Lloyd-Max codec:
+                          entry 0 of a token is its scale sigma, the others are 0) */
+  uint16_t* zero16;    /* [2][H][N][D/32] fp16 bits; only where flag (0 for the Hadamard / Lloyd-Max codec) */
 } anchorkv_unit_arrays;
 
 /* Write one unit (plan->unit_bytes bytes, header included) into host memory

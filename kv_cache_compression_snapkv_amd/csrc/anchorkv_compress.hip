@@ -872,6 +872,123 @@ __global__ __launch_bounds__(256) void k_quant(const void* Kv, const void* Vv, u
   }
 }
 
+// The paper's codec (Pith review of AnchorKV, "Referee Report" summary and
+// "Assumptions & free parameters": randomized Hadamard rotation with a fixed
+// seed, 2-bit Lloyd-Max codebook for a unit Gaussian).  Per record, the 16
+// lanes of a group hold coordinates 8j..8j+7: the residual is sign-flipped,
+// Walsh-Hadamard transformed (three stages inside a lane, four across lanes:
+// DPP for lane distances 1, 2 and 8, a swizzle for 4), and each coordinate
+// of y / (sqrt(D) sigma) is compared with the thresholds -t, 0, t of the
+// codebook; sigma = ||r|| / sqrt(D) in fp16.
+constexpr float kLmThreshold = 0.98159882f;   // between the levels 0.45278 and 1.51042
+__device__ __forceinline__ float swz_xor4(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (4 << 10)));
+}
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant_hlm(const void* Kv, const void* Vv, uint8_t* cache, int64_t stride,
+                                                  int64_t off_ak, int64_t off_av, int64_t off_rk, int64_t off_rv,
+                                                  const int* sel_list, const int2* sel_aux, int Rmax, int H, int N,
+                                                  int A, int R, int nblk, int joint, uint4 signs) {
+  using T = typename Elem<DT>::T;
+  constexpr int D = kHeadDim;
+  constexpr int QG = kQuantPerGroup;
+  __shared__ uint8_t codes_s[16][QG][128];
+  int bid = blockIdx.x;
+  const int blk = bid % nblk; bid /= nblk;
+  const int side_b = joint ? 0 : bid % 2;
+  const int u = joint ? bid : bid / 2;
+  const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int us = joint ? u : u * 2 + side_b;
+  const int rec0 = (blk * 16 + grp) * QG;
+  const uint32_t sw = j < 4 ? signs.x : j < 8 ? signs.y : j < 12 ? signs.z : signs.w;
+  const uint32_t sbyte = (sw >> (8 * (j & 3))) & 0xFFu;    // signs of coordinates 8j .. 8j+7
+  int flat[QG], a[QG], sd[QG];
+  float g[QG];
+#pragma unroll
+  for (int k = 0; k < QG; ++k) {
+    const bool act = rec0 + k < R;
+    flat[k] = act ? sel_list[(int64_t)us * Rmax + rec0 + k] : 0;
+    const int2 x = act ? sel_aux[(int64_t)us * Rmax + rec0 + k] : make_int2(0, 0);
+    a[k] = x.x;
+    g[k] = __int_as_float(x.y);
+    sd[k] = joint ? (flat[k] >= H * N ? 1 : 0) : side_b;
+    flat[k] -= joint && sd[k] ? H * N : 0;
+  }
+  uint16_t sb[QG];
+#pragma unroll
+  for (int k = 0; k < QG; ++k) {
+    const int side = sd[k];
+    const int h = (int)((unsigned)flat[k] / (unsigned)N), t = flat[k] - h * N;
+    const T* X = reinterpret_cast<const T*>(side ? Vv : Kv) + (((int64_t)u * H + h) * N + t) * D + 8 * j;
+    const T* AX = reinterpret_cast<const T*>(cache + (int64_t)u * stride + (side ? off_av : off_ak)) +
+                  ((int64_t)h * A + a[k]) * D + 8 * j;
+    T xv[8], av[8];
+    if constexpr (DT == ANCHORKV_BF16) {
+      const uint4 x4 = *reinterpret_cast<const uint4*>(X), a4 = *reinterpret_cast<const uint4*>(AX);
+      __builtin_memcpy(xv, &x4, 16);
+      __builtin_memcpy(av, &a4, 16);
+    } else {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(X), x1 = *reinterpret_cast<const uint4*>(X + 4);
+      const uint4 a0 = *reinterpret_cast<const uint4*>(AX), a1 = *reinterpret_cast<const uint4*>(AX + 4);
+      __builtin_memcpy(xv, &x0, 16); __builtin_memcpy(xv + 4, &x1, 16);
+      __builtin_memcpy(av, &a0, 16); __builtin_memcpy(av + 4, &a1, 16);
+    }
+    float y[8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float r = fmaf(-g[k], Elem<DT>::f(av[e]), Elem<DT>::f(xv[e]));
+      ss = fmaf(r, r, ss);
+      y[e] = (sbyte >> e) & 1u ? -r : r;
+    }
+    // scale: ||r|| / sqrt(D) in fp16
+    ss = row_sum(ss);
+    sb[k] = f2h_sat(sqrtf(ss) * 0.088388347648318f);
+    // Walsh-Hadamard transform over i = 8j + e: bits 0-2 of i inside the lane
+#pragma unroll
+    for (int b = 1; b < 8; b <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!(e & b)) {
+          const float p0 = y[e], p1 = y[e | b];
+          y[e] = p0 + p1;
+          y[e | b] = p0 - p1;
+        }
+    // bits 3-6 of i are bits 0-3 of the lane: the upper lane of a pair takes
+    // partner - own, the lower own + partner
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float o = dpp<kDppXor1>(y[e]);
+      y[e] = (j & 1) ? o - y[e] : y[e] + o;
+      o = dpp<kDppXor2>(y[e]);
+      y[e] = (j & 2) ? o - y[e] : y[e] + o;
+      o = swz_xor4(y[e]);
+      y[e] = (j & 4) ? o - y[e] : y[e] + o;
+      o = dpp<kDppRor8>(y[e]);            // lane j + 8 mod 16 = lane j ^ 8
+      y[e] = (j & 8) ? o - y[e] : y[e] + o;
+    }
+    const float sg = h2f(sb[k]);
+    const float inv = sg > 0.0f ? 1.0f / (11.313708498984761f * sg) : 0.0f;   // 1 / (sqrt(D) sigma)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float uu = y[e] * inv;
+      const int c = (uu >= -kLmThreshold ? 1 : 0) + (uu >= 0.0f ? 1 : 0) + (uu >= kLmThreshold ? 1 : 0);
+      codes_s[grp][k][8 * j + e] = sg > 0.0f ? (uint8_t)c : (uint8_t)0;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < QG; ++k) {
+    if (rec0 + k >= R) break;
+    uint16_t wv = 0;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) wv |= (uint16_t)(codes_s[grp][k][j + 16 * cc] << (2 * cc));
+    uint8_t* recp = cache + (int64_t)u * stride + (sd[k] ? off_rv : off_rk) + (int64_t)(rec0 + k) * kRecBytesHlm;
+    reinterpret_cast<uint16_t*>(recp)[j] = wv;
+    if (j == 0) *reinterpret_cast<uint32_t*>(recp + 32) = (uint32_t)sb[k];
+  }
+}
+
 // ------------------------------------------------------------ launch sequence
 template <int DT, int MODE>
 static int launch_obs(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t st) {
@@ -1097,10 +1214,19 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   prof_mark(st, "topr");
   if (R > 0) {
     const int nblk = (R + 16 * kQuantPerGroup - 1) / (16 * kQuantPerGroup);
-    k_quant<DT><<<(unsigned)((int64_t)US * nblk), 256, 0, st>>>(
-        K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_res_k, p.off_res_v, sel_list,
-        reinterpret_cast<const int2*>(ws + w.sel_aux), Rmax, H, N, A, R, nblk, joint ? 1 : 0);
-    AKV_CHECK_LAUNCH("k_quant");
+    if (p.params.codec == ANCHORKV_CODEC_HADAMARD_LM) {
+      const uint4 sg = make_uint4(p.params.hadamard_signs[0], p.params.hadamard_signs[1], p.params.hadamard_signs[2],
+                                  p.params.hadamard_signs[3]);
+      k_quant_hlm<DT><<<(unsigned)((int64_t)US * nblk), 256, 0, st>>>(
+          K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_res_k, p.off_res_v, sel_list,
+          reinterpret_cast<const int2*>(ws + w.sel_aux), Rmax, H, N, A, R, nblk, joint ? 1 : 0, sg);
+      AKV_CHECK_LAUNCH("k_quant_hlm");
+    } else {
+      k_quant<DT><<<(unsigned)((int64_t)US * nblk), 256, 0, st>>>(
+          K, V, cache, p.unit_stride, p.off_anchor_k, p.off_anchor_v, p.off_res_k, p.off_res_v, sel_list,
+          reinterpret_cast<const int2*>(ws + w.sel_aux), Rmax, H, N, A, R, nblk, joint ? 1 : 0);
+      AKV_CHECK_LAUNCH("k_quant");
+    }
   }
   prof_mark(st, "quant");
   return 0;

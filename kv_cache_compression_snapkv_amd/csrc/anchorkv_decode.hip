@@ -74,8 +74,24 @@ struct DecArgs {
   int H, N, A, C, S2, cps, R_K, R_V;
   int force_part;    // publish partials even with one range (a tail follows)
   int joint, R_total; // one record section for both sides (keys first), R_total records
+  int codec;          // residual codec of the cache (anchorkv_codec)
+  uint4 signs;        // rotation signs of the Hadamard / Lloyd-Max codec
   float c;
 };
+
+// Hadamard / Lloyd-Max codec (Pith review of AnchorKV, "Referee Report"
+// summary and "Assumptions & free parameters"): level(c) = -l2 + (l2 - l1) c
+// + (3 l1 - l2) hi(c) with hi(c) the high bit of the 2-bit code, exact for
+// the four levels -l2, -l1, l1, l2; the MFMAs produce sums over the codes and
+// over their high bits.
+constexpr float kLmL1 = 0.45278002f, kLmL2 = 1.5104176f;
+constexpr float kLmAlpha = kLmL2 - kLmL1;              // weight of the code
+constexpr float kLmBeta = 0.5f * (3.0f * kLmL1 - kLmL2);   // weight of the high-bit plane (which carries 2 hi)
+// sign of coordinate i from the 128-bit mask
+__device__ __forceinline__ float sign_of(uint4 s, int i) {
+  const uint32_t w = i < 32 ? s.x : i < 64 ? s.y : i < 96 ? s.z : s.w;
+  return (w >> (i & 31)) & 1u ? -1.0f : 1.0f;
+}
 
 __device__ __forceinline__ bf16x8 u4_to_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return bits_to_frag(make_uint4(a, b, c, d));
@@ -182,24 +198,29 @@ template <int G> constexpr int kGPad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
 // sums [NW][4 BR] and the softmax sums [NW][GP] reuse the region.
 struct DecLds {
   size_t S, rows, qbs, qcs, main;
-  size_t pv, pwv, pz, pl, epi;
+  size_t pv, pwv, pz, pl, prot, epi;
   size_t total;
 };
 __host__ __device__ constexpr size_t lds_align(size_t x) { return (x + 15) & ~(size_t)15; }
-__host__ __device__ inline DecLds dec_lds(int G, int A, bool qsplit, int NW) {
+__host__ __device__ inline DecLds dec_lds(int G, int A, bool qsplit, int NW, int codec = 0) {
   const size_t GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-  const size_t NB = (4 * (size_t)G + 15) / 16, BR = 4 * NB;
+  const bool hlm = codec == ANCHORKV_CODEC_HADAMARD_LM;
+  // Hadamard / Lloyd-Max: one 16-column block (q-head, hi / lo part of the
+  // rotated query) and rows of GP floats
+  const size_t NB = hlm ? 1 : (4 * (size_t)G + 15) / 16, BR = hlm ? GP : 4 * NB;
+  const size_t QH = (qsplit && !hlm) ? 2 : 1;
   DecLds L{};
   L.S = lds_align(8 * (size_t)G * A);
   L.rows = L.S + lds_align(4 * GP * (size_t)A);
   L.qbs = L.rows + (size_t)kTile * BR * 4;
-  L.qcs = L.qbs + NB * 4 * (qsplit ? 2 : 1) * 64 * 16;
+  L.qcs = L.qbs + NB * 4 * QH * 64 * 16;
   L.main = L.qcs + NB * 64 * 8;
   L.pv = 0;
   L.pwv = L.pv + (size_t)NW * G * kHeadDim * 4;
   L.pz = L.pwv + (size_t)(NW / 8) * G * kHeadDim * 4;
   L.pl = L.pz + (size_t)NW * BR * 4 * 4;
-  L.epi = L.pl + (size_t)NW * GP * 4;
+  L.prot = L.pl + lds_align((size_t)NW * GP * 4);
+  L.epi = L.prot + (hlm ? (size_t)G * kHeadDim * 4 : 0);
   L.total = L.main > L.epi ? L.main : L.epi;
   return L;
 }
@@ -226,7 +247,7 @@ __host__ __device__ inline DecLds dec_lds(int G, int A, bool qsplit, int NW) {
 //    tile cannot race with a wave still reading the previous one.
 // The epilogue sums the waves' partial outputs in a fixed order (no float
 // atomics), so the output does not depend on the order the waves ran in.
-template <int DT, int G, int NW>
+template <int DT, int G, int NW, int CD>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stream(DecArgs a) {
   using T = typename Elem<DT>::T;
   using M = Mfma<ANCHORKV_BF16>;
@@ -234,14 +255,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   constexpr int TT = kTile / NW;                 // tokens per wave per tile
   constexpr int TPL = TT / 64;                   // tokens per lane (adjacent)
   static_assert(TPL == 1 || TPL == 2, "one or two tokens per lane");
+  // Hadamard / Lloyd-Max codec: the key MFMA columns are (q-head, hi / lo
+  // bf16 part of the rotated query), the value MFMA rows (q-head, hi / lo
+  // part of p * sigma); one 16-wide block for up to 8 q-heads
+  constexpr bool HLM = CD == ANCHORKV_CODEC_HADAMARD_LM;
+  constexpr int RB = HLM ? kRecBytesHlm : kRecBytes;   // bytes per residual record
   constexpr int GP = kGPad<G>;                   // q-heads per anchor row in LDS (padded)
-  constexpr int NB = (4 * G + 15) / 16;          // 16-wide blocks of (q-head, group) pairs
-  constexpr int BR = 4 * NB;                     // floats per wave row (q-heads >= G read as 0)
-  constexpr bool QSPLIT = DT == ANCHORKV_F32;   // f32 queries enter the key MFMA as bf16 hi + lo
+  constexpr int NB = HLM ? 1 : (4 * G + 15) / 16;  // 16-wide blocks of (q-head, group) pairs
+  constexpr int BR = HLM ? GP : 4 * NB;          // floats per wave row (q-heads >= G read as 0)
+  constexpr bool QSPLIT = DT == ANCHORKV_F32 && !HLM;   // f32 queries enter the key MFMA as bf16 hi + lo
   constexpr int QH = QSPLIT ? 2 : 1;
   extern __shared__ __align__(16) float sm[];
   const int A = a.A;
-  const DecLds L = dec_lds(G, A, QSPLIT, NW);
+  const DecLds L = dec_lds(G, A, DT == ANCHORKV_F32, NW, CD);
   uint8_t* smb = reinterpret_cast<uint8_t*>(sm);
   // w[g][a] in fixed point, q-head-major (random anchors spread over the banks)
   unsigned long long* wi = reinterpret_cast<unsigned long long*>(smb);
@@ -282,7 +308,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   {
     const UnitHeader* hd = reinterpret_cast<const UnitHeader*>(base);
     if (hd->magic != kMagic || hd->H != a.H || hd->N != a.N || hd->A != A || hd->R_K != a.R_K || hd->R_V != a.R_V ||
-        hd->unit_stride != a.stride || hd->off_words != a.off_words) {
+        hd->unit_stride != a.stride || hd->off_words != a.off_words || hd->codec != a.codec ||
+        (HLM && (hd->signs[0] != a.signs.x || hd->signs[1] != a.signs.y || hd->signs[2] != a.signs.z ||
+                 hd->signs[3] != a.signs.w))) {
       const float nan = __builtin_nanf("");
       if (a.S2 == 1 && !a.force_part) {
         for (int i = threadIdx.x; i < G * D; i += blockDim.x) a.o[uh * G * D + i] = nan;
@@ -322,6 +350,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // code-plane constants: masks (SGPRs) and the exponent bias (one VGPR)
   uint32_t MK[3] = {0x00030003u, 0x000C000Cu, 0x00300030u};
   asm volatile("" : "+s"(MK[0]), "+s"(MK[1]), "+s"(MK[2]));
+  // high bit of each code (Hadamard / Lloyd-Max codec): 128 + 2 hi 4^m
+  uint32_t MKH[3] = {0x00020002u, 0x00080008u, 0x00200020u};
+  if constexpr (HLM) asm volatile("" : "+s"(MKH[0]), "+s"(MKH[1]), "+s"(MKH[2]));
   uint32_t vbias = kCodeBias;
   asm volatile("" : "+v"(vbias));
 
@@ -332,7 +363,55 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // cinit = -128 * (sum of what the column is fed), so the accumulator ends at
   // sum_d q[g][d] code_d.  The same in every wave: wave 0 writes them to LDS,
   // with each column's query sum and initial value.
-  if (wave == 0) {
+  if (HLM && wave == 0) {
+    // Hadamard / Lloyd-Max codec: rotate the queries once, q' = (1/sqrt(D))
+    // H_D diag(s) q (Walsh-Hadamard butterflies: bit 6 of the coordinate
+    // inside the lane, bits 0-5 across lanes), then column (q-head g, part)
+    // of every step is fed the bf16 hi (part 0) or lo (part 1) piece of q'
+    // at all 32 coordinates of the step (scaled by 4^-m like the codes).
+    float* qr = qf + G * D;
+    for (int g = 0; g < G; ++g) {
+      float x0 = sign_of(a.signs, lane) * qf[g * D + lane];
+      float x1 = sign_of(a.signs, lane + 64) * qf[g * D + lane + 64];
+      const float s0 = x0 + x1, s1 = x0 - x1;
+      x0 = s0; x1 = s1;
+#pragma unroll
+      for (int b = 1; b < 64; b <<= 1) {
+        const float o0 = __shfl_xor(x0, b, 64), o1 = __shfl_xor(x1, b, 64);
+        x0 = (lane & b) ? o0 - x0 : x0 + o0;
+        x1 = (lane & b) ? o1 - x1 : x1 + o1;
+      }
+      qr[g * D + lane] = x0 * 0.088388347648318f;
+      qr[g * D + lane + 64] = x1 * 0.088388347648318f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int g = col & 7, part = col >> 3;
+    float qs = 0.0f, fed = 0.0f;
+    if (g < G)
+      for (int d = 0; d < D; ++d) {
+        const float x = qr[g * D + d];
+        const float xh = bf2f(f2bf(x));
+        qs += x;
+        fed += (part ? bf2f(f2bf(x - xh)) : xh) * kPlaneInv[plane_of(d >> 4).m];
+      }
+    qcs[lane] = make_float2(qs, -128.0f * fed);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint16_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 2 * st + (e >> 2);
+        const int d = (4 * kg + (e & 3)) + 16 * c;
+        const float x = g < G ? qr[g * D + d] : 0.0f;
+        const uint16_t xh = f2bf(x);
+        const uint16_t xp = part ? f2bf(x - bf2f(xh)) : xh;
+        v[e] = f2bf(bf2f(xp) * kPlaneInv[plane_of(c).m]);  // exact: power-of-two scaling
+      }
+      qbs[st][lane] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                                 v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+    }
+  }
+  if (!HLM && wave == 0) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       const int kap = 16 * cb + col;
@@ -454,35 +533,36 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // buffer descriptor in scalar registers (a descriptor in vector registers
   // turns every load into a loop over its distinct values)
   auto run_bytes = [](int n) -> uint32_t {
-    return (uint32_t)__builtin_amdgcn_readfirstlane(min(max(n, 0), 16) * kRecBytes);
+    return (uint32_t)__builtin_amdgcn_readfirstlane(min(max(n, 0), 16) * RB);
   };
   // key batch: lane (col, kg) holds bytes 8kg..8kg+7 of record col and the
   // (scale, zero) word of group col & 3 of records 4kg + r
   uint2 kx;
   uint32_t ksz[4];
   auto load_keys = [&](int kb, int nk, uint2& x, uint32_t (&sz)[4]) {
-    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)kb * kRecBytes, run_bytes(nk));
-    const auto xx = __builtin_amdgcn_raw_buffer_load_b64(r, col * kRecBytes + 8 * kg, 0, 0);
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)kb * RB, run_bytes(nk));
+    const auto xx = __builtin_amdgcn_raw_buffer_load_b64(r, col * RB + 8 * kg, 0, 0);
     x = make_uint2(xx[0], xx[1]);
+    // (scale, zero) of group col & 3, or the scale of the Hadamard / Lloyd-Max record
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      sz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
+      sz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * RB + 32 + (HLM ? 0 : 4 * (col & 3)), 0, 0);
   };
   // value batch: code word col of records 4kg + e (pairs packed), and the
   // (scale, zero) word of group col & 3 of the same records
   uint32_t vpr[2], vsz[4];
   auto load_values = [&](int vb, int nv, uint32_t (&pr)[2], uint32_t (&sz)[4]) {
-    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)vb * kRecBytes, run_bytes(nv));
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(recV + (int64_t)vb * RB, run_bytes(nv));
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
       const int r0 = 4 * kg + 2 * e2;
-      const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b16(r, r0 * kRecBytes + 2 * col, 0, 0);
-      const uint32_t w1 = __builtin_amdgcn_raw_buffer_load_b16(r, (r0 + 1) * kRecBytes + 2 * col, 0, 0);
+      const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b16(r, r0 * RB + 2 * col, 0, 0);
+      const uint32_t w1 = __builtin_amdgcn_raw_buffer_load_b16(r, (r0 + 1) * RB + 2 * col, 0, 0);
       pr[e2] = w0 | (w1 << 16);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      sz[e] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + e) * kRecBytes + 32 + 4 * (col & 3), 0, 0);
+      sz[e] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + e) * RB + 32 + (HLM ? 0 : 4 * (col & 3)), 0, 0);
   };
   int kb_cur, nk_cur, vb_cur, nv_cur;
   run_of(0, 0, kb_cur, nk_cur, vb_cur, nv_cur);
@@ -505,12 +585,55 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   float zt[NB];        // value side: sum of p * zero for row (rb, col)
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) zt[rb] = 0.0f;
+  // Hadamard / Lloyd-Max value side: lane (col, kg) accumulates, in the
+  // rotated coordinates, q-head 4 (kg & 1) + r (the hi part for kg < 2, the lo
+  // part for kg >= 2) at coordinate col + 16 cc; zh sums p * sigma of q-head
+  // col (lanes col < 8)
+  float vh[HLM ? 8 : 1][4];
+#pragma unroll
+  for (int cc = 0; cc < (HLM ? 8 : 1); ++cc)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vh[cc][r] = 0.0f;
+  float zh = 0.0f;
 
   // ---- key-residual logits (log2 units) of records b0 .. b0+15 of the
   // wave's run, from the fragments (x, sz) into the wave's rows [b0, b0 + 16)
   // (row = rank)
   auto kbatch = [&](int b0, int nk, uint2 x, const uint32_t (&sz)[4]) {
     const uint32_t xs[3][2] = {{x.x, x.y}, {x.x >> 6, x.y >> 6}, {x.x >> 12, x.y >> 12}};
+    if constexpr (HLM) {
+      // sums over the codes (c-plane) and over their high bits (hi-plane)
+      // of the rotated query, then the level polynomial and the record scale
+      bf16x8 afc[4], afh[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const Plane p0 = plane_of(2 * st), p1 = plane_of(2 * st + 1);
+        const int i0 = p0.sh / 6, i1 = p1.sh / 6;
+        afc[st] = u4_to_frag(and_or(xs[i0][0], MK[p0.m], vbias), and_or(xs[i0][1], MK[p0.m], vbias),
+                             and_or(xs[i1][0], MK[p1.m], vbias), and_or(xs[i1][1], MK[p1.m], vbias));
+        afh[st] = u4_to_frag(and_or(xs[i0][0], MKH[p0.m], vbias), and_or(xs[i0][1], MKH[p0.m], vbias),
+                             and_or(xs[i1][0], MKH[p1.m], vbias), and_or(xs[i1][1], MKH[p1.m], vbias));
+      }
+      const float2 qc = qcs[lane];   // (sum of q' of q-head col & 7, initial accumulator of the column)
+      f32x4 cacc = {qc.y, qc.y, qc.y, qc.y}, hacc = cacc;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 bq = bits_to_frag(qbs[st][lane]);
+        cacc = M::mma(afc[st], bq, cacc);
+        hacc = M::mma(afh[st], bq, hacc);
+      }
+      const bool wr = col < G;   // column col (hi part) plus column col + 8 (lo part)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = b0 + 4 * kg + r;
+        const float C = cacc[r] + dpp<kDppRor8>(cacc[r]);
+        const float Hh = hacc[r] + dpp<kDppRor8>(hacc[r]);
+        const float sg = h2f((uint16_t)(sz[r] & 0xFFFFu));
+        const float val = sg * fmaf(kLmAlpha, C, fmaf(kLmBeta, Hh, -kLmL2 * qc.x));
+        if (wr && ii < nk) wrow[ii * BR + col] = val * a.c;
+      }
+      return;
+    }
     bf16x8 af[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -543,6 +666,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // the wave's rows [b0, b0 + 16), zeros past the run), on the K = 16 MFMA:
   // lane (col, kg) feeds records 4kg .. 4kg + 3 of the batch
   auto vbatch = [&](int b0, const uint32_t (&pr)[2], const uint32_t (&sz)[4]) {
+    if constexpr (HLM) {
+      // rows (q-head col & 7, hi / lo part col >> 3) of A = p * sigma; B =
+      // the c-plane and the hi-plane of the codes; both start from the bias
+      // term -128 * (row sums of A)
+      const int g = col & 7, part = col >> 3;
+      float ps[4];
+      float zs = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pv = g < G ? wrow[(b0 + 4 * kg + e) * BR + g] : 0.0f;
+        ps[e] = pv * h2f((uint16_t)(sz[e] & 0xFFFFu));
+        zs += ps[e];
+      }
+      zh += part == 0 ? zs : 0.0f;
+      uint32_t ap[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t hb = bf16_pack(ps[2 * k], ps[2 * k + 1]);
+        const float d0 = ps[2 * k] - __uint_as_float(hb << 16);
+        const float d1 = ps[2 * k + 1] - __uint_as_float(hb & 0xFFFF0000u);
+        ap[k] = part ? bf16_pack(d0, d1) : hb;
+      }
+      const bf16x4 a4 = u2_to_frag4(ap[0], ap[1]);
+      const f32x4 zb = mma16k(a4, bm128_4, f32x4{0, 0, 0, 0});
+      const uint32_t ps6[2] = {pr[0] >> 6, pr[1] >> 6};
+      const uint32_t ps12[2] = {pr[0] >> 12, pr[1] >> 12};
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const Plane pl = plane_of(cc);
+        const uint32_t* src = pl.sh == 0 ? pr : pl.sh == 6 ? ps6 : ps12;
+        const bf16x4 bc = u2_to_frag4(and_or(src[0], MK[pl.m], vbias), and_or(src[1], MK[pl.m], vbias));
+        const bf16x4 bh = u2_to_frag4(and_or(src[0], MKH[pl.m], vbias), and_or(src[1], MKH[pl.m], vbias));
+        const f32x4 tc = mma16k(a4, bc, zb);
+        const f32x4 th = mma16k(a4, bh, zb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vh[cc][r] = fmaf(kLmAlpha, tc[r], fmaf(kLmBeta, th[r], vh[cc][r]));
+      }
+      return;
+    }
     bf16x4 ahi[NB], alo[NB];
     f32x4 zb[NB];  // -128 * row sums of A: cancels the code bias
 #pragma unroll
@@ -720,8 +882,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
           if (fct[g] != 1.0f)
             for (int i = threadIdx.x; i < A; i += blockDim.x)
               wi[g * A + i] = (unsigned long long)__double2ll_rn((double)(long long)wi[g * A + i] * (double)fct[g]);
+        if constexpr (HLM) {
 #pragma unroll
-        for (int rb = 0; rb < NB; ++rb) {
+          for (int r = 0; r < 4; ++r) {
+            const int g = 4 * (kg & 1) + r;
+            float f = 1.0f;
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) vh[cc][r] *= f;
+          }
+          float fz = 1.0f;
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) fz = (gg == (col & 7)) ? fct[gg] : fz;
+          zh *= fz;
+        }
+#pragma unroll
+        for (int rb = 0; rb < (HLM ? 0 : NB); ++rb) {
           const int g = 4 * rb + kg;  // accumulator rows 16rb + 4kg + r -> q-head 4rb + kg
           float f = 1.0f;
 #pragma unroll
@@ -858,8 +1035,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   float* pwv = reinterpret_cast<float*>(smb + L.pwv);  // [NPART][G][D]
   float* pz = reinterpret_cast<float*>(smb + L.pz);    // [NW][4 BR]: (q-head, group) = 4g + grp
   float* pl = reinterpret_cast<float*>(smb + L.pl);    // [NW][GP]
+  if constexpr (HLM) {
+    // hi part (lanes kg < 2) plus lo part (lane + 32) of q-head 4 kg + r at
+    // coordinate col + 16 cc, in the rotated coordinates
 #pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
+    for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(vh[cc][r]), __float_as_uint(vh[cc][r]), false,
+                                                         false);
+        const float hs = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int gq = 4 * kg + r;
+        if (kg < 2 && gq < G) pv[(wave * G + gq) * D + col + 16 * cc] = hs * kPlaneInv[plane_of(cc).m];
+      }
+    float z = zh;
+    z += __shfl_xor(z, 16, 64);
+    z += __shfl_xor(z, 32, 64);
+    if (kg == 0 && col < G) pz[wave * 4 * BR + col] = z;
+  }
+#pragma unroll
+  for (int rb = 0; rb < (HLM ? 0 : NB); ++rb) {
     // lane (col, kg) of column block cc holds q-head 4rb + kg, coordinate col + 16cc
     const int gq = 4 * rb + kg;
     if (gq < G)
@@ -879,6 +1074,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   for (int g = 0; g < G; ++g)
     if (lane == g) pl[wave * GP + g] = lw[g];
   __syncthreads();
+  float* prot = reinterpret_cast<float*>(smb + L.prot);  // [G][D] (Hadamard / Lloyd-Max codec)
+  if constexpr (HLM) {
+    // residual part in the rotated coordinates: the waves' partials in a
+    // fixed order, minus l2 * sum of p * sigma (the constant term of the levels)
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+      const int g = i / D, dd = i % D;
+      float r = 0.0f, z = 0.0f;
+#pragma unroll 4
+      for (int w2 = 0; w2 < NW; ++w2) {
+        r += pv[(w2 * G + g) * D + dd];
+        z += pz[w2 * 4 * BR + g];
+      }
+      prot[i] = fmaf(-kLmL2, z, r);
+    }
+    __syncthreads();
+  }
   // thread (q-head, coordinate): the waves' partials in a fixed order
   const int64_t ps = uh * a.S2 + sp;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
@@ -887,10 +1098,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
     for (int pp = 0; pp < NPART; ++pp) val += pwv[(pp * G + g) * D + dd];
     float l = 0.0f;
+    if constexpr (HLM) {
+      // back to the input coordinates: diag(s) (1/sqrt(D)) H_D applied to the rotated sum
+      float acc = 0.0f;
+      for (int k = 0; k < D; ++k) {
+        const float x = prot[g * D + k];
+        acc += (__popc((unsigned)(dd & k)) & 1) ? -x : x;
+      }
+      val = fmaf(sign_of(a.signs, dd) * 0.088388347648318f, acc, val);
 #pragma unroll 4
-    for (int w2 = 0; w2 < NW; ++w2) {
-      val += pv[(w2 * G + g) * D + dd] + pz[w2 * 4 * BR + 4 * g + dd / 32];
-      l += pl[w2 * GP + g];
+      for (int w2 = 0; w2 < NW; ++w2) l += pl[w2 * GP + g];
+    } else {
+#pragma unroll 4
+      for (int w2 = 0; w2 < NW; ++w2) {
+        val += pv[(w2 * G + g) * D + dd] + pz[w2 * 4 * BR + 4 * g + dd / 32];
+        l += pl[w2 * GP + g];
+      }
     }
     const float m = mrun_s[0][g];
     if (a.S2 == 1 && !a.force_part) {
@@ -1159,25 +1382,29 @@ constexpr size_t kLdsLimit = 158 * 1024;  // dynamic part; the static part is un
 
 // Waves per workgroup: 8 (two tokens per lane) when two workgroups fit a
 // compute unit's LDS, else 16 (one token per lane, one workgroup).
-static int decode_waves(int G, int A, bool f32) {
-  return 2 * (dec_lds(G, A, f32, 8).total + 2048) <= 160 * 1024 ? 8 : 16;
+static int decode_waves(int G, int A, bool f32, int codec) {
+  return 2 * (dec_lds(G, A, f32, 8, codec).total + 2048) <= 160 * 1024 ? 8 : 16;
 }
 
-template <int DT, int G, int NW>
+template <int DT, int G, int NW, int CD>
 static int launch_stream_nw(const DecArgs& a, unsigned grid, hipStream_t st) {
   static size_t done = 0;
-  const size_t lds = dec_lds(G, a.A, DT == ANCHORKV_F32, NW).total;
+  const size_t lds = dec_lds(G, a.A, DT == ANCHORKV_F32, NW, CD).total;
   if (lds > kLdsLimit) return fail(ANCHORKV_E_SHAPE, "decode: q_per_kv * anchors too large for LDS");
-  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G, NW>), lds, &done)) return rc;
-  k_dec_stream<DT, G, NW><<<grid, 64 * NW, lds, st>>>(a);
+  if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_stream<DT, G, NW, CD>), lds, &done)) return rc;
+  k_dec_stream<DT, G, NW, CD><<<grid, 64 * NW, lds, st>>>(a);
   AKV_CHECK_LAUNCH("k_dec_stream");
   return 0;
 }
 
 template <int DT, int G>
 static int launch_stream(const DecArgs& a, unsigned grid, hipStream_t st) {
-  if (decode_waves(G, a.A, DT == ANCHORKV_F32) == 8) return launch_stream_nw<DT, G, 8>(a, grid, st);
-  return launch_stream_nw<DT, G, 16>(a, grid, st);
+  const bool nw8 = decode_waves(G, a.A, DT == ANCHORKV_F32, a.codec) == 8;
+  if (a.codec == ANCHORKV_CODEC_HADAMARD_LM)
+    return nw8 ? launch_stream_nw<DT, G, 8, ANCHORKV_CODEC_HADAMARD_LM>(a, grid, st)
+               : launch_stream_nw<DT, G, 16, ANCHORKV_CODEC_HADAMARD_LM>(a, grid, st);
+  return nw8 ? launch_stream_nw<DT, G, 8, ANCHORKV_CODEC_AFFINE>(a, grid, st)
+             : launch_stream_nw<DT, G, 16, ANCHORKV_CODEC_AFFINE>(a, grid, st);
 }
 
 template <int DT>
@@ -1201,6 +1428,9 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   a.c = kLog2e / sqrtf((float)kHeadDim);
   a.R_K = p.R_K; a.R_V = p.R_V;
   a.joint = p.joint; a.R_total = p.R_total;
+  a.codec = p.params.codec;
+  a.signs = make_uint4(p.params.hadamard_signs[0], p.params.hadamard_signs[1], p.params.hadamard_signs[2],
+                       p.params.hadamard_signs[3]);
   a.force_part = n_tail > 0 ? 1 : 0;
   const unsigned grid = (unsigned)((int64_t)U * H * S2);
   int rc = 0;
@@ -1239,14 +1469,15 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   return 0;
 }
 
-int decode_blocks_per_cu(int G, int A, bool f32, int64_t, int64_t, int64_t, int64_t) {
+int decode_blocks_per_cu(int G, int A, bool f32, int codec) {
   // 8-wave workgroups two per compute unit, 16-wave ones alone (four waves per SIMD either way)
-  return decode_waves(G, A, f32) == 8 ? 2 : 1;
+  return decode_waves(G, A, f32, codec) == 8 ? 2 : 1;
 }
 
 int decode_supports(const anchorkv_plan_info& p) {
   if (p.G > kMaxG) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: decode supports q_per_kv <= %d", kMaxG);
-  if (dec_lds(p.G, p.A, p.dtype == ANCHORKV_F32, decode_waves(p.G, p.A, p.dtype == ANCHORKV_F32)).total > kLdsLimit)
+  const bool f32 = p.dtype == ANCHORKV_F32;
+  if (dec_lds(p.G, p.A, f32, decode_waves(p.G, p.A, f32, p.params.codec), p.params.codec).total > kLdsLimit)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %d anchors x %d q-heads exceed the decode kernel's LDS", p.A, p.G);
   if (p.decode_splits > 64 || p.n_chunks > 128 * p.decode_splits)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: n_tokens %d too large for the decode ranges", p.N);

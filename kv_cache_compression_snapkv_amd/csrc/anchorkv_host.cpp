@@ -93,8 +93,8 @@ DecodeWs decode_ws_layout(const anchorkv_plan_info& p) {
 static int decode_split_count(const anchorkv_plan_info& p) {
   const int64_t heads = (int64_t)p.units * p.H;
   const int64_t C = p.n_chunks;   // splits start on 1024-token chunk boundaries
-  const int64_t slots = 256 * (int64_t)decode_blocks_per_cu(p.G, p.A, p.dtype == ANCHORKV_F32, p.R_K, p.R_V, p.H, C);
-  const int64_t chunk_bytes = 8 * 1024 + kRecBytes * (int64_t)records_per_unit(p) / std::max<int64_t>(1, p.H * C);
+  const int64_t slots = 256 * (int64_t)decode_blocks_per_cu(p.G, p.A, p.dtype == ANCHORKV_F32, p.params.codec);
+  const int64_t chunk_bytes = 8 * 1024 + rec_bytes_of(p) * (int64_t)records_per_unit(p) / std::max<int64_t>(1, p.H * C);
   const int64_t anchor_bytes = 2 * (int64_t)p.A * p.D * p.elem_bytes;
   int best = 1;
   int64_t best_cost = INT64_MAX;
@@ -108,6 +108,7 @@ static int decode_split_count(const anchorkv_plan_info& p) {
 
 static void layout(anchorkv_plan_info* p) {
   const int64_t H = p->H, N = p->N, D = p->D, A = p->A, e = p->elem_bytes, C = p->n_chunks;
+  const int64_t RB = rec_bytes_of(*p);
   int64_t off = kHeaderBytes;
   p->off_anchor_k = off; off += H * A * D * e;
   p->off_anchor_v = off; off += H * A * D * e;
@@ -115,10 +116,10 @@ static void layout(anchorkv_plan_info* p) {
     // one section: key records first, then value records (the split is the data's)
     p->off_res_k = off;
     p->off_res_v = off;
-    off += (int64_t)kRecBytes * p->R_total;
+    off += RB * p->R_total;
   } else {
-    p->off_res_k = off; off += (int64_t)kRecBytes * p->R_K;
-    p->off_res_v = off; off += (int64_t)kRecBytes * p->R_V;
+    p->off_res_k = off; off += RB * p->R_K;
+    p->off_res_v = off; off += RB * p->R_V;
   }
   p->off_words = off; off += 8 * H * N;
   p->off_chunk_k = off; off += 4 * H * C;
@@ -147,7 +148,20 @@ void fill_header(const anchorkv_plan_info& p, UnitHeader* h) {
   h->anchor_div = p.params.anchor_div; h->pool = p.params.pool; h->group = p.params.group;
   h->pool_kv_jointly = p.params.pool_kv_jointly; h->rho = p.params.rho;
   h->R_total = p.R_total;
+  h->codec = p.params.codec;
+  for (int i = 0; i < 4; ++i) h->signs[i] = p.params.hadamard_signs[i];
 }
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", 2014): advance the state by the golden-ratio increment, then
+// mix it with two multiply-xorshift rounds.
+static uint64_t splitmix64(uint64_t& state) {
+  uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+static constexpr uint64_t kSignSeed = 0x416E63686F724B56ull;
 
 static void params_default(anchorkv_params* q, float theta, int32_t window) {
   std::memset(q, 0, sizeof(*q));
@@ -158,6 +172,11 @@ static void params_default(anchorkv_params* q, float theta, int32_t window) {
   q->pool = 7;
   q->group = kGroup;
   q->pool_kv_jointly = 0;
+  q->codec = ANCHORKV_CODEC_AFFINE;
+  uint64_t st = kSignSeed;
+  const uint64_t a = splitmix64(st), b = splitmix64(st);
+  q->hadamard_signs[0] = (uint32_t)a; q->hadamard_signs[1] = (uint32_t)(a >> 32);
+  q->hadamard_signs[2] = (uint32_t)b; q->hadamard_signs[3] = (uint32_t)(b >> 32);
 }
 
 static int check_params(const anchorkv_params& q) {
@@ -169,6 +188,8 @@ static int check_params(const anchorkv_params& q) {
   if (q.group != kGroup) return fail(ANCHORKV_E_ARG, "anchorkv_plan: codec group %d: only %d is supported", q.group, kGroup);
   if (q.pool_kv_jointly != 0 && q.pool_kv_jointly != 1)
     return fail(ANCHORKV_E_ARG, "anchorkv_plan: pool_kv_jointly %d must be 0 or 1", q.pool_kv_jointly);
+  if (q.codec != ANCHORKV_CODEC_AFFINE && q.codec != ANCHORKV_CODEC_HADAMARD_LM)
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: codec %d is not 0 (affine) or 1 (Hadamard / Lloyd-Max)", q.codec);
   for (int i = 0; i < (int)(sizeof(q.reserved) / sizeof(q.reserved[0])); ++i)
     if (q.reserved[i] != 0) return fail(ANCHORKV_E_ARG, "anchorkv_plan: reserved parameter fields must be zero");
   return 0;
@@ -215,7 +236,7 @@ static int plan_impl(const anchorkv_dims* d, const anchorkv_params* prm, anchork
   p.A = (int32_t)A; p.k_scored = (int32_t)k_s; p.k_uniform = (int32_t)(k_nw - k_s);
   const int64_t budget = (int64_t)std::floor(th * (double)(H * N * D * e));
   const int64_t fixed = 128 + H * (A * D * e + 4 * N + 2 * A + 4 * C);
-  const int64_t rec = D / 4 + D / 8;
+  const int64_t rec = rec_bytes_of(prm->codec);   // D/4 + D/8, or D/4 + 4 (D = 128)
   const int64_t R = std::max<int64_t>(0, std::min(H * (N - A), (budget - fixed) / rec));
   p.R_K = p.R_V = (int32_t)R;
   p.budget_bytes_per_side = budget;
@@ -250,6 +271,8 @@ static int plan_from_header_impl(const void* header_host, int32_t units, anchork
   params_default(&q, h.theta, h.window);
   q.anchor_div = h.anchor_div; q.rho = h.rho; q.pool = h.pool; q.group = h.group;
   q.pool_kv_jointly = h.pool_kv_jointly;
+  q.codec = h.codec;
+  for (int i = 0; i < 4; ++i) q.hadamard_signs[i] = h.signs[i];
   int rc = plan_impl(&d, &q, out);
   if (rc) return rc == ANCHORKV_E_ARG ? fail(ANCHORKV_E_LAYOUT, "%s: header parameters are invalid", fn) : rc;
   if (out->A != h.A || out->R_K != h.R_K || out->R_V != h.R_V || out->R_total != h.R_total ||
@@ -290,7 +313,7 @@ int anchorkv_cache_layout(const void* header_host, anchorkv_layout* out) {
   out->off_res_k = p.off_res_k; out->off_res_v = p.off_res_v; out->off_words = p.off_words;
   out->off_chunk_k = p.off_chunk_k; out->off_chunk_v = p.off_chunk_v; out->off_positions = p.off_positions;
   out->unit_bytes = p.unit_bytes; out->unit_stride = p.unit_stride;
-  out->A = p.A; out->R_K = p.R_K; out->R_V = p.R_V; out->n_chunks = p.n_chunks; out->record_bytes = kRecBytes;
+  out->A = p.A; out->R_K = p.R_K; out->R_V = p.R_V; out->n_chunks = p.n_chunks; out->record_bytes = rec_bytes_of(p);
   return 0;
 }
 
@@ -382,6 +405,8 @@ int anchorkv_unit_pack_host(const anchorkv_plan_info* p, const anchorkv_unit_arr
   std::memcpy(base + p->off_anchor_v, in->anchors_v, (size_t)(H * A * D * e));
   std::memcpy(base + p->off_positions, in->positions, (size_t)(4 * H * A));
   uint32_t* words = (uint32_t*)(base + p->off_words);
+  const int64_t RB = rec_bytes_of(*p);
+  const bool hlm = p->params.codec == ANCHORKV_CODEC_HADAMARD_LM;
   int64_t r = 0;   // record index from the section start (joint: runs on from the key records)
   for (int s = 0; s < 2; ++s) {
     uint8_t* rec = base + (s ? p->off_res_v : p->off_res_k);
@@ -402,11 +427,16 @@ int anchorkv_unit_pack_host(const anchorkv_plan_info* p, const anchorkv_unit_arr
           uint16_t cw[16] = {0};
           const uint8_t* cd = in->codes + i * D;
           for (int d = 0; d < D; ++d) cw[d % 16] |= (uint16_t)((cd[d] & 3u) << (2 * (d / 16)));
-          uint8_t* out = rec + r * kRecBytes;
+          uint8_t* out = rec + r * RB;
           std::memcpy(out, cw, 32);
-          for (int g = 0; g < D / kGroup; ++g) {
-            uint16_t sz[2] = {in->scale16[i * (D / kGroup) + g], in->zero16[i * (D / kGroup) + g]};
-            std::memcpy(out + 32 + 4 * g, sz, 4);
+          if (hlm) {
+            const uint16_t sg[2] = {in->scale16[i * (D / kGroup)], 0};
+            std::memcpy(out + 32, sg, 4);
+          } else {
+            for (int g = 0; g < D / kGroup; ++g) {
+              uint16_t sz[2] = {in->scale16[i * (D / kGroup) + g], in->zero16[i * (D / kGroup) + g]};
+              std::memcpy(out + 32 + 4 * g, sz, 4);
+            }
           }
           ++r;
         }
@@ -435,6 +465,8 @@ int anchorkv_unit_unpack_host(const anchorkv_plan_info* p, const void* unit_in, 
   if (out->anchors_v) std::memcpy(out->anchors_v, base + p->off_anchor_v, (size_t)(H * A * D * e));
   if (out->positions) std::memcpy(out->positions, base + p->off_positions, (size_t)(4 * H * A));
   const uint32_t* words = (const uint32_t*)(base + p->off_words);
+  const int64_t RB = rec_bytes_of(*p);
+  const bool hlm = p->params.codec == ANCHORKV_CODEC_HADAMARD_LM;
   int64_t r = 0;   // record index from the section start (joint: runs on from the key records)
   for (int s = 0; s < 2; ++s) {
     const uint8_t* rec = base + (s ? p->off_res_v : p->off_res_k);
@@ -455,14 +487,20 @@ int anchorkv_unit_unpack_host(const anchorkv_plan_info* p, const void* unit_in, 
         if (out->flag) out->flag[i] = f ? 1 : 0;
         if (f) {
           if (r >= cap) return fail(ANCHORKV_E_LAYOUT, "unpack: more flags than records on side %d", s);
-          const uint8_t* in = rec + r * kRecBytes;
+          const uint8_t* in = rec + r * RB;
           uint16_t cw[16];
           std::memcpy(cw, in, 32);
           if (out->codes)
             for (int d = 0; d < D; ++d) out->codes[i * D + d] = (uint8_t)((cw[d % 16] >> (2 * (d / 16))) & 3u);
           for (int g = 0; g < D / kGroup; ++g) {
             uint16_t sz[2];
-            std::memcpy(sz, in + 32 + 4 * g, 4);
+            if (hlm) {
+              std::memcpy(sz, in + 32, 4);
+              if (g > 0) sz[0] = 0;
+              sz[1] = 0;
+            } else {
+              std::memcpy(sz, in + 32 + 4 * g, 4);
+            }
             if (out->scale16) out->scale16[i * (D / kGroup) + g] = sz[0];
             if (out->zero16) out->zero16[i * (D / kGroup) + g] = sz[1];
           }

@@ -12,7 +12,10 @@ namespace akv {
 
 constexpr int kHeaderBytes = 256;
 constexpr int kChunk = 1024;          // tokens per residual-offset chunk
-constexpr int kRecBytes = 48;         // residual record: 32 B codes + 4 x (fp16 scale, fp16 zero)
+constexpr int kRecBytes = 48;         // group-affine residual record: 32 B codes + 4 x (fp16 scale, fp16 zero)
+constexpr int kRecBytesHlm = 36;      // Hadamard / Lloyd-Max record: 32 B codes + fp16 scale + 2 zero bytes
+inline int rec_bytes_of(int codec) { return codec == ANCHORKV_CODEC_HADAMARD_LM ? kRecBytesHlm : kRecBytes; }
+inline int rec_bytes_of(const anchorkv_plan_info& p) { return rec_bytes_of(p.params.codec); }
 constexpr int kGroup = 32;            // codec group (coordinates)
 constexpr int kHeadDim = 128;         // the only supported head dim
 constexpr uint32_t kMagic = 0x31564B41u;  // "AKV1"
@@ -90,7 +93,9 @@ struct UnitHeader {
   int32_t anchor_div, pool, group, pool_kv_jointly;
   double rho;
   int32_t R_total, pad1;   // joint ranking: residual records of both sides
-  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8 - 4 * 4 - 8 - 8];
+  int32_t codec;           // residual codec (anchorkv_codec)
+  uint32_t signs[4];       // rotation signs of the Hadamard / Lloyd-Max codec
+  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8 - 4 * 4 - 8 - 8 - 4 - 16];
 };
 static_assert(sizeof(UnitHeader) == 256, "header must be 256 bytes");
 void fill_header(const anchorkv_plan_info& p, UnitHeader* h);
@@ -112,7 +117,7 @@ int run_decode_tail(const anchorkv_plan_info& p, const void* cache, const void* 
 constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
 int run_decode_noalloc(const anchorkv_plan_info& p, const void* cache, const void* q, float* o, void* stream);
 // Workgroups of the decode kernel that fit one compute unit (LDS and registers).
-int decode_blocks_per_cu(int G, int A, bool f32, int64_t R_K, int64_t R_V, int64_t H, int64_t C);
+int decode_blocks_per_cu(int G, int A, bool f32, int codec);
 // Host-only checks (no HIP calls) that the kernels can run a plan: 0, or a
 // negative code with the message set.  anchorkv_plan refuses what fails them.
 int compress_supports(const anchorkv_plan_info& p);

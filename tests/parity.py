@@ -44,12 +44,18 @@ def storage_to_f64(a, dtype_code):
 
 
 def oracle_arrays(c: O.Compressed, dtype_code):
-    """Oracle compressed unit -> arrays for the host packer."""
+    """Oracle compressed unit -> arrays for the host packer (the Hadamard /
+    Lloyd-Max codec's scale goes in entry 0 of each token's scale16)."""
+    scale16, zero16 = bits_f16(c.scale), bits_f16(c.zero)
+    if c.codec == O.CODEC_HLM:
+        scale16 = np.zeros(c.scale.shape, np.uint16)
+        scale16[..., 0] = bits_f16(c.sigma)
+        zero16 = np.zeros(c.zero.shape, np.uint16)
     return dict(positions=c.anchor_pos.astype(np.int32),
                 anchors_k=anchors_to_storage(c.anchors[0], dtype_code),
                 anchors_v=anchors_to_storage(c.anchors[1], dtype_code),
                 idx=c.idx.astype(np.int32), gamma16=bits_f16(c.gamma16), flag=c.flag.astype(np.uint8),
-                codes=c.codes.astype(np.uint8), scale16=bits_f16(c.scale), zero16=bits_f16(c.zero))
+                codes=c.codes.astype(np.uint8), scale16=scale16, zero16=zero16)
 
 
 def fp16_midpoint_distance(x):
@@ -104,7 +110,10 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
     prm = dict(params or {})
     H, N, D = K.shape
     dtype_code = 1 if e == 2 else 2
-    p = O.plan(H, N, D, e, theta, W, **{k: v for k, v in prm.items() if k in ("anchor_div", "rho", "pool_kv_jointly")})
+    p = O.plan(H, N, D, e, theta, W,
+               **{k: v for k, v in prm.items() if k in ("anchor_div", "rho", "pool_kv_jointly", "codec")})
+    hlm = prm.get("codec", O.CODEC_AFFINE) == O.CODEC_HLM
+    words = tuple(prm.get("sign_words", O.default_sign_words()))
     # 1. anchors (per head), from the oracle's own pooled score
     first = O.compress_unit(K, V, Q, G, n_obs, theta, W, e, **prm)
     if taps is not None and "score" in taps:
@@ -166,6 +175,19 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
         r = fourth.resid[s][fl]                       # [R, D]
         if r.shape[0] == 0:
             continue
+        if hlm:
+            # scale fp16(||r|| / sqrt(D)) away from fp16 rounding midpoints;
+            # codes where the rotated coordinate is away from the thresholds
+            codes_o, sg_o = O.quantize_hlm(r, words)
+            safe_s = fp16_midpoint_distance(np.linalg.norm(r, axis=1) / math.sqrt(D)) > 1e-3
+            sg_g = f16_bits_to_f64(gpu["scale16"][s][fl][:, 0])
+            assert np.all((sg_g == sg_o) | ~safe_s), f"side {s}: scales differ"
+            assert not gpu["zero16"][s][fl].any() and not gpu["scale16"][s][fl][:, 1:].any()
+            safe_e = (O.hlm_code_margin(r, sg_o, words) > 1e-3) & safe_s[:, None]
+            bad = (gpu["codes"][s][fl] != codes_o) & safe_e
+            assert not bad.any(), f"side {s}: {int(bad.sum())} codes differ away from thresholds"
+            rep[f"codes_checked_{s}"] = int(safe_e.sum())
+            continue
         codes_o, sc_o, ze_o = O.quantize(r)
         lo = r.reshape(r.shape[0], -1, 32).min(-1)
         hi = r.reshape(r.shape[0], -1, 32).max(-1)
@@ -193,6 +215,8 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
         cond.codes = np.where(gflag[..., None], gpu["codes"], 0).astype(np.uint8)
         cond.scale = f16_bits_to_f64(gpu["scale16"])
         cond.zero = f16_bits_to_f64(gpu["zero16"])
+        if hlm:
+            cond.sigma = np.where(gflag, f16_bits_to_f64(gpu["scale16"][..., 0]), 0.0)
         o_ref = O.decode_unit(cond, q)
         err = np.linalg.norm(o_gpu - o_ref, axis=1) / np.maximum(np.linalg.norm(o_ref, axis=1), 1e-30)
         rep["decode_max_rel_err"] = float(err.max())

@@ -161,17 +161,20 @@ def test_params_defaults_and_range_checks(akv):
     & free parameters": k = S/128, rho = 0.7, pooling width 7) and the plan
     refuses parameters outside their documented ranges."""
     q = akv.params(0.05, 32)
-    assert (q.theta, q.window, q.anchor_div, q.rho, q.pool, q.group, q.pool_kv_jointly) == \
-        (pytest.approx(0.05), 32, 128, 0.7, 7, 32, 0)
+    assert (q.theta, q.window, q.anchor_div, q.rho, q.pool, q.group, q.pool_kv_jointly, q.codec) == \
+        (pytest.approx(0.05), 32, 128, 0.7, 7, 32, 0, 0)
+    # the default rotation signs are the oracle's SplitMix64 words (each side
+    # implements the generator from its published definition)
+    assert list(q.hadamard_signs) == O.default_sign_words()
     E = akv.AnchorKVError
     for kw in (dict(pool=6), dict(pool=17), dict(pool=0), dict(group=64), dict(pool_kv_jointly=2),
-               dict(rho=-0.1), dict(rho=1.5), dict(anchor_div=0)):
+               dict(rho=-0.1), dict(rho=1.5), dict(anchor_div=0), dict(codec=2), dict(codec=-1)):
         with pytest.raises(E) as e:
             akv.plan(1, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32, **kw)
         assert e.value.code == -1, kw
     d = akv.binding.Dims(1, 8, 4, 8192, 128, 32, akv.BF16)
     q = akv.params(0.1, 32)
-    q.reserved[3] = 1
+    q.reserved[2] = 1
     out = akv.PlanInfo()
     assert akv.lib().anchorkv_plan(ct.byref(d), ct.byref(q), ct.byref(out)) == -1
 
@@ -291,3 +294,67 @@ def test_joint_pack_unpack_roundtrip(akv):
     bad["flag"][1, 0, 5] ^= 1
     with pytest.raises(akv.AnchorKVError):
         akv.pack_unit(p, bad)
+
+
+@pytest.mark.parametrize("H,N,theta,W,e,joint", [(8, 8192, 0.1, 32, 2, 0), (8, 32768, 0.05, 32, 2, 0),
+                                                 (3, 5000, 0.07, 16, 2, 1), (1, 512, 0.1, 32, 4, 0),
+                                                 (8, 131072, 0.05, 32, 2, 0)])
+def test_hlm_plan_matches_oracle(akv, H, N, theta, W, e, joint):
+    """The paper's codec: 36-byte records, so more residual slots than the
+    group-affine codec under the same budget; counts equal the oracle's."""
+    p = akv.plan(1, H, 2, N, 128, 8, akv.BF16 if e == 2 else akv.F32, theta, W, codec=1, pool_kv_jointly=joint)
+    o = O.plan(H, N, 128, e, theta, W, pool_kv_jointly=bool(joint), codec=O.CODEC_HLM)
+    assert (p.A, p.R_K, p.R_V, p.R_total) == (o.A, o.R_K, o.R_V, o.R_total)
+    recs = o.R_total if joint else o.R_K + o.R_V
+    assert p.unit_bytes == 2 * o.fixed_per_side + 36 * recs
+    pa = akv.plan(1, H, 2, N, 128, 8, akv.BF16 if e == 2 else akv.F32, theta, W, pool_kv_jointly=joint)
+    assert p.R_K >= pa.R_K and p.A == pa.A
+    if N <= 8192:
+        blob = akv.pack_unit(p, _joint_flagged(akv, p) if joint else _flagged_arrays(akv, p))
+        assert akv.cache_layout(blob[:256])["record_bytes"] == 36
+        assert akv.plan_from_header(blob[:256], 1).as_dict() == p.as_dict()
+
+
+def _joint_flagged(akv, p):
+    arr = _no_residual_arrays(akv, p)
+    H, N = p.H, p.N
+    flat = arr["flag"].reshape(-1)
+    elig = np.ones(2 * H * N, bool)
+    for s in range(2):
+        for h in range(H):
+            elig[(s * H + h) * N + arr["positions"][h]] = False
+    flat[np.flatnonzero(elig)[:p.R_total]] = 1
+    return arr
+
+
+def test_hlm_pack_unpack_roundtrip_and_header(akv):
+    """A cache of the paper's codec packed from the oracle's arrays unpacks to
+    the same codes and scales (scale in entry 0 of scale16, zeros elsewhere);
+    the header records the codec and the rotation signs, so the plan rebuilt
+    from it is the same, custom signs included."""
+    r = np.random.default_rng(6)
+    H, G, N, D, n_obs, W = 2, 2, 1500, 128, 8, 8
+    K = r.standard_normal((H, N, D)).astype(np.float32).astype(np.float64)
+    V = (4.0 * r.standard_normal((H, N, D))).astype(np.float32).astype(np.float64)
+    Q = r.standard_normal((H * G, n_obs, D)).astype(np.float32).astype(np.float64)
+    words = [0x12345678, 0x9ABCDEF0, 0x0F0F0F0F, 0xFFFF0000]
+    c = O.compress_unit(K, V, Q, G, n_obs, 0.1, W, 4, codec=O.CODEC_HLM, sign_words=words)
+    p = akv.plan(1, H, G, N, D, n_obs, akv.F32, 0.1, W, codec=1, hadamard_signs=words)
+    assert list(p.params.hadamard_signs) == words and p.params.codec == 1
+    assert c.flag[0].sum() == p.R_K and c.flag[1].sum() == p.R_V
+    from tests.parity import oracle_arrays
+    arr = oracle_arrays(c, 2)
+    blob = akv.pack_unit(p, arr)
+    back = akv.unpack_unit(p, blob)
+    fl = arr["flag"].astype(bool)
+    for k in ("idx", "gamma16", "flag"):
+        np.testing.assert_array_equal(back[k], arr[k])
+    np.testing.assert_array_equal(back["codes"][fl], arr["codes"][fl])
+    np.testing.assert_array_equal(back["scale16"][fl], arr["scale16"][fl])
+    assert not back["zero16"][fl].any()
+    assert akv.plan_from_header(blob[:256], 1).as_dict() == p.as_dict()
+    assert akv.cache_layout(blob[:256])["record_bytes"] == 36
+    # record r of the key section: 32 code bytes, the fp16 scale, two zero bytes
+    rec0 = np.frombuffer(blob[p.off_res_k:p.off_res_k + 36], np.uint8)
+    first = np.argwhere(fl[0])[0]
+    assert rec0[32:34].view(np.uint16)[0] == arr["scale16"][0, first[0], first[1], 0] and not rec0[34:36].any()

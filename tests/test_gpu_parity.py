@@ -55,11 +55,19 @@ SMALL = {
     "bf16_joint": W_["llama8b_32k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=3000, n_dirs=32),
     "bf16_joint_stress": W_["stress_64k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, theta=0.06),
     "f32_joint": W_["tiny_f32"],
+    # the paper's residual codec (Hadamard rotation + Lloyd-Max codebook)
+    "bf16_hlm": W_["llama8b_32k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=3000, n_dirs=32),
+    "bf16_hlm_g8": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=4500, theta=0.08),
+    "bf16_hlm_stress": W_["stress_64k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, theta=0.05),
+    "f32_hlm": W_["tiny_f32"].scaled(n_tokens=1500),
+    "bf16_hlm_joint": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=2500, n_obs=16, window=16),
 }
 # non-default method parameters of some cases (anchorkv_params)
 PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40),
           "bf16_joint": dict(pool_kv_jointly=1), "bf16_joint_stress": dict(pool_kv_jointly=1),
-          "f32_joint": dict(pool_kv_jointly=1)}
+          "f32_joint": dict(pool_kv_jointly=1),
+          "bf16_hlm": dict(codec=1), "bf16_hlm_g8": dict(codec=1), "bf16_hlm_stress": dict(codec=1),
+          "f32_hlm": dict(codec=1), "bf16_hlm_joint": dict(codec=1, pool_kv_jointly=1)}
 
 
 def _flush(msg):
@@ -121,7 +129,8 @@ def test_compress_decode_parity(akv, name):
         _flush(f"[parity] {name} unit {u}: {rep}")
 
 
-@pytest.mark.parametrize("name", ["bf16_ragged", "f32_tiny", "bf16_stress_short", "bf16_joint"])
+@pytest.mark.parametrize("name", ["bf16_ragged", "f32_tiny", "bf16_stress_short", "bf16_joint", "bf16_hlm_g8",
+                                  "f32_hlm", "bf16_hlm_stress"])
 def test_decode_on_host_packed_oracle_cache(akv, name):
     """Decode alone: the oracle's compressed representation, packed on the
     host into the cache layout, decoded on the GPU."""
