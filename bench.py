@@ -55,8 +55,10 @@ def stage_work(p, stage):
     if stage == "obs_util":                      # Q K^T for p, Q R_K, V O
         return U * H * 3 * 2.0 * N * GQ * D, 2 * xb + qb + U * 2 * H * N * 4
     if stage == "dec_stream":                    # anchors, pointer words, residual records, q, o
+        rec = 36 if p.params.codec == 1 else 48
+        nrec = p.R_total if p.joint else p.R_K + p.R_V
         return (U * H * N * G * 6.0 + 2 * U * H * G * A * 2.0 * D,
-                U * (8 * H * N + 48 * (p.R_K + p.R_V) + 2 * H * A * D * e) + U * H * G * D * (e + 4))
+                U * (8 * H * N + rec * nrec + 2 * H * A * D * e) + U * H * G * D * (e + 4))
     return 0.0, 0.0
 
 
@@ -126,6 +128,41 @@ def measure_one_unit(akv, w, cache, p, q, stream, reps=20):
     st = sorted(ms for n, ms in akv.profile_read() if n == "dec_stream")
     akv.profile_enable(False)
     return {"units": 1, "us": st[len(st) // 2] * 1e3, "bytes": decode_bytes(p1)}
+
+
+COMPRESS_STAGES = ["obs_stats", "ml_combine", "obs_score", "o_combine", "select", "assign", "obs_util", "util_fix",
+                   "topr", "quant"]
+
+
+def measure_variant(akv, w, K, V, Q, q, stream, reps=3, **kw):
+    """Compress and one decode step of the same inputs under other method
+    parameters (kw: codec, pool_kv_jointly, ...), outside the timed steps:
+    HIP-event stage times, median over reps of the per-call sums."""
+    import torch
+    p = akv.plan(w.units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs,
+                 akv.BF16 if w.dtype == "bf16" else akv.F32, w.theta, w.window, **kw)
+    cache, ws, dws = akv.alloc(p, K.device)
+    o = torch.empty(w.units, w.kv_heads * w.q_per_kv, w.head_dim, dtype=torch.float32, device=K.device)
+    akv.compress(p, K, V, Q, cache, ws, stream)
+    akv.decode_attn(p, cache, q, o, dws, stream)
+    torch.cuda.synchronize()
+    akv.profile_enable(True)
+    akv.profile_read()
+    comp, dec = [], []
+    for _ in range(reps):
+        akv.compress(p, K, V, Q, cache, ws, stream)
+        comp.append(sum(ms for n, ms in akv.profile_read() if n in COMPRESS_STAGES))
+        akv.decode_attn(p, cache, q, o, dws, stream)
+        dec.append(sum(ms for n, ms in akv.profile_read() if n == "dec_stream"))
+    akv.profile_enable(False)
+    comp_ms, dec_ms = sorted(comp)[reps // 2], sorted(dec)[reps // 2]
+    db = decode_bytes(p)
+    _, sb = stage_work(p, "dec_stream")
+    del cache, ws, dws
+    return {"params": kw, "compress_ms": comp_ms, "decode_us": dec_ms * 1e3, "decode_bytes": db,
+            "decode_GB_s": db / (dec_ms * 1e-3) / 1e9, "decode_hbm_frac": sb / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "residual_records_per_unit": p.R_total if p.joint else p.R_K + p.R_V,
+            "compression_ratio": p.compression_ratio}
 
 
 def cpu_baseline(w, budget_s=20.0):
@@ -336,6 +373,9 @@ def main():
     extras = not args.no_extras
     tail_rec = measure_tail(akv, w, p, cache, qs[0], o, dws, stream, args.tail) if extras and args.tail > 0 else None
     unit_rec = measure_one_unit(akv, w, cache, p, qs[0], stream) if extras else None
+    # the same inputs under the paper's codec and under the joint key/value ranking
+    variants = [measure_variant(akv, w, K, V, Q, qs[0], stream, **kw)
+                for kw in (dict(codec=1), dict(pool_kv_jointly=1))] if extras else None
     total_s = t1 - t0
     ms_per_step = total_s * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
@@ -345,8 +385,7 @@ def main():
         agg[name] = agg.get(name, 0.0) + ms
         cnt[name] = cnt.get(name, 0) + 1
     stage_ms = {k: agg[k] / cnt[k] for k in agg}           # average per launch
-    comp_stages = ["obs_stats", "ml_combine", "obs_score", "o_combine", "select", "assign", "obs_util", "util_fix",
-                   "topr", "quant"]
+    comp_stages = COMPRESS_STAGES
     dec_stages = ["dec_stream"]
     compress_ms = sum(stage_ms.get(k, 0.0) for k in comp_stages)
     decode_ms = sum(stage_ms.get(k, 0.0) for k in dec_stages)
@@ -396,6 +435,7 @@ def main():
         "stages_ms": stage_ms,
         "decode_tail": tail_rec,
         "decode_one_unit": unit_rec,
+        "variants": variants,
         "roofline": rl,
         # each main stage against its own roofline (the contraction of the
         # assignment also against the bf16 MFMA peak, whatever bounds it)
