@@ -1069,7 +1069,19 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
     g.tiles_per_block = tpb;
     g.nblk = (ntiles_hs + tpb - 1) / tpb;
   }
-  const unsigned grid = (unsigned)(hs * g.nblk);
+  g.xcd_groups = 0;
+  unsigned grid = (unsigned)(hs * g.nblk);
+  if (A > kAssignResMax) {
+    // anchors in parts reloaded every tile: the blocks of a (unit, side,
+    // head) run together on one XCD (32 compute units) so that the reloads
+    // hit its L2
+    const int nb = 32;
+    g.tiles_per_block = (ntiles_hs + nb - 1) / nb;
+    g.nblk = (ntiles_hs + g.tiles_per_block - 1) / g.tiles_per_block;
+    g.xcd_groups = (int)hs;
+    const int64_t rounds = (hs + 7) / 8;
+    grid = (unsigned)(rounds * 8 * g.nblk);
+  }
   g.a0 = 0; g.a1 = A;
   if (A <= kAssignResMax) {
     const size_t lds = assign_lds_bytes(A, waves);

@@ -66,6 +66,7 @@ struct AssignArgs {
   float* util;               // [U][2][H][N] (value side written here)
   int H, N, A, a0, a1;       // anchors [a0, a1) of this launch
   int tiles_per_block, nblk;  // token tiles per block, blocks per (unit, side, head)
+  int xcd_groups;             // > 0: XCD-grouped order (see k_assign_res), the number of (unit, side, head) groups
 };
 
 // Projection epilogue of one 16-token row block: lane (col, kg) holds
@@ -152,7 +153,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, kg = lane >> 4;
+  // Workgroups go to the eight XCDs in turn (workgroup b to XCD b mod 8).
+  // With xcd_groups > 0 the blocks of one (unit, side, head) all go to one
+  // XCD and run there together, so the anchor parts they reload tile after
+  // tile stay in that XCD's L2: XCD x takes groups x, x + 8, ... one after
+  // the other, nblk blocks each (nblk is one per compute unit of an XCD).
   int bid = blockIdx.x;
+  if (g.xcd_groups > 0) {
+    const int x = bid & 7, k = bid >> 3;
+    const int grp = x + 8 * (k / g.nblk);
+    if (grp >= g.xcd_groups) return;   // padding of the last round (whole block)
+    bid = grp * g.nblk + k % g.nblk;
+  }
   const int blk = bid % g.nblk; bid /= g.nblk;
   const int h = bid % g.H; bid /= g.H;
   const int side = bid % 2;
