@@ -70,7 +70,7 @@ typedef struct {
  * setting worth tuning": theta is the only knob a user is meant to turn).
  * Fill with anchorkv_params_default, then change fields as needed. */
 typedef struct {
-  float theta;             /* bytes per side kept: floor(theta*H*N*D*e) per unit (> 0) */
+  float theta;             /* bytes per side kept: floor(theta*H*N*D*e) per unit (0 < theta <= 1024) */
   int32_t window;          /* last `window` positions are always anchors (1 <= window <= n_tokens) */
   int32_t anchor_div;      /* non-window anchors k = floor(N / anchor_div), capped by the budget (>= 1; 128) */
   int32_t pool;            /* width of the positional pooling of the score (odd, 1..15; 7) */

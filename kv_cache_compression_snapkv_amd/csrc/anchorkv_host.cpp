@@ -180,7 +180,8 @@ static void params_default(anchorkv_params* q, float theta, int32_t window) {
 }
 
 static int check_params(const anchorkv_params& q) {
-  if (!(q.theta > 0.0f) || !std::isfinite(q.theta)) return fail(ANCHORKV_E_ARG, "anchorkv_plan: theta must be > 0");
+  if (!(q.theta > 0.0f) || !(q.theta <= 1024.0f))
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: theta must be in (0, 1024]");
   if (q.anchor_div < 1) return fail(ANCHORKV_E_ARG, "anchorkv_plan: anchor_div %d must be >= 1", q.anchor_div);
   if (!(q.rho >= 0.0 && q.rho <= 1.0)) return fail(ANCHORKV_E_ARG, "anchorkv_plan: rho must be in [0, 1]");
   if (q.pool < 1 || q.pool > kMaxPool || q.pool % 2 == 0)
@@ -228,7 +229,7 @@ static int plan_impl(const anchorkv_dims* d, const anchorkv_params* prm, anchork
   const double amax_d = std::floor((B - 4.0 * (double)N - 4.0 * (double)C - 128.0 / (double)H) / (double)(D * e + 2));
   if (amax_d < (double)W)
     return fail(ANCHORKV_E_BUDGET, "anchorkv_plan: theta %.6g cannot pay for %d window anchors and the pointers", th, window);
-  const int64_t A_max = (int64_t)amax_d;
+  const int64_t A_max = (int64_t)std::min(amax_d, (double)N);   // at most N anchors are ever usable
   const int64_t k_nw = std::max<int64_t>(0, std::min(std::min(N / prm->anchor_div, A_max - W), N - W));
   const int64_t k_s = std::min(k_nw, (int64_t)std::floor(prm->rho * (double)k_nw));
   const int64_t A = W + k_nw;

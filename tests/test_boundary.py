@@ -177,6 +177,10 @@ def test_params_defaults_and_range_checks(akv):
     q.reserved[2] = 1
     out = akv.PlanInfo()
     assert akv.lib().anchorkv_plan(ct.byref(d), ct.byref(q), ct.byref(out)) == -1
+    for theta in (0.0, -1.0, 2000.0, float("inf"), float("nan")):
+        with pytest.raises(E) as e:
+            akv.plan(1, 8, 4, 8192, 128, 32, akv.BF16, theta, 32)
+        assert e.value.code == -1, theta
 
 
 @pytest.mark.parametrize("kw", [dict(anchor_div=64), dict(rho=0.5), dict(pool=5), dict(pool=1), dict(pool=15),
