@@ -1126,32 +1126,53 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
-// Per (unit, head) with several token ranges (and an optional tail partial):
-// o = sum_s f_s acc_s / sum_s f_s l_s with f_s = 2^(m_s - max m).  One thread
-// per (q-head, coordinate).
-__global__ __launch_bounds__(256) void k_dec_merge(const float2* part_ml, const float* part_acc, const float2* tail_ml,
+// Per (unit, head, q-head) with several token ranges (and an optional tail
+// partial): o = sum_s f_s acc_s / sum_s f_s l_s with f_s = 2^(m_s - max m).
+// One block of 128 threads (one per coordinate) per q-head: the range
+// weights f_s are formed once in LDS, then every thread sums its coordinate
+// over the ranges in a fixed order with the loads issued together.
+constexpr int kMergeMax = 64 + 16;   // compressed ranges (<= 64) + tail ranges (<= 16)
+__global__ __launch_bounds__(128) void k_dec_merge(const float2* part_ml, const float* part_acc, const float2* tail_ml,
                                                   const float* tail_acc, float* o, int G, int S2, int St) {
-  const int64_t uh = blockIdx.x;
-  for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) {
-    const int g = i / kHeadDim, d = i % kHeadDim;
-    float M = -INFINITY;
-    for (int s = 0; s < S2; ++s) M = fmaxf(M, part_ml[(uh * S2 + s) * G + g].x);
-    for (int s = 0; s < St; ++s) M = fmaxf(M, tail_ml[(uh * St + s) * G + g].x);
-    float L = 0.0f, acc = 0.0f;
-    for (int s = 0; s < S2; ++s) {
+  __shared__ float fs[kMergeMax];
+  __shared__ float lsum;
+  const int64_t uhg = blockIdx.x;              // (unit, head) * G + q-head
+  const int64_t uh = uhg / G;
+  const int g = (int)(uhg % G);
+  const int d = threadIdx.x;
+  if (threadIdx.x < 64) {
+    // wave 0: maxima and weights of the S2 + St ranges
+    const int s = threadIdx.x;
+    float m = -INFINITY, l = 0.0f;
+    if (s < S2) {
       const float2 v = part_ml[(uh * S2 + s) * G + g];
-      const float f = v.x == -INFINITY ? 0.0f : exp2_fast(v.x - M);
-      L += f * v.y;
-      acc = fmaf(f, part_acc[((uh * S2 + s) * G + g) * kHeadDim + d], acc);
+      m = v.x; l = v.y;
     }
-    for (int s = 0; s < St; ++s) {
+    float mt = -INFINITY, lt = 0.0f;
+    if (s < St) {
       const float2 v = tail_ml[(uh * St + s) * G + g];
-      const float f = v.x == -INFINITY ? 0.0f : exp2_fast(v.x - M);
-      L += f * v.y;
-      acc = fmaf(f, tail_acc[((uh * St + s) * G + g) * kHeadDim + d], acc);
+      mt = v.x; lt = v.y;
     }
-    o[(uh * G + g) * kHeadDim + d] = acc / L;
+    const float M = wave_max(fmaxf(m, mt));
+    const float f = m == -INFINITY ? 0.0f : exp2_fast(m - M);
+    const float ft = mt == -INFINITY ? 0.0f : exp2_fast(mt - M);
+    if (s < S2) fs[s] = f;
+    if (s < St) fs[64 + s] = ft;
+    // the sum of f_s l_s in a fixed order (lane order, then the tail)
+    const float L = wave_sum(f * l) + wave_sum(ft * lt);
+    if (s == 0) lsum = L;
   }
+  __syncthreads();
+  float acc = 0.0f;
+  const float* pa = part_acc + (uh * S2 * G + g) * kHeadDim + d;
+#pragma unroll 8
+  for (int s = 0; s < S2; ++s) acc = fmaf(fs[s], pa[(int64_t)s * G * kHeadDim], acc);
+  if (St > 0) {
+    const float* ta = tail_acc + (uh * St * G + g) * kHeadDim + d;
+#pragma unroll 8
+    for (int s = 0; s < St; ++s) acc = fmaf(fs[64 + s], ta[(int64_t)s * G * kHeadDim], acc);
+  }
+  o[uhg * kHeadDim + d] = acc / lsum;
 }
 
 // One tail tile's loads: VPT value chunks of the thread, the lane's key-row quarter.
@@ -1456,13 +1477,13 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
       k_dec_tail<DT><<<(unsigned)((int64_t)U * H * w.St), 256, 0, st>>>(q, K_tail, V_tail, n_tail, tail_cap, G, w.St,
                                                                           a.c, tml, tacc);
     AKV_CHECK_LAUNCH("k_dec_tail");
-    k_dec_merge<<<(unsigned)((int64_t)U * H), 256, 0, st>>>(a.part_ml, a.part_acc, tml, tacc, o, G, S2, w.St);
+    k_dec_merge<<<(unsigned)((int64_t)U * H * G), kHeadDim, 0, st>>>(a.part_ml, a.part_acc, tml, tacc, o, G, S2, w.St);
     AKV_CHECK_LAUNCH("k_dec_merge");
     prof_mark(st, "dec_tail");
     return 0;
   }
   if (S2 > 1) {
-    k_dec_merge<<<(unsigned)((int64_t)U * H), 256, 0, st>>>(a.part_ml, a.part_acc, nullptr, nullptr, o, G, S2, 0);
+    k_dec_merge<<<(unsigned)((int64_t)U * H * G), kHeadDim, 0, st>>>(a.part_ml, a.part_acc, nullptr, nullptr, o, G, S2, 0);
     AKV_CHECK_LAUNCH("k_dec_merge");
   }
   prof_mark(st, "dec_stream");

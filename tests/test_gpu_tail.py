@@ -26,7 +26,10 @@ CASES = {
     "bf16_8b_short": SMALL["bf16_8b_short"],
     # eight q-heads per KV head (one 8-wave workgroup per CU in the stream kernel)
     "bf16_g8": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, n_dirs=16),
+    # the paper's codec (Hadamard rotation + Lloyd-Max), 8 q-heads, two units
+    "bf16_hlm_g8": W_["llama70b_128k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=2500, n_dirs=16),
 }
+PARAMS = {"bf16_hlm_g8": dict(codec=1)}
 TAILS = [0, 1, 37, 300, 600]
 
 
@@ -42,14 +45,15 @@ def akv():
     return m
 
 
-def packed_oracle_cache(akv, w, p):
+def packed_oracle_cache(akv, w, p, params=None):
     K, V, Q = make_inputs(w)
     K64, V64, Q64 = (kvsynth.to_f64(t) for t in (K, V, Q))
     code = 1 if w.dtype == "bf16" else 2
     cache_h = np.zeros(p.cache_bytes, dtype=np.uint8)
     comps = []
     for u in range(w.units):
-        c = O.compress_unit(K64[u], V64[u], Q64[u], w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes)
+        c = O.compress_unit(K64[u], V64[u], Q64[u], w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes,
+                            **(params or {}))
         comps.append(c)
         cache_h[u * p.unit_stride: u * p.unit_stride + p.unit_bytes] = np.frombuffer(
             akv.pack_unit(p, oracle_arrays(c, code)), np.uint8)
@@ -69,8 +73,9 @@ def tail_inputs(w, cap, seed):
 def test_decode_tail_parity(akv, name):
     w = CASES[name]
     _flush(f"[tail] {name}: U={w.units} H={w.kv_heads} G={w.q_per_kv} N={w.n_tokens} dtype={w.dtype}")
-    p = plan_for(akv, w)
-    cache, comps = packed_oracle_cache(akv, w, p)
+    prm = PARAMS.get(name, {})
+    p = plan_for(akv, w, prm)
+    cache, comps = packed_oracle_cache(akv, w, p, prm)
     _, _, dws = akv.alloc(p, "cuda")
     q = kvsynth.decode_queries(w, 0, device="cuda").contiguous()
     q64 = kvsynth.to_f64(q)
