@@ -585,15 +585,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   float zt[NB];        // value side: sum of p * zero for row (rb, col)
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) zt[rb] = 0.0f;
-  // Hadamard / Lloyd-Max value side: lane (col, kg) accumulates, in the
-  // rotated coordinates, q-head 4 (kg & 1) + r (the hi part for kg < 2, the lo
-  // part for kg >= 2) at coordinate col + 16 cc; zh sums p * sigma of q-head
-  // col (lanes col < 8)
-  float vh[HLM ? 8 : 1][4];
+  // Hadamard / Lloyd-Max value side: the value MFMA rows are the q-heads,
+  // q-head g on row 4 (g >> 1) + (g & 1), so that lane (col, kg) holds q-heads
+  // 2 kg and 2 kg + 1 (r = 0, 1) of coordinate col + 16 cc, in the rotated
+  // coordinates; zh sums p * sigma of the q-head of row col
+  float vh[HLM ? 8 : 1][2];
 #pragma unroll
   for (int cc = 0; cc < (HLM ? 8 : 1); ++cc)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vh[cc][r] = 0.0f;
+    for (int r = 0; r < 2; ++r) vh[cc][r] = 0.0f;
   float zh = 0.0f;
 
   // ---- key-residual logits (log2 units) of records b0 .. b0+15 of the
@@ -604,23 +604,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     if constexpr (HLM) {
       // sums over the codes (c-plane) and over their high bits (hi-plane)
       // of the rotated query, then the level polynomial and the record scale
-      bf16x8 afc[4], afh[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const Plane p0 = plane_of(2 * st), p1 = plane_of(2 * st + 1);
-        const int i0 = p0.sh / 6, i1 = p1.sh / 6;
-        afc[st] = u4_to_frag(and_or(xs[i0][0], MK[p0.m], vbias), and_or(xs[i0][1], MK[p0.m], vbias),
-                             and_or(xs[i1][0], MK[p1.m], vbias), and_or(xs[i1][1], MK[p1.m], vbias));
-        afh[st] = u4_to_frag(and_or(xs[i0][0], MKH[p0.m], vbias), and_or(xs[i0][1], MKH[p0.m], vbias),
-                             and_or(xs[i1][0], MKH[p1.m], vbias), and_or(xs[i1][1], MKH[p1.m], vbias));
-      }
       const float2 qc = qcs[lane];   // (sum of q' of q-head col & 7, initial accumulator of the column)
       f32x4 cacc = {qc.y, qc.y, qc.y, qc.y}, hacc = cacc;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
+        const Plane p0 = plane_of(2 * st), p1 = plane_of(2 * st + 1);
+        const int i0 = p0.sh / 6, i1 = p1.sh / 6;
         const bf16x8 bq = bits_to_frag(qbs[st][lane]);
-        cacc = M::mma(afc[st], bq, cacc);
-        hacc = M::mma(afh[st], bq, hacc);
+        cacc = M::mma(u4_to_frag(and_or(xs[i0][0], MK[p0.m], vbias), and_or(xs[i0][1], MK[p0.m], vbias),
+                                 and_or(xs[i1][0], MK[p1.m], vbias), and_or(xs[i1][1], MK[p1.m], vbias)),
+                      bq, cacc);
+        hacc = M::mma(u4_to_frag(and_or(xs[i0][0], MKH[p0.m], vbias), and_or(xs[i0][1], MKH[p0.m], vbias),
+                                 and_or(xs[i1][0], MKH[p1.m], vbias), and_or(xs[i1][1], MKH[p1.m], vbias)),
+                      bq, hacc);
       }
       const bool wr = col < G;   // column col (hi part) plus column col + 8 (lo part)
 #pragma unroll
@@ -667,29 +663,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // lane (col, kg) feeds records 4kg .. 4kg + 3 of the batch
   auto vbatch = [&](int b0, const uint32_t (&pr)[2], const uint32_t (&sz)[4]) {
     if constexpr (HLM) {
-      // rows (q-head col & 7, hi / lo part col >> 3) of A = p * sigma; B =
-      // the c-plane and the hi-plane of the codes; both start from the bias
-      // term -128 * (row sums of A)
-      const int g = col & 7, part = col >> 3;
+      // A = p * sigma as bf16 hi + lo (two MFMAs into one accumulator), rows
+      // 4 (g >> 1) + (g & 1) for q-head g, the other rows zero; B = the
+      // c-plane and the hi-plane of the codes; both start from the bias term
+      // -128 * (row sums of A)
+      const bool rowq = (col & 3) < 2;
+      const int g = 2 * (col >> 2) + (col & 1);
       float ps[4];
       float zs = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pv = g < G ? wrow[(b0 + 4 * kg + e) * BR + g] : 0.0f;
+        const float pv = (rowq && g < G) ? wrow[(b0 + 4 * kg + e) * BR + g] : 0.0f;
         ps[e] = pv * h2f((uint16_t)(sz[e] & 0xFFFFu));
         zs += ps[e];
       }
-      zh += part == 0 ? zs : 0.0f;
-      uint32_t ap[2];
+      zh += zs;
+      uint32_t hp[2], lp[2];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const uint32_t hb = bf16_pack(ps[2 * k], ps[2 * k + 1]);
-        const float d0 = ps[2 * k] - __uint_as_float(hb << 16);
-        const float d1 = ps[2 * k + 1] - __uint_as_float(hb & 0xFFFF0000u);
-        ap[k] = part ? bf16_pack(d0, d1) : hb;
+        hp[k] = hb;
+        lp[k] = bf16_pack(ps[2 * k] - __uint_as_float(hb << 16), ps[2 * k + 1] - __uint_as_float(hb & 0xFFFF0000u));
       }
-      const bf16x4 a4 = u2_to_frag4(ap[0], ap[1]);
-      const f32x4 zb = mma16k(a4, bm128_4, f32x4{0, 0, 0, 0});
+      const bf16x4 ah = u2_to_frag4(hp[0], hp[1]), al = u2_to_frag4(lp[0], lp[1]);
+      f32x4 zb = mma16k(ah, bm128_4, f32x4{0, 0, 0, 0});
+      zb = mma16k(al, bm128_4, zb);
       const uint32_t ps6[2] = {pr[0] >> 6, pr[1] >> 6};
       const uint32_t ps12[2] = {pr[0] >> 12, pr[1] >> 12};
 #pragma unroll
@@ -698,10 +696,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
         const uint32_t* src = pl.sh == 0 ? pr : pl.sh == 6 ? ps6 : ps12;
         const bf16x4 bc = u2_to_frag4(and_or(src[0], MK[pl.m], vbias), and_or(src[1], MK[pl.m], vbias));
         const bf16x4 bh = u2_to_frag4(and_or(src[0], MKH[pl.m], vbias), and_or(src[1], MKH[pl.m], vbias));
-        const f32x4 tc = mma16k(a4, bc, zb);
-        const f32x4 th = mma16k(a4, bh, zb);
+        f32x4 tc = mma16k(ah, bc, zb);
+        tc = mma16k(al, bc, tc);
+        f32x4 th = mma16k(ah, bh, zb);
+        th = mma16k(al, bh, th);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vh[cc][r] = fmaf(kLmAlpha, tc[r], fmaf(kLmBeta, th[r], vh[cc][r]));
+        for (int r = 0; r < 2; ++r) vh[cc][r] = fmaf(kLmAlpha, tc[r], fmaf(kLmBeta, th[r], vh[cc][r]));
       }
       return;
     }
@@ -884,17 +884,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
               wi[g * A + i] = (unsigned long long)__double2ll_rn((double)(long long)wi[g * A + i] * (double)fct[g]);
         if constexpr (HLM) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int g = 4 * (kg & 1) + r;
+          for (int r = 0; r < 2; ++r) {
+            const int g = 2 * kg + r;
             float f = 1.0f;
 #pragma unroll
             for (int gg = 0; gg < G; ++gg) f = (gg == g) ? fct[gg] : f;
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) vh[cc][r] *= f;
           }
+          const int gz = 2 * (col >> 2) + (col & 1);   // q-head of row col
           float fz = 1.0f;
 #pragma unroll
-          for (int gg = 0; gg < G; ++gg) fz = (gg == (col & 7)) ? fct[gg] : fz;
+          for (int gg = 0; gg < G; ++gg) fz = (gg == gz) ? fct[gg] : fz;
           zh *= fz;
         }
 #pragma unroll
@@ -1036,22 +1037,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   float* pz = reinterpret_cast<float*>(smb + L.pz);    // [NW][4 BR]: (q-head, group) = 4g + grp
   float* pl = reinterpret_cast<float*>(smb + L.pl);    // [NW][GP]
   if constexpr (HLM) {
-    // hi part (lanes kg < 2) plus lo part (lane + 32) of q-head 4 kg + r at
-    // coordinate col + 16 cc, in the rotated coordinates
+    // q-heads 2 kg + r (r = 0, 1) at coordinate col + 16 cc, in the rotated coordinates
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(vh[cc][r]), __float_as_uint(vh[cc][r]), false,
-                                                         false);
-        const float hs = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const int gq = 4 * kg + r;
-        if (kg < 2 && gq < G) pv[(wave * G + gq) * D + col + 16 * cc] = hs * kPlaneInv[plane_of(cc).m];
+      for (int r = 0; r < 2; ++r) {
+        const int gq = 2 * kg + r;
+        if (gq < G) pv[(wave * G + gq) * D + col + 16 * cc] = vh[cc][r] * kPlaneInv[plane_of(cc).m];
       }
     float z = zh;
     z += __shfl_xor(z, 16, 64);
     z += __shfl_xor(z, 32, 64);
-    if (kg == 0 && col < G) pz[wave * 4 * BR + col] = z;
+    const int gz = 2 * (col >> 2) + (col & 1);
+    if (kg == 0 && (col & 3) < 2 && gz < G) pz[wave * 4 * BR + gz] = z;
   }
 #pragma unroll
   for (int rb = 0; rb < (HLM ? 0 : NB); ++rb) {
