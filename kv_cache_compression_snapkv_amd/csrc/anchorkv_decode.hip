@@ -801,8 +801,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
     __builtin_amdgcn_wave_barrier();  // the wave's rows written before other lanes read them
 
-    // ---- logits of the lane's tokens; tile maximum when one passes m_run + kLazy
-    // (recomputed after the barrier rather than kept in registers across it)
+    // ---- logits of the lane's tokens (kept in registers across the barrier;
+    // recomputing them costs two LDS row reads per token, which at eight
+    // q-heads cost more than the registers); tile maximum when one passes
+    // m_run + kLazy
     auto logits = [&](int k, float (&s)[G]) {
       float Sv[GP], Rv[GP];
       ldsv<GP>(S + (wk[k] & 0x7FFF) * GP, Sv);
@@ -811,6 +813,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
       for (int g = 0; g < G; ++g) s[g] = valid[k] ? fmaf(gK, Sv[g], Rv[g]) : -INFINITY;
     };
+    float sk[TPL][G];
     {
       float mv[GP];
       ldsv<GP>(mrun, mv);
@@ -818,7 +821,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
       float smax[G];
 #pragma unroll
       for (int k = 0; k < TPL; ++k) {
-        float s[G];
+        float (&s)[G] = sk[k];
         logits(k, s);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -927,14 +930,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
       fast = fast && (!valid[k] || (gV >= 0.0f && gV < 8.0f));
     }
     fast = __all(fast);
-    // every token's logits are read from the rows before any value row is
+    // every token's logits were read from the rows before any value row is
     // written over them (the rows of key logits and of value weights are the
     // same wave-private rows)
     float pk[TPL][BR];
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
-      float s[G];
-      logits(k, s);
+      const float (&s)[G] = sk[k];
 #pragma unroll
       for (int g = 0; g < BR; ++g) pk[k][g] = 0.0f;
 #pragma unroll
