@@ -82,6 +82,11 @@ def run_workload(akv, w, step=0):
     return p, K, V, Q, cache, ws, q, o
 
 
+def plan_for_units(akv, w, units):
+    dt = akv.BF16 if w.dtype == "bf16" else akv.F32
+    return akv.plan(units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs, dt, w.theta, w.window)
+
+
 def unit_taps(akv, p, ws, u):
     offs = akv.workspace_offsets(p)
     U, H, N = p.units, p.H, p.N
@@ -329,5 +334,18 @@ def test_fullsize_sampled(akv, wname):
     _flush(f"[fullsize] {wname}: compressed and decoded; checking unit {w.units - 1}")
     rep = check_sampled_unit(akv, w, p, K, V, Q, cache, ws, q, o, w.units - 1)
     _flush(f"[fullsize] {wname}: {rep}")
+    # one unit per launch (the per-layer call): its plan splits every head into
+    # many more token ranges, merged by the range-merge kernel; the outputs
+    # equal those of the full-cache launch up to the order of the sums
+    p1 = plan_for_units(akv, w, 1)
+    assert p1.decode_splits > p.decode_splits
+    _, _, dws1 = akv.alloc(p1, "cuda")
+    o1 = torch.empty(1, w.kv_heads * w.q_per_kv, w.head_dim, dtype=torch.float32, device="cuda")
+    akv.decode_attn(p1, cache[:p1.cache_bytes], q[:1].contiguous(), o1, dws1)
+    torch.cuda.synchronize()
+    d = (torch.linalg.norm(o1[0] - o[0], dim=-1) / torch.linalg.norm(o[0], dim=-1)).max().item()
+    _flush(f"[fullsize] {wname}: one-unit launch ({p1.decode_splits} ranges per head) vs full launch "
+           f"({p.decode_splits}): {d:.3g}")
+    assert d <= 1e-5
     del K, V, Q, cache, ws
     torch.cuda.empty_cache()
