@@ -235,3 +235,40 @@ def test_save_restore_decodes_bitwise_identically(akv, tmp_path):
     akv.decode_attn(p2, restored, q, o2, dws2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+# decode instances for every q_per_kv the kernels are built for (1..8), both
+# codecs and both element types, on host-packed oracle caches: short contexts
+# with ragged tails, 8- and 16-wave workgroups (the 16-wave ones where the
+# weight tables of many anchors do not leave room for two workgroups per CU)
+DECODE_SHAPES = [(g, dt, codec, n_tok, window)
+                 for g in (1, 2, 3, 5, 6, 7)
+                 for dt, codec, n_tok, window in (("bf16", 0, 2600, 32), ("bf16", 1, 2100, 32),
+                                                  ("f32", 0, 1800, 16), ("f32", 1, 1300, 16))] + \
+                [(5, "bf16", 0, 9000, 800), (7, "bf16", 1, 9000, 800), (6, "f32", 0, 6000, 800)]
+
+
+@pytest.mark.parametrize("G,dt,codec,n_tok,window", DECODE_SHAPES)
+def test_decode_instances_on_packed_oracle_cache(akv, G, dt, codec, n_tok, window):
+    base = W_["llama8b_32k"] if dt == "bf16" else W_["tiny_f32"]
+    w = base.scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=G, n_tokens=n_tok, n_obs=16, window=window,
+                    theta=0.12 if window < 100 else 0.3, n_dirs=16)
+    prm = dict(codec=codec)
+    _flush(f"[decode-inst] G={G} {dt} codec={codec} N={n_tok} W={window}")
+    K, V, Q = make_inputs(w)
+    p = plan_for(akv, w, prm)
+    K64, V64, Q64 = (kvsynth.to_f64(t) for t in (K, V, Q))
+    c = O.compress_unit(K64[0], V64[0], Q64[0], G, w.n_obs, w.theta, w.window, w.elem_bytes, **prm)
+    assert c.flag.any()
+    cache_h = np.zeros(p.cache_bytes, dtype=np.uint8)
+    cache_h[:p.unit_bytes] = np.frombuffer(akv.pack_unit(p, oracle_arrays(c, 1 if dt == "bf16" else 2)), np.uint8)
+    cache = torch.from_numpy(cache_h).cuda()
+    _, _, dws = akv.alloc(p, "cuda")
+    for step in range(2):
+        q = kvsynth.decode_queries(w, step, device="cuda").contiguous()
+        o = torch.empty(1, 2 * G, w.head_dim, dtype=torch.float32, device="cuda")
+        akv.decode_attn(p, cache, q, o, dws)
+        torch.cuda.synchronize()
+        ref = O.decode_unit(c, kvsynth.to_f64(q)[0])
+        err = np.linalg.norm(o[0].cpu().numpy().astype(np.float64) - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        assert err.max() <= 1e-3, (step, err.max())
