@@ -61,6 +61,9 @@ SMALL = {
     "bf16_hlm_stress": W_["stress_64k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, theta=0.05),
     "f32_hlm": W_["tiny_f32"].scaled(n_tokens=1500),
     "bf16_hlm_joint": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=2500, n_obs=16, window=16),
+    # other query-group sizes through the whole path
+    "bf16_g6": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=6, n_tokens=2800, n_dirs=16),
+    "f32_g3": W_["tiny_f32"].scaled(kv_heads=2, q_per_kv=3, n_tokens=1400),
 }
 # non-default method parameters of some cases (anchorkv_params)
 PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40),
