@@ -1096,7 +1096,7 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
     }
   } else {
     // the parts are walked inside the kernel (tokens read once)
-    const size_t lds = assign_lds_bytes(kAssignResMax, 16, true);
+    const size_t lds = assign_lds_bytes(kAssignResMax, 16);
     static size_t done = 0;
     if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<true, 16>), lds, &done)) return rc;
     k_assign_res<true, 16><<<grid, 64 * 16, lds, st>>>(g);

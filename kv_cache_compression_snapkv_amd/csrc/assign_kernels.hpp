@@ -13,16 +13,17 @@
 // v_mfma_f32_16x16x32_bf16 on exact bf16 operands and is scaled by
 // 1/||x_a|| in f32.
 //
-// Argmax key: the bits of the scaled cosine with the 5 lowest mantissa bits
-// replaced by (31 - anchor block) (at most 32 blocks of 16 anchors per part),
-// compared as signed integers, so one v_max_i32 per element keeps both the
-// running maximum and (within a lane's column) the lowest anchor block on
-// ties.  A key differs from its value by less than 2^-18 relative, so two
-// anchors can only swap order when their cosines are closer than 2^-17
-// (7.6e-6) relative, which the tie rule of the method (top-2 margin below
-// 1e-5 relative) already excuses.  The 16 anchor columns of a token are then
-// reduced with a DPP row maximum; the lowest column holding it (a ballot and
-// a bit scan) wins equal keys.
+// Argmax key: the scaled cosine with its 5 lowest mantissa bits replaced by
+// a tag, the anchor's position among the 32 anchors a lane sees in an epoch
+// of 8 blocks (31 - position, so that among equal positive keys the earlier
+// anchor wins), compared as floats (v_max3_f32 orders negative values
+// correctly; the tag only decides between keys equal after masking).  A key
+// differs from its value by less than 2^-18 relative, so two anchors can only
+// swap order when their cosines are closer than 2^-17 (7.6e-6) relative,
+// which the tie rule of the method (top-2 margin below 1e-5 relative) already
+// excuses.  Each epoch's winner is compared with the token's best so far, and
+// the four lanes that share a token merge their bests at the end (larger
+// key, then lower index).
 //
 // Blocks of 8 waves run two per compute unit when the anchors of a part fit
 // twice in LDS (up to ~300 anchors), so that one block's loads (its anchors,
@@ -30,9 +31,8 @@
 // blocks, one per compute unit.
 //
 // Anchor sets larger than kAssignResMax are processed in parts inside the
-// kernel: every token tile walks the parts, keeping each token's best as a
-// 64-bit key (monotone cosine bits << 32 | ~index), so the tokens are read
-// once.
+// kernel: every token tile walks the parts with each token's best carried in
+// registers from part to part, so the tokens are read once.
 #pragma once
 
 #include "device_common.hpp"
@@ -44,11 +44,25 @@
 namespace akv {
 
 constexpr int kAssignSlot = 2 * 64 * 4;   // per-wave LDS bytes: token scalars of a 64-token tile
-// Dynamic LDS of a block with `waves` waves over `nA` anchors.
-// (multi: anchors in parts; a 64-bit running best per token of each wave)
-inline size_t assign_lds_bytes(int nA, int waves, bool multi = false) {
+// Dynamic LDS of a block with `waves` waves over `nA` anchors (one part).
+inline size_t assign_lds_bytes(int nA, int waves) {
   const size_t rows = (size_t)((nA + 15) / 16) * 16;
-  return rows * kHeadDim * 2 + rows * 8 + (size_t)waves * kAssignSlot + (multi ? (size_t)waves * 64 * 8 : 0);
+  return rows * kHeadDim * 2 + rows * 8 + (size_t)waves * kAssignSlot;
+}
+
+// max(a, b, c) of finite floats in one instruction (fmaxf on values made from
+// integer bits would first be canonicalised, one more instruction per input)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float d;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+// (v, a) <- the better of the two candidates (larger value, then lower index);
+// the candidates are this lane's and its partner's, in either order.
+__device__ __forceinline__ void take_better(float& v, int& a, float v0, int a0, float v1, int a1) {
+  const bool first = v0 > v1 || (v0 == v1 && a0 < a1);
+  v = first ? v0 : v1;
+  a = first ? a0 : a1;
 }
 
 struct AssignArgs {
@@ -138,11 +152,10 @@ __device__ __forceinline__ void assign_project(const AssignArgs& g, int u, int s
 __device__ __forceinline__ int res_phys(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 
 // MULTI: the anchors of the head exceed one LDS part (kAssignResMax); every
-// token tile walks all parts (each copied into LDS in turn, the tokens staying
-// in registers), keeping each token's best as a 64-bit key (monotone cosine
-// bits << 32 | ~anchor index: lowest index on equal keys); the projection
-// then reads the winning anchor row from the cache.  The tokens are read from
-// memory once, whatever the number of parts.
+// token tile walks all parts (each copied into LDS in turn, the tokens and
+// their running bests staying in registers); the projection then reads the
+// winning anchor row from the cache.  The tokens are read from memory once,
+// whatever the number of parts.
 template <bool MULTI, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
   constexpr int kTile = 64 * WAVES;   // tokens per block tile
@@ -177,14 +190,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
   uint4* As = dyn_lds;                                            // [nab*16 rows][16 chunks], swizzled
   float* inv_s = reinterpret_cast<float*>(As + nab_max * 16 * 16);  // [nab*16] 1/||x_a||
   float* na2_s = inv_s + nab_max * 16;                                // [nab*16] ||x_a||^2
-  // per wave: [64] anchor_of of its tokens (then the chosen anchor, bit 31 =
-  // anchor token), [64] observation scores
+  // per wave: [64] anchor_of of its tokens (>= 0: an anchor token), [64]
+  // observation scores
   int* selfs = reinterpret_cast<int*>(na2_s + nab_max * 16) + wave * (kAssignSlot / 4);
   float* scs = reinterpret_cast<float*>(selfs + 64);
-  // MULTI: [64] running best key of the wave's tokens
-  unsigned long long* runb = reinterpret_cast<unsigned long long*>(
-                                 reinterpret_cast<int*>(na2_s + nab_max * 16) + WAVES * (kAssignSlot / 4)) +
-                             wave * 64;
   const uint16_t* X = (side ? g.V : g.K) + uh * N * D;
   const uint16_t* AX = reinterpret_cast<const uint16_t*>(g.cache + (int64_t)u * g.stride +
                                                          (side ? g.off_anchor_v : g.off_anchor_k)) +
@@ -203,8 +212,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
     }
   };
   // anchors [a0, a1) into LDS (rows beyond a1 repeat the last one: padding
-  // rows copy the last anchor's row and 1/||x_a||, tie with it and lose on
-  // the column, so they never win)
+  // rows copy the last anchor's row and 1/||x_a|| and so tie with it)
   auto load_part = [&](int a0, int a1) {
     const int nA = a1 - a0, nab = (nA + 15) >> 4;
     for (int jj = wave; jj < nab * 4; jj += WAVES) {
@@ -227,41 +235,54 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
     __syncthreads();
   }
 
-  // Running maximum of the keys as signed integers: for non-negative
-  // cosines the float bits order like the values, so v_max_i32 needs no NaN
-  // canonicalisation.  A wave holding a token whose best key over the part's
-  // anchors is negative (every cosine <= 0, rare) redoes the search with
-  // sign-corrected keys; the test is on the token's row maximum, since a
-  // lane's own column sees only A/16 anchors and is often all negative.
-  // the mask lives in a VGPR so that (bits & mask) | tag is one v_and_or_b32
-  // (an empty asm makes the value opaque; the move itself is the compiler's,
-  // so its hazard checks see every instruction)
+  // (bits & keymask) | tag is one v_and_or_b32 with the mask in a VGPR (an
+  // empty asm makes the value opaque; the move itself is the compiler's, so
+  // its hazard checks see every instruction)
   unsigned keymask = 0xffffffe0u;
   __asm__ volatile("" : "+v"(keymask));
-  auto search = [&](const bf16x8 (&xt)[4][4], int (&best)[4][4], int nab, auto mono_tag) {
-    constexpr bool mono = decltype(mono_tag)::value;
-    for (int rb = 0; rb < 4; ++rb)
-      for (int r = 0; r < 4; ++r) best[rb][r] = INT_MIN;
-    auto mfmas = [&](int ab, f32x4 (&acc)[4]) {
-      for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0, 0, 0, 0};
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 bf = bits_to_frag(As[res_phys(ab * 16 + col, st * 4 + kg)]);
-        for (int rb = 0; rb < 4; ++rb) acc[rb] = M::mma(xt[rb][st], bf, acc[rb]);
-      }
-    };
-    auto keys = [&](int ab, const f32x4 (&acc)[4]) {
-      const float inv = inv_s[ab * 16 + col];
-      const unsigned tag = 31u - (unsigned)ab;
-      for (int rb = 0; rb < 4; ++rb)
-        for (int r = 0; r < 4; ++r) {
-          unsigned b = __float_as_uint(acc[rb][r] * inv);
-          if constexpr (mono) b ^= (unsigned)((int)b >> 31) & 0x7FFFFFFFu;
-          const int key = (int)((b & keymask) | tag);
-          best[rb][r] = max(best[rb][r], key);
+
+  // Anchors of one part: blocks of 16 anchors in epochs of 8 blocks.  The
+  // MFMA takes the anchors as its A operand and the tokens as B, so lane
+  // (col, kg) receives anchors ab*16 + kg*4 + r (r = 0..3) of token
+  // rb*16 + col: its four keys of a block all belong to one token and fold
+  // into that token's running key with two v_max3_f32.  At the end of an
+  // epoch the running key (masked value, tag = epoch position) is compared
+  // with the token's best so far (bv, bix) and restarted.
+  auto search_part = [&](int nab, int gab0, float (&bv)[4], int (&bix)[4]) {
+    for (int e = 0; e < nab; e += 8) {
+      float run[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j > 0 && e + j >= nab) break;
+        const int ab = e + j;
+        f32x4 acc[4];
+        for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0, 0, 0, 0};
+        for (int st = 0; st < 4; ++st) {
+          const bf16x8 af = bits_to_frag(As[res_phys(ab * 16 + col, st * 4 + kg)]);
+          for (int rb = 0; rb < 4; ++rb) acc[rb] = M::mma(af, xf[rb][st], acc[rb]);
         }
-    };
-    f32x4 acc0[4];
-    for (int ab = 0; ab < nab; ++ab) { mfmas(ab, acc0); keys(ab, acc0); }
+        const float4 inv = *reinterpret_cast<const float4*>(inv_s + ab * 16 + kg * 4);
+        const float iv[4] = {inv.x, inv.y, inv.z, inv.w};
+        for (int rb = 0; rb < 4; ++rb) {
+          float k[4];
+          for (int r = 0; r < 4; ++r)
+            k[r] = __uint_as_float((__float_as_uint(acc[rb][r] * iv[r]) & keymask) | (31u - (unsigned)(j * 4 + r)));
+          if (j == 0)
+            run[rb] = max3f(max3f(k[0], k[1], k[2]), k[3], k[3]);
+          else
+            run[rb] = max3f(max3f(run[rb], k[0], k[1]), k[2], k[3]);
+        }
+      }
+      const int ge = (gab0 + e) >> 3;   // global epoch of these blocks
+      for (int rb = 0; rb < 4; ++rb) {
+        const unsigned b = __float_as_uint(run[rb]);
+        const float m = __uint_as_float(b & keymask);
+        if (m > bv[rb]) {
+          bv[rb] = m;
+          bix[rb] = (ge << 5) | (int)(b & 31u);
+        }
+      }
+    }
   };
 
   for (int tile = tile0; tile < tile1; ++tile) {
@@ -272,85 +293,44 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
       dma4(g.anchor_of + uh * N + t, selfs);
       if (side) dma4(g.score + uh * N + t, scs);
     }
-    // MULTI: running best of each token (written by the lane that takes it)
-    if (MULTI) runb[lane] = 0ull;
+    float bv[4];
+    int bix[4];
+    for (int rb = 0; rb < 4; ++rb) { bv[rb] = -__builtin_inff(); bix[rb] = 0; }
     for (int part = 0; part < nparts; ++part) {
       const int a0 = part * pa, a1 = min(A, a0 + pa);
-      const int nab = (a1 - a0 + 15) >> 4;
       if (MULTI) {
         __syncthreads();          // every wave is done with the previous part
         load_part(a0, a1);
         __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));
         __syncthreads();
       }
-      int best[4][4];
-      int mk[4][4];   // row (token) maxima of the keys
-      auto row_maxima = [&]() {
-        for (int rb = 0; rb < 4; ++rb)
-          for (int r = 0; r < 4; ++r) mk[rb][r] = row_max_i32(best[rb][r]);
-      };
-      search(xf, best, nab, std::false_type{});
-      row_maxima();
-      bool neg = false;
-      for (int rb = 0; rb < 4; ++rb)
-        for (int r = 0; r < 4; ++r) neg |= mk[rb][r] < 0;
-      if (__builtin_amdgcn_ballot_w64(neg) != 0) {
-        search(xf, best, nab, std::true_type{});
-        row_maxima();
-      }
-      __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));   // this wave's copies of selfs / scs
-      // ---- reduce the 16 anchor columns of every token: row maximum of the
-      // keys, lowest column holding it; lanes col < 4 of row kg take token
-      // rb*16 + kg*4 + col
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        int wv[4];
-        for (int r = 0; r < 4; ++r) {
-          const int m = mk[rb][r];
-          const unsigned long long eq = __builtin_amdgcn_ballot_w64(best[rb][r] == m);
-          const unsigned bits = (unsigned)(eq >> (kg * 16)) & 0xFFFFu;   // never 0: the row holds its maximum
-          wv[r] = a0 + __builtin_ctz(bits) + 16 * (31 - (m & 31));
-        }
-        if (col < 4) {
-          if constexpr (MULTI) {
-            // (one static index per pass: a select over mk would become a
-            // private-memory array lookup)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (col == r) {
-                // signed-monotone key -> unsigned order, then ~index for lowest-index ties
-                const unsigned long long key64 =
-                    ((unsigned long long)(((unsigned)mk[rb][r] & keymask) ^ 0x80000000u) << 32) |
-                    (unsigned long long)(0xFFFFFFFFu - (unsigned)wv[r]);
-                const int tl = rb * 16 + kg * 4 + r;
-                runb[tl] = max(runb[tl], key64);
-              }
-            }
-          } else {
-            const int w = col == 0 ? wv[0] : col == 1 ? wv[1] : col == 2 ? wv[2] : wv[3];
-            const int tl = rb * 16 + kg * 4 + col;   // token of the wave's tile
-            const int self = selfs[tl];
-            selfs[tl] = self >= 0 ? (int)(0x80000000u | (unsigned)self) : w;
-          }
-        }
-      }
+      search_part((a1 - a0 + 15) >> 4, a0 >> 4, bv, bix);
     }
-    if constexpr (MULTI) {
-      // each token's entry was written by its own lane: one lane per token now
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
-      const int w = (int)(0xFFFFFFFFu - (unsigned)(runb[lane] & 0xFFFFFFFFull));
-      const int self = selfs[lane];
-      selfs[lane] = self >= 0 ? (int)(0x80000000u | (unsigned)self) : w;
+    // ---- each token's anchor: decode the lane's best (epoch, position),
+    // then the larger key over the four lanes of the token (kg = 0..3), the
+    // lower index on equal keys.  Rows past the last anchor repeat it; a tie
+    // with one of them can only decode past A - 1 and is clamped back.
+    int best_a[4];
+    for (int rb = 0; rb < 4; ++rb) {
+      const int li = 31 - (bix[rb] & 31);
+      int a = (((bix[rb] >> 5) << 3) + (li >> 2)) * 16 + kg * 4 + (li & 3);
+      a = min(a, A - 1);
+      float v = bv[rb];
+      const auto v32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      const auto a32 = __builtin_amdgcn_permlane32_swap((unsigned)a, (unsigned)a, false, false);
+      take_better(v, a, __uint_as_float(v32[0]), (int)a32[0], __uint_as_float(v32[1]), (int)a32[1]);
+      const auto v16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      const auto a16 = __builtin_amdgcn_permlane16_swap((unsigned)a, (unsigned)a, false, false);
+      take_better(v, a, __uint_as_float(v16[0]), (int)a16[0], __uint_as_float(v16[1]), (int)a16[1]);
+      best_a[rb] = a;
     }
-    // ---- projection of every token onto its anchor
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's selfs writes done
-    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));   // this wave's copies of selfs / scs
+    // ---- projection of every token onto its anchor (anchor tokens onto themselves)
     for (int rb = 0; rb < 4; ++rb) {
       const int t = tile * kTile + wave * 64 + rb * 16 + col;
-      const int sa = selfs[rb * 16 + col];
-      const bool is_anchor = sa < 0;
-      const int a = sa & 0x7FFFFFFF;
+      const int self = selfs[rb * 16 + col];
+      const bool is_anchor = self >= 0;
+      const int a = is_anchor ? self : best_a[rb];
       if constexpr (MULTI)
         assign_project(g, u, side, h, t, a, is_anchor, an[a].x, scs[rb * 16 + col], xf[rb],
                        [&](int c) { return *reinterpret_cast<const uint4*>(AX + (int64_t)a * D + c * 8); }, kg);
