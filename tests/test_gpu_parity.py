@@ -64,13 +64,24 @@ SMALL = {
     # other query-group sizes through the whole path
     "bf16_g6": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=6, n_tokens=2800, n_dirs=16),
     "f32_g3": W_["tiny_f32"].scaled(kv_heads=2, q_per_kv=3, n_tokens=1400),
+    # four anchors per head: many tokens have a negative cosine with every
+    # anchor, and the anchors fill a quarter of one 16-anchor block
+    "bf16_few_anchors": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=2, n_tokens=700, n_obs=4,
+                                               window=2, n_dirs=8),
+    # 529 anchors: a second part of 17 (one block with a single anchor)
+    "bf16_a529": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=2, n_tokens=2048, n_obs=16,
+                                        window=513, theta=0.5, n_dirs=8),
+    # 1040 anchors: three parts, the last one a single block
+    "bf16_a1040": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=2, n_tokens=3000, n_obs=16,
+                                         window=1017, theta=0.5, n_dirs=8),
 }
 # non-default method parameters of some cases (anchorkv_params)
 PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40),
           "bf16_joint": dict(pool_kv_jointly=1), "bf16_joint_stress": dict(pool_kv_jointly=1),
           "f32_joint": dict(pool_kv_jointly=1),
           "bf16_hlm": dict(codec=1), "bf16_hlm_g8": dict(codec=1), "bf16_hlm_stress": dict(codec=1),
-          "f32_hlm": dict(codec=1), "bf16_hlm_joint": dict(codec=1, pool_kv_jointly=1)}
+          "f32_hlm": dict(codec=1), "bf16_hlm_joint": dict(codec=1, pool_kv_jointly=1),
+          "bf16_few_anchors": dict(anchor_div=300)}
 
 
 def _flush(msg):
