@@ -599,7 +599,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   // ---- key-residual logits (log2 units) of records b0 .. b0+15 of the
   // wave's run, from the fragments (x, sz) into the wave's rows [b0, b0 + 16)
   // (row = rank)
-  auto kbatch = [&](int b0, int nk, uint2 x, const uint32_t (&sz)[4]) {
+  auto kbatch = [&](int b0, uint2 x, const uint32_t (&sz)[4]) {
     const uint32_t xs[3][2] = {{x.x, x.y}, {x.x >> 6, x.y >> 6}, {x.x >> 12, x.y >> 12}};
     if constexpr (HLM) {
       // sums over the codes (c-plane) and over their high bits (hi-plane)
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
         const float Hh = hacc[r] + dpp<kDppRor8>(hacc[r]);
         const float sg = h2f((uint16_t)(sz[r] & 0xFFFFu));
         const float val = sg * fmaf(kLmAlpha, C, fmaf(kLmBeta, Hh, -kLmL2 * qc.x));
-        if (wr && ii < nk) wrow[ii * BR + col] = val * a.c;
+        if (wr) wrow[ii * BR + col] = val * a.c;   // rows past the run: see below
       }
       return;
     }
@@ -648,13 +648,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
         if constexpr (QSPLIT) cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH + 1][lane]), cacc);
       }
       const int kap = 16 * cb + col, g = kap >> 2, grp = kap & 3;
-      const bool wr = grp == 0 && g < G;
+      // the four lanes of a quad hold the same sum and write the same value;
+      // rows past the run (ii >= nk, still below the wave's TT rows since the
+      // batch starts below nk) take values no one reads: key logits are read
+      // for ranks below nk only, and the value weights and zeros are written
+      // over every row the value batches read before they read it
+      const bool wr = g < G;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ii = b0 + 4 * kg + r;
         const float sc = h2f((uint16_t)(sz[r] & 0xFFFFu)), z = h2f((uint16_t)(sz[r] >> 16));
         const float val = quad_sum(fmaf(sc, cacc[r], z * qc.x));
-        if (wr && ii < nk) wrow[ii * BR + g] = val * a.c;
+        if (wr) wrow[ii * BR + g] = val * a.c;
       }
     }
   };
@@ -796,7 +801,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
       uint32_t sz[4] = {ksz[0], ksz[1], ksz[2], ksz[3]};
       for (int b0 = 0; b0 < nK; b0 += 16) {
         if (b0 > 0) load_keys(kb_cur + b0, nK - b0, x, sz);
-        kbatch(b0, nK, x, sz);
+        kbatch(b0, x, sz);
       }
     }
     __builtin_amdgcn_wave_barrier();  // the wave's rows written before other lanes read them
