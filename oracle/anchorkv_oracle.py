@@ -50,6 +50,9 @@ FP16_MAX = 65504.0
 CODEC_AFFINE = 0    # 2-bit group-affine residual codec (implementation contract)
 CODEC_HLM = 1       # the paper's codec: randomized Hadamard rotation + 4-level Lloyd-Max
 SIGN_SEED = 0x416E63686F724B56   # seed of the default rotation signs (reading R22)
+ANCHORS_UNIFORM = 0   # the non-scored anchors are stratified uniform picks (reading R5)
+ANCHORS_COVER = 1     # coverage-optimised picks: batched furthest-point sampling (reading R23)
+COVER_ROUNDS = 8      # rounds of the coverage picks (R = k_u is plain furthest-point sampling)
 
 
 # --------------------------------------------------------------------------
@@ -206,17 +209,73 @@ def anchor_score(P, W, pool=POOL):
     return score, pooled
 
 
-def select_anchors(pooled, N, W, k_s, k_u):
+def cover_rounds_of(k_u, rounds):
+    """Round sizes of the coverage picks: R = min(rounds, k_u) rounds, round r
+    takes floor(k_u (r+1) / R) - floor(k_u r / R) picks."""
+    R = max(1, min(rounds, k_u))
+    return [k_u * (r + 1) // R - k_u * r // R for r in range(R)] if k_u > 0 else []
+
+
+def cover_picks(X, base_pos, L, k_u, rounds=COVER_ROUNDS, picks_override=None):
+    """Coverage-optimised anchor picks [Pith, "Reading between the lines":
+    anchors placed for coverage, by k-means or furthest-point picks, in place
+    of the uniform ones], read as batched furthest-point sampling on the key
+    side (reading R23): starting from the anchors base_pos, round r adds the
+    b_r positions t < L that are not anchors yet with the lowest maximum signed
+    cosine to the current anchors (cosine_table: 0 where a norm is 0), ties to
+    the lower position.  With rounds >= k_u every round adds one position:
+    plain furthest-point sampling.
+
+    Returns (picks in round order, per-round margins): the margin of a round
+    is (m_(b+1) - m_(b)) / max(|m_(b+1)|, |m_(b)|) for the b-th and (b+1)-th
+    lowest maxima of that round (inf when no candidate is left out), the gap
+    the tie rule compares with 1e-5.
+    picks_override: the picks of another implementation in round order; each
+    round then continues from those (a parity test checks them first).
+    """
+    cur = [int(t) for t in base_pos]
+    picks, margins = [], []
+    k = 0
+    for b in cover_rounds_of(k_u, rounds):
+        c, _ = cosine_table(X[:L], X[np.asarray(cur, dtype=np.int64)])
+        mx = c.max(axis=1)
+        cand = np.ones(L, dtype=bool)
+        cur_a = np.asarray(cur, dtype=np.int64)
+        cand[cur_a[cur_a < L]] = False
+        pos = np.nonzero(cand)[0]
+        order = pos[np.lexsort((pos, mx[pos]))]         # by (max cosine, position)
+        new = order[:b]
+        if order.size > b:
+            m0, m1 = mx[order[b - 1]], mx[order[b]]
+            den = max(abs(m0), abs(m1))
+            margins.append((m1 - m0) / den if den > 0 else 0.0)
+        else:
+            margins.append(np.inf)
+        if picks_override is not None:
+            new = np.asarray(picks_override[k:k + b], dtype=np.int64)
+        k += b
+        picks.extend(int(t) for t in new)
+        cur.extend(int(t) for t in new)
+    return np.asarray(picks, dtype=np.int64), np.asarray(margins)
+
+
+def select_anchors(pooled, N, W, k_s, k_u, mode=ANCHORS_UNIFORM, X=None, rounds=COVER_ROUNDS, picks_override=None):
     """Anchor positions, ascending (reading R9: the anchor index is the rank).
 
     * window: the last W positions [Pith, "Assumptions & free parameters"];
     * scored: the k_s largest pooled scores, ties to the lower position;
     * uniform (reading R5): with c the remaining non-window positions in
-      ascending order (M of them), take c[floor((2i+1) * M / (2 k_u))], i < k_u.
+      ascending order (M of them), take c[floor((2i+1) * M / (2 k_u))], i < k_u;
+    * or, with mode ANCHORS_COVER, k_u coverage picks over the keys X
+      (cover_picks, starting from the scored and window anchors).
     """
     L = N - W
     order = np.lexsort((np.arange(L), -pooled))   # by (-pooled, position)
     scored = np.sort(order[:k_s])
+    if mode == ANCHORS_COVER:
+        base = np.concatenate([scored, np.arange(L, N)])
+        picks, _ = cover_picks(X, base, L, k_u, rounds, picks_override)
+        return np.sort(np.concatenate([base, picks])).astype(np.int64)
     taken = np.zeros(L, dtype=bool)
     taken[scored] = True
     rest = np.nonzero(~taken)[0]
@@ -526,7 +585,8 @@ class Compressed:
 def compress_unit(K, V, Q, G, n_obs, theta, W, e,
                   anchor_override=None, idx_override=None, flag_override=None,
                   anchor_div=ANCHOR_DIV, rho=RHO, pool=POOL, pool_kv_jointly=False,
-                  codec=CODEC_AFFINE, sign_words=None):
+                  codec=CODEC_AFFINE, sign_words=None, anchor_mode=ANCHORS_UNIFORM, cover_rounds=COVER_ROUNDS,
+                  picks_override=None):
     """K, V: [H, N, D] float64; Q: [H*G, n_obs, D] float64.
 
     anchor_div, rho, pool: the method's fixed parameters (see plan and
@@ -537,11 +597,14 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
     codec: CODEC_AFFINE (group-affine, scale and zero per 32 coordinates) or
     CODEC_HLM (randomized Hadamard rotation with the signs sign_words, the
     default ones when None, and the Lloyd-Max codebook; reading R22).
+    anchor_mode: ANCHORS_UNIFORM (stratified picks) or ANCHORS_COVER
+    (coverage picks over the keys in cover_rounds rounds, reading R23).
 
     The *_override arguments let a parity test continue from decisions the GPU
     took where the oracle's own decision was within the stated tie margin:
     anchor_override [H, A] positions, idx_override [2, H, N], flag_override
-    [2, H, N] bool.  The test checks the overrides before passing them.
+    [2, H, N] bool, picks_override [H] lists of coverage picks in round order.
+    The test checks the overrides before passing them.
     """
     H, N, D = K.shape
     p = plan(H, N, D, e, theta, W, anchor_div, rho, pool_kv_jointly, codec)
@@ -564,7 +627,8 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
         Ps.append(P)
         Os[h] = O
         score[h], pooled[h] = anchor_score(P, W, pool)
-        pos = select_anchors(pooled[h], N, W, p.k_s, p.k_u)
+        pos = select_anchors(pooled[h], N, W, p.k_s, p.k_u, anchor_mode, K[h], cover_rounds,
+                             None if picks_override is None else picks_override[h])
         if anchor_override is not None:
             pos = np.sort(np.asarray(anchor_override[h], dtype=np.int64))
         anchor_pos[h] = pos

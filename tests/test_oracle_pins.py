@@ -169,6 +169,98 @@ def test_select_anchors_bruteforce(seed):
     assert set(range(N - W, N)) <= set(pos.tolist())
 
 
+# ---------------------------------------------------------------- coverage-optimised anchors
+def _greedy_fps(X, base, L, k):
+    """Furthest-point sampling one pick at a time, written with explicit
+    loops: the candidate (t < L, not an anchor) whose largest cosine to the
+    current anchors is smallest, the lower position on ties."""
+    cur = list(base)
+    out = []
+    norm = [math.sqrt(float(np.dot(x, x))) for x in X]
+    for _ in range(k):
+        best_t, best_v = None, None
+        for t in range(L):
+            if t in cur:
+                continue
+            v = -math.inf
+            for a in cur:
+                den = norm[t] * norm[a]
+                c = float(np.dot(X[t], X[a])) / den if den > 0 else 0.0
+                v = max(v, c)
+            if best_v is None or v < best_v:
+                best_t, best_v = t, v
+        out.append(best_t)
+        cur.append(best_t)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_cover_picks_one_per_round_is_furthest_point_sampling(seed):
+    r = rng(40 + seed)
+    N, D, W = int(r.integers(20, 45)), 8, int(r.integers(1, 4))
+    X = r.standard_normal((N, D))
+    X[int(r.integers(0, N - W))] = 0.0            # a zero-norm token: cosine 0 with everything
+    L = N - W
+    base = sorted(set(r.integers(0, L, 3).tolist())) + list(range(L, N))
+    k = int(r.integers(1, 7))
+    picks, margins = O.cover_picks(X, np.array(base), L, k, rounds=k)
+    assert picks.tolist() == _greedy_fps(X, base, L, k)
+    assert margins.shape == (k,)
+
+
+def test_cover_picks_hand_worked():
+    # exact cosines: tokens (0,-1), (1,1), (-1,0), (0,1) and the window anchor
+    # (1,0).  The opposite token (-1,0) (cosine -1) comes first; then (0,-1)
+    # and (0,1) both have largest cosine 0 and the lower position wins the
+    # tie; (1,1) stays (largest cosine 1/sqrt(2)).
+    X = np.zeros((5, 4))
+    X[0, :2], X[1, :2], X[2, :2], X[3, :2], X[4, :2] = (0, -1), (1, 1), (-1, 0), (0, 1), (1, 0)
+    picks, margins = O.cover_picks(X, np.array([4]), 4, 2, rounds=2)
+    assert picks.tolist() == [2, 0]
+    assert margins[0] == 1.0 and margins[1] == 0.0   # a clear first pick, an exact tie second
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_cover_picks_rounds_and_invariants(seed):
+    r = rng(50 + seed)
+    N, D, W = 80, 16, 5
+    X = r.standard_normal((N, D))
+    L = N - W
+    base = list(range(0, L, 17)) + list(range(L, N))
+    for k, R in ((10, 8), (3, 8), (12, 5), (7, 1)):
+        sizes = O.cover_rounds_of(k, R)
+        assert sum(sizes) == k and len(sizes) == min(R, k) and min(sizes) >= 1
+        picks, margins = O.cover_picks(X, np.array(base), L, k, rounds=R)
+        assert len(picks) == k == len(set(picks.tolist()))
+        assert all(0 <= t < L and t not in base for t in picks.tolist())
+        assert margins.shape == (len(sizes),) and (margins >= 0).all()
+        # the first round's picks are the k-lowest maxima over the base set
+        c, _ = O.cosine_table(X[:L], X[np.array(base)])
+        mx = c.max(axis=1)
+        cand = [t for t in range(L) if t not in base]
+        first = sorted(cand, key=lambda t: (mx[t], t))[:sizes[0]]
+        assert picks[:sizes[0]].tolist() == first
+    # one round takes the k worst-covered candidates at once; k rounds are
+    # greedy furthest-point sampling, which re-evaluates after every pick
+    p1, _ = O.cover_picks(X, np.array(base), L, 6, rounds=1)
+    c, _ = O.cosine_table(X[:L], X[np.array(base)])
+    mx = c.max(axis=1)
+    assert p1.tolist() == sorted([t for t in range(L) if t not in base], key=lambda t: (mx[t], t))[:6]
+
+
+def test_select_anchors_cover_mode():
+    r = rng(60)
+    N, D, W, k_s, k_u = 70, 8, 4, 5, 6
+    X = r.standard_normal((N, D))
+    pooled = r.random(N - W)
+    pos = O.select_anchors(pooled, N, W, k_s, k_u, mode=O.ANCHORS_COVER, X=X, rounds=3)
+    scored = sorted(np.argsort(-pooled, kind="stable")[:k_s].tolist())
+    base = scored + list(range(N - W, N))
+    picks, _ = O.cover_picks(X, np.array(base), N - W, k_u, rounds=3)
+    assert pos.tolist() == sorted(base + picks.tolist())
+    assert len(set(pos.tolist())) == W + k_s + k_u
+
+
 # ---------------------------------------------------------------- assignment & projection
 def test_projection_hand_worked_example():
     g = json.load(open(os.path.join(GOLD, "projection_example.json")))
