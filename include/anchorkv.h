@@ -83,8 +83,23 @@ typedef struct {
                                  set means coordinate i is negated before the transform; the default is
                                  the first two SplitMix64 outputs from seed 0x416E63686F724B56, low word
                                  first (Steele, Lea and Flood 2014) */
-  int32_t reserved[3];     /* zero */
+  int32_t anchor_mode;     /* the k_uniform non-scored anchors: ANCHORKV_ANCHORS_UNIFORM (default) or
+                              ANCHORKV_ANCHORS_COVER */
+  int32_t cover_rounds;    /* ANCHORKV_ANCHORS_COVER: rounds of the picks (1..1024; 8); with
+                              cover_rounds >= k_uniform every round adds one anchor */
+  int32_t reserved[1];     /* zero */
 } anchorkv_params;
+
+/* How the non-scored anchors are picked.  UNIFORM: stratified over the
+ * positions left after the scored ones.  COVER: coverage-optimised (Pith
+ * review of AnchorKV, "Reading between the lines": anchors placed for
+ * coverage, by k-means or furthest-point picks), furthest-point sampling on
+ * the keys in cover_rounds batched rounds: starting from the scored and window
+ * anchors, round r adds the floor(k_u (r+1)/R) - floor(k_u r/R) non-window
+ * positions that are not anchors yet with the lowest largest signed cosine to
+ * the current anchors (0 where a norm is 0), the lower position on ties.
+ * Counts and layout do not depend on the mode; decode does not read it. */
+typedef enum { ANCHORKV_ANCHORS_UNIFORM = 0, ANCHORKV_ANCHORS_COVER = 1 } anchorkv_anchor_mode;
 
 /* Residual codecs.  AFFINE: 2-bit codes with an fp16 scale and zero per 32
  * coordinates (48-byte records at head_dim 128).  HADAMARD_LM, the paper's

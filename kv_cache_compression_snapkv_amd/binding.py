@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libanchorkv.so")
 
 BF16, F32 = 1, 2
 CODEC_AFFINE, CODEC_HADAMARD_LM = 0, 1
+ANCHORS_UNIFORM, ANCHORS_COVER = 0, 1
 
 ERRORS = {-1: "E_ARG", -2: "E_DTYPE", -3: "E_SHAPE", -4: "E_BUDGET", -5: "E_SMALL_BUFFER", -6: "E_HIP", -7: "E_LAYOUT"}
 
@@ -35,7 +36,8 @@ class Dims(ct.Structure):
 class Params(ct.Structure):
     _fields_ = [("theta", ct.c_float), ("window", ct.c_int32), ("anchor_div", ct.c_int32), ("pool", ct.c_int32),
                 ("rho", ct.c_double), ("group", ct.c_int32), ("pool_kv_jointly", ct.c_int32),
-                ("codec", ct.c_int32), ("hadamard_signs", ct.c_uint32 * 4), ("reserved", ct.c_int32 * 3)]
+                ("codec", ct.c_int32), ("hadamard_signs", ct.c_uint32 * 4), ("anchor_mode", ct.c_int32),
+                ("cover_rounds", ct.c_int32), ("reserved", ct.c_int32 * 1)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("reserved", "hadamard_signs")}
@@ -140,7 +142,8 @@ def version() -> str:
 def params(theta, window, **kw) -> Params:
     """The method's parameters: defaults (anchorkv_params_default) with the
     given theta and window, then any of anchor_div, rho, pool, group,
-    pool_kv_jointly, codec, hadamard_signs (four 32-bit words) replaced."""
+    pool_kv_jointly, codec, hadamard_signs (four 32-bit words), anchor_mode,
+    cover_rounds replaced."""
     q = Params()
     lib().anchorkv_params_default(ct.byref(q), ct.c_float(theta), int(window))
     for k, v in kw.items():
@@ -148,7 +151,7 @@ def params(theta, window, **kw) -> Params:
             for i, x in enumerate(v):
                 q.hadamard_signs[i] = int(x)
             continue
-        if k not in ("anchor_div", "rho", "pool", "group", "pool_kv_jointly", "codec"):
+        if k not in ("anchor_div", "rho", "pool", "group", "pool_kv_jointly", "codec", "anchor_mode", "cover_rounds"):
             raise TypeError(f"unknown parameter {k}")
         setattr(q, k, v)
     return q

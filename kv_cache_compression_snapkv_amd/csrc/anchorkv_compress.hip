@@ -158,6 +158,69 @@ __device__ void find_bucket(const unsigned* hist, int nbins, unsigned need, int*
   __syncthreads();
 }
 
+// The k positions t < L with the largest keys key(t) (ties to the lower
+// position), ascending into out[0..k): a 3-pass radix select over the 32-bit
+// keys (11 + 11 + 10 bits), then an ordered compaction in which each wave
+// walks one contiguous range of positions 64 at a time, ranks from ballots.
+// Whole block; key(t) is read once per pass and twice in the compaction.
+template <typename KeyF>
+__device__ void select_top(int L, int k, KeyF key, int* out, unsigned* hist, int* sh, int* s_b, unsigned* s_above) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  unsigned prefix = 0, need = (unsigned)k;
+  if (k > 0) {
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int p = 0; p < 3; ++p) {
+      for (int b = tid; b < kHistBins; b += nt) hist[b] = 0;
+      __syncthreads();
+      const unsigned hmask = p == 0 ? 0u : (0xFFFFFFFFu << (shifts[p] + widths[p]));
+      for (int t0 = 0; t0 < L; t0 += nt) {  // wave-uniform trip count
+        const int t = t0 + tid;
+        const unsigned kv = t < L ? key(t) : 0u;
+        hist_add_wave(hist, (kv >> shifts[p]) & ((1u << widths[p]) - 1), t < L && (kv & hmask) == (prefix & hmask));
+      }
+      __syncthreads();
+      if (tid == 0) { *s_b = 0; *s_above = 0; }
+      __syncthreads();
+      find_bucket(hist, 1 << widths[p], need, sh, s_b, s_above);
+      prefix = prefix | ((unsigned)*s_b << shifts[p]);
+      need = need - *s_above;
+      __syncthreads();
+    }
+  }
+  const unsigned T_key = prefix;
+  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  const int seg = (((L + nw - 1) / nw) + 63) & ~63;
+  const int s0 = min(L, wave * seg), s1 = min(L, s0 + seg);
+  int ng = 0, nti = 0;  // wave totals (uniform)
+  if (k > 0)
+    for (int t0 = s0; t0 < s1; t0 += 64) {
+      const int t = t0 + lane;
+      const unsigned kv = t < s1 ? key(t) : 0u;
+      ng += __popcll(__ballot(t < s1 && kv > T_key));
+      nti += __popcll(__ballot(t < s1 && kv == T_key));
+    }
+  int tot;
+  const int tie_pre = __builtin_amdgcn_readlane(block_excl_scan(lane == 0 ? nti : 0, sh, &tot), 0);
+  // selected in this range: all greater + ties while tie rank < need
+  const int take_ties = k > 0 ? max(0, min(nti, (int)need - tie_pre)) : 0;
+  const int sel_pre = __builtin_amdgcn_readlane(block_excl_scan(lane == 0 && k > 0 ? ng + take_ties : 0, sh, &tot), 0);
+  if (k > 0) {
+    int o = sel_pre, tr = tie_pre;
+    for (int t0 = s0; t0 < s1; t0 += 64) {
+      const int t = t0 + lane;
+      const unsigned kv = t < s1 ? key(t) : 0u;
+      const bool tie = t < s1 && kv == T_key;
+      const unsigned long long tm = __ballot(tie);
+      const bool sel = (t < s1 && kv > T_key) || (tie && tr + lanes_before(tm) < (int)need);
+      const unsigned long long sm = __ballot(sel);
+      if (sel) out[o + lanes_before(sm)] = t;
+      o += __popcll(sm);
+      tr += __popcll(tm);
+    }
+  }
+}
+
 // ---------------------------------------------------------- anchor selection
 constexpr int kSelectLdsMaxL = 32768;   // pooled score in LDS up to this many positions (128 KB)
 // One 1024-thread block per (unit, head).  score -> pooled (window sum of
@@ -171,7 +234,7 @@ template <int DT, bool LP>
 __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv, const float* score, float* pooled,
                                                  uint8_t* cache, int64_t stride, int64_t off_ak, int64_t off_av,
                                                  int64_t off_pos, int* anchor_of, float2* anorm, int H, int N, int W,
-                                                 int k_s, int k_u, int A, int pool) {
+                                                 int k_s, int k_u, int A, int pool, int mode, int* clist) {
   using T = typename Elem<DT>::T;
   constexpr int D = kHeadDim;
   __shared__ unsigned hist[kHistBins];
@@ -189,6 +252,9 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
   float* pl = LP ? plds : pooled + uh * N;
   const int tid = threadIdx.x, nt = blockDim.x;
 
+  // coverage anchors (mode 1, 2; see k_cover): the picks list of this head
+  int* cl = clist + uh * (int64_t)(k_s + k_u);
+  if (mode != 2) {
   // pooled_t = score_{t-hw} + ... + score_{t+hw} over [0, L), hw = pool/2
   // (zeros outside, added in position order)
   const int hw = pool >> 1;
@@ -234,64 +300,14 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
     }
   }
 
-  // radix select of the k_s-th largest key (keys = f32 bits of non-negative values)
-  unsigned prefix = 0, need = (unsigned)k_s;
-  if (k_s > 0) {
-    const int shifts[3] = {21, 10, 0};
-    const int widths[3] = {11, 11, 10};
-    for (int p = 0; p < 3; ++p) {
-      for (int b = tid; b < kHistBins; b += nt) hist[b] = 0;
-      __syncthreads();
-      const unsigned hmask = p == 0 ? 0u : (0xFFFFFFFFu << (shifts[p] + widths[p]));
-      for (int t0 = 0; t0 < L; t0 += nt) {  // wave-uniform trip count
-        const int t = t0 + tid;
-        const unsigned key = t < L ? __float_as_uint(pl[t]) : 0u;
-        hist_add_wave(hist, (key >> shifts[p]) & ((1u << widths[p]) - 1), t < L && (key & hmask) == (prefix & hmask));
-      }
-      __syncthreads();
-      if (tid == 0) { s_b = 0; s_above = 0; }
-      __syncthreads();
-      find_bucket(hist, 1 << widths[p], need, sh, &s_b, &s_above);
-      prefix = prefix | ((unsigned)s_b << shifts[p]);
-      need = need - s_above;
-      __syncthreads();
-    }
-  }
-  const unsigned T_key = prefix;
-  // ordered compaction of the scored set: each wave walks one contiguous range
-  // of positions 64 at a time, ranks from ballots
-  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
-  const int seg = (((L + nw - 1) / nw) + 63) & ~63;
-  const int s0 = min(L, wave * seg), s1 = min(L, s0 + seg);
-  int ng = 0, nti = 0;  // wave totals (uniform)
-  if (k_s > 0)
-    for (int t0 = s0; t0 < s1; t0 += 64) {
-      const int t = t0 + lane;
-      const unsigned key = t < s1 ? __float_as_uint(pl[t]) : 0u;
-      ng += __popcll(__ballot(t < s1 && key > T_key));
-      nti += __popcll(__ballot(t < s1 && key == T_key));
-    }
-  int tot;
-  const int tie_pre = __builtin_amdgcn_readlane(block_excl_scan(lane == 0 ? nti : 0, sh, &tot), 0);
-  // selected in this range: all greater + ties while tie rank < need
-  const int take_ties = k_s > 0 ? max(0, min(nti, (int)need - tie_pre)) : 0;
-  const int sel_pre =
-      __builtin_amdgcn_readlane(block_excl_scan(lane == 0 && k_s > 0 ? ng + take_ties : 0, sh, &tot), 0);
-  if (k_s > 0) {
-    int o = sel_pre, tr = tie_pre;
-    for (int t0 = s0; t0 < s1; t0 += 64) {
-      const int t = t0 + lane;
-      const unsigned key = t < s1 ? __float_as_uint(pl[t]) : 0u;
-      const bool tie = t < s1 && key == T_key;
-      const unsigned long long tm = __ballot(tie);
-      const bool sel = (t < s1 && key > T_key) || (tie && tr + lanes_before(tm) < (int)need);
-      const unsigned long long sm = __ballot(sel);
-      if (sel) s_pos[o + lanes_before(sm)] = t;
-      o += __popcll(sm);
-      tr += __popcll(tm);
-    }
-  }
+  // the k_s largest pooled scores (f32 bits of non-negative values), ties to
+  // the lower position, ascending into s_pos
+  select_top(L, k_s, [&](int t) { return __float_as_uint(pl[t]); }, s_pos, hist, sh, &s_b, &s_above);
   __syncthreads();
+  if (mode == 1) {   // scored positions only: the coverage picks follow (k_cover)
+    for (int i = tid; i < k_s; i += nt) cl[i] = s_pos[i];
+    return;
+  }
   // uniform picks: the c-th remaining position is c + j, j = first index with scored[j] - j > c
   const int M = L - k_s;
   for (int i = tid; i < k_u; i += nt) {
@@ -303,6 +319,19 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
     }
     s_pos[k_s + i] = (int)(c + lo);
   }
+  } else {
+    // mode 2: the scored positions (ascending) and the coverage picks (in
+    // round order, distinct) from the list; the picks go to s_pos[k_s..]
+    // ascending (rank = picks below)
+    for (int i = tid; i < k_s; i += nt) s_pos[i] = cl[i];
+    for (int i = tid; i < k_u; i += nt) {
+      const int v = cl[k_s + i];
+      int rank = 0;
+      for (int j = 0; j < k_u; ++j) rank += cl[k_s + j] < v ? 1 : 0;
+      s_pos[k_s + rank] = v;
+    }
+  }
+  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
   __syncthreads();
   // merge scored (sorted) and uniform (sorted) into anchor order (ranks by
   // binary search, then written over s_pos once every read is done), then the
@@ -384,6 +413,149 @@ __global__ __launch_bounds__(1024) void k_select(const void* Kv, const void* Vv,
       anorm[((int64_t)u * 2 * H + h) * A + i] = make_float2(sk, sk > 0.0f ? 1.0f / sqrtf(sk) : 0.0f);
       anorm[((int64_t)u * 2 * H + H + h) * A + i] = make_float2(sv, sv > 0.0f ? 1.0f / sqrtf(sv) : 0.0f);
     }
+  }
+}
+
+// ------------------------------------------------- coverage anchor picks
+// anchor_mode == ANCHORKV_ANCHORS_COVER (Pith review, "Reading between the
+// lines": anchors placed for coverage, by k-means or furthest-point picks, in
+// place of the uniform ones), read as furthest-point sampling on the keys in
+// batched rounds.  One 1024-thread block per (unit, head), between k_select's
+// first pass (scored positions into the list) and its second (final order,
+// anchor map, copies):
+//  * mc[t], t < L: largest signed cosine of key t to the scored and window
+//    anchors, on MFMA (anchor rows from the keys as the A operand, 16 tokens
+//    per row block as B), then +inf at the scored anchors;
+//  * each round: the b positions with the lowest mc, ties to the lower one
+//    (select_top on the complemented order-preserving bits), are appended to
+//    the list and get mc = +inf; mc then takes the maximum with their cosines
+//    (every round but the last).
+constexpr int kCoverMaxA = 4096;   // A <= 4096 is checked on the host
+
+__device__ __forceinline__ float frag_sq(float v) { return v * v; }
+__device__ __forceinline__ float frag_sq(bf16x8 v) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float f = (float)v[e];
+    s = fmaf(f, f, s);
+  }
+  return s;
+}
+// maximum over the four 16-lane rows (every lane gets it)
+__device__ __forceinline__ float max_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <int DT>
+__global__ __launch_bounds__(1024) void k_cover(const void* Kv, int* clist, float* mcb, int H, int N, int W, int k_s,
+                                                int k_u, int rounds) {
+  using T = typename Elem<DT>::T;
+  using MS = Mfma<DT>;
+  constexpr int D = kHeadDim;
+  constexpr int NST = D / MS::KSTEP;
+  constexpr int RB = DT == ANCHORKV_BF16 ? 2 : 1;   // 16-token row blocks per wave
+  constexpr int TW = 16 * RB;                       // tokens per wave
+  __shared__ unsigned hist[kHistBins];
+  __shared__ int sh[32];
+  __shared__ int s_b;
+  __shared__ unsigned s_above;
+  __shared__ int s_new[kCoverMaxA];     // the round's picks, ascending
+  __shared__ float s_inv[kCoverMaxA];   // 1/||x_a|| of the anchors being added (0 for a zero row)
+  const int h = blockIdx.x % H, u = blockIdx.x / H;
+  const int64_t uh = (int64_t)u * H + h;
+  const int L = N - W;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const T* X = reinterpret_cast<const T*>(Kv) + uh * (int64_t)N * D;
+  int* cl = clist + uh * (int64_t)(k_s + k_u);
+  float* mc = mcb + uh * (int64_t)N;
+
+  // mc[t] <- cosine to the na anchors at positions apos(i) (first), else the
+  // larger of mc[t] and that
+  auto update = [&](auto apos, int na, bool first) {
+    for (int i = tid; i < na; i += nt) {
+      const T* r = X + (int64_t)apos(i) * D;
+      float s2 = 0.0f;
+      for (int d = 0; d < D; ++d) {
+        const float v = Elem<DT>::f(r[d]);
+        s2 = fmaf(v, v, s2);
+      }
+      s_inv[i] = s2 > 0.0f ? 1.0f / sqrtf(s2) : 0.0f;
+    }
+    __syncthreads();
+    const int nab = (na + 15) >> 4;
+    for (int t0 = wave * TW; t0 < L; t0 += nw * TW) {   // wave-uniform
+      typename MS::frag xf[RB][NST];
+      float xx[RB], run[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int t = min(t0 + rb * 16 + col, L - 1);
+        xx[rb] = 0.0f;
+        run[rb] = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          xf[rb][st] = MS::load(X + (int64_t)t * D + st * MS::KSTEP + kg * MS::KW);
+          xx[rb] += frag_sq(xf[rb][st]);
+        }
+      }
+      for (int ab = 0; ab < nab; ++ab) {
+        // A operand: anchor row ab*16 + col (rows past the last anchor repeat it)
+        const T* arow = X + (int64_t)apos(min(ab * 16 + col, na - 1)) * D;
+        f32x4 acc[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const typename MS::frag af = MS::load(arow + st * MS::KSTEP + kg * MS::KW);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[rb] = MS::mma(af, xf[rb][st], acc[rb]);
+        }
+        // lane (col, kg) holds anchors ab*16 + kg*4 + r of token rb*16 + col
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float iv = s_inv[min(ab * 16 + kg * 4 + r, na - 1)];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) run[rb] = fmaxf(run[rb], acc[rb][r] * iv);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float x2 = sum_rows4(xx[rb]);
+        const float m = max_rows4(run[rb]);
+        const float c = x2 > 0.0f ? m / sqrtf(x2) : 0.0f;
+        const int t = t0 + rb * 16 + col;
+        if (kg == 0 && t < L) mc[t] = first ? c : fmaxf(mc[t], c);
+      }
+    }
+    __syncthreads();
+  };
+
+  // scored positions (ascending, from k_select's first pass), then the window
+  update([&](int i) { return i < k_s ? cl[i] : L + (i - k_s); }, k_s + W, true);
+  for (int i = tid; i < k_s; i += nt) mc[cl[i]] = INFINITY;
+  __syncthreads();
+  const int R = max(1, min(rounds, k_u));
+  int done = 0;
+  for (int r = 0; r < R && k_u > 0; ++r) {
+    const int b = (int)(((int64_t)k_u * (r + 1)) / R - ((int64_t)k_u * r) / R);
+    // the b lowest mc first: complement of the order-preserving bits
+    select_top(L, b, [&](int t) {
+      const unsigned x = __float_as_uint(mc[t]);
+      return ~((int)x < 0 ? ~x : (x | 0x80000000u));
+    }, s_new, hist, sh, &s_b, &s_above);
+    __syncthreads();
+    for (int i = tid; i < b; i += nt) {
+      cl[k_s + done + i] = s_new[i];
+      mc[s_new[i]] = INFINITY;
+    }
+    done += b;
+    __syncthreads();
+    if (r + 1 < R) update([&](int i) { return s_new[i]; }, b, false);
   }
 }
 
@@ -1167,18 +1339,30 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   {
     // pooled score in LDS while it fits next to the static arrays (~26 KB)
     const size_t plb = sizeof(float) * (size_t)(N - p.window);
-    auto sel = [&](auto kern, size_t dyn) {
+    const bool cover = p.params.anchor_mode == ANCHORKV_ANCHORS_COVER;
+    int* clist = reinterpret_cast<int*>(ws + w.cover_list);
+    auto sel = [&](auto kern, size_t dyn, int mode) {
       kern<<<(unsigned)(U * H), 1024, dyn, st>>>(
           K, V, a.score, reinterpret_cast<float*>(ws + w.pooled), cache, p.unit_stride, p.off_anchor_k,
           p.off_anchor_v, p.off_positions, reinterpret_cast<int*>(ws + w.anchor_of),
-          reinterpret_cast<float2*>(ws + w.anorm), H, N, p.window, p.k_scored, p.k_uniform, A, p.params.pool);
+          reinterpret_cast<float2*>(ws + w.anorm), H, N, p.window, p.k_scored, p.k_uniform, A, p.params.pool, mode,
+          clist);
     };
-    if (N - p.window <= kSelectLdsMaxL) {
-      static size_t sdone = 0;
-      if ((rc = set_dyn_lds(reinterpret_cast<const void*>(&k_select<DT, true>), plb, &sdone))) return rc;
-      sel(k_select<DT, true>, plb);
-    } else {
-      sel(k_select<DT, false>, 0);
+    // coverage anchors: scored positions (pass 1), the coverage picks, then
+    // the final order, map and copies (pass 2)
+    for (int pass = cover ? 1 : 0; pass <= (cover ? 2 : 0); ++pass) {
+      if (pass == 2) {
+        k_cover<DT><<<(unsigned)(U * H), 1024, 0, st>>>(K, clist, reinterpret_cast<float*>(ws + w.cover_mc), H, N,
+                                                        p.window, p.k_scored, p.k_uniform, p.params.cover_rounds);
+        AKV_CHECK_LAUNCH("k_cover");
+      }
+      if (N - p.window <= kSelectLdsMaxL) {
+        static size_t sdone = 0;
+        if ((rc = set_dyn_lds(reinterpret_cast<const void*>(&k_select<DT, true>), plb, &sdone))) return rc;
+        sel(k_select<DT, true>, plb, pass);
+      } else {
+        sel(k_select<DT, false>, 0, pass);
+      }
     }
   }
   AKV_CHECK_LAUNCH("k_select");

@@ -64,6 +64,9 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
   w.sel_list = take(4 * U * 2 * std::max<int64_t>(1, sel_stride(p)));
   w.sel_aux = take(8 * U * 2 * std::max<int64_t>(1, sel_stride(p)));
   w.sel_groups = take(8 * U * 2 * ((H * N + 1023) / 1024) + 8 * U * 2);
+  const bool cover = p.params.anchor_mode == ANCHORKV_ANCHORS_COVER;
+  w.cover_mc = take(cover ? 4 * U * H * N : 0);
+  w.cover_list = take(cover ? 4 * U * H * std::max<int64_t>(1, (int64_t)p.k_scored + p.k_uniform) : 0);
   w.total = off;
   return w;
 }
@@ -173,6 +176,8 @@ static void params_default(anchorkv_params* q, float theta, int32_t window) {
   q->group = kGroup;
   q->pool_kv_jointly = 0;
   q->codec = ANCHORKV_CODEC_AFFINE;
+  q->anchor_mode = ANCHORKV_ANCHORS_UNIFORM;
+  q->cover_rounds = 8;
   uint64_t st = kSignSeed;
   const uint64_t a = splitmix64(st), b = splitmix64(st);
   q->hadamard_signs[0] = (uint32_t)a; q->hadamard_signs[1] = (uint32_t)(a >> 32);
@@ -191,6 +196,10 @@ static int check_params(const anchorkv_params& q) {
     return fail(ANCHORKV_E_ARG, "anchorkv_plan: pool_kv_jointly %d must be 0 or 1", q.pool_kv_jointly);
   if (q.codec != ANCHORKV_CODEC_AFFINE && q.codec != ANCHORKV_CODEC_HADAMARD_LM)
     return fail(ANCHORKV_E_ARG, "anchorkv_plan: codec %d is not 0 (affine) or 1 (Hadamard / Lloyd-Max)", q.codec);
+  if (q.anchor_mode != ANCHORKV_ANCHORS_UNIFORM && q.anchor_mode != ANCHORKV_ANCHORS_COVER)
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: anchor_mode %d is not 0 (uniform) or 1 (coverage)", q.anchor_mode);
+  if (q.cover_rounds < 1 || q.cover_rounds > 1024)
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: cover_rounds %d must be in [1, 1024]", q.cover_rounds);
   for (int i = 0; i < (int)(sizeof(q.reserved) / sizeof(q.reserved[0])); ++i)
     if (q.reserved[i] != 0) return fail(ANCHORKV_E_ARG, "anchorkv_plan: reserved parameter fields must be zero");
   return 0;

@@ -64,6 +64,9 @@ struct CompressWs {
   int64_t sel_list; // int32 [U][2][Rmax] flat (head*N + t) in record order
   int64_t sel_aux;  // (int32 anchor index, f32 unrounded gamma) [U][2][Rmax] in record order
   int64_t sel_groups; // u32 [U][2][ceil(H*N/1024)][2] record / tie bases per 1024 positions, then [U][2][2] (T, need)
+  // coverage anchors only (params.anchor_mode == ANCHORKV_ANCHORS_COVER, else empty):
+  int64_t cover_mc;   // f32 [U][H][N] largest cosine of each position to the anchors so far (+inf: an anchor)
+  int64_t cover_list; // int32 [U][H][k_s + k_u] scored positions (ascending), then the picks in round order
   int64_t total;
 };
 CompressWs compress_ws_layout(const anchorkv_plan_info& p);

@@ -100,6 +100,56 @@ def check_anchor_set(pooled, gpu_pos, N, W, k_s, k_u):
     return False, "no tie-band explanation"
 
 
+def check_cover_set(X, pooled, gpu_pos, N, W, k_s, k_u, rounds):
+    """Coverage anchors of one head (reading R23): the GPU set must hold the
+    window, the scored set (the k_s largest pooled scores, inside the tie band
+    at the cut) and k_u picks that replay round by round: in each round the
+    GPU's picks are the b lowest largest-cosines among its remaining picks,
+    and no candidate left out has a largest cosine below the round's highest
+    pick by more than the tie margin (relative).  X: the head's keys.
+    Returns (ok, why)."""
+    L = N - W
+    g = np.sort(np.asarray(gpu_pos, dtype=np.int64))
+    if not np.array_equal(g[g >= L], np.arange(L, N)):
+        return False, "window"
+    nonw = g[g < L]
+    if nonw.size != k_s + k_u:
+        return False, "count"
+    order = np.lexsort((np.arange(L), -pooled))
+    scored = set(order[:k_s].tolist())
+    if k_s > 0 and not scored <= set(nonw.tolist()):
+        # scored decisions inside the tie band: the GPU's scored set is the
+        # k_s of its anchors with the largest pooled scores
+        cut = pooled[order[k_s - 1]]
+        miss = [t for t in scored if t not in set(nonw.tolist())]
+        if any(abs(pooled[t] - cut) > MARGIN * abs(cut) for t in miss):
+            return False, "scored set outside the tie band"
+        gs = nonw[np.lexsort((nonw, -pooled[nonw]))][:k_s]
+        scored = set(gs.tolist())
+    cur = sorted(scored) + list(range(L, N))
+    remaining = sorted(set(nonw.tolist()) - scored)
+    exact_rounds = True
+    for b in O.cover_rounds_of(k_u, rounds):
+        c, _ = O.cosine_table(X[:L], X[np.asarray(cur, dtype=np.int64)])
+        mx = c.max(axis=1)
+        rem = np.asarray(remaining, dtype=np.int64)
+        chosen = rem[np.lexsort((rem, mx[rem]))][:b]
+        top = mx[chosen].max()
+        cand = np.ones(L, dtype=bool)
+        cand[np.asarray([t for t in cur if t < L], dtype=np.int64)] = False
+        cand[chosen] = False
+        if cand.any():
+            low = mx[cand].min()
+            if low < top - MARGIN * max(abs(top), 1e-30):
+                return False, f"round pick above a left-out candidate ({top} vs {low})"
+        pos_c = np.nonzero(~np.isin(np.arange(L), np.asarray(cur)))[0]
+        want = pos_c[np.lexsort((pos_c, mx[pos_c]))][:b]
+        exact_rounds &= set(want.tolist()) == set(chosen.tolist())
+        cur += chosen.tolist()
+        remaining = [t for t in remaining if t not in set(chosen.tolist())]
+    return True, "exact" if exact_rounds else "tie-band"
+
+
 def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=None, report=None, params=None):
     """Compare one unit.  K, V, Q: float64 inputs; gpu: unpacked GPU arrays;
     taps: optional dict of GPU workspace arrays for this unit (score [H,N],
@@ -128,8 +178,13 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
         bad = np.nonzero(np.any(ga != want, axis=-1))
         assert bad[0].size == 0, f"side {s_}: {bad[0].size} stored anchor rows differ, first (head, idx) {bad[0][:3], bad[1][:3]}"
     exact = 0
+    cover = prm.get("anchor_mode", O.ANCHORS_UNIFORM) == O.ANCHORS_COVER
     for h in range(H):
-        ok, why = check_anchor_set(first.pooled[h], gpos[h], N, W, p.k_s, p.k_u)
+        if cover:
+            ok, why = check_cover_set(K[h], first.pooled[h], gpos[h], N, W, p.k_s, p.k_u,
+                                      prm.get("cover_rounds", O.COVER_ROUNDS))
+        else:
+            ok, why = check_anchor_set(first.pooled[h], gpos[h], N, W, p.k_s, p.k_u)
         assert ok, f"anchor set head {h}: {why}"
         exact += why == "exact"
     rep["anchor_heads_exact"] = exact

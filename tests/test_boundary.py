@@ -166,15 +166,23 @@ def test_params_defaults_and_range_checks(akv):
     # the default rotation signs are the oracle's SplitMix64 words (each side
     # implements the generator from its published definition)
     assert list(q.hadamard_signs) == O.default_sign_words()
+    assert (q.anchor_mode, q.cover_rounds) == (O.ANCHORS_UNIFORM, O.COVER_ROUNDS)
+    # the anchor mode changes neither counts nor layout, only the workspace
+    pu = akv.plan(2, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32)
+    pc = akv.plan(2, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32, anchor_mode=akv.ANCHORS_COVER, cover_rounds=3)
+    for f in ("A", "k_scored", "k_uniform", "R_K", "R_V", "unit_bytes", "cache_bytes", "off_words"):
+        assert getattr(pu, f) == getattr(pc, f), f
+    assert pc.compress_workspace_bytes >= pu.compress_workspace_bytes + 4 * 2 * 8 * 8192
     E = akv.AnchorKVError
     for kw in (dict(pool=6), dict(pool=17), dict(pool=0), dict(group=64), dict(pool_kv_jointly=2),
-               dict(rho=-0.1), dict(rho=1.5), dict(anchor_div=0), dict(codec=2), dict(codec=-1)):
+               dict(rho=-0.1), dict(rho=1.5), dict(anchor_div=0), dict(codec=2), dict(codec=-1),
+               dict(anchor_mode=2), dict(anchor_mode=-1), dict(cover_rounds=0), dict(cover_rounds=1025)):
         with pytest.raises(E) as e:
             akv.plan(1, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32, **kw)
         assert e.value.code == -1, kw
     d = akv.binding.Dims(1, 8, 4, 8192, 128, 32, akv.BF16)
     q = akv.params(0.1, 32)
-    q.reserved[2] = 1
+    q.reserved[0] = 1
     out = akv.PlanInfo()
     assert akv.lib().anchorkv_plan(ct.byref(d), ct.byref(q), ct.byref(out)) == -1
     for theta in (0.0, -1.0, 2000.0, float("inf"), float("nan")):

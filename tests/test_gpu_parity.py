@@ -74,6 +74,12 @@ SMALL = {
     # 1040 anchors: three parts, the last one a single block
     "bf16_a1040": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=2, n_tokens=3000, n_obs=16,
                                          window=1017, theta=0.5, n_dirs=8),
+    # coverage-optimised anchors (furthest-point picks in batched rounds)
+    "bf16_cover": W_["llama8b_32k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=3000, n_dirs=32),
+    "f32_cover": W_["tiny_f32"].scaled(n_tokens=1500),
+    "bf16_cover_fps": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=2, n_tokens=2500, n_obs=16,
+                                             window=16, n_dirs=8),
+    "bf16_cover_g8": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=4500, theta=0.08),
 }
 # non-default method parameters of some cases (anchorkv_params)
 PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40),
@@ -81,7 +87,11 @@ PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dic
           "f32_joint": dict(pool_kv_jointly=1),
           "bf16_hlm": dict(codec=1), "bf16_hlm_g8": dict(codec=1), "bf16_hlm_stress": dict(codec=1),
           "f32_hlm": dict(codec=1), "bf16_hlm_joint": dict(codec=1, pool_kv_jointly=1),
-          "bf16_few_anchors": dict(anchor_div=300)}
+          "bf16_few_anchors": dict(anchor_div=300),
+          "bf16_cover": dict(anchor_mode=1, cover_rounds=4), "f32_cover": dict(anchor_mode=1, cover_rounds=3),
+          # one pick per round: plain furthest-point sampling
+          "bf16_cover_fps": dict(anchor_mode=1, cover_rounds=1024, anchor_div=100),
+          "bf16_cover_g8": dict(anchor_mode=1)}
 
 
 def _flush(msg):

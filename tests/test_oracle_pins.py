@@ -920,3 +920,25 @@ def test_hlm_compress_reconstruct_and_decode():
         ref = torch.nn.functional.scaled_dot_product_attention(
             torch.from_numpy(q[h * G:(h + 1) * G])[None], torch.from_numpy(Ki[h])[None], torch.from_numpy(Vi[h])[None])
         np.testing.assert_allclose(o[h * G:(h + 1) * G], ref[0].numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_cover_set_check_accepts_the_oracle_and_rejects_a_swap():
+    # the parity helper's round replay: the oracle's own coverage set passes
+    # as exact; swapping a pick for a well-covered token fails
+    from tests.parity import check_cover_set
+    r = rng(70)
+    N, D, W, k_s, k_u, R = 90, 16, 6, 6, 8, 3
+    X = r.standard_normal((N, D))
+    pooled = r.random(N - W)
+    pos = O.select_anchors(pooled, N, W, k_s, k_u, mode=O.ANCHORS_COVER, X=X, rounds=R)
+    ok, why = check_cover_set(X, pooled, pos, N, W, k_s, k_u, R)
+    assert ok and why == "exact", why
+    scored = set(np.argsort(-pooled, kind="stable")[:k_s].tolist())
+    picks = [t for t in pos.tolist() if t < N - W and t not in scored]
+    c, _ = O.cosine_table(X[:N - W], X[pos])
+    mx = c.max(axis=1)
+    outside = [t for t in range(N - W) if t not in set(pos.tolist())]
+    best_covered = max(outside, key=lambda t: mx[t])
+    bad = np.sort(np.array([t for t in pos.tolist() if t != picks[0]] + [best_covered]))
+    ok, why = check_cover_set(X, pooled, bad, N, W, k_s, k_u, R)
+    assert not ok, why
