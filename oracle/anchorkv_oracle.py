@@ -24,7 +24,8 @@ zero per 32 contiguous coordinates (residual records of D/4 + D/8 bytes); the
 paper's codec (randomized Hadamard rotation + 4-level Lloyd-Max, one fp16
 scale per residual, records of D/4 + 4 bytes) is the alternative; anchors cost
 D*e bytes, pointers 4 bytes (2-byte index + 2-byte fp16 coefficient); decode
-logits are gamma * <q, k_anchor> + <q, r~> with no RoPE.
+logits are gamma * <q, k_anchor> + <q, r~> with no RoPE by default, and with
+pre-RoPE key storage (rope_theta given) <q, R_t(gamma k_anchor + r~)>.
 
 Parity status: every function here is pinned by tests under tests/ (library
 routines, closed forms, brute force, finite differences, invariants), except
@@ -53,6 +54,7 @@ SIGN_SEED = 0x416E63686F724B56   # seed of the default rotation signs (reading R
 ANCHORS_UNIFORM = 0   # the non-scored anchors are stratified uniform picks (reading R5)
 ANCHORS_COVER = 1     # coverage-optimised picks: batched furthest-point sampling (reading R23)
 COVER_ROUNDS = 8      # rounds of the coverage picks (R = k_u is plain furthest-point sampling)
+ROPE_THETA = 500000.0  # default base of the rotary embedding with pre-RoPE keys (reading R24)
 
 
 # --------------------------------------------------------------------------
@@ -554,6 +556,34 @@ def hlm_code_margin(r, sigma, words):
 
 
 # --------------------------------------------------------------------------
+# Pre-RoPE key storage [Pith, "Assumptions & free parameters" (RoPE is a
+# per-position orthogonal linear map R_t, so R_t K_t = R_t K~_t + R_t r_t and
+# ||R_t r_t|| = ||r_t||, which justifies storing keys before the rotation and
+# rotating at decode time) and "Referee Report" (pre-RoPE key storage with
+# RoPE distributing over the decomposition)].  The pages fix neither the
+# pairing nor the frequencies; reading R24: the rotate-half pairing of the
+# Llama models the pages evaluate, coordinates i and i + D/2 turned by the
+# angle t * theta_i with theta_i = base^(-2i/D), the key at position t.
+# --------------------------------------------------------------------------
+def rope_freqs(D, base):
+    """theta_i = base^(-2i/D) for i < D/2 (reading R24)."""
+    i = np.arange(D // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / D)
+
+
+def rope(X, base, positions=None):
+    """R_t X_t for rows X [N, D] at positions (default 0..N-1): coordinate
+    pairs (i, i + D/2) rotated by t * theta_i (reading R24)."""
+    N, D = X.shape
+    pos = np.arange(N, dtype=np.float64) if positions is None else np.asarray(positions, dtype=np.float64)
+    ang = pos[:, None] * rope_freqs(D, base)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    h = D // 2
+    x0, x1 = X[:, :h], X[:, h:]
+    return np.concatenate([x0 * c - x1 * s, x0 * s + x1 * c], axis=1)
+
+
+# --------------------------------------------------------------------------
 # The whole compression pass of one unit [Pith, "What carries the argument";
 # Velox, "Adaptation notes" (one-shot compression at the end of prefill)].
 # --------------------------------------------------------------------------
@@ -580,13 +610,14 @@ class Compressed:
     codec: int = CODEC_AFFINE
     sigma: np.ndarray = None      # [2, H, N] fp16 scale of the Hadamard / Lloyd-Max codec
     sign_words: tuple = None      # rotation signs of that codec
+    rope_theta: float = None      # pre-RoPE keys: the rotary base (None: keys attended as stored)
 
 
 def compress_unit(K, V, Q, G, n_obs, theta, W, e,
                   anchor_override=None, idx_override=None, flag_override=None,
                   anchor_div=ANCHOR_DIV, rho=RHO, pool=POOL, pool_kv_jointly=False,
                   codec=CODEC_AFFINE, sign_words=None, anchor_mode=ANCHORS_UNIFORM, cover_rounds=COVER_ROUNDS,
-                  picks_override=None):
+                  picks_override=None, rope_theta=None):
     """K, V: [H, N, D] float64; Q: [H*G, n_obs, D] float64.
 
     anchor_div, rho, pool: the method's fixed parameters (see plan and
@@ -599,6 +630,12 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
     default ones when None, and the Lloyd-Max codebook; reading R22).
     anchor_mode: ANCHORS_UNIFORM (stratified picks) or ANCHORS_COVER
     (coverage picks over the keys in cover_rounds rounds, reading R23).
+    rope_theta: None, or the rotary base when K holds pre-RoPE keys (reading
+    R25): the observation-window attention (and with it the score, p and o)
+    sees the rotated keys R_t K_t, and the key channel of the utility the
+    rotated residual R_t r_t of each token at its own position; the anchors,
+    the nearest-anchor assignment, gamma, the residuals and their codes stay
+    in the stored (pre-RoPE) space.
 
     The *_override arguments let a parity test continue from decisions the GPU
     took where the oracle's own decision was within the stated tie margin:
@@ -623,7 +660,8 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
     Ps, Os = [], np.zeros((H, GQ, D))
     for h in range(H):
         Qh = Q[h * G:(h + 1) * G].reshape(GQ, D)
-        P, O = obs_attention(Qh, K[h], V[h], n_obs)
+        Ka = K[h] if rope_theta is None else rope(K[h], rope_theta)
+        P, O = obs_attention(Qh, Ka, V[h], n_obs)
         Ps.append(P)
         Os[h] = O
         score[h], pooled[h] = anchor_score(P, W, pool)
@@ -638,7 +676,8 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
             idx[s, h], gamma[s, h], gamma16[s, h] = a["idx"], a["gamma"], a["gamma16"]
             resid[s, h], margin[s, h] = a["r"], a["margin"]
             eligible[h] = ~a["is_anchor"]
-        u[0, h], u[1, h] = utilities(P, O, Qh, V[h], resid[0, h], resid[1, h], eligible[h])
+        rK = resid[0, h] if rope_theta is None else rope(resid[0, h], rope_theta)
+        u[0, h], u[1, h] = utilities(P, O, Qh, V[h], rK, resid[1, h], eligible[h])
     flag = np.zeros((2, H, N), dtype=bool)
     if p.joint:
         # the stacked (side, head) rows rank by (-u, side, head, position)
@@ -661,12 +700,13 @@ def compress_unit(K, V, Q, G, n_obs, theta, W, e,
     codes = np.where(flag[..., None], codes, 0).astype(np.uint8)
     anchors = np.stack([K[np.arange(H)[:, None], anchor_pos], V[np.arange(H)[:, None], anchor_pos]])
     return Compressed(p, G, anchor_pos, idx, gamma, gamma16, resid, flag, codes, sc, ze,
-                      anchors, score, pooled, Ps, Os, u, margin, codec, sigma, words)
+                      anchors, score, pooled, Ps, Os, u, margin, codec, sigma, words, rope_theta)
 
 
 def reconstruct(c: Compressed):
     """K^, V^ [H, N, D]: fp16(gamma) * x_a + [flag] * dequantised residual
-    [Pith, "What carries the argument"], with the cache's codec."""
+    [Pith, "What carries the argument"], with the cache's codec, in the stored
+    space (pre-RoPE keys when c.rope_theta is set; see attended_keys)."""
     out = []
     H = c.anchor_pos.shape[0]
     for s in range(2):
@@ -688,10 +728,20 @@ def attention(q, K, V):
     return (p @ V) / p.sum(axis=-1, keepdims=True)
 
 
+def attended_keys(c: Compressed, Kh):
+    """The keys decode attends to: the reconstruction itself, or with pre-RoPE
+    storage R_t K^_t at each token's position (reading R26)."""
+    if c.rope_theta is None:
+        return Kh
+    return np.stack([rope(Kh[h], c.rope_theta) for h in range(Kh.shape[0])])
+
+
 def decode_unit(c: Compressed, q):
     """Decode attention over the compressed cache of one unit.
-    q: [H*G, D] float64; q-head h*G + g reads KV head h.  Returns o [H*G, D]."""
+    q: [H*G, D] float64 (post-RoPE when the keys are stored pre-RoPE); q-head
+    h*G + g reads KV head h.  Returns o [H*G, D]."""
     Kh, Vh = reconstruct(c)
+    Kh = attended_keys(c, Kh)
     H = Kh.shape[0]
     G = c.G
     o = np.zeros_like(q)
@@ -706,8 +756,11 @@ def decode_unit_tail(c: Compressed, q, K_tail, V_tail):
     (AnchorKV-adapted page, "Adaptation notes": tokens produced during decode
     are appended at full precision and never re-anchored).  One softmax per
     q-head over the N reconstructed tokens and the tail of its KV head.
-    q: [H*G, D]; K_tail, V_tail: [H, T, D] float64, T >= 0.  Returns o [H*G, D]."""
+    q: [H*G, D]; K_tail, V_tail: [H, T, D] float64, T >= 0, tail keys attended
+    as given (already rotated with pre-RoPE storage, reading R27).
+    Returns o [H*G, D]."""
     Kh, Vh = reconstruct(c)
+    Kh = attended_keys(c, Kh)
     H = Kh.shape[0]
     G = c.G
     o = np.zeros_like(q)

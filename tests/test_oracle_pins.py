@@ -942,3 +942,200 @@ def test_cover_set_check_accepts_the_oracle_and_rejects_a_swap():
     bad = np.sort(np.array([t for t in pos.tolist() if t != picks[0]] + [best_covered]))
     ok, why = check_cover_set(X, pooled, bad, N, W, k_s, k_u, R)
     assert not ok, why
+
+
+# ---------------------------------------------------------------- pre-RoPE key storage
+def _rot_complex(X, base, positions):
+    """R_t X_t through complex numbers: coordinate pair (i, i + D/2) as
+    z = x_i + 1j x_{i+D/2}, turned by exp(1j t base^(-2i/D)) (a route
+    independent of the oracle's cos/sin form)."""
+    N, D = X.shape
+    h = D // 2
+    z = X[:, :h] + 1j * X[:, h:]
+    w = np.exp(-(2.0 * np.arange(h) / D) * math.log(base))
+    z = z * np.exp(1j * np.asarray(positions, dtype=np.float64)[:, None] * w[None, :])
+    return np.concatenate([z.real, z.imag], axis=1)
+
+
+@pytest.mark.parametrize("D,base", [(128, 500000.0), (64, 10000.0), (8, 50.0)])
+def test_rope_is_an_orthogonal_rotation(D, base):
+    """Pith, "Assumptions & free parameters": R_t is a per-position orthogonal
+    linear map.  The rotation equals the complex-number form, preserves norms
+    and inner products at one position, is the identity at position 0, and its
+    matrix (from the images of the unit vectors) is orthogonal with
+    determinant 1."""
+    r = rng(40)
+    N = 37
+    X = r.standard_normal((N, D))
+    pos = r.integers(0, 200000, N)
+    Y = O.rope(X, base, pos)
+    np.testing.assert_allclose(Y, _rot_complex(X, base, pos), rtol=0, atol=1e-9)
+    np.testing.assert_allclose(np.linalg.norm(Y, axis=1), np.linalg.norm(X, axis=1), rtol=1e-13)
+    np.testing.assert_array_equal(O.rope(X, base, np.zeros(N)), X)
+    for t in (1, 977, 131071):
+        Rt = O.rope(np.eye(D), base, np.full(D, t)).T     # column k = R_t e_k
+        np.testing.assert_allclose(Rt.T @ Rt, np.eye(D), atol=1e-12)
+        assert np.linalg.det(Rt) == pytest.approx(1.0, abs=1e-9)
+
+
+def test_rope_closed_forms():
+    """The first pair turns by t radians (theta_0 = 1) and the pair D/4 by
+    t / sqrt(base) (theta_{D/4} = base^(-1/2)); default keys sit at
+    positions 0..N-1."""
+    D, base, N = 16, 10000.0, 9
+    X = np.zeros((N, D))
+    X[:, 0] = 1.0
+    X[:, D // 4] = 1.0
+    Y = O.rope(X, base)
+    t = np.arange(N)
+    np.testing.assert_allclose(Y[:, 0], np.cos(t), atol=1e-15)
+    np.testing.assert_allclose(Y[:, D // 2], np.sin(t), atol=1e-15)
+    np.testing.assert_allclose(Y[:, D // 4], np.cos(t / 100.0), atol=1e-15)
+    np.testing.assert_allclose(Y[:, D // 4 + D // 2], np.sin(t / 100.0), atol=1e-15)
+
+
+def test_rope_depends_on_relative_position_only():
+    """<R_m q, R_t k> = <q, R_{t-m} k>: the logit of a rotated query and key
+    depends on their offset alone."""
+    r = rng(41)
+    D, base = 64, 500000.0
+    for _ in range(20):
+        q, k = r.standard_normal((1, D)), r.standard_normal((1, D))
+        m, t = r.integers(0, 100000, 2)
+        lhs = float((O.rope(q, base, [m]) @ O.rope(k, base, [t]).T)[0, 0])
+        rhs = float((q @ O.rope(k, base, [t - m]).T)[0, 0])
+        assert lhs == pytest.approx(rhs, rel=1e-9, abs=1e-9)
+
+
+def _rope_unit(seed, H=2, G=2, N=300, D=32, n_obs=6, W=6):
+    r = rng(seed)
+    K = bf16_exact(clustered(r, H, N, D, ndir=6))
+    V = bf16_exact(r.standard_normal((H, N, D)) + 0.5)
+    Q = bf16_exact(r.standard_normal((H * G, n_obs, D)) * 2.0)
+    return K, V, Q
+
+
+def test_rope_compress_attends_rotated_keys_and_stores_prerope_ones():
+    """Pre-RoPE storage: the observation-window attention (score, p, o) is the
+    one over the rotated keys, while the anchors, the assignment, gamma and the
+    residual are those of the stored keys (the same as without rotation for the
+    same anchors); the key utility uses the residual rotated at the token's
+    position."""
+    K, V, Q = _rope_unit(42)
+    base, G, n_obs, W = 10000.0, 2, 6, 6
+    c = O.compress_unit(K, V, Q, G, n_obs, 0.3, W, 2, rope_theta=base)
+    Krot = np.stack([_rot_complex(K[h], base, np.arange(K.shape[1])) for h in range(K.shape[0])])
+    post = O.compress_unit(Krot, V, Q, G, n_obs, 0.3, W, 2)
+    np.testing.assert_allclose(c.score, post.score, rtol=1e-9, atol=1e-15)
+    np.testing.assert_array_equal(c.anchor_pos, post.anchor_pos)
+    plain = O.compress_unit(K, V, Q, G, n_obs, 0.3, W, 2, anchor_override=c.anchor_pos)
+    for a, b in [(c.idx, plain.idx), (c.gamma, plain.gamma), (c.resid, plain.resid)]:
+        np.testing.assert_array_equal(a, b)
+    # the stored anchors are the pre-RoPE rows
+    np.testing.assert_array_equal(c.anchors[0], K[np.arange(2)[:, None], c.anchor_pos])
+    # key utility: sum_j p_jt |<q_j, R_t r_t>| / sqrt(D) ||v_t - o_j||, with
+    # R_t r_t built through the complex form
+    D = K.shape[2]
+    for h in range(2):
+        Qh = Q[h * G:(h + 1) * G].reshape(G * n_obs, D)
+        Rr = _rot_complex(c.resid[0, h], base, np.arange(K.shape[1]))
+        P, Oo = c.P[h], c.O[h]
+        for t in (3, 50, 151):
+            if not np.isfinite(c.u[0, h, t]):
+                continue
+            want = sum(P[j, t] * abs(Qh[j] @ Rr[t]) / math.sqrt(D) * np.linalg.norm(V[h, t] - Oo[j])
+                       for j in range(G * n_obs))
+            assert c.u[0, h, t] == pytest.approx(want, rel=1e-10)
+
+
+def test_rope_utility_equals_first_order_output_change():
+    """With pre-RoPE storage the attention sees R_t k_t: moving the stored k_t
+    by eps*r moves logit t by eps<q, R_t r>/sqrt(D), so the first-order output
+    change is eps alpha_t <q, R_t r>/sqrt(D) (v_t - o); its norm summed over the
+    observation queries is the key utility."""
+    r = rng(43)
+    N, D, GQ, base = 20, 16, 3, 100.0
+    K = r.standard_normal((N, D))
+    V = r.standard_normal((N, D))
+    Qo = r.standard_normal((GQ, D))
+    rK = r.standard_normal((N, D)) * 0.3
+    P, Oo = O.obs_attention(Qo, O.rope(K, base), V, n_obs=1)
+    uK, _ = O.utilities(P, Oo, Qo, V, O.rope(rK, base), rK, np.ones(N, bool))
+    eps = 1e-6
+    for t in range(N):
+        fd = 0.0
+        for j in range(GQ):
+            Kp, Km = K.copy(), K.copy()
+            Kp[t] += eps * rK[t]
+            Km[t] -= eps * rK[t]
+            fd += np.linalg.norm((_attn(Qo[j], _rot_complex(Kp, base, np.arange(N)), V) -
+                                  _attn(Qo[j], _rot_complex(Km, base, np.arange(N)), V)) / (2 * eps))
+        assert uK[t] == pytest.approx(fd, rel=1e-6)
+
+
+def test_rope_decode_distributes_over_the_decomposition():
+    """Pith, "Referee Report" (RoPE distributing over the decomposition): decode
+    over a pre-RoPE cache attends R_t(h(gamma) k_a + r~_t) = h(gamma) R_t k_a
+    + R_t r~_t, the anchor turned at the token's position (not the anchor's);
+    checked against SDPA over keys built that way element by element."""
+    r = rng(44)
+    H, G, N, D, n_obs, W, base = 2, 2, 160, 32, 4, 4, 10000.0
+    K = bf16_exact(clustered(r, H, N, D, ndir=4))
+    V = bf16_exact(r.standard_normal((H, N, D)) + 1.0)
+    Q = bf16_exact(r.standard_normal((H * G, n_obs, D)))
+    c = O.compress_unit(K, V, Q, G, n_obs, 0.2, W, 2, rope_theta=base)
+    assert 0 < c.flag[0].sum()
+    Ki, Vi = _independent_reconstruction(c, K, V)
+    q = bf16_exact(r.standard_normal((H * G, D)) * 2.0)
+    o = O.decode_unit(c, q)
+    for h in range(H):
+        xa = K[h, c.anchor_pos[h]][c.idx[0, h]]
+        rt = Ki[h] - c.gamma16[0, h][:, None] * xa
+        Kr = c.gamma16[0, h][:, None] * _rot_complex(xa, base, np.arange(N)) + _rot_complex(rt, base, np.arange(N))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[h * G:(h + 1) * G])[None], torch.from_numpy(Kr)[None], torch.from_numpy(Vi[h])[None])
+        np.testing.assert_allclose(o[h * G:(h + 1) * G], ref[0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_rope_all_anchor_cache_is_exact_rotary_attention_and_tail_as_given():
+    """Every token an anchor: decode equals attention over the rotated keys; a
+    tail appended after compression is attended as given (its keys already
+    rotated)."""
+    r = rng(45)
+    H, G, N, D, T, base = 2, 2, 64, 32, 5, 500000.0
+    K = bf16_exact(r.standard_normal((H, N, D)))
+    V = bf16_exact(r.standard_normal((H, N, D)))
+    Q = bf16_exact(r.standard_normal((H * G, 4, D)))
+    c = O.compress_unit(K, V, Q, G, 4, 1.5, N, 2, rope_theta=base)
+    assert c.plan.A == N and c.flag.sum() == 0
+    q = bf16_exact(r.standard_normal((H * G, D)) * 3.0)
+    Kt = bf16_exact(r.standard_normal((H, T, D)))
+    Vt = bf16_exact(r.standard_normal((H, T, D)))
+    o = O.decode_unit(c, q)
+    ot = O.decode_unit_tail(c, q, Kt, Vt)
+    for h in range(H):
+        Kr = _rot_complex(K[h], base, np.arange(N))
+        np.testing.assert_allclose(o[h * G:(h + 1) * G], O.attention(q[h * G:(h + 1) * G], Kr, V[h]), rtol=1e-9)
+        np.testing.assert_allclose(ot[h * G:(h + 1) * G],
+                                   O.attention(q[h * G:(h + 1) * G], np.concatenate([Kr, Kt[h]]),
+                                               np.concatenate([V[h], Vt[h]])), rtol=1e-9)
+
+
+def test_rope_theorem1_bound_holds():
+    """Theorem 1 with the rotated keys: ||R_t K_t - R_t K^_t|| = ||K_t - K^_t||,
+    so the bound holds with the stored-space key error."""
+    K, V, Q = _rope_unit(46, N=400)
+    base = 10000.0
+    c = O.compress_unit(K, V, Q, 2, 6, 0.15, 6, 2, rope_theta=base)
+    Kh, Vh = O.reconstruct(c)
+    r = rng(47)
+    for h in range(2):
+        Kr = O.rope(K[h], base)
+        Khr = O.rope(Kh[h], base)
+        np.testing.assert_allclose(np.linalg.norm(Kr - Khr, axis=1), np.linalg.norm(K[h] - Kh[h], axis=1),
+                                   rtol=1e-9, atol=1e-12)
+        for _ in range(10):
+            q = r.standard_normal(K.shape[2]) * 3
+            err, val, key, val2, key2 = O.theorem1_terms(q, Kr, V[h], Khr, Vh[h])
+            tol = 1e-12 * (1 + np.linalg.norm(V[h]))
+            assert err <= val + key + tol and err <= val2 + key2 + tol
