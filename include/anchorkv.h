@@ -87,8 +87,26 @@ typedef struct {
                               ANCHORKV_ANCHORS_COVER */
   int32_t cover_rounds;    /* ANCHORKV_ANCHORS_COVER: rounds of the picks (1..1024; 8); with
                               cover_rounds >= k_uniform every round adds one anchor */
-  int32_t reserved[1];     /* zero */
+  int32_t rope;            /* 0: K holds the keys as attended (default); 1: K holds pre-RoPE keys and
+                              the library applies the rotary embedding wherever a key meets a query
+                              (see below) */
+  float rope_theta;        /* rope = 1: rotary base (1 < rope_theta <= 1e10; 500000) */
+  int32_t reserved[2];     /* zero */
 } anchorkv_params;
+
+/* Pre-RoPE key storage (rope = 1; Pith review of AnchorKV, "Assumptions &
+ * free parameters": RoPE is a per-position orthogonal linear map R_t, so
+ * R_t K_t = R_t K~_t + R_t r_t with ||R_t r_t|| = ||r_t||; "Referee Report":
+ * pre-RoPE key storage with RoPE distributing over the decomposition).  R_t
+ * turns coordinate pairs (i, i + 64) by the angle t * rope_theta^(-2i/128),
+ * the key at position t (0-based).  Compress: the observation-window
+ * attention, the anchor score and the key utility see the rotated keys (the
+ * residual rotated at the token's position); anchors, nearest-anchor
+ * assignment, gamma and residuals are those of the stored pre-RoPE keys.
+ * Decode: logits <q, R_t(gamma k_a + r~)>/sqrt(D) with q given already
+ * rotated; an appended tail is attended as given (its keys already rotated).
+ * Needs the group-affine codec and q_per_kv * n_obs <= 128 (the observation
+ * pass runs in f32 on the rotated keys). */
 
 /* How the non-scored anchors are picked.  UNIFORM: stratified over the
  * positions left after the scored ones.  COVER: coverage-optimised (Pith

@@ -37,7 +37,8 @@ class Params(ct.Structure):
     _fields_ = [("theta", ct.c_float), ("window", ct.c_int32), ("anchor_div", ct.c_int32), ("pool", ct.c_int32),
                 ("rho", ct.c_double), ("group", ct.c_int32), ("pool_kv_jointly", ct.c_int32),
                 ("codec", ct.c_int32), ("hadamard_signs", ct.c_uint32 * 4), ("anchor_mode", ct.c_int32),
-                ("cover_rounds", ct.c_int32), ("reserved", ct.c_int32 * 1)]
+                ("cover_rounds", ct.c_int32), ("rope", ct.c_int32), ("rope_theta", ct.c_float),
+                ("reserved", ct.c_int32 * 2)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("reserved", "hadamard_signs")}
@@ -143,7 +144,7 @@ def params(theta, window, **kw) -> Params:
     """The method's parameters: defaults (anchorkv_params_default) with the
     given theta and window, then any of anchor_div, rho, pool, group,
     pool_kv_jointly, codec, hadamard_signs (four 32-bit words), anchor_mode,
-    cover_rounds replaced."""
+    cover_rounds, rope, rope_theta replaced."""
     q = Params()
     lib().anchorkv_params_default(ct.byref(q), ct.c_float(theta), int(window))
     for k, v in kw.items():
@@ -151,7 +152,8 @@ def params(theta, window, **kw) -> Params:
             for i, x in enumerate(v):
                 q.hadamard_signs[i] = int(x)
             continue
-        if k not in ("anchor_div", "rho", "pool", "group", "pool_kv_jointly", "codec", "anchor_mode", "cover_rounds"):
+        if k not in ("anchor_div", "rho", "pool", "group", "pool_kv_jointly", "codec", "anchor_mode", "cover_rounds",
+                     "rope", "rope_theta"):
             raise TypeError(f"unknown parameter {k}")
         setattr(q, k, v)
     return q

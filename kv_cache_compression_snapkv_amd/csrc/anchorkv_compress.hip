@@ -1161,9 +1161,37 @@ __global__ __launch_bounds__(256) void k_quant_hlm(const void* Kv, const void* V
   }
 }
 
+// (cos, sin) of the rotation angle t * base^(-2i/D) of every position t < N
+// and pair i < D/2 (Pith review, "Assumptions & free parameters": RoPE as a
+// per-position orthogonal map): angle and functions in double precision,
+// rounded once to float.
+__global__ __launch_bounds__(256) void k_rope_table(float2* cs, int N, double base) {
+  constexpr int P = kHeadDim / 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)N * P) return;
+  const int t = (int)(i / P), j = (int)(i % P);
+  const double ang = (double)t * pow(base, -2.0 * j / kHeadDim);
+  double sn, cn;
+  sincos(ang, &sn, &cn);
+  cs[i] = make_float2((float)cn, (float)sn);
+}
+
 // ------------------------------------------------------------ launch sequence
+// Observation-window kernels on pre-RoPE keys: the f32 kernels, with the keys
+// (and in UTIL each token's anchor row) rotated while the tiles are staged.
+template <int DT, int MODE>
+static int launch_obs_rope(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t st) {
+  const int QB = a.GQp / 16;
+  if (QB > 8) return fail(ANCHORKV_E_SHAPE, "pre-RoPE keys: q_per_kv*n_obs must be <= 128");
+  const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1));
+  k_obs<ANCHORKV_F32, MODE, 1, DT, true><<<grid, dim3(64 * QB), 0, st>>>(a);
+  AKV_CHECK_LAUNCH("k_obs (pre-RoPE keys)");
+  return 0;
+}
+
 template <int DT, int MODE>
 static int launch_obs(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t st) {
+  if (p.params.rope) return launch_obs_rope<DT, MODE>(p, a, st);
   const int QB = a.GQp / 16;
   int qpw = QB <= 8 ? 1 : 2;
   if (DT == ANCHORKV_F32 && QB > 8) return fail(ANCHORKV_E_SHAPE, "f32 path supports q_per_kv*n_obs <= 128");
@@ -1317,6 +1345,13 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   a.A = A;
   a.c = kLog2e / sqrtf((float)kHeadDim);
   a.inv_sqrt_d = 1.0f / sqrtf((float)kHeadDim);
+  a.rope_cs = reinterpret_cast<const float2*>(ws + w.rope_cs);
+  if (p.params.rope) {
+    const int64_t n = (int64_t)N * (kHeadDim / 2);
+    k_rope_table<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<float2*>(ws + w.rope_cs), N,
+                                                            (double)p.params.rope_theta);
+    AKV_CHECK_LAUNCH("k_rope_table");
+  }
 
   int rc;
   if ((rc = launch_obs<DT, OBS_STATS>(p, a, st))) return rc;
@@ -1382,7 +1417,7 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
   prof_mark(st, "assign");
 
   if ((rc = launch_obs<DT, OBS_UTIL>(p, a, st))) return rc;
-  prof_mark(st, DT == ANCHORKV_BF16 ? "util_fix" : "obs_util");
+  prof_mark(st, DT == ANCHORKV_BF16 && !p.params.rope ? "util_fix" : "obs_util");
 
   // top-R per (unit, side) with R_K == R_V, or per unit over both sides (joint)
   const bool joint = p.joint != 0;
@@ -1431,6 +1466,8 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
 int compress_supports(const anchorkv_plan_info& p) {
   const int QB = padded_queries(p) / 16;
   if (p.dtype == ANCHORKV_F32 && QB > 8) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: f32 needs q_per_kv*n_obs <= 128");
+  if (p.params.rope && QB > 8)
+    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: pre-RoPE keys need q_per_kv*n_obs <= 128");
   if (QB > 16) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: q_per_kv*n_obs must be <= 256");
   if (p.A > 4096) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %d anchors per head; compress supports <= 4096", p.A);
   if (p.params.pool > kMaxPool) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: pool width > %d", kMaxPool);

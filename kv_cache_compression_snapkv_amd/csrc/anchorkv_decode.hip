@@ -72,11 +72,14 @@ struct DecArgs {
   float* part_acc;   // [U][H][S2][G][D] unnormalised output of each range (same cases)
   float* o;          // [U][H][G][D]
   int H, N, A, C, S2, cps, R_K, R_V;
+  int G;              // q-heads per KV head
   int force_part;    // publish partials even with one range (a tail follows)
   int joint, R_total; // one record section for both sides (keys first), R_total records
   int codec;          // residual codec of the cache (anchorkv_codec)
   uint4 signs;        // rotation signs of the Hadamard / Lloyd-Max codec
   float c;
+  int rope;           // keys stored pre-RoPE (decoded by k_dec_rope)
+  float rope_theta;   // their rotary base
 };
 
 // Hadamard / Lloyd-Max codec (Pith review of AnchorKV, "Referee Report"
@@ -1131,6 +1134,303 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
+// ------------------------------------------------------------ pre-RoPE keys
+// Decode attention over a cache whose keys were stored before the rotary
+// embedding (Pith review of AnchorKV, "Assumptions & free parameters": R_t is
+// a per-position orthogonal map, so R_t k^_t = gamma R_t k_a + R_t r~_t;
+// "Referee Report": RoPE distributes over the decomposition).  The rotation
+// depends on each token's position, so the anchor-logit table of the stream
+// kernel does not apply: keys are rebuilt and rotated tile by tile in
+// registers (the fused-decoder idea of the AnchorKV-adapted page, "Adaptation
+// notes"; the layout here is our own) and values rebuilt into LDS.  One
+// workgroup of four waves per (unit, head, range of 1024-token chunks), tiles
+// of 64 tokens:
+//  * wave 0 reads the tile's pointer words, forms the residual-flag masks and
+//    the record index of the tile's first flagged token per side, and
+//    e^{i t0 theta_p} of the tile's first position for the 64 frequencies
+//    (double precision);
+//  * wave w rebuilds keys 16w..16w+15 in MFMA A-operand layout: lane (token,
+//    kg) holds coordinates 32 st + 8 kg + e (st = 0..3), so the pair (p, p +
+//    64) of a rotation sits in one lane; pair p turns by e^{i t0 theta_p}
+//    e^{i j theta_p} (j = t - t0, the second factor from a table built once
+//    per workgroup); logits against the q-heads on MFMA with the key as bf16
+//    hi + lo (the query exact bf16, or hi + lo for f32 caches);
+//  * every thread rebuilds a quarter of one value row (bf16 hi + lo planes in LDS);
+//  * softmax per q-head by one wave (running maximum, exact rescale);
+//  * p v on MFMA: rows q-heads (p as hi + lo), K = 32 tokens, columns 16
+//    coordinates (v as hi + lo), three products per block.
+// Partials (max, sum, unnormalised output) go to k_dec_merge as the stream
+// kernel's do.
+template <int DT>
+__global__ __launch_bounds__(256) void k_dec_rope(DecArgs a) {
+  using T = typename Elem<DT>::T;
+  using M = Mfma<ANCHORKV_BF16>;
+  constexpr int D = kHeadDim, TT = 64, P = D / 2;
+  constexpr int EPC = 16 / (int)sizeof(T);    // elements per 16-byte load
+  __shared__ __align__(16) float2 ftab[TT][P];       // e^{i j theta_p}, j < 64
+  __shared__ __align__(16) float2 e0[P];             // e^{i t0 theta_p} of the tile
+  __shared__ __align__(16) uint16_t vh[TT][D];       // rebuilt value rows, bf16 hi
+  __shared__ __align__(16) uint16_t vl[TT][D];       // and lo
+  __shared__ __align__(16) float ps[16][TT];         // logits, then p (rows >= G stay zero)
+  __shared__ uint2 wds[TT];                          // the tile's pointer words (K, V)
+  __shared__ unsigned long long fmask[2];            // residual flags of the tile's tokens per side
+  __shared__ int rbase[2];                           // record of the tile's first flagged token per side
+  __shared__ float fr[kMaxG], mrun[kMaxG], lrun[kMaxG];
+
+  const int G = a.G;
+  int bid = blockIdx.x;
+  const int sp = bid % a.S2; bid /= a.S2;
+  const int h = bid % a.H;
+  const int u = bid / a.H;
+  const int64_t uh = (int64_t)u * a.H + h;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int c0 = sp * a.cps, c1 = min(a.C, c0 + a.cps);
+  const int t_beg = c0 * kTile, t_end = min(a.N, c1 * kTile);
+  const uint8_t* base = a.cache + (int64_t)u * a.stride;
+  const uint8_t* recK = base + a.off_rk;
+  const uint8_t* recV = base + a.off_rv;
+  const T* AK = reinterpret_cast<const T*>(base + a.off_ak) + (int64_t)h * a.A * D;
+  const T* AV = reinterpret_cast<const T*>(base + a.off_av) + (int64_t)h * a.A * D;
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(base + a.off_words) + (int64_t)h * a.N * 2;
+  const int* chk = reinterpret_cast<const int*>(base + a.off_ck) + h * a.C;
+  const int* chv = reinterpret_cast<const int*>(base + a.off_cv) + h * a.C;
+  const T* qp = reinterpret_cast<const T*>(a.q) + uh * G * D;
+
+  // the unit's header must describe the plan's cache (see k_dec_stream)
+  {
+    const UnitHeader* hd = reinterpret_cast<const UnitHeader*>(base);
+    if (hd->magic != kMagic || hd->H != a.H || hd->N != a.N || hd->A != a.A || hd->R_K != a.R_K ||
+        hd->R_V != a.R_V || hd->unit_stride != a.stride || hd->off_words != a.off_words || hd->codec != a.codec ||
+        hd->rope != 1 || hd->rope_theta != a.rope_theta) {
+      const float nan = __builtin_nanf("");
+      if (a.S2 == 1 && !a.force_part) {
+        for (int i = tid; i < G * D; i += 256) a.o[uh * G * D + i] = nan;
+      } else {
+        const int64_t slot = uh * a.S2 + sp;
+        for (int i = tid; i < G * D; i += 256) a.part_acc[slot * G * D + i] = nan;
+        if (tid < G) a.part_ml[slot * G + tid] = make_float2(nan, nan);
+      }
+      return;
+    }
+  }
+
+  // query fragments (B operand: column = q-head, the lane's K-slice of each
+  // 32-coordinate step); f32 queries as bf16 hi + lo
+  bf16x8 qb[4], qbl[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = col < G ? Elem<DT>::f(qp[col * D + 32 * st + 8 * kg + e]) : 0.0f;
+    split8(x, qb[st], qbl[st]);
+  }
+  // theta of frequency lane (every thread of a column of ftab has the same
+  // one: 256 is a multiple of P); e^{i j theta_p} for j < 64 in double
+  // precision, rounded once
+  const double theta_l = pow((double)a.rope_theta, -2.0 * lane / D);
+  for (int j = tid / P; j < TT; j += 256 / P) {
+    double sn, cn;
+    sincos((double)j * theta_l, &sn, &cn);
+    ftab[j][lane] = make_float2((float)cn, (float)sn);
+  }
+  for (int i = tid; i < 16 * TT; i += 256) (&ps[0][0])[i] = 0.0f;
+  if (tid < kMaxG) { mrun[tid] = -INFINITY; lrun[tid] = 0.0f; }
+  int run_k = 0, run_v = 0;   // wave 0: flagged tokens of the current chunk before the tile
+  f32x4 oacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+
+  for (int t0 = t_beg; t0 < t_end; t0 += TT) {
+    // ---- wave 0: words, flags, record bases, e^{i t0 theta}
+    if (wave == 0) {
+      if ((t0 & (kTile - 1)) == 0) { run_k = 0; run_v = 0; }
+      const int t = t0 + lane;
+      uint2 wd = make_uint2(0u, 0u);
+      if (t < t_end) wd = *reinterpret_cast<const uint2*>(words + (int64_t)t * 2);
+      wds[lane] = wd;
+      const unsigned long long mk = __ballot((wd.x & 0x8000u) != 0);
+      const unsigned long long mv = __ballot((wd.y & 0x8000u) != 0);
+      if (lane == 0) {
+        const int c = t0 / kTile;
+        fmask[0] = mk; fmask[1] = mv;
+        rbase[0] = chk[c] + run_k;
+        rbase[1] = chv[c] + run_v;
+      }
+      run_k += __popcll(mk);
+      run_v += __popcll(mv);
+      double sn, cn;
+      sincos((double)t0 * theta_l, &sn, &cn);
+      e0[lane] = make_float2((float)cn, (float)sn);
+    }
+    __syncthreads();
+
+    // ---- keys of wave w's 16 tokens: rebuild, rotate, logits on MFMA
+    {
+      const int j = 16 * wave + col, t = t0 + j;
+      const bool valid = t < t_end;
+      const uint32_t wk = wds[j].x;
+      const float gk = h2f((uint16_t)(wk >> 16));
+      const T* ar = AK + (int64_t)(wk & 0x7FFF) * D;
+      float x[4][8];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int e0i = 0; e0i < 8; e0i += EPC) {
+          T v[EPC];
+          *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(ar + 32 * st + 8 * kg + e0i);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) x[st][e0i + e] = gk * Elem<DT>::f(v[e]);
+        }
+      if (wk & 0x8000u) {
+        // the token's key record: code words 8 (kg & 1) .. + 7 (coordinates
+        // 32 st + 8 kg + e lie in code word 8 (kg & 1) + e, plane 2 st + kg / 2)
+        const int rk = rbase[0] + __popcll(fmask[0] & ((1ull << j) - 1ull));
+        const uint8_t* rp = recK + (int64_t)rk * kRecBytes;
+        const uint4 cw = *reinterpret_cast<const uint4*>(rp + 16 * (kg & 1));
+        const uint4 sz = *reinterpret_cast<const uint4*>(rp + 32);
+        const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
+        const uint32_t szs[4] = {sz.x, sz.y, sz.z, sz.w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const float sc = h2f((uint16_t)(szs[st] & 0xFFFFu)), zr = h2f((uint16_t)(szs[st] >> 16));
+          const int sh = 2 * (2 * st + (kg >> 1));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t code = ((cws[e >> 1] >> (16 * (e & 1) + sh)) & 3u);
+            x[st][e] += fmaf(sc, (float)code, zr);
+          }
+        }
+      }
+      // pair p = 32 st + 8 kg + e (st = 0, 1) with p + 64: turn by t theta_p
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pp = 32 * st + 8 * kg + e;
+          const float2 a0 = e0[pp], b0 = ftab[j][pp];
+          const float cs = a0.x * b0.x - a0.y * b0.y, sn = a0.x * b0.y + a0.y * b0.x;
+          const float x0 = x[st][e], x1 = x[st + 2][e];
+          x[st][e] = x0 * cs - x1 * sn;
+          x[st + 2][e] = x0 * sn + x1 * cs;
+        }
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bf16x8 kh, kl;
+        split8(x[st], kh, kl);
+        acc = M::mma(kh, qb[st], acc);
+        acc = M::mma(kl, qb[st], acc);
+        if constexpr (DT == ANCHORKV_F32) acc = M::mma(kh, qbl[st], acc);
+      }
+      if (col < G)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jr = 16 * wave + 4 * kg + r;
+          ps[col][jr] = t0 + jr < t_end ? acc[r] * a.c : -INFINITY;
+        }
+      (void)valid;
+    }
+    // ---- values: thread (token r, quarter qq) rebuilds coordinates 32 qq .. + 31
+    {
+      const int r = tid >> 2, qq = tid & 3, t = t0 + r;
+      const uint32_t wv = wds[r].y;
+      const float gv = h2f((uint16_t)(wv >> 16));
+      const T* vr = AV + (int64_t)(wv & 0x7FFF) * D + 32 * qq;
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; i += EPC) {
+        T x[EPC];
+        *reinterpret_cast<uint4*>(x) = *reinterpret_cast<const uint4*>(vr + i);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) v[i + e] = gv * Elem<DT>::f(x[e]);
+      }
+      if (wv & 0x8000u) {
+        // coordinate 32 qq + e: code word e & 15, plane 2 qq + e / 16; group qq
+        const int rv = rbase[1] + __popcll(fmask[1] & ((1ull << r) - 1ull));
+        const uint8_t* rp = recV + (int64_t)rv * kRecBytes;
+        const uint4 c01 = *reinterpret_cast<const uint4*>(rp), c23 = *reinterpret_cast<const uint4*>(rp + 16);
+        const uint32_t cw[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
+        const uint32_t szv = *reinterpret_cast<const uint32_t*>(rp + 32 + 4 * qq);
+        const float sc = h2f((uint16_t)(szv & 0xFFFFu)), zr = h2f((uint16_t)(szv >> 16));
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const int jw = e & 15, sh = 2 * (2 * qq + (e >> 4));
+          const uint32_t code = (cw[jw >> 1] >> (16 * (jw & 1) + sh)) & 3u;
+          v[e] += fmaf(sc, (float)code, zr);
+        }
+      }
+      if (t >= t_end)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) v[e] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bf16x8 hi, lo;
+        split8(v + 8 * k, hi, lo);
+        *reinterpret_cast<bf16x8*>(&vh[r][32 * qq + 8 * k]) = hi;
+        *reinterpret_cast<bf16x8*>(&vl[r][32 * qq + 8 * k]) = lo;
+      }
+    }
+    __syncthreads();
+    // ---- softmax per q-head: wave w takes q-heads w, w + 4
+    for (int g = wave; g < G; g += 4) {
+      const float x = ps[g][lane];
+      const float mn = fmaxf(mrun[g], wave_max(x));
+      const float f = mrun[g] == -INFINITY ? 0.0f : exp2_fast(mrun[g] - mn);
+      const float p = x == -INFINITY ? 0.0f : exp2_fast(x - mn);
+      ps[g][lane] = p;
+      const float sum = wave_sum(p);
+      if (lane == 0) { fr[g] = f; lrun[g] = fmaf(lrun[g], f, sum); mrun[g] = mn; }
+    }
+    __syncthreads();
+    // ---- p v: wave w owns coordinate blocks 2w, 2w + 1
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * kg + r;
+      const float f = g < G ? fr[g] : 0.0f;
+      oacc[0][r] *= f;
+      oacc[1][r] *= f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < TT / 32; ++ks) {
+      float p8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p8[e] = ps[col][ks * 32 + kg * 8 + e];
+      bf16x8 ph, pl;
+      split8(p8, ph, pl);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int d = (2 * wave + b) * 16 + col;
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r0 = ks * 32 + kg * 8 + 2 * e;
+          wh[e] = (uint32_t)vh[r0][d] | ((uint32_t)vh[r0 + 1][d] << 16);
+          wl[e] = (uint32_t)vl[r0][d] | ((uint32_t)vl[r0 + 1][d] << 16);
+        }
+        const bf16x8 vbh = bits_to_frag(make_uint4(wh[0], wh[1], wh[2], wh[3]));
+        const bf16x8 vbl = bits_to_frag(make_uint4(wl[0], wl[1], wl[2], wl[3]));
+        oacc[b] = M::mma(ph, vbh, oacc[b]);
+        oacc[b] = M::mma(pl, vbh, oacc[b]);
+        oacc[b] = M::mma(ph, vbl, oacc[b]);
+      }
+    }
+    __syncthreads();   // words, e0, value rows, ps and fr are rewritten by the next tile
+  }
+  const bool part = a.S2 > 1 || a.force_part;
+  const int64_t slot = uh * a.S2 + sp;
+  if (part && tid < G) a.part_ml[slot * G + tid] = make_float2(mrun[tid], lrun[tid]);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * kg + r;
+      const int d = (2 * wave + b) * 16 + col;
+      if (g < G) {
+        if (part) a.part_acc[(slot * G + g) * D + d] = oacc[b][r];
+        else a.o[(uh * G + g) * D + d] = oacc[b][r] / lrun[g];
+      }
+    }
+}
+
 // Per (unit, head, q-head) with several token ranges (and an optional tail
 // partial): o = sum_s f_s acc_s / sum_s f_s l_s with f_s = 2^(m_s - max m).
 // One block of 128 threads (one per coordinate) per q-head: the range
@@ -1458,9 +1758,15 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   a.signs = make_uint4(p.params.hadamard_signs[0], p.params.hadamard_signs[1], p.params.hadamard_signs[2],
                        p.params.hadamard_signs[3]);
   a.force_part = n_tail > 0 ? 1 : 0;
+  a.G = G;
+  a.rope = p.params.rope;
+  a.rope_theta = p.params.rope_theta;
   const unsigned grid = (unsigned)((int64_t)U * H * S2);
   int rc = 0;
-  switch (G) {
+  if (a.rope) {
+    k_dec_rope<DT><<<grid, 256, 0, st>>>(a);
+    AKV_CHECK_LAUNCH("k_dec_rope");
+  } else switch (G) {
     case 1: rc = launch_stream<DT, 1>(a, grid, st); break;
     case 2: rc = launch_stream<DT, 2>(a, grid, st); break;
     case 3: rc = launch_stream<DT, 3>(a, grid, st); break;
@@ -1503,7 +1809,11 @@ int decode_blocks_per_cu(int G, int A, bool f32, int codec) {
 int decode_supports(const anchorkv_plan_info& p) {
   if (p.G > kMaxG) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: decode supports q_per_kv <= %d", kMaxG);
   const bool f32 = p.dtype == ANCHORKV_F32;
-  if (dec_lds(p.G, p.A, f32, decode_waves(p.G, p.A, f32, p.params.codec), p.params.codec).total > kLdsLimit)
+  if (p.params.rope && p.params.codec != ANCHORKV_CODEC_AFFINE)
+    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: pre-RoPE keys need the group-affine codec");
+  // the pre-RoPE kernel reads anchors from memory: no anchor limit from LDS
+  if (!p.params.rope &&
+      dec_lds(p.G, p.A, f32, decode_waves(p.G, p.A, f32, p.params.codec), p.params.codec).total > kLdsLimit)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %d anchors x %d q-heads exceed the decode kernel's LDS", p.A, p.G);
   if (p.decode_splits > 64 || p.n_chunks > 128 * p.decode_splits)
     return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: n_tokens %d too large for the decode ranges", p.N);

@@ -67,6 +67,7 @@ CompressWs compress_ws_layout(const anchorkv_plan_info& p) {
   const bool cover = p.params.anchor_mode == ANCHORKV_ANCHORS_COVER;
   w.cover_mc = take(cover ? 4 * U * H * N : 0);
   w.cover_list = take(cover ? 4 * U * H * std::max<int64_t>(1, (int64_t)p.k_scored + p.k_uniform) : 0);
+  w.rope_cs = take(p.params.rope ? 8 * N * (D / 2) : 0);
   w.total = off;
   return w;
 }
@@ -153,6 +154,8 @@ void fill_header(const anchorkv_plan_info& p, UnitHeader* h) {
   h->R_total = p.R_total;
   h->codec = p.params.codec;
   for (int i = 0; i < 4; ++i) h->signs[i] = p.params.hadamard_signs[i];
+  h->rope = p.params.rope;
+  h->rope_theta = p.params.rope_theta;
 }
 
 // SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
@@ -178,6 +181,8 @@ static void params_default(anchorkv_params* q, float theta, int32_t window) {
   q->codec = ANCHORKV_CODEC_AFFINE;
   q->anchor_mode = ANCHORKV_ANCHORS_UNIFORM;
   q->cover_rounds = 8;
+  q->rope = 0;
+  q->rope_theta = 500000.0f;
   uint64_t st = kSignSeed;
   const uint64_t a = splitmix64(st), b = splitmix64(st);
   q->hadamard_signs[0] = (uint32_t)a; q->hadamard_signs[1] = (uint32_t)(a >> 32);
@@ -200,6 +205,11 @@ static int check_params(const anchorkv_params& q) {
     return fail(ANCHORKV_E_ARG, "anchorkv_plan: anchor_mode %d is not 0 (uniform) or 1 (coverage)", q.anchor_mode);
   if (q.cover_rounds < 1 || q.cover_rounds > 1024)
     return fail(ANCHORKV_E_ARG, "anchorkv_plan: cover_rounds %d must be in [1, 1024]", q.cover_rounds);
+  if (q.rope != 0 && q.rope != 1) return fail(ANCHORKV_E_ARG, "anchorkv_plan: rope %d must be 0 or 1", q.rope);
+  if (!(q.rope_theta > 1.0f) || !(q.rope_theta <= 1e10f))
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: rope_theta must be in (1, 1e10]");
+  if (q.rope && q.codec != ANCHORKV_CODEC_AFFINE)
+    return fail(ANCHORKV_E_ARG, "anchorkv_plan: pre-RoPE keys (rope = 1) need the group-affine codec");
   for (int i = 0; i < (int)(sizeof(q.reserved) / sizeof(q.reserved[0])); ++i)
     if (q.reserved[i] != 0) return fail(ANCHORKV_E_ARG, "anchorkv_plan: reserved parameter fields must be zero");
   return 0;
@@ -283,6 +293,8 @@ static int plan_from_header_impl(const void* header_host, int32_t units, anchork
   q.pool_kv_jointly = h.pool_kv_jointly;
   q.codec = h.codec;
   for (int i = 0; i < 4; ++i) q.hadamard_signs[i] = h.signs[i];
+  q.rope = h.rope;
+  q.rope_theta = h.rope_theta;
   int rc = plan_impl(&d, &q, out);
   if (rc) return rc == ANCHORKV_E_ARG ? fail(ANCHORKV_E_LAYOUT, "%s: header parameters are invalid", fn) : rc;
   if (out->A != h.A || out->R_K != h.R_K || out->R_V != h.R_V || out->R_total != h.R_total ||

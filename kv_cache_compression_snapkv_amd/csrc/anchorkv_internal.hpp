@@ -67,6 +67,8 @@ struct CompressWs {
   // coverage anchors only (params.anchor_mode == ANCHORKV_ANCHORS_COVER, else empty):
   int64_t cover_mc;   // f32 [U][H][N] largest cosine of each position to the anchors so far (+inf: an anchor)
   int64_t cover_list; // int32 [U][H][k_s + k_u] scored positions (ascending), then the picks in round order
+  // pre-RoPE keys only (params.rope == 1, else empty):
+  int64_t rope_cs;    // float2 [N][64] (cos, sin) of t * rope_theta^(-2i/128)
   int64_t total;
 };
 CompressWs compress_ws_layout(const anchorkv_plan_info& p);
@@ -98,7 +100,9 @@ struct UnitHeader {
   int32_t R_total, pad1;   // joint ranking: residual records of both sides
   int32_t codec;           // residual codec (anchorkv_codec)
   uint32_t signs[4];       // rotation signs of the Hadamard / Lloyd-Max codec
-  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8 - 4 * 4 - 8 - 8 - 4 - 16];
+  int32_t rope;            // 1: keys stored pre-RoPE, rotated at decode
+  float rope_theta;        // rotary base of those keys
+  uint8_t pad[256 - 16 * 4 - 10 * 8 - 8 - 4 * 4 - 8 - 8 - 4 - 16 - 8];
 };
 static_assert(sizeof(UnitHeader) == 256, "header must be 256 bytes");
 void fill_header(const anchorkv_plan_info& p, UnitHeader* h);

@@ -52,6 +52,7 @@ struct ObsArgs {
   int S1u, kps_u;         // key splits of the pipelined UTIL kernel (<= 2048 keys each)
   float c;               // log2(e)/sqrt(D)
   float inv_sqrt_d;
+  const float2* rope_cs; // pre-RoPE keys: (cos, sin) [N][D/2] of the rotation at each position
 };
 
 template <int DT> struct ObsCfg {
@@ -63,13 +64,49 @@ template <int DT> struct ObsCfg {
   static constexpr int NSTEP = D / Mfma<DT>::KSTEP;
 };
 
-template <int DT, int MODE, int QPW>
+// Four consecutive elements of a row as floats (bf16: 8-byte load, f32:
+// 16-byte load; the caller keeps the address aligned to that size).
+template <int SRC> __device__ __forceinline__ void ld4f(const typename Elem<SRC>::T* p, float (&o)[4]) {
+  if constexpr (SRC == ANCHORKV_BF16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+}
+
+// Rotary embedding of coordinates i0..i0+3 (x0) and their partners
+// 64+i0..64+i0+3 (x1) with (cos, sin) of the position: (x0, x1) ->
+// (x0 cos - x1 sin, x0 sin + x1 cos).
+__device__ __forceinline__ void rope4(float (&x0)[4], float (&x1)[4], const float2* cs) {
+  const float4 ca = reinterpret_cast<const float4*>(cs)[0], cb = reinterpret_cast<const float4*>(cs)[1];
+  const float c[4] = {ca.x, ca.z, cb.x, cb.z}, s[4] = {ca.y, ca.w, cb.y, cb.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = x0[i], b = x1[i];
+    x0[i] = fmaf(a, c[i], -b * s[i]);
+    x1[i] = fmaf(a, s[i], b * c[i]);
+  }
+}
+
+// DT: the arithmetic (tile and MFMA) type; SRC: the storage type of K, V, Q
+// and the cache's anchors (== DT except with pre-RoPE keys); ROPE: K holds
+// pre-RoPE keys (Pith review, "Assumptions & free parameters": R_t is a
+// per-position orthogonal map), rotated here at their positions while the
+// tile is staged (f32 arithmetic), and in UTIL the gathered anchor row of
+// each token is rotated at the token's position, so <q, R_t k_t> -
+// gamma_t <q, R_t k_a(t)> = <q, R_t r_t>.
+template <int DT, int MODE, int QPW, int SRC = DT, bool ROPE = false>
 __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
   using C = ObsCfg<DT>;
   using T = typename C::T;
+  using S = typename Elem<SRC>::T;
   using M = Mfma<DT>;
   using frag = typename M::frag;
   constexpr int D = C::D, LDK = C::LDK, NSTEP = C::NSTEP, LDVT = C::LDVT;
+  static_assert(SRC == DT || (ROPE && DT == ANCHORKV_F32), "storage differs from arithmetic only for pre-RoPE keys");
 
   __shared__ __attribute__((aligned(16))) T Ks[64 * LDK];
   __shared__ __attribute__((aligned(16))) T Vs[(MODE == OBS_STATS) ? 16 : (MODE == OBS_SCORE ? D * LDVT : 64 * LDK)];
@@ -88,9 +125,9 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
   const int k0 = s * a.kps;
   const int k1 = min(N, k0 + a.kps);
   const int64_t uh = (int64_t)u * H + h;
-  const T* Kp = reinterpret_cast<const T*>(a.K) + uh * N * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + uh * N * D;
-  const T* Qp = reinterpret_cast<const T*>(a.Q) + ((int64_t)u * H * a.G + (int64_t)h * a.G) * a.n_obs * D;
+  const S* Kp = reinterpret_cast<const S*>(a.K) + uh * N * D;
+  const S* Vp = reinterpret_cast<const S*>(a.V) + uh * N * D;
+  const S* Qp = reinterpret_cast<const S*>(a.Q) + ((int64_t)u * H * a.G + (int64_t)h * a.G) * a.n_obs * D;
 
   // ---- per-wave query blocks and their B fragments (constant over all keys)
   frag qf[QPW][NSTEP];
@@ -106,7 +143,8 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
     qj[qi] = q % a.n_obs;
     for (int st = 0; st < NSTEP; ++st) {
       const int kk = st * M::KSTEP + kg * M::KW;
-      qf[qi][st] = qvalid[qi] ? M::load(Qp + (int64_t)q * D + kk) : M::zero();
+      if constexpr (SRC == DT) qf[qi][st] = qvalid[qi] ? M::load(Qp + (int64_t)q * D + kk) : M::zero();
+      else qf[qi][st] = qvalid[qi] ? Elem<SRC>::f(Qp[(int64_t)q * D + kk]) : M::zero();
       if constexpr (MODE == OBS_UTIL) {
         if constexpr (DT == ANCHORKV_BF16) {
           const uint16_t* oh = a.ohl + (uh * 2 + 0) * a.GQp * D;
@@ -145,7 +183,52 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
     // ---- stage the key tile (and value / gathered-anchor tiles)
     constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;          // chunks per row
-    for (int ch = threadIdx.x; ch < 64 * CPR; ch += blockDim.x) {
+    if constexpr (ROPE) {
+      // item (row r, coordinates i0..i0+3 and 64+i0..64+i0+3): rotated keys,
+      // values as floats, and (UTIL) the token's anchor row rotated at the
+      // token's position
+      for (int it = threadIdx.x; it < 64 * 16; it += blockDim.x) {
+        const int r = it >> 4, i0 = (it & 15) * 4;
+        const int t = t0 + r;
+        float x0[4] = {0, 0, 0, 0}, x1[4] = {0, 0, 0, 0};
+        if (t < k1) {
+          ld4f<SRC>(Kp + (int64_t)t * D + i0, x0);
+          ld4f<SRC>(Kp + (int64_t)t * D + 64 + i0, x1);
+          rope4(x0, x1, a.rope_cs + (int64_t)t * (D / 2) + i0);
+        }
+        *reinterpret_cast<float4*>(&Ks[r * LDK + i0]) = make_float4(x0[0], x0[1], x0[2], x0[3]);
+        *reinterpret_cast<float4*>(&Ks[r * LDK + 64 + i0]) = make_float4(x1[0], x1[1], x1[2], x1[3]);
+        if constexpr (MODE == OBS_UTIL) {
+          float v0[4] = {0, 0, 0, 0}, v1[4] = {0, 0, 0, 0}, g0[4] = {0, 0, 0, 0}, g1[4] = {0, 0, 0, 0};
+          if (t < k1) {
+            ld4f<SRC>(Vp + (int64_t)t * D + i0, v0);
+            ld4f<SRC>(Vp + (int64_t)t * D + 64 + i0, v1);
+            const int an = a.aidx[((int64_t)u * 2 * H + h) * N + t];  // side 0 = K
+            const S* ap = reinterpret_cast<const S*>(a.cache + (int64_t)u * a.stride + a.off_anchor_k) +
+                          ((int64_t)h * a.A + an) * D;
+            ld4f<SRC>(ap + i0, g0);
+            ld4f<SRC>(ap + 64 + i0, g1);
+            rope4(g0, g1, a.rope_cs + (int64_t)t * (D / 2) + i0);
+          }
+          *reinterpret_cast<float4*>(&Vs[r * LDK + i0]) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+          *reinterpret_cast<float4*>(&Vs[r * LDK + 64 + i0]) = make_float4(v1[0], v1[1], v1[2], v1[3]);
+          *reinterpret_cast<float4*>(&Gs[r * LDK + i0]) = make_float4(g0[0], g0[1], g0[2], g0[3]);
+          *reinterpret_cast<float4*>(&Gs[r * LDK + 64 + i0]) = make_float4(g1[0], g1[1], g1[2], g1[3]);
+        }
+      }
+      if constexpr (MODE == OBS_SCORE) {
+        // transposed value tile Vt[d][key] as floats; consecutive threads take consecutive keys
+        for (int it = threadIdx.x; it < 64 * (D / 4); it += blockDim.x) {
+          const int r = it % 64, d0 = (it / 64) * 4;
+          const int t = t0 + r;
+          float v[4] = {0, 0, 0, 0};
+          if (t < k1) ld4f<SRC>(Vp + (int64_t)t * D + d0, v);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Vs[(d0 + i) * LDVT + r] = v[i];
+        }
+      }
+    }
+    for (int ch = threadIdx.x; ch < (ROPE ? 0 : 64 * CPR); ch += blockDim.x) {
       const int r = ch / CPR, cc = ch % CPR;
       const int t = t0 + r;
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -164,7 +247,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
         *reinterpret_cast<uint4*>(&Gs[r * LDK + cc * EPC]) = g;
       }
     }
-    if constexpr (MODE == OBS_SCORE) {
+    if constexpr (MODE == OBS_SCORE && !ROPE) {
       // transposed value tile Vt[d][key]; consecutive threads take consecutive keys
       for (int ch = threadIdx.x; ch < 64 * CPR; ch += blockDim.x) {
         const int r = ch % 64, cc = ch / 64;

@@ -22,6 +22,18 @@ MARGIN = 1e-5      # relative tie margin for discrete decisions
 OUT_RTOL = 1e-3    # decode output: ||o_gpu - o_ref|| <= 1e-3 ||o_ref|| per (unit, q-head)
 
 
+def oracle_params(params):
+    """The library's method parameters as the oracle's keyword arguments:
+    pre-RoPE keys (rope = 1, rope_theta) become rope_theta (the rotary base,
+    500000 by default), everything else is passed through."""
+    prm = dict(params or {})
+    rope = prm.pop("rope", 0)
+    base = prm.pop("rope_theta", 500000.0)
+    if rope:
+        prm["rope_theta"] = float(np.float32(base))
+    return prm
+
+
 def bits_f16(x):
     return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
 
@@ -157,7 +169,7 @@ def compare_unit(K, V, Q, G, n_obs, theta, W, e, gpu, taps=None, q=None, o_gpu=N
     params: the method's parameters other than theta and window (anchor_div,
     rho, pool) when they differ from the pages' values."""
     rep = {} if report is None else report
-    prm = dict(params or {})
+    prm = oracle_params(params)
     H, N, D = K.shape
     dtype_code = 1 if e == 2 else 2
     p = O.plan(H, N, D, e, theta, W,

@@ -370,3 +370,49 @@ def test_hlm_pack_unpack_roundtrip_and_header(akv):
     rec0 = np.frombuffer(blob[p.off_res_k:p.off_res_k + 36], np.uint8)
     first = np.argwhere(fl[0])[0]
     assert rec0[32:34].view(np.uint16)[0] == arr["scale16"][0, first[0], first[1], 0] and not rec0[34:36].any()
+
+
+def test_rope_parameters(akv):
+    """Pre-RoPE key storage (anchorkv_params.rope, rope_theta): off by default
+    with base 500000; it changes neither counts nor layout; the header records
+    it (the plan rebuilt from a packed unit's header keeps it); the plan
+    refuses it with the Hadamard / Lloyd-Max codec, with more than 128
+    observation queries per KV head, and with a base outside (1, 1e10]."""
+    q = akv.params(0.05, 32)
+    assert (q.rope, q.rope_theta) == (0, 500000.0)
+    pu = akv.plan(2, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32)
+    pr = akv.plan(2, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32, rope=1, rope_theta=10000.0)
+    for f in ("A", "k_scored", "k_uniform", "R_K", "R_V", "unit_bytes", "cache_bytes", "off_words"):
+        assert getattr(pu, f) == getattr(pr, f), f
+    assert pr.compress_workspace_bytes >= pu.compress_workspace_bytes + 8 * 8192 * 64
+    # header round trip through a host-packed unit
+    pr1 = akv.plan(1, 2, 4, 600, 128, 8, akv.BF16, 0.2, 8, rope=1, rope_theta=10000.0)
+    H, N, A, D = 2, 600, pr1.A, 128
+    arrays = dict(positions=np.tile(np.arange(N - A, N, dtype=np.int32), (H, 1)),
+                  anchors_k=np.zeros((H, A, D), np.uint16), anchors_v=np.zeros((H, A, D), np.uint16),
+                  idx=np.zeros((2, H, N), np.int32), gamma16=np.zeros((2, H, N), np.uint16),
+                  flag=np.zeros((2, H, N), np.uint8), codes=np.zeros((2, H, N, D), np.uint8),
+                  scale16=np.zeros((2, H, N, D // 32), np.uint16), zero16=np.zeros((2, H, N, D // 32), np.uint16))
+    flat = np.zeros((H, N), bool)
+    order = np.arange(H * N)
+    take = order[:pr1.R_K]
+    flat.reshape(-1)[take] = True
+    flat[np.arange(H)[:, None], arrays["positions"]] = False
+    extra = np.nonzero(~flat.reshape(-1) & ~np.isin(np.arange(H * N) % N, np.arange(N - A, N)))[0]
+    flat.reshape(-1)[extra[:pr1.R_K - flat.sum()]] = True
+    arrays["flag"][:] = flat[None]
+    for s_ in range(2):
+        arrays["idx"][s_] = np.where(np.arange(N)[None] >= N - A, np.arange(N)[None] - (N - A), 0)
+    unit = akv.pack_unit(pr1, arrays)
+    back = akv.plan_from_header(unit[:256], 1)
+    assert (back.params.rope, back.params.rope_theta) == (1, 10000.0)
+    assert back.as_dict() == pr1.as_dict()
+    E = akv.AnchorKVError
+    for kw in (dict(rope=2), dict(rope=-1), dict(rope=1, rope_theta=1.0), dict(rope=1, rope_theta=0.5),
+               dict(rope=1, rope_theta=2e10), dict(rope=1, rope_theta=float("nan")), dict(rope=1, codec=1)):
+        with pytest.raises(E) as e:
+            akv.plan(1, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32, **kw)
+        assert e.value.code == -1, kw
+    with pytest.raises(E) as e:
+        akv.plan(1, 8, 8, 8192, 128, 32, akv.BF16, 0.1, 32, rope=1)   # 256 observation queries per KV head
+    assert e.value.code == -3

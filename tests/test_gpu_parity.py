@@ -14,7 +14,7 @@ import torch
 
 import kvsynth
 from oracle import anchorkv_oracle as O
-from tests.parity import compare_unit, oracle_arrays
+from tests.parity import compare_unit, oracle_arrays, oracle_params
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +80,12 @@ SMALL = {
     "bf16_cover_fps": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=2, n_tokens=2500, n_obs=16,
                                              window=16, n_dirs=8),
     "bf16_cover_g8": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=4500, theta=0.08),
+    # keys stored before the rotary embedding, rotated wherever they meet a query
+    "bf16_rope": W_["llama8b_32k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=3000, n_dirs=32),
+    "bf16_rope_base1e4": W_["llama3b_8k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=2500, n_dirs=16),
+    "f32_rope": W_["tiny_f32"].scaled(n_tokens=1500),
+    "bf16_rope_g8": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=4500, n_obs=16, theta=0.08),
+    "bf16_rope_joint": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, n_dirs=32),
 }
 # non-default method parameters of some cases (anchorkv_params)
 PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40),
@@ -91,7 +97,10 @@ PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dic
           "bf16_cover": dict(anchor_mode=1, cover_rounds=4), "f32_cover": dict(anchor_mode=1, cover_rounds=3),
           # one pick per round: plain furthest-point sampling
           "bf16_cover_fps": dict(anchor_mode=1, cover_rounds=1024, anchor_div=100),
-          "bf16_cover_g8": dict(anchor_mode=1)}
+          "bf16_cover_g8": dict(anchor_mode=1),
+          "bf16_rope": dict(rope=1), "bf16_rope_base1e4": dict(rope=1, rope_theta=10000.0),
+          "f32_rope": dict(rope=1, rope_theta=10000.0), "bf16_rope_g8": dict(rope=1),
+          "bf16_rope_joint": dict(rope=1, pool_kv_jointly=1)}
 
 
 def _flush(msg):
@@ -154,7 +163,8 @@ def test_compress_decode_parity(akv, name):
 
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "f32_tiny", "bf16_stress_short", "bf16_joint", "bf16_hlm_g8",
-                                  "f32_hlm", "bf16_hlm_stress"])
+                                  "f32_hlm", "bf16_hlm_stress", "bf16_rope", "f32_rope", "bf16_rope_g8",
+                                  "bf16_rope_joint"])
 def test_decode_on_host_packed_oracle_cache(akv, name):
     """Decode alone: the oracle's compressed representation, packed on the
     host into the cache layout, decoded on the GPU."""
@@ -168,7 +178,8 @@ def test_decode_on_host_packed_oracle_cache(akv, name):
     cache_h = np.zeros(p.cache_bytes, dtype=np.uint8)
     comps = []
     for u in range(w.units):
-        c = O.compress_unit(K64[u], V64[u], Q64[u], w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes, **prm)
+        c = O.compress_unit(K64[u], V64[u], Q64[u], w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes,
+                            **oracle_params(prm))
         comps.append(c)
         unit = akv.pack_unit(p, oracle_arrays(c, dtype_code))
         cache_h[u * p.unit_stride: u * p.unit_stride + p.unit_bytes] = np.frombuffer(unit, np.uint8)

@@ -14,7 +14,7 @@ import torch
 
 import kvsynth
 from oracle import anchorkv_oracle as O
-from tests.parity import oracle_arrays
+from tests.parity import oracle_arrays, oracle_params
 from tests.test_gpu_parity import SMALL, make_inputs, plan_for
 
 pytestmark = pytest.mark.gpu
@@ -28,8 +28,11 @@ CASES = {
     "bf16_g8": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, n_dirs=16),
     # the paper's codec (Hadamard rotation + Lloyd-Max), 8 q-heads, two units
     "bf16_hlm_g8": W_["llama70b_128k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=2500, n_dirs=16),
+    # keys stored before the rotary embedding (the tail's keys are given rotated)
+    "bf16_rope_g8": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, n_obs=16, n_dirs=16),
+    "f32_rope": W_["tiny_f32"].scaled(n_tokens=1300),
 }
-PARAMS = {"bf16_hlm_g8": dict(codec=1)}
+PARAMS = {"bf16_hlm_g8": dict(codec=1), "bf16_rope_g8": dict(rope=1), "f32_rope": dict(rope=1, rope_theta=10000.0)}
 TAILS = [0, 1, 37, 300, 600]
 
 
@@ -53,7 +56,7 @@ def packed_oracle_cache(akv, w, p, params=None):
     comps = []
     for u in range(w.units):
         c = O.compress_unit(K64[u], V64[u], Q64[u], w.q_per_kv, w.n_obs, w.theta, w.window, w.elem_bytes,
-                            **(params or {}))
+                            **oracle_params(params))
         comps.append(c)
         cache_h[u * p.unit_stride: u * p.unit_stride + p.unit_bytes] = np.frombuffer(
             akv.pack_unit(p, oracle_arrays(c, code)), np.uint8)
@@ -95,7 +98,7 @@ def test_decode_tail_parity(akv, name):
         akv.decode_attn_tail(p, cache, q, Kg, Vg, n, o, dws)
         torch.cuda.synchronize()
         o_h = o.cpu().numpy().astype(np.float64)
-        if n == 0:   # the same launches as decode_attn (float LDS atomics: equal up to summation order)
+        if n == 0:   # the same launches as decode_attn
             assert torch.allclose(o, o_plain, rtol=1e-5, atol=1e-6), "empty tail must reproduce decode_attn"
         worst = 0.0
         K64t, V64t = kvsynth.to_f64(Kt[:, :, :n]), kvsynth.to_f64(Vt[:, :, :n])
