@@ -139,8 +139,11 @@ def measure_variant(akv, w, K, V, Q, q, stream, reps=3, **kw):
     parameters (kw: codec, pool_kv_jointly, ...), outside the timed steps:
     HIP-event stage times, median over reps of the per-call sums."""
     import torch
-    p = akv.plan(w.units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs,
-                 akv.BF16 if w.dtype == "bf16" else akv.F32, w.theta, w.window, **kw)
+    try:
+        p = akv.plan(w.units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs,
+                     akv.BF16 if w.dtype == "bf16" else akv.F32, w.theta, w.window, **kw)
+    except akv.AnchorKVError as e:   # a variant this workload's shape does not allow
+        return {"params": kw, "refused": str(e)}
     cache, ws, dws = akv.alloc(p, K.device)
     o = torch.empty(w.units, w.kv_heads * w.q_per_kv, w.head_dim, dtype=torch.float32, device=K.device)
     akv.compress(p, K, V, Q, cache, ws, stream)
@@ -244,7 +247,8 @@ def kernel_stage(name):
         return {0: "obs_stats", 1: "obs_score", 2: "obs_util", 3: "util_fix"}[int(m.group(1))]
     for key, stage in (("k_ml_combine", "ml_combine"), ("k_o_combine", "o_combine"), ("k_select", "select"),
                        ("k_assign", "assign"), ("k_topr", "topr"), ("k_quant", "quant"), ("k_headers", "headers"),
-                       ("k_dec_stream", "dec_stream"), ("k_dec_merge", "dec_stream"), ("k_dec_tail", "dec_tail"),
+                       ("k_dec_stream", "dec_stream"), ("k_dec_rope", "dec_stream"), ("k_dec_merge", "dec_stream"),
+                       ("k_dec_tail", "dec_tail"), ("k_rope_table", "obs_stats"),
                        ("k_zero_u32", "zero")):
         if key in name:
             return stage
@@ -373,9 +377,11 @@ def main():
     extras = not args.no_extras
     tail_rec = measure_tail(akv, w, p, cache, qs[0], o, dws, stream, args.tail) if extras and args.tail > 0 else None
     unit_rec = measure_one_unit(akv, w, cache, p, qs[0], stream) if extras else None
-    # the same inputs under the paper's codec and under the joint key/value ranking
+    # the same inputs under the paper's codec, the joint key/value ranking and
+    # pre-RoPE key storage (the keys taken as pre-RoPE; refused where the
+    # shape has more than 128 observation queries per KV head)
     variants = [measure_variant(akv, w, K, V, Q, qs[0], stream, **kw)
-                for kw in (dict(codec=1), dict(pool_kv_jointly=1))] if extras else None
+                for kw in (dict(codec=1), dict(pool_kv_jointly=1), dict(rope=1))] if extras else None
     total_s = t1 - t0
     ms_per_step = total_s * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)

@@ -1167,11 +1167,13 @@ __global__ __launch_bounds__(256) void k_dec_rope(DecArgs a) {
   using M = Mfma<ANCHORKV_BF16>;
   constexpr int D = kHeadDim, TT = 64, P = D / 2;
   constexpr int EPC = 16 / (int)sizeof(T);    // elements per 16-byte load
-  __shared__ __align__(16) float2 ftab[TT][P];       // e^{i j theta_p}, j < 64
+  // rows padded so that the 16 tokens (or q-heads) of one MFMA operand read
+  // fall on different LDS banks
+  __shared__ __align__(16) float2 ftab[TT][P + 2];   // e^{i j theta_p}, j < 64
   __shared__ __align__(16) float2 e0[P];             // e^{i t0 theta_p} of the tile
-  __shared__ __align__(16) uint16_t vh[TT][D];       // rebuilt value rows, bf16 hi
-  __shared__ __align__(16) uint16_t vl[TT][D];       // and lo
-  __shared__ __align__(16) float ps[16][TT];         // logits, then p (rows >= G stay zero)
+  __shared__ __align__(16) uint16_t vh[TT][D + 8];   // rebuilt value rows, bf16 hi
+  __shared__ __align__(16) uint16_t vl[TT][D + 8];   // and lo
+  __shared__ __align__(16) float ps[16][TT + 4];     // logits, then p (rows >= G stay zero)
   __shared__ uint2 wds[TT];                          // the tile's pointer words (K, V)
   __shared__ unsigned long long fmask[2];            // residual flags of the tile's tokens per side
   __shared__ int rbase[2];                           // record of the tile's first flagged token per side
@@ -1234,18 +1236,31 @@ __global__ __launch_bounds__(256) void k_dec_rope(DecArgs a) {
     sincos((double)j * theta_l, &sn, &cn);
     ftab[j][lane] = make_float2((float)cn, (float)sn);
   }
-  for (int i = tid; i < 16 * TT; i += 256) (&ps[0][0])[i] = 0.0f;
+  for (int i = tid; i < 16 * (TT + 4); i += 256) (&ps[0][0])[i] = 0.0f;
   if (tid < kMaxG) { mrun[tid] = -INFINITY; lrun[tid] = 0.0f; }
   int run_k = 0, run_v = 0;   // wave 0: flagged tokens of the current chunk before the tile
   f32x4 oacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 
+  // wave 0 holds the next tile's pointer words and e^{i t0 theta} in
+  // registers: the words are loaded a tile ahead, the phase advances by
+  // e^{i 64 theta} per tile and is recomputed exactly at every 1024-token chunk
+  uint2 wd_n = make_uint2(0u, 0u);
+  float2 e0_n = make_float2(1.0f, 0.0f), p64 = make_float2(1.0f, 0.0f);
+  if (wave == 0) {
+    double sn, cn;
+    sincos(64.0 * theta_l, &sn, &cn);
+    p64 = make_float2((float)cn, (float)sn);
+    if (t_beg + lane < t_end) wd_n = *reinterpret_cast<const uint2*>(words + (int64_t)(t_beg + lane) * 2);
+    sincos((double)t_beg * theta_l, &sn, &cn);
+    e0_n = make_float2((float)cn, (float)sn);
+  }
+
   for (int t0 = t_beg; t0 < t_end; t0 += TT) {
-    // ---- wave 0: words, flags, record bases, e^{i t0 theta}
+    // ---- wave 0: publish the tile's words, flags, record bases and phase,
+    // then start on the next tile's
     if (wave == 0) {
       if ((t0 & (kTile - 1)) == 0) { run_k = 0; run_v = 0; }
-      const int t = t0 + lane;
-      uint2 wd = make_uint2(0u, 0u);
-      if (t < t_end) wd = *reinterpret_cast<const uint2*>(words + (int64_t)t * 2);
+      const uint2 wd = wd_n;
       wds[lane] = wd;
       const unsigned long long mk = __ballot((wd.x & 0x8000u) != 0);
       const unsigned long long mv = __ballot((wd.y & 0x8000u) != 0);
@@ -1257,38 +1272,71 @@ __global__ __launch_bounds__(256) void k_dec_rope(DecArgs a) {
       }
       run_k += __popcll(mk);
       run_v += __popcll(mv);
-      double sn, cn;
-      sincos((double)t0 * theta_l, &sn, &cn);
-      e0[lane] = make_float2((float)cn, (float)sn);
+      e0[lane] = e0_n;
+      const int t1 = t0 + TT;
+      wd_n = make_uint2(0u, 0u);
+      if (t1 + lane < t_end) wd_n = *reinterpret_cast<const uint2*>(words + (int64_t)(t1 + lane) * 2);
+      if ((t1 & (kTile - 1)) == 0) {
+        double sn, cn;
+        sincos((double)t1 * theta_l, &sn, &cn);
+        e0_n = make_float2((float)cn, (float)sn);
+      } else {
+        e0_n = make_float2(e0_n.x * p64.x - e0_n.y * p64.y, e0_n.x * p64.y + e0_n.y * p64.x);
+      }
     }
     __syncthreads();
 
+    // ---- every gather of the tile first (anchor rows and records of the
+    // key and the value side), then the arithmetic
+    const int j = 16 * wave + col;               // key side: this lane's token
+    const uint32_t wk = wds[j].x;
+    const int r = tid >> 2, qq = tid & 3;        // value side: token r, coordinates 32 qq .. + 31
+    const uint32_t wv = wds[r].y;
+    uint4 kraw[4][8 / EPC], vraw[32 / EPC];
+    {
+      const T* ar = AK + (int64_t)(wk & 0x7FFF) * D;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 8 / EPC; ++i) kraw[st][i] = *reinterpret_cast<const uint4*>(ar + 32 * st + 8 * kg + EPC * i);
+      const T* vr = AV + (int64_t)(wv & 0x7FFF) * D + 32 * qq;
+#pragma unroll
+      for (int i = 0; i < 32 / EPC; ++i) vraw[i] = *reinterpret_cast<const uint4*>(vr + EPC * i);
+    }
+    // key record: code words 8 (kg & 1) .. + 7 (coordinates 32 st + 8 kg + e
+    // lie in code word 8 (kg & 1) + e, plane 2 st + kg / 2) and the four
+    // (scale, zero) words; value record: all 16 code words and the (scale,
+    // zero) of group qq
+    uint4 kcw = make_uint4(0, 0, 0, 0), ksz = make_uint4(0, 0, 0, 0), vc01 = kcw, vc23 = kcw;
+    uint32_t vsz = 0;
+    if (wk & 0x8000u) {
+      const uint8_t* rp = recK + (int64_t)(rbase[0] + __popcll(fmask[0] & ((1ull << j) - 1ull))) * kRecBytes;
+      kcw = *reinterpret_cast<const uint4*>(rp + 16 * (kg & 1));
+      ksz = *reinterpret_cast<const uint4*>(rp + 32);
+    }
+    if (wv & 0x8000u) {
+      const uint8_t* rp = recV + (int64_t)(rbase[1] + __popcll(fmask[1] & ((1ull << r) - 1ull))) * kRecBytes;
+      vc01 = *reinterpret_cast<const uint4*>(rp);
+      vc23 = *reinterpret_cast<const uint4*>(rp + 16);
+      vsz = *reinterpret_cast<const uint32_t*>(rp + 32 + 4 * qq);
+    }
+
     // ---- keys of wave w's 16 tokens: rebuild, rotate, logits on MFMA
     {
-      const int j = 16 * wave + col, t = t0 + j;
-      const bool valid = t < t_end;
-      const uint32_t wk = wds[j].x;
       const float gk = h2f((uint16_t)(wk >> 16));
-      const T* ar = AK + (int64_t)(wk & 0x7FFF) * D;
       float x[4][8];
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int e0i = 0; e0i < 8; e0i += EPC) {
+        for (int i = 0; i < 8 / EPC; ++i) {
           T v[EPC];
-          *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(ar + 32 * st + 8 * kg + e0i);
+          *reinterpret_cast<uint4*>(v) = kraw[st][i];
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) x[st][e0i + e] = gk * Elem<DT>::f(v[e]);
+          for (int e = 0; e < EPC; ++e) x[st][EPC * i + e] = gk * Elem<DT>::f(v[e]);
         }
       if (wk & 0x8000u) {
-        // the token's key record: code words 8 (kg & 1) .. + 7 (coordinates
-        // 32 st + 8 kg + e lie in code word 8 (kg & 1) + e, plane 2 st + kg / 2)
-        const int rk = rbase[0] + __popcll(fmask[0] & ((1ull << j) - 1ull));
-        const uint8_t* rp = recK + (int64_t)rk * kRecBytes;
-        const uint4 cw = *reinterpret_cast<const uint4*>(rp + 16 * (kg & 1));
-        const uint4 sz = *reinterpret_cast<const uint4*>(rp + 32);
-        const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
-        const uint32_t szs[4] = {sz.x, sz.y, sz.z, sz.w};
+        const uint32_t cws[4] = {kcw.x, kcw.y, kcw.z, kcw.w};
+        const uint32_t szs[4] = {ksz.x, ksz.y, ksz.z, ksz.w};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const float sc = h2f((uint16_t)(szs[st] & 0xFFFFu)), zr = h2f((uint16_t)(szs[st] >> 16));
@@ -1323,34 +1371,26 @@ __global__ __launch_bounds__(256) void k_dec_rope(DecArgs a) {
       }
       if (col < G)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jr = 16 * wave + 4 * kg + r;
-          ps[col][jr] = t0 + jr < t_end ? acc[r] * a.c : -INFINITY;
+        for (int rr = 0; rr < 4; ++rr) {
+          const int jr = 16 * wave + 4 * kg + rr;
+          ps[col][jr] = t0 + jr < t_end ? acc[rr] * a.c : -INFINITY;
         }
-      (void)valid;
     }
     // ---- values: thread (token r, quarter qq) rebuilds coordinates 32 qq .. + 31
     {
-      const int r = tid >> 2, qq = tid & 3, t = t0 + r;
-      const uint32_t wv = wds[r].y;
       const float gv = h2f((uint16_t)(wv >> 16));
-      const T* vr = AV + (int64_t)(wv & 0x7FFF) * D + 32 * qq;
       float v[32];
 #pragma unroll
-      for (int i = 0; i < 32; i += EPC) {
-        T x[EPC];
-        *reinterpret_cast<uint4*>(x) = *reinterpret_cast<const uint4*>(vr + i);
+      for (int i = 0; i < 32 / EPC; ++i) {
+        T xx[EPC];
+        *reinterpret_cast<uint4*>(xx) = vraw[i];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) v[i + e] = gv * Elem<DT>::f(x[e]);
+        for (int e = 0; e < EPC; ++e) v[EPC * i + e] = gv * Elem<DT>::f(xx[e]);
       }
       if (wv & 0x8000u) {
         // coordinate 32 qq + e: code word e & 15, plane 2 qq + e / 16; group qq
-        const int rv = rbase[1] + __popcll(fmask[1] & ((1ull << r) - 1ull));
-        const uint8_t* rp = recV + (int64_t)rv * kRecBytes;
-        const uint4 c01 = *reinterpret_cast<const uint4*>(rp), c23 = *reinterpret_cast<const uint4*>(rp + 16);
-        const uint32_t cw[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
-        const uint32_t szv = *reinterpret_cast<const uint32_t*>(rp + 32 + 4 * qq);
-        const float sc = h2f((uint16_t)(szv & 0xFFFFu)), zr = h2f((uint16_t)(szv >> 16));
+        const uint32_t cw[8] = {vc01.x, vc01.y, vc01.z, vc01.w, vc23.x, vc23.y, vc23.z, vc23.w};
+        const float sc = h2f((uint16_t)(vsz & 0xFFFFu)), zr = h2f((uint16_t)(vsz >> 16));
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
           const int jw = e & 15, sh = 2 * (2 * qq + (e >> 4));
@@ -1358,7 +1398,7 @@ __global__ __launch_bounds__(256) void k_dec_rope(DecArgs a) {
           v[e] += fmaf(sc, (float)code, zr);
         }
       }
-      if (t >= t_end)
+      if (t0 + r >= t_end)
 #pragma unroll
         for (int e = 0; e < 32; ++e) v[e] = 0.0f;
 #pragma unroll
