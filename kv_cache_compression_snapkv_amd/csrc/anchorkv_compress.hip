@@ -1184,7 +1184,9 @@ static int launch_obs_rope(const anchorkv_plan_info& p, const ObsArgs& a, hipStr
   const int QB = a.GQp / 16;
   if (QB > 8) return fail(ANCHORKV_E_SHAPE, "pre-RoPE keys: q_per_kv*n_obs must be <= 128");
   const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1));
-  k_obs<ANCHORKV_F32, MODE, 1, DT, true><<<grid, dim3(64 * QB), 0, st>>>(a);
+  // bf16: rotated keys as bf16 hi + lo on the bf16 MFMA; f32: f32 MFMA
+  if constexpr (DT == ANCHORKV_BF16) k_obs<ANCHORKV_BF16, MODE, 1, ANCHORKV_BF16, true><<<grid, dim3(64 * QB), 0, st>>>(a);
+  else k_obs<ANCHORKV_F32, MODE, 1, ANCHORKV_F32, true><<<grid, dim3(64 * QB), 0, st>>>(a);
   AKV_CHECK_LAUNCH("k_obs (pre-RoPE keys)");
   return 0;
 }

@@ -92,12 +92,14 @@ __device__ __forceinline__ void rope4(float (&x0)[4], float (&x1)[4], const floa
 }
 
 // DT: the arithmetic (tile and MFMA) type; SRC: the storage type of K, V, Q
-// and the cache's anchors (== DT except with pre-RoPE keys); ROPE: K holds
-// pre-RoPE keys (Pith review, "Assumptions & free parameters": R_t is a
-// per-position orthogonal map), rotated here at their positions while the
-// tile is staged (f32 arithmetic), and in UTIL the gathered anchor row of
+// and the cache's anchors (== DT except with pre-RoPE keys in f32
+// arithmetic); ROPE: K holds pre-RoPE keys (Pith review, "Assumptions & free
+// parameters": R_t is a per-position orthogonal map), rotated here at their
+// positions while the tile is staged, and in UTIL the gathered anchor row of
 // each token is rotated at the token's position, so <q, R_t k_t> -
-// gamma_t <q, R_t k_a(t)> = <q, R_t r_t>.
+// gamma_t <q, R_t k_a(t)> = <q, R_t r_t>.  In bf16 arithmetic the rotated
+// rows are kept as bf16 hi + lo (two tiles, two MFMAs per step; about 16
+// significant bits), the queries and values stay exact.
 template <int DT, int MODE, int QPW, int SRC = DT, bool ROPE = false>
 __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
   using C = ObsCfg<DT>;
@@ -107,10 +109,13 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
   using frag = typename M::frag;
   constexpr int D = C::D, LDK = C::LDK, NSTEP = C::NSTEP, LDVT = C::LDVT;
   static_assert(SRC == DT || (ROPE && DT == ANCHORKV_F32), "storage differs from arithmetic only for pre-RoPE keys");
+  constexpr bool SPLIT = ROPE && DT == ANCHORKV_BF16;   // rotated rows as bf16 hi + lo
 
   __shared__ __attribute__((aligned(16))) T Ks[64 * LDK];
   __shared__ __attribute__((aligned(16))) T Vs[(MODE == OBS_STATS) ? 16 : (MODE == OBS_SCORE ? D * LDVT : 64 * LDK)];
   __shared__ __attribute__((aligned(16))) T Gs[(MODE == OBS_UTIL) ? 64 * LDK : 16];
+  __shared__ __attribute__((aligned(16))) T Ks2[SPLIT ? 64 * LDK : 8];                        // lo parts
+  __shared__ __attribute__((aligned(16))) T Gs2[(SPLIT && MODE == OBS_UTIL) ? 64 * LDK : 8];
   __shared__ float colpart[8][64];
   __shared__ float vv_s[64];
   __shared__ float gam_s[64];
@@ -196,13 +201,24 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
           ld4f<SRC>(Kp + (int64_t)t * D + 64 + i0, x1);
           rope4(x0, x1, a.rope_cs + (int64_t)t * (D / 2) + i0);
         }
-        *reinterpret_cast<float4*>(&Ks[r * LDK + i0]) = make_float4(x0[0], x0[1], x0[2], x0[3]);
-        *reinterpret_cast<float4*>(&Ks[r * LDK + 64 + i0]) = make_float4(x1[0], x1[1], x1[2], x1[3]);
+        // four rotated coordinates into a tile row: f32, or bf16 hi (and lo)
+        auto put4 = [&](T* hi, T* lo, int off, const float (&x)[4]) {
+          if constexpr (SPLIT) {
+            uint16_t h4[4], l4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { h4[i] = f2bf(x[i]); l4[i] = f2bf(x[i] - bf2f(h4[i])); }
+            *reinterpret_cast<uint2*>(&hi[off]) = make_uint2(h4[0] | (uint32_t)h4[1] << 16, h4[2] | (uint32_t)h4[3] << 16);
+            *reinterpret_cast<uint2*>(&lo[off]) = make_uint2(l4[0] | (uint32_t)l4[1] << 16, l4[2] | (uint32_t)l4[3] << 16);
+          } else {
+            (void)lo;
+            *reinterpret_cast<float4*>(&hi[off]) = make_float4(x[0], x[1], x[2], x[3]);
+          }
+        };
+        put4(Ks, Ks2, r * LDK + i0, x0);
+        put4(Ks, Ks2, r * LDK + 64 + i0, x1);
         if constexpr (MODE == OBS_UTIL) {
-          float v0[4] = {0, 0, 0, 0}, v1[4] = {0, 0, 0, 0}, g0[4] = {0, 0, 0, 0}, g1[4] = {0, 0, 0, 0};
+          float g0[4] = {0, 0, 0, 0}, g1[4] = {0, 0, 0, 0};
           if (t < k1) {
-            ld4f<SRC>(Vp + (int64_t)t * D + i0, v0);
-            ld4f<SRC>(Vp + (int64_t)t * D + 64 + i0, v1);
             const int an = a.aidx[((int64_t)u * 2 * H + h) * N + t];  // side 0 = K
             const S* ap = reinterpret_cast<const S*>(a.cache + (int64_t)u * a.stride + a.off_anchor_k) +
                           ((int64_t)h * a.A + an) * D;
@@ -210,13 +226,29 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
             ld4f<SRC>(ap + 64 + i0, g1);
             rope4(g0, g1, a.rope_cs + (int64_t)t * (D / 2) + i0);
           }
-          *reinterpret_cast<float4*>(&Vs[r * LDK + i0]) = make_float4(v0[0], v0[1], v0[2], v0[3]);
-          *reinterpret_cast<float4*>(&Vs[r * LDK + 64 + i0]) = make_float4(v1[0], v1[1], v1[2], v1[3]);
-          *reinterpret_cast<float4*>(&Gs[r * LDK + i0]) = make_float4(g0[0], g0[1], g0[2], g0[3]);
-          *reinterpret_cast<float4*>(&Gs[r * LDK + 64 + i0]) = make_float4(g1[0], g1[1], g1[2], g1[3]);
+          put4(Gs, Gs2, r * LDK + i0, g0);
+          put4(Gs, Gs2, r * LDK + 64 + i0, g1);
+          if constexpr (SPLIT) {
+            // values stay exact bf16: 8-byte copies
+            uint2 v0 = make_uint2(0, 0), v1 = make_uint2(0, 0);
+            if (t < k1) {
+              v0 = *reinterpret_cast<const uint2*>(Vp + (int64_t)t * D + i0);
+              v1 = *reinterpret_cast<const uint2*>(Vp + (int64_t)t * D + 64 + i0);
+            }
+            *reinterpret_cast<uint2*>(&Vs[r * LDK + i0]) = v0;
+            *reinterpret_cast<uint2*>(&Vs[r * LDK + 64 + i0]) = v1;
+          } else {
+            float v0[4] = {0, 0, 0, 0}, v1[4] = {0, 0, 0, 0};
+            if (t < k1) {
+              ld4f<SRC>(Vp + (int64_t)t * D + i0, v0);
+              ld4f<SRC>(Vp + (int64_t)t * D + 64 + i0, v1);
+            }
+            *reinterpret_cast<float4*>(&Vs[r * LDK + i0]) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+            *reinterpret_cast<float4*>(&Vs[r * LDK + 64 + i0]) = make_float4(v1[0], v1[1], v1[2], v1[3]);
+          }
         }
       }
-      if constexpr (MODE == OBS_SCORE) {
+      if constexpr (MODE == OBS_SCORE && !SPLIT) {
         // transposed value tile Vt[d][key] as floats; consecutive threads take consecutive keys
         for (int it = threadIdx.x; it < 64 * (D / 4); it += blockDim.x) {
           const int r = it % 64, d0 = (it / 64) * 4;
@@ -247,7 +279,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
         *reinterpret_cast<uint4*>(&Gs[r * LDK + cc * EPC]) = g;
       }
     }
-    if constexpr (MODE == OBS_SCORE && !ROPE) {
+    if constexpr (MODE == OBS_SCORE && (!ROPE || SPLIT)) {
       // transposed value tile Vt[d][key]; consecutive threads take consecutive keys
       for (int ch = threadIdx.x; ch < 64 * CPR; ch += blockDim.x) {
         const int r = ch % 64, cc = ch / 64;
@@ -290,13 +322,17 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       frag af[2][NSTEP];
       frag gf[(MODE == OBS_UTIL) ? 2 : 1][NSTEP];
       frag vf[(MODE == OBS_UTIL) ? 2 : 1][NSTEP];
+      frag af2[SPLIT ? 2 : 1][SPLIT ? NSTEP : 1];
+      frag gf2[(SPLIT && MODE == OBS_UTIL) ? 2 : 1][(SPLIT && MODE == OBS_UTIL) ? NSTEP : 1];
       for (int k2 = 0; k2 < 2; ++k2) {
         const int row = (c2 * 2 + k2) * 16 + col;
         for (int st = 0; st < NSTEP; ++st) {
           const int kk = st * M::KSTEP + kg * M::KW;
           af[k2][st] = M::load(&Ks[row * LDK + kk]);
+          if constexpr (SPLIT) af2[k2][st] = M::load(&Ks2[row * LDK + kk]);
           if constexpr (MODE == OBS_UTIL) {
             gf[k2][st] = M::load(&Gs[row * LDK + kk]);
+            if constexpr (SPLIT) gf2[k2][st] = M::load(&Gs2[row * LDK + kk]);
             vf[k2][st] = M::load(&Vs[row * LDK + kk]);
           }
         }
@@ -323,8 +359,12 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
           const int kb = c2 * 2 + k2;
           f32x4 acc = {0, 0, 0, 0}, accg = {0, 0, 0, 0}, accv = {0, 0, 0, 0};
           for (int st = 0; st < NSTEP; ++st) acc = M::mma(af[k2][st], qf[qi][st], acc);
+          if constexpr (SPLIT)
+            for (int st = 0; st < NSTEP; ++st) acc = M::mma(af2[k2][st], qf[qi][st], acc);
           if constexpr (MODE == OBS_UTIL) {
             for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf[k2][st], qf[qi][st], accg);
+            if constexpr (SPLIT)
+              for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf2[k2][st], qf[qi][st], accg);
             for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[k2][st], ofh[qi][st], accv);
             if constexpr (DT == ANCHORKV_BF16)
               for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[k2][st], ofl[qi][st], accv);
