@@ -1252,9 +1252,15 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
   g.util = oa.util;
   g.H = H; g.N = N; g.A = A;
   const int64_t hs = (int64_t)U * 2 * H;
-  // 8-wave blocks, two per compute unit, when a part's anchors fit twice in LDS
-  const int part_a = std::min(A, kAssignResMax);
-  const bool w8 = A <= kAssignResMax && 2 * assign_lds_bytes(part_a, 8) <= 160 * 1024;
+  // 8-wave blocks, two per compute unit, when a part's anchors fit twice in
+  // LDS; larger anchor sets are walked in the fewest equal parts of at most
+  // kAssignPartMax anchors by 16-wave blocks (each part reload is a barrier,
+  // a copy and a wait for the whole compute unit)
+  const bool multi = A > kAssignResMax;
+  const int nparts = multi ? (A + kAssignPartMax - 1) / kAssignPartMax : 1;
+  g.part = multi ? (int)round_up((A + nparts - 1) / nparts, 16) : A;
+  const int part_a = std::min(A, g.part);
+  const bool w8 = !multi && 2 * assign_lds_bytes(part_a, 8) <= 160 * 1024;
   const int waves = w8 ? 8 : 16;
   const int ntiles_hs = (N + 64 * waves - 1) / (64 * waves);
   // tiles per block: fewest rounds of resident blocks times (tiles + a prologue
@@ -1277,7 +1283,7 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
     // anchors in parts reloaded every tile: the blocks of a (unit, side,
     // head) run together on one XCD (32 compute units) so that the reloads
     // hit its L2
-    const int nb = 32;
+    const int nb = 32;   // one block on each of the XCD's 32 compute units
     g.tiles_per_block = (ntiles_hs + nb - 1) / nb;
     g.nblk = (ntiles_hs + g.tiles_per_block - 1) / g.tiles_per_block;
     g.xcd_groups = (int)hs;
@@ -1298,7 +1304,7 @@ static int launch_assign_bf16(const anchorkv_plan_info& p, const CompressWs& w, 
     }
   } else {
     // the parts are walked inside the kernel (tokens read once)
-    const size_t lds = assign_lds_bytes(kAssignResMax, 16);
+    const size_t lds = assign_lds_bytes(g.part, 16);
     static size_t done = 0;
     if (int rc = set_dyn_lds(reinterpret_cast<const void*>(&k_assign_res<true, 16>), lds, &done)) return rc;
     k_assign_res<true, 16><<<grid, 64 * 16, lds, st>>>(g);

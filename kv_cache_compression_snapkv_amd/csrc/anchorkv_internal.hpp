@@ -21,7 +21,8 @@ constexpr int kHeadDim = 128;         // the only supported head dim
 constexpr uint32_t kMagic = 0x31564B41u;  // "AKV1"
 constexpr int kMaxAnchors = 32767;
 constexpr int kHistBins = 2048;       // radix-select digit bins (11 bits)
-constexpr int kAssignResMax = 512;    // anchors per LDS-resident part of the bf16 assignment
+constexpr int kAssignResMax = 512;    // anchors per head held in LDS at once by the bf16 assignment
+constexpr int kAssignPartMax = 576;   // larger sets: at most this many anchors per part (one block per compute unit)
 
 void set_error(const char* fmt, ...);
 int fail(int code, const char* fmt, ...);

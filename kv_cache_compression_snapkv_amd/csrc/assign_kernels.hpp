@@ -81,6 +81,7 @@ struct AssignArgs {
   int H, N, A, a0, a1;       // anchors [a0, a1) of this launch
   int tiles_per_block, nblk;  // token tiles per block, blocks per (unit, side, head)
   int xcd_groups;             // > 0: XCD-grouped order (see k_assign_res), the number of (unit, side, head) groups
+  int part;                   // MULTI: anchors per LDS part (a multiple of 16)
 };
 
 // Projection epilogue of one 16-token row block: lane (col, kg) holds
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
   const int u = bid / 2;
   const int N = g.N, A = g.A;
   const int64_t uh = (int64_t)u * g.H + h;
-  const int pa = MULTI ? kAssignResMax : A;           // anchors per part
+  const int pa = MULTI ? g.part : A;                  // anchors per part
   const int nparts = (A + pa - 1) / pa;
   const int nab_max = (pa + 15) >> 4;
   uint4* As = dyn_lds;                                            // [nab*16 rows][16 chunks], swizzled
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
             run[rb] = max3f(max3f(run[rb], k[0], k[1]), k[2], k[3]);
         }
       }
-      const int ge = (gab0 + e) >> 3;   // global epoch of these blocks
+      const int ge = gab0 + e;          // first block of this epoch (parts need not start on an epoch of the head)
       for (int rb = 0; rb < 4; ++rb) {
         const unsigned b = __float_as_uint(run[rb]);
         const float m = __uint_as_float(b & keymask);
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
     int best_a[4];
     for (int rb = 0; rb < 4; ++rb) {
       const int li = 31 - (bix[rb] & 31);
-      int a = (((bix[rb] >> 5) << 3) + (li >> 2)) * 16 + kg * 4 + (li & 3);
+      int a = ((bix[rb] >> 5) + (li >> 2)) * 16 + kg * 4 + (li & 3);
       a = min(a, A - 1);
       float v = bv[rb];
       const auto v32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
