@@ -278,7 +278,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
       for (int rb = 0; rb < 4; ++rb) {
         const unsigned b = __float_as_uint(run[rb]);
         const float m = __uint_as_float(b & keymask);
-        if (m > bv[rb]) {
+        // the larger value, the earlier epoch on equal values (parts are
+        // visited in either order)
+        if (m > bv[rb] || (m == bv[rb] && ge < (bix[rb] >> 5))) {
           bv[rb] = m;
           bix[rb] = (ge << 5) | (int)(b & 31u);
         }
@@ -286,6 +288,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
     }
   };
 
+  int loaded = -1;   // the part in LDS (MULTI)
   for (int tile = tile0; tile < tile1; ++tile) {
     // per-token scalars of the epilogue, copied into this wave's LDS slots
     // while the search runs (no registers held across it)
@@ -296,14 +299,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
     }
     float bv[4];
     int bix[4];
-    for (int rb = 0; rb < 4; ++rb) { bv[rb] = -__builtin_inff(); bix[rb] = 0; }
-    for (int part = 0; part < nparts; ++part) {
+    for (int rb = 0; rb < 4; ++rb) { bv[rb] = -__builtin_inff(); bix[rb] = 0x7FFFFFFF; }
+    // odd tiles walk the parts backwards, so the part in LDS at the end of a
+    // tile serves the start of the next one without a reload
+    const bool back = MULTI && ((tile - tile0) & 1);
+    for (int pi = 0; pi < nparts; ++pi) {
+      const int part = back ? nparts - 1 - pi : pi;
       const int a0 = part * pa, a1 = min(A, a0 + pa);
-      if (MULTI) {
+      if (MULTI && part != loaded) {
         __syncthreads();          // every wave is done with the previous part
         load_part(a0, a1);
         __builtin_amdgcn_s_waitcnt(AKV_VMCNT_IMM(0));
         __syncthreads();
+        loaded = part;
       }
       search_part((a1 - a0 + 15) >> 4, a0 >> 4, bv, bix);
     }
