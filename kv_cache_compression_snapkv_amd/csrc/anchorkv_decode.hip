@@ -19,8 +19,9 @@
 //    (max, sum, output) triples.
 // Residual records are handled in batches on MFMA.  A code c enters as an
 // exact bf16 value 128 + c * 4^m (one AND-OR per pair of codes) and the
-// constant part is cancelled exactly.  Keys: rows = records, columns =
-// (q-head, group), so one 16x16 tile serves 4 q-heads x 4 groups.  Values:
+// constant part is cancelled exactly.  Keys: rows = (q-head, group),
+// columns = records, so one 16x16 tile serves 4 q-heads x 4 groups and a
+// lane holds the four groups of one q-head and record.  Values:
 // rows = (q-head, group), K = records, columns = coordinates; A = p * scale
 // split into bf16 hi + lo.
 // One workgroup (8 waves) per (unit, head, 1024-token-aligned range).  The
@@ -539,17 +540,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     return (uint32_t)__builtin_amdgcn_readfirstlane(min(max(n, 0), 16) * RB);
   };
   // key batch: lane (col, kg) holds bytes 8kg..8kg+7 of record col and the
-  // (scale, zero) word of group col & 3 of records 4kg + r
+  // (scale, zero) words of record col's four groups (Hadamard / Lloyd-Max:
+  // the scales of records 4kg + r)
   uint2 kx;
   uint32_t ksz[4];
   auto load_keys = [&](int kb, int nk, uint2& x, uint32_t (&sz)[4]) {
     const __amdgpu_buffer_rsrc_t r = buf_rsrc(recK + (int64_t)kb * RB, run_bytes(nk));
     const auto xx = __builtin_amdgcn_raw_buffer_load_b64(r, col * RB + 8 * kg, 0, 0);
     x = make_uint2(xx[0], xx[1]);
-    // (scale, zero) of group col & 3, or the scale of the Hadamard / Lloyd-Max record
+    if constexpr (HLM) {
+      // the scale of records 4kg + rr (rows of the Hadamard / Lloyd-Max key MFMA)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      sz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * RB + 32 + (HLM ? 0 : 4 * (col & 3)), 0, 0);
+      for (int rr = 0; rr < 4; ++rr) sz[rr] = __builtin_amdgcn_raw_buffer_load_b32(r, (4 * kg + rr) * RB + 32, 0, 0);
+    } else {
+      // the (scale, zero) words of the four groups of record col
+      const uint4 v = buf_load16(r, col * RB + 32);
+      sz[0] = v.x; sz[1] = v.y; sz[2] = v.z; sz[3] = v.w;
+    }
   };
   // value batch: code word col of records 4kg + e (pairs packed), and the
   // (scale, zero) word of group col & 3 of the same records
@@ -633,37 +640,47 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
       }
       return;
     }
-    bf16x8 af[4];
+    // code fragments as the B operand (K-slice of record col), the query
+    // fragments as the A operand: the rows are (q-head, group) pairs kappa =
+    // 16 cb + 4 kg + r, so a lane's four accumulators are the four groups of
+    // one q-head and one record, and the groups' scales and zeros combine in
+    // the lane
+    bf16x8 bf[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const Plane p0 = plane_of(2 * st), p1 = plane_of(2 * st + 1);
       const int i0 = p0.sh / 6, i1 = p1.sh / 6;
-      af[st] = u4_to_frag(and_or(xs[i0][0], MK[p0.m], vbias), and_or(xs[i0][1], MK[p0.m], vbias),
+      bf[st] = u4_to_frag(and_or(xs[i0][0], MK[p0.m], vbias), and_or(xs[i0][1], MK[p0.m], vbias),
                           and_or(xs[i1][0], MK[p1.m], vbias), and_or(xs[i1][1], MK[p1.m], vbias));
+    }
+    float scg[4], zrg[4];   // (scale, zero) of the four groups of record col
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      scg[r] = h2f((uint16_t)(sz[r] & 0xFFFFu));
+      zrg[r] = h2f((uint16_t)(sz[r] >> 16));
     }
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-      const float2 qc = qcs[cb * 64 + lane];  // (sum of q, initial accumulator)
-      f32x4 cacc = {qc.y, qc.y, qc.y, qc.y};
+      // (sum of q over the group, initial accumulator) of rows 16 cb + 4 kg + r
+      const float4 qa = *reinterpret_cast<const float4*>(&qcs[cb * 64 + 4 * kg]);
+      const float4 qb = *reinterpret_cast<const float4*>(&qcs[cb * 64 + 4 * kg + 2]);
+      f32x4 cacc = {qa.y, qa.w, qb.y, qb.w};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH][lane]), cacc);
-        if constexpr (QSPLIT) cacc = M::mma(af[st], bits_to_frag(qbs[(cb * 4 + st) * QH + 1][lane]), cacc);
+        cacc = M::mma(bits_to_frag(qbs[(cb * 4 + st) * QH][lane]), bf[st], cacc);
+        if constexpr (QSPLIT) cacc = M::mma(bits_to_frag(qbs[(cb * 4 + st) * QH + 1][lane]), bf[st], cacc);
       }
-      const int kap = 16 * cb + col, g = kap >> 2, grp = kap & 3;
-      // the four lanes of a quad hold the same sum and write the same value;
-      // rows past the run (ii >= nk, still below the wave's TT rows since the
-      // batch starts below nk) take values no one reads: key logits are read
-      // for ranks below nk only, and the value weights and zeros are written
-      // over every row the value batches read before they read it
-      const bool wr = g < G;
+      const float qsum[4] = {qa.x, qa.z, qb.x, qb.z};
+      float val = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ii = b0 + 4 * kg + r;
-        const float sc = h2f((uint16_t)(sz[r] & 0xFFFFu)), z = h2f((uint16_t)(sz[r] >> 16));
-        const float val = quad_sum(fmaf(sc, cacc[r], z * qc.x));
-        if (wr) wrow[ii * BR + g] = val * a.c;
-      }
+      for (int r = 0; r < 4; ++r) val = fmaf(scg[r], cacc[r], fmaf(zrg[r], qsum[r], val));
+      // rows past the run (record b0 + col >= nk, still below the wave's TT
+      // rows since the batch starts below nk) take values no one reads: key
+      // logits are read for ranks below nk only, and the value weights and
+      // zeros are written over every row the value batches read before they
+      // read it
+      const int g = 4 * cb + kg;
+      if (g < G) wrow[(b0 + col) * BR + g] = val * a.c;
     }
   };
   // ---- value residuals of records b0 .. b0+15 of the wave's run (weights in
