@@ -59,12 +59,13 @@ def ws_view(ws, off, count, dtype=torch.float32):
     return ws[off:off + nbytes].view(dtype)
 
 
-def run_workload(akv, w, step=0):
+def run_workload(akv, w, step=0, params=None):
     """Inputs generated in place on the GPU, then compress (all units, one call)
     and one decode step (all units), as the benchmark launches them."""
     dev = "cuda"
     dt = akv.BF16 if w.dtype == "bf16" else akv.F32
-    p = akv.plan(w.units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs, dt, w.theta, w.window)
+    p = akv.plan(w.units, w.kv_heads, w.q_per_kv, w.n_tokens, w.head_dim, w.n_obs, dt, w.theta, w.window,
+                 **(params or {}))
     K = torch.empty(w.units, w.kv_heads, w.n_tokens, w.head_dim, dtype=w.torch_dtype, device=dev)
     V = torch.empty_like(K)
     Q = torch.empty(w.units, w.kv_heads * w.q_per_kv, w.n_obs, w.head_dim, dtype=w.torch_dtype, device=dev)
@@ -349,3 +350,21 @@ def test_fullsize_sampled(akv, wname):
     assert d <= 1e-5
     del K, V, Q, cache, ws
     torch.cuda.empty_cache()
+
+
+def test_fullsize_llama3b_8k_rope_last_unit(akv):
+    """3B-shaped workload at full size with the keys taken as pre-RoPE
+    (28 units x 8 heads x 8192 tokens, rotary base 500000): whole-unit
+    comparison of the last unit (rotated observation attention, utilities,
+    residual ids, codes, decode over 8 chunks per head)."""
+    w = kvsynth.WORKLOADS["llama3b_8k"]
+    prm = dict(rope=1)
+    _flush(f"[fullsize] {w.name} pre-RoPE: units={w.units} N={w.n_tokens}")
+    p, K, V, Q, cache, ws, q, o = run_workload(akv, w, params=prm)
+    u = w.units - 1
+    score, util = unit_taps(akv, p, ws, u)
+    arr = unit_arrays(akv, p, cache, u)
+    rep = compare_unit(kvsynth.to_f64(K[u]), kvsynth.to_f64(V[u]), kvsynth.to_f64(Q[u]), w.q_per_kv, w.n_obs,
+                       w.theta, w.window, w.elem_bytes, arr, taps=dict(score=score, util=util),
+                       q=kvsynth.to_f64(q[u]), o_gpu=o[u].cpu().numpy().astype(np.float64), params=prm)
+    _flush(f"[fullsize] {w.name} pre-RoPE unit {u}: {rep}")
