@@ -1488,6 +1488,506 @@ __global__ __launch_bounds__(256) void k_dec_rope(DecArgs a) {
     }
 }
 
+// ------------------------------------------------ pre-RoPE keys, weight table
+// The same decode as k_dec_rope with the value side organised as in the
+// stream kernel: o = (w V_anchors) + sum over value-flagged tokens of
+// p_t r~^V_t, with w[g][a] = sum over tokens of anchor a of p_t gamma^V_t
+// accumulated in LDS in 64-bit fixed point (scale and rounding as in the
+// stream kernel), so no value anchor row is gathered per token; only the
+// value residuals of flagged tokens are rebuilt (bf16 hi + lo rows, compacted)
+// and multiplied on MFMA.  The running maximum is lazy (raised when a tile
+// passes it by 2^1), so w is rescaled only then.  Keys as in k_dec_rope, with
+// each wave's phases e^{i t theta_p} taken from its first token and a table
+// for the 16 tokens after it; a tile's anchor rows and key records are loaded
+// a tile ahead.  One workgroup of four waves per (unit, head, range), tiles
+// of 64 tokens, two barriers per tile:
+//  A. wave w rebuilds, rotates and scores the keys of tokens 16w .. 16w + 15
+//     and publishes its tile maxima when they pass the running maximum by 2^1;
+//  B. after the first barrier: rescale if a maximum was published; thread
+//     (token, q-head quarter) forms p, scatters p gamma^V into w, and writes p
+//     of a value-flagged token into its compacted column; the flagged tokens'
+//     value residuals are rebuilt into LDS rows;
+//  C. after the second barrier: p r~^V on MFMA over the compacted rows.
+// Every wave holds the pointer words of the whole tile (one token per lane,
+// loaded two tiles ahead), so residual ranks and record offsets come from its
+// own ballots.  Used while the [G][A] table fits kRopeWMaxBytes.
+constexpr int kRopeWMaxBytes = 64 * 1024;
+constexpr int kRopeRows = 32;   // compacted value-residual rows per round
+
+template <int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_rope_w(DecArgs a) {
+  using T = typename Elem<DT>::T;
+  using M = Mfma<ANCHORKV_BF16>;
+  constexpr int D = kHeadDim, TT = 64, P = D / 2, RR = kRopeRows;
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte load
+  constexpr int NK = 8 / EPC;                // 16-byte loads per 8 coordinates
+  extern __shared__ __align__(16) unsigned long long wi[];   // [G][A] fixed point
+  __shared__ __align__(16) float2 ftab[16][P + 2];   // e^{i j theta_p}, j < 16
+  __shared__ __align__(16) float2 e0w[4][P];         // e^{i t_w theta_p}, t_w = wave w's first key token
+  __shared__ __align__(16) float ps[kMaxG][TT + 4];  // logits (log2 units), one row per q-head
+  __shared__ __align__(16) float pc[kMaxG][TT + 4];  // p of the value-flagged tokens, compacted (zeros after)
+  __shared__ __align__(16) uint16_t vh[RR][D + 8];   // their value residuals, bf16 hi
+  __shared__ __align__(16) uint16_t vl[RR][D + 8];   // and lo
+  __shared__ int tmaxb[2][kMaxG];
+  __shared__ int hotb[2];
+  __shared__ float lsum[4][kMaxG];
+  __shared__ __align__(16) uint4 qfr[4][2][64];      // query B fragments per step (bf16 hi, lo)
+  __shared__ double thl[P];                          // theta_p
+  __shared__ float2 p64s[P];                         // e^{i 64 theta_p}
+
+  const int G = a.G, A = a.A;
+  int bid = blockIdx.x;
+  const int sp = bid % a.S2; bid /= a.S2;
+  const int h = bid % a.H;
+  const int u = bid / a.H;
+  const int64_t uh = (int64_t)u * a.H + h;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, kg = lane >> 4;
+  const int c0 = sp * a.cps, c1 = min(a.C, c0 + a.cps);
+  const int t_beg = c0 * kTile, t_end = min(a.N, c1 * kTile);
+  const int ntile = max(0, (t_end - t_beg + TT - 1) / TT);
+  const uint8_t* base = a.cache + (int64_t)u * a.stride;
+  const uint8_t* recK = base + a.off_rk;
+  const uint8_t* recV = base + a.off_rv;
+  const T* AK = reinterpret_cast<const T*>(base + a.off_ak) + (int64_t)h * A * D;
+  const T* AV = reinterpret_cast<const T*>(base + a.off_av) + (int64_t)h * A * D;
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(base + a.off_words) + (int64_t)h * a.N * 2;
+  const int* chk = reinterpret_cast<const int*>(base + a.off_ck) + h * a.C;
+  const int* chv = reinterpret_cast<const int*>(base + a.off_cv) + h * a.C;
+  const T* qp = reinterpret_cast<const T*>(a.q) + uh * G * D;
+
+  // the unit's header must describe the plan's cache (see k_dec_stream)
+  {
+    const UnitHeader* hd = reinterpret_cast<const UnitHeader*>(base);
+    if (hd->magic != kMagic || hd->H != a.H || hd->N != a.N || hd->A != A || hd->R_K != a.R_K ||
+        hd->R_V != a.R_V || hd->unit_stride != a.stride || hd->off_words != a.off_words || hd->codec != a.codec ||
+        hd->rope != 1 || hd->rope_theta != a.rope_theta) {
+      const float nan = __builtin_nanf("");
+      if (a.S2 == 1 && !a.force_part) {
+        for (int i = tid; i < G * D; i += 256) a.o[uh * G * D + i] = nan;
+      } else {
+        const int64_t slot = uh * a.S2 + sp;
+        for (int i = tid; i < G * D; i += 256) a.part_acc[slot * G * D + i] = nan;
+        if (tid < G) a.part_ml[slot * G + tid] = make_float2(nan, nan);
+      }
+      return;
+    }
+  }
+
+  // query fragments (B operand: column = q-head, the lane's K-slice of each
+  // 32-coordinate step) as bf16 hi + lo, in LDS (read per tile, no
+  // registers held across the loop); wave w writes step w
+  {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = col < G ? Elem<DT>::f(qp[col * D + 32 * wave + 8 * kg + e]) : 0.0f;
+    bf16x8 hi, lo;
+    split8(x, hi, lo);
+    qfr[wave][0][lane] = __builtin_bit_cast(uint4, hi);
+    qfr[wave][1][lane] = __builtin_bit_cast(uint4, lo);
+  }
+  // lane = frequency p of the wave's phase: theta_p in double precision
+  {
+    const double theta_l = pow((double)a.rope_theta, -2.0 * lane / D);
+    for (int j = wave; j < 16; j += 4) {
+      double sn, cn;
+      sincos((double)j * theta_l, &sn, &cn);
+      ftab[j][lane] = make_float2((float)cn, (float)sn);
+    }
+    if (wave == 0) {
+      double sn, cn;
+      sincos(64.0 * theta_l, &sn, &cn);
+      thl[lane] = theta_l;
+      p64s[lane] = make_float2((float)cn, (float)sn);
+    }
+  }
+  for (int i = tid; i < G * A; i += 256) wi[i] = 0ull;
+  for (int i = tid; i < kMaxG * (TT + 4); i += 256) (&pc[0][0])[i] = 0.0f;
+  // value rows start as zeros: a row past a tile's flagged count keeps an
+  // earlier tile's finite values, multiplied by a zero p
+  for (int i = tid; i < RR * (D + 8); i += 256) { (&vh[0][0])[i] = 0; (&vl[0][0])[i] = 0; }
+  if (tid < 2 * kMaxG) (&tmaxb[0][0])[tid] = kKeyNegInf;
+  if (tid < 2) hotb[tid] = 0;
+  float2 e0r = make_float2(1.0f, 0.0f);   // e^{i (t0 + 16 wave) theta_lane} of the current tile
+
+  // pointer words, one token per lane, two tiles ahead (zero past the range)
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(words + (int64_t)t_beg * 2, (uint32_t)(t_end - t_beg) * 8u);
+  auto load_words = [&](int it) -> uint2 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(wrs, (int)((uint32_t)(it * TT + lane) * 8u), 0, 0);
+    return make_uint2(v[0], v[1]);
+  };
+  uint2 wd0 = load_words(0), wd1 = load_words(1), wd2;
+
+  // this lane's key token (16 wave + col): anchor row chunks, and its record
+  // (code words 8 (kg & 1) .. + 7 and the four (scale, zero) words) when flagged
+  uint32_t wk = 0;
+  uint4 kraw[4][NK];
+  uint4 kcw = make_uint4(0, 0, 0, 0), ksz = kcw;
+  // (rank: the token's place among the tile's key-flagged tokens)
+  auto load_key = [&](uint32_t w, int rb, int rank) {
+    const T* ar = AK + (int64_t)(w & 0x7FFF) * D;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < NK; ++i) kraw[st][i] = *reinterpret_cast<const uint4*>(ar + 32 * st + 8 * kg + EPC * i);
+    if (w & 0x8000u) {
+      const uint8_t* rp = recK + (int64_t)(rb + rank) * kRecBytes;
+      kcw = *reinterpret_cast<const uint4*>(rp + 16 * (kg & 1));
+      ksz = *reinterpret_cast<const uint4*>(rp + 32);
+    }
+  };
+  // chunk bookkeeping (uniform): flagged tokens of the current chunk before the tile
+  int run_k = 0, run_v = 0;
+  {
+    // lane = token: its rank among the flagged tokens, handed to key lane (col, kg)
+    const int rk = lanes_below(__ballot((wd0.x & 0x8000u) != 0));
+    wk = __shfl(wd0.x, 16 * wave + col, 64);
+    load_key(wk, __builtin_amdgcn_readfirstlane(chk[c0]), __shfl(rk, 16 * wave + col, 64));
+  }
+
+  float m_run[kMaxG];
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g) m_run[g] = -INFINITY;
+  // copies for this thread's q-heads: column col of the key MFMA, and q-heads
+  // (lane & 3) + 4 gi of the softmax step (refreshed when m_run changes)
+  float m_col = -INFINITY, m_q[2] = {-INFINITY, -INFINITY};
+  float lacc[2] = {0.0f, 0.0f};
+  f32x4 oacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  __syncthreads();   // ftab, wi, pc, tmaxb
+
+  for (int it = 0; it < ntile; ++it) {
+    const int t0 = t_beg + it * TT;
+    const int par = it & 1;
+    const int c = t0 / kTile;
+    if ((t0 & (kTile - 1)) == 0) { run_k = 0; run_v = 0; }
+    const int rbk = __builtin_amdgcn_readfirstlane(chk[c]) + run_k;
+    const int rbv = __builtin_amdgcn_readfirstlane(chv[c]) + run_v;
+    const unsigned long long kmask = __ballot((wd0.x & 0x8000u) != 0);
+    const unsigned long long vmask = __ballot((wd0.y & 0x8000u) != 0);
+    const int nfl = __popcll(vmask);
+    wd2 = load_words(it + 2);
+
+    // value residual records of this tile's first round of compacted rows:
+    // wave rank wr = (wave - tile) mod 4 rebuilds rows 16 wr + (lane >> 2),
+    // coordinates 32 (lane & 3) .. + 31 (ranks 0, 1: rows 0..31, the first
+    // round; 2, 3: the second), so that with few flagged tokens one wave
+    // does the work, a different one from tile to tile
+    const int qq = lane & 3;
+    const int wr = (wave - it) & 3;
+    const int vrow = 16 * wr + (lane >> 2);
+    uint4 vc01 = make_uint4(0, 0, 0, 0), vc23 = vc01;
+    uint32_t vsz = 0;
+    if (wr < 2 && vrow < nfl) {
+      const uint8_t* rp = recV + (int64_t)(rbv + vrow) * kRecBytes;
+      vc01 = *reinterpret_cast<const uint4*>(rp);
+      vc23 = *reinterpret_cast<const uint4*>(rp + 16);
+      vsz = *reinterpret_cast<const uint32_t*>(rp + 32 + 4 * qq);
+    }
+
+    // ---- A. the wave's phases for this tile, then its 16 keys
+    if ((t0 & (kTile - 1)) == 0) {
+      double sn, cn;
+      sincos((double)(t0 + 16 * wave) * thl[lane], &sn, &cn);
+      e0r = make_float2((float)cn, (float)sn);
+    } else {
+      const float2 p64 = p64s[lane];
+      e0r = make_float2(e0r.x * p64.x - e0r.y * p64.y, e0r.x * p64.y + e0r.y * p64.x);
+    }
+    e0w[wave][lane] = e0r;
+    __builtin_amdgcn_wave_barrier();
+    {
+      const float gk = h2f((uint16_t)(wk >> 16));
+      float x[4][8];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+          T v[EPC];
+          *reinterpret_cast<uint4*>(v) = kraw[st][i];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) x[st][EPC * i + e] = gk * Elem<DT>::f(v[e]);
+        }
+      if (wk & 0x8000u) {
+        const uint32_t cws[4] = {kcw.x, kcw.y, kcw.z, kcw.w};
+        const uint32_t szs[4] = {ksz.x, ksz.y, ksz.z, ksz.w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const float sc = h2f((uint16_t)(szs[st] & 0xFFFFu)), zr = h2f((uint16_t)(szs[st] >> 16));
+          const int sh = 2 * (2 * st + (kg >> 1));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t code = (cws[e >> 1] >> (16 * (e & 1) + sh)) & 3u;
+            x[st][e] += fmaf(sc, (float)code, zr);
+          }
+        }
+      }
+      // pair p = 32 st + 8 kg + e (st = 0, 1) with p + 64: turn by t theta_p,
+      // t = t_w + col
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pp = 32 * st + 8 * kg + e;
+          const float2 a0 = e0w[wave][pp], b0 = ftab[col][pp];
+          const float cs = a0.x * b0.x - a0.y * b0.y, sn = a0.x * b0.y + a0.y * b0.x;
+          const float x0 = x[st][e], x1 = x[st + 2][e];
+          x[st][e] = x0 * cs - x1 * sn;
+          x[st + 2][e] = x0 * sn + x1 * cs;
+        }
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bf16x8 kh, kl;
+        split8(x[st], kh, kl);
+        const bf16x8 qh = bits_to_frag(qfr[st][0][lane]);
+        acc = M::mma(kh, qh, acc);
+        acc = M::mma(kl, qh, acc);
+        if constexpr (DT == ANCHORKV_F32) acc = M::mma(kh, bits_to_frag(qfr[st][1][lane]), acc);
+      }
+      // logits of tokens 16 wave + 4 kg + rr for q-head col; the tile maximum
+      // of the column, published when it passes the running maximum by 2^1
+      float lm = -INFINITY;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int jr = 16 * wave + 4 * kg + rr;
+        const float s = t0 + jr < t_end ? acc[rr] * a.c : -INFINITY;
+        if (col < G) ps[col][jr] = s;
+        lm = fmaxf(lm, s);
+      }
+      lm = fmaxf(lm, __shfl_xor(lm, 16, 64));
+      lm = fmaxf(lm, __shfl_xor(lm, 32, 64));
+      const bool hot = col < G && lm > m_col + kLazy;
+      if (__any(hot)) {
+        if (hot && kg == 0) atomicMax(&tmaxb[par][col], fkey(lm));
+        if (lane == 0) hotb[par] = 1;
+      }
+    }
+    // the next tile's key gathers (its words arrived a tile ago)
+    {
+      const int t1 = t0 + TT;
+      const int rbk1 = (t1 & (kTile - 1)) == 0 ? __builtin_amdgcn_readfirstlane(chk[min(c + 1, a.C - 1)])
+                                                : rbk + __popcll(kmask);
+      const int rk = lanes_below(__ballot((wd1.x & 0x8000u) != 0));
+      wk = __shfl(wd1.x, 16 * wave + col, 64);
+      kcw = make_uint4(0, 0, 0, 0);
+      ksz = kcw;
+      load_key(wk, rbk1, __shfl(rk, 16 * wave + col, 64));
+    }
+    lds_barrier();
+
+    // ---- B. rescale (uniform decision), p, w scatter, compacted rows
+    if (__builtin_amdgcn_readfirstlane(hotb[par])) {
+      bool any = false;
+      float f[kMaxG];
+#pragma unroll
+      for (int g = 0; g < kMaxG; ++g) {
+        f[g] = 1.0f;
+        if (g < G) {
+          const float tm = fkey_inv(__builtin_amdgcn_readfirstlane(tmaxb[par][g]));
+          if (tm > m_run[g] + kLazy) {
+            f[g] = m_run[g] == -INFINITY ? 0.0f : exp2_fast(m_run[g] - tm);
+            m_run[g] = tm;
+            any = true;
+          }
+        }
+      }
+      if (any) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          float fg = 1.0f, mg = -INFINITY;
+#pragma unroll
+          for (int g = 0; g < kMaxG; ++g) {
+            fg = (g == qq + 4 * gi) ? f[g] : fg;
+            mg = (g == qq + 4 * gi) ? m_run[g] : mg;
+          }
+          lacc[gi] *= fg;
+          m_q[gi] = mg;
+        }
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g) m_col = (g == col) ? m_run[g] : m_col;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float fg = 1.0f;
+#pragma unroll
+          for (int g = 0; g < kMaxG; ++g) fg = (g == 4 * kg + rr) ? f[g] : fg;
+          oacc[0][rr] *= fg;
+          oacc[1][rr] *= fg;
+        }
+        for (int i = tid; i < G * A; i += 256) {
+          const int g = i / A;
+          float fg = 1.0f;
+#pragma unroll
+          for (int gg = 0; gg < kMaxG; ++gg) fg = (gg == g) ? f[gg] : fg;
+          if (fg != 1.0f) wi[i] = (unsigned long long)__double2ll_rn((double)(long long)wi[i] * (double)fg);
+        }
+        lds_barrier();   // every thread takes this branch: w rescaled before any scatter below
+      }
+    }
+    if (tid < kMaxG) tmaxb[par ^ 1][tid] = kKeyNegInf;   // read last in the previous tile
+    if (tid == 0) hotb[par ^ 1] = 0;
+    {
+      // thread (token r, quarter qq): q-heads qq, qq + 4
+      const int r = 16 * wave + (lane >> 2);
+      const uint32_t wv = __shfl(wd0.y, r, 64);
+      const bool valid = t0 + r < t_end;
+      const int aV = wv & 0x7FFF;
+      const float gV = h2f((uint16_t)(wv >> 16));
+      const bool fl = (wv & 0x8000u) != 0;
+      const int kr = __shfl(lanes_below(vmask), r, 64);   // rank among the value-flagged tokens
+      const bool fast = gV >= 0.0f && gV < 8.0f;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int g = qq + 4 * gi;
+        if (g < G && valid) {
+          const float p = exp2_fast(ps[g][r] - m_q[gi]);
+          lacc[gi] += p;
+          const unsigned long long fx =
+              fast ? (unsigned long long)__double_as_longlong(fma((double)p, (double)gV * kFxScaleD, kRoundMagic)) &
+                         kMagicMask
+                   : fx_general(p * gV * kFxScale);
+          atomicAdd(wi + g * A + aV, fx);
+          if (fl) pc[g][kr] = p;
+        }
+      }
+      // zeros after the compacted columns, up to the rounds' width (thread:
+      // q-head tid / 32, column tid % 32 of each round)
+      {
+        const int g = tid >> 5, k = tid & 31;
+        if (g < G) {
+          if (k >= nfl) pc[g][k] = 0.0f;
+          if (nfl > RR && k + RR >= nfl) pc[g][k + RR] = 0.0f;
+        }
+      }
+    }
+    // value residual rows of the first round
+    auto rebuild = [&](int slot, const uint4& c01, const uint4& c23, uint32_t sz) {
+      float v[32];
+      const uint32_t cw[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
+      const float sc = h2f((uint16_t)(sz & 0xFFFFu)), zr = h2f((uint16_t)(sz >> 16));
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int jw = e & 15, sh = 2 * (2 * qq + (e >> 4));
+        const uint32_t code = (cw[jw >> 1] >> (16 * (jw & 1) + sh)) & 3u;
+        v[e] = fmaf(sc, (float)code, zr);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bf16x8 hi, lo;
+        split8(v + 8 * k, hi, lo);
+        *reinterpret_cast<bf16x8*>(&vh[slot][32 * qq + 8 * k]) = hi;
+        *reinterpret_cast<bf16x8*>(&vl[slot][32 * qq + 8 * k]) = lo;
+      }
+    };
+    if (wr < 2 && vrow < nfl) rebuild(vrow, vc01, vc23, vsz);
+    lds_barrier();
+
+    // ---- C. p r~ on MFMA: rows q-heads (p as hi + lo), K = 32 compacted
+    // tokens, columns 16 coordinates (r~ as hi + lo); wave w owns coordinate
+    // blocks 2w, 2w + 1
+    auto pv_round = [&](int k0) {
+      float p8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p8[e] = col < G ? pc[col][k0 + 8 * kg + e] : 0.0f;
+      bf16x8 ph, pl;
+      split8(p8, ph, pl);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int d = (2 * wave + b) * 16 + col;
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r0 = 8 * kg + 2 * e;
+          wh[e] = (uint32_t)vh[r0][d] | ((uint32_t)vh[r0 + 1][d] << 16);
+          wl[e] = (uint32_t)vl[r0][d] | ((uint32_t)vl[r0 + 1][d] << 16);
+        }
+        const bf16x8 vbh = bits_to_frag(make_uint4(wh[0], wh[1], wh[2], wh[3]));
+        const bf16x8 vbl = bits_to_frag(make_uint4(wl[0], wl[1], wl[2], wl[3]));
+        oacc[b] = M::mma(ph, vbh, oacc[b]);
+        oacc[b] = M::mma(pl, vbh, oacc[b]);
+        oacc[b] = M::mma(ph, vbl, oacc[b]);
+      }
+    };
+    if (nfl > 0) {
+      pv_round(0);
+      if (nfl > RR) {
+        // rare: a second round of rows (every thread takes it: nfl is uniform)
+        lds_barrier();   // round-0 rows read
+        if (wr >= 2 && vrow < nfl) {
+          const int row = vrow;   // 32 .. 63
+          const uint8_t* rp = recV + (int64_t)(rbv + row) * kRecBytes;
+          const uint4 c01 = *reinterpret_cast<const uint4*>(rp);
+          const uint4 c23 = *reinterpret_cast<const uint4*>(rp + 16);
+          const uint32_t sz = *reinterpret_cast<const uint32_t*>(rp + 32 + 4 * qq);
+          rebuild(row - RR, c01, c23, sz);
+        }
+        lds_barrier();
+        pv_round(RR);
+      }
+    }
+    run_k += __popcll(kmask);
+    run_v += nfl;
+    wd0 = wd1;
+    wd1 = wd2;
+  }
+
+  // ---- epilogue: softmax sums, residual part, w V (thread: coordinate d,
+  // q-heads gh, gh + 2, gh + 4, gh + 6)
+  const int qq = lane & 3;
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    float v = lacc[gi];
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    const int g = qq + 4 * gi;
+    if (lane < 4 && g < G) lsum[wave][g] = v;
+  }
+  __syncthreads();   // every scatter into w done; vh is free
+  float* po = reinterpret_cast<float*>(&vh[0][0]);   // [G][D] residual part
+  static_assert(sizeof(vh) >= kMaxG * D * sizeof(float), "residual part fits the rows");
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int g = 4 * kg + rr;
+      if (g < G) po[g * D + (2 * wave + b) * 16 + col] = oacc[b][rr];
+    }
+  __syncthreads();
+  const int d = tid & (D - 1), gh = tid >> 7;
+  float accv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int aa = 0; aa < A; ++aa) {
+    const float v = Elem<DT>::f(AV[(int64_t)aa * D + d]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int g = gh + 2 * k;
+      if (g < G) accv[k] = fmaf((float)((double)(long long)wi[g * A + aa] * kFxInv), v, accv[k]);
+    }
+  }
+  const bool part = a.S2 > 1 || a.force_part;
+  const int64_t slot = uh * a.S2 + sp;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int g = gh + 2 * k;
+    if (g < G) {
+      const float l = (lsum[0][g] + lsum[1][g]) + (lsum[2][g] + lsum[3][g]);
+      const float val = accv[k] + po[g * D + d];
+      if (part) {
+        a.part_acc[(slot * G + g) * D + d] = val;
+        if (d == 0) {
+          float mg = 0.0f;
+#pragma unroll
+          for (int gg = 0; gg < kMaxG; ++gg) mg = (gg == g) ? m_run[gg] : mg;
+          a.part_ml[slot * G + g] = make_float2(mg, l);
+        }
+      } else {
+        a.o[(uh * G + g) * D + d] = val / l;
+      }
+    }
+  }
+}
+
 // Per (unit, head, q-head) with several token ranges (and an optional tail
 // partial): o = sum_s f_s acc_s / sum_s f_s l_s with f_s = 2^(m_s - max m).
 // One block of 128 threads (one per coordinate) per q-head: the range
@@ -1821,8 +2321,18 @@ static int decode_impl(const anchorkv_plan_info& p, const void* cache_v, const v
   const unsigned grid = (unsigned)((int64_t)U * H * S2);
   int rc = 0;
   if (a.rope) {
-    k_dec_rope<DT><<<grid, 256, 0, st>>>(a);
-    AKV_CHECK_LAUNCH("k_dec_rope");
+    // the weight-table kernel while its [G][A] table fits, else the one that
+    // rebuilds every value row
+    const size_t wl = (size_t)G * A * sizeof(unsigned long long);
+    if (wl <= (size_t)kRopeWMaxBytes) {
+      static size_t done = 0;
+      if (int rc2 = set_dyn_lds(reinterpret_cast<const void*>(&k_dec_rope_w<DT>), wl, &done)) return rc2;
+      k_dec_rope_w<DT><<<grid, 256, wl, st>>>(a);
+      AKV_CHECK_LAUNCH("k_dec_rope_w");
+    } else {
+      k_dec_rope<DT><<<grid, 256, 0, st>>>(a);
+      AKV_CHECK_LAUNCH("k_dec_rope");
+    }
   } else switch (G) {
     case 1: rc = launch_stream<DT, 1>(a, grid, st); break;
     case 2: rc = launch_stream<DT, 2>(a, grid, st); break;

@@ -30,9 +30,11 @@
 // its first token tile) overlap the other's compute; larger parts use 16-wave
 // blocks, one per compute unit.
 //
-// Anchor sets larger than kAssignResMax are processed in parts inside the
-// kernel: every token tile walks the parts with each token's best carried in
-// registers from part to part, so the tokens are read once.
+// Anchor sets larger than kAssignResMax are processed inside the kernel in
+// the fewest equal parts of at most kAssignPartMax anchors: every token tile
+// walks the parts with each token's best carried in registers from part to
+// part, so the tokens are read once, and odd tiles walk them backwards so
+// that the part left in LDS by one tile starts the next.
 #pragma once
 
 #include "device_common.hpp"
@@ -278,9 +280,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
       for (int rb = 0; rb < 4; ++rb) {
         const unsigned b = __float_as_uint(run[rb]);
         const float m = __uint_as_float(b & keymask);
-        // the larger value, the earlier epoch on equal values (parts are
-        // visited in either order)
-        if (m > bv[rb] || (m == bv[rb] && ge < (bix[rb] >> 5))) {
+        // the larger value, the earlier epoch on equal values (epochs come
+        // in increasing order in one part; parts are visited in either order)
+        if (m > bv[rb] || (MULTI && m == bv[rb] && ge < (bix[rb] >> 5))) {
           bv[rb] = m;
           bix[rb] = (ge << 5) | (int)(b & 31u);
         }

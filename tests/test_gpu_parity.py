@@ -88,6 +88,12 @@ SMALL = {
     "bf16_rope_joint": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, n_dirs=32),
     # one 8B-shaped head at its full 32K tokens: 32 chunks of phase recurrence per decode range
     "bf16_rope_long": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=1),
+    # pre-RoPE decode with a large [q-head][anchor] weight table (8 x 865, 55 KB of LDS) and, past
+    # the table's limit, the decode that rebuilds every value row (8 x 1462 anchors)
+    "bf16_rope_wide": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=1, n_tokens=5000, n_obs=16, n_dirs=16,
+                                                 theta=0.25),
+    "bf16_rope_bigA": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=1, n_tokens=8000, n_obs=16, n_dirs=16,
+                                                 theta=0.2),
 }
 # non-default method parameters of some cases (anchorkv_params)
 PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dict(pool=3, rho=0.9, anchor_div=40),
@@ -102,7 +108,8 @@ PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dic
           "bf16_cover_g8": dict(anchor_mode=1),
           "bf16_rope": dict(rope=1), "bf16_rope_base1e4": dict(rope=1, rope_theta=10000.0),
           "f32_rope": dict(rope=1, rope_theta=10000.0), "bf16_rope_g8": dict(rope=1),
-          "bf16_rope_joint": dict(rope=1, pool_kv_jointly=1), "bf16_rope_long": dict(rope=1, rope_theta=10000.0)}
+          "bf16_rope_joint": dict(rope=1, pool_kv_jointly=1), "bf16_rope_long": dict(rope=1, rope_theta=10000.0),
+          "bf16_rope_wide": dict(rope=1, anchor_div=6), "bf16_rope_bigA": dict(rope=1, anchor_div=4)}
 
 
 def _flush(msg):
@@ -166,7 +173,7 @@ def test_compress_decode_parity(akv, name):
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "f32_tiny", "bf16_stress_short", "bf16_joint", "bf16_hlm_g8",
                                   "f32_hlm", "bf16_hlm_stress", "bf16_rope", "f32_rope", "bf16_rope_g8",
-                                  "bf16_rope_joint", "bf16_rope_long"])
+                                  "bf16_rope_joint", "bf16_rope_long", "bf16_rope_wide", "bf16_rope_bigA"])
 def test_decode_on_host_packed_oracle_cache(akv, name):
     """Decode alone: the oracle's compressed representation, packed on the
     host into the cache layout, decoded on the GPU."""
