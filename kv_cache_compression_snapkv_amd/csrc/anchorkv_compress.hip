@@ -1177,16 +1177,18 @@ __global__ __launch_bounds__(256) void k_rope_table(float2* cs, int N, double ba
 }
 
 // ------------------------------------------------------------ launch sequence
-// Observation-window kernels on pre-RoPE keys: the f32 kernels, with the keys
-// (and in UTIL each token's anchor row) rotated while the tiles are staged.
+// Observation-window kernels on pre-RoPE keys: the generic kernels, with the
+// keys (and in UTIL each token's anchor row) rotated while the tiles are
+// staged; always 512 threads (the staging takes two items per thread; waves
+// past the query blocks only stage).
 template <int DT, int MODE>
 static int launch_obs_rope(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t st) {
   const int QB = a.GQp / 16;
   if (QB > 8) return fail(ANCHORKV_E_SHAPE, "pre-RoPE keys: q_per_kv*n_obs must be <= 128");
   const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1));
   // bf16: rotated keys as bf16 hi + lo on the bf16 MFMA; f32: f32 MFMA
-  if constexpr (DT == ANCHORKV_BF16) k_obs<ANCHORKV_BF16, MODE, 1, ANCHORKV_BF16, true><<<grid, dim3(64 * QB), 0, st>>>(a);
-  else k_obs<ANCHORKV_F32, MODE, 1, ANCHORKV_F32, true><<<grid, dim3(64 * QB), 0, st>>>(a);
+  if constexpr (DT == ANCHORKV_BF16) k_obs<ANCHORKV_BF16, MODE, 1, ANCHORKV_BF16, true><<<grid, dim3(512), 0, st>>>(a);
+  else k_obs<ANCHORKV_F32, MODE, 1, ANCHORKV_F32, true><<<grid, dim3(512), 0, st>>>(a);
   AKV_CHECK_LAUNCH("k_obs (pre-RoPE keys)");
   return 0;
 }

@@ -184,82 +184,145 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
 
   const int vis_base = N - a.n_obs;  // query j sees keys <= vis_base + j
 
+  // ---- pre-RoPE staging, software-pipelined: item (row r, coordinates
+  // i0..i0+3 and 64+i0..64+i0+3), RIT per thread (the block has 512 threads);
+  // the key rows of tile t0 + 64 and their (cos, sin) (and in SCORE the value
+  // tile) are loaded into registers while tile t0 is computed, and rotated
+  // into the tile buffers after the tile's barrier
+  using R4 = typename std::conditional<SRC == ANCHORKV_BF16, uint2, float4>::type;
+  constexpr int RIT = ROPE ? 2 : 1;                                      // 64 x 16 items / 512 threads
+  constexpr int VIT = (ROPE && MODE == OBS_SCORE) ? (SPLIT ? 2 : 4) : 1;  // transposed-value items
+  struct RopeRaw { R4 k0, k1; float4 ca, cb; };
+  RopeRaw rr[RIT];
+  uint4 vtr[VIT];   // SCORE: 16-byte value chunks (bf16) or 4 floats (f32) of the transposed tile
+  auto r4f = [](const R4& x, float (&o)[4]) {
+    if constexpr (SRC == ANCHORKV_BF16) {
+      o[0] = __uint_as_float(x.x << 16); o[1] = __uint_as_float(x.x & 0xFFFF0000u);
+      o[2] = __uint_as_float(x.y << 16); o[3] = __uint_as_float(x.y & 0xFFFF0000u);
+    } else {
+      o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    }
+  };
+  auto load_raw = [&](int tb) {
+#pragma unroll
+    for (int k = 0; k < RIT; ++k) {
+      const int it = threadIdx.x + k * 512;
+      const int r = it >> 4, i0 = (it & 15) * 4;
+      const int t = min(tb + r, k1 - 1);   // rows past the range repeat the last one (masked later)
+      rr[k].k0 = *reinterpret_cast<const R4*>(Kp + (int64_t)t * D + i0);
+      rr[k].k1 = *reinterpret_cast<const R4*>(Kp + (int64_t)t * D + 64 + i0);
+      if constexpr (MODE != OBS_UTIL) {
+        const float4* cs = reinterpret_cast<const float4*>(a.rope_cs + (int64_t)t * (D / 2) + i0);
+        rr[k].ca = cs[0];
+        rr[k].cb = cs[1];
+      }
+    }
+    if constexpr (MODE == OBS_SCORE) {
+#pragma unroll
+      for (int k = 0; k < VIT; ++k) {
+        // bf16: chunk (row ch % 64, 16-byte column ch / 64); f32: 4 floats
+        const int ch = threadIdx.x + k * 512;
+        const int r = ch % 64, c4 = ch / 64;
+        const int t = min(tb + r, k1 - 1);
+        vtr[k] = *reinterpret_cast<const uint4*>(Vp + (int64_t)t * D + c4 * (16 / (int)sizeof(S)));
+      }
+    }
+  };
+  // rotate the loaded rows of tile tb into the tile buffers (rows past the range: zeros)
+  auto store_rot = [&](int tb) {
+    // four rotated coordinates into a tile row: f32, or bf16 hi (and lo)
+    auto put4 = [&](T* hi, T* lo, int off, const float (&x)[4]) {
+      if constexpr (SPLIT) {
+        uint16_t h4[4], l4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { h4[i] = f2bf(x[i]); l4[i] = f2bf(x[i] - bf2f(h4[i])); }
+        *reinterpret_cast<uint2*>(&hi[off]) = make_uint2(h4[0] | (uint32_t)h4[1] << 16, h4[2] | (uint32_t)h4[3] << 16);
+        *reinterpret_cast<uint2*>(&lo[off]) = make_uint2(l4[0] | (uint32_t)l4[1] << 16, l4[2] | (uint32_t)l4[3] << 16);
+      } else {
+        (void)lo;
+        *reinterpret_cast<float4*>(&hi[off]) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < RIT; ++k) {
+      const int it = threadIdx.x + k * 512;
+      const int r = it >> 4, i0 = (it & 15) * 4;
+      const bool ok = tb + r < k1;
+      if constexpr (MODE == OBS_UTIL) {
+        // UTIL holds more registers across the tile: its (cos, sin) are read here
+        const float4* csp = reinterpret_cast<const float4*>(a.rope_cs + (int64_t)min(tb + r, k1 - 1) * (D / 2) + i0);
+        rr[k].ca = csp[0];
+        rr[k].cb = csp[1];
+      }
+      float2 cs[4] = {make_float2(rr[k].ca.x, rr[k].ca.y), make_float2(rr[k].ca.z, rr[k].ca.w),
+                      make_float2(rr[k].cb.x, rr[k].cb.y), make_float2(rr[k].cb.z, rr[k].cb.w)};
+      float x0[4], x1[4];
+      r4f(rr[k].k0, x0);
+      r4f(rr[k].k1, x1);
+      rope4(x0, x1, cs);
+      if (!ok)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x0[i] = 0.0f; x1[i] = 0.0f; }
+      put4(Ks, Ks2, r * LDK + i0, x0);
+      put4(Ks, Ks2, r * LDK + 64 + i0, x1);
+      if constexpr (MODE == OBS_UTIL) {
+        // the token's anchor row (L2-resident: the head's anchors) and its
+        // value row are read here, so that fewer registers are held across
+        // the tile's compute
+        const int tv = min(tb + r, k1 - 1);
+        const int an = a.aidx[((int64_t)u * 2 * H + h) * N + tv];  // side 0 = K
+        const S* ap = reinterpret_cast<const S*>(a.cache + (int64_t)u * a.stride + a.off_anchor_k) +
+                      ((int64_t)h * a.A + an) * D;
+        float g0[4], g1[4];
+        r4f(*reinterpret_cast<const R4*>(ap + i0), g0);
+        r4f(*reinterpret_cast<const R4*>(ap + 64 + i0), g1);
+        rope4(g0, g1, cs);
+        if (!ok)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { g0[i] = 0.0f; g1[i] = 0.0f; }
+        put4(Gs, Gs2, r * LDK + i0, g0);
+        put4(Gs, Gs2, r * LDK + 64 + i0, g1);
+        const R4 rv0 = *reinterpret_cast<const R4*>(Vp + (int64_t)tv * D + i0);
+        const R4 rv1 = *reinterpret_cast<const R4*>(Vp + (int64_t)tv * D + 64 + i0);
+        if constexpr (SPLIT) {
+          // values stay exact bf16: 8-byte copies
+          *reinterpret_cast<uint2*>(&Vs[r * LDK + i0]) = ok ? rv0 : make_uint2(0, 0);
+          *reinterpret_cast<uint2*>(&Vs[r * LDK + 64 + i0]) = ok ? rv1 : make_uint2(0, 0);
+        } else {
+          float v0[4], v1[4];
+          r4f(rv0, v0);
+          r4f(rv1, v1);
+          if (!ok)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { v0[i] = 0.0f; v1[i] = 0.0f; }
+          *reinterpret_cast<float4*>(&Vs[r * LDK + i0]) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+          *reinterpret_cast<float4*>(&Vs[r * LDK + 64 + i0]) = make_float4(v1[0], v1[1], v1[2], v1[3]);
+        }
+      }
+    }
+    if constexpr (MODE == OBS_SCORE) {
+      // transposed value tile Vt[d][key]
+#pragma unroll
+      for (int k = 0; k < VIT; ++k) {
+        const int ch = threadIdx.x + k * 512;
+        const int r = ch % 64, c4 = ch / 64;
+        const bool ok = tb + r < k1;
+        constexpr int EPC4 = 16 / (int)sizeof(S);
+        S tmp[EPC4];
+        const uint4 raw = ok ? vtr[k] : make_uint4(0, 0, 0, 0);
+        __builtin_memcpy(tmp, &raw, 16);
+#pragma unroll
+        for (int i = 0; i < EPC4; ++i) Vs[(c4 * EPC4 + i) * LDVT + r] = tmp[i];
+      }
+    }
+  };
+  if constexpr (ROPE) load_raw(k0);
+
   for (int t0 = k0; t0 < k1; t0 += 64) {
     // ---- stage the key tile (and value / gathered-anchor tiles)
     constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;          // chunks per row
-    if constexpr (ROPE) {
-      // item (row r, coordinates i0..i0+3 and 64+i0..64+i0+3): rotated keys,
-      // values as floats, and (UTIL) the token's anchor row rotated at the
-      // token's position
-      for (int it = threadIdx.x; it < 64 * 16; it += blockDim.x) {
-        const int r = it >> 4, i0 = (it & 15) * 4;
-        const int t = t0 + r;
-        float x0[4] = {0, 0, 0, 0}, x1[4] = {0, 0, 0, 0};
-        if (t < k1) {
-          ld4f<SRC>(Kp + (int64_t)t * D + i0, x0);
-          ld4f<SRC>(Kp + (int64_t)t * D + 64 + i0, x1);
-          rope4(x0, x1, a.rope_cs + (int64_t)t * (D / 2) + i0);
-        }
-        // four rotated coordinates into a tile row: f32, or bf16 hi (and lo)
-        auto put4 = [&](T* hi, T* lo, int off, const float (&x)[4]) {
-          if constexpr (SPLIT) {
-            uint16_t h4[4], l4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { h4[i] = f2bf(x[i]); l4[i] = f2bf(x[i] - bf2f(h4[i])); }
-            *reinterpret_cast<uint2*>(&hi[off]) = make_uint2(h4[0] | (uint32_t)h4[1] << 16, h4[2] | (uint32_t)h4[3] << 16);
-            *reinterpret_cast<uint2*>(&lo[off]) = make_uint2(l4[0] | (uint32_t)l4[1] << 16, l4[2] | (uint32_t)l4[3] << 16);
-          } else {
-            (void)lo;
-            *reinterpret_cast<float4*>(&hi[off]) = make_float4(x[0], x[1], x[2], x[3]);
-          }
-        };
-        put4(Ks, Ks2, r * LDK + i0, x0);
-        put4(Ks, Ks2, r * LDK + 64 + i0, x1);
-        if constexpr (MODE == OBS_UTIL) {
-          float g0[4] = {0, 0, 0, 0}, g1[4] = {0, 0, 0, 0};
-          if (t < k1) {
-            const int an = a.aidx[((int64_t)u * 2 * H + h) * N + t];  // side 0 = K
-            const S* ap = reinterpret_cast<const S*>(a.cache + (int64_t)u * a.stride + a.off_anchor_k) +
-                          ((int64_t)h * a.A + an) * D;
-            ld4f<SRC>(ap + i0, g0);
-            ld4f<SRC>(ap + 64 + i0, g1);
-            rope4(g0, g1, a.rope_cs + (int64_t)t * (D / 2) + i0);
-          }
-          put4(Gs, Gs2, r * LDK + i0, g0);
-          put4(Gs, Gs2, r * LDK + 64 + i0, g1);
-          if constexpr (SPLIT) {
-            // values stay exact bf16: 8-byte copies
-            uint2 v0 = make_uint2(0, 0), v1 = make_uint2(0, 0);
-            if (t < k1) {
-              v0 = *reinterpret_cast<const uint2*>(Vp + (int64_t)t * D + i0);
-              v1 = *reinterpret_cast<const uint2*>(Vp + (int64_t)t * D + 64 + i0);
-            }
-            *reinterpret_cast<uint2*>(&Vs[r * LDK + i0]) = v0;
-            *reinterpret_cast<uint2*>(&Vs[r * LDK + 64 + i0]) = v1;
-          } else {
-            float v0[4] = {0, 0, 0, 0}, v1[4] = {0, 0, 0, 0};
-            if (t < k1) {
-              ld4f<SRC>(Vp + (int64_t)t * D + i0, v0);
-              ld4f<SRC>(Vp + (int64_t)t * D + 64 + i0, v1);
-            }
-            *reinterpret_cast<float4*>(&Vs[r * LDK + i0]) = make_float4(v0[0], v0[1], v0[2], v0[3]);
-            *reinterpret_cast<float4*>(&Vs[r * LDK + 64 + i0]) = make_float4(v1[0], v1[1], v1[2], v1[3]);
-          }
-        }
-      }
-      if constexpr (MODE == OBS_SCORE && !SPLIT) {
-        // transposed value tile Vt[d][key] as floats; consecutive threads take consecutive keys
-        for (int it = threadIdx.x; it < 64 * (D / 4); it += blockDim.x) {
-          const int r = it % 64, d0 = (it / 64) * 4;
-          const int t = t0 + r;
-          float v[4] = {0, 0, 0, 0};
-          if (t < k1) ld4f<SRC>(Vp + (int64_t)t * D + d0, v);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Vs[(d0 + i) * LDVT + r] = v[i];
-        }
-      }
-    }
+    if constexpr (ROPE) store_rot(t0);
     for (int ch = threadIdx.x; ch < (ROPE ? 0 : 64 * CPR); ch += blockDim.x) {
       const int r = ch / CPR, cc = ch % CPR;
       const int t = t0 + r;
@@ -279,7 +342,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
         *reinterpret_cast<uint4*>(&Gs[r * LDK + cc * EPC]) = g;
       }
     }
-    if constexpr (MODE == OBS_SCORE && (!ROPE || SPLIT)) {
+    if constexpr (MODE == OBS_SCORE && !ROPE) {
       // transposed value tile Vt[d][key]; consecutive threads take consecutive keys
       for (int ch = threadIdx.x; ch < 64 * CPR; ch += blockDim.x) {
         const int r = ch % 64, cc = ch / 64;
@@ -298,6 +361,10 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       }
     }
     __syncthreads();
+    // pre-RoPE: the next tile's rows are loaded while this one is computed
+    if constexpr (ROPE) {
+      if (t0 + 64 < k1) load_raw(t0 + 64);
+    }
     if constexpr (MODE == OBS_UTIL) {
       // ||v||^2 per key from the staged tile: 4 consecutive threads per key
       for (int kk = threadIdx.x >> 2; kk < 64; kk += blockDim.x >> 2) {

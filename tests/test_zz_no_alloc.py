@@ -27,9 +27,9 @@ def akv():
     return m
 
 
-def _run_both(akv, w):
+def _run_both(akv, w, params=None):
     K, V, Q = make_inputs(w)
-    p = plan_for(akv, w)
+    p = plan_for(akv, w, params or {})
     cache, ws, dws = akv.alloc(p, "cuda")
     akv.compress(p, K, V, Q, cache, ws)
     q = kvsynth.decode_queries(w, 1, device="cuda").contiguous()
@@ -52,6 +52,11 @@ def test_noalloc_decode_matches_workspace_decode_twice(akv):
         assert torch.equal(o_ref, o_na)
     # f32 cache, one range per head
     p, o_ref, o_na = _run_both(akv, SMALL["f32_tiny"])
+    assert torch.equal(o_ref, o_na)
+    # keys stored before the rotary embedding (the weight-table decode), heads split into ranges
+    p, o_ref, o_na = _run_both(akv, SMALL["bf16_rope"], dict(rope=1))
+    _flush(f"[noalloc] pre-RoPE ranges/head={p.decode_splits}")
+    assert p.decode_splits > 1 and torch.isfinite(o_ref).all()
     assert torch.equal(o_ref, o_na)
 
 
