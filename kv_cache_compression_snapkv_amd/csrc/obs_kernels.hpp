@@ -186,14 +186,16 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
 
   // ---- pre-RoPE staging, software-pipelined: item (row r, coordinates
   // i0..i0+3 and 64+i0..64+i0+3), RIT per thread (the block has 512 threads);
-  // the key rows of tile t0 + 64 and their (cos, sin) (and in SCORE the value
-  // tile) are loaded into registers while tile t0 is computed, and rotated
-  // into the tile buffers after the tile's barrier
+  // the rows of tile t0 + 64 (keys and their (cos, sin); in UTIL also values
+  // and the tokens' anchor rows, whose indices come a tile earlier; in SCORE
+  // the value tile) are loaded into registers while tile t0 is computed, and
+  // rotated into the tile buffers after the tile's barrier
   using R4 = typename std::conditional<SRC == ANCHORKV_BF16, uint2, float4>::type;
   constexpr int RIT = ROPE ? 2 : 1;                                      // 64 x 16 items / 512 threads
   constexpr int VIT = (ROPE && MODE == OBS_SCORE) ? (SPLIT ? 2 : 4) : 1;  // transposed-value items
-  struct RopeRaw { R4 k0, k1; float4 ca, cb; };
+  struct RopeRaw { R4 k0, k1, g0, g1, v0, v1; float4 ca, cb; };
   RopeRaw rr[RIT];
+  int ran[RIT];   // UTIL: anchor index of the item's token in the next tile load_raw reads
   uint4 vtr[VIT];   // SCORE: 16-byte value chunks (bf16) or 4 floats (f32) of the transposed tile
   auto r4f = [](const R4& x, float (&o)[4]) {
     if constexpr (SRC == ANCHORKV_BF16) {
@@ -211,10 +213,17 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       const int t = min(tb + r, k1 - 1);   // rows past the range repeat the last one (masked later)
       rr[k].k0 = *reinterpret_cast<const R4*>(Kp + (int64_t)t * D + i0);
       rr[k].k1 = *reinterpret_cast<const R4*>(Kp + (int64_t)t * D + 64 + i0);
-      if constexpr (MODE != OBS_UTIL) {
-        const float4* cs = reinterpret_cast<const float4*>(a.rope_cs + (int64_t)t * (D / 2) + i0);
-        rr[k].ca = cs[0];
-        rr[k].cb = cs[1];
+      const float4* cs = reinterpret_cast<const float4*>(a.rope_cs + (int64_t)t * (D / 2) + i0);
+      rr[k].ca = cs[0];
+      rr[k].cb = cs[1];
+      if constexpr (MODE == OBS_UTIL) {
+        const S* ap = reinterpret_cast<const S*>(a.cache + (int64_t)u * a.stride + a.off_anchor_k) +
+                      ((int64_t)h * a.A + ran[k]) * D;
+        rr[k].g0 = *reinterpret_cast<const R4*>(ap + i0);
+        rr[k].g1 = *reinterpret_cast<const R4*>(ap + 64 + i0);
+        rr[k].v0 = *reinterpret_cast<const R4*>(Vp + (int64_t)t * D + i0);
+        rr[k].v1 = *reinterpret_cast<const R4*>(Vp + (int64_t)t * D + 64 + i0);
+        ran[k] = a.aidx[((int64_t)u * 2 * H + h) * N + min(tb + 64 + r, k1 - 1)];   // side 0 = K
       }
     }
     if constexpr (MODE == OBS_SCORE) {
@@ -248,12 +257,6 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       const int it = threadIdx.x + k * 512;
       const int r = it >> 4, i0 = (it & 15) * 4;
       const bool ok = tb + r < k1;
-      if constexpr (MODE == OBS_UTIL) {
-        // UTIL holds more registers across the tile: its (cos, sin) are read here
-        const float4* csp = reinterpret_cast<const float4*>(a.rope_cs + (int64_t)min(tb + r, k1 - 1) * (D / 2) + i0);
-        rr[k].ca = csp[0];
-        rr[k].cb = csp[1];
-      }
       float2 cs[4] = {make_float2(rr[k].ca.x, rr[k].ca.y), make_float2(rr[k].ca.z, rr[k].ca.w),
                       make_float2(rr[k].cb.x, rr[k].cb.y), make_float2(rr[k].cb.z, rr[k].cb.w)};
       float x0[4], x1[4];
@@ -266,24 +269,16 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       put4(Ks, Ks2, r * LDK + i0, x0);
       put4(Ks, Ks2, r * LDK + 64 + i0, x1);
       if constexpr (MODE == OBS_UTIL) {
-        // the token's anchor row (L2-resident: the head's anchors) and its
-        // value row are read here, so that fewer registers are held across
-        // the tile's compute
-        const int tv = min(tb + r, k1 - 1);
-        const int an = a.aidx[((int64_t)u * 2 * H + h) * N + tv];  // side 0 = K
-        const S* ap = reinterpret_cast<const S*>(a.cache + (int64_t)u * a.stride + a.off_anchor_k) +
-                      ((int64_t)h * a.A + an) * D;
         float g0[4], g1[4];
-        r4f(*reinterpret_cast<const R4*>(ap + i0), g0);
-        r4f(*reinterpret_cast<const R4*>(ap + 64 + i0), g1);
+        r4f(rr[k].g0, g0);
+        r4f(rr[k].g1, g1);
         rope4(g0, g1, cs);
         if (!ok)
 #pragma unroll
           for (int i = 0; i < 4; ++i) { g0[i] = 0.0f; g1[i] = 0.0f; }
         put4(Gs, Gs2, r * LDK + i0, g0);
         put4(Gs, Gs2, r * LDK + 64 + i0, g1);
-        const R4 rv0 = *reinterpret_cast<const R4*>(Vp + (int64_t)tv * D + i0);
-        const R4 rv1 = *reinterpret_cast<const R4*>(Vp + (int64_t)tv * D + 64 + i0);
+        const R4 rv0 = rr[k].v0, rv1 = rr[k].v1;
         if constexpr (SPLIT) {
           // values stay exact bf16: 8-byte copies
           *reinterpret_cast<uint2*>(&Vs[r * LDK + i0]) = ok ? rv0 : make_uint2(0, 0);
@@ -316,7 +311,16 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       }
     }
   };
-  if constexpr (ROPE) load_raw(k0);
+  if constexpr (ROPE) {
+    if constexpr (MODE == OBS_UTIL) {
+#pragma unroll
+      for (int k = 0; k < RIT; ++k) {
+        const int r = (threadIdx.x + k * 512) >> 4;
+        ran[k] = a.aidx[((int64_t)u * 2 * H + h) * N + min(k0 + r, k1 - 1)];
+      }
+    }
+    load_raw(k0);
+  }
 
   for (int t0 = k0; t0 < k1; t0 += 64) {
     // ---- stage the key tile (and value / gathered-anchor tiles)
@@ -386,24 +390,6 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       for (int r = 0; r < 4; ++r) colsum[kb][r] = 0.0f;
 
     for (int c2 = 0; c2 < 2; ++c2) {
-      frag af[2][NSTEP];
-      frag gf[(MODE == OBS_UTIL) ? 2 : 1][NSTEP];
-      frag vf[(MODE == OBS_UTIL) ? 2 : 1][NSTEP];
-      frag af2[SPLIT ? 2 : 1][SPLIT ? NSTEP : 1];
-      frag gf2[(SPLIT && MODE == OBS_UTIL) ? 2 : 1][(SPLIT && MODE == OBS_UTIL) ? NSTEP : 1];
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int row = (c2 * 2 + k2) * 16 + col;
-        for (int st = 0; st < NSTEP; ++st) {
-          const int kk = st * M::KSTEP + kg * M::KW;
-          af[k2][st] = M::load(&Ks[row * LDK + kk]);
-          if constexpr (SPLIT) af2[k2][st] = M::load(&Ks2[row * LDK + kk]);
-          if constexpr (MODE == OBS_UTIL) {
-            gf[k2][st] = M::load(&Gs[row * LDK + kk]);
-            if constexpr (SPLIT) gf2[k2][st] = M::load(&Gs2[row * LDK + kk]);
-            vf[k2][st] = M::load(&Vs[row * LDK + kk]);
-          }
-        }
-      }
       // value B-fragments of this 32-key chunk for the PV product
       frag vb[(MODE == OBS_SCORE) ? 8 : 1][(MODE == OBS_SCORE && DT == ANCHORKV_F32) ? 8 : 1];
       if constexpr (MODE == OBS_SCORE) {
@@ -424,17 +410,33 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
         float pv[2][4];
         for (int k2 = 0; k2 < 2; ++k2) {
           const int kb = c2 * 2 + k2;
+          // A fragments of key block kb (one block at a time: fewer registers)
+          frag af[NSTEP], gf[(MODE == OBS_UTIL) ? NSTEP : 1], vf[(MODE == OBS_UTIL) ? NSTEP : 1];
+          frag af2[SPLIT ? NSTEP : 1], gf2[(SPLIT && MODE == OBS_UTIL) ? NSTEP : 1];
+          {
+            const int row = kb * 16 + col;
+            for (int st = 0; st < NSTEP; ++st) {
+              const int kk = st * M::KSTEP + kg * M::KW;
+              af[st] = M::load(&Ks[row * LDK + kk]);
+              if constexpr (SPLIT) af2[st] = M::load(&Ks2[row * LDK + kk]);
+              if constexpr (MODE == OBS_UTIL) {
+                gf[st] = M::load(&Gs[row * LDK + kk]);
+                if constexpr (SPLIT) gf2[st] = M::load(&Gs2[row * LDK + kk]);
+                vf[st] = M::load(&Vs[row * LDK + kk]);
+              }
+            }
+          }
           f32x4 acc = {0, 0, 0, 0}, accg = {0, 0, 0, 0}, accv = {0, 0, 0, 0};
-          for (int st = 0; st < NSTEP; ++st) acc = M::mma(af[k2][st], qf[qi][st], acc);
+          for (int st = 0; st < NSTEP; ++st) acc = M::mma(af[st], qf[qi][st], acc);
           if constexpr (SPLIT)
-            for (int st = 0; st < NSTEP; ++st) acc = M::mma(af2[k2][st], qf[qi][st], acc);
+            for (int st = 0; st < NSTEP; ++st) acc = M::mma(af2[st], qf[qi][st], acc);
           if constexpr (MODE == OBS_UTIL) {
-            for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf[k2][st], qf[qi][st], accg);
+            for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf[st], qf[qi][st], accg);
             if constexpr (SPLIT)
-              for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf2[k2][st], qf[qi][st], accg);
-            for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[k2][st], ofh[qi][st], accv);
+              for (int st = 0; st < NSTEP; ++st) accg = M::mma(gf2[st], qf[qi][st], accg);
+            for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[st], ofh[qi][st], accv);
             if constexpr (DT == ANCHORKV_BF16)
-              for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[k2][st], ofl[qi][st], accv);
+              for (int st = 0; st < NSTEP; ++st) accv = M::mma(vf[st], ofl[qi][st], accv);
           }
           for (int r = 0; r < 4; ++r) {
             const int kl = kb * 16 + kg * 4 + r;  // key within the tile
