@@ -279,20 +279,26 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
         put4(Gs, Gs2, r * LDK + i0, g0);
         put4(Gs, Gs2, r * LDK + 64 + i0, g1);
         const R4 rv0 = rr[k].v0, rv1 = rr[k].v1;
+        float v0[4], v1[4];
+        r4f(rv0, v0);
+        r4f(rv1, v1);
+        if (!ok)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { v0[i] = 0.0f; v1[i] = 0.0f; }
         if constexpr (SPLIT) {
           // values stay exact bf16: 8-byte copies
           *reinterpret_cast<uint2*>(&Vs[r * LDK + i0]) = ok ? rv0 : make_uint2(0, 0);
           *reinterpret_cast<uint2*>(&Vs[r * LDK + 64 + i0]) = ok ? rv1 : make_uint2(0, 0);
         } else {
-          float v0[4], v1[4];
-          r4f(rv0, v0);
-          r4f(rv1, v1);
-          if (!ok)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { v0[i] = 0.0f; v1[i] = 0.0f; }
           *reinterpret_cast<float4*>(&Vs[r * LDK + i0]) = make_float4(v0[0], v0[1], v0[2], v0[3]);
           *reinterpret_cast<float4*>(&Vs[r * LDK + 64 + i0]) = make_float4(v1[0], v1[1], v1[2], v1[3]);
         }
+        // ||v||^2 of the row: the 16 items of a row are 16 consecutive lanes
+        float vv = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv = fmaf(v0[i], v0[i], fmaf(v1[i], v1[i], vv));
+        vv = row_sum(vv);
+        if ((it & 15) == 0) vv_s[r] = vv;
       }
     }
     if constexpr (MODE == OBS_SCORE) {
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
     if constexpr (ROPE) {
       if (t0 + 64 < k1) load_raw(t0 + 64);
     }
-    if constexpr (MODE == OBS_UTIL) {
+    if constexpr (MODE == OBS_UTIL && !ROPE) {
       // ||v||^2 per key from the staged tile: 4 consecutive threads per key
       for (int kk = threadIdx.x >> 2; kk < 64; kk += blockDim.x >> 2) {
         const int part = threadIdx.x & 3;
@@ -506,11 +512,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       // column sums over the 16 query lanes, then over waves in a fixed order
       for (int kb = 0; kb < 4; ++kb)
         for (int r = 0; r < 4; ++r) {
-          float v = colsum[kb][r];
-          v += __shfl_xor(v, 1, 64);
-          v += __shfl_xor(v, 2, 64);
-          v += __shfl_xor(v, 4, 64);
-          v += __shfl_xor(v, 8, 64);
+          const float v = row_sum(colsum[kb][r]);   // over the 16 query lanes (DPP)
           if (col == 0) colpart[wave][kb * 16 + kg * 4 + r] = v;
         }
       __syncthreads();
