@@ -116,7 +116,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
   __shared__ __attribute__((aligned(16))) T Gs[(MODE == OBS_UTIL) ? 64 * LDK : 16];
   __shared__ __attribute__((aligned(16))) T Ks2[SPLIT ? 64 * LDK : 8];                        // lo parts
   __shared__ __attribute__((aligned(16))) T Gs2[(SPLIT && MODE == OBS_UTIL) ? 64 * LDK : 8];
-  __shared__ float colpart[8][64];
+  __shared__ float colpart[2][8][64];   // per tile parity: the waves' column sums
   __shared__ float vv_s[64];
   __shared__ float gam_s[64];
 
@@ -317,6 +317,23 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       }
     }
   };
+  // score / key utility of the keys of tile tb from the waves' column sums
+  auto finish_tile = [&](int tb) {
+    if (threadIdx.x < 64) {
+      const int t = tb + threadIdx.x;
+      float v = 0.0f;
+      for (int w = 0; w < nw; ++w) v += colpart[((tb - k0) >> 6) & 1][w][threadIdx.x];
+      if (t < k1) {
+        if constexpr (MODE == OBS_SCORE) {
+          a.score[uh * N + t] = v;
+        } else {
+          const bool anc = a.anchor_of[uh * N + t] >= 0;
+          const int64_t iK = ((int64_t)u * 2 * H + h) * N + t;
+          a.util[iK] = anc ? -1.0f : v;
+        }
+      }
+    }
+  };
   if constexpr (ROPE) {
     if constexpr (MODE == OBS_UTIL) {
 #pragma unroll
@@ -371,6 +388,9 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       }
     }
     __syncthreads();
+    if constexpr (MODE != OBS_STATS) {
+      if (t0 > k0) finish_tile(t0 - 64);
+    }
     // pre-RoPE: the next tile's rows are loaded while this one is computed
     if constexpr (ROPE) {
       if (t0 + 64 < k1) load_raw(t0 + 64);
@@ -509,29 +529,18 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
     }
 
     if constexpr (MODE != OBS_STATS) {
-      // column sums over the 16 query lanes, then over waves in a fixed order
+      // column sums over the 16 query lanes; summed over the waves (fixed
+      // order) after the next tile's staging barrier, or after the loop
       for (int kb = 0; kb < 4; ++kb)
         for (int r = 0; r < 4; ++r) {
           const float v = row_sum(colsum[kb][r]);   // over the 16 query lanes (DPP)
-          if (col == 0) colpart[wave][kb * 16 + kg * 4 + r] = v;
+          if (col == 0) colpart[((t0 - k0) >> 6) & 1][wave][kb * 16 + kg * 4 + r] = v;
         }
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        const int t = t0 + threadIdx.x;
-        float v = 0.0f;
-        for (int w = 0; w < nw; ++w) v += colpart[w][threadIdx.x];
-        if (t < k1) {
-          if constexpr (MODE == OBS_SCORE) {
-            a.score[uh * N + t] = v;
-          } else {
-            const bool anc = a.anchor_of[uh * N + t] >= 0;
-            const int64_t iK = ((int64_t)u * 2 * H + h) * N + t;
-            a.util[iK] = anc ? -1.0f : v;
-          }
-        }
-      }
     }
-    __syncthreads();
+    __syncthreads();   // the tile's buffers are free; its column sums are published
+  }
+  if constexpr (MODE != OBS_STATS) {
+    if (k1 > k0) finish_tile(k0 + ((k1 - k0 - 1) >> 6) * 64);
   }
 
   if constexpr (MODE == OBS_STATS) {
