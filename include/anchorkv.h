@@ -105,8 +105,10 @@ typedef struct {
  * assignment, gamma and residuals are those of the stored pre-RoPE keys.
  * Decode: logits <q, R_t(gamma k_a + r~)>/sqrt(D) with q given already
  * rotated; an appended tail is attended as given (its keys already rotated).
- * Needs the group-affine codec and q_per_kv * n_obs <= 128 (the observation
- * pass runs in f32 on the rotated keys). */
+ * Needs the group-affine codec.  With more than 128 observation queries per
+ * KV head (q_per_kv * n_obs up to 256) the observation passes give each
+ * (unit, head, key range) two workgroups of up to 128 queries whose score and
+ * key-utility partials are added. */
 
 /* How the non-scored anchors are picked.  UNIFORM: stratified over the
  * positions left after the scored ones.  COVER: coverage-optimised (Pith

@@ -23,6 +23,12 @@ __global__ void k_zero_u32(unsigned* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
+// Zeroes nseg segments of len words, seg_stride words apart.
+__global__ void k_zero_seg(unsigned* p, int64_t len, int64_t seg_stride, int64_t nseg) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < len * nseg) p[(i / len) * seg_stride + i % len] = 0u;
+}
+
 // ------------------------------------------------------------------ headers
 __global__ void k_headers(UnitHeader hd, uint8_t* cache, int64_t stride) {
   const int u = blockIdx.x;
@@ -1181,11 +1187,26 @@ __global__ __launch_bounds__(256) void k_rope_table(float2* cs, int N, double ba
 // keys (and in UTIL each token's anchor row) rotated while the tiles are
 // staged; always 512 threads (the staging takes two items per thread; waves
 // past the query blocks only stage).
+// More than 8 query blocks (up to 16) take two workgroups per (unit, head,
+// key split), each with 8 query blocks; their score (SCORE) and key-utility
+// (UTIL) partials are added onto words zeroed here.
 template <int DT, int MODE>
-static int launch_obs_rope(const anchorkv_plan_info& p, const ObsArgs& a, hipStream_t st) {
-  const int QB = a.GQp / 16;
-  if (QB > 8) return fail(ANCHORKV_E_SHAPE, "pre-RoPE keys: q_per_kv*n_obs must be <= 128");
-  const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1));
+static int launch_obs_rope(const anchorkv_plan_info& p, const ObsArgs& a0, hipStream_t st) {
+  const int QB = a0.GQp / 16;
+  if (QB > 16) return fail(ANCHORKV_E_SHAPE, "pre-RoPE keys: q_per_kv*n_obs must be <= 256");
+  ObsArgs a = a0;
+  a.qsplit = QB > 8 ? 2 : 1;
+  if (a.qsplit > 1 && MODE != OBS_STATS) {
+    const int64_t H = p.H, N = p.N;
+    // SCORE: score [U][H][N]; UTIL: the key side of util [U][2][H][N]
+    unsigned* z = reinterpret_cast<unsigned*>(MODE == OBS_SCORE ? a.score : a.util);
+    const int64_t len = MODE == OBS_SCORE ? (int64_t)p.units * H * N : H * N;
+    const int64_t seg = MODE == OBS_SCORE ? len : 2 * H * N;
+    const int64_t nseg = MODE == OBS_SCORE ? 1 : p.units;
+    k_zero_seg<<<(unsigned)((len * nseg + 255) / 256), 256, 0, st>>>(z, len, seg, nseg);
+    AKV_CHECK_LAUNCH("k_zero_seg");
+  }
+  const dim3 grid((unsigned)((int64_t)p.units * p.H * a.S1 * a.qsplit));
   // bf16: rotated keys as bf16 hi + lo on the bf16 MFMA; f32: f32 MFMA
   if constexpr (DT == ANCHORKV_BF16) k_obs<ANCHORKV_BF16, MODE, 1, ANCHORKV_BF16, true><<<grid, dim3(512), 0, st>>>(a);
   else k_obs<ANCHORKV_F32, MODE, 1, ANCHORKV_F32, true><<<grid, dim3(512), 0, st>>>(a);
@@ -1476,8 +1497,6 @@ static int compress_impl(const anchorkv_plan_info& p, const void* K, const void*
 int compress_supports(const anchorkv_plan_info& p) {
   const int QB = padded_queries(p) / 16;
   if (p.dtype == ANCHORKV_F32 && QB > 8) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: f32 needs q_per_kv*n_obs <= 128");
-  if (p.params.rope && QB > 8)
-    return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: pre-RoPE keys need q_per_kv*n_obs <= 128");
   if (QB > 16) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: q_per_kv*n_obs must be <= 256");
   if (p.A > 4096) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: %d anchors per head; compress supports <= 4096", p.A);
   if (p.params.pool > kMaxPool) return fail(ANCHORKV_E_SHAPE, "anchorkv_plan: pool width > %d", kMaxPool);

@@ -53,6 +53,8 @@ struct ObsArgs {
   float c;               // log2(e)/sqrt(D)
   float inv_sqrt_d;
   const float2* rope_cs; // pre-RoPE keys: (cos, sin) [N][D/2] of the rotation at each position
+  int qsplit;            // generic kernel: query-block groups per (unit, head, key split), each its own
+                         // block of 8 query blocks; > 1 adds the groups' score / key-utility partials
 };
 
 template <int DT> struct ObsCfg {
@@ -124,6 +126,12 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
   const int col = lane & 15, kg = lane >> 4;
   int bid = blockIdx.x;
   const int s = bid % a.S1; bid /= a.S1;
+  // query-block group of this block: blocks 0..nw-1 of the padded queries,
+  // then nw..2nw-1, ... (more than 8 query blocks take several workgroups)
+  int qgrp = 0;
+  if (a.qsplit > 1) { qgrp = bid % a.qsplit; bid /= a.qsplit; }
+  const int qbase = qgrp * nw;
+  const bool qadd = a.qsplit > 1;   // partials of several groups are added
   const int h = bid % a.H;
   const int u = bid / a.H;
   const int N = a.N, H = a.H;
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
   bool qvalid[QPW];
   int qj[QPW];
   for (int qi = 0; qi < QPW; ++qi) {
-    const int qb = wave + qi * nw;
+    const int qb = qbase + wave + qi * nw;
     const int q = qb * 16 + col;
     qvalid[qi] = (qb * 16 < a.GQp) && q < a.GQ;
     qj[qi] = q % a.n_obs;
@@ -324,12 +332,17 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
       float v = 0.0f;
       for (int w = 0; w < nw; ++w) v += colpart[((tb - k0) >> 6) & 1][w][threadIdx.x];
       if (t < k1) {
+        // with query groups the two-or-more partials are added onto a zeroed
+        // word (with two of them the sum does not depend on their order)
         if constexpr (MODE == OBS_SCORE) {
-          a.score[uh * N + t] = v;
+          if (qadd) atomicAdd(&a.score[uh * N + t], v);
+          else a.score[uh * N + t] = v;
         } else {
           const bool anc = a.anchor_of[uh * N + t] >= 0;
           const int64_t iK = ((int64_t)u * 2 * H + h) * N + t;
-          a.util[iK] = anc ? -1.0f : v;
+          if (anc) a.util[iK] = -1.0f;
+          else if (qadd) atomicAdd(&a.util[iK], v);
+          else a.util[iK] = v;
         }
       }
     }
@@ -432,7 +445,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
         }
       }
       for (int qi = 0; qi < QPW; ++qi) {
-        if (!(wave + qi * nw < a.GQp / 16)) continue;  // wave-uniform
+        if (!(qbase + wave + qi * nw < a.GQp / 16)) continue;  // wave-uniform
         float pv[2][4];
         for (int k2 = 0; k2 < 2; ++k2) {
           const int kb = c2 * 2 + k2;
@@ -482,7 +495,7 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
                   const float qr = fabsf(acc[r] - gam_s[kl] * accg[r]) * a.inv_sqrt_d;
                   float vo2 = vv_s[kl] - 2.0f * accv[r] + ooq[qi];
                   if (vo2 < 0.5f * (vv_s[kl] + ooq[qi])) {  // cancellation: recompute directly
-                    const int q = (wave + qi * nw) * 16 + col;
+                    const int q = (qbase + wave + qi * nw) * 16 + col;
                     const float* orow = a.ofull + (uh * a.GQp + q) * D;
                     float acc2 = 0.0f;
                     for (int d = 0; d < D; ++d) {
@@ -554,13 +567,13 @@ __global__ __launch_bounds__(512) void k_obs(ObsArgs a) {
           m = mx;
         }
       }
-      const int qb = wave + qi * nw;
+      const int qb = qbase + wave + qi * nw;
       if (kg == 0 && qb * 16 < a.GQp) a.ml_part[(uh * a.S1 + s) * a.GQp + qb * 16 + col] = make_float2(m, l);
     }
   }
   if constexpr (MODE == OBS_SCORE) {
     for (int qi = 0; qi < QPW; ++qi) {
-      const int qb = wave + qi * nw;
+      const int qb = qbase + wave + qi * nw;
       if (qb * 16 >= a.GQp) continue;
       for (int db = 0; db < 8; ++db)
         for (int r = 0; r < 4; ++r) {

@@ -376,8 +376,9 @@ def test_rope_parameters(akv):
     """Pre-RoPE key storage (anchorkv_params.rope, rope_theta): off by default
     with base 500000; it changes neither counts nor layout; the header records
     it (the plan rebuilt from a packed unit's header keeps it); the plan
-    refuses it with the Hadamard / Lloyd-Max codec, with more than 128
-    observation queries per KV head, and with a base outside (1, 1e10]."""
+    refuses it with the Hadamard / Lloyd-Max codec and with a base outside
+    (1, 1e10]; 256 observation queries per KV head are accepted, more are
+    refused as for keys stored rotated."""
     q = akv.params(0.05, 32)
     assert (q.rope, q.rope_theta) == (0, 500000.0)
     pu = akv.plan(2, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32)
@@ -413,6 +414,9 @@ def test_rope_parameters(akv):
         with pytest.raises(E) as e:
             akv.plan(1, 8, 4, 8192, 128, 32, akv.BF16, 0.1, 32, **kw)
         assert e.value.code == -1, kw
+    # 256 observation queries per KV head: two query groups per key range
+    p256 = akv.plan(1, 8, 8, 8192, 128, 32, akv.BF16, 0.1, 32, rope=1)
+    assert p256.params.rope == 1 and p256.G == 8 and p256.n_obs == 32
     with pytest.raises(E) as e:
-        akv.plan(1, 8, 8, 8192, 128, 32, akv.BF16, 0.1, 32, rope=1)   # 256 observation queries per KV head
+        akv.plan(1, 8, 8, 8192, 128, 33, akv.BF16, 0.1, 32, rope=1)   # 264 > 256
     assert e.value.code == -3

@@ -86,6 +86,12 @@ SMALL = {
     "f32_rope": W_["tiny_f32"].scaled(n_tokens=1500),
     "bf16_rope_g8": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=4500, n_obs=16, theta=0.08),
     "bf16_rope_joint": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=3000, n_dirs=32),
+    # more than 128 observation queries per KV head: two query groups per key range whose score
+    # and key-utility partials are added (the 70B shape's 8 x 32; 6 x 32 leaves the second
+    # group half empty)
+    "bf16_rope_q256": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=4500, theta=0.08),
+    "bf16_rope_q192": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=6, n_tokens=3300,
+                                               n_dirs=32),
     # one 8B-shaped head at its full 32K tokens: 32 chunks of phase recurrence per decode range
     "bf16_rope_long": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=1),
     # pre-RoPE decode with a large [q-head][anchor] weight table (8 x 865, 55 KB of LDS) and, past
@@ -108,7 +114,8 @@ PARAMS = {"bf16_params": dict(pool=5, rho=0.5, anchor_div=64), "f32_params": dic
           "bf16_cover_g8": dict(anchor_mode=1),
           "bf16_rope": dict(rope=1), "bf16_rope_base1e4": dict(rope=1, rope_theta=10000.0),
           "f32_rope": dict(rope=1, rope_theta=10000.0), "bf16_rope_g8": dict(rope=1),
-          "bf16_rope_joint": dict(rope=1, pool_kv_jointly=1), "bf16_rope_long": dict(rope=1, rope_theta=10000.0),
+          "bf16_rope_joint": dict(rope=1, pool_kv_jointly=1), "bf16_rope_q256": dict(rope=1),
+          "bf16_rope_q192": dict(rope=1, rope_theta=10000.0), "bf16_rope_long": dict(rope=1, rope_theta=10000.0),
           "bf16_rope_wide": dict(rope=1, anchor_div=6), "bf16_rope_bigA": dict(rope=1, anchor_div=4)}
 
 
