@@ -251,20 +251,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_assign_res(AssignArgs g) {
   // into that token's running key with two v_max3_f32.  At the end of an
   // epoch the running key (masked value, tag = epoch position) is compared
   // with the token's best so far (bv, bix) and restarted.
+  // A block's 1/||x_a|| are read before its MFMAs, and the next block's first
+  // A fragment before its keys are formed, so both LDS reads are in flight
+  // while the block's MFMA and VALU work runs.
   auto search_part = [&](int nab, int gab0, float (&bv)[4], int (&bix)[4]) {
+    bf16x8 af0 = bits_to_frag(As[res_phys(col, kg)]);
     for (int e = 0; e < nab; e += 8) {
       float run[4];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j > 0 && e + j >= nab) break;
         const int ab = e + j;
+        const float4 inv = *reinterpret_cast<const float4*>(inv_s + ab * 16 + kg * 4);
         f32x4 acc[4];
         for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0, 0, 0, 0};
         for (int st = 0; st < 4; ++st) {
-          const bf16x8 af = bits_to_frag(As[res_phys(ab * 16 + col, st * 4 + kg)]);
+          const bf16x8 af = st == 0 ? af0 : bits_to_frag(As[res_phys(ab * 16 + col, st * 4 + kg)]);
           for (int rb = 0; rb < 4; ++rb) acc[rb] = M::mma(af, xf[rb][st], acc[rb]);
         }
-        const float4 inv = *reinterpret_cast<const float4*>(inv_s + ab * 16 + kg * 4);
+        // rows past the part's padded blocks are never read: the last block
+        // reads its own first fragment again
+        af0 = bits_to_frag(As[res_phys(min(ab + 1, nab - 1) * 16 + col, kg)]);
         const float iv[4] = {inv.x, inv.y, inv.z, inv.w};
         for (int rb = 0; rb < 4; ++rb) {
           float k[4];
