@@ -89,7 +89,7 @@ SMALL = {
     # more than 128 observation queries per KV head: two query groups per key range whose score
     # and key-utility partials are added (the 70B shape's 8 x 32; 6 x 32 leaves the second
     # group half empty)
-    "bf16_rope_q256": W_["llama70b_128k"].scaled(seqs=1, layers=1, kv_heads=2, n_tokens=4500, theta=0.08),
+    "bf16_rope_q256": W_["llama70b_128k"].scaled(seqs=1, layers=2, kv_heads=2, n_tokens=4500, theta=0.08),
     "bf16_rope_q192": W_["llama8b_32k"].scaled(seqs=1, layers=1, kv_heads=2, q_per_kv=6, n_tokens=3300,
                                                n_dirs=32),
     # one 8B-shaped head at its full 32K tokens: 32 chunks of phase recurrence per decode range
@@ -212,6 +212,29 @@ def test_decode_on_host_packed_oracle_cache(akv, name):
             err = np.linalg.norm(o_h[u] - ref, axis=1) / np.linalg.norm(ref, axis=1)
             assert err.max() <= 1e-3, (step, u, err.max())
     _flush(f"[decode-packed] {name}: ok")
+
+
+@pytest.mark.parametrize("name", ["bf16_rope_q256", "bf16_rope_g8", "bf16_rope", "bf16_cover_g8"])
+def test_compress_on_a_dirty_workspace(akv, name):
+    """A workspace full of garbage gives the same cache, bit for bit, as a
+    clean one; with pre-RoPE keys and 256 observation queries per KV head the
+    two query groups add their score and key-utility partials onto words
+    cleared inside compress."""
+    w = SMALL[name]
+    _flush(f"[determinism] {name}: U={w.units}")
+    K, V, Q = make_inputs(w)
+    p = plan_for(akv, w, PARAMS[name])
+    c1, ws, _ = akv.alloc(p, "cuda")
+    c2 = torch.empty_like(c1)
+    ws.zero_()
+    akv.compress(p, K, V, Q, c1, ws)
+    ws.fill_(0xAB)
+    akv.compress(p, K, V, Q, c2, ws)
+    torch.cuda.synchronize()
+    # each unit's bytes (the padding up to the unit stride is not written)
+    for u in range(w.units):
+        a, b = u * p.unit_stride, u * p.unit_stride + p.unit_bytes
+        assert torch.equal(c1[a:b], c2[a:b]), u
 
 
 def test_compress_is_deterministic_and_header_roundtrips(akv):
